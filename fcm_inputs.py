@@ -1,0 +1,186 @@
+"""Seeded synthetic workloads for the fused depthwise->pointwise module and the
+3x3->1x1 back-to-back pair.
+
+This module only describes shapes and draws random numbers: it holds none of the
+method's arithmetic and imports neither the HIP library nor the oracle, so both sides
+can take their inputs from it.
+
+Every tensor is drawn in float64 from ``numpy.random.default_rng(seed)`` in the fixed
+order X, first-layer weights, scale1, bias1, second-layer weights, scale2, bias2, then
+narrowed to float32 and from there to the storage type with torch's round-to-nearest-
+even casts.  The narrowed values *are* the inputs: both the oracle and the GPU see the
+same numbers.  Weight layouts are PyTorch's: depthwise [C, 3, 3], pointwise [K, C],
+standard conv [K1, C, 3, 3], second conv [K, K1].
+
+The five workloads stand in for the layer shapes the pages evaluate (MobileNet-style
+depthwise-separable blocks, the forum's CIFAR network, ResNet-style 3x3 -> 1x1 pairs);
+no dataset or trained weight is involved.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "dwpw" or "b2b"
+    dtype: str           # "f32" | "f16" | "bf16"
+    N: int
+    H: int
+    W: int
+    C: int
+    K: int               # output channels of the final 1x1 conv
+    K1: int              # b2b: output channels of the 3x3 conv; dwpw: == C
+    stride: int = 1
+    pad: int = 1
+    R: int = 3
+    S: int = 3
+    act1: str = "none"
+    act2: str = "none"
+    scale1: bool = False  # whether a per-channel scale / bias array is passed
+    bias1: bool = False
+    scale2: bool = False
+    bias2: bool = False
+    x_dist: tuple = ("normal", 0.0, 1.0)
+    w_dist: tuple = ("normal", 0.0, 0.1)
+    scale_dist: tuple = ("uniform", 0.5, 1.5)
+    bias_dist: tuple = ("normal", 0.0, 0.1)
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def Ho(self) -> int:
+        return (self.H + 2 * self.pad - self.R) // self.stride + 1
+
+    @property
+    def Wo(self) -> int:
+        return (self.W + 2 * self.pad - self.S) // self.stride + 1
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "cfg1": Workload(
+        "cfg1", "dwpw", "f32", N=1, H=16, W=16, C=32, K=32, K1=32,
+        bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("uniform", -0.5, 0.5),
+        bias_dist=("zero",), seed=1,
+        description="DW 3x3 s1 p1 + PW 1x1, fp32, N=1 16x16 C=32 K=32, bias 0, "
+                    "no activation"),
+    "cfg2": Workload(
+        "cfg2", "dwpw", "f16", N=8, H=112, W=112, C=64, K=128, K1=64,
+        act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
+        x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=2,
+        description="MobileNetV1-style block: DW 3x3 s1 C=64 + scale/bias+ReLU6, "
+                    "PW 64->128 + scale/bias+ReLU6, fp16, N=8 112x112"),
+    "cfg3": Workload(
+        "cfg3", "dwpw", "bf16", N=256, H=32, W=32, C=128, K=128, K1=128,
+        act2="relu", bias2=True, x_dist=("uniform", -1.0, 1.0),
+        w_dist=("normal", 0.0, 0.05), bias_dist=("normal", 0.0, 0.05), seed=3,
+        description="CIFAR-style DW+PW pair: DW 3x3 s1 groups=C + PW 128->128, bf16, "
+                    "N=256 32x32, bias+ReLU after PW"),
+    "cfg4a": Workload(
+        "cfg4a", "dwpw", "f16", N=64, H=56, W=56, C=256, K=512, K1=256, stride=2,
+        act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
+        w_dist=("normal", 0.0, 0.05), seed=41,
+        description="Downsampling FCM: DW 3x3 s2 C=256 + PW 256->512, scale/bias+ReLU6 "
+                    "each, fp16, N=64 56x56 -> 28x28"),
+    "cfg4b": Workload(
+        "cfg4b", "dwpw", "f16", N=64, H=7, W=7, C=1024, K=1024, K1=1024,
+        act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
+        w_dist=("normal", 0.0, 0.05), seed=42,
+        description="Late-stage FCM: DW 3x3 s1 C=1024 + PW 1024->1024, "
+                    "scale/bias+ReLU6 each, fp16, N=64 7x7"),
+    "cfg5": Workload(
+        "cfg5", "b2b", "f16", N=32, H=56, W=56, C=64, K=64, K1=64,
+        act1="relu", act2="relu", scale1=True, bias1=True, scale2=True, bias2=True,
+        w_dist=("normal", 0.0, 0.05), seed=5,
+        description="Back-to-back: conv 3x3 p1 64->64 + scale_bias_relu, conv 1x1 "
+                    "64->64 + scale_bias_relu, fp16, N=32 56x56"),
+}
+
+
+def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
+    kind = dist[0]
+    if kind == "normal":
+        return rng.normal(dist[1], dist[2], size=shape)
+    if kind == "uniform":
+        return rng.uniform(dist[1], dist[2], size=shape)
+    if kind == "zero":
+        return np.zeros(shape)
+    if kind == "int":          # small integers in [lo, hi]
+        return rng.integers(dist[1], dist[2] + 1, size=shape).astype(np.float64)
+    if kind == "sparse_sign":  # values in {-1, 0, 1} with P(nonzero) = dist[1]
+        mag = rng.random(size=shape) < dist[1]
+        sign = np.where(rng.random(size=shape) < 0.5, -1.0, 1.0)
+        return np.where(mag, sign, 0.0)
+    raise ValueError(f"unknown distribution {dist}")
+
+
+def _narrow(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> float32 -> storage type (torch RNE casts); returned as float64."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    return t.to(tdt).to(torch.float64).numpy()
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None) -> dict:
+    """Draw the workload's tensors.  Returns float64 numpy arrays whose values are
+    exactly representable in the storage type (scale/bias are float32 values)."""
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = _draw(rng, wl.x_dist, (wl.N, wl.H, wl.W, wl.C))
+    if wl.kind == "dwpw":
+        w1 = _draw(rng, wl.w_dist, (wl.C, wl.R, wl.S))
+        n1 = wl.C
+    else:
+        w1 = _draw(rng, wl.w_dist, (wl.K1, wl.C, wl.R, wl.S))
+        n1 = wl.K1
+    s1 = _draw(rng, wl.scale_dist, (n1,)) if wl.scale1 else None
+    b1 = _draw(rng, wl.bias_dist, (n1,)) if wl.bias1 else None
+    w2 = _draw(rng, wl.w_dist, (wl.K, n1))
+    s2 = _draw(rng, wl.scale_dist, (wl.K,)) if wl.scale2 else None
+    b2 = _draw(rng, wl.bias_dist, (wl.K,)) if wl.bias2 else None
+    out = {
+        "x": _narrow(x, wl.dtype),
+        "w1": _narrow(w1, wl.dtype),
+        "w2": _narrow(w2, wl.dtype),
+        "scale1": None if s1 is None else _narrow(s1, "f32"),
+        "bias1": None if b1 is None else _narrow(b1, "f32"),
+        "scale2": None if s2 is None else _narrow(s2, "f32"),
+        "bias2": None if b2 is None else _narrow(b2, "f32"),
+    }
+    return out
+
+
+def to_torch(a: Optional[np.ndarray], dtype: str, device=None):
+    """Cast a float64 array (already representable) to a torch tensor of the storage
+    type, optionally on a device."""
+    if a is None:
+        return None
+    import torch
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(tdt)
+    return t.to(device) if device is not None else t
+
+
+def sample_pixels(wl: Workload, count: int, seed: int = 1234) -> np.ndarray:
+    """Output pixels (n, oh, ow) to check at full size: all four image corners and
+    edges of the first and last image plus uniformly drawn interior pixels."""
+    rng = np.random.default_rng(seed)
+    fixed = []
+    for n in {0, wl.N - 1}:
+        for oh in {0, wl.Ho - 1, wl.Ho // 2}:
+            for ow in {0, wl.Wo - 1, wl.Wo // 2}:
+                fixed.append((n, oh, ow))
+    k = max(0, count - len(fixed))
+    rnd = np.stack([rng.integers(0, wl.N, k), rng.integers(0, wl.Ho, k),
+                    rng.integers(0, wl.Wo, k)], axis=1) if k else np.zeros((0, 3), int)
+    return np.concatenate([np.array(fixed, dtype=np.int64).reshape(-1, 3), rnd]).astype(
+        np.int32)

@@ -1,0 +1,317 @@
+/*
+ * fcm_oracle.c -- CPU oracle for the fused depthwise->pointwise convolution module
+ * (FCM) and the back-to-back 3x3 -> 1x1 convolution pair.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this
+ * file: only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes is the plain, unfused definition, evaluated in double precision
+ * with direct loops in a fixed order:
+ *
+ *   depthwise conv   -- one filter per channel slid over height and width
+ *                       ("Fusing Depthwise and Pointwise Convolutions for Efficient
+ *                       Inference on GPUs", Sec. II-B, Fig. 2);
+ *   pointwise conv   -- a 1x1 filter spanning all channels (same section);
+ *   standard conv    -- the first layer of the back-to-back pair, [N,H,W,C] x
+ *                       [K,C,R,S] ("Fusing two back-to-back convolutions", the
+ *                       CONV1/CONV2 example);
+ *   epilogue         -- conv -> normalisation -> activation, i.e. a per-channel
+ *                       scale and bias followed by ReLU or ReLU6 (FCM paper Sec. III-A
+ *                       "up to 6 layers"; the CUTLASS discussion's scale_bias_relu);
+ *   storage rounding -- each layer's output is rounded to the storage type before the
+ *                       next layer reads it, exactly as a layer-by-layer execution
+ *                       that writes its output feature maps to memory would do (FCM
+ *                       paper Sec. II-D, Fig. 3(a)).  Fusion changes where the
+ *                       intermediate lives, not its value.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - cross-correlation (no filter flip), as PyTorch's nn.Conv2d used on the forum
+ *     page ("Using optimised depthwise convolutions", SeparableConv2d listing);
+ *   - zero padding; output size floor((H + 2p - R)/s) + 1;
+ *   - epilogue y = act(scale[c]*acc + bias[c]); a NULL scale means 1, a NULL bias 0;
+ *   - rounding to binary16 / bfloat16 / binary32 is IEEE round-to-nearest-even,
+ *     implemented below from the format definitions (not with a library cast).
+ *
+ * Layouts (PyTorch's, independent of the GPU library's packed layouts):
+ *   activations NHWC [N][H][W][C]; depthwise weights [C][R][S]; pointwise weights
+ *   [K][C]; standard conv weights [K][C][R][S].
+ *
+ * Parallelism: an OpenMP loop over output rows; every output element is still a
+ * sequential sum in a fixed order, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_F16 1
+#define ORACLE_BF16 2
+
+#define ACT_NONE 0
+#define ACT_RELU 1
+#define ACT_RELU6 2
+
+/* ------------------------------------------------------------------------------ */
+/* IEEE-754 round-to-nearest-even into a binary format with `mant` explicit       */
+/* fraction bits and exponent range [emin, emax].  binary16: (10, -14, 15);       */
+/* bfloat16: (7, -126, 127); binary32: (23, -126, 127).  Works on the value: the  */
+/* representable numbers near |v| are integer multiples of the quantum            */
+/* 2^(max(e, emin) - mant) where 2^e <= |v| < 2^(e+1); subnormals share the       */
+/* quantum of the smallest normal binade.                                           */
+/* ------------------------------------------------------------------------------ */
+static double round_binary(double v, int mant, int emin, int emax) {
+    if (v != v || v == 0.0 || isinf(v)) return v;
+    double a = fabs(v);
+    int e2;
+    frexp(a, &e2);          /* a = f * 2^e2 with f in [0.5, 1)  =>  2^(e2-1) <= a */
+    int e = e2 - 1;
+    if (e < emin) e = emin;
+    double quantum = ldexp(1.0, e - mant);
+    double n = a / quantum; /* exact: scaling by a power of two */
+    double fl = floor(n);
+    double rem = n - fl;    /* exact */
+    if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double r = fl * quantum;
+    double max_finite = ldexp(2.0 - ldexp(1.0, -mant), emax);
+    if (r > max_finite) r = INFINITY;
+    return copysign(r, v);
+}
+
+double fcm_oracle_round(double v, int dtype) {
+    switch (dtype) {
+    case ORACLE_F16: return round_binary(v, 10, -14, 15);
+    case ORACLE_BF16: return round_binary(v, 7, -126, 127);
+    default: return round_binary(v, 23, -126, 127);
+    }
+}
+
+void fcm_oracle_round_array(double* a, int64_t n, int dtype) {
+    for (int64_t i = 0; i < n; ++i) a[i] = fcm_oracle_round(a[i], dtype);
+}
+
+/* Bit pattern of the binary16 / bfloat16 value nearest to v (RNE).  Built from the
+ * rounded value: sign, biased exponent, fraction. */
+static uint16_t encode16(double v, int mant, int emin, int bias) {
+    double r = (mant == 10) ? round_binary(v, 10, -14, 15) : round_binary(v, 7, -126, 127);
+    uint16_t sign = (uint16_t)(signbit(r) ? 0x8000u : 0u);
+    int ebits = 15 - mant;
+    uint16_t exp_all = (uint16_t)(((1u << ebits) - 1u) << mant);
+    if (r != r) return (uint16_t)(exp_all | (1u << (mant - 1)));
+    double a = fabs(r);
+    if (isinf(a)) return (uint16_t)(sign | exp_all);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int e = e2 - 1;
+    if (e < emin) { /* subnormal: a = frac * 2^(emin - mant) */
+        uint16_t frac = (uint16_t)ldexp(a, mant - emin);
+        return (uint16_t)(sign | frac);
+    }
+    uint16_t frac = (uint16_t)(ldexp(a, mant - e) - ldexp(1.0, mant));
+    return (uint16_t)(sign | ((uint16_t)(e + bias) << mant) | frac);
+}
+
+uint16_t fcm_oracle_f16_bits(double v) { return encode16(v, 10, -14, 15); }
+uint16_t fcm_oracle_bf16_bits(double v) { return encode16(v, 7, -126, 127); }
+
+/* ------------------------------------------------------------------------------ */
+/* Layers                                                                           */
+/* ------------------------------------------------------------------------------ */
+static int out_size(int in, int pad, int filt, int stride) {
+    return (in + 2 * pad - filt) / stride + 1;
+}
+
+/* Depthwise convolution: t[n][oh][ow][c] = sum_{r,s} x[n][ih][iw][c] * w[c][r][s],
+ * ih = oh*sh - ph + r, iw = ow*sw - pw + s, x = 0 outside the image. */
+void fcm_oracle_dw(const double* x, int N, int H, int W, int C, const double* w, int R,
+                   int S, int sh, int sw, int ph, int pw, double* t) {
+    int Ho = out_size(H, ph, R, sh), Wo = out_size(W, pw, S, sw);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int oh = 0; oh < Ho; ++oh)
+            for (int ow = 0; ow < Wo; ++ow)
+                for (int c = 0; c < C; ++c) {
+                    double acc = 0.0;
+                    for (int r = 0; r < R; ++r)
+                        for (int s = 0; s < S; ++s) {
+                            int ih = oh * sh - ph + r, iw = ow * sw - pw + s;
+                            if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;
+                            acc += x[(((int64_t)n * H + ih) * W + iw) * C + c] *
+                                   w[((int64_t)c * R + r) * S + s];
+                        }
+                    t[(((int64_t)n * Ho + oh) * Wo + ow) * C + c] = acc;
+                }
+}
+
+/* Pointwise (1x1) convolution over M = N*H*W pixels: y[m][k] = sum_c t[m][c]*w[k][c]. */
+static void pw_row(const double* t, int C, const double* w, int K, double* y);
+void fcm_oracle_pw(const double* t, int64_t M, int C, const double* w, int K, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) pw_row(t + m * C, C, w, K, y + m * K);
+}
+
+/* Standard convolution: y[n][oh][ow][k] = sum_{c,r,s} x[n][ih][iw][c] * w[k][c][r][s]. */
+void fcm_oracle_conv(const double* x, int N, int H, int W, int C, const double* w, int K,
+                     int R, int S, int sh, int sw, int ph, int pw, double* y) {
+    int Ho = out_size(H, ph, R, sh), Wo = out_size(W, pw, S, sw);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int oh = 0; oh < Ho; ++oh)
+            for (int ow = 0; ow < Wo; ++ow)
+                for (int k = 0; k < K; ++k) {
+                    double acc = 0.0;
+                    for (int c = 0; c < C; ++c)
+                        for (int r = 0; r < R; ++r)
+                            for (int s = 0; s < S; ++s) {
+                                int ih = oh * sh - ph + r, iw = ow * sw - pw + s;
+                                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;
+                                acc += x[(((int64_t)n * H + ih) * W + iw) * C + c] *
+                                       w[(((int64_t)k * C + c) * R + r) * S + s];
+                            }
+                    y[(((int64_t)n * Ho + oh) * Wo + ow) * K + k] = acc;
+                }
+}
+
+/* Per-channel normalisation + activation of one pixel's C values, in place. */
+static void epilogue_row(double* a, int C, const double* scale, const double* bias, int act) {
+    for (int c = 0; c < C; ++c) {
+        double v = a[c];
+        if (scale) v = scale[c] * v;
+        if (bias) v = v + bias[c];
+        if (act == ACT_RELU || act == ACT_RELU6) v = v > 0.0 ? v : 0.0;
+        if (act == ACT_RELU6) v = v < 6.0 ? v : 6.0;
+        a[c] = v;
+    }
+}
+
+/* One pixel of the pointwise conv: y[k] = sum_c t[c] * w[k][c]. */
+static void pw_row(const double* t, int C, const double* w, int K, double* y) {
+    for (int k = 0; k < K; ++k) {
+        double acc = 0.0;
+        for (int c = 0; c < C; ++c) acc += t[c] * w[(int64_t)k * C + c];
+        y[k] = acc;
+    }
+}
+
+/* Per-channel normalisation + activation in place over a [M][C] array. */
+void fcm_oracle_epilogue(double* a, int64_t M, int C, const double* scale,
+                         const double* bias, int act) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) epilogue_row(a + m * C, C, scale, bias, act);
+}
+
+/* ------------------------------------------------------------------------------ */
+/* The two modules, layer by layer.  t_out (optional) receives the rounded          */
+/* intermediate that a layer-by-layer execution would store.  Returns 0, or -1 if   */
+/* memory for the intermediate could not be obtained.                               */
+/* ------------------------------------------------------------------------------ */
+int fcm_oracle_dwpw(const double* x, int N, int H, int W, int C, const double* w_dw,
+                    int R, int S, int sh, int sw, int ph, int pw, const double* scale1,
+                    const double* bias1, int act1, const double* w_pw, int K,
+                    const double* scale2, const double* bias2, int act2, int dtype,
+                    double* t_out, double* y) {
+    int Ho = out_size(H, ph, R, sh), Wo = out_size(W, pw, S, sw);
+    int64_t M = (int64_t)N * Ho * Wo;
+    double* t = t_out ? t_out : (double*)malloc(sizeof(double) * (size_t)(M * C));
+    if (!t) return -1;
+    fcm_oracle_dw(x, N, H, W, C, w_dw, R, S, sh, sw, ph, pw, t);
+    fcm_oracle_epilogue(t, M, C, scale1, bias1, act1);
+    fcm_oracle_round_array(t, M * C, dtype);
+    fcm_oracle_pw(t, M, C, w_pw, K, y);
+    fcm_oracle_epilogue(y, M, K, scale2, bias2, act2);
+    fcm_oracle_round_array(y, M * K, dtype);
+    if (!t_out) free(t);
+    return 0;
+}
+
+int fcm_oracle_b2b(const double* x, int N, int H, int W, int C, const double* w1, int K1,
+                   int R, int S, int sh, int sw, int ph, int pw, const double* scale1,
+                   const double* bias1, int act1, const double* w2, int K,
+                   const double* scale2, const double* bias2, int act2, int dtype,
+                   double* t_out, double* y) {
+    int Ho = out_size(H, ph, R, sh), Wo = out_size(W, pw, S, sw);
+    int64_t M = (int64_t)N * Ho * Wo;
+    double* t = t_out ? t_out : (double*)malloc(sizeof(double) * (size_t)(M * K1));
+    if (!t) return -1;
+    fcm_oracle_conv(x, N, H, W, C, w1, K1, R, S, sh, sw, ph, pw, t);
+    fcm_oracle_epilogue(t, M, K1, scale1, bias1, act1);
+    fcm_oracle_round_array(t, M * K1, dtype);
+    fcm_oracle_pw(t, M, K1, w2, K, y);
+    fcm_oracle_epilogue(y, M, K, scale2, bias2, act2);
+    fcm_oracle_round_array(y, M * K, dtype);
+    if (!t_out) free(t);
+    return 0;
+}
+
+/* Same modules evaluated only at a list of output pixels (n, oh, ow), for checks at
+ * full size where the whole output is not needed: y_rows[i][k] for pixel i.  The
+ * intermediate at one pixel depends only on that pixel's input window, so each
+ * sampled row is computed from scratch by the definitions above. */
+int fcm_oracle_dwpw_at(const double* x, int N, int H, int W, int C, const double* w_dw,
+                       int R, int S, int sh, int sw, int ph, int pw, const double* scale1,
+                       const double* bias1, int act1, const double* w_pw, int K,
+                       const double* scale2, const double* bias2, int act2, int dtype,
+                       const int32_t* pix /* [P][3] */, int64_t P, double* y_rows) {
+    (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < P; ++i) {
+        int n = pix[3 * i], oh = pix[3 * i + 1], ow = pix[3 * i + 2];
+        double* t = (double*)malloc(sizeof(double) * (size_t)C);
+        if (!t) continue;
+        for (int c = 0; c < C; ++c) {
+            double acc = 0.0;
+            for (int r = 0; r < R; ++r)
+                for (int s = 0; s < S; ++s) {
+                    int ih = oh * sh - ph + r, iw = ow * sw - pw + s;
+                    if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;
+                    acc += x[(((int64_t)n * H + ih) * W + iw) * C + c] *
+                           w_dw[((int64_t)c * R + r) * S + s];
+                }
+            t[c] = acc;
+        }
+        epilogue_row(t, C, scale1, bias1, act1);
+        fcm_oracle_round_array(t, C, dtype);
+        double* yr = y_rows + i * K;
+        pw_row(t, C, w_pw, K, yr);
+        epilogue_row(yr, K, scale2, bias2, act2);
+        fcm_oracle_round_array(yr, K, dtype);
+        free(t);
+    }
+    return 0;
+}
+
+int fcm_oracle_b2b_at(const double* x, int N, int H, int W, int C, const double* w1,
+                      int K1, int R, int S, int sh, int sw, int ph, int pw,
+                      const double* scale1, const double* bias1, int act1, const double* w2,
+                      int K, const double* scale2, const double* bias2, int act2, int dtype,
+                      const int32_t* pix, int64_t P, double* y_rows) {
+    (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < P; ++i) {
+        int n = pix[3 * i], oh = pix[3 * i + 1], ow = pix[3 * i + 2];
+        double* t = (double*)malloc(sizeof(double) * (size_t)K1);
+        if (!t) continue;
+        for (int k1 = 0; k1 < K1; ++k1) {
+            double acc = 0.0;
+            for (int c = 0; c < C; ++c)
+                for (int r = 0; r < R; ++r)
+                    for (int s = 0; s < S; ++s) {
+                        int ih = oh * sh - ph + r, iw = ow * sw - pw + s;
+                        if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;
+                        acc += x[(((int64_t)n * H + ih) * W + iw) * C + c] *
+                               w1[(((int64_t)k1 * C + c) * R + r) * S + s];
+                    }
+            t[k1] = acc;
+        }
+        epilogue_row(t, K1, scale1, bias1, act1);
+        fcm_oracle_round_array(t, K1, dtype);
+        double* yr = y_rows + i * K;
+        pw_row(t, K1, w2, K, yr);
+        epilogue_row(yr, K, scale2, bias2, act2);
+        fcm_oracle_round_array(yr, K, dtype);
+        free(t);
+    }
+    return 0;
+}

@@ -1,0 +1,397 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+* library routines it must reduce to: torch.nn.functional.conv2d (groups=C for the
+  depthwise layer), batch_norm + relu/relu6 for the epilogue, numpy/torch casts for
+  IEEE round-to-nearest-even;
+* exact invariants of convolution (identity filters, one-hot taps, linearity,
+  stride-2 as a subsample of stride-1, channel permutation, batch independence, a
+  diagonal standard conv equal to a depthwise conv);
+* facts the pages print about shapes and memory accounting (tests/golden).
+
+A plausible mistake anywhere in the oracle (a dropped tap, a flipped filter, a wrong
+padding or stride, a transposed weight, an epilogue applied in the wrong order, a
+rounding in the wrong place or mode) fails at least one test here.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import accounting
+import fcm_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def _torch_dw(x, w, stride, pad):
+    xt = torch.from_numpy(x).permute(0, 3, 1, 2)
+    wt = torch.from_numpy(w)[:, None]
+    return F.conv2d(xt, wt, stride=stride, padding=pad, groups=x.shape[3]).permute(
+        0, 2, 3, 1).numpy()
+
+
+def _torch_conv(x, w, stride, pad):
+    xt = torch.from_numpy(x).permute(0, 3, 1, 2)
+    return F.conv2d(xt, torch.from_numpy(w), stride=stride, padding=pad).permute(
+        0, 2, 3, 1).numpy()
+
+
+# ---------------------------------------------------------------------------------
+# rounding
+# ---------------------------------------------------------------------------------
+def test_f16_all_patterns_and_midpoints():
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    fin = np.isfinite(vals)
+    r = oracle.round_to(vals[fin], "f16")
+    assert np.array_equal(r, vals[fin])
+    for b in bits[fin][::97]:
+        v = float(np.uint16(b).view(np.float16))
+        assert oracle.f16_bits(v) == int(b), hex(b)
+    # midpoints between consecutive positive finite values: ties go to even
+    pos = np.sort(np.unique(vals[fin & (vals >= 0)]))
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    expect = mids.astype(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.round_to(mids, "f16"), expect)
+    assert np.array_equal(oracle.round_to(-mids, "f16"), -expect)
+    # just above / below the largest finite value and the overflow threshold
+    edge = np.array([65504.0, 65519.0, 65519.999, 65520.0, 1e6, 2.0 ** -25,
+                     2.0 ** -25 * 1.0000001, 2.0 ** -24 * 1.5, 6.0e-8, -0.0])
+    with np.errstate(over="ignore"):
+        expect_edge = edge.astype(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.round_to(edge, "f16"), expect_edge)
+
+
+def test_f16_random_against_numpy():
+    rng = _rng(1)
+    v = rng.standard_normal(200000) * np.exp(rng.uniform(-20, 12, 200000))
+    with np.errstate(over="ignore"):
+        expect = v.astype(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.round_to(v, "f16"), expect)
+
+
+def test_bf16_all_patterns_and_midpoints():
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    vals = bits.view(torch.bfloat16).to(torch.float64).numpy()
+    fin = np.isfinite(vals)
+    assert np.array_equal(oracle.round_to(vals[fin], "bf16"), vals[fin])
+    raw = np.arange(65536)[fin]
+    for b in raw[::101]:
+        v = float(torch.tensor([b], dtype=torch.int32).to(torch.int16).view(
+            torch.bfloat16).to(torch.float64))
+        assert oracle.bf16_bits(v) == int(b), hex(int(b))
+    pos = np.sort(np.unique(vals[fin & (vals >= 0)]))
+    mids = (pos[:-1] + pos[1:]) / 2.0            # exactly representable in binary32
+    expect = torch.from_numpy(mids.astype(np.float32)).to(torch.bfloat16).to(
+        torch.float64).numpy()
+    assert np.array_equal(oracle.round_to(mids, "bf16"), expect)
+
+
+def test_bf16_random_against_torch():
+    rng = _rng(2)
+    v32 = (rng.standard_normal(200000) * np.exp(rng.uniform(-60, 60, 200000))).astype(
+        np.float32)
+    v = v32.astype(np.float64)
+    expect = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_to(v, "bf16"), expect)
+
+
+def test_f32_random_against_numpy():
+    rng = _rng(3)
+    v = rng.standard_normal(200000) * np.exp(rng.uniform(-80, 80, 200000))
+    assert np.array_equal(oracle.round_to(v, "f32"), v.astype(np.float32).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------------
+# layers against torch.nn.functional.conv2d in float64
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("N,H,W,C,stride,pad,R", [
+    (1, 1, 1, 1, 1, 1, 3), (2, 5, 7, 8, 1, 1, 3), (2, 9, 6, 16, 2, 1, 3),
+    (1, 8, 8, 24, 2, 0, 3), (3, 4, 9, 8, 1, 0, 3), (1, 6, 5, 4, 1, 0, 2),
+    (1, 7, 7, 16, 1, 2, 5)])
+def test_dw_matches_torch_grouped_conv(N, H, W, C, stride, pad, R):
+    rng = _rng(N * 100 + H)
+    x = rng.standard_normal((N, H, W, C))
+    w = rng.standard_normal((C, R, R))
+    t = oracle.dw(x, w, (stride, stride), (pad, pad))
+    ref = _torch_dw(x, w, stride, pad)
+    assert t.shape == ref.shape
+    assert np.max(np.abs(t - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("C,K", [(1, 1), (8, 32), (32, 8), (24, 40)])
+def test_pw_matches_torch_1x1(C, K):
+    rng = _rng(C + 7 * K)
+    t = rng.standard_normal((2, 5, 3, C))
+    w = rng.standard_normal((K, C))
+    y = oracle.pw(t, w)
+    ref = _torch_conv(t, w[:, :, None, None], 1, 0)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("N,H,W,C,K,stride,pad", [
+    (1, 5, 5, 8, 16, 1, 1), (2, 7, 4, 16, 8, 2, 1), (1, 6, 6, 3, 5, 1, 0)])
+def test_conv_matches_torch(N, H, W, C, K, stride, pad):
+    rng = _rng(K)
+    x = rng.standard_normal((N, H, W, C))
+    w = rng.standard_normal((K, C, 3, 3))
+    y = oracle.conv(x, w, (stride, stride), (pad, pad))
+    ref = _torch_conv(x, w, stride, pad)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "relu6"])
+def test_epilogue_is_folded_batchnorm_then_activation(act):
+    rng = _rng(5)
+    C = 12
+    a = rng.standard_normal((3, 4, 5, C)) * 4
+    gamma, beta = rng.uniform(0.5, 1.5, C), rng.standard_normal(C)
+    mean, var, eps = rng.standard_normal(C), rng.uniform(0.5, 2.0, C), 1e-5
+    scale = gamma / np.sqrt(var + eps)
+    bias = beta - mean * scale
+    out = oracle.epilogue(a, scale, bias, act)
+    at = torch.from_numpy(a).permute(0, 3, 1, 2)
+    bn = F.batch_norm(at, torch.from_numpy(mean), torch.from_numpy(var),
+                      torch.from_numpy(gamma), torch.from_numpy(beta), False, 0.0, eps)
+    bn = {"none": lambda v: v, "relu": F.relu, "relu6": F.relu6}[act](bn)
+    ref = bn.permute(0, 2, 3, 1).numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+    # null arrays are the identity
+    assert np.array_equal(oracle.epilogue(a, None, None, "none"), a)
+
+
+def _torch_round(a, dtype):
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float64)
+    if dtype == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_dwpw_module_is_layer_by_layer_pipeline(dtype):
+    rng = _rng(11)
+    N, H, W, C, K = 2, 6, 5, 8, 12
+    x = oracle.round_to(rng.standard_normal((N, H, W, C)), dtype)
+    wd = oracle.round_to(rng.standard_normal((C, 3, 3)) * 0.3, dtype)
+    wp = oracle.round_to(rng.standard_normal((K, C)) * 0.3, dtype)
+    s1, b1 = rng.uniform(0.5, 1.5, C), rng.standard_normal(C) * 0.1
+    s2, b2 = rng.uniform(0.5, 1.5, K), rng.standard_normal(K) * 0.1
+    y, t = oracle.dwpw(x, wd, wp, (1, 1), (1, 1), s1, b1, "relu6", s2, b2, "relu", dtype,
+                       return_t=True)
+    # reference pipeline from library routines; rounding by numpy/torch casts
+    tt = _torch_dw(x, wd, 1, 1) * s1 + b1
+    tt = np.clip(tt, 0, 6)
+    tr = _torch_round(tt, dtype)
+    yy = np.maximum(_torch_conv(tr, wp[:, :, None, None], 1, 0) * s2 + b2, 0)
+    yr = _torch_round(yy, dtype)
+    ulp = {"f32": 2.0 ** -23, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[dtype]
+    # torch's bfloat16 cast rounds via binary32, so allow a rare one-ulp difference
+    assert np.all(np.abs(t - tr) <= ulp * np.abs(tr) + 1e-30)
+    assert np.all(np.abs(y - yr) <= 2 * ulp * np.maximum(np.abs(yr), 1e-3) + 1e-30)
+    frac_exact = np.mean(y == yr)
+    assert frac_exact > 0.97
+
+
+def test_b2b_module_is_layer_by_layer_pipeline():
+    rng = _rng(12)
+    N, H, W, C, K1, K = 2, 5, 6, 8, 16, 8
+    x = oracle.round_to(rng.standard_normal((N, H, W, C)), "f16")
+    w1 = oracle.round_to(rng.standard_normal((K1, C, 3, 3)) * 0.1, "f16")
+    w2 = oracle.round_to(rng.standard_normal((K, K1)) * 0.2, "f16")
+    s1, b1 = rng.uniform(0.5, 1.5, K1), rng.standard_normal(K1) * 0.1
+    s2, b2 = rng.uniform(0.5, 1.5, K), rng.standard_normal(K) * 0.1
+    y, t = oracle.b2b(x, w1, w2, (1, 1), (1, 1), s1, b1, "relu", s2, b2, "relu", "f16",
+                      return_t=True)
+    tr = _torch_round(np.maximum(_torch_conv(x, w1, 1, 1) * s1 + b1, 0), "f16")
+    yr = _torch_round(np.maximum(_torch_conv(tr, w2[:, :, None, None], 1, 0) * s2 + b2, 0),
+                      "f16")
+    assert np.array_equal(t, tr)
+    assert np.array_equal(y, yr)
+
+
+# ---------------------------------------------------------------------------------
+# exact invariants
+# ---------------------------------------------------------------------------------
+def test_identity_depthwise_and_pointwise_are_noops():
+    rng = _rng(20)
+    for dtype in ("f32", "f16", "bf16"):
+        x = oracle.round_to(rng.standard_normal((2, 7, 5, 16)), dtype)
+        wd = np.zeros((16, 3, 3))
+        wd[:, 1, 1] = 1.0
+        wp = np.eye(16)
+        y, t = oracle.dwpw(x, wd, wp, dtype=dtype, return_t=True)
+        assert np.array_equal(t, x)
+        assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("r,s", [(0, 0), (0, 2), (2, 1), (1, 0), (2, 2)])
+def test_one_hot_tap_is_a_shift_with_zero_border(r, s):
+    rng = _rng(21)
+    x = rng.standard_normal((1, 6, 7, 4))
+    w = np.zeros((4, 3, 3))
+    w[:, r, s] = 1.0
+    t = oracle.dw(x, w)
+    xp = np.pad(x, ((0, 0), (1, 1), (1, 1), (0, 0)))
+    expect = xp[:, r:r + 6, s:s + 7, :]
+    assert np.array_equal(t, expect)
+
+
+def test_linearity():
+    rng = _rng(22)
+    x1, x2 = rng.standard_normal((2, 2, 5, 6, 8))
+    wd, wp = rng.standard_normal((8, 3, 3)), rng.standard_normal((5, 8))
+    a, b = 0.75, -1.25
+    y = oracle.pw(oracle.dw(a * x1 + b * x2, wd), wp)
+    y12 = a * oracle.pw(oracle.dw(x1, wd), wp) + b * oracle.pw(oracle.dw(x2, wd), wp)
+    assert np.max(np.abs(y - y12)) <= 1e-12 * np.max(np.abs(y))
+
+
+def test_stride2_is_stride1_subsampled():
+    rng = _rng(23)
+    x = rng.standard_normal((2, 9, 8, 8))
+    w = rng.standard_normal((8, 3, 3))
+    t1 = oracle.dw(x, w, (1, 1), (1, 1))
+    t2 = oracle.dw(x, w, (2, 2), (1, 1))
+    assert np.array_equal(t2, t1[:, ::2, ::2, :])
+
+
+def test_channel_permutation_and_batch_independence():
+    rng = _rng(24)
+    x = rng.standard_normal((3, 5, 5, 8))
+    w = rng.standard_normal((8, 3, 3))
+    perm = rng.permutation(8)
+    t = oracle.dw(x, w)
+    assert np.array_equal(oracle.dw(x[..., perm], w[perm]), t[..., perm])
+    assert np.array_equal(oracle.dw(x[1:2], w), t[1:2])
+
+
+def test_diagonal_standard_conv_equals_depthwise():
+    rng = _rng(25)
+    C = 8
+    x = oracle.round_to(rng.standard_normal((2, 6, 5, C)), "f16")
+    wd = oracle.round_to(rng.standard_normal((C, 3, 3)) * 0.4, "f16")
+    wp = oracle.round_to(rng.standard_normal((6, C)) * 0.4, "f16")
+    w1 = np.zeros((C, C, 3, 3))
+    for c in range(C):
+        w1[c, c] = wd[c]
+    kw = dict(scale1=rng.uniform(0.5, 1.5, C), bias1=rng.standard_normal(C) * 0.1,
+              act1="relu6", bias2=rng.standard_normal(6) * 0.1, act2="relu", dtype="f16")
+    assert np.array_equal(oracle.b2b(x, w1, wp, **kw), oracle.dwpw(x, wd, wp, **kw))
+
+
+def test_sampled_rows_equal_full_outputs():
+    wl = fcm_inputs.WORKLOADS["cfg2"].replace(N=2, H=9, W=20)
+    inp = fcm_inputs.make_inputs(wl)
+    kw = dict(stride=(1, 1), pad=(1, 1), scale1=inp["scale1"], bias1=inp["bias1"],
+              act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"], act2=wl.act2,
+              dtype=wl.dtype)
+    full = oracle.dwpw(inp["x"], inp["w1"], inp["w2"], **kw)
+    pix = fcm_inputs.sample_pixels(wl, 40)
+    rows = oracle.dwpw_at(inp["x"], inp["w1"], inp["w2"], pix, **kw)
+    assert np.array_equal(rows, full[pix[:, 0], pix[:, 1], pix[:, 2]])
+
+
+# ---------------------------------------------------------------------------------
+# the pages' own facts
+# ---------------------------------------------------------------------------------
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def test_page_dw_tile_shape():
+    g = _golden()["dw_tile_shape"]
+    x = np.ones((1,) + tuple(g["ifm_hw"]) + (1,))
+    w = np.ones((1,) + tuple(g["filter_rs"]))
+    t = oracle.dw(x, w, (g["stride"],) * 2, (g["pad"],) * 2)
+    assert list(t.shape[1:3]) == g["ofm_hw"]
+
+
+def test_page_b2b_and_cifar_extents():
+    g = _golden()
+    b = g["b2b_example"]
+    h = oracle.out_size(b["conv1"]["in_hwc"][0], 1, b["conv1"]["filter_rs"][0], 1)
+    assert h == b["conv1"]["out_hwc"][0]
+    assert oracle.out_size(b["conv2"]["in_hwc"][0], 0, 1, 1) == b["conv2"]["out_hwc"][0]
+    c = g["cifar_net_extents"]
+    assert oracle.out_size(c["input_hw"], c["dw_pad"], c["dw_kernel"], 1) == c["after_dw"]
+    p1 = oracle.out_size(c["after_dw"], 0, c["pool_kernel"], c["pool_stride"])
+    assert p1 == c["after_pool1"]
+    assert oracle.out_size(p1, 0, c["pool_kernel"], c["pool_stride"]) == c["after_pool2"]
+
+
+def test_page_fusion_saves_half_and_writes_half():
+    g = _golden()
+    # C = K, stride 1: the unfused pair moves X, T, T, Y; the fused module X, Y.
+    wl = fcm_inputs.Workload("t", "dwpw", "f16", N=64, H=112, W=112, C=32, K=32, K1=32)
+    s = accounting.sizes(wl)
+    no_w = (s["x"] + s["y"]) / (s["x"] + 2 * s["t"] + s["y"])
+    assert 1.0 - no_w == g["fusion_saves_half"]["saving"]
+    assert abs(accounting.fused_savings(wl) - g["fusion_saves_half"]["saving"]) < 1e-4
+    # writes: unfused writes T and Y, fused only Y
+    assert (s["t"] + s["y"]) / s["y"] == g["separable_writes_twice"][
+        "write_ratio_unfused_over_fused"]
+
+
+def test_accounting_of_the_five_workloads():
+    # closed forms: X + Y + weights + epilogue arrays; unfused adds 2|T|
+    for name, wl in fcm_inputs.WORKLOADS.items():
+        s = accounting.sizes(wl)
+        e = fcm_inputs.ELEM_BYTES[wl.dtype]
+        assert s["x"] == wl.N * wl.H * wl.W * wl.C * e
+        assert s["y"] == wl.N * wl.Ho * wl.Wo * wl.K * e
+        assert accounting.alg_bytes(wl, False) - accounting.alg_bytes(wl, True) == 2 * s["t"]
+    assert accounting.alg_bytes(fcm_inputs.WORKLOADS["cfg1"]) == 70912
+    assert accounting.alg_bytes(fcm_inputs.WORKLOADS["cfg2"]) == 38554240
+    assert fcm_inputs.WORKLOADS["cfg4a"].Ho == 28
+
+
+# ---------------------------------------------------------------------------------
+# FusePlanner equations
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("cw,ch,tw,th,f,s", [
+    (16, 16, 4, 16, 3, 1), (17, 9, 5, 9, 3, 1), (32, 8, 8, 8, 3, 2), (12, 12, 12, 3, 3, 1),
+    (20, 20, 7, 20, 5, 1), (9, 9, 2, 9, 3, 3)])
+def test_eq1_overlap_one_direction_equals_brute_force(cw, ch, tw, th, f, s):
+    # tiles that split only one direction: Eq. 1 counts exactly the repeated loads
+    assert accounting.eq1_overlap(cw, ch, tw, th, f, f, s) == \
+        accounting.brute_force_overlap(cw, ch, tw, th, f, s)
+
+
+@pytest.mark.parametrize("cw,ch,tw,th", [(16, 16, 4, 4), (17, 11, 5, 3), (8, 8, 3, 5)])
+def test_eq1_overlap_two_directions_misses_only_corners(cw, ch, tw, th):
+    # with both directions split, each border crossing's corner block is loaded by
+    # four tiles; Eq. 1 charges it twice, so the brute force exceeds it by one per
+    # corner element
+    f, s = 3, 1
+    corners = (-(-cw // tw) - 1) * (-(-ch // th) - 1) * (f - s) ** 2
+    assert accounting.brute_force_overlap(cw, ch, tw, th, f, s) == \
+        accounting.eq1_overlap(cw, ch, tw, th, f, f, s) + corners
+
+
+def test_eq2_eq3_reduce_to_compulsory_traffic_without_tiling():
+    # one weight tile, one output tile per SM, no spatial split: every tensor once
+    W, I, O = 1000, 5000, 7000
+    assert accounting.eq2_pw_gma(W, W, I, O, O, I, I + O + W, 1) == I + O + W
+    assert accounting.eq3_dw_gma(8, 0, I, O, 100, 100, W, I, O, W, 1, I + O + W, 1) == \
+        I + O + W
+    # the weight tile count multiplies IFM reads; the OFM tile count multiplies weights
+    assert accounting.eq2_pw_gma(W, W // 4, I, O, O // 2, 1, 10 ** 9, 1) == \
+        4 * I + O + 2 * W
+
+
+def test_equations_mark_infeasible_tilings_infinite():
+    assert accounting.eq2_pw_gma(10, 10, 10, 10, 10, 10, 29, 1) == float("inf")
+    assert accounting.eq2_pw_gma(10, 10, 10, 100, 10, 10, 1000, 11) == float("inf")
+    assert accounting.dwpw_gma(8, 0, 10, 1, 1, 1, 10, 10, 100, 4, 99, 1) == float("inf")
+    assert accounting.eq4_pwdw_gma(1, 0, 1, 1, 1, 1, 1, 1, 1, 1, 1, 5, 1, 4, 1) == \
+        float("inf")
