@@ -1,0 +1,254 @@
+"""Python binding of libfcm.so, the MI355X (gfx950) fused convolution module library.
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels.  The functions carry the C ABI's names (see ``include/fcm.h``):
+
+    plan = fcm_plan(problem(...))
+    fcm_pack_weights(plan, w1_src, w1_dst, w2_src, w2_dst)
+    fcm_dwpw_fwd(plan, x, w_dw, scale1, bias1, w_pw, scale2, bias2, y)
+    fcm_b2b_conv_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y)
+    fcm_dw_fwd / fcm_pw_fwd / fcm_conv_fwd   (layer-by-layer baselines)
+
+Tensor arguments are torch tensors on the GPU (or raw integer device addresses, or
+None where the ABI allows NULL); PyTorch only provides device memory and the stream
+(``torch.cuda.current_stream()`` unless one is passed).  A non-OK status raises
+:class:`FcmError`.  If ``libfcm.so`` has not been built the first call raises: there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfcm.so")
+
+FCM_OK, FCM_ERR_INVALID_ARG, FCM_ERR_UNSUPPORTED, FCM_ERR_HIP = 0, 1, 2, 3
+FCM_F32, FCM_F16, FCM_BF16 = 0, 1, 2
+FCM_ACT_NONE, FCM_ACT_RELU, FCM_ACT_RELU6 = 0, 1, 2
+FCM_KIND_DWPW, FCM_KIND_B2B = 0, 1
+FCM_PLAN_VERSION = 1
+
+DTYPE_CODES = {"f32": FCM_F32, "f16": FCM_F16, "bf16": FCM_BF16}
+ACT_CODES = {"none": FCM_ACT_NONE, "relu": FCM_ACT_RELU, "relu6": FCM_ACT_RELU6}
+KIND_CODES = {"dwpw": FCM_KIND_DWPW, "b2b": FCM_KIND_B2B}
+
+
+class FcmError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)}: {detail}")
+
+
+_STATUS = {0: "FCM_OK", 1: "FCM_ERR_INVALID_ARG", 2: "FCM_ERR_UNSUPPORTED", 3: "FCM_ERR_HIP"}
+
+_i32, _i64, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+
+
+class fcm_problem(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in ("kind", "dtype", "N", "H", "W", "C", "K1", "K", "R", "S",
+                                    "stride_h", "stride_w", "pad_h", "pad_w", "act1", "act2")]
+
+
+class fcm_device_spec(ctypes.Structure):
+    _fields_ = [("num_cus", _i32), ("num_xcds", _i32), ("simds_per_cu", _i32),
+                ("wave_size", _i32), ("max_waves_per_simd", _i32),
+                ("vgprs_per_simd_lane", _i32), ("lds_bytes_per_cu", _i32),
+                ("lds_bytes_per_wg", _i32), ("l2_bytes_per_xcd", _i64),
+                ("hbm_bytes_per_s", _f64), ("mfma_f16_flops", _f64),
+                ("mfma_f32_flops", _f64), ("valu_f32_flops", _f64)]
+
+
+class fcm_plan_t(ctypes.Structure):
+    _fields_ = [("version", _i32), ("prob", fcm_problem), ("Ho", _i32), ("Wo", _i32),
+                ("variant", _i32), ("tile_h", _i32), ("tile_w", _i32), ("k_tile", _i32),
+                ("c_chunk", _i32), ("waves_per_wg", _i32), ("wgs_per_cu", _i32),
+                ("num_tiles", _i32), ("grid", _i32), ("lds_bytes", _i32), ("fuse", _i32),
+                ("w1_packed_bytes", _i64), ("w2_packed_bytes", _i64),
+                ("workspace_bytes", _i64), ("alg_bytes_fused", _i64),
+                ("alg_bytes_unfused", _i64), ("pred_bytes_fused", _i64),
+                ("pred_bytes_unfused", _i64), ("gma_paper_fused", _f64),
+                ("gma_paper_unfused", _f64), ("flops", _f64), ("pred_us_fused", _f64)]
+
+    def as_dict(self) -> dict:
+        d = {}
+        for name, _ in self._fields_:
+            v = getattr(self, name)
+            if isinstance(v, fcm_problem):
+                v = {n: getattr(v, n) for n, _ in fcm_problem._fields_}
+            d[name] = v
+        return d
+
+
+# every symbol include/fcm.h declares
+EXPORTS = ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan", "fcm_plan_variant",
+           "fcm_num_variants", "fcm_variant_name", "fcm_pack_weights", "fcm_dwpw_fwd",
+           "fcm_b2b_conv_fwd", "fcm_dw_fwd", "fcm_pw_fwd", "fcm_conv_fwd", "fcm_status_str",
+           "fcm_last_error")
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfcm.so (built in-tree by ``build.py``); raise if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise FcmError(FCM_ERR_HIP, "load",
+                               f"{LIB_PATH} is not built; run "
+                               "`python -m depthwise_pointwise_convolution_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, fp = ctypes.c_void_p, ctypes.c_void_p
+            P = ctypes.POINTER
+            L.fcm_default_device_spec.argtypes = [P(fcm_device_spec)]
+            L.fcm_query_device_spec.argtypes = [ctypes.c_int, P(fcm_device_spec)]
+            L.fcm_plan.argtypes = [P(fcm_problem), P(fcm_device_spec), P(fcm_plan_t)]
+            L.fcm_plan_variant.argtypes = [P(fcm_problem), P(fcm_device_spec), _i32,
+                                           P(fcm_plan_t)]
+            L.fcm_num_variants.restype = _i32
+            L.fcm_num_variants.argtypes = []
+            L.fcm_variant_name.restype = ctypes.c_char_p
+            L.fcm_variant_name.argtypes = [_i32]
+            L.fcm_pack_weights.argtypes = [P(fcm_plan_t), vp, vp, vp, vp, vp]
+            L.fcm_dwpw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
+            L.fcm_b2b_conv_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
+            L.fcm_dw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
+            L.fcm_pw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
+            L.fcm_conv_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
+            L.fcm_status_str.restype = ctypes.c_char_p
+            L.fcm_status_str.argtypes = [ctypes.c_int]
+            L.fcm_last_error.restype = ctypes.c_char_p
+            L.fcm_last_error.argtypes = []
+            for name in ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan",
+                         "fcm_plan_variant", "fcm_pack_weights", "fcm_dwpw_fwd",
+                         "fcm_b2b_conv_fwd", "fcm_dw_fwd", "fcm_pw_fwd", "fcm_conv_fwd"):
+                getattr(L, name).restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != FCM_OK:
+        detail = lib().fcm_last_error().decode(errors="replace")
+        raise FcmError(status, where, detail)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor (or an int address); None stays NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------------------------
+# host-side calls
+# ------------------------------------------------------------------------------------
+def problem(kind="dwpw", dtype="f16", N=1, H=1, W=1, C=8, K=8, K1=None, R=3, S=3,
+            stride=1, pad=1, act1="none", act2="none") -> fcm_problem:
+    """Build an fcm_problem; K1 defaults to C (depthwise)."""
+    p = fcm_problem()
+    p.kind = KIND_CODES[kind] if isinstance(kind, str) else kind
+    p.dtype = DTYPE_CODES[dtype] if isinstance(dtype, str) else dtype
+    p.N, p.H, p.W, p.C, p.K = N, H, W, C, K
+    p.K1 = C if K1 is None else K1
+    p.R, p.S = R, S
+    sh, sw = (stride, stride) if isinstance(stride, int) else stride
+    ph, pw = (pad, pad) if isinstance(pad, int) else pad
+    p.stride_h, p.stride_w, p.pad_h, p.pad_w = sh, sw, ph, pw
+    p.act1 = ACT_CODES[act1] if isinstance(act1, str) else act1
+    p.act2 = ACT_CODES[act2] if isinstance(act2, str) else act2
+    return p
+
+
+def fcm_default_device_spec() -> fcm_device_spec:
+    s = fcm_device_spec()
+    _check(lib().fcm_default_device_spec(ctypes.byref(s)), "fcm_default_device_spec")
+    return s
+
+
+def fcm_query_device_spec(device: int = 0) -> fcm_device_spec:
+    s = fcm_device_spec()
+    _check(lib().fcm_query_device_spec(device, ctypes.byref(s)), "fcm_query_device_spec")
+    return s
+
+
+def fcm_plan(prob: fcm_problem, spec: Optional[fcm_device_spec] = None) -> fcm_plan_t:
+    out = fcm_plan_t()
+    _check(lib().fcm_plan(ctypes.byref(prob), ctypes.byref(spec) if spec else None,
+                          ctypes.byref(out)), "fcm_plan")
+    return out
+
+
+def fcm_plan_variant(prob: fcm_problem, variant: int,
+                     spec: Optional[fcm_device_spec] = None) -> fcm_plan_t:
+    out = fcm_plan_t()
+    _check(lib().fcm_plan_variant(ctypes.byref(prob), ctypes.byref(spec) if spec else None,
+                                  variant, ctypes.byref(out)), "fcm_plan_variant")
+    return out
+
+
+def fcm_num_variants() -> int:
+    return int(lib().fcm_num_variants())
+
+
+def fcm_variant_name(variant: int) -> str:
+    return lib().fcm_variant_name(variant).decode()
+
+
+def fcm_status_str(status: int) -> str:
+    return lib().fcm_status_str(status).decode()
+
+
+def fcm_last_error() -> str:
+    return lib().fcm_last_error().decode(errors="replace")
+
+
+# ------------------------------------------------------------------------------------
+# device calls (asynchronous on the stream)
+# ------------------------------------------------------------------------------------
+def fcm_pack_weights(plan, w1_src, w1_dst, w2_src=None, w2_dst=None, stream=None):
+    _check(lib().fcm_pack_weights(ctypes.byref(plan), _ptr(w1_src), _ptr(w1_dst),
+                                  _ptr(w2_src), _ptr(w2_dst), _stream(stream)),
+           "fcm_pack_weights")
+
+
+def fcm_dwpw_fwd(plan, x, w_dw, scale1, bias1, w_pw, scale2, bias2, y, stream=None):
+    _check(lib().fcm_dwpw_fwd(ctypes.byref(plan), _ptr(x), _ptr(w_dw), _ptr(scale1),
+                              _ptr(bias1), _ptr(w_pw), _ptr(scale2), _ptr(bias2), _ptr(y),
+                              _stream(stream)), "fcm_dwpw_fwd")
+
+
+def fcm_b2b_conv_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y, stream=None):
+    _check(lib().fcm_b2b_conv_fwd(ctypes.byref(plan), _ptr(x), _ptr(w1), _ptr(scale1),
+                                  _ptr(bias1), _ptr(w2), _ptr(scale2), _ptr(bias2), _ptr(y),
+                                  _stream(stream)), "fcm_b2b_conv_fwd")
+
+
+def fcm_dw_fwd(plan, x, w_dw, scale1, bias1, t, stream=None):
+    _check(lib().fcm_dw_fwd(ctypes.byref(plan), _ptr(x), _ptr(w_dw), _ptr(scale1),
+                            _ptr(bias1), _ptr(t), _stream(stream)), "fcm_dw_fwd")
+
+
+def fcm_pw_fwd(plan, t, w_pw, scale2, bias2, y, stream=None):
+    _check(lib().fcm_pw_fwd(ctypes.byref(plan), _ptr(t), _ptr(w_pw), _ptr(scale2),
+                            _ptr(bias2), _ptr(y), _stream(stream)), "fcm_pw_fwd")
+
+
+def fcm_conv_fwd(plan, x, w1, scale1, bias1, t, stream=None):
+    _check(lib().fcm_conv_fwd(ctypes.byref(plan), _ptr(x), _ptr(w1), _ptr(scale1),
+                              _ptr(bias1), _ptr(t), _stream(stream)), "fcm_conv_fwd")

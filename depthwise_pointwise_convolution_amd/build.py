@@ -1,0 +1,88 @@
+"""Build libfcm.so (the C ABI + gfx950 kernels) in-tree with hipcc.
+
+    python -m depthwise_pointwise_convolution_amd.build [--jobs N]
+
+Each translation unit is compiled to an object under ``_build/`` in parallel and
+the objects are linked into ``depthwise_pointwise_convolution_amd/libfcm.so``.
+Device code is built for gfx950 only, with packed fp32 arithmetic disabled.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfcm.so")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+
+SOURCES = [
+    ("kernels/dwpw.hip", True),
+    ("kernels/lbl.hip", True),
+    ("kernels/b2b.hip", True),
+    ("api.cpp", True),
+    ("plan.cpp", False),
+]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
+
+
+def _flags(device: bool) -> list:
+    f = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+         "-I" + INCLUDE, "-I" + CSRC]
+    if device:
+        f = ["-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature",
+             "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"] + f
+    return f
+
+
+def _compile(src: str, device: bool, verbose: bool) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
+    cmd = [_hipcc()] + _flags(device) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{out}")
+    if out.strip() and verbose:
+        print(out)
+    return obj
+
+
+def build(jobs: int = 0, verbose: bool = False) -> str:
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s[0], s[1], verbose), SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("linking libfcm.so failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=0)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    print(build(args.jobs, args.verbose))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,420 @@
+// api.cpp -- the C ABI of libfcm.so: argument validation, plan checks, dispatch to the
+// kernel variants and the layer-by-layer baselines.  Every check happens on the host
+// before anything is enqueued; errors come back as status codes with a per-thread
+// message (fcm_last_error).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/fcm.h"
+#include "kargs.h"
+#include "launchers.h"
+#include "lbl_tiles.h"
+#include "plan.h"
+
+namespace fcm {
+namespace {
+
+thread_local std::string g_last_error;
+
+fcm_status fail(fcm_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+fcm_status ok() {
+    g_last_error.clear();
+    return FCM_OK;
+}
+
+struct VariantImpl {
+    launch_fn launch;
+    occupancy_fn occupancy;
+};
+
+const VariantImpl kImpls[] = {
+#define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES) \
+    {launch_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES>, occ_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES>},
+#define FCM_V_DWPW32(name, S, TH, TW, KT, CC) \
+    {launch_dwpw_f32<S, TH, TW, KT, CC>, occ_dwpw_f32<S, TH, TW, KT, CC>},
+#define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
+    {launch_b2b_mfma<CT, S, TH, TW, K1, KT, CC>, occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>},
+#include "variants.def"
+#undef FCM_V_DWPW
+#undef FCM_V_DWPW32
+#undef FCM_V_B2B
+};
+static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
+
+// (device, variant) -> (CUs, workgroups per CU), filled on first use.
+std::mutex g_occ_mu;
+std::map<std::pair<int, int>, std::pair<int, int>> g_occ;
+
+fcm_status device_capacity(int variant, int* cus, int* per_cu) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(FCM_ERR_HIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_occ_mu);
+    auto it = g_occ.find({dev, variant});
+    if (it == g_occ.end()) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return fail(FCM_ERR_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed");
+        const int occ = kImpls[variant].occupancy();
+        if (occ <= 0) return fail(FCM_ERR_HIP, "occupancy query failed for the kernel variant");
+        it = g_occ.emplace(std::make_pair(dev, variant), std::make_pair(n, occ)).first;
+    }
+    *cus = it->second.first;
+    *per_cu = it->second.second;
+    return FCM_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Re-derive what a plan must contain from its problem and compare: a plan that was
+// edited, truncated or made for another problem is rejected.
+fcm_status check_plan(const fcm_plan_t* plan, int kind) {
+    if (!plan) return fail(FCM_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->version != FCM_PLAN_VERSION)
+        return fail(FCM_ERR_INVALID_ARG, "plan version mismatch");
+    std::string err;
+    fcm_status st = validate_problem(&plan->prob, &err);
+    if (st != FCM_OK) return fail(st, "plan holds an invalid problem: " + err);
+    if (plan->prob.kind != kind)
+        return fail(FCM_ERR_INVALID_ARG, "plan is for the other module kind");
+    if (plan->Ho != conv_out(plan->prob.H, plan->prob.pad_h, plan->prob.R, plan->prob.stride_h) ||
+        plan->Wo != conv_out(plan->prob.W, plan->prob.pad_w, plan->prob.S, plan->prob.stride_w))
+        return fail(FCM_ERR_INVALID_ARG, "plan output extent does not match its problem");
+    return FCM_OK;
+}
+
+fcm_status check_variant(const fcm_plan_t* plan) {
+    if (plan->variant < 0 || plan->variant >= kNumVariants)
+        return fail(FCM_ERR_INVALID_ARG, "plan names no compiled variant");
+    const VariantDesc& v = kVariants[plan->variant];
+    std::string why;
+    if (!variant_runs(v, plan->prob, &why)) return fail(FCM_ERR_INVALID_ARG, "plan variant: " + why);
+    if (plan->tile_h != v.th || plan->tile_w != v.tw || plan->k_tile != v.kt ||
+        plan->c_chunk != v.cc)
+        return fail(FCM_ERR_INVALID_ARG, "plan tiling does not match its variant");
+    if (plan->grid <= 0) return fail(FCM_ERR_INVALID_ARG, "plan grid must be positive");
+    return FCM_OK;
+}
+
+fcm_status need(const void* p, const char* what, uintptr_t align) {
+    if (!p) return fail(FCM_ERR_INVALID_ARG, std::string(what) + " is NULL");
+    if (!aligned(p, align))
+        return fail(FCM_ERR_INVALID_ARG,
+                    std::string(what) + " is not " + std::to_string(align) + "-byte aligned");
+    return FCM_OK;
+}
+fcm_status optional(const void* p, const char* what) {
+    if (p && !aligned(p, 4))
+        return fail(FCM_ERR_INVALID_ARG, std::string(what) + " is not 4-byte aligned");
+    return FCM_OK;
+}
+
+#define FCM_TRY(expr)                      \
+    do {                                   \
+        fcm_status _s = (expr);            \
+        if (_s != FCM_OK) return _s;       \
+    } while (0)
+
+KArgs base_args(const fcm_plan_t* plan) {
+    KArgs a;
+    memset(&a, 0, sizeof(a));
+    const fcm_problem& p = plan->prob;
+    a.N = p.N;
+    a.H = p.H;
+    a.W = p.W;
+    a.C = p.C;
+    a.K1 = p.K1;
+    a.K = p.K;
+    a.Ho = plan->Ho;
+    a.Wo = plan->Wo;
+    a.pad_h = p.pad_h;
+    a.pad_w = p.pad_w;
+    a.act1 = p.act1;
+    a.act2 = p.act2;
+    return a;
+}
+
+void set_tiles(KArgs* a, int th, int tw, int kt, int kdim) {
+    a->tiles_h = (a->Ho + th - 1) / th;
+    a->tiles_w = (a->Wo + tw - 1) / tw;
+    a->num_ptiles = a->N * a->tiles_h * a->tiles_w;
+    a->num_ktiles = (kdim + kt - 1) / kt;
+}
+
+fcm_status launch_fused(const fcm_plan_t* plan, KArgs& a, void* stream) {
+    const VariantDesc& v = kVariants[plan->variant];
+    set_tiles(&a, v.th, v.tw, v.kt, plan->prob.K);
+    int cus = 0, per_cu = 0;
+    FCM_TRY(device_capacity(plan->variant, &cus, &per_cu));
+    // persistent grid: never more workgroups than tiles or than the GPU holds at once,
+    // a multiple of the output-channel tile count (each workgroup keeps one slice)
+    int64_t grid = plan->grid;
+    const int64_t work = (int64_t)a.num_ptiles * a.num_ktiles;
+    grid = std::min<int64_t>(grid, work);
+    grid = std::min<int64_t>(grid, (int64_t)cus * per_cu);
+    grid = std::max<int64_t>(grid / a.num_ktiles, 1) * a.num_ktiles;
+    const int64_t unit = (int64_t)a.num_ktiles * 8;
+    if (grid >= unit) grid = grid / unit * unit;
+    const int rc = kImpls[plan->variant].launch(a, (int)grid, stream);
+    if (rc != 0)
+        return fail(FCM_ERR_HIP, std::string("kernel launch failed: ") +
+                                     hipGetErrorString((hipError_t)rc));
+    return ok();
+}
+
+}  // namespace
+}  // namespace fcm
+
+using namespace fcm;
+
+extern "C" {
+
+const char* fcm_status_str(fcm_status s) {
+    switch (s) {
+    case FCM_OK: return "FCM_OK";
+    case FCM_ERR_INVALID_ARG: return "FCM_ERR_INVALID_ARG";
+    case FCM_ERR_UNSUPPORTED: return "FCM_ERR_UNSUPPORTED";
+    case FCM_ERR_HIP: return "FCM_ERR_HIP";
+    }
+    return "FCM_ERR_UNKNOWN";
+}
+
+const char* fcm_last_error(void) { return g_last_error.c_str(); }
+
+fcm_status fcm_default_device_spec(fcm_device_spec* out) {
+    if (!out) return fail(FCM_ERR_INVALID_ARG, "spec output pointer is NULL");
+    memset(out, 0, sizeof(*out));
+    out->num_cus = 256;
+    out->num_xcds = 8;
+    out->simds_per_cu = 4;
+    out->wave_size = 64;
+    out->max_waves_per_simd = 8;
+    out->vgprs_per_simd_lane = 512;
+    out->lds_bytes_per_cu = 160 * 1024;
+    out->lds_bytes_per_wg = 160 * 1024;
+    out->l2_bytes_per_xcd = 4LL * 1024 * 1024;
+    out->hbm_bytes_per_s = 8.0e12;
+    out->mfma_f16_flops = 2.5e15;
+    out->mfma_f32_flops = 157.3e12;
+    // 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz, no packed fp32 math
+    out->valu_f32_flops = 256.0 * 4 * 16 * 2 * 2.4e9;
+    return ok();
+}
+
+fcm_status fcm_query_device_spec(int device, fcm_device_spec* out) {
+    FCM_TRY(fcm_default_device_spec(out));
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return fail(FCM_ERR_HIP, "cannot query the device's compute-unit count");
+    out->num_cus = n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device) ==
+            hipSuccess &&
+        n > 0)
+        out->lds_bytes_per_cu = n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, device) ==
+            hipSuccess &&
+        n > 0)
+        out->lds_bytes_per_wg = n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeL2CacheSize, device) == hipSuccess && n > 0)
+        out->l2_bytes_per_xcd = n;
+    return ok();
+}
+
+fcm_status fcm_plan(const fcm_problem* prob, const fcm_device_spec* spec, fcm_plan_t* out) {
+    std::string err;
+    fcm_status s = plan_problem(prob, spec, -1, out, &err);
+    return s == FCM_OK ? ok() : fail(s, err);
+}
+
+fcm_status fcm_plan_variant(const fcm_problem* prob, const fcm_device_spec* spec,
+                            int32_t variant, fcm_plan_t* out) {
+    if (variant < 0 || variant >= kNumVariants)
+        return fail(FCM_ERR_INVALID_ARG, "variant index out of range");
+    std::string err;
+    fcm_status s = plan_problem(prob, spec, variant, out, &err);
+    return s == FCM_OK ? ok() : fail(s, err);
+}
+
+int32_t fcm_num_variants(void) { return kNumVariants; }
+
+const char* fcm_variant_name(int32_t variant) {
+    if (variant < 0 || variant >= kNumVariants) return "";
+    return kVariants[variant].name;
+}
+
+fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1_dst,
+                            const void* w2_src, void* w2_dst, void* stream) {
+    if (!plan) return fail(FCM_ERR_INVALID_ARG, "plan is NULL");
+    FCM_TRY(check_plan(plan, plan->prob.kind));
+    const fcm_problem& p = plan->prob;
+    const int e = p.dtype == FCM_F32 ? 4 : 2;
+    if ((w1_src == nullptr) != (w1_dst == nullptr))
+        return fail(FCM_ERR_INVALID_ARG, "w1_src and w1_dst must both be given or both NULL");
+    if ((w2_src == nullptr) != (w2_dst == nullptr))
+        return fail(FCM_ERR_INVALID_ARG, "w2_src and w2_dst must both be given or both NULL");
+    if (w1_src) {
+        if (!aligned(w1_src, e) || !aligned(w1_dst, 16))
+            return fail(FCM_ERR_INVALID_ARG, "w1 source must be element-aligned, w1 destination "
+                                             "16-byte aligned");
+        const char* s = (const char*)w1_src;
+        const char* d = (const char*)w1_dst;
+        const int64_t nb = plan->w1_packed_bytes;
+        if (s < d + nb && d < s + nb) return fail(FCM_ERR_INVALID_ARG, "w1 buffers overlap");
+    }
+    if (w2_src) {
+        if (!aligned(w2_src, e) || !aligned(w2_dst, 16))
+            return fail(FCM_ERR_INVALID_ARG, "w2 source must be element-aligned, w2 destination "
+                                             "16-byte aligned");
+        const char* s = (const char*)w2_src;
+        const char* d = (const char*)w2_dst;
+        const int64_t nb = plan->w2_packed_bytes;
+        if (s < d + nb && d < s + nb) return fail(FCM_ERR_INVALID_ARG, "w2 buffers overlap");
+    }
+    if (w1_src) {
+        int rc;
+        if (p.kind == FCM_KIND_DWPW)
+            rc = launch_pack_dw(e, w1_src, w1_dst, p.C, p.R * p.S, stream);
+        else
+            rc = launch_pack_conv(e, w1_src, w1_dst, p.K1, p.C, p.R * p.S, stream);
+        if (rc != 0)
+            return fail(FCM_ERR_HIP, std::string("weight packing failed: ") +
+                                         hipGetErrorString((hipError_t)rc));
+    }
+    if (w2_src) {
+        const int rc = launch_copy(w2_src, w2_dst, plan->w2_packed_bytes, stream);
+        if (rc != 0)
+            return fail(FCM_ERR_HIP, std::string("weight copy failed: ") +
+                                         hipGetErrorString((hipError_t)rc));
+    }
+    return ok();
+}
+
+fcm_status fcm_dwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
+                        const float* scale1, const float* bias1, const void* w_pw,
+                        const float* scale2, const float* bias2, void* y, void* stream) {
+    FCM_TRY(check_plan(plan, FCM_KIND_DWPW));
+    FCM_TRY(check_variant(plan));
+    FCM_TRY(need(x, "x", 16));
+    FCM_TRY(need(w_dw, "w_dw", 16));
+    FCM_TRY(need(w_pw, "w_pw", 16));
+    FCM_TRY(need(y, "y", 16));
+    FCM_TRY(optional(scale1, "scale1"));
+    FCM_TRY(optional(bias1, "bias1"));
+    FCM_TRY(optional(scale2, "scale2"));
+    FCM_TRY(optional(bias2, "bias2"));
+    KArgs a = base_args(plan);
+    a.x = x;
+    a.w1 = w_dw;
+    a.s1 = scale1;
+    a.b1 = bias1;
+    a.w2 = w_pw;
+    a.s2 = scale2;
+    a.b2 = bias2;
+    a.y = y;
+    return launch_fused(plan, a, stream);
+}
+
+fcm_status fcm_b2b_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
+                            const float* scale1, const float* bias1, const void* w2,
+                            const float* scale2, const float* bias2, void* y, void* stream) {
+    FCM_TRY(check_plan(plan, FCM_KIND_B2B));
+    FCM_TRY(check_variant(plan));
+    FCM_TRY(need(x, "x", 16));
+    FCM_TRY(need(w1, "w1", 16));
+    FCM_TRY(need(w2, "w2", 16));
+    FCM_TRY(need(y, "y", 16));
+    FCM_TRY(optional(scale1, "scale1"));
+    FCM_TRY(optional(bias1, "bias1"));
+    FCM_TRY(optional(scale2, "scale2"));
+    FCM_TRY(optional(bias2, "bias2"));
+    KArgs a = base_args(plan);
+    a.x = x;
+    a.w1 = w1;
+    a.s1 = scale1;
+    a.b1 = bias1;
+    a.w2 = w2;
+    a.s2 = scale2;
+    a.b2 = bias2;
+    a.y = y;
+    return launch_fused(plan, a, stream);
+}
+
+fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
+                      const float* scale1, const float* bias1, void* t, void* stream) {
+    FCM_TRY(check_plan(plan, FCM_KIND_DWPW));
+    FCM_TRY(need(x, "x", 16));
+    FCM_TRY(need(w_dw, "w_dw", 16));
+    FCM_TRY(need(t, "t", 16));
+    FCM_TRY(optional(scale1, "scale1"));
+    FCM_TRY(optional(bias1, "bias1"));
+    KArgs a = base_args(plan);
+    a.x = x;
+    a.w1 = w_dw;
+    a.s1 = scale1;
+    a.b1 = bias1;
+    a.y = t;
+    set_tiles(&a, lbl::DW_TH, lbl::DW_TW, 1, 1);
+    const int rc = launch_dw_lbl(plan->prob.dtype, plan->prob.stride_h, a, stream);
+    if (rc != 0)
+        return fail(FCM_ERR_HIP,
+                    std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)rc));
+    return ok();
+}
+
+fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
+                      const float* scale2, const float* bias2, void* y, void* stream) {
+    if (!plan) return fail(FCM_ERR_INVALID_ARG, "plan is NULL");
+    FCM_TRY(check_plan(plan, plan->prob.kind));
+    FCM_TRY(need(t, "t", 16));
+    FCM_TRY(need(w_pw, "w_pw", 16));
+    FCM_TRY(need(y, "y", 16));
+    FCM_TRY(optional(scale2, "scale2"));
+    FCM_TRY(optional(bias2, "bias2"));
+    KArgs a = base_args(plan);
+    // the 1x1 layer reads the intermediate as its input: [N*Ho*Wo][C or K1]
+    if (plan->prob.kind == FCM_KIND_B2B) a.C = plan->prob.K1;
+    a.x = t;
+    a.w2 = w_pw;
+    a.s2 = scale2;
+    a.b2 = bias2;
+    a.y = y;
+    const int kt = plan->prob.dtype == FCM_F32 ? lbl::PW_KT32 : lbl::PW_KT16;
+    a.num_ktiles = (plan->prob.K + kt - 1) / kt;
+    const int rc = launch_pw_lbl(plan->prob.dtype, a, stream);
+    if (rc != 0)
+        return fail(FCM_ERR_HIP,
+                    std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)rc));
+    return ok();
+}
+
+fcm_status fcm_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
+                        const float* scale1, const float* bias1, void* t, void* stream) {
+    FCM_TRY(check_plan(plan, FCM_KIND_B2B));
+    FCM_TRY(need(x, "x", 16));
+    FCM_TRY(need(w1, "w1", 16));
+    FCM_TRY(need(t, "t", 16));
+    FCM_TRY(optional(scale1, "scale1"));
+    FCM_TRY(optional(bias1, "bias1"));
+    KArgs a = base_args(plan);
+    a.x = x;
+    a.w1 = w1;
+    a.s1 = scale1;
+    a.b1 = bias1;
+    a.y = t;
+    set_tiles(&a, lbl::CV_TH, lbl::CV_TW, lbl::CV_KT, plan->prob.K1);
+    const int rc = launch_conv_lbl(plan->prob.dtype, plan->prob.stride_h, a, stream);
+    if (rc != 0)
+        return fail(FCM_ERR_HIP,
+                    std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)rc));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// launchers.h -- declarations of the templated kernel launchers.  Their definitions
+// and explicit instances live in the kernels/*.hip translation units; this header
+// lets the API layer refer to them without seeing any device code.
+#pragma once
+
+#include "kargs.h"
+
+namespace fcm {
+
+template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES>
+int launch_dwpw_mfma(const KArgs& a, int grid, void* stream);
+template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES>
+int occ_dwpw_mfma();
+
+template <int S, int TH, int TW, int KT, int CC>
+int launch_dwpw_f32(const KArgs& a, int grid, void* stream);
+template <int S, int TH, int TW, int KT, int CC>
+int occ_dwpw_f32();
+
+template <typename T, int S, int TH, int TW, int K1, int KT, int CC>
+int launch_b2b_mfma(const KArgs& a, int grid, void* stream);
+template <typename T, int S, int TH, int TW, int K1, int KT, int CC>
+int occ_b2b_mfma();
+
+// Layer-by-layer baselines (fixed tilings; see lbl.hip / b2b.hip).
+int launch_dw_lbl(int dtype, int stride, const KArgs& a, void* stream);
+int launch_pw_lbl(int dtype, const KArgs& a, void* stream);
+int launch_conv_lbl(int dtype, int stride, const KArgs& a, void* stream);
+// (tilings in lbl_tiles.h; the caller fills KArgs tiles_* / num_ptiles / num_ktiles
+// accordingly)
+
+// Weight packing (see pack.hip).
+int launch_pack_dw(int elem_bytes, const void* src, void* dst, int C, int RS, void* stream);
+int launch_pack_conv(int elem_bytes, const void* src, void* dst, int K1, int C, int RS,
+                     void* stream);
+int launch_copy(const void* src, void* dst, long long bytes, void* stream);
+
+}  // namespace fcm

@@ -1,0 +1,476 @@
+// plan.cpp -- FusePlanner for gfx950 ("Fusing Depthwise and Pointwise Convolutions for
+// Efficient Inference on GPUs", Sec. IV), host only.
+//
+// Inputs are the problem and the device's compute-unit count and on-chip memory
+// sizes.  The candidates are the fused kernel variants compiled into the library
+// (variants.def); for each one that can run the problem the planner
+//   - checks the two constraints of Eq. 2-4: the workgroup's tiles fit the on-chip
+//     memory (here: LDS per workgroup; registers are budgeted separately) and the
+//     module has at least as many output tiles as there are compute units;
+//   - computes the bytes the variant requests from the memory hierarchy with its
+//     real tile geometry (exact halo footprint clipped at the image border, input
+//     re-read once per output-channel tile, weights once per tile or once per
+//     workgroup when they stay in registers, output once);
+//   - computes the pages' own Eq. 1-3 estimate for the same tiling;
+// and keeps the feasible variant with the shortest roofline time (the slowest of
+// HBM, on-chip traffic, matrix and vector work, each counting recomputation; within
+// 1%: fewer bytes, less redundant arithmetic, more occupancy).  A
+// variant that breaks a constraint costs +infinity and is never preferred to a
+// finite one.  It then compares against the layer-by-layer kernels with the same
+// models and sets `fuse` when the fused module needs fewer global memory accesses
+// (Sec. IV-B, last paragraph).
+#include "plan.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "lbl_tiles.h"
+
+namespace fcm {
+
+const VariantDesc kVariants[] = {
+#define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES) \
+    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0},
+#define FCM_V_DWPW32(name, S, TH, TW, KT, CC) {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0},
+#define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
+    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, K1},
+#include "variants.def"
+#undef FCM_V_DWPW
+#undef FCM_V_DWPW32
+#undef FCM_V_B2B
+};
+const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+
+namespace {
+
+int elem_bytes(int dtype) { return dtype == FCM_F32 ? 4 : 2; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Rows (or columns) of the input that the halo window of output tile `t` (extent
+// `tile` outputs, stride s, 3 taps, padding pad) covers inside [0, in).
+int64_t window_inside(int t, int tile, int s, int pad, int in) {
+    const int64_t lo = (int64_t)t * tile * s - pad;
+    const int64_t hi = lo + (int64_t)(tile - 1) * s + 3;  // exclusive
+    const int64_t a = std::max<int64_t>(lo, 0), b = std::min<int64_t>(hi, in);
+    return b > a ? b - a : 0;
+}
+
+// Sum over all output tiles of an image of the input pixels their halo windows
+// load (clipped to the image): the exact per-image footprint of a tiled
+// 3x3 stencil, overlaps counted once per tile that loads them.
+int64_t halo_pixels(int Ho, int Wo, int H, int W, int th, int tw, int s, int ph, int pw) {
+    int64_t rows = 0, cols = 0;
+    for (int t = 0; t < cdiv(Ho, th); ++t) rows += window_inside(t, th, s, ph, H);
+    for (int t = 0; t < cdiv(Wo, tw); ++t) cols += window_inside(t, tw, s, pw, W);
+    return rows * cols;
+}
+
+// FCM paper Eq. 1 over the input plane, with the tile extents in input pixels.
+double eq1_overlap(int chw, int chh, int tilew, int tileh, int filt, int stride) {
+    const int o = std::max(filt - stride, 0);
+    return (double)(cdiv(chw, tilew) - 1) * o * chh + (double)(cdiv(chh, tileh) - 1) * o * chw;
+}
+
+}  // namespace
+
+int variant_lds_bytes(const VariantDesc& v) {
+    const int e = elem_bytes(v.dtype);
+    const int IH = (v.th - 1) * v.stride + 3, IW = (v.tw - 1) * v.stride + 3;
+    const int P = v.th * v.tw;
+    switch (v.vkind) {
+    case VK_DWPW:
+        return IH * IW * (v.cc + 8) * e + P * (v.cc + 8) * e + 9 * v.cc * 4 + 2 * v.cc * 4 +
+               2 * v.kt * 4;
+    case VK_DWPW32:
+        return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 1) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4;
+    default:
+        return IH * IW * (v.cc + 8) * e + 2 * v.k1 * 4 + 2 * v.kt * 4;
+    }
+}
+
+int variant_vgpr_estimate(const VariantDesc& v) {
+    const int P = v.th * v.tw;
+    const int MBW = P / 64;
+    switch (v.vkind) {
+    case VK_DWPW: {
+        const int KB = v.kt / 16, KS = v.cc / 32;
+        const int cg = v.cc / 8;
+        int vb = (v.th * v.tw * cg) / 256;
+        if (vb < 1) vb = 1;
+        return 40 + MBW * KB * 4 + (v.wres ? KS * KB * 4 : 12) + vb * 8 + 24;
+    }
+    case VK_DWPW32:
+        return 64 + P * v.kt / 256 + 24;
+    default: {
+        const int KB1 = v.k1 / 16, KB2 = v.kt / 16, KS2 = v.k1 / 32;
+        return 40 + MBW * KB1 * 4 + KS2 * KB2 * 4 + KB2 * 4 + MBW * 4 + 24;
+    }
+    }
+}
+
+fcm_status validate_problem(const fcm_problem* p, std::string* err) {
+    if (!p) {
+        *err = "problem pointer is NULL";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->kind != FCM_KIND_DWPW && p->kind != FCM_KIND_B2B) {
+        *err = "unknown kind";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->dtype < FCM_F32 || p->dtype > FCM_BF16) {
+        *err = "unknown dtype";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->act1 < FCM_ACT_NONE || p->act1 > FCM_ACT_RELU6 || p->act2 < FCM_ACT_NONE ||
+        p->act2 > FCM_ACT_RELU6) {
+        *err = "unknown activation";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->N <= 0 || p->H <= 0 || p->W <= 0 || p->C <= 0 || p->K <= 0 || p->K1 <= 0 ||
+        p->R <= 0 || p->S <= 0 || p->stride_h <= 0 || p->stride_w <= 0 || p->pad_h < 0 ||
+        p->pad_w < 0) {
+        *err = "sizes, filter extent and strides must be positive, padding non-negative";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->kind == FCM_KIND_DWPW && p->K1 != p->C) {
+        *err = "a depthwise layer keeps the channel count: K1 must equal C";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->pad_h >= p->R || p->pad_w >= p->S) {
+        *err = "padding must be smaller than the filter";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->H + 2 * p->pad_h < p->R || p->W + 2 * p->pad_w < p->S) {
+        *err = "padded input is smaller than the filter";
+        return FCM_ERR_INVALID_ARG;
+    }
+    const int64_t big = (int64_t)1 << 31;
+    if ((int64_t)p->N * p->H * p->W * p->C >= big || (int64_t)p->N * p->H * p->W * p->K >= big ||
+        (int64_t)p->N * p->H * p->W * p->K1 >= big) {
+        *err = "tensor element counts must stay below 2^31";
+        return FCM_ERR_UNSUPPORTED;
+    }
+    if (p->R != 3 || p->S != 3) {
+        *err = "only 3x3 first-layer filters have kernels";
+        return FCM_ERR_UNSUPPORTED;
+    }
+    if (p->stride_h != p->stride_w || (p->stride_h != 1 && p->stride_h != 2)) {
+        *err = "stride must be 1 or 2 in both directions";
+        return FCM_ERR_UNSUPPORTED;
+    }
+    if (p->pad_h > 1 || p->pad_w > 1) {
+        *err = "padding must be 0 or 1";
+        return FCM_ERR_UNSUPPORTED;
+    }
+    if (p->C % 8 || p->K % 8 || p->K1 % 8) {
+        *err = "channel counts must be multiples of 8 (16-byte NHWC vectors)";
+        return FCM_ERR_UNSUPPORTED;
+    }
+    if (p->kind == FCM_KIND_B2B && p->dtype == FCM_F32) {
+        *err = "the back-to-back kernels need 16-bit storage (fp16 or bf16)";
+        return FCM_ERR_UNSUPPORTED;
+    }
+    return FCM_OK;
+}
+
+bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
+    const int want = p.kind == FCM_KIND_B2B ? VK_B2B : (p.dtype == FCM_F32 ? VK_DWPW32 : VK_DWPW);
+    if (v.vkind != want || v.dtype != p.dtype) {
+        if (why) *why = "variant is for another module kind or storage type";
+        return false;
+    }
+    if (v.stride != p.stride_h) {
+        if (why) *why = "variant is compiled for another stride";
+        return false;
+    }
+    if (v.wres && v.vkind == VK_DWPW && p.C > v.cc) {
+        if (why) *why = "register-resident pointwise weights need C <= channel chunk";
+        return false;
+    }
+    if (v.vkind == VK_B2B && p.K1 > v.k1) {
+        if (why) *why = "variant is compiled for fewer intermediate channels";
+        return false;
+    }
+    return true;
+}
+
+namespace {
+
+struct Estimate {
+    double t_us;      // roofline time model
+    int64_t pred;     // bytes requested from the memory hierarchy
+    double waste;     // arithmetic done beyond the module's own (recompute, padding)
+    double gma;       // pages' Eq.-style estimate (inf when infeasible)
+    int wgs_per_cu;
+    int num_tiles;
+    int grid;
+    bool feasible;
+};
+
+Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_spec& d, int Ho,
+                  int Wo) {
+    Estimate r{};
+    const int e = elem_bytes(p.dtype);
+    const int lds = variant_lds_bytes(v);
+    int vg = variant_vgpr_estimate(v);
+    vg = (vg + 7) / 8 * 8;
+    int occ_lds = lds > 0 ? d.lds_bytes_per_cu / lds : 8;
+    int occ_vgpr = d.vgprs_per_simd_lane / std::max(vg, 1);
+    int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd);
+    if (lds > d.lds_bytes_per_wg) occ = 0;
+    r.wgs_per_cu = occ;
+    const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);
+    const int64_t ptiles = (int64_t)p.N * tiles_h * tiles_w;
+    const int ktiles = (int)cdiv(p.K, v.kt);
+    r.num_tiles = (int)std::min<int64_t>(ptiles * ktiles, INT32_MAX);
+    int64_t grid = std::min<int64_t>(ptiles * ktiles, (int64_t)d.num_cus * std::max(occ, 1));
+    grid = std::max<int64_t>(grid / ktiles, 1) * ktiles;
+    const int64_t unit = (int64_t)ktiles * 8;
+    if (grid >= unit) grid = grid / unit * unit;
+    r.grid = (int)grid;
+
+    const int64_t halo = halo_pixels(Ho, Wo, p.H, p.W, v.th, v.tw, p.stride_h, p.pad_h, p.pad_w);
+    const int64_t x_reads = halo * p.N * p.C * e * ktiles;
+    const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K * e;
+    const int n1 = p.kind == FCM_KIND_B2B ? p.K1 : p.C;
+    const int64_t w1_bytes =
+        (int64_t)(p.kind == FCM_KIND_B2B ? (int64_t)p.K1 * 9 * p.C : 9LL * p.C) * e;
+    const int64_t w2_slice = (int64_t)std::min(v.kt, p.K) * n1 * e;
+    const int64_t epi = (int64_t)4 * 2 * (n1 + v.kt);
+    int64_t w_reads;
+    if (v.vkind == VK_B2B) {
+        // 3x3 filters are streamed for every tile, 1x1 filters stay in registers
+        w_reads = (int64_t)r.num_tiles * w1_bytes + grid * (w2_slice + epi);
+    } else if (v.wres) {
+        w_reads = grid * (w2_slice + w1_bytes + epi);
+    } else {
+        w_reads = (int64_t)r.num_tiles * (w2_slice + w1_bytes) + grid * epi;
+    }
+    r.pred = x_reads + y_bytes + w_reads;
+    // redundant work: the first layer is recomputed once per output-channel tile
+    // (no redundancy at all with a single tile, as the DWPW module promises) and
+    // channels the variant is compiled for but the problem lacks are computed as 0
+    r.waste = (double)ktiles * (v.vkind == VK_B2B ? (double)v.k1 / p.K1 : 1.0) *
+              ((double)tiles_h * v.th * tiles_w * v.tw) / ((double)Ho * Wo);
+
+    // Roofline time: the slowest of compulsory HBM traffic, traffic requested from
+    // the on-chip caches (modelled at 4x HBM), matrix-core work and vector work, each
+    // with the variant's redundancy; divided by the fraction of CUs the grid covers.
+    const double P = (double)p.N * Ho * Wo;
+    const double pad_px = (double)tiles_h * v.th * tiles_w * v.tw / ((double)Ho * Wo);
+    const double alg = (double)p.N * p.H * p.W * p.C * e + (double)y_bytes + (double)w1_bytes +
+                       (double)p.K * n1 * e;
+    double t_mat, t_vec;
+    if (v.vkind == VK_B2B) {
+        t_mat = 2.0 * P * pad_px * ((double)v.k1 * 9 * p.C * ktiles + (double)v.k1 * p.K) /
+                d.mfma_f16_flops;
+        t_vec = 0.0;
+    } else if (v.vkind == VK_DWPW) {
+        t_mat = 2.0 * P * pad_px * (double)p.C * p.K / d.mfma_f16_flops;
+        t_vec = 2.0 * 9 * P * pad_px * (double)p.C * ktiles / d.valu_f32_flops;
+    } else {
+        t_mat = 0.0;
+        t_vec = (2.0 * 9 * P * pad_px * (double)p.C * ktiles + 2.0 * P * pad_px * p.C * p.K) /
+                d.valu_f32_flops;
+    }
+    const double t_hbm = alg / d.hbm_bytes_per_s;
+    const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);
+    const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
+    r.t_us = std::max(std::max(t_hbm, t_l2), std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+
+    // Eq.-style estimate (FCM paper Sec. IV): DW->PW constructed from Eq. 2 and 3.
+    const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, 3,
+                                       p.stride_h);
+    const double ifm = (double)p.N * p.H * p.W * p.C * e;
+    const double w_pw = (double)p.K * n1 * e;
+    const double w_pw_tile = (double)std::min(v.kt, p.K) * n1 * e;
+    const double ofm = (double)y_bytes;
+    const double ofm_tile = (double)v.th * v.tw * std::min(v.kt, p.K) * e;
+    const bool fits = lds <= d.lds_bytes_per_wg && occ > 0;
+    const bool enough = r.num_tiles >= d.num_cus;
+    r.feasible = fits && enough;
+    if (!fits || !enough) {
+        r.gma = INFINITY;
+    } else {
+        r.gma = (2.0 * p.C * overlap * p.N * e + ifm) * ceil(w_pw / w_pw_tile) +
+                ceil(ofm / ofm_tile) * (w_pw + (double)w1_bytes) + ofm;
+    }
+    return r;
+}
+
+// Layer-by-layer bytes with the baseline kernels' fixed tilings, and the pages'
+// Eq. 3 (first layer) + Eq. 2 (1x1 layer) estimate.
+void estimate_unfused(const fcm_problem& p, const fcm_device_spec& d, int Ho, int Wo,
+                      int64_t* pred, double* gma) {
+    const int e = elem_bytes(p.dtype);
+    const int n1 = p.kind == FCM_KIND_B2B ? p.K1 : p.C;
+    const int64_t t_bytes = (int64_t)p.N * Ho * Wo * n1 * e;
+    const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K * e;
+    const int64_t w2 = (int64_t)p.K * n1 * e;
+    int th, tw, l1_kt;
+    if (p.kind == FCM_KIND_B2B) {
+        th = lbl::CV_TH;
+        tw = lbl::CV_TW;
+        l1_kt = lbl::CV_KT;
+    } else {
+        th = lbl::DW_TH;
+        tw = lbl::DW_TW;
+        l1_kt = p.C;  // depthwise: channels split, no re-read of the input
+    }
+    const int64_t halo = halo_pixels(Ho, Wo, p.H, p.W, th, tw, p.stride_h, p.pad_h, p.pad_w);
+    const int64_t l1_tiles_px = (int64_t)p.N * cdiv(Ho, th) * cdiv(Wo, tw);
+    int64_t first;
+    if (p.kind == FCM_KIND_B2B) {
+        const int64_t kts = cdiv(p.K1, lbl::CV_KT);
+        const int64_t w1 = (int64_t)p.K1 * 9 * p.C * e;
+        first = halo * p.N * p.C * e * kts + l1_tiles_px * w1 + t_bytes;
+    } else {
+        const int cc = p.dtype == FCM_F32 ? lbl::DW_CC32 : lbl::DW_CC16;
+        const int64_t chunks = cdiv(p.C, cc);
+        first = halo * p.N * p.C * e + l1_tiles_px * chunks * 9LL * cc * e + t_bytes;
+    }
+    (void)l1_kt;
+    const int mt = p.dtype == FCM_F32 ? lbl::PW_MT32 : lbl::PW_MT16;
+    const int kt = p.dtype == FCM_F32 ? lbl::PW_KT32 : lbl::PW_KT16;
+    const int64_t m = (int64_t)p.N * Ho * Wo;
+    const int64_t pw_tiles_m = cdiv(m, mt), pw_tiles_k = cdiv(p.K, kt);
+    const int64_t second = t_bytes * pw_tiles_k + pw_tiles_m * w2 + y_bytes;
+    *pred = first + second;
+
+    // Eq. 3 for the depthwise layer (or Eq. 2-style for the 3x3 conv) + Eq. 2.
+    const double ifm = (double)p.N * p.H * p.W * p.C * e;
+    const double overlap = eq1_overlap(p.W, p.H, tw * p.stride_w, th * p.stride_h, 3, p.stride_h);
+    double g1;
+    if (p.kind == FCM_KIND_B2B) {
+        const double w1 = (double)p.K1 * 9 * p.C * e;
+        g1 = (2.0 * p.C * overlap * p.N * e + ifm) * ceil((double)p.K1 / lbl::CV_KT) +
+             (double)t_bytes + ceil((double)t_bytes / ((double)th * tw * lbl::CV_KT * e)) * w1;
+    } else {
+        g1 = 2.0 * p.C * overlap * p.N * e + ifm + (double)t_bytes +
+             ceil((double)Ho * Wo / (double)(th * tw)) * 9.0 * p.C * e;
+    }
+    const double g2 = ceil((double)w2 / ((double)std::min(kt, p.K) * n1 * e)) * (double)t_bytes +
+                      (double)y_bytes + ceil((double)y_bytes / ((double)mt * std::min(kt, p.K) * e)) *
+                                            (double)w2;
+    *gma = g1 + g2;
+    (void)d;
+}
+
+}  // namespace
+
+fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int forced,
+                        fcm_plan_t* out, std::string* err) {
+    if (!out) {
+        *err = "plan output pointer is NULL";
+        return FCM_ERR_INVALID_ARG;
+    }
+    fcm_status st = validate_problem(p, err);
+    if (st != FCM_OK) return st;
+    fcm_device_spec d;
+    if (spec) {
+        d = *spec;
+    } else {
+        fcm_default_device_spec(&d);
+    }
+    if (d.num_cus <= 0 || d.lds_bytes_per_cu <= 0 || d.lds_bytes_per_wg <= 0 ||
+        d.vgprs_per_simd_lane <= 0 || d.max_waves_per_simd <= 0) {
+        *err = "device spec has a non-positive field";
+        return FCM_ERR_INVALID_ARG;
+    }
+    const int Ho = conv_out(p->H, p->pad_h, p->R, p->stride_h);
+    const int Wo = conv_out(p->W, p->pad_w, p->S, p->stride_w);
+
+    int best = -1;
+    Estimate be{};
+    std::string why;
+    for (int i = 0; i < kNumVariants; ++i) {
+        if (forced >= 0 && i != forced) continue;
+        const VariantDesc& v = kVariants[i];
+        if (!variant_runs(v, *p, forced >= 0 ? &why : nullptr)) continue;
+        Estimate e = estimate(v, *p, d, Ho, Wo);
+        if (e.wgs_per_cu <= 0) {
+            if (forced >= 0) why = "variant's LDS or registers exceed the device budget";
+            continue;
+        }
+        bool better;
+        if (best < 0) {
+            better = true;
+        } else if (e.feasible != be.feasible) {
+            better = e.feasible;  // a constraint violation never beats a feasible tiling
+        } else if (!e.feasible && e.num_tiles != be.num_tiles) {
+            better = e.num_tiles > be.num_tiles;  // infeasible: keep the CUs busiest
+        } else if (fabs(e.t_us - be.t_us) > 0.01 * std::min(e.t_us, be.t_us)) {
+            better = e.t_us < be.t_us;  // modelled time decides unless within 1%
+        } else if (e.pred != be.pred) {
+            better = e.pred < be.pred;
+        } else if (e.waste != be.waste) {
+            better = e.waste < be.waste;
+        } else {
+            better = e.wgs_per_cu > be.wgs_per_cu;
+        }
+        if (better) {
+            best = i;
+            be = e;
+        }
+    }
+    if (best < 0) {
+        *err = forced >= 0 ? ("variant cannot run this problem: " + why)
+                           : std::string("no compiled kernel variant fits this problem");
+        return (forced >= 0 && (forced >= kNumVariants)) ? FCM_ERR_INVALID_ARG
+                                                         : FCM_ERR_UNSUPPORTED;
+    }
+    const VariantDesc& v = kVariants[best];
+    fcm_plan_t pl;
+    memset(&pl, 0, sizeof(pl));
+    pl.version = FCM_PLAN_VERSION;
+    pl.prob = *p;
+    pl.Ho = Ho;
+    pl.Wo = Wo;
+    pl.variant = best;
+    pl.tile_h = v.th;
+    pl.tile_w = v.tw;
+    pl.k_tile = v.kt;
+    pl.c_chunk = v.cc;
+    pl.waves_per_wg = 4;
+    pl.wgs_per_cu = be.wgs_per_cu;
+    pl.num_tiles = be.num_tiles;
+    pl.grid = be.grid;
+    pl.lds_bytes = variant_lds_bytes(v);
+    const int e = elem_bytes(p->dtype);
+    const int n1 = p->kind == FCM_KIND_B2B ? p->K1 : p->C;
+    pl.w1_packed_bytes =
+        (int64_t)(p->kind == FCM_KIND_B2B ? (int64_t)p->K1 * p->R * p->S * p->C
+                                          : (int64_t)p->R * p->S * p->C) * e;
+    pl.w2_packed_bytes = (int64_t)p->K * n1 * e;
+    pl.workspace_bytes = (int64_t)p->N * Ho * Wo * n1 * e;
+    const int64_t x_bytes = (int64_t)p->N * p->H * p->W * p->C * e;
+    const int64_t y_bytes = (int64_t)p->N * Ho * Wo * p->K * e;
+    // epilogue arrays are counted as passed: scale and bias for both layers
+    const int64_t epi = (int64_t)4 * 2 * (n1 + p->K);
+    pl.alg_bytes_fused = x_bytes + y_bytes + pl.w1_packed_bytes + pl.w2_packed_bytes + epi;
+    pl.alg_bytes_unfused = pl.alg_bytes_fused + 2 * pl.workspace_bytes;
+    pl.pred_bytes_fused = be.pred;
+    int64_t pu = 0;
+    double gu = 0;
+    estimate_unfused(*p, d, Ho, Wo, &pu, &gu);
+    pl.pred_bytes_unfused = pu;
+    pl.gma_paper_fused = be.gma;
+    pl.gma_paper_unfused = gu;
+    // FusePlanner's rule: fuse when the module's estimated global memory accesses are
+    // below those of its layers run one by one (finite beats infinite).
+    pl.fuse = (be.gma < gu) ? 1 : 0;
+    pl.pred_us_fused = be.t_us;
+    const double P = (double)p->N * Ho * Wo;
+    pl.flops = p->kind == FCM_KIND_B2B
+                   ? 2.0 * P * p->K1 * p->C * p->R * p->S + 2.0 * P * p->K1 * p->K
+                   : 2.0 * P * p->C * p->R * p->S + 2.0 * P * p->C * p->K;
+    *out = pl;
+    return FCM_OK;
+}
+
+}  // namespace fcm

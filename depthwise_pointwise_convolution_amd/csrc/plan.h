@@ -1,0 +1,46 @@
+// plan.h -- the gfx950 FusePlanner (host only, no HIP dependency).
+#pragma once
+
+#include <string>
+
+#include "../../include/fcm.h"
+
+namespace fcm {
+
+enum VKind { VK_DWPW = 0, VK_DWPW32 = 1, VK_B2B = 2 };
+
+struct VariantDesc {
+    const char* name;
+    int vkind;   // VKind
+    int dtype;   // fcm_dtype
+    int stride;
+    int th, tw;  // output tile
+    int kt;      // output channels per workgroup
+    int cc;      // input channels per LDS pass
+    int wres;    // pointwise weights resident in registers
+    int k1;      // back-to-back: intermediate channels compiled in (0 otherwise)
+};
+
+extern const VariantDesc kVariants[];
+extern const int kNumVariants;
+
+// LDS bytes and a per-lane VGPR estimate of one workgroup of variant v.
+int variant_lds_bytes(const VariantDesc& v);
+int variant_vgpr_estimate(const VariantDesc& v);
+
+// Checks every field of the problem (see fcm_plan in fcm.h for the rules).
+fcm_status validate_problem(const fcm_problem* p, std::string* err);
+
+// Whether variant v can run problem p (kind, type, stride, channel limits).
+bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why);
+
+// Fill *out for problem p with variant `forced` (or the cheapest one if forced < 0).
+fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int forced,
+                        fcm_plan_t* out, std::string* err);
+
+// Output extent of a convolution.
+inline int conv_out(int in, int pad, int filt, int stride) {
+    return (in + 2 * pad - filt) / stride + 1;
+}
+
+}  // namespace fcm

@@ -1,0 +1,78 @@
+"""Convenience wrapper over the C ABI for one module instance: plans the problem,
+packs the PyTorch-layout weights once (the offline packing step), allocates outputs
+with torch, and runs the fused kernel or the layer-by-layer pair.  Marshalling only.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (fcm_b2b_conv_fwd, fcm_conv_fwd, fcm_dw_fwd, fcm_dwpw_fwd, fcm_pack_weights,
+               fcm_plan, fcm_plan_variant, fcm_pw_fwd, problem, FCM_KIND_B2B)
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+class FcmModule:
+    """w1: depthwise [C,3,3] or standard [K1,C,3,3]; w2: [K,C] or [K,K1] (torch, on
+    the GPU, storage dtype); scale/bias: float32 per-channel tensors or None."""
+
+    def __init__(self, kind: str, dtype: str, N: int, H: int, W: int, C: int, K: int,
+                 K1: Optional[int], stride: int, pad: int, act1: str, act2: str, w1, w2,
+                 scale1=None, bias1=None, scale2=None, bias2=None,
+                 variant: Optional[int] = None, stream=None):
+        self.prob = problem(kind, dtype, N, H, W, C, K, K1, stride=stride, pad=pad,
+                            act1=act1, act2=act2)
+        self.plan = fcm_plan(self.prob) if variant is None else fcm_plan_variant(self.prob,
+                                                                                 variant)
+        self.dtype = dtype
+        self.tdtype = TORCH_DTYPES[dtype]
+        dev = w1.device
+        e = torch.empty((), dtype=self.tdtype).element_size()
+        self.w1p = torch.empty(self.plan.w1_packed_bytes // e, dtype=self.tdtype, device=dev)
+        self.w2p = torch.empty(self.plan.w2_packed_bytes // e, dtype=self.tdtype, device=dev)
+        fcm_pack_weights(self.plan, w1.contiguous(), self.w1p, w2.contiguous(), self.w2p,
+                         stream)
+        self.s1, self.b1, self.s2, self.b2 = scale1, bias1, scale2, bias2
+        self.out_shape = (N, self.plan.Ho, self.plan.Wo, K)
+        self.t_shape = (N, self.plan.Ho, self.plan.Wo, C if K1 is None else K1)
+        self.b2b = self.prob.kind == FCM_KIND_B2B
+
+    def new_output(self, device) -> torch.Tensor:
+        return torch.empty(self.out_shape, dtype=self.tdtype, device=device)
+
+    def fused(self, x, y=None, stream=None) -> torch.Tensor:
+        y = self.new_output(x.device) if y is None else y
+        fn = fcm_b2b_conv_fwd if self.b2b else fcm_dwpw_fwd
+        fn(self.plan, x, self.w1p, self.s1, self.b1, self.w2p, self.s2, self.b2, y, stream)
+        return y
+
+    def first_layer(self, x, t=None, stream=None) -> torch.Tensor:
+        t = torch.empty(self.t_shape, dtype=self.tdtype, device=x.device) if t is None else t
+        fn = fcm_conv_fwd if self.b2b else fcm_dw_fwd
+        fn(self.plan, x, self.w1p, self.s1, self.b1, t, stream)
+        return t
+
+    def second_layer(self, t, y=None, stream=None) -> torch.Tensor:
+        y = self.new_output(t.device) if y is None else y
+        fcm_pw_fwd(self.plan, t, self.w2p, self.s2, self.b2, y, stream)
+        return y
+
+    def unfused(self, x, t=None, y=None, stream=None) -> torch.Tensor:
+        return self.second_layer(self.first_layer(x, t, stream), y, stream)
+
+
+def from_workload(wl, tensors: dict, device="cuda", variant=None) -> "FcmModule":
+    """Build a module from a workload description and float64 numpy inputs."""
+    tdt = TORCH_DTYPES[wl.dtype]
+
+    def dev(a, dt):
+        return None if a is None else torch.from_numpy(a).to(dt).to(device)
+
+    return FcmModule(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
+                     None if wl.kind == "dwpw" else wl.K1, wl.stride, wl.pad, wl.act1,
+                     wl.act2, dev(tensors["w1"], tdt), dev(tensors["w2"], tdt),
+                     dev(tensors["scale1"], torch.float32), dev(tensors["bias1"], torch.float32),
+                     dev(tensors["scale2"], torch.float32), dev(tensors["bias2"], torch.float32),
+                     variant=variant)

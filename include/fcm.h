@@ -1,0 +1,209 @@
+/*
+ * fcm.h -- C ABI of the MI355X (gfx950) fused convolution module library (libfcm.so).
+ *
+ * The library runs a depthwise 3x3 convolution and the 1x1 (pointwise) convolution
+ * that follows it in ONE kernel, keeping the intermediate feature-map tile on chip
+ * (LDS / registers) instead of writing it to HBM: the "Fused Convolutional Module"
+ * (FCM) of "Fusing Depthwise and Pointwise Convolutions for Efficient Inference on
+ * GPUs" (Sec. III, DWPW case, Fig. 3(b)).  The same family covers the back-to-back
+ * pair of a standard 3x3 convolution followed by a 1x1 convolution ("Fusing two
+ * back-to-back convolutions", the CONV1/CONV2 example); the second convolution must
+ * be 1x1 so that every workgroup's input to it is produced by that workgroup alone
+ * (same discussion).  Each convolution is followed by a per-channel scale, bias and
+ * ReLU/ReLU6 epilogue (conv -> normalisation -> activation, FCM paper Sec. III-A).
+ * Unfused layer-by-layer entry points, with the same stage code, serve as the
+ * baseline the FCM paper compares against (Sec. V-C) and as the fallback when a plan
+ * says not to fuse (Sec. IV).
+ *
+ * Conventions for every entry point:
+ *  - Activations are NHWC and densely packed: x[N][H][W][C], y[N][Ho][Wo][K] with
+ *    Ho = (H + 2*pad_h - R)/stride_h + 1 (floor), likewise Wo.
+ *  - Convolution is cross-correlation (no filter flip) with zero padding.
+ *  - Activations and weights share one storage type (fcm_dtype); accumulation and
+ *    the epilogue are fp32; each layer's output is rounded to the storage type with
+ *    round-to-nearest-even.
+ *  - Epilogue of a layer with n output channels: out[c] = act(scale[c]*acc[c] +
+ *    bias[c]) with fp32 arrays scale[n], bias[n] in device memory; a NULL scale means
+ *    1 and a NULL bias means 0.
+ *  - All tensor pointers are device pointers owned by the caller; the library never
+ *    allocates, frees or retains device memory.  Every device pointer must be 16-byte
+ *    aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  *_fwd and
+ *    fcm_pack_weights are asynchronous on that stream; they validate every argument
+ *    on the host before enqueueing anything, and return a status.
+ *  - No function throws or aborts.  On error nothing is enqueued and a description
+ *    is available from fcm_last_error() on the calling thread.
+ *  - The library is stateless apart from a per-thread error string and a per-process
+ *    cache of device properties; concurrent calls from several threads are safe.
+ */
+#ifndef FCM_H
+#define FCM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FCM_PLAN_VERSION 1
+
+typedef enum {
+    FCM_OK = 0,
+    FCM_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, plan mismatch */
+    FCM_ERR_UNSUPPORTED = 2, /* valid problem this library has no kernel for */
+    FCM_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+} fcm_status;
+
+typedef enum { FCM_F32 = 0, FCM_F16 = 1, FCM_BF16 = 2 } fcm_dtype;
+
+typedef enum { FCM_ACT_NONE = 0, FCM_ACT_RELU = 1, FCM_ACT_RELU6 = 2 } fcm_act;
+
+typedef enum {
+    FCM_KIND_DWPW = 0, /* depthwise RxS conv (C -> C) then pointwise 1x1 (C -> K) */
+    FCM_KIND_B2B = 1   /* standard RxS conv (C -> K1) then 1x1 conv (K1 -> K) */
+} fcm_kind;
+
+/* The problem, in the pages' terms: NHWC input feature maps, per-channel depthwise
+ * filters or a [CRSK]-style standard filter bank, a CxK pointwise filter matrix,
+ * stride/padding, and one epilogue per convolution. */
+typedef struct {
+    int32_t kind;     /* fcm_kind */
+    int32_t dtype;    /* fcm_dtype of activations and weights */
+    int32_t N, H, W;  /* input batch and spatial extent */
+    int32_t C;        /* input channels */
+    int32_t K1;       /* B2B: output channels of the first conv.  DWPW: must equal C */
+    int32_t K;        /* output channels of the final 1x1 conv */
+    int32_t R, S;     /* first conv's filter height/width (only 3x3 has kernels) */
+    int32_t stride_h, stride_w, pad_h, pad_w; /* first conv; the 1x1 is stride 1 */
+    int32_t act1, act2; /* fcm_act after the first / second conv */
+} fcm_problem;
+
+/* What the planner needs to know about the GPU (FusePlanner's inputs: number of
+ * compute units, on-chip memory sizes; FCM paper Sec. IV). */
+typedef struct {
+    int32_t num_cus;             /* 256 on MI355X */
+    int32_t num_xcds;            /* 8 */
+    int32_t simds_per_cu;        /* 4 */
+    int32_t wave_size;           /* 64 */
+    int32_t max_waves_per_simd;  /* 8 */
+    int32_t vgprs_per_simd_lane; /* 512 (architectural + accumulation) */
+    int32_t lds_bytes_per_cu;    /* 163840 */
+    int32_t lds_bytes_per_wg;    /* largest LDS allocation of one workgroup */
+    int64_t l2_bytes_per_xcd;    /* 4 MiB */
+    double hbm_bytes_per_s;      /* 8.0e12 */
+    double mfma_f16_flops;       /* dense fp16/bf16 matrix peak, 2.5e15 */
+    double mfma_f32_flops;       /* dense fp32 matrix peak, 157.3e12 */
+    double valu_f32_flops;       /* fp32 vector FMA peak without packed math */
+} fcm_device_spec;
+
+/* A plan: the problem plus the tiling and launch shape chosen for it.  POD; the
+ * caller owns it.  Produced by fcm_plan / fcm_plan_variant, consumed by *_fwd. */
+typedef struct {
+    int32_t version;        /* FCM_PLAN_VERSION */
+    fcm_problem prob;
+    int32_t Ho, Wo;
+    int32_t variant;        /* index of the fused kernel variant chosen */
+    int32_t tile_h, tile_w; /* output pixels of one workgroup tile */
+    int32_t k_tile;         /* output channels of one workgroup tile */
+    int32_t c_chunk;        /* input channels staged in LDS per pass */
+    int32_t waves_per_wg;
+    int32_t wgs_per_cu;     /* occupancy the LDS/VGPR budgets allow */
+    int32_t num_tiles;      /* pixel tiles x K tiles */
+    int32_t grid;           /* workgroups launched (persistent kernels loop) */
+    int32_t lds_bytes;      /* LDS of one workgroup */
+    int32_t fuse;           /* 1: the fused kernel moves fewer bytes than LBL */
+    int64_t w1_packed_bytes, w2_packed_bytes; /* sizes fcm_pack_weights writes */
+    int64_t workspace_bytes;  /* intermediate tensor of the unfused path */
+    int64_t alg_bytes_fused;  /* compulsory HBM bytes: X + Y + weights + epilogue */
+    int64_t alg_bytes_unfused;/* ... + intermediate written and read back */
+    int64_t pred_bytes_fused;   /* bytes the chosen tiling requests from L2 */
+    int64_t pred_bytes_unfused; /* same for the layer-by-layer kernels */
+    double gma_paper_fused;   /* FusePlanner estimate (Eq. 1-4 style), bytes */
+    double gma_paper_unfused; /* Eq. 2 + Eq. 3, bytes */
+    double flops;             /* 2 * multiply-adds of both convolutions */
+    double pred_us_fused;     /* roofline time model of the chosen variant, us */
+} fcm_plan_t;
+
+/* MI355X published figures; no HIP call (usable without a GPU). */
+fcm_status fcm_default_device_spec(fcm_device_spec* out);
+
+/* Properties of HIP device `device` (CU count, LDS sizes) over the MI355X defaults.
+ * Returns FCM_ERR_HIP if the device cannot be queried. */
+fcm_status fcm_query_device_spec(int device, fcm_device_spec* out);
+
+/* FusePlanner for gfx950 (FCM paper Sec. IV): validates the problem, enumerates the
+ * compiled kernel variants whose tiles fit the LDS and register budgets, estimates
+ * each one's memory traffic and, since a gfx950 workgroup can also be bound by its
+ * matrix or vector units, a roofline time (the slowest of HBM, on-chip traffic,
+ * matrix and vector work including recomputation); keeps the fastest; and decides
+ * with the pages' rule (fewer estimated global memory accesses) whether fusing
+ * beats the layer-by-layer kernels.  spec == NULL uses the MI355X defaults.
+ * Host only; makes no HIP call.  Errors: INVALID_ARG (null pointer, non-positive
+ * size, K1 != C for DWPW, padding >= filter), UNSUPPORTED (filter not 3x3, stride
+ * not 1 or 2, padding not 0 or 1, a channel count not a multiple of 8, or no variant
+ * fits). */
+fcm_status fcm_plan(const fcm_problem* prob, const fcm_device_spec* spec, fcm_plan_t* out);
+
+/* Same, but with the fused kernel variant forced (for tests and on-device tuning).
+ * UNSUPPORTED if that variant cannot run the problem. */
+fcm_status fcm_plan_variant(const fcm_problem* prob, const fcm_device_spec* spec,
+                            int32_t variant, fcm_plan_t* out);
+
+/* Number of fused kernel variants compiled into the library, and a short name for
+ * one of them ("" if out of range). */
+int32_t fcm_num_variants(void);
+const char* fcm_variant_name(int32_t variant);
+
+/* Offline weight packing ("weights are packed offline since they do not change in
+ * inference", FCM paper Sec. III-B): converts PyTorch-layout filters into the
+ * layouts the kernels read.
+ *   DWPW: w1_src depthwise [C][R][S]      -> w1_dst [R*S][C]      (channel fastest)
+ *         w2_src pointwise [K][C]         -> w2_dst [K][C]        (copied as is)
+ *   B2B:  w1_src standard  [K1][C][R][S]  -> w1_dst [K1][R*S][C]  (channel fastest)
+ *         w2_src 1x1       [K][K1]        -> w2_dst [K][K1]
+ * Sizes in bytes are plan->w1_packed_bytes / w2_packed_bytes.  Either pair may be
+ * NULL to skip it.  Source and destination must not overlap. */
+fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1_dst,
+                            const void* w2_src, void* w2_dst, void* stream);
+
+/* Fused DW -> PW module (FCM DWPW).  x: [N][H][W][C]; w_dw: packed [R*S][C];
+ * w_pw: packed [K][C]; scale1/bias1: [C] or NULL; scale2/bias2: [K] or NULL;
+ * y: [N][Ho][Wo][K].  plan->prob.kind must be FCM_KIND_DWPW. */
+fcm_status fcm_dwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
+                        const float* scale1, const float* bias1, const void* w_pw,
+                        const float* scale2, const float* bias2, void* y, void* stream);
+
+/* Fused standard 3x3 conv -> 1x1 conv (back-to-back).  x: [N][H][W][C];
+ * w1: packed [K1][R*S][C]; w2: packed [K][K1]; scale1/bias1: [K1] or NULL;
+ * scale2/bias2: [K] or NULL; y: [N][Ho][Wo][K].  plan->prob.kind must be
+ * FCM_KIND_B2B. */
+fcm_status fcm_b2b_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
+                            const float* scale1, const float* bias1, const void* w2,
+                            const float* scale2, const float* bias2, void* y,
+                            void* stream);
+
+/* Layer-by-layer baseline, first layer of a DWPW plan: depthwise conv + epilogue 1,
+ * writing the intermediate t: [N][Ho][Wo][C] (plan->workspace_bytes bytes). */
+fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
+                      const float* scale1, const float* bias1, void* t, void* stream);
+
+/* Layer-by-layer baseline, second layer of a DWPW or B2B plan: 1x1 conv + epilogue 2
+ * reading the intermediate t: [N][Ho][Wo][C or K1], writing y: [N][Ho][Wo][K]. */
+fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
+                      const float* scale2, const float* bias2, void* y, void* stream);
+
+/* Layer-by-layer baseline, first layer of a B2B plan: standard conv + epilogue 1,
+ * writing t: [N][Ho][Wo][K1]. */
+fcm_status fcm_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
+                        const float* scale1, const float* bias1, void* t, void* stream);
+
+/* Static description of a status code, and the calling thread's last error detail
+ * (empty after a successful call). */
+const char* fcm_status_str(fcm_status s);
+const char* fcm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FCM_H */

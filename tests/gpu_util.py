@@ -1,0 +1,116 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and the CPU
+oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import numpy as np
+
+import fcm_inputs
+import oracle
+
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Normwise max relative error: max|got - ref| / max|ref|."""
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    return num / den if den > 0 else num
+
+
+def oracle_kwargs(wl, inp) -> dict:
+    return dict(stride=(wl.stride, wl.stride), pad=(wl.pad, wl.pad), scale1=inp["scale1"],
+                bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],
+                act2=wl.act2, dtype=wl.dtype)
+
+
+def oracle_full(wl, inp) -> np.ndarray:
+    fn = oracle.dwpw if wl.kind == "dwpw" else oracle.b2b
+    return fn(inp["x"], inp["w1"], inp["w2"], **oracle_kwargs(wl, inp))
+
+
+def oracle_rows(wl, inp, pix) -> np.ndarray:
+    fn = oracle.dwpw_at if wl.kind == "dwpw" else oracle.b2b_at
+    return fn(inp["x"], inp["w1"], inp["w2"], pix, **oracle_kwargs(wl, inp))
+
+
+def run_gpu(wl, inp, variant=None, path="fused"):
+    """Run the module on the GPU; returns the output as float64 numpy."""
+    import torch
+    from depthwise_pointwise_convolution_amd.module import TORCH_DTYPES, from_workload
+    mod = from_workload(wl, inp, device="cuda", variant=variant)
+    x = torch.from_numpy(inp["x"]).to(TORCH_DTYPES[wl.dtype]).cuda()
+    y = mod.fused(x) if path == "fused" else mod.unfused(x)
+    torch.cuda.synchronize()
+    return y.double().cpu().numpy(), mod
+
+
+def int_inputs(wl, seed: int) -> dict:
+    """Small-integer inputs for which every step is exact in every storage type:
+    |x| <= 2, filters in {-1, 0, 1} with few non-zeros per output row, scale 1 or 2,
+    integer bias.  Intermediates stay below 256 in magnitude, so rounding to bf16,
+    fp16 or fp32 never changes a value and the GPU must equal the oracle bit for
+    bit whatever its summation order."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-2, 3, size=(wl.N, wl.H, wl.W, wl.C)).astype(np.float64)
+    n1 = wl.C if wl.kind == "dwpw" else wl.K1
+    if wl.kind == "dwpw":
+        w1 = rng.integers(-1, 2, size=(wl.C, 3, 3)).astype(np.float64)
+        acc1 = 9 * 2       # |first-layer sum| <= 9 taps * |x|
+    else:
+        w1 = np.zeros((wl.K1, wl.C, 3, 3))
+        for k in range(wl.K1):
+            idx = rng.choice(wl.C * 9, size=min(6, wl.C * 9), replace=False)
+            w1[k].reshape(-1)[idx] = rng.choice([-1.0, 1.0], size=idx.size)
+        acc1 = 6 * 2
+    s1 = rng.choice([1.0, 2.0], size=n1) if wl.scale1 else None
+    b1 = rng.integers(-2, 3, size=n1).astype(np.float64) if wl.bias1 else None
+    t_max = acc1 * (2 if s1 is not None else 1) + 2
+    # second layer: nz non-zeros per output row keep |sum| <= 100, so after a scale
+    # of at most 2 and a bias of at most 2 every value is an integer below 256
+    nz = max(1, min(n1, 100 // t_max))
+    w2 = np.zeros((wl.K, n1))
+    for k in range(wl.K):
+        idx = rng.choice(n1, size=nz, replace=False)
+        w2[k, idx] = rng.choice([-1.0, 1.0], size=nz)
+    s2 = rng.choice([1.0, 2.0], size=wl.K) if wl.scale2 else None
+    b2 = rng.integers(-2, 3, size=wl.K).astype(np.float64) if wl.bias2 else None
+    return {"x": x, "w1": w1, "w2": w2, "scale1": s1, "bias1": b1, "scale2": s2, "bias2": b2}
+
+
+def all_variants_for(wl):
+    """Indices of every compiled variant able to run the workload."""
+    import depthwise_pointwise_convolution_amd as F
+    p = F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
+                  None if wl.kind == "dwpw" else wl.K1, stride=wl.stride, pad=wl.pad,
+                  act1=wl.act1, act2=wl.act2)
+    out = []
+    for v in range(F.fcm_num_variants()):
+        try:
+            F.fcm_plan_variant(p, v)
+            out.append(v)
+        except F.FcmError:
+            pass
+    return out
+
+
+REDUCED = {
+    # ragged spatial tails (not multiples of the tiles) and several tiles per image
+    "cfg1": dict(),
+    "cfg2": dict(N=2, H=29, W=37),
+    "cfg3": dict(N=3),
+    "cfg4a": dict(N=2, H=57, W=45),
+    "cfg4b": dict(N=3),
+    "cfg5": dict(N=2, H=23, W=37),
+}
+
+
+def reduced(name: str):
+    return fcm_inputs.WORKLOADS[name].replace(**REDUCED[name])

@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same
+seeded inputs.
+
+Bars: bit-exact on integer probes (every step exact, so any index, halo, stride,
+padding, tiling or layout mistake shows); normwise max relative error <= 1e-5 for
+fp32 storage and <= 2e-2 (fp32 accumulation) for fp16/bf16 otherwise.
+"""
+import numpy as np
+import pytest
+
+import fcm_inputs
+from gpu_util import (TOL, all_variants_for, gpu_available, int_inputs, oracle_full,
+                      oracle_rows, reduced, rel_err, run_gpu)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+NAMES = list(fcm_inputs.WORKLOADS)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_reduced_config_full_compare(name, path):
+    wl = reduced(name)
+    inp = fcm_inputs.make_inputs(wl)
+    _log(f"case {name} reduced {wl.N}x{wl.H}x{wl.W}x{wl.C}->{wl.K} {path}")
+    got, mod = run_gpu(wl, inp, path=path)
+    ref = oracle_full(wl, inp)
+    assert got.shape == ref.shape
+    err = rel_err(got, ref)
+    _log(f"  variant {mod.plan.variant} rel err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[wl.dtype], err
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_full_size_config_sampled(name, path):
+    """BASELINE-size workloads in the launch configuration the benchmark times,
+    checked on sampled output pixels (all image corners and edge midpoints of the
+    first and last image, plus random pixels), and by properties over the whole
+    output."""
+    wl = fcm_inputs.WORKLOADS[name]
+    inp = fcm_inputs.make_inputs(wl)
+    _log(f"case {name} full {path}")
+    got, _ = run_gpu(wl, inp, path=path)
+    pix = fcm_inputs.sample_pixels(wl, 1500)
+    rows = oracle_rows(wl, inp, pix)
+    sel = got[pix[:, 0], pix[:, 1], pix[:, 2]]
+    err = rel_err(sel, rows)
+    _log(f"  sampled rel err {err:.3e}")
+    assert err <= TOL[wl.dtype], err
+    assert np.all(np.isfinite(got))
+    if wl.act2 == "relu6":
+        assert got.min() >= 0 and got.max() <= 6
+    elif wl.act2 == "relu":
+        assert got.min() >= 0
+
+
+CASES_INT = [
+    # (kind, dtype, N, H, W, C, K, K1, stride, pad, act1, act2, epilogue flags)
+    ("dwpw", "f16", 2, 9, 21, 64, 128, None, 1, 1, "relu6", "relu6", True),
+    ("dwpw", "bf16", 2, 11, 17, 128, 128, None, 1, 1, "none", "relu", False),
+    ("dwpw", "f16", 1, 13, 15, 256, 512, None, 2, 1, "relu6", "relu6", True),
+    ("dwpw", "f16", 2, 7, 7, 1024, 1024, None, 1, 1, "relu6", "relu6", True),
+    ("dwpw", "bf16", 2, 12, 10, 40, 24, None, 2, 0, "relu", "none", True),
+    ("dwpw", "f32", 1, 16, 16, 32, 32, None, 1, 1, "none", "none", False),
+    ("dwpw", "f32", 2, 9, 13, 40, 72, None, 2, 1, "relu6", "relu", True),
+    ("b2b", "f16", 2, 9, 19, 64, 64, 64, 1, 1, "relu", "relu", True),
+    ("b2b", "bf16", 1, 10, 9, 32, 48, 32, 1, 0, "none", "relu", True),
+    ("b2b", "f16", 1, 11, 12, 40, 24, 96, 2, 1, "relu6", "none", True),
+]
+
+
+def _int_workload(case):
+    kind, dtype, N, H, W, C, K, K1, stride, pad, act1, act2, epi = case
+    return fcm_inputs.Workload("int", kind, dtype, N=N, H=H, W=W, C=C, K=K,
+                               K1=C if K1 is None else K1, stride=stride, pad=pad, act1=act1,
+                               act2=act2, scale1=epi, bias1=epi, scale2=epi, bias2=epi)
+
+
+@pytest.mark.parametrize("case", CASES_INT, ids=lambda c: "-".join(map(str, c[:10])))
+def test_integer_probes_bit_exact_every_variant(case):
+    wl = _int_workload(case)
+    inp = int_inputs(wl, seed=sum(map(hash, map(str, case))) % 1000)
+    ref = oracle_full(wl, inp)
+    variants = all_variants_for(wl)
+    assert variants, "no variant runs this problem"
+    for v in variants:
+        _log(f"case int {case} variant {v}")
+        got, _ = run_gpu(wl, inp, variant=v)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"variant {v}: {len(bad)} mismatches, first {bad[:3].tolist()}"
+    got, _ = run_gpu(wl, inp, path="unfused")
+    assert np.array_equal(got, ref), "layer-by-layer path"
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = "b2b" if rng.random() < 0.3 else "dwpw"
+        dtype = rng.choice(["f16", "bf16"] + ([] if kind == "b2b" else ["f32"]))
+        C = int(rng.choice([8, 16, 24, 40, 64, 72, 136]))
+        K = int(rng.choice([8, 24, 40, 64, 136, 200]))
+        K1 = int(rng.choice([8, 32, 64, 96])) if kind == "b2b" else C
+        out.append(fcm_inputs.Workload(
+            f"rnd{i}", kind, str(dtype), N=int(rng.integers(1, 3)), H=int(rng.integers(1, 24)),
+            W=int(rng.integers(1, 24)), C=C, K=K, K1=K1, stride=int(rng.integers(1, 3)),
+            pad=int(rng.integers(0, 2)), act1=str(rng.choice(["none", "relu", "relu6"])),
+            act2=str(rng.choice(["none", "relu", "relu6"])), scale1=bool(rng.random() < .5),
+            bias1=bool(rng.random() < .5), scale2=bool(rng.random() < .5),
+            bias2=bool(rng.random() < .5), seed=int(rng.integers(1 << 30))))
+    return [w for w in out if w.H + 2 * w.pad >= 3 and w.W + 2 * w.pad >= 3]
+
+
+@pytest.mark.parametrize("wl", _random_cases(24, 7), ids=lambda w: w.name)
+def test_random_small_shapes(wl):
+    inp = fcm_inputs.make_inputs(wl)
+    ref = oracle_full(wl, inp)
+    for path in ("fused", "unfused"):
+        _log(f"case {wl} {path}")
+        got, _ = run_gpu(wl, inp, path=path)
+        err = rel_err(got, ref)
+        assert err <= TOL[wl.dtype], (path, err)
+
+
+def test_output_guard_bands_and_every_output_written():
+    import torch
+    from depthwise_pointwise_convolution_amd.module import from_workload
+    wl = reduced("cfg2")
+    inp = fcm_inputs.make_inputs(wl)
+    mod = from_workload(wl, inp)
+    x = torch.from_numpy(inp["x"]).half().cuda()
+    n = int(np.prod(mod.out_shape))
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
+    y = buf[guard:guard + n].view(mod.out_shape)
+    mod.fused(x, y)
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.isnan(b[:guard]).all() and torch.isnan(b[guard + n:]).all()
+    assert not torch.isnan(b[guard:guard + n]).any()
+
+
+def test_repeated_runs_are_bitwise_identical():
+    import torch
+    from depthwise_pointwise_convolution_amd.module import from_workload
+    wl = fcm_inputs.WORKLOADS["cfg2"]
+    inp = fcm_inputs.make_inputs(wl)
+    mod = from_workload(wl, inp)
+    x = torch.from_numpy(inp["x"]).half().cuda()
+    first = mod.fused(x).clone()
+    for _ in range(20):
+        assert torch.equal(mod.fused(x), first)
+
+
+def test_device_argument_errors_enqueue_nothing():
+    import torch
+    import depthwise_pointwise_convolution_amd as F
+    from depthwise_pointwise_convolution_amd.module import from_workload
+    wl = reduced("cfg2")
+    inp = fcm_inputs.make_inputs(wl)
+    mod = from_workload(wl, inp)
+    x = torch.from_numpy(inp["x"]).half().cuda()
+    y = mod.new_output("cuda")
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_dwpw_fwd(mod.plan, x.data_ptr() + 2, mod.w1p, None, None, mod.w2p, None, None, y)
+    assert ei.value.status == F.FCM_ERR_INVALID_ARG
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_b2b_conv_fwd(mod.plan, x, mod.w1p, None, None, mod.w2p, None, None, y)
+    assert ei.value.status == F.FCM_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("H,W,stride,pad", [(1, 1, 1, 1), (2, 3, 2, 1), (3, 3, 1, 0),
+                                             (5, 2, 2, 0), (1, 40, 1, 1)])
+def test_degenerate_extents(H, W, stride, pad):
+    for dtype in ("f16", "f32"):
+        wl = fcm_inputs.Workload("deg", "dwpw", dtype, N=1, H=H, W=W, C=8, K=8, K1=8,
+                                 stride=stride, pad=pad, bias2=True, seed=H * 7 + W)
+        if H + 2 * pad < 3 or W + 2 * pad < 3:
+            continue
+        inp = fcm_inputs.make_inputs(wl)
+        got, _ = run_gpu(wl, inp)
+        assert rel_err(got, oracle_full(wl, inp)) <= TOL[dtype]
