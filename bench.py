@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused depthwise->pointwise module on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2]
+
+A step is one invocation of the fused DW->PW kernel (one layer) on one batch of the
+MobileNetV1-style block: DW 3x3 s1 p1 over C=64 + scale/bias/ReLU6, PW 64->128 +
+scale/bias/ReLU6, fp16 NHWC, N=8, 112x112 (synthetic seeded inputs).  Inputs sit in
+HBM before the timed region.  The timed launches rotate over enough input/output
+buffer sets (footprint > the 256 MB Infinity Cache) that every step streams its
+input from HBM rather than from a cache.  The K steps are captured once in a HIP
+graph and replayed, so the host's launch cost does not enter the measurement;
+timing uses HIP events on the stream the kernels run on, bracketed by device
+synchronisation.  The layer-by-layer pair (DW kernel writing the intermediate to
+HBM + PW kernel reading it back) is timed the same way for comparison.
+
+Prints ONE JSON line on stdout.  Diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MALL_BYTES = 256 * 1024 * 1024   # Infinity Cache
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["depthwise_pointwise_convolution_amd/csrc/kernels/dwpw.hip",
+                  "depthwise_pointwise_convolution_amd/csrc/kernels/stages.h",
+                  "depthwise_pointwise_convolution_amd/csrc/kernels/common.h",
+                  "depthwise_pointwise_convolution_amd/csrc/variants.def"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, variant: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, f"traffic_{variant}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_graph(fn_list, steps, warmup, torch, stream):
+    """Run fn_list[i % n] for warmup steps eagerly, capture `steps` calls in a HIP
+    graph, replay it once untimed and once timed.  Returns ms per step."""
+    n = len(fn_list)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn_list[i % n]()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            fn_list[i % n]()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def time_eager(fn_list, steps, warmup, torch, stream):
+    n = len(fn_list)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn_list[i % n]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for i in range(steps):
+            fn_list[i % n]()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The CPU oracle, as it stands, on the same workload: the full layer (all N
+    images) run repeatedly until `budget_s` of wall time is spent; median time."""
+    import oracle
+    import fcm_inputs
+    inp = fcm_inputs.make_inputs(wl)
+    kw = dict(stride=(wl.stride,) * 2, pad=(wl.pad,) * 2, scale1=inp["scale1"],
+              bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],
+              act2=wl.act2, dtype=wl.dtype)
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.dwpw(inp["x"], inp["w1"], inp["w2"], **kw)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all >= budget_s or len(times) >= 50:
+            break
+    med = statistics.median(times)
+    return {"value": round(med * 1e6, 1), "unit": "us/layer", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"full layer (N={wl.N}) evaluated {len(times)} times, median; "
+                      f"C/OpenMP double-precision direct loops"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="cfg2")
+    ap.add_argument("--variant", type=int, default=None, help="force a fused kernel variant")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle time for the cpu_baseline leg (0 = skip)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "fused-only", "unfused-only",
+                                                        "copy"],
+                    help="profiling helpers: run only one path (or a plain copy) K times")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the module shards "
+              "over the batch with no exchange, see the design notes", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fcm_inputs
+    from depthwise_pointwise_convolution_amd import fcm_variant_name
+    from depthwise_pointwise_convolution_amd.module import TORCH_DTYPES, from_workload
+
+    assert torch.cuda.is_available(), "bench.py needs the MI355X"
+    dev = torch.device("cuda:0")
+    wl = fcm_inputs.WORKLOADS[args.workload]
+    inp = fcm_inputs.make_inputs(wl)
+    mod = from_workload(wl, inp, device=dev, variant=args.variant)
+    plan = mod.plan
+    tdt = TORCH_DTYPES[wl.dtype]
+    vname = fcm_variant_name(plan.variant)
+
+    # buffer sets: enough that the rotation's footprint exceeds the Infinity Cache
+    x0 = torch.from_numpy(inp["x"]).to(tdt).to(dev)
+    set_bytes = plan.alg_bytes_fused + plan.workspace_bytes
+    nsets = max(2, -(-2 * MALL_BYTES // set_bytes))
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    ys = [mod.new_output(dev) for _ in range(nsets)]
+    ts = [torch.empty(mod.t_shape, dtype=tdt, device=dev) for _ in range(nsets)]
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: {wl.description}")
+    log(f"variant {plan.variant} {vname}, grid {plan.grid}, {nsets} buffer sets "
+        f"({nsets * set_bytes / 2**20:.0f} MiB rotation)")
+
+    if args.mode == "copy":
+        # plain copy of known size for counter calibration
+        a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {args.steps} x {a.numel()} bytes")
+        return 0
+
+    fused = [lambda i=i: mod.fused(xs[i], ys[i]) for i in range(nsets)]
+    unfused = [lambda i=i: mod.unfused(xs[i], ts[i], ys[i]) for i in range(nsets)]
+
+    if args.mode in ("fused-only", "unfused-only"):
+        fl = fused if args.mode == "fused-only" else unfused
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup + args.steps):
+                fl[i % nsets]()
+        torch.cuda.synchronize()
+        log(f"{args.mode}: {args.warmup + args.steps} launches done")
+        return 0
+
+    timer = time_eager if args.eager else time_graph
+    ms_fused = timer(fused, args.steps, args.warmup, torch, stream)
+    log(f"fused: {ms_fused * 1e3:.2f} us/layer")
+    ms_unfused = None
+    if not args.no_unfused:
+        ms_unfused = timer(unfused, args.steps, args.warmup, torch, stream)
+        log(f"unfused (DW + PW kernels): {ms_unfused * 1e3:.2f} us/layer")
+
+    # sanity: the timed path still matches the first output of an eager call
+    ref = mod.fused(xs[0]).double()
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].double(), ref), "graph replay output differs from eager"
+
+    us = ms_fused * 1e3
+    alg = plan.alg_bytes_fused
+    achieved = alg / (us * 1e-6) / 1e9
+    traffic = measured_traffic(wl.name, vname)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic}
+    out = {
+        "metric": "fused DW+PW us/layer and achieved HBM GB/s (% of peak) vs unfused, 1 MI355X",
+        "value": round(us, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_fused, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.description}", "N": wl.N, "H": wl.H,
+                   "W": wl.W, "C": wl.C, "K": wl.K, "stride": wl.stride,
+                   "kernel_variant": vname, "timing": "eager" if args.eager else "hip-graph",
+                   "buffer_sets": nsets},
+        "roofline": roofline,
+        "hbm_gbs": round(achieved, 1),
+        "hbm_pct_of_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "alg_bytes_fused": alg,
+        "alg_bytes_unfused": plan.alg_bytes_unfused,
+    }
+    if ms_unfused is not None:
+        uu = ms_unfused * 1e3
+        out["unfused"] = {"value": round(uu, 3), "unit": "us/layer",
+                          "hbm_gbs": round(plan.alg_bytes_unfused / (uu * 1e-6) / 1e9, 1),
+                          "speedup_fused_over_unfused": round(uu / us, 3)}
+    if args.cpu_budget > 0:
+        cb = cpu_baseline(wl, args.cpu_budget)
+        out["cpu_baseline"] = cb
+        log(f"cpu oracle: {cb['value']} us/layer on {cb['cores']} threads")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

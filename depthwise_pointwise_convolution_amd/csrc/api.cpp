@@ -37,8 +37,9 @@ struct VariantImpl {
 };
 
 const VariantImpl kImpls[] = {
-#define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES) \
-    {launch_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES>, occ_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES>},
+#define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES, OCC)  \
+    {launch_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES, OCC>,          \
+     occ_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES, OCC>},
 #define FCM_V_DWPW32(name, S, TH, TW, KT, CC) \
     {launch_dwpw_f32<S, TH, TW, KT, CC>, occ_dwpw_f32<S, TH, TW, KT, CC>},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \

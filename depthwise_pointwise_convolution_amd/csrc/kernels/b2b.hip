@@ -73,6 +73,8 @@ __global__ __launch_bounds__(256) void b2b_mfma_kernel(KArgs a) {
     __shared__ float s1s[K1], b1s[K1], s2s[KT], b2s[KT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int lr = lane & 15, lg = lane >> 4;
     const int G = gridDim.x;
     const int L = xcd_logical_id(blockIdx.x, G);
@@ -132,8 +134,8 @@ __global__ __launch_bounds__(256) void b2b_mfma_kernel(KArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = lg * (K1 / 4) + ks2 * 8 + i;
-                    o[i] = epilogue(acc1[mi][2 * ks2][i], s1s[c], b1s[c], a.act1);
-                    o[4 + i] = epilogue(acc1[mi][2 * ks2 + 1][i], s1s[c + 4], b1s[c + 4], a.act1);
+                    o[i] = epilogue(acc1[mi][2 * ks2][i], s1s[c], b1s[c], act1);
+                    o[4 + i] = epilogue(acc1[mi][2 * ks2 + 1][i], s1s[c + 4], b1s[c + 4], act1);
                 }
                 b2f[ks2] = pack16<T>(o);
             }
@@ -156,9 +158,9 @@ __global__ __launch_bounds__(256) void b2b_mfma_kernel(KArgs a) {
                         float o[8];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            o[i] = epilogue(acc2[kb][i], s2s[kl + i], b2s[kl + i], a.act2);
+                            o[i] = epilogue(acc2[kb][i], s2s[kl + i], b2s[kl + i], act2);
                             o[4 + i] =
-                                epilogue(acc2[kb + 1][i], s2s[kl + 4 + i], b2s[kl + 4 + i], a.act2);
+                                epilogue(acc2[kb + 1][i], s2s[kl + 4 + i], b2s[kl + 4 + i], act2);
                         }
                         st16(yp + k0 + kl, pack16<T>(o));
                     }
@@ -180,6 +182,7 @@ __global__ __launch_bounds__(256) void conv_lbl_kernel(KArgs a) {
     __shared__ __attribute__((aligned(16))) T xs[IH * IW * XS];
     __shared__ float s1s[K1T], b1s[K1T];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int lr = lane & 15, lg = lane >> 4;
     const int b = blockIdx.x;
     const int k0 = (b % a.num_ktiles) * K1T;
@@ -222,9 +225,9 @@ __global__ __launch_bounds__(256) void conv_lbl_kernel(KArgs a) {
                     float o[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        o[i] = epilogue(acc[mi][kb][i], s1s[kl + i], b1s[kl + i], a.act1);
+                        o[i] = epilogue(acc[mi][kb][i], s1s[kl + i], b1s[kl + i], act1);
                         o[4 + i] = epilogue(acc[mi][kb + 1][i], s1s[kl + 4 + i], b1s[kl + 4 + i],
-                                            a.act1);
+                                            act1);
                     }
                     st16(tp + k0 + kl, pack16<T>(o));
                 }

@@ -43,13 +43,21 @@ __device__ __forceinline__ u32x4 pack16(const float* in) {
     return __builtin_bit_cast(u32x4, v);
 }
 
-// conv -> normalisation -> activation epilogue on one fp32 accumulator.
-// act: 0 none, 1 ReLU, 2 ReLU6.
-__device__ __forceinline__ float epilogue(float acc, float scale, float bias, int act) {
-    float v = __builtin_fmaf(scale, acc, bias);
-    if (act != 0) v = __builtin_fmaxf(v, 0.0f);
-    if (act == 2) v = __builtin_fminf(v, 6.0f);
-    return v;
+// Activation as a clamp to [lo, hi]: none (-inf, inf), ReLU (0, inf), ReLU6 (0, 6).
+struct Act {
+    float lo, hi;
+};
+__device__ __forceinline__ Act act_bounds(int act) {
+    Act a;
+    a.lo = act != 0 ? 0.0f : -__builtin_inff();
+    a.hi = act == 2 ? 6.0f : __builtin_inff();
+    return a;
+}
+
+// conv -> normalisation -> activation epilogue on one fp32 accumulator: one fused
+// multiply-add and one median-of-three (the clamp), whatever the activation.
+__device__ __forceinline__ float epilogue(float acc, float scale, float bias, Act act) {
+    return __builtin_amdgcn_fmed3f(__builtin_fmaf(scale, acc, bias), act.lo, act.hi);
 }
 
 // D(16x16 fp32) += A(16x32) * B(32x16) on the matrix cores.  Lane l supplies row

@@ -24,8 +24,9 @@
 
 namespace fcm {
 
-template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES>
-__global__ __launch_bounds__(256) void dwpw_mfma_kernel(KArgs a) {
+template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void dwpw_mfma_kernel(KArgs a) {
     constexpr int NT = 256;
     constexpr int VN = Vec<T>::N;
     static_assert(VN == 8, "matrix-core path is for 16-bit storage types");
@@ -45,6 +46,7 @@ __global__ __launch_bounds__(256) void dwpw_mfma_kernel(KArgs a) {
     __shared__ __attribute__((aligned(16))) float s2s[KT], b2s[KT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int lr = lane & 15, lg = lane >> 4;
     const int G = gridDim.x;
     const int L = xcd_logical_id(blockIdx.x, G);
@@ -54,6 +56,24 @@ __global__ __launch_bounds__(256) void dwpw_mfma_kernel(KArgs a) {
     const T* __restrict__ wdw = (const T*)a.w1;
     const T* __restrict__ wpw = (const T*)a.w2;
     T* __restrict__ y = (T*)a.y;
+    const int per_img = a.tiles_h * a.tiles_w;
+    const int nchunks = (a.C + CC - 1) / CC;
+
+    // the first tile's input is requested before anything else
+    HaloTile<T, IH, IW, CC, NT> halo;
+    int pt = L / a.num_ktiles;
+    auto tile_origin = [&](int t, int* n, int* oh0, int* ow0) {
+        *n = t / per_img;
+        const int rem = t - *n * per_img;
+        const int th = rem / a.tiles_w;
+        *oh0 = th * TH;
+        *ow0 = (rem - th * a.tiles_w) * TW;
+    };
+    if (pt < a.num_ptiles) {
+        int n, oh0, ow0;
+        tile_origin(pt, &n, &oh0, &ow0);
+        halo.load(x, a, n, oh0 * S - a.pad_h, ow0 * S - a.pad_w, 0, tid);
+    }
 
     for (int i = tid; i < KT; i += NT) {
         const int k = k0 + i;
@@ -73,25 +93,36 @@ __global__ __launch_bounds__(256) void dwpw_mfma_kernel(KArgs a) {
         stage_dw_weights<T, CC, NT>(wdw_s, s1s, b1s, wdw, a, 0, tid);
     }
 
-    const int per_img = a.tiles_h * a.tiles_w;
-    for (int pt = L / a.num_ktiles; pt < a.num_ptiles; pt += pstep) {
-        const int n = pt / per_img;
-        const int rem = pt - n * per_img;
-        const int th = rem / a.tiles_w, tw = rem - th * a.tiles_w;
-        const int oh0 = th * TH, ow0 = tw * TW;
+    for (; pt < a.num_ptiles; pt += pstep) {
+        int n, oh0, ow0;
+        tile_origin(pt, &n, &oh0, &ow0);
         f32x4 acc[MBW][KB];
 #pragma unroll
         for (int mi = 0; mi < MBW; ++mi)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) acc[mi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        for (int c0 = 0; c0 < a.C; c0 += CC) {
-            stage_input<T, IH, IW, CC, XS, NT>(xs, x, a, n, oh0 * S - a.pad_h,
-                                               ow0 * S - a.pad_w, c0, tid);
+        for (int ci = 0; ci < nchunks; ++ci) {
+            const int c0 = ci * CC;
+            halo.template store<XS>(xs, tid);
             if constexpr (!WRES) stage_dw_weights<T, CC, NT>(wdw_s, s1s, b1s, wdw, a, c0, tid);
             __syncthreads();
+            // software pipelining: request the next chunk (or the next tile's first
+            // chunk) now; the loads stay in flight through this chunk's compute
+            {
+                int nt = pt, nc = c0 + CC;
+                if (nc >= a.C) {
+                    nt = pt + pstep;
+                    nc = 0;
+                }
+                if (nt < a.num_ptiles) {
+                    int nn, noh0, now0;
+                    tile_origin(nt, &nn, &noh0, &now0);
+                    halo.load(x, a, nn, noh0 * S - a.pad_h, now0 * S - a.pad_w, nc, tid);
+                }
+            }
             dw_stage<T, S, TH, TW, CC, XS, IW, VB, NT>(
-                xs, wdw_s, s1s, b1s, a.act1, tid, [&](int ohl, int col, int cg, u32x4 v) {
+                xs, wdw_s, s1s, b1s, act1, tid, [&](int ohl, int col, int cg, u32x4 v) {
                     st16(ts + (ohl * TW + col) * TS + cg * VN, v);
                 });
             __syncthreads();
@@ -115,10 +146,9 @@ __global__ __launch_bounds__(256) void dwpw_mfma_kernel(KArgs a) {
                     }
                 }
             }
-            // No barrier here: the next chunk's staging writes xs / wdw_s, which
-            // were last read before the barrier above, and ts is rewritten only
-            // after the next staging barrier, which every wave reaches only once
-            // it has finished reading ts.
+            // No barrier here: the next chunk's LDS stores (xs, wdw_s) target data last
+            // read before the barrier above, and ts is rewritten only after the next
+            // staging barrier, which a wave reaches only once it is done reading ts.
         }
 
 #pragma unroll
@@ -126,7 +156,7 @@ __global__ __launch_bounds__(256) void dwpw_mfma_kernel(KArgs a) {
             const int px = (wave + 4 * mi) * 16 + lr;
             const int oh = oh0 + px / TW, ow = ow0 + px % TW;
             if (oh < a.Ho && ow < a.Wo) {
-                T* yp = y + (((int64_t)n * a.Ho + oh) * a.Wo + ow) * a.K;
+                T* yp = y + (((int64_t)n * a.Ho + oh) * a.Wo + ow) * a.K + k0;
 #pragma unroll
                 for (int kb = 0; kb < KB; kb += 2) {
                     const int kl = lg * (KT / 4) + kb * 4;
@@ -134,11 +164,11 @@ __global__ __launch_bounds__(256) void dwpw_mfma_kernel(KArgs a) {
                         float o[8];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            o[i] = epilogue(acc[mi][kb][i], s2s[kl + i], b2s[kl + i], a.act2);
+                            o[i] = epilogue(acc[mi][kb][i], s2s[kl + i], b2s[kl + i], act2);
                             o[4 + i] = epilogue(acc[mi][kb + 1][i], s2s[kl + 4 + i],
-                                                b2s[kl + 4 + i], a.act2);
+                                                b2s[kl + 4 + i], act2);
                         }
-                        st16(yp + k0 + kl, pack16<T>(o));
+                        st16(yp + kl, pack16<T>(o));
                     }
                 }
             }
@@ -168,6 +198,8 @@ __global__ __launch_bounds__(256) void dwpw_f32_kernel(KArgs a) {
     __shared__ float s1s[CC], b1s[CC];
 
     const int tid = threadIdx.x;
+
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int G = gridDim.x;
     const int L = xcd_logical_id(blockIdx.x, G);
     const int k0 = (L % a.num_ktiles) * KT;
@@ -197,7 +229,7 @@ __global__ __launch_bounds__(256) void dwpw_f32_kernel(KArgs a) {
             stage_dw_weights<T, CC, NT>(wdw_s, s1s, b1s, wdw, a, c0, tid);
             __syncthreads();
             dw_stage<T, S, TH, TW, CC, XS, IW, VB, NT>(
-                xs, wdw_s, s1s, b1s, a.act1, tid, [&](int ohl, int col, int cg, u32x4 v) {
+                xs, wdw_s, s1s, b1s, act1, tid, [&](int ohl, int col, int cg, u32x4 v) {
                     float f[4];
                     unpack16<float>(v, f);
                     float* d = ts + (ohl * TW + col) * TS + cg * VN;
@@ -219,7 +251,7 @@ __global__ __launch_bounds__(256) void dwpw_f32_kernel(KArgs a) {
                 const int oh = oh0 + px / TW, ow = ow0 + px % TW;
                 if (oh < a.Ho && ow < a.Wo)
                     y[(((int64_t)n * a.Ho + oh) * a.Wo + ow) * a.K + k] =
-                        epilogue(acc[i], sc2, bi2, a.act2);
+                        epilogue(acc[i], sc2, bi2, act2);
             }
         }
     }
@@ -228,18 +260,18 @@ __global__ __launch_bounds__(256) void dwpw_f32_kernel(KArgs a) {
 // ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
-template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES>
+template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES, int OCC>
 int launch_dwpw_mfma(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((dwpw_mfma_kernel<T, S, TH, TW, KT, CC, WRES>), dim3(grid), dim3(256),
-                       0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((dwpw_mfma_kernel<T, S, TH, TW, KT, CC, WRES, OCC>), dim3(grid),
+                       dim3(256), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
-template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES>
+template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES, int OCC>
 int occ_dwpw_mfma() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, dwpw_mfma_kernel<T, S, TH, TW, KT, CC, WRES>, 256, 0) != hipSuccess)
+            &n, dwpw_mfma_kernel<T, S, TH, TW, KT, CC, WRES, OCC>, 256, 0) != hipSuccess)
         return 0;
     return n;
 }
@@ -260,9 +292,10 @@ int occ_dwpw_f32() {
 }
 
 // explicit instances of every DW->PW variant listed in variants.def
-#define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES)                                 \
-    template int launch_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES>(const KArgs&, int, void*); \
-    template int occ_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES>();
+#define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES, OCC)                \
+    template int launch_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES, OCC>(const KArgs&, int, \
+                                                                     void*);            \
+    template int occ_dwpw_mfma<CT, S, TH, TW, KT, CC, WRES, OCC>();
 #define FCM_V_DWPW32(name, S, TH, TW, KT, CC)                                  \
     template int launch_dwpw_f32<S, TH, TW, KT, CC>(const KArgs&, int, void*); \
     template int occ_dwpw_f32<S, TH, TW, KT, CC>();

@@ -25,6 +25,8 @@ __global__ __launch_bounds__(256) void dw_lbl_kernel(KArgs a) {
     __shared__ __attribute__((aligned(16))) float s1s[CC], b1s[CC];
 
     const int tid = threadIdx.x;
+
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int nchunks = (a.C + CC - 1) / CC;
     const int b = blockIdx.x;
     const int pt = b / nchunks, c0 = (b - pt * nchunks) * CC;
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(256) void dw_lbl_kernel(KArgs a) {
     stage_dw_weights<T, CC, NT>(wdw_s, s1s, b1s, (const T*)a.w1, a, c0, tid);
     __syncthreads();
     dw_stage<T, S, TH, TW, CC, XS, IW, VB, NT>(
-        xs, wdw_s, s1s, b1s, a.act1, tid, [&](int ohl, int col, int cg, u32x4 v) {
+        xs, wdw_s, s1s, b1s, act1, tid, [&](int ohl, int col, int cg, u32x4 v) {
             const int oh = oh0 + ohl, ow = ow0 + col, c = c0 + cg * VN;
             if (oh < a.Ho && ow < a.Wo && c < a.C)
                 st16(t + (((int64_t)n * a.Ho + oh) * a.Wo + ow) * a.C + c, v);
@@ -56,6 +58,7 @@ __global__ __launch_bounds__(256) void pw_lbl_kernel(KArgs a) {
     constexpr int KB = KT / 16;
     __shared__ float s2s[KT], b2s[KT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = (int64_t)a.N * a.Ho * a.Wo;
     const int b = blockIdx.x;
@@ -105,9 +108,9 @@ __global__ __launch_bounds__(256) void pw_lbl_kernel(KArgs a) {
                     float o[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        o[i] = epilogue(acc[mi][kb][i], s2s[kl + i], b2s[kl + i], a.act2);
+                        o[i] = epilogue(acc[mi][kb][i], s2s[kl + i], b2s[kl + i], act2);
                         o[4 + i] =
-                            epilogue(acc[mi][kb + 1][i], s2s[kl + 4 + i], b2s[kl + 4 + i], a.act2);
+                            epilogue(acc[mi][kb + 1][i], s2s[kl + 4 + i], b2s[kl + 4 + i], act2);
                     }
                     st16(y + m * a.K + k0 + kl, pack16<T>(o));
                 }
@@ -121,6 +124,7 @@ __global__ __launch_bounds__(256) void pw_lbl_kernel(KArgs a) {
 __global__ __launch_bounds__(256) void pw_lbl_f32_kernel(KArgs a) {
     static_assert(lbl::PW_KT32 * lbl::PW_MT32 == 256, "one output per thread");
     const int tid = threadIdx.x;
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int64_t M = (int64_t)a.N * a.Ho * a.Wo;
     const int kt = blockIdx.x % a.num_ktiles;
     const int64_t m = (int64_t)(blockIdx.x / a.num_ktiles) * lbl::PW_MT32 + tid / lbl::PW_KT32;
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(256) void pw_lbl_f32_kernel(KArgs a) {
     float acc = 0.0f;
     for (int c = 0; c < a.C; ++c) acc = __builtin_fmaf(t[c], w[c], acc);
     const float sc = a.s2 ? a.s2[k] : 1.0f, bi = a.b2 ? a.b2[k] : 0.0f;
-    ((float*)a.y)[m * a.K + k] = epilogue(acc, sc, bi, a.act2);
+    ((float*)a.y)[m * a.K + k] = epilogue(acc, sc, bi, act2);
 }
 
 // ------------------------------------------------------------------------------------

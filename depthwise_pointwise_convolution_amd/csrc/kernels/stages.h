@@ -9,40 +9,56 @@
 
 namespace fcm {
 
-// Copy the input halo tile of one channel chunk, global -> LDS.
+// The input halo tile of one channel chunk, global -> registers -> LDS.
 // LDS layout: [IH][IW][XS] storage elements (XS >= CC; the tail of each pixel is
-// padding that spreads the MFMA operand reads over the LDS banks).  Pixels outside
-// the image (the zero padding of the convolution) and channels >= C are written as
-// zeros.  Loads are 16-byte vectors along the contiguous channel dimension, all
-// issued before any LDS store.
+// padding that spreads the matrix-operand reads over the LDS banks).  Pixels outside
+// the image (the zero padding of the convolution) and channels >= C are zeros.
+// Loads are 16-byte vectors along the contiguous channel dimension; splitting the
+// load from the LDS store lets a kernel issue the next tile's loads early and keep
+// them in flight while it computes the current tile.
+template <typename T, int IH, int IW, int CC, int NT>
+struct HaloTile {
+    static constexpr int VN = Vec<T>::N;
+    static constexpr int CG = CC / VN;
+    static constexpr int TOTAL = IH * IW * CG;
+    static constexpr int ITERS = (TOTAL + NT - 1) / NT;
+    u32x4 val[ITERS];
+
+    __device__ __forceinline__ void load(const T* __restrict__ x, const KArgs& a, int n, int ih0,
+                                         int iw0, int c0, int tid) {
+        const T* xn = x + (int64_t)n * a.H * a.W * a.C;
+#pragma unroll
+        for (int i = 0; i < ITERS; ++i) {
+            const int v = tid + i * NT;
+            val[i] = u32x4{0u, 0u, 0u, 0u};
+            if (v < TOTAL) {
+                const int p = v / CG, cv = v - p * CG;
+                const int ihl = p / IW, iwl = p - ihl * IW;
+                const int ih = ih0 + ihl, iw = iw0 + iwl, c = c0 + cv * VN;
+                if ((unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W && c < a.C)
+                    val[i] = ld16(xn + (ih * a.W + iw) * a.C + c);
+            }
+        }
+    }
+    template <int XS>
+    __device__ __forceinline__ void store(T* xs, int tid) const {
+#pragma unroll
+        for (int i = 0; i < ITERS; ++i) {
+            const int v = tid + i * NT;
+            if (v < TOTAL) {
+                const int p = v / CG, cv = v - p * CG;
+                st16(xs + p * XS + cv * VN, val[i]);
+            }
+        }
+    }
+};
+
 template <typename T, int IH, int IW, int CC, int XS, int NT>
 __device__ __forceinline__ void stage_input(T* xs, const T* __restrict__ x, const KArgs& a,
                                             int n, int ih0, int iw0, int c0, int tid) {
-    constexpr int VN = Vec<T>::N;
-    constexpr int CG = CC / VN;
-    constexpr int TOTAL = IH * IW * CG;
-    constexpr int ITERS = (TOTAL + NT - 1) / NT;
-    u32x4 val[ITERS];
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-        const int v = tid + i * NT;
-        val[i] = u32x4{0u, 0u, 0u, 0u};
-        if (v < TOTAL) {
-            const int p = v / CG, cv = v - p * CG;
-            const int ihl = p / IW, iwl = p - ihl * IW;
-            const int ih = ih0 + ihl, iw = iw0 + iwl, c = c0 + cv * VN;
-            if ((unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W && c < a.C)
-                val[i] = ld16(x + (((int64_t)n * a.H + ih) * a.W + iw) * a.C + c);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-        const int v = tid + i * NT;
-        if (v < TOTAL) {
-            const int p = v / CG, cv = v - p * CG;
-            st16(xs + p * XS + cv * VN, val[i]);
-        }
-    }
+    HaloTile<T, IH, IW, CC, NT> h;
+    h.load(x, a, n, ih0, iw0, c0, tid);
+    h.template store<XS>(xs, tid);
 }
 
 // Depthwise weights of one chunk as fp32 [9][CC], plus epilogue-1 scale/bias.
@@ -72,7 +88,7 @@ __device__ __forceinline__ void stage_dw_weights(float* wdw_s, float* s1s, float
 template <typename T, int S, int TH, int TW, int CC, int XS, int IW, int VB, int NT,
           typename Sink>
 __device__ __forceinline__ void dw_stage(const T* xs, const float* wdw_s, const float* s1s,
-                                         const float* b1s, int act1, int tid, Sink sink) {
+                                         const float* b1s, Act act1, int tid, Sink sink) {
     constexpr int VN = Vec<T>::N;
     constexpr int CG = CC / VN;
     constexpr int NITEM = TW * (TH / VB) * CG;

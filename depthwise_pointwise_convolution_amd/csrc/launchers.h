@@ -7,9 +7,9 @@
 
 namespace fcm {
 
-template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES>
+template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES, int OCC>
 int launch_dwpw_mfma(const KArgs& a, int grid, void* stream);
-template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES>
+template <typename T, int S, int TH, int TW, int KT, int CC, bool WRES, int OCC>
 int occ_dwpw_mfma();
 
 template <int S, int TH, int TW, int KT, int CC>

@@ -34,11 +34,12 @@
 namespace fcm {
 
 const VariantDesc kVariants[] = {
-#define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES) \
-    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0},
-#define FCM_V_DWPW32(name, S, TH, TW, KT, CC) {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0},
+#define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES, OCC) \
+    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0, OCC},
+#define FCM_V_DWPW32(name, S, TH, TW, KT, CC) \
+    {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 1},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
-    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, K1},
+    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, K1, 1},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -220,7 +221,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     int vg = variant_vgpr_estimate(v);
     vg = (vg + 7) / 8 * 8;
     int occ_lds = lds > 0 ? d.lds_bytes_per_cu / lds : 8;
-    int occ_vgpr = d.vgprs_per_simd_lane / std::max(vg, 1);
+    int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ);
     int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd);
     if (lds > d.lds_bytes_per_wg) occ = 0;
     r.wgs_per_cu = occ;

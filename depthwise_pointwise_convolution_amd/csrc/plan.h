@@ -19,6 +19,7 @@ struct VariantDesc {
     int cc;      // input channels per LDS pass
     int wres;    // pointwise weights resident in registers
     int k1;      // back-to-back: intermediate channels compiled in (0 otherwise)
+    int occ;     // waves per SIMD the kernel is compiled to allow (register budget)
 };
 
 extern const VariantDesc kVariants[];

@@ -57,6 +57,8 @@ def _load():
             lib = ctypes.CDLL(LIB)
             dp = ctypes.POINTER(ctypes.c_double)
             i32, i64 = ctypes.c_int32, ctypes.c_int64
+            lib.fcm_oracle_threads.restype = ctypes.c_int
+            lib.fcm_oracle_threads.argtypes = []
             lib.fcm_oracle_round.restype = ctypes.c_double
             lib.fcm_oracle_round.argtypes = [ctypes.c_double, ctypes.c_int]
             lib.fcm_oracle_round_array.argtypes = [dp, i64, ctypes.c_int]
@@ -87,6 +89,11 @@ def _load():
             lib.fcm_oracle_b2b_at.restype = ctypes.c_int
             _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().fcm_oracle_threads())
 
 
 def _f64(a):
