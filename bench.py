@@ -139,6 +139,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="cfg2")
     ap.add_argument("--variant", type=int, default=None, help="force a fused kernel variant")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input/output buffer sets in rotation (0 = enough to exceed the "
+                         "Infinity Cache, so inputs stream from HBM)")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=8.0,
                     help="seconds of oracle time for the cpu_baseline leg (0 = skip)")
@@ -171,7 +174,7 @@ def main(argv=None) -> int:
     # buffer sets: enough that the rotation's footprint exceeds the Infinity Cache
     x0 = torch.from_numpy(inp["x"]).to(tdt).to(dev)
     set_bytes = plan.alg_bytes_fused + plan.workspace_bytes
-    nsets = max(2, -(-2 * MALL_BYTES // set_bytes))
+    nsets = args.sets if args.sets > 0 else max(2, -(-2 * MALL_BYTES // set_bytes))
     xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
     ys = [mod.new_output(dev) for _ in range(nsets)]
     ts = [torch.empty(mod.t_shape, dtype=tdt, device=dev) for _ in range(nsets)]

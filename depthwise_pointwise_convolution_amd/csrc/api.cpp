@@ -44,10 +44,13 @@ const VariantImpl kImpls[] = {
     {launch_dwpw_f32<S, TH, TW, KT, CC>, occ_dwpw_f32<S, TH, TW, KT, CC>},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
     {launch_b2b_mfma<CT, S, TH, TW, K1, KT, CC>, occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>},
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, DWL, OCC) \
+    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, DWL, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, DWL, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
+#undef FCM_V_DWPW_MM
 };
 static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
 
@@ -155,15 +158,10 @@ fcm_status launch_fused(const fcm_plan_t* plan, KArgs& a, void* stream) {
     set_tiles(&a, v.th, v.tw, v.kt, plan->prob.K);
     int cus = 0, per_cu = 0;
     FCM_TRY(device_capacity(plan->variant, &cus, &per_cu));
-    // persistent grid: never more workgroups than tiles or than the GPU holds at once,
-    // a multiple of the output-channel tile count (each workgroup keeps one slice)
-    int64_t grid = plan->grid;
-    const int64_t work = (int64_t)a.num_ptiles * a.num_ktiles;
-    grid = std::min<int64_t>(grid, work);
-    grid = std::min<int64_t>(grid, (int64_t)cus * per_cu);
-    grid = std::max<int64_t>(grid / a.num_ktiles, 1) * a.num_ktiles;
-    const int64_t unit = (int64_t)a.num_ktiles * 8;
-    if (grid >= unit) grid = grid / unit * unit;
+    // persistent grid within what the GPU holds at once (measured occupancy) and the
+    // plan's own grid
+    const int64_t cap = std::min<int64_t>(plan->grid, (int64_t)cus * per_cu);
+    const int64_t grid = persistent_grid(a.num_ptiles, a.num_ktiles, cap);
     const int rc = kImpls[plan->variant].launch(a, (int)grid, stream);
     if (rc != 0)
         return fail(FCM_ERR_HIP, std::string("kernel launch failed: ") +

@@ -300,9 +300,11 @@ int occ_dwpw_f32() {
     template int launch_dwpw_f32<S, TH, TW, KT, CC>(const KArgs&, int, void*); \
     template int occ_dwpw_f32<S, TH, TW, KT, CC>();
 #define FCM_V_B2B(...)
+#define FCM_V_DWPW_MM(...)
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
+#undef FCM_V_DWPW_MM
 
 }  // namespace fcm

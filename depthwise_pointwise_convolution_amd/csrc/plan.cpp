@@ -35,15 +35,18 @@ namespace fcm {
 
 const VariantDesc kVariants[] = {
 #define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES, OCC) \
-    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0, OCC},
+    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0, 0, OCC},
 #define FCM_V_DWPW32(name, S, TH, TW, KT, CC) \
-    {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 1},
+    {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 0, 1},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
-    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, K1, 1},
+    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, 0, K1, 1},
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, DWL, OCC) \
+    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, DWL ? 0 : 1, 0, OCC},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
+#undef FCM_V_DWPW_MM
 };
 const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -79,6 +82,24 @@ double eq1_overlap(int chw, int chh, int tilew, int tileh, int filt, int stride)
 
 }  // namespace
 
+// A multiple of ktiles (a workgroup keeps one output-channel slice for all its tiles),
+// of 8 * ktiles once that large (the same share for every XCD), never above capacity
+// (a workgroup that has to wait for a free slot doubles the run time), and balanced:
+// every workgroup gets the same number of tiles up to one.
+int64_t persistent_grid(int64_t ptiles, int ktiles, int64_t capacity) {
+    const int64_t work = ptiles * ktiles;
+    capacity = std::max<int64_t>(capacity, ktiles);
+    int64_t g = std::min(work, capacity);
+    g = cdiv(work, cdiv(work, g));
+    auto fit = [&](int64_t q) {
+        const int64_t up = cdiv(g, q) * q;
+        return up <= capacity ? up : std::max<int64_t>(g / q, 1) * q;
+    };
+    g = fit(ktiles);
+    if (g >= 8 * (int64_t)ktiles) g = fit(8 * (int64_t)ktiles);
+    return g;
+}
+
 int variant_lds_bytes(const VariantDesc& v) {
     const int e = elem_bytes(v.dtype);
     const int IH = (v.th - 1) * v.stride + 3, IW = (v.tw - 1) * v.stride + 3;
@@ -89,6 +110,15 @@ int variant_lds_bytes(const VariantDesc& v) {
                2 * v.kt * 4;
     case VK_DWPW32:
         return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 1) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4;
+    case VK_DWPW_MM: {
+        // input tile (one buffer), intermediate tile, LDS copy of the depthwise
+        // matrix operand (when not rebuilt in registers), epilogue-1 arrays, filters
+        const int slots = IH * IW * (v.cc / 8);
+        const int slots_p = (slots + 255) / 256 * 256;
+        const int tls = v.th * (v.cc / 32) * 64 * 16;
+        const int dwf = v.dwr ? 0 : (v.cc / 16) * 5 * 64 * 16;
+        return slots_p * 16 + tls + dwf + 2 * v.cc * 4 + 9 * v.cc * e;
+    }
     default:
         return IH * IW * (v.cc + 8) * e + 2 * v.k1 * 4 + 2 * v.kt * 4;
     }
@@ -107,6 +137,16 @@ int variant_vgpr_estimate(const VariantDesc& v) {
     }
     case VK_DWPW32:
         return 64 + P * v.kt / 256 + 24;
+    case VK_DWPW_MM: {
+        // per wave: pointwise operands of its KT/4 output channels, their epilogue
+        // constants, the depthwise operand words (when rebuilt in registers), the
+        // direct-load plan, accumulators and addressing
+        const int ncb = v.cc / 16, nks = v.cc / 32, kbw = v.kt / 64;
+        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * (v.cc / 8);
+        (void)MBW;
+        return 32 + nks * kbw * 4 + v.kt / 8 + (v.dwr ? ncb * 5 : 0) + 2 * ((slots + 255) / 256) +
+               kbw * 4 + 16;
+    }
     default: {
         const int KB1 = v.k1 / 16, KB2 = v.kt / 16, KS2 = v.k1 / 32;
         return 40 + MBW * KB1 * 4 + KS2 * KB2 * 4 + KB2 * 4 + MBW * 4 + 24;
@@ -181,7 +221,8 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
     const int want = p.kind == FCM_KIND_B2B ? VK_B2B : (p.dtype == FCM_F32 ? VK_DWPW32 : VK_DWPW);
-    if (v.vkind != want || v.dtype != p.dtype) {
+    const int kind = v.vkind == VK_DWPW_MM ? VK_DWPW : v.vkind;
+    if (kind != want || v.dtype != p.dtype) {
         if (why) *why = "variant is for another module kind or storage type";
         return false;
     }
@@ -192,6 +233,20 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
     if (v.wres && v.vkind == VK_DWPW && p.C > v.cc) {
         if (why) *why = "register-resident pointwise weights need C <= channel chunk";
         return false;
+    }
+    if (v.vkind == VK_DWPW_MM) {
+        if (p.C > v.cc) {
+            if (why) *why = "matrix-core depthwise variant needs C <= its channel chunk";
+            return false;
+        }
+        const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
+        const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
+        const int64_t e = p.dtype == FCM_F32 ? 4 : 2;
+        if ((int64_t)p.H * p.W * p.C * e >= ((int64_t)1 << 31) ||
+            (int64_t)Ho * Wo * p.K * e >= ((int64_t)1 << 31)) {
+            if (why) *why = "one image's feature maps must stay below 2 GiB";
+            return false;
+        }
     }
     if (v.vkind == VK_B2B && p.K1 > v.k1) {
         if (why) *why = "variant is compiled for fewer intermediate channels";
@@ -229,10 +284,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     const int64_t ptiles = (int64_t)p.N * tiles_h * tiles_w;
     const int ktiles = (int)cdiv(p.K, v.kt);
     r.num_tiles = (int)std::min<int64_t>(ptiles * ktiles, INT32_MAX);
-    int64_t grid = std::min<int64_t>(ptiles * ktiles, (int64_t)d.num_cus * std::max(occ, 1));
-    grid = std::max<int64_t>(grid / ktiles, 1) * ktiles;
-    const int64_t unit = (int64_t)ktiles * 8;
-    if (grid >= unit) grid = grid / unit * unit;
+    const int64_t grid = persistent_grid(ptiles, ktiles, (int64_t)d.num_cus * std::max(occ, 1));
     r.grid = (int)grid;
 
     const int64_t halo = halo_pixels(Ho, Wo, p.H, p.W, v.th, v.tw, p.stride_h, p.pad_h, p.pad_w);
@@ -247,7 +299,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     if (v.vkind == VK_B2B) {
         // 3x3 filters are streamed for every tile, 1x1 filters stay in registers
         w_reads = (int64_t)r.num_tiles * w1_bytes + grid * (w2_slice + epi);
-    } else if (v.wres) {
+    } else if (v.wres || v.vkind == VK_DWPW_MM) {
         w_reads = grid * (w2_slice + w1_bytes + epi);
     } else {
         w_reads = (int64_t)r.num_tiles * (w2_slice + w1_bytes) + grid * epi;
@@ -266,18 +318,27 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     const double pad_px = (double)tiles_h * v.th * tiles_w * v.tw / ((double)Ho * Wo);
     const double alg = (double)p.N * p.H * p.W * p.C * e + (double)y_bytes + (double)w1_bytes +
                        (double)p.K * n1 * e;
+    // vector work in lane-operations per output pixel (fma + clamp + conversion per
+    // epilogue value; 9 multiply-adds per depthwise value on the vector path; 5 mask
+    // operations per value when the depthwise matrix operand is rebuilt each use);
+    // matrix work as executed (the block-diagonal depthwise product runs at 1/16 of
+    // the dense rate: 5 16x16x32 instructions per 16 channels x 16 pixels)
+    const double lane_ops_per_s = d.valu_f32_flops / 2.0;
     double t_mat, t_vec;
+    const double epi_ops = 3.0 * ((double)n1 * ktiles + p.K);
     if (v.vkind == VK_B2B) {
         t_mat = 2.0 * P * pad_px * ((double)v.k1 * 9 * p.C * ktiles + (double)v.k1 * p.K) /
                 d.mfma_f16_flops;
-        t_vec = 0.0;
+        t_vec = P * pad_px * epi_ops / lane_ops_per_s;
     } else if (v.vkind == VK_DWPW) {
         t_mat = 2.0 * P * pad_px * (double)p.C * p.K / d.mfma_f16_flops;
-        t_vec = 2.0 * 9 * P * pad_px * (double)p.C * ktiles / d.valu_f32_flops;
+        t_vec = P * pad_px * (9.0 * p.C * ktiles + epi_ops) / lane_ops_per_s;
+    } else if (v.vkind == VK_DWPW_MM) {
+        t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * v.cc * ktiles) / d.mfma_f16_flops;
+        t_vec = P * pad_px * (epi_ops + (v.dwr ? 0.0 : 5.0 * v.cc * ktiles)) / lane_ops_per_s;
     } else {
         t_mat = 0.0;
-        t_vec = (2.0 * 9 * P * pad_px * (double)p.C * ktiles + 2.0 * P * pad_px * p.C * p.K) /
-                d.valu_f32_flops;
+        t_vec = P * pad_px * (9.0 * p.C * ktiles + (double)p.C * p.K + epi_ops) / lane_ops_per_s;
     }
     const double t_hbm = alg / d.hbm_bytes_per_s;
     const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);

@@ -7,7 +7,7 @@
 
 namespace fcm {
 
-enum VKind { VK_DWPW = 0, VK_DWPW32 = 1, VK_B2B = 2 };
+enum VKind { VK_DWPW = 0, VK_DWPW32 = 1, VK_B2B = 2, VK_DWPW_MM = 3 };
 
 struct VariantDesc {
     const char* name;
@@ -18,6 +18,7 @@ struct VariantDesc {
     int kt;      // output channels per workgroup
     int cc;      // input channels per LDS pass
     int wres;    // pointwise weights resident in registers
+    int dwr;     // depthwise matrix operand resident in registers (matrix-core DW only)
     int k1;      // back-to-back: intermediate channels compiled in (0 otherwise)
     int occ;     // waves per SIMD the kernel is compiled to allow (register budget)
 };
@@ -27,6 +28,9 @@ extern const int kNumVariants;
 
 // LDS bytes and a per-lane VGPR estimate of one workgroup of variant v.
 int variant_lds_bytes(const VariantDesc& v);
+// Workgroup count of a persistent launch over ptiles pixel tiles x ktiles output-
+// channel tiles when the GPU holds `capacity` workgroups at once.
+int64_t persistent_grid(int64_t ptiles, int ktiles, int64_t capacity);
 int variant_vgpr_estimate(const VariantDesc& v);
 
 // Checks every field of the problem (see fcm_plan in fcm.h for the rules).
