@@ -72,6 +72,14 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("linking libfcm.so failed:\n" + r.stdout + r.stderr)
+    # a kernel template whose host launch stub was never emitted leaves an undefined
+    # symbol that only fails when the library is loaded: refuse such a link here
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    r = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "fcm" in l]
+    if r.returncode != 0 or missing:
+        os.remove(tmp)
+        raise RuntimeError("libfcm.so would have undefined symbols: " + " ".join(missing[:8]))
     os.replace(tmp, LIB)
     return LIB
 

@@ -44,8 +44,8 @@ const VariantImpl kImpls[] = {
     {launch_dwpw_f32<S, TH, TW, KT, CC>, occ_dwpw_f32<S, TH, TW, KT, CC>},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
     {launch_b2b_mfma<CT, S, TH, TW, K1, KT, CC>, occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>},
-#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, DWL, OCC) \
-    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, DWL, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, DWL, OCC>},
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
+    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32

@@ -43,6 +43,16 @@ __device__ __forceinline__ u32x4 pack16(const float* in) {
     return __builtin_bit_cast(u32x4, v);
 }
 
+// Round four fp32 values to a 16-bit storage type and pack 8 bytes.
+template <typename T>
+__device__ __forceinline__ uint2 pack8(const float* in) {
+    static_assert(sizeof(T) == 2, "8-byte packs of four 16-bit values");
+    vec_t<T, 4> v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (T)in[i];
+    return __builtin_bit_cast(uint2, v);
+}
+
 // Activation as a clamp to [lo, hi]: none (-inf, inf), ReLU (0, inf), ReLU6 (0, 6).
 struct Act {
     float lo, hi;

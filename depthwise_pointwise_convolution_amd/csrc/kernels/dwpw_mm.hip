@@ -33,16 +33,22 @@
 // The intermediate thus lives only in LDS (the commBuffer of the page's design) and
 // never reaches HBM.
 //
-// Input tiles arrive by direct global->LDS loads (buffer_load_dwordx4 ... lds): the
-// next tile's halo is requested as soon as phase A of the current tile has finished
-// reading the input buffer, so it streams in during phase B.  Out-of-image pixels (the
-// zero padding) come back as zeros from the buffer resource's range check.  Each
-// pixel's 16-byte channel chunks are XOR-swizzled so the 16 lanes of an operand read
-// (16 consecutive pixels, same chunk) hit distinct LDS banks.  Outputs are written
-// with buffer stores whose out-of-range lanes are dropped by the same range check, so
-// every wave issues the same number of memory instructions per tile and the wait for
-// the next tile's input can count them exactly (gfx9 vector memory operations
-// complete in issue order).
+// The two phases are software-pipelined over a workgroup's tiles with one barrier per
+// step: step i runs phase A of tile i+1 and phase B of tile i (two input tile buffers,
+// two intermediate buffers), so the matrix products of one phase interleave with the
+// vector epilogue of the other, and tile i+2's input is requested at the start of the
+// step and has a whole step to arrive.
+//
+// Input tiles arrive by direct global->LDS loads (buffer_load_dwordx4 ... lds).
+// Out-of-image pixels (the zero padding) come back as zeros from the buffer resource's
+// range check.  Each pixel's 16-byte channel chunks are XOR-swizzled so the 16 lanes of
+// an operand read (16 consecutive pixels, same chunk) hit distinct LDS banks.  Outputs
+// are written with buffer stores whose out-of-range lanes are dropped by the same range
+// check, so every wave issues the same number of memory instructions per step and the
+// wait for the next tile's input can count them exactly (gfx9 vector memory operations
+// complete in issue order).  Per-lane offsets are fixed for the whole kernel; the
+// tile's position enters as a scalar offset, so interior tiles need no per-lane
+// address arithmetic at all.
 #include <type_traits>
 
 #include "stages.h"
@@ -66,13 +72,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 constexpr uint32_t kOob = 0x80000000u;  // byte offset beyond any range: load 0 / drop
 
+// A tile's image, tile row and tile column, and the byte offsets derived from them:
+// input window origin (may be negative at the top/left border) and output tile origin,
+// both from the start of the whole tensor.
+struct TilePos {
+    int n, th, tw;
+    int ih0, iw0, oh0, ow0;
+    int in_base, out_base;
+};
+
 }  // namespace mm
 
-template <typename T, int S, int TH, int TW, int KT, int CC, bool DWL, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CC, int OCC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void dwpw_mm_kernel(KArgs a) {
     constexpr int NT = 256;
-    static_assert(TH == 4 && TW == 16, "one 16-pixel output row per wave");
+    static_assert(TH == 4 && TW == 16, "4 rows of 16 pixels per tile");
     constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3, NPIX = IH * IW;
     constexpr int CH = CC / 8;  // 16-byte chunks per pixel
     static_assert(CH == 8 || CH == 16, "swizzle needs 8 or 16 chunks per pixel");
@@ -80,17 +95,26 @@ void dwpw_mm_kernel(KArgs a) {
     constexpr int R = (SLOTS + NT - 1) / NT;  // direct-load rounds per tile
     constexpr int SLOTS_P = R * NT;
     constexpr int NCB = CC / 16, NKS = CC / 32, NTP = 5;
-    constexpr int KW = KT / 4;    // output channels per wave
+    constexpr int CBW = NCB / 4;  // depthwise channel blocks per wave
+    static_assert(NCB % 4 == 0, "each wave owns whole channel blocks");
+    constexpr int KW = KT / 4;    // pointwise output channels per wave
     constexpr int KBW = KW / 16;  // 16-channel output blocks per wave
-    static_assert(KT % 64 == 0, "each wave owns whole 16-channel output blocks");
-    constexpr int NST = TH * (KBW / 2);  // buffer stores per lane per tile
-    static_assert(KBW % 2 == 0 && NST < 64, "store count");
+    static_assert(KT % 128 == 0, "each wave stores 16-byte runs of 8 output channels");
+    constexpr int NST = TH * (KBW / 2);  // buffer stores per lane per step
+    static_assert(NST < 64, "vmcnt range");
+    constexpr uint32_t ROW_BYTES = (uint32_t)S * IW * CH * 16;  // one output row down
 
-    __shared__ __attribute__((aligned(16))) u32x4 xs[SLOTS_P];                 // input tile
-    __shared__ __attribute__((aligned(16))) u32x4 tls[TH * NKS * 64];          // intermediate
-    __shared__ __attribute__((aligned(16))) u32x4 dwf[DWL ? NCB * NTP * 64 : 1];  // DW operand
-    __shared__ __attribute__((aligned(16))) float s1s[CC], b1s[CC];
-    __shared__ __attribute__((aligned(16))) T dws[9 * CC];
+    // separate arrays per buffer: the compiler then sees that reading one buffer does
+    // not depend on the direct loads still in flight into the other
+    __shared__ __attribute__((aligned(16))) u32x4 xs0[SLOTS_P];
+    __shared__ __attribute__((aligned(16))) u32x4 xs1[SLOTS_P];
+    __shared__ __attribute__((aligned(16))) u32x4 tl0[TH * NKS * 64];
+    __shared__ __attribute__((aligned(16))) u32x4 tl1[TH * NKS * 64];
+    // the lambdas below see the buffers through these pointers
+    u32x4* const X0 = xs0;
+    u32x4* const X1 = xs1;
+    u32x4* const T0 = tl0;
+    u32x4* const T1 = tl1;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -99,78 +123,150 @@ void dwpw_mm_kernel(KArgs a) {
     const int L = xcd_logical_id(blockIdx.x, G);
     const int k0 = (L % a.num_ktiles) * KT;
     const int kw0 = k0 + wave * KW;  // this wave's output channels
-    const int pstep = G / a.num_ktiles;
-    const int per_img = a.tiles_h * a.tiles_w;
     const T* __restrict__ wdw = (const T*)a.w1;
     const T* __restrict__ wpw = (const T*)a.w2;
-    const uint32_t img_in_bytes = (uint32_t)(a.H * a.W * a.C) * (uint32_t)sizeof(T);
-    const uint32_t img_out_bytes = (uint32_t)(a.Ho * a.Wo * a.K) * (uint32_t)sizeof(T);
+    // one buffer resource per tensor (the host guarantees whole tensors below 2 GiB)
+    const int es = (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rx = mm::rsrc(a.x, (uint32_t)(a.N * a.H * a.W * a.C * es));
+    const __amdgpu_buffer_rsrc_t ry = mm::rsrc(a.y, (uint32_t)(a.N * a.Ho * a.Wo * a.K * es));
+    const int in_img = a.H * a.W * a.C * es, in_row = a.W * a.C * es;
+    const int out_img = a.Ho * a.Wo * a.K * es, out_row = a.Wo * a.K * es;
 
-    // ---- direct-load plan (tile invariant): slot -> source offset, window position ---
-    int dl_off[R], dl_pos[R];
+    // ---- tile walk: tiles pt0, pt0 + pstep, ... as (image, tile row, tile column),
+    // advanced by mixed-radix addition (no division inside the loop) -----------------
+    const int pstep = G / a.num_ktiles;
+    using Pos = mm::TilePos;
+    auto derive = [&](Pos& p) {
+        p.oh0 = p.th * TH;
+        p.ow0 = p.tw * TW;
+        p.ih0 = p.oh0 * S - a.pad_h;
+        p.iw0 = p.ow0 * S - a.pad_w;
+        p.in_base = p.n * in_img + p.ih0 * in_row + p.iw0 * a.C * es;
+        p.out_base = p.n * out_img + p.oh0 * out_row + p.ow0 * a.K * es;
+    };
+    auto split = [&](int t) {
+        Pos p;
+        const int per_img = a.tiles_h * a.tiles_w;
+        p.n = t / per_img;
+        const int rem = t - p.n * per_img;
+        p.th = rem / a.tiles_w;
+        p.tw = rem - p.th * a.tiles_w;
+        derive(p);
+        return p;
+    };
+    const Pos step = split(pstep);
+    auto advance = [&](Pos p) {
+        p.tw += step.tw;
+        if (p.tw >= a.tiles_w) {
+            p.tw -= a.tiles_w;
+            ++p.th;
+        }
+        p.th += step.th;
+        if (p.th >= a.tiles_h) {
+            p.th -= a.tiles_h;
+            ++p.n;
+        }
+        p.n += step.n;
+        derive(p);
+        return p;
+    };
+
+    // ---- direct-load plan (tile invariant) ---------------------------------------------
+    // LDS slot s holds chunk q of window pixel p = s / CH with s % CH = q ^ (column & 7):
+    // the 16 lanes of an operand read (consecutive columns, same chunk) then fall in
+    // distinct bank groups, and moving down a row moves every slot by a constant.
+    // dl_off: byte offset of the slot's source relative to the window origin (kOob for
+    // padding slots); dl_pos: the slot's window row and column.
+    uint32_t dl_off[R];
+    int dl_pos[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int s = r * NT + tid;
-        const int p = s / CH, qs = s % CH;
-        const int q = qs ^ (p & 7);
-        const int ihl = p / IW, iwl = p % IW;
-        dl_off[r] = (ihl * a.W + iwl) * a.C + q * 8;
-        dl_pos[r] = (s < SLOTS && q * 8 < a.C) ? (ihl << 16) | iwl : 0x7fff7fff;
+        const int p = s / CH, ihl = p / IW, iwl = p % IW;
+        const int q = (s % CH) ^ (iwl & 7);
+        const bool real = s < SLOTS && q * 8 < a.C;
+        dl_off[r] = real ? (uint32_t)((ihl * a.W + iwl) * a.C + q * 8) * (uint32_t)sizeof(T)
+                         : mm::kOob;
+        dl_pos[r] = real ? (ihl << 16) | iwl : 0;
     }
-    auto tile_origin = [&](int t, int* n, int* oh0, int* ow0) {
-        *n = t / per_img;
-        const int rem = t - *n * per_img;
-        const int th = rem / a.tiles_w;
-        *oh0 = th * TH;
-        *ow0 = (rem - th * a.tiles_w) * TW;
-    };
-    auto issue_tile = [&](int t) {
-        int n, oh0, ow0;
-        tile_origin(t, &n, &oh0, &ow0);
-        const T* img = (const T*)a.x + (int64_t)n * a.H * a.W * a.C;
-        const __amdgpu_buffer_rsrc_t rs = mm::rsrc(img, img_in_bytes);
-        const int ih0 = oh0 * S - a.pad_h, iw0 = ow0 * S - a.pad_w;
-        const int base = (ih0 * a.W + iw0) * a.C;
+    // The loads of one tile, always R per lane (a tile past the end loads nothing: every
+    // lane gets the out-of-range offset), so the wait counts below are exact.  A window
+    // inside the image needs no per-lane test: the window origin is a scalar offset.
+    auto issue_tile = [&](const Pos& t, auto buf) {
+        u32x4* dst = decltype(buf)::value == 0 ? X0 : X1;
+        const bool live = t.n < a.N;
+        const bool inside = live && t.ih0 >= 0 && t.iw0 >= 0 && t.ih0 + IH <= a.H &&
+                            t.iw0 + IW <= a.W;
+        if (inside) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int ih = ih0 + (dl_pos[r] >> 16), iw = iw0 + (dl_pos[r] & 0xffff);
-            const bool ok = (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
-            const uint32_t off = ok ? (uint32_t)(base + dl_off[r]) * (uint32_t)sizeof(T) : mm::kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void*)(xs + r * NT + wave * 64), 16, off, 0,
-                0, 0);
+            for (int r = 0; r < R; ++r) {
+                // (a copy: an element of the captured array passed straight to the
+                // builtin makes the host pass drop the kernel's launch stub)
+                const uint32_t off = dl_off[r];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(dst + r * NT + wave * 64), 16,
+                    off, t.in_base, 0, 0);
+            }
+        } else {
+            // border tile (or past the end): test every lane's pixel
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int ih = t.ih0 + (dl_pos[r] >> 16), iw = t.iw0 + (dl_pos[r] & 0xffff);
+                const bool ok = live && dl_off[r] != mm::kOob && (unsigned)ih < (unsigned)a.H &&
+                                (unsigned)iw < (unsigned)a.W;
+                const uint32_t off = ok ? (uint32_t)(t.in_base + (int)dl_off[r]) : mm::kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(dst + r * NT + wave * 64), 16,
+                    off, 0, 0, 0);
+            }
         }
     };
 
-    // ---- constants ---------------------------------------------------------------------
-    // depthwise filters [9][CC] and epilogue-1 arrays via LDS (one coalesced load)
-    {
-        constexpr int DI = (9 * CC + NT - 1) / NT;
-        T tmp[DI];
+    // ---- per-wave constants ----------------------------------------------------------
+    // depthwise: this wave owns channel blocks cb = wave + 4j.  Matrix operand of block
+    // cb and tap pair tp, lane (l%16, l/16): row = channel 16cb + l%16, reduction index
+    // 8(l/16) + e = (tap 2tp + (l/16)/2, channel 16cb + 8((l/16)&1) + e); non-zero only
+    // where that channel is the row's, i.e. one 16-bit element per lane.  The tenth tap
+    // of the last pair is empty (zero weights).
+    const bool dw_active = (lr >> 3) == (lg & 1);
+    const int dw_e = lr & 7;
+    uint32_t wdc[CBW][NTP];
+    float s1r[CBW][4], b1r[CBW][4];
 #pragma unroll
-        for (int i = 0; i < DI; ++i) {
-            const int v = tid + i * NT;
-            const int t = v / CC, c = v % CC;
-            const bool ok = v < 9 * CC && c < a.C;
-            const T val = wdw[ok ? t * a.C + c : 0];
-            tmp[i] = ok ? val : (T)0.0f;
+    for (int j = 0; j < CBW; ++j) {
+        const int cb = wave + 4 * j;
+#pragma unroll
+        for (int tp = 0; tp < NTP; ++tp) {
+            const int t = 2 * tp + (lg >> 1), c = cb * 16 + lr;
+            const bool ok = dw_active && t < 9 && c < a.C;
+            const uint16_t h = __builtin_bit_cast(uint16_t, wdw[ok ? t * a.C + c : 0]);
+            const uint32_t v = ok ? (uint32_t)h : 0u;
+            wdc[j][tp] = (dw_e & 1) ? (v << 16) : v;
         }
 #pragma unroll
-        for (int i = 0; i < DI; ++i) {
-            const int v = tid + i * NT;
-            if (v < 9 * CC) dws[v] = tmp[i];
+        for (int i = 0; i < 4; ++i) {
+            const int c = cb * 16 + lg * 4 + i;
+            const bool ok = c < a.C;
+            const float sv = a.s1 ? a.s1[ok ? c : 0] : 1.0f;
+            const float bv = a.b1 ? a.b1[ok ? c : 0] : 0.0f;
+            s1r[j][i] = ok ? sv : 1.0f;
+            b1r[j][i] = ok ? bv : 0.0f;
         }
-        for (int i = tid; i < CC; i += NT) {
-            const bool ok = i < a.C;
-            const float sv = a.s1 ? a.s1[ok ? i : 0] : 1.0f;
-            const float bv = a.b1 ? a.b1[ok ? i : 0] : 0.0f;
-            s1s[i] = ok ? sv : 1.0f;
-            b1s[i] = ok ? bv : 0.0f;
-        }
+    }
+    auto dw_operand = [&](uint32_t v) {
+        const int w = dw_e >> 1;
+        return u32x4{w == 0 ? v : 0u, w == 1 ? v : 0u, w == 2 ? v : 0u, w == 3 ? v : 0u};
+    };
+    // with one block per wave the expanded operands stay in registers for the whole
+    // kernel; with more they are expanded per block and step
+    u32x4 wdf[CBW == 1 ? NTP : 1];
+    if constexpr (CBW == 1) {
+#pragma unroll
+        for (int tp = 0; tp < NTP; ++tp) wdf[tp] = dw_operand(wdc[0][tp]);
     }
     // pointwise A operand of this wave's slice for reduction step ks, block kb: row
     // kperm<KW>(kb, l%16) of the slice, reduction channels 32ks + 4(l/16) + [0,4) and
-    // 32ks + 16 + 4(l/16) + [0,4) (the order the depthwise result arrives in)
+    // 32ks + 16 + 4(l/16) + [0,4) (the order the depthwise result is stored in)
     u32x4 wa[NKS][KBW];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -195,145 +291,163 @@ void dwpw_mm_kernel(KArgs a) {
         s2r[i] = ok ? sv : 1.0f;
         b2r[i] = ok ? bv : 0.0f;
     }
-    __syncthreads();  // dws / s1s / b1s visible
-    // depthwise A operand (block diagonal) for channel block cb, tap pair tp: row l%16
-    // = channel 16cb + l%16; reduction index 8(l/16) + j = (tap 2tp + (l/16)/2,
-    // channel 8((l/16)&1) + j); non-zero only where that channel is the row's.
-    const bool dw_active = (lr >> 3) == (lg & 1);
-    const int dw_j = lr & 7;
-    uint32_t dmask[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dmask[i] = (i == (dw_j >> 1)) ? 0xffffffffu : 0u;
-    auto dw_value = [&](int cb, int tp) -> uint32_t {
-        const int t = 2 * tp + (lg >> 1);
-        const uint16_t h = __builtin_bit_cast(uint16_t, dws[(t < 9 ? t : 0) * CC + cb * 16 + lr]);
-        const uint32_t v = (dw_active && t < 9) ? (uint32_t)h : 0u;
-        return (dw_j & 1) ? (v << 16) : v;
-    };
-    uint32_t wdc[DWL ? 1 : NCB][DWL ? 1 : NTP];
-    if constexpr (DWL) {
-        for (int f = wave; f < NCB * NTP; f += 4) {
-            const uint32_t v = dw_value(f / NTP, f % NTP);
-            dwf[f * 64 + lane] = u32x4{v & dmask[0], v & dmask[1], v & dmask[2], v & dmask[3]};
-        }
-    } else {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int tp = 0; tp < NTP; ++tp) wdc[cb][tp] = dw_value(cb, tp);
-    }
-    // LDS operand offsets of this lane's pixel (tile invariant): pixel index x chunks
-    // and the chunk XOR of its swizzle, per tap pair; the 10th tap (tp 4, upper lanes)
-    // reads a valid slot and is zeroed
-    int xb_pix[NTP], xb_x[NTP];
-    bool xb_ok[NTP];
+    // LDS byte offsets of this lane's depthwise operand reads in output row 0, block
+    // cb = wave, per tap pair (row r adds r * ROW_BYTES, block cb + 4j adds 128j bytes:
+    // bit 3 of the chunk index is untouched by the swizzle).  The empty tenth tap
+    // reads the first tap's pixel (finite data times a zero weight).
+    uint32_t xoff[NTP];
 #pragma unroll
     for (int tp = 0; tp < NTP; ++tp) {
-        xb_ok[tp] = 2 * tp + (lg >> 1) < 9;
-        const int t = xb_ok[tp] ? 2 * tp + (lg >> 1) : 0;
-        const int p_in = (wave * S + t / 3) * IW + lr * S + t % 3;
-        xb_pix[tp] = p_in * CH;
-        xb_x[tp] = (lg & 1) ^ (p_in & 7);
+        const int t0 = 2 * tp + (lg >> 1), t = t0 < 9 ? t0 : 0;
+        const int col = lr * S + t % 3;
+        const int p = (t / 3) * IW + col;
+        const int q = 2 * wave + (lg & 1);
+        xoff[tp] = (uint32_t)(p * CH + (q ^ (col & 7))) * 16u;
     }
-    __syncthreads();  // dwf visible; every wave is past its reads of dws
+    const uint32_t tls_w = (uint32_t)lane * 16u + (uint32_t)(wave & 1) * 8u;
+    // store offset of the lane's first output channel within a pixel row of the tile
+    // (kOob when the channel does not exist); the pixel row enters as a scalar offset
+    const int kl = kw0 + lg * (KW / 4);
+    const uint32_t st_lane =
+        kl < a.K ? (uint32_t)(lr * a.K + kl) * (uint32_t)sizeof(T) : mm::kOob;
 
-    // ---- persistent tile loop -------------------------------------------------------------
-    int pt = L / a.num_ktiles;
-    if (pt < a.num_ptiles) issue_tile(pt);
-    bool first = true;
-    for (; pt < a.num_ptiles; pt += pstep) {
-        // this tile's input (issued before the previous tile's NST stores) has landed
-        if (first) mm::wait_vmcnt<0>(); else mm::wait_vmcnt<NST>();
-        first = false;
-        __builtin_amdgcn_s_barrier();  // xs complete; every wave is done reading tls
-        // phase A: depthwise on the matrix cores for this wave's 16-pixel row, epilogue
-        // 1, and the result -- already in pointwise operand order -- to tls
+    // phase A of one tile: depthwise on the matrix cores, this wave's channel blocks
+    // for all TH rows; epilogue 1; 8 bytes per lane into the intermediate tile, where
+    // they form half of a pointwise B operand
+    auto phase_a = [&](const u32x4* src, u32x4* dst, int salt) {
+        const char* xb = reinterpret_cast<const char*>(src);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int j = 0; j < CBW; ++j) {
+            u32x4 wf[NTP];
 #pragma unroll
             for (int tp = 0; tp < NTP; ++tp) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int cb = 2 * ks + h;
-                    u32x4 xb = xs[xb_pix[tp] + ((2 * cb) ^ xb_x[tp])];
-                    if (!xb_ok[tp]) xb = u32x4{0u, 0u, 0u, 0u};
-                    u32x4 wf;
-                    if constexpr (DWL) {
-                        wf = dwf[(cb * NTP + tp) * 64 + lane];
-                    } else {
-                        uint32_t v = wdc[cb][tp];
-                        asm volatile("" : "+v"(v));  // rebuilt per use, not hoisted
-                        wf = u32x4{v & dmask[0], v & dmask[1], v & dmask[2], v & dmask[3]};
-                    }
-                    d[h] = mfma<T>(wf, xb, d[h]);
+                if constexpr (CBW == 1) {
+                    wf[tp] = wdf[tp];
+                } else {
+                    // expanded per step: the empty statement takes a loop-variant input,
+                    // so the optimiser cannot hoist all blocks' expanded operands out of
+                    // the loop, while the scheduler may still move it
+                    uint32_t v = wdc[j][tp];
+                    asm("" : "+v"(v) : "s"(salt));
+                    wf[tp] = dw_operand(v);
                 }
             }
-            float o[8];
+            const int cb = wave + 4 * j;
+            // tap pairs outer, rows inner: TH independent accumulation chains, so a
+            // product never waits for the previous one of its own chain
+            f32x4 d[TH];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int c = (2 * ks + h) * 16 + lg * 4;
-                const f32x4 sc = *reinterpret_cast<const f32x4*>(s1s + c);
-                const f32x4 bi = *reinterpret_cast<const f32x4*>(b1s + c);
+            for (int r = 0; r < TH; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[4 * h + i] = epilogue(d[h][i], sc[i], bi[i], act1);
+            for (int tp = 0; tp < NTP; ++tp) {
+                u32x4 xv[TH];
+#pragma unroll
+                for (int r = 0; r < TH; ++r)
+                    xv[r] = *reinterpret_cast<const u32x4*>(xb + xoff[tp] + r * ROW_BYTES +
+                                                            j * 128);
+#pragma unroll
+                for (int r = 0; r < TH; ++r) d[r] = mfma<T>(wf[tp], xv[r], d[r]);
             }
-            tls[(wave * NKS + ks) * 64 + lane] = pack16<T>(o);
+#pragma unroll
+            for (int r = 0; r < TH; ++r) {
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = epilogue(d[r][i], s1r[j][i], b1r[j][i], act1);
+                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
+                                          ((r * NKS + (cb >> 1)) * 64) * 16 + tls_w) =
+                    pack8<T>(o);
+            }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's tls writes done
-        __builtin_amdgcn_s_barrier();       // tls complete; xs free
-        if (pt + pstep < a.num_ptiles) issue_tile(pt + pstep);
-        // phase B: pointwise on the matrix cores, this wave's KW output channels for all
-        // TH rows of the tile, epilogue 2, 16-byte stores (64 contiguous bytes per pixel
-        // per store instruction; out-of-range lanes dropped by the range check)
-        int n, oh0, ow0;
-        tile_origin(pt, &n, &oh0, &ow0);
-        const __amdgpu_buffer_rsrc_t ry =
-            mm::rsrc((const T*)a.y + (int64_t)n * a.Ho * a.Wo * a.K, img_out_bytes);
+    };
+    // phase B of one tile: pointwise on the matrix cores, this wave's KW output
+    // channels for all TH rows, epilogue 2, 16-byte stores; always NST stores per lane
+    // (rows or lanes outside the output get the out-of-range offset)
+    auto phase_b = [&](const u32x4* src, const Pos& t) {
+        u32x4 bfr[TH][NKS];
+#pragma unroll
+        for (int mb = 0; mb < TH; ++mb)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) bfr[mb][ks] = src[(mb * NKS + ks) * 64 + lane];
+        f32x4 acc[TH][KBW];
+#pragma unroll
+        for (int mb = 0; mb < TH; ++mb)
+#pragma unroll
+            for (int kb = 0; kb < KBW; ++kb) {
+                acc[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    acc[mb][kb] = mfma<T>(wa[ks][kb], bfr[mb][ks], acc[mb][kb]);
+            }
+        const uint32_t voff = t.ow0 + lr < a.Wo ? st_lane : mm::kOob;
 #pragma unroll
         for (int mb = 0; mb < TH; ++mb) {
-            f32x4 acc[KBW];
-#pragma unroll
-            for (int kb = 0; kb < KBW; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const u32x4 bfr = tls[(mb * NKS + ks) * 64 + lane];
-#pragma unroll
-                for (int kb = 0; kb < KBW; ++kb) acc[kb] = mfma<T>(wa[ks][kb], bfr, acc[kb]);
-            }
-            const int oh = oh0 + mb, ow = ow0 + lr;
-            const bool pix_ok = oh < a.Ho && ow < a.Wo;
+            const bool row_ok = t.oh0 + mb < a.Ho;
+            const uint32_t v = row_ok ? voff : mm::kOob;
+            const int srow = row_ok ? t.out_base + mb * out_row : 0;
 #pragma unroll
             for (int kb = 0; kb < KBW; kb += 2) {
                 float o[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    o[i] = epilogue(acc[kb][i], s2r[kb * 4 + i], b2r[kb * 4 + i], act2);
-                    o[4 + i] =
-                        epilogue(acc[kb + 1][i], s2r[kb * 4 + 4 + i], b2r[kb * 4 + 4 + i], act2);
+                    o[i] = epilogue(acc[mb][kb][i], s2r[kb * 4 + i], b2r[kb * 4 + i], act2);
+                    o[4 + i] = epilogue(acc[mb][kb + 1][i], s2r[kb * 4 + 4 + i],
+                                        b2r[kb * 4 + 4 + i], act2);
                 }
-                const int k = kw0 + lg * (KW / 4) + kb * 4;
-                const bool ok = pix_ok && k < a.K;
-                const uint32_t off =
-                    ok ? (uint32_t)((oh * a.Wo + ow) * a.K + k) * (uint32_t)sizeof(T) : mm::kOob;
-                __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, v + kb * 4 * sizeof(T),
+                                                       srow, 0);
             }
         }
+    };
+
+    // ---- software-pipelined tile loop -----------------------------------------------
+    // Step i (buffers P = i % 2): wait for tile i+1's input; barrier (all of phase A of
+    // tile i is in tls[P], nobody reads xs[P] or tls[1-P] any more); request tile i+2
+    // into xs[P]; phase A of tile i+1 (xs[1-P] -> tls[1-P]); phase B of tile i (tls[P]).
+    // Vector-memory operations issued after tile i+1's loads: none before step 0, the
+    // NST stores of step i-1 before step i.
+    Pos cur = split(L / a.num_ktiles);
+    Pos nxt = advance(cur);
+    issue_tile(cur, std::integral_constant<int, 0>{});
+    issue_tile(nxt, std::integral_constant<int, 1>{});
+    mm::wait_vmcnt<R>();
+    __builtin_amdgcn_s_barrier();
+    if (cur.n < a.N) phase_a(X0, T0, 0);
+    auto step_fn = [&](auto par, bool first) {
+        constexpr int P = decltype(par)::value;
+        if (first) mm::wait_vmcnt<0>(); else mm::wait_vmcnt<NST>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own intermediate writes done
+        __builtin_amdgcn_s_barrier();
+        const Pos nn = advance(nxt);
+        issue_tile(nn, std::integral_constant<int, P>{});
+        if (nxt.n < a.N) phase_a(P == 0 ? X1 : X0, P == 0 ? T1 : T0, nxt.tw);
+        phase_b(P == 0 ? T0 : T1, cur);
+        cur = nxt;
+        nxt = nn;
+    };
+    bool first = true;
+    while (cur.n < a.N) {
+        step_fn(std::integral_constant<int, 0>{}, first);
+        first = false;
+        if (cur.n >= a.N) break;
+        step_fn(std::integral_constant<int, 1>{}, false);
     }
+    // loads of tiles past the end may still be in flight into LDS: drain them before
+    // the workgroup's LDS can be handed to another workgroup
+    mm::wait_vmcnt<0>();
 }
 
-template <typename T, int S, int TH, int TW, int KT, int CC, bool DWL, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CC, int OCC>
 int launch_dwpw_mm(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((dwpw_mm_kernel<T, S, TH, TW, KT, CC, DWL, OCC>), dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL((dwpw_mm_kernel<T, S, TH, TW, KT, CC, OCC>), dim3(grid), dim3(256), 0,
                        (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
-template <typename T, int S, int TH, int TW, int KT, int CC, bool DWL, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CC, int OCC>
 int occ_dwpw_mm() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, dwpw_mm_kernel<T, S, TH, TW, KT, CC, DWL, OCC>, 256, 0) != hipSuccess)
+            &n, dwpw_mm_kernel<T, S, TH, TW, KT, CC, OCC>, 256, 0) != hipSuccess)
         return 0;
     return n;
 }
@@ -341,9 +455,9 @@ int occ_dwpw_mm() {
 #define FCM_V_DWPW(...)
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
-#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, DWL, OCC)                           \
-    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, DWL, OCC>(const KArgs&, int, void*); \
-    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, DWL, OCC>();
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC)                              \
+    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>(const KArgs&, int, void*); \
+    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>();
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32

@@ -40,8 +40,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 0, 1},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
     {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, 0, K1, 1},
-#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, DWL, OCC) \
-    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, DWL ? 0 : 1, 0, OCC},
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
+    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -111,13 +111,11 @@ int variant_lds_bytes(const VariantDesc& v) {
     case VK_DWPW32:
         return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 1) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4;
     case VK_DWPW_MM: {
-        // input tile (one buffer), intermediate tile, LDS copy of the depthwise
-        // matrix operand (when not rebuilt in registers), epilogue-1 arrays, filters
+        // input tile buffers and as many intermediate tiles
         const int slots = IH * IW * (v.cc / 8);
         const int slots_p = (slots + 255) / 256 * 256;
         const int tls = v.th * (v.cc / 32) * 64 * 16;
-        const int dwf = v.dwr ? 0 : (v.cc / 16) * 5 * 64 * 16;
-        return slots_p * 16 + tls + dwf + 2 * v.cc * 4 + 9 * v.cc * e;
+        return v.nbuf * (slots_p * 16 + tls);
     }
     default:
         return IH * IW * (v.cc + 8) * e + 2 * v.k1 * 4 + 2 * v.kt * 4;
@@ -138,14 +136,14 @@ int variant_vgpr_estimate(const VariantDesc& v) {
     case VK_DWPW32:
         return 64 + P * v.kt / 256 + 24;
     case VK_DWPW_MM: {
-        // per wave: pointwise operands of its KT/4 output channels, their epilogue
-        // constants, the depthwise operand words (when rebuilt in registers), the
-        // direct-load plan, accumulators and addressing
-        const int ncb = v.cc / 16, nks = v.cc / 32, kbw = v.kt / 64;
+        // per wave: pointwise operands of its KT/4 output channels and their epilogue
+        // constants, its depthwise operands and epilogue-1 constants, the direct-load
+        // plan, accumulators, staging and addressing
+        const int cbw = v.cc / 64, nks = v.cc / 32, kbw = v.kt / 64;
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * (v.cc / 8);
         (void)MBW;
-        return 32 + nks * kbw * 4 + v.kt / 8 + (v.dwr ? ncb * 5 : 0) + 2 * ((slots + 255) / 256) +
-               kbw * 4 + 16;
+        return nks * kbw * 4 + v.kt / 8 + (cbw == 1 ? 20 : cbw * 5 + 20) + cbw * 8 +
+               2 * ((slots + 255) / 256) + 16 + kbw * 4 + 24 + 16;
     }
     default: {
         const int KB1 = v.k1 / 16, KB2 = v.kt / 16, KS2 = v.k1 / 32;
@@ -242,9 +240,9 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
         const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
         const int64_t e = p.dtype == FCM_F32 ? 4 : 2;
-        if ((int64_t)p.H * p.W * p.C * e >= ((int64_t)1 << 31) ||
-            (int64_t)Ho * Wo * p.K * e >= ((int64_t)1 << 31)) {
-            if (why) *why = "one image's feature maps must stay below 2 GiB";
+        if ((int64_t)p.N * p.H * p.W * p.C * e >= ((int64_t)1 << 31) ||
+            (int64_t)p.N * Ho * Wo * p.K * e >= ((int64_t)1 << 31)) {
+            if (why) *why = "matrix-core depthwise variant addresses whole tensors below 2 GiB";
             return false;
         }
     }
@@ -335,7 +333,9 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
         t_vec = P * pad_px * (9.0 * p.C * ktiles + epi_ops) / lane_ops_per_s;
     } else if (v.vkind == VK_DWPW_MM) {
         t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * v.cc * ktiles) / d.mfma_f16_flops;
-        t_vec = P * pad_px * (epi_ops + (v.dwr ? 0.0 : 5.0 * v.cc * ktiles)) / lane_ops_per_s;
+        // operand expansion when a wave owns several depthwise channel blocks
+        t_vec = P * pad_px * (epi_ops + (v.cc > 64 ? 1.25 * v.cc * ktiles : 0.0)) /
+                lane_ops_per_s;
     } else {
         t_mat = 0.0;
         t_vec = P * pad_px * (9.0 * p.C * ktiles + (double)p.C * p.K + epi_ops) / lane_ops_per_s;

@@ -18,7 +18,7 @@ struct VariantDesc {
     int kt;      // output channels per workgroup
     int cc;      // input channels per LDS pass
     int wres;    // pointwise weights resident in registers
-    int dwr;     // depthwise matrix operand resident in registers (matrix-core DW only)
+    int nbuf;    // input tile buffers in LDS (matrix-core DW only)
     int k1;      // back-to-back: intermediate channels compiled in (0 otherwise)
     int occ;     // waves per SIMD the kernel is compiled to allow (register budget)
 };
