@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MALL_BYTES = 256 * 1024 * 1024   # Infinity Cache
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["depthwise_pointwise_convolution_amd/csrc/kernels/dwpw.hip",
+KERNEL_SOURCES = ["depthwise_pointwise_convolution_amd/csrc/kernels/dwpw_mm.hip",
+                  "depthwise_pointwise_convolution_amd/csrc/kernels/dwpw.hip",
                   "depthwise_pointwise_convolution_amd/csrc/kernels/stages.h",
                   "depthwise_pointwise_convolution_amd/csrc/kernels/common.h",
                   "depthwise_pointwise_convolution_amd/csrc/variants.def"]
@@ -138,6 +139,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="cfg2")
     ap.add_argument("--variant", type=int, default=None, help="force a fused kernel variant")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="use the analytic plan instead of the measured choice (fcm_tune)")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--sets", type=int, default=0,
                     help="input/output buffer sets in rotation (0 = enough to exceed the "
@@ -167,22 +170,28 @@ def main(argv=None) -> int:
     wl = fcm_inputs.WORKLOADS[args.workload]
     inp = fcm_inputs.make_inputs(wl)
     mod = from_workload(wl, inp, device=dev, variant=args.variant)
-    plan = mod.plan
     tdt = TORCH_DTYPES[wl.dtype]
-    vname = fcm_variant_name(plan.variant)
 
     # buffer sets: enough that the rotation's footprint exceeds the Infinity Cache
     x0 = torch.from_numpy(inp["x"]).to(tdt).to(dev)
-    set_bytes = plan.alg_bytes_fused + plan.workspace_bytes
+    set_bytes = mod.plan.alg_bytes_fused + mod.plan.workspace_bytes
     nsets = args.sets if args.sets > 0 else max(2, -(-2 * MALL_BYTES // set_bytes))
     xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
     ys = [mod.new_output(dev) for _ in range(nsets)]
     ts = [torch.empty(mod.t_shape, dtype=tdt, device=dev) for _ in range(nsets)]
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
+    if args.variant is None and not args.no_tune and args.mode != "copy":
+        # measured choice of variant and grid (untimed, before the benchmark proper)
+        with torch.cuda.stream(stream):
+            mod.tune(x0, ys[0], iters=20, stream=stream)
+        torch.cuda.synchronize()
+    plan = mod.plan
+    vname = fcm_variant_name(plan.variant)
     log(f"workload {wl.name}: {wl.description}")
-    log(f"variant {plan.variant} {vname}, grid {plan.grid}, {nsets} buffer sets "
-        f"({nsets * set_bytes / 2**20:.0f} MiB rotation)")
+    log(f"variant {plan.variant} {vname}, grid {plan.grid}"
+        + (f" (tuned: {plan.tuned_us:.2f} us)" if plan.tuned_us > 0 else " (analytic plan)")
+        + f", {nsets} buffer sets ({nsets * set_bytes / 2**20:.0f} MiB rotation)")
 
     if args.mode == "copy":
         # plain copy of known size for counter calibration
@@ -241,7 +250,9 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.description}", "N": wl.N, "H": wl.H,
                    "W": wl.W, "C": wl.C, "K": wl.K, "stride": wl.stride,
-                   "kernel_variant": vname, "timing": "eager" if args.eager else "hip-graph",
+                   "kernel_variant": vname, "grid": plan.grid,
+                   "selection": "measured (fcm_tune)" if plan.tuned_us > 0 else "analytic plan",
+                   "timing": "eager" if args.eager else "hip-graph",
                    "buffer_sets": nsets},
         "roofline": roofline,
         "hbm_gbs": round(achieved, 1),

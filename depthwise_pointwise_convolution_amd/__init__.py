@@ -29,7 +29,7 @@ FCM_OK, FCM_ERR_INVALID_ARG, FCM_ERR_UNSUPPORTED, FCM_ERR_HIP = 0, 1, 2, 3
 FCM_F32, FCM_F16, FCM_BF16 = 0, 1, 2
 FCM_ACT_NONE, FCM_ACT_RELU, FCM_ACT_RELU6 = 0, 1, 2
 FCM_KIND_DWPW, FCM_KIND_B2B = 0, 1
-FCM_PLAN_VERSION = 1
+FCM_PLAN_VERSION = 2
 
 DTYPE_CODES = {"f32": FCM_F32, "f16": FCM_F16, "bf16": FCM_BF16}
 ACT_CODES = {"none": FCM_ACT_NONE, "relu": FCM_ACT_RELU, "relu6": FCM_ACT_RELU6}
@@ -70,7 +70,8 @@ class fcm_plan_t(ctypes.Structure):
                 ("workspace_bytes", _i64), ("alg_bytes_fused", _i64),
                 ("alg_bytes_unfused", _i64), ("pred_bytes_fused", _i64),
                 ("pred_bytes_unfused", _i64), ("gma_paper_fused", _f64),
-                ("gma_paper_unfused", _f64), ("flops", _f64), ("pred_us_fused", _f64)]
+                ("gma_paper_unfused", _f64), ("flops", _f64), ("pred_us_fused", _f64),
+                ("tuned_us", _f64)]
 
     def as_dict(self) -> dict:
         d = {}
@@ -85,6 +86,7 @@ class fcm_plan_t(ctypes.Structure):
 # every symbol include/fcm.h declares
 EXPORTS = ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan", "fcm_plan_variant",
            "fcm_num_variants", "fcm_variant_name", "fcm_pack_weights", "fcm_dwpw_fwd",
+           "fcm_tune",
            "fcm_b2b_conv_fwd", "fcm_dw_fwd", "fcm_pw_fwd", "fcm_conv_fwd", "fcm_status_str",
            "fcm_last_error")
 
@@ -116,6 +118,8 @@ def lib() -> ctypes.CDLL:
             L.fcm_pack_weights.argtypes = [P(fcm_plan_t), vp, vp, vp, vp, vp]
             L.fcm_dwpw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
             L.fcm_b2b_conv_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
+            L.fcm_tune.argtypes = [P(fcm_problem), P(fcm_device_spec), vp, vp, fp, fp, vp, fp,
+                                   fp, vp, vp, _i32, P(fcm_plan_t)]
             L.fcm_dw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
             L.fcm_pw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
             L.fcm_conv_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
@@ -237,6 +241,16 @@ def fcm_b2b_conv_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y, stream=No
     _check(lib().fcm_b2b_conv_fwd(ctypes.byref(plan), _ptr(x), _ptr(w1), _ptr(scale1),
                                   _ptr(bias1), _ptr(w2), _ptr(scale2), _ptr(bias2), _ptr(y),
                                   _stream(stream)), "fcm_b2b_conv_fwd")
+
+
+def fcm_tune(prob, x, w1, scale1, bias1, w2, scale2, bias2, y, iters=20, spec=None,
+             stream=None) -> "fcm_plan_t":
+    out = fcm_plan_t()
+    _check(lib().fcm_tune(ctypes.byref(prob), ctypes.byref(spec) if spec else None, _ptr(x),
+                          _ptr(w1), _ptr(scale1), _ptr(bias1), _ptr(w2), _ptr(scale2),
+                          _ptr(bias2), _ptr(y), _stream(stream), int(iters), ctypes.byref(out)),
+           "fcm_tune")
+    return out
 
 
 def fcm_dw_fwd(plan, x, w_dw, scale1, bias1, t, stream=None):

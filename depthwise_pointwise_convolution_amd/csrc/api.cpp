@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -344,6 +345,78 @@ fcm_status fcm_b2b_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w
     a.b2 = bias2;
     a.y = y;
     return launch_fused(plan, a, stream);
+}
+
+fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, const void* x,
+                    const void* w1, const float* scale1, const float* bias1, const void* w2,
+                    const float* scale2, const float* bias2, void* y, void* stream,
+                    int32_t iters, fcm_plan_t* out) {
+    if (!out) return fail(FCM_ERR_INVALID_ARG, "plan output pointer is NULL");
+    if (iters <= 0) return fail(FCM_ERR_INVALID_ARG, "iters must be positive");
+    fcm_plan_t first;
+    FCM_TRY(fcm_plan(prob, spec, &first));  // validates the problem
+    auto run = [&](const fcm_plan_t* pl) {
+        return prob->kind == FCM_KIND_DWPW
+                   ? fcm_dwpw_fwd(pl, x, w1, scale1, bias1, w2, scale2, bias2, y, stream)
+                   : fcm_b2b_conv_fwd(pl, x, w1, scale1, bias1, w2, scale2, bias2, y, stream);
+    };
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return fail(FCM_ERR_HIP, "hipEventCreate failed");
+    }
+    fcm_status st = FCM_OK;
+    fcm_plan_t best = first;
+    double best_us = 0.0;
+    for (int v = 0; v < kNumVariants && st == FCM_OK; ++v) {
+        fcm_plan_t pv;
+        std::string err;
+        if (plan_problem(prob, spec, v, &pv, &err) != FCM_OK) continue;
+        const VariantDesc& vd = kVariants[v];
+        std::string why;
+        if (!variant_runs(vd, pv.prob, &why)) continue;
+        int cus = 0, per_cu = 0;
+        st = device_capacity(v, &cus, &per_cu);
+        if (st != FCM_OK) break;
+        const int64_t ptiles = (int64_t)prob->N * ((pv.Ho + vd.th - 1) / vd.th) *
+                               ((pv.Wo + vd.tw - 1) / vd.tw);
+        const int ktiles = (prob->K + vd.kt - 1) / vd.kt;
+        int64_t last_grid = -1;
+        for (int w = 1; w <= std::min(4, per_cu) && st == FCM_OK; ++w) {
+            const int64_t g = persistent_grid(ptiles, ktiles, (int64_t)cus * w);
+            if (g == last_grid) continue;
+            last_grid = g;
+            fcm_plan_t cand = pv;
+            cand.grid = (int32_t)g;
+            cand.wgs_per_cu = w;
+            for (int i = 0; i < 2 && st == FCM_OK; ++i) st = run(&cand);  // warm-up
+            if (st != FCM_OK) break;
+            if (hipEventRecord(e0, (hipStream_t)stream) != hipSuccess) {
+                st = fail(FCM_ERR_HIP, "hipEventRecord failed");
+                break;
+            }
+            for (int i = 0; i < iters && st == FCM_OK; ++i) st = run(&cand);
+            if (st != FCM_OK) break;
+            float ms = 0.f;
+            if (hipEventRecord(e1, (hipStream_t)stream) != hipSuccess ||
+                hipEventSynchronize(e1) != hipSuccess ||
+                hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+                st = fail(FCM_ERR_HIP, "timing events failed");
+                break;
+            }
+            const double us = 1e3 * ms / iters;
+            if (best_us == 0.0 || us < best_us) {
+                best_us = us;
+                best = cand;
+            }
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != FCM_OK) return st;
+    best.tuned_us = best_us;
+    *out = best;
+    return ok();
 }
 
 fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,

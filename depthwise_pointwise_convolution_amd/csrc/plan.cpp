@@ -83,21 +83,12 @@ double eq1_overlap(int chw, int chh, int tilew, int tileh, int filt, int stride)
 }  // namespace
 
 // A multiple of ktiles (a workgroup keeps one output-channel slice for all its tiles),
-// of 8 * ktiles once that large (the same share for every XCD), never above capacity
-// (a workgroup that has to wait for a free slot doubles the run time), and balanced:
-// every workgroup gets the same number of tiles up to one.
+// no more workgroups than tiles, and never above capacity: a workgroup that has to
+// wait for a free slot would run after all the others.
 int64_t persistent_grid(int64_t ptiles, int ktiles, int64_t capacity) {
     const int64_t work = ptiles * ktiles;
-    capacity = std::max<int64_t>(capacity, ktiles);
-    int64_t g = std::min(work, capacity);
-    g = cdiv(work, cdiv(work, g));
-    auto fit = [&](int64_t q) {
-        const int64_t up = cdiv(g, q) * q;
-        return up <= capacity ? up : std::max<int64_t>(g / q, 1) * q;
-    };
-    g = fit(ktiles);
-    if (g >= 8 * (int64_t)ktiles) g = fit(8 * (int64_t)ktiles);
-    return g;
+    const int64_t g = std::min(work, std::max<int64_t>(capacity, ktiles));
+    return std::max<int64_t>(g / ktiles, 1) * ktiles;
 }
 
 int variant_lds_bytes(const VariantDesc& v) {
@@ -276,6 +267,8 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     int occ_lds = lds > 0 ? d.lds_bytes_per_cu / lds : 8;
     int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ);
     int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd);
+    // the workgroups per CU the kernel's register allocation was tuned for
+    if (v.vkind == VK_DWPW_MM) occ = std::min(occ, v.occ);
     if (lds > d.lds_bytes_per_wg) occ = 0;
     r.wgs_per_cu = occ;
     const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);

@@ -9,7 +9,7 @@ from typing import Optional
 import torch
 
 from . import (fcm_b2b_conv_fwd, fcm_conv_fwd, fcm_dw_fwd, fcm_dwpw_fwd, fcm_pack_weights,
-               fcm_plan, fcm_plan_variant, fcm_pw_fwd, problem, FCM_KIND_B2B)
+               fcm_plan, fcm_plan_variant, fcm_pw_fwd, fcm_tune, problem, FCM_KIND_B2B)
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -47,6 +47,13 @@ class FcmModule:
         fn = fcm_b2b_conv_fwd if self.b2b else fcm_dwpw_fwd
         fn(self.plan, x, self.w1p, self.s1, self.b1, self.w2p, self.s2, self.b2, y, stream)
         return y
+
+    def tune(self, x, y=None, iters: int = 20, stream=None) -> None:
+        """Replace the plan by the fastest measured variant and grid (fcm_tune); the
+        packed weights serve every variant of the module kind."""
+        y = self.new_output(x.device) if y is None else y
+        self.plan = fcm_tune(self.prob, x, self.w1p, self.s1, self.b1, self.w2p, self.s2,
+                             self.b2, y, iters, stream=stream)
 
     def first_layer(self, x, t=None, stream=None) -> torch.Tensor:
         t = torch.empty(self.t_shape, dtype=self.tdtype, device=x.device) if t is None else t

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FCM_PLAN_VERSION 1
+#define FCM_PLAN_VERSION 2
 
 typedef enum {
     FCM_OK = 0,
@@ -123,6 +123,7 @@ typedef struct {
     double gma_paper_unfused; /* Eq. 2 + Eq. 3, bytes */
     double flops;             /* 2 * multiply-adds of both convolutions */
     double pred_us_fused;     /* roofline time model of the chosen variant, us */
+    double tuned_us;          /* fcm_tune: measured time of this plan, us (0 otherwise) */
 } fcm_plan_t;
 
 /* MI355X published figures; no HIP call (usable without a GPU). */
@@ -149,6 +150,21 @@ fcm_status fcm_plan(const fcm_problem* prob, const fcm_device_spec* spec, fcm_pl
  * UNSUPPORTED if that variant cannot run the problem. */
 fcm_status fcm_plan_variant(const fcm_problem* prob, const fcm_device_spec* spec,
                             int32_t variant, fcm_plan_t* out);
+
+/* Measured selection (the profiling step of the TVM conv2d profiler page: every
+ * candidate kernel is compiled once, run on the device, and the fastest is kept).
+ * Runs every fused variant able to take `prob`, at persistent grids of 1, 2, 3 and 4
+ * workgroups per CU (as far as its occupancy allows), `iters` times each on `stream`
+ * with the caller's tensors -- laid out as for fcm_dwpw_fwd / fcm_b2b_conv_fwd
+ * (weights packed by fcm_pack_weights); y is overwritten -- and writes the plan of
+ * the fastest to *out, with out->grid the chosen grid and out->tuned_us its mean
+ * time per call.  Synchronises `stream`.  Allocates no device memory.
+ * Errors: FCM_ERR_INVALID_ARG / FCM_ERR_UNSUPPORTED as fcm_plan and the *_fwd
+ * calls; FCM_ERR_HIP if a launch or an event fails. */
+fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, const void* x,
+                    const void* w1, const float* scale1, const float* bias1, const void* w2,
+                    const float* scale2, const float* bias2, void* y, void* stream,
+                    int32_t iters, fcm_plan_t* out);
 
 /* Number of fused kernel variants compiled into the library, and a short name for
  * one of them ("" if out of range). */

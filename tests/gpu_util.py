@@ -41,12 +41,16 @@ def oracle_rows(wl, inp, pix) -> np.ndarray:
     return fn(inp["x"], inp["w1"], inp["w2"], pix, **oracle_kwargs(wl, inp))
 
 
-def run_gpu(wl, inp, variant=None, path="fused"):
-    """Run the module on the GPU; returns the output as float64 numpy."""
+def run_gpu(wl, inp, variant=None, path="fused", tune=False):
+    """Run the module on the GPU; returns the output as float64 numpy.  With tune the
+    plan is first replaced by the measured choice (fcm_tune), as the benchmark does."""
     import torch
     from depthwise_pointwise_convolution_amd.module import TORCH_DTYPES, from_workload
     mod = from_workload(wl, inp, device="cuda", variant=variant)
     x = torch.from_numpy(inp["x"]).to(TORCH_DTYPES[wl.dtype]).cuda()
+    if tune:
+        mod.tune(x, iters=3)
+        torch.cuda.synchronize()
     y = mod.fused(x) if path == "fused" else mod.unfused(x)
     torch.cuda.synchronize()
     return y.double().cpu().numpy(), mod

