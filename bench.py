@@ -218,15 +218,15 @@ def main(argv=None) -> int:
     timer = time_eager if args.eager else time_graph
     ms_fused = timer(fused, args.steps, args.warmup, torch, stream)
     log(f"fused: {ms_fused * 1e3:.2f} us/layer")
+    # sanity: the replayed launches wrote what an eager call of the same plan writes
+    ref = mod.fused(xs[0]).double()
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].double(), ref), "graph replay output differs from eager"
     ms_unfused = None
     if not args.no_unfused:
         ms_unfused = timer(unfused, args.steps, args.warmup, torch, stream)
         log(f"unfused (DW + PW kernels): {ms_unfused * 1e3:.2f} us/layer")
 
-    # sanity: the timed path still matches the first output of an eager call
-    ref = mod.fused(xs[0]).double()
-    torch.cuda.synchronize()
-    assert torch.equal(ys[0].double(), ref), "graph replay output differs from eager"
 
     us = ms_fused * 1e3
     alg = plan.alg_bytes_fused
