@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused depthwise->pointwise module on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mbv1_f16_8x112x112_c64_k128]
 
 A step is one invocation of the fused DW->PW kernel (one layer) on one batch of the
 MobileNetV1-style block: DW 3x3 s1 p1 over C=64 + scale/bias/ReLU6, PW 64->128 +
@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MALL_BYTES = 256 * 1024 * 1024   # Infinity Cache
+COPY_BYTES = 256 * 1024 * 1024   # plain copy used to calibrate the byte counters
+COPY_STEPS = 5                   # copies a calibration run makes (--mode copy --steps 5)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["depthwise_pointwise_convolution_amd/csrc/kernels/dwpw_mm.hip",
                   "depthwise_pointwise_convolution_amd/csrc/kernels/dwpw.hip",
@@ -62,6 +64,50 @@ def measured_traffic(workload: str, variant: str):
     if t.get("kernel_source_sha") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def summarize_pmc(workload: str, kernel: str, last: int, fetch_csv: str, write_csv: str,
+                  copy_fetch_csv: str, copy_write_csv: str, copy_bytes: int) -> dict:
+    """HBM bytes per launch of `kernel` from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for a
+    plain copy of copy_bytes (read and written once).  Uses the last `last`
+    dispatches of the kernel (the timed ones)."""
+    import csv
+    import statistics as st
+
+    def rows(path, match):
+        out = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if match in r["Kernel_Name"]:
+                    out.append((int(r["Dispatch_Id"]), r["Counter_Name"],
+                                float(r["Counter_Value"]), r["Kernel_Name"]))
+        out.sort()
+        return out
+
+    def per_dispatch(path, match, counter, tail):
+        rs = [r for r in rows(path, match) if r[1] == counter]
+        rs = rs[-tail:] if tail else rs
+        if not rs:
+            raise SystemExit(f"no {counter} rows for {match!r} in {path}")
+        return st.median(v for _, _, v, _ in rs), rs[-1][3], len(rs)
+
+    fetch, kname, nf = per_dispatch(fetch_csv, kernel, "FETCH_SIZE", last)
+    write, _, nw = per_dispatch(write_csv, kernel, "WRITE_SIZE", last)
+    # the plain copies are the last COPY_STEPS copy dispatches of a --mode copy run
+    # (earlier ones are the smaller set-up copies)
+    cf, _, _ = per_dispatch(copy_fetch_csv, "copyBuffer", "FETCH_SIZE", COPY_STEPS)
+    cw, _, _ = per_dispatch(copy_write_csv, "copyBuffer", "WRITE_SIZE", COPY_STEPS)
+    k_fetch = copy_bytes / (cf * 1024.0)
+    k_write = copy_bytes / (cw * 1024.0)
+    read_b = fetch * 1024.0 * k_fetch
+    write_b = write * 1024.0 * k_write
+    return {"workload": workload, "kernel": kname, "dispatches": [nf, nw],
+            "fetch_kib": fetch, "write_kib": write, "copy_fetch_kib": cf, "copy_write_kib": cw,
+            "copy_bytes": copy_bytes, "scale_fetch": k_fetch, "scale_write": k_write,
+            "hbm_read_bytes_per_launch": int(read_b), "hbm_write_bytes_per_launch": int(write_b),
+            "hbm_bytes_per_launch": int(read_b + write_b),
+            "kernel_source_sha": kernel_source_hash()}
 
 
 def time_graph(fn_list, steps, warmup, torch, stream):
@@ -121,7 +167,7 @@ def cpu_baseline(wl, budget_s: float):
     t_all = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.dwpw(inp["x"], inp["w1"], inp["w2"], **kw)
+        (oracle.dwpw if wl.kind == "dwpw" else oracle.b2b)(inp["x"], inp["w1"], inp["w2"], **kw)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_all >= budget_s or len(times) >= 50:
             break
@@ -137,7 +183,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="cfg2")
+    ap.add_argument("--workload", default="mbv1_f16_8x112x112_c64_k128")
     ap.add_argument("--variant", type=int, default=None, help="force a fused kernel variant")
     ap.add_argument("--no-tune", action="store_true",
                     help="use the analytic plan instead of the measured choice (fcm_tune)")
@@ -151,7 +197,24 @@ def main(argv=None) -> int:
     ap.add_argument("--mode", default="bench", choices=["bench", "fused-only", "unfused-only",
                                                         "copy"],
                     help="profiling helpers: run only one path (or a plain copy) K times")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
+                                                          "COPY_WRITE"),
+                    help="write profiles/traffic_<variant>_<workload>.json from rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE csv files of --mode fused-only and "
+                         "--mode copy runs (no GPU needed)")
+    ap.add_argument("--kernel", default="dwpw_mm_kernel", help="kernel name for --summarize-pmc")
+    ap.add_argument("--variant-name", default=None, help="variant name for --summarize-pmc")
     args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        t = summarize_pmc(args.workload, args.kernel, args.steps, *args.summarize_pmc,
+                          copy_bytes=COPY_BYTES)
+        t["variant"] = args.variant_name
+        path = os.path.join(PROFILES, f"traffic_{args.variant_name}_{args.workload}.json")
+        with open(path, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the module shards "
@@ -195,7 +258,7 @@ def main(argv=None) -> int:
 
     if args.mode == "copy":
         # plain copy of known size for counter calibration
-        a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
+        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(args.steps):
             b.copy_(a)

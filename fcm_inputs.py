@@ -67,38 +67,38 @@ class Workload:
 
 
 WORKLOADS = {
-    "cfg1": Workload(
-        "cfg1", "dwpw", "f32", N=1, H=16, W=16, C=32, K=32, K1=32,
+    "tiny_f32_1x16x16_c32": Workload(
+        "tiny_f32_1x16x16_c32", "dwpw", "f32", N=1, H=16, W=16, C=32, K=32, K1=32,
         bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("uniform", -0.5, 0.5),
         bias_dist=("zero",), seed=1,
         description="DW 3x3 s1 p1 + PW 1x1, fp32, N=1 16x16 C=32 K=32, bias 0, "
                     "no activation"),
-    "cfg2": Workload(
-        "cfg2", "dwpw", "f16", N=8, H=112, W=112, C=64, K=128, K1=64,
+    "mbv1_f16_8x112x112_c64_k128": Workload(
+        "mbv1_f16_8x112x112_c64_k128", "dwpw", "f16", N=8, H=112, W=112, C=64, K=128, K1=64,
         act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
         x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=2,
         description="MobileNetV1-style block: DW 3x3 s1 C=64 + scale/bias+ReLU6, "
                     "PW 64->128 + scale/bias+ReLU6, fp16, N=8 112x112"),
-    "cfg3": Workload(
-        "cfg3", "dwpw", "bf16", N=256, H=32, W=32, C=128, K=128, K1=128,
+    "cifar_bf16_256x32x32_c128": Workload(
+        "cifar_bf16_256x32x32_c128", "dwpw", "bf16", N=256, H=32, W=32, C=128, K=128, K1=128,
         act2="relu", bias2=True, x_dist=("uniform", -1.0, 1.0),
         w_dist=("normal", 0.0, 0.05), bias_dist=("normal", 0.0, 0.05), seed=3,
         description="CIFAR-style DW+PW pair: DW 3x3 s1 groups=C + PW 128->128, bf16, "
                     "N=256 32x32, bias+ReLU after PW"),
-    "cfg4a": Workload(
-        "cfg4a", "dwpw", "f16", N=64, H=56, W=56, C=256, K=512, K1=256, stride=2,
+    "down_f16_64x56x56_c256_k512_s2": Workload(
+        "down_f16_64x56x56_c256_k512_s2", "dwpw", "f16", N=64, H=56, W=56, C=256, K=512, K1=256, stride=2,
         act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
         w_dist=("normal", 0.0, 0.05), seed=41,
         description="Downsampling FCM: DW 3x3 s2 C=256 + PW 256->512, scale/bias+ReLU6 "
                     "each, fp16, N=64 56x56 -> 28x28"),
-    "cfg4b": Workload(
-        "cfg4b", "dwpw", "f16", N=64, H=7, W=7, C=1024, K=1024, K1=1024,
+    "late_f16_64x7x7_c1024": Workload(
+        "late_f16_64x7x7_c1024", "dwpw", "f16", N=64, H=7, W=7, C=1024, K=1024, K1=1024,
         act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
         w_dist=("normal", 0.0, 0.05), seed=42,
         description="Late-stage FCM: DW 3x3 s1 C=1024 + PW 1024->1024, "
                     "scale/bias+ReLU6 each, fp16, N=64 7x7"),
-    "cfg5": Workload(
-        "cfg5", "b2b", "f16", N=32, H=56, W=56, C=64, K=64, K1=64,
+    "b2b_f16_32x56x56_c64": Workload(
+        "b2b_f16_32x56x56_c64", "b2b", "f16", N=32, H=56, W=56, C=64, K=64, K1=64,
         act1="relu", act2="relu", scale1=True, bias1=True, scale2=True, bias2=True,
         w_dist=("normal", 0.0, 0.05), seed=5,
         description="Back-to-back: conv 3x3 p1 64->64 + scale_bias_relu, conv 1x1 "

@@ -107,12 +107,12 @@ def all_variants_for(wl):
 
 REDUCED = {
     # ragged spatial tails (not multiples of the tiles) and several tiles per image
-    "cfg1": dict(),
-    "cfg2": dict(N=2, H=29, W=37),
-    "cfg3": dict(N=3),
-    "cfg4a": dict(N=2, H=57, W=45),
-    "cfg4b": dict(N=3),
-    "cfg5": dict(N=2, H=23, W=37),
+    "tiny_f32_1x16x16_c32": dict(),
+    "mbv1_f16_8x112x112_c64_k128": dict(N=2, H=29, W=37),
+    "cifar_bf16_256x32x32_c128": dict(N=3),
+    "down_f16_64x56x56_c256_k512_s2": dict(N=2, H=57, W=45),
+    "late_f16_64x7x7_c1024": dict(N=3),
+    "b2b_f16_32x56x56_c64": dict(N=2, H=23, W=37),
 }
 
 

@@ -151,8 +151,8 @@ def test_eq1_overlap_in_planner_units_matches_brute_force():
     # the paper-model estimate of the library must grow with the overlap term
     F = _lib()
     spec = _spec(F)
-    a = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["cfg2"]), spec)
-    b = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["cfg2"].replace(H=224, W=224)), spec)
+    a = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["mbv1_f16_8x112x112_c64_k128"]), spec)
+    b = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["mbv1_f16_8x112x112_c64_k128"].replace(H=224, W=224)), spec)
     assert b.gma_paper_fused > a.gma_paper_fused > 0
     assert a.gma_paper_unfused > a.gma_paper_fused
 
@@ -194,7 +194,7 @@ def test_forward_calls_reject_bad_arguments_before_any_hip_call():
     import ctypes
     F = _lib()
     L = F.lib()
-    wl = fcm_inputs.WORKLOADS["cfg2"]
+    wl = fcm_inputs.WORKLOADS["mbv1_f16_8x112x112_c64_k128"]
     pl = F.fcm_plan(_problem(F, wl), _spec(F))
     fake = ctypes.c_void_p(0x1000)          # aligned, never dereferenced on the host
     odd = ctypes.c_void_p(0x1002)           # not 16-byte aligned

@@ -136,7 +136,7 @@ def test_random_small_shapes(wl):
 def test_output_guard_bands_and_every_output_written():
     import torch
     from depthwise_pointwise_convolution_amd.module import from_workload
-    wl = reduced("cfg2")
+    wl = reduced("mbv1_f16_8x112x112_c64_k128")
     inp = fcm_inputs.make_inputs(wl)
     mod = from_workload(wl, inp)
     x = torch.from_numpy(inp["x"]).half().cuda()
@@ -154,7 +154,7 @@ def test_output_guard_bands_and_every_output_written():
 def test_repeated_runs_are_bitwise_identical():
     import torch
     from depthwise_pointwise_convolution_amd.module import from_workload
-    wl = fcm_inputs.WORKLOADS["cfg2"]
+    wl = fcm_inputs.WORKLOADS["mbv1_f16_8x112x112_c64_k128"]
     inp = fcm_inputs.make_inputs(wl)
     mod = from_workload(wl, inp)
     x = torch.from_numpy(inp["x"]).half().cuda()
@@ -167,7 +167,7 @@ def test_device_argument_errors_enqueue_nothing():
     import torch
     import depthwise_pointwise_convolution_amd as F
     from depthwise_pointwise_convolution_amd.module import from_workload
-    wl = reduced("cfg2")
+    wl = reduced("mbv1_f16_8x112x112_c64_k128")
     inp = fcm_inputs.make_inputs(wl)
     mod = from_workload(wl, inp)
     x = torch.from_numpy(inp["x"]).half().cuda()

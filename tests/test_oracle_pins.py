@@ -289,7 +289,7 @@ def test_diagonal_standard_conv_equals_depthwise():
 
 
 def test_sampled_rows_equal_full_outputs():
-    wl = fcm_inputs.WORKLOADS["cfg2"].replace(N=2, H=9, W=20)
+    wl = fcm_inputs.WORKLOADS["mbv1_f16_8x112x112_c64_k128"].replace(N=2, H=9, W=20)
     inp = fcm_inputs.make_inputs(wl)
     kw = dict(stride=(1, 1), pad=(1, 1), scale1=inp["scale1"], bias1=inp["bias1"],
               act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"], act2=wl.act2,
@@ -350,9 +350,9 @@ def test_accounting_of_the_five_workloads():
         assert s["x"] == wl.N * wl.H * wl.W * wl.C * e
         assert s["y"] == wl.N * wl.Ho * wl.Wo * wl.K * e
         assert accounting.alg_bytes(wl, False) - accounting.alg_bytes(wl, True) == 2 * s["t"]
-    assert accounting.alg_bytes(fcm_inputs.WORKLOADS["cfg1"]) == 70912
-    assert accounting.alg_bytes(fcm_inputs.WORKLOADS["cfg2"]) == 38554240
-    assert fcm_inputs.WORKLOADS["cfg4a"].Ho == 28
+    assert accounting.alg_bytes(fcm_inputs.WORKLOADS["tiny_f32_1x16x16_c32"]) == 70912
+    assert accounting.alg_bytes(fcm_inputs.WORKLOADS["mbv1_f16_8x112x112_c64_k128"]) == 38554240
+    assert fcm_inputs.WORKLOADS["down_f16_64x56x56_c256_k512_s2"].Ho == 28
 
 
 # ---------------------------------------------------------------------------------
