@@ -24,6 +24,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 SOURCES = [
     ("kernels/dwpw.hip", True),
     ("kernels/dwpw_mm.hip", True),
+    ("kernels/dwpw_mmc.hip", True),
     ("kernels/lbl.hip", True),
     ("kernels/b2b.hip", True),
     ("api.cpp", True),

@@ -47,11 +47,14 @@ const VariantImpl kImpls[] = {
     {launch_b2b_mfma<CT, S, TH, TW, K1, KT, CC>, occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>},
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
     {launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>},
+#define FCM_V_DWPW_MMC(name, dt, CT, S, KT, OCC) \
+    {launch_dwpw_mmc<CT, S, KT, OCC>, occ_dwpw_mmc<CT, S, KT, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
+#undef FCM_V_DWPW_MMC
 };
 static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
 

@@ -51,37 +51,10 @@
 // address arithmetic at all.
 #include <type_traits>
 
-#include "stages.h"
+#include "mm_common.h"
 
 namespace fcm {
 
-namespace mm {
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    // gfx9 raw buffer: stride 0, range check on `bytes`, dword3 = 0x00020000
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-constexpr uint32_t kOob = 0x80000000u;  // byte offset beyond any range: load 0 / drop
-
-// A tile's image, tile row and tile column, and the byte offsets derived from them:
-// input window origin (may be negative at the top/left border) and output tile origin,
-// both from the start of the whole tensor.
-struct TilePos {
-    int n, th, tw;
-    int ih0, iw0, oh0, ow0;
-    int in_base, out_base;
-};
-
-}  // namespace mm
 
 template <typename T, int S, int TH, int TW, int KT, int CC, int OCC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
@@ -455,6 +428,7 @@ int occ_dwpw_mm() {
 #define FCM_V_DWPW(...)
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
+#define FCM_V_DWPW_MMC(...)
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC)                              \
     template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>(const KArgs&, int, void*); \
     template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>();
@@ -463,5 +437,6 @@ int occ_dwpw_mm() {
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
+#undef FCM_V_DWPW_MMC
 
 }  // namespace fcm

@@ -42,11 +42,14 @@ const VariantDesc kVariants[] = {
     {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, 0, K1, 1},
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
     {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC},
+#define FCM_V_DWPW_MMC(name, dt, CT, S, KT, OCC) \
+    {#name, VK_DWPW_MMC, dt, S, 4, 16, KT, 64, 0, 2, 0, OCC},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
+#undef FCM_V_DWPW_MMC
 };
 const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -101,8 +104,9 @@ int variant_lds_bytes(const VariantDesc& v) {
                2 * v.kt * 4;
     case VK_DWPW32:
         return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 1) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4;
-    case VK_DWPW_MM: {
-        // input tile buffers and as many intermediate tiles
+    case VK_DWPW_MM:
+    case VK_DWPW_MMC: {
+        // input tile (or chunk) buffers and as many intermediate tiles
         const int slots = IH * IW * (v.cc / 8);
         const int slots_p = (slots + 255) / 256 * 256;
         const int tls = v.th * (v.cc / 32) * 64 * 16;
@@ -135,6 +139,14 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         (void)MBW;
         return nks * kbw * 4 + v.kt / 8 + (cbw == 1 ? 20 : cbw * 5 + 20) + cbw * 8 +
                2 * ((slots + 255) / 256) + 16 + kbw * 4 + 24 + 16;
+    }
+    case VK_DWPW_MMC: {
+        // per wave: accumulators and two sets of per-chunk pointwise operands of its
+        // KT/4 output channels, their epilogue constants, two sets of depthwise operands,
+        // the direct-load plan, staging and addressing
+        const int kbw = v.kt / 64;
+        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
+        return 16 * kbw + 16 * kbw + v.kt / 8 + 26 + 20 + 2 * ((slots + 255) / 256) + 32 + 24;
     }
     default: {
         const int KB1 = v.k1 / 16, KB2 = v.kt / 16, KS2 = v.k1 / 32;
@@ -210,7 +222,7 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
     const int want = p.kind == FCM_KIND_B2B ? VK_B2B : (p.dtype == FCM_F32 ? VK_DWPW32 : VK_DWPW);
-    const int kind = v.vkind == VK_DWPW_MM ? VK_DWPW : v.vkind;
+    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC) ? VK_DWPW : v.vkind;
     if (kind != want || v.dtype != p.dtype) {
         if (why) *why = "variant is for another module kind or storage type";
         return false;
@@ -223,9 +235,13 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         if (why) *why = "register-resident pointwise weights need C <= channel chunk";
         return false;
     }
-    if (v.vkind == VK_DWPW_MM) {
-        if (p.C > v.cc) {
+    if (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC) {
+        if (v.vkind == VK_DWPW_MM && p.C > v.cc) {
             if (why) *why = "matrix-core depthwise variant needs C <= its channel chunk";
+            return false;
+        }
+        if (v.vkind == VK_DWPW_MMC && p.C % 64 != 0) {
+            if (why) *why = "chunked matrix-core variant needs C a multiple of 64";
             return false;
         }
         const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
@@ -268,7 +284,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ);
     int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd);
     // the workgroups per CU the kernel's register allocation was tuned for
-    if (v.vkind == VK_DWPW_MM) occ = std::min(occ, v.occ);
+    if (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC) occ = std::min(occ, v.occ);
     if (lds > d.lds_bytes_per_wg) occ = 0;
     r.wgs_per_cu = occ;
     const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);
@@ -324,6 +340,11 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     } else if (v.vkind == VK_DWPW) {
         t_mat = 2.0 * P * pad_px * (double)p.C * p.K / d.mfma_f16_flops;
         t_vec = P * pad_px * (9.0 * p.C * ktiles + epi_ops) / lane_ops_per_s;
+    } else if (v.vkind == VK_DWPW_MMC) {
+        // block-diagonal depthwise products (320 flop-equivalents per channel and
+        // pixel) recomputed for every K tile
+        t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * p.C * ktiles) / d.mfma_f16_flops;
+        t_vec = P * pad_px * (epi_ops + 1.25 * p.C * ktiles) / lane_ops_per_s;
     } else if (v.vkind == VK_DWPW_MM) {
         t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * v.cc * ktiles) / d.mfma_f16_flops;
         // operand expansion when a wave owns several depthwise channel blocks
