@@ -25,6 +25,7 @@ SOURCES = [
     ("kernels/dwpw.hip", True),
     ("kernels/dwpw_mm.hip", True),
     ("kernels/dwpw_mmc.hip", True),
+    ("kernels/b2b_mm.hip", True),
     ("kernels/lbl.hip", True),
     ("kernels/b2b.hip", True),
     ("api.cpp", True),

@@ -49,12 +49,14 @@ const VariantImpl kImpls[] = {
     {launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>},
 #define FCM_V_DWPW_MMC(name, dt, CT, S, KT, OCC) \
     {launch_dwpw_mmc<CT, S, KT, OCC>, occ_dwpw_mmc<CT, S, KT, OCC>},
+#define FCM_V_B2B_MM(name, dt, CT, S, OCC) {launch_b2b_mm<CT, S, OCC>, occ_b2b_mm<CT, S, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
 #undef FCM_V_DWPW_MMC
+#undef FCM_V_B2B_MM
 };
 static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
 

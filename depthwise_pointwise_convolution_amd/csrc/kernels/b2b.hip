@@ -284,11 +284,13 @@ int launch_conv_lbl(int dtype, int stride, const KArgs& a, void* stream) {
     template int occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>();
 #define FCM_V_DWPW_MM(...)
 #define FCM_V_DWPW_MMC(...)
+#define FCM_V_B2B_MM(...)
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
 #undef FCM_V_DWPW_MMC
+#undef FCM_V_B2B_MM
 
 }  // namespace fcm

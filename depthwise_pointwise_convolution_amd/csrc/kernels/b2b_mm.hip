@@ -1,0 +1,317 @@
+// b2b_mm.hip -- back-to-back standard 3x3 conv -> 1x1 conv ("Fusing two back-to-back
+// convolutions": block-resident fusion, the second conv 1x1) for up to 64 channels in
+// each layer, both convolutions on the gfx950 matrix cores, with the input pipeline of
+// the matrix-core DW->PW kernel (dwpw_mm.hip): direct global->LDS loads of 4x16-pixel
+// tiles plus halo, XOR-swizzled chunks, two input and two intermediate buffers, one
+// barrier per software-pipelined step.
+//
+// Step s runs phase A of tile s+1 and phase B of tile s:
+//   phase A  the 3x3 conv as an implicit GEMM whose reduction index runs over (tap,
+//            32-channel half): 18 steps of v_mfma_f32_16x16x32.  Wave w owns
+//            intermediate channels [16w, 16w+16) of all 4 rows; its 18 filter operands
+//            stay in registers for the whole kernel (the "weights resident" end of the
+//            CUTLASS discussion's design space), the 16-pixel input operands are read
+//            from the LDS tile.  Epilogue 1, rounding, and 8 bytes per lane into the LDS
+//            intermediate tile in 1x1-operand order (the accumulator -> operand
+//            hand-off, through LDS because a wave holds only 16 of the 64 channels).
+//   phase B  the 1x1 conv: wave w owns output row w, all (up to 64) output channels,
+//            with resident filter operands; epilogue 2; two 16-byte stores per lane.
+#include <type_traits>
+
+#include "mm_common.h"
+
+namespace fcm {
+
+template <typename T, int S, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void b2b_mm_kernel(KArgs a) {
+    constexpr int NT = 256, TH = 4, TW = 16, CC = 64, K1T = 64, KT = 64;
+    constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3, NPIX = IH * IW;
+    constexpr int CH = CC / 8;
+    constexpr int SLOTS = NPIX * CH;
+    constexpr int R = (SLOTS + NT - 1) / NT;
+    constexpr int SLOTS_P = R * NT;
+    constexpr int NK1 = 18;              // reduction steps of the 3x3 conv: 9 taps x 2
+    constexpr int NKS2 = K1T / 32;       // reduction steps of the 1x1 conv
+    constexpr int KB2 = KT / 16;         // 16-channel output blocks of a wave's row
+    constexpr int NST = 2;               // stores per lane per step
+    constexpr uint32_t ROW_BYTES = (uint32_t)S * IW * CH * 16;
+
+    __shared__ __attribute__((aligned(16))) u32x4 xs0[SLOTS_P];
+    __shared__ __attribute__((aligned(16))) u32x4 xs1[SLOTS_P];
+    __shared__ __attribute__((aligned(16))) u32x4 tl0[TH * NKS2 * 64];
+    __shared__ __attribute__((aligned(16))) u32x4 tl1[TH * NKS2 * 64];
+    u32x4* const X0 = xs0;
+    u32x4* const X1 = xs1;
+    u32x4* const T0 = tl0;
+    u32x4* const T1 = tl1;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
+    const int G = gridDim.x;
+    const int L = xcd_logical_id(blockIdx.x, G);
+    const T* __restrict__ w1 = (const T*)a.w1;
+    const T* __restrict__ w2 = (const T*)a.w2;
+    const int es = (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rx = mm::rsrc(a.x, (uint32_t)(a.N * a.H * a.W * a.C * es));
+    const __amdgpu_buffer_rsrc_t ry = mm::rsrc(a.y, (uint32_t)(a.N * a.Ho * a.Wo * a.K * es));
+    const int in_img = a.H * a.W * a.C * es, in_row = a.W * a.C * es;
+    const int out_img = a.Ho * a.Wo * a.K * es, out_row = a.Wo * a.K * es;
+
+    // ---- tile walk (one output-channel tile: the grid is the pixel-tile step) --------
+    const int pstep = G;
+    using Pos = mm::TilePos;
+    auto derive = [&](Pos& p) {
+        p.oh0 = p.th * TH;
+        p.ow0 = p.tw * TW;
+        p.ih0 = p.oh0 * S - a.pad_h;
+        p.iw0 = p.ow0 * S - a.pad_w;
+        p.in_base = p.n * in_img + p.ih0 * in_row + p.iw0 * a.C * es;
+        p.out_base = p.n * out_img + p.oh0 * out_row + p.ow0 * a.K * es;
+    };
+    auto split = [&](int t) {
+        Pos p;
+        const int per_img = a.tiles_h * a.tiles_w;
+        p.n = t / per_img;
+        const int rem = t - p.n * per_img;
+        p.th = rem / a.tiles_w;
+        p.tw = rem - p.th * a.tiles_w;
+        derive(p);
+        return p;
+    };
+    const Pos step = split(pstep);
+    auto advance = [&](Pos p) {
+        p.tw += step.tw;
+        if (p.tw >= a.tiles_w) {
+            p.tw -= a.tiles_w;
+            ++p.th;
+        }
+        p.th += step.th;
+        if (p.th >= a.tiles_h) {
+            p.th -= a.tiles_h;
+            ++p.n;
+        }
+        p.n += step.n;
+        derive(p);
+        return p;
+    };
+
+    // ---- direct-load plan: slot s = chunk q of window pixel s / CH, s % CH = q ^ (col & 7)
+    uint32_t dl_off[R];
+    int dl_pos[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int s = r * NT + tid;
+        const int p = s / CH, ihl = p / IW, iwl = p % IW;
+        const int q = (s % CH) ^ (iwl & 7);
+        const bool real = s < SLOTS && q * 8 < a.C;
+        dl_off[r] = real ? (uint32_t)((ihl * a.W + iwl) * a.C + q * 8) * (uint32_t)es : mm::kOob;
+        dl_pos[r] = real ? (ihl << 16) | iwl : 0;
+    }
+    auto issue_tile = [&](const Pos& t, auto buf) {
+        u32x4* dst = decltype(buf)::value == 0 ? X0 : X1;
+        const bool live = t.n < a.N;
+        const bool inside = live && t.ih0 >= 0 && t.iw0 >= 0 && t.ih0 + IH <= a.H &&
+                            t.iw0 + IW <= a.W;
+        if (inside) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t off = dl_off[r];  // (a copy, see dwpw_mm.hip)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(dst + r * NT + wave * 64), 16,
+                    off, t.in_base, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int ih = t.ih0 + (dl_pos[r] >> 16), iw = t.iw0 + (dl_pos[r] & 0xffff);
+                const bool ok = live && dl_off[r] != mm::kOob && (unsigned)ih < (unsigned)a.H &&
+                                (unsigned)iw < (unsigned)a.W;
+                const uint32_t off = ok ? (uint32_t)(t.in_base + (int)dl_off[r]) : mm::kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(dst + r * NT + wave * 64), 16,
+                    off, 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- resident operands -------------------------------------------------------------
+    // 3x3 filters of intermediate channels [16w, 16w+16), packed [K1][9][C]: operand of
+    // reduction step ks = (tap ks/2, channel half ks%2), lane (l%16, l/16): channel
+    // 16w + l%16, input channels 32(ks%2) + 8(l/16) + [0,8)
+    u32x4 wa1[NK1];
+#pragma unroll
+    for (int ks = 0; ks < NK1; ++ks) {
+        const int k1 = 16 * wave + lr, t = ks >> 1, c = 32 * (ks & 1) + 8 * lg;
+        const bool ok = k1 < a.K1 && c < a.C;
+        const u32x4 v = ld16(w1 + ((int64_t)(ok ? k1 : 0) * 9 + t) * a.C + (ok ? c : 0));
+        wa1[ks] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+    float s1r[4], b1r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k1 = 16 * wave + 4 * lg + i;
+        const bool ok = k1 < a.K1;
+        const float sv = a.s1 ? a.s1[ok ? k1 : 0] : 1.0f;
+        const float bv = a.b1 ? a.b1[ok ? k1 : 0] : 0.0f;
+        s1r[i] = ok ? sv : 1.0f;
+        b1r[i] = ok ? bv : 0.0f;
+    }
+    // 1x1 filters, [K][K1]: operand of step ks2, block kb: row kperm<64>(kb, l%16),
+    // intermediate channels 32ks2 + 4(l/16) + [0,4) and 32ks2 + 16 + 4(l/16) + [0,4)
+    u32x4 wa2[NKS2][KB2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < NKS2; ++ks2)
+#pragma unroll
+        for (int kb = 0; kb < KB2; ++kb) {
+            const int ko = kperm<KT>(kb, lr), c = ks2 * 32 + lg * 4;
+            const bool ok_lo = ko < a.K && c < a.K1, ok_hi = ko < a.K && c + 16 < a.K1;
+            const T* row = w2 + (int64_t)(ko < a.K ? ko : 0) * a.K1;
+            const uint2 lo = *reinterpret_cast<const uint2*>(row + (ok_lo ? c : 0));
+            const uint2 hi = *reinterpret_cast<const uint2*>(row + (ok_hi ? c + 16 : 0));
+            wa2[ks2][kb] = u32x4{ok_lo ? lo.x : 0u, ok_lo ? lo.y : 0u, ok_hi ? hi.x : 0u,
+                                 ok_hi ? hi.y : 0u};
+        }
+    // epilogue-2 constants in LDS (read back four at a time per use: registers are
+    // the scarce resource of this kernel)
+    __shared__ __attribute__((aligned(16))) float s2s[KT], b2s[KT];
+    for (int k = tid; k < KT; k += NT) {
+        const bool ok = k < a.K;
+        const float sv = a.s2 ? a.s2[ok ? k : 0] : 1.0f;
+        const float bv = a.b2 ? a.b2[ok ? k : 0] : 0.0f;
+        s2s[k] = ok ? sv : 1.0f;
+        b2s[k] = ok ? bv : 0.0f;
+    }
+    const float* const S2 = s2s;
+    const float* const B2 = b2s;
+    // LDS byte offsets of the lane's 3x3 input operand in output row 0, per step
+    uint32_t xoff[NK1];
+#pragma unroll
+    for (int ks = 0; ks < NK1; ++ks) {
+        const int t = ks >> 1, col = lr * S + t % 3;
+        const int p = (t / 3) * IW + col;
+        const int q = 4 * (ks & 1) + lg;
+        xoff[ks] = (uint32_t)(p * CH + (q ^ (col & 7))) * 16u;
+    }
+    const uint32_t tls_w = (uint32_t)lane * 16u + (uint32_t)(wave & 1) * 8u;
+    // store offsets of the lane's two 8-channel runs within a pixel row (kOob when the
+    // run lies beyond K)
+    const uint32_t st0 = 16 * lg < a.K ? (uint32_t)(lr * a.K + 16 * lg) * (uint32_t)es : mm::kOob;
+    const uint32_t st1 =
+        16 * lg + 8 < a.K ? (uint32_t)(lr * a.K + 16 * lg + 8) * (uint32_t)es : mm::kOob;
+
+    auto phase_a = [&](const u32x4* src, u32x4* dst) {
+        const char* xb = reinterpret_cast<const char*>(src);
+        f32x4 d[TH];
+#pragma unroll
+        for (int r = 0; r < TH; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NK1; ++ks) {
+            u32x4 xv[TH];
+#pragma unroll
+            for (int r = 0; r < TH; ++r)
+                xv[r] = *reinterpret_cast<const u32x4*>(xb + xoff[ks] + r * ROW_BYTES);
+#pragma unroll
+            for (int r = 0; r < TH; ++r) d[r] = mfma<T>(wa1[ks], xv[r], d[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < TH; ++r) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = epilogue(d[r][i], s1r[i], b1r[i], act1);
+            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
+                                      ((r * NKS2 + (wave >> 1)) * 64) * 16 + tls_w) = pack8<T>(v);
+        }
+    };
+    auto phase_b = [&](const u32x4* src, const Pos& t) {
+        f32x4 acc[KB2];
+#pragma unroll
+        for (int kb = 0; kb < KB2; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks2 = 0; ks2 < NKS2; ++ks2) {
+            const u32x4 bfr = src[(wave * NKS2 + ks2) * 64 + lane];
+#pragma unroll
+            for (int kb = 0; kb < KB2; ++kb) acc[kb] = mfma<T>(wa2[ks2][kb], bfr, acc[kb]);
+        }
+        // lane holds output channels 16(l/16) + 4kb + [0,4) of pixel l%16 in row w
+        float o[16];
+#pragma unroll
+        for (int kb = 0; kb < KB2; ++kb) {
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(S2 + 16 * lg + 4 * kb);
+            const f32x4 bi = *reinterpret_cast<const f32x4*>(B2 + 16 * lg + 4 * kb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[4 * kb + i] = epilogue(acc[kb][i], sc[i], bi[i], act2);
+        }
+        const bool ok = t.oh0 + wave < a.Ho && t.ow0 + lr < a.Wo;
+        const int srow = ok ? t.out_base + wave * out_row : 0;
+        __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, ok ? st0 : mm::kOob, srow, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o + 8), ry, ok ? st1 : mm::kOob, srow,
+                                               0);
+    };
+
+    // ---- software-pipelined tile loop (see dwpw_mm.hip): step i waits for tile i+1's
+    // input (only step i-1's NST stores were issued after it), barrier, requests tile
+    // i+2, phase A of tile i+1, phase B of tile i
+    Pos cur = split(L);
+    Pos nxt = advance(cur);
+    issue_tile(cur, std::integral_constant<int, 0>{});
+    issue_tile(nxt, std::integral_constant<int, 1>{});
+    mm::wait_vmcnt<R>();
+    __builtin_amdgcn_s_barrier();
+    if (cur.n < a.N) phase_a(X0, T0);
+    auto step_fn = [&](auto par, bool first) {
+        constexpr int P = decltype(par)::value;
+        if (first) mm::wait_vmcnt<0>(); else mm::wait_vmcnt<NST>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own intermediate writes done
+        __builtin_amdgcn_s_barrier();
+        const Pos nn = advance(nxt);
+        issue_tile(nn, std::integral_constant<int, P>{});
+        if (nxt.n < a.N) phase_a(P == 0 ? X1 : X0, P == 0 ? T1 : T0);
+        phase_b(P == 0 ? T0 : T1, cur);
+        cur = nxt;
+        nxt = nn;
+    };
+    bool first = true;
+    while (cur.n < a.N) {
+        step_fn(std::integral_constant<int, 0>{}, first);
+        first = false;
+        if (cur.n >= a.N) break;
+        step_fn(std::integral_constant<int, 1>{}, false);
+    }
+    mm::wait_vmcnt<0>();
+}
+
+template <typename T, int S, int OCC>
+int launch_b2b_mm(const KArgs& a, int grid, void* stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((b2b_mm_kernel<T, S, OCC>), dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       a);
+    return (int)hipGetLastError();
+}
+template <typename T, int S, int OCC>
+int occ_b2b_mm() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, b2b_mm_kernel<T, S, OCC>, 256, 0) !=
+        hipSuccess)
+        return 0;
+    return n;
+}
+
+#define FCM_V_DWPW(...)
+#define FCM_V_DWPW32(...)
+#define FCM_V_B2B(...)
+#define FCM_V_DWPW_MM(...)
+#define FCM_V_DWPW_MMC(...)
+#define FCM_V_B2B_MM(name, dt, CT, S, OCC)                                   \
+    template int launch_b2b_mm<CT, S, OCC>(const KArgs&, int, void*); \
+    template int occ_b2b_mm<CT, S, OCC>();
+#include "../variants.def"
+#undef FCM_V_DWPW
+#undef FCM_V_DWPW32
+#undef FCM_V_B2B
+#undef FCM_V_DWPW_MM
+#undef FCM_V_DWPW_MMC
+#undef FCM_V_B2B_MM
+
+}  // namespace fcm

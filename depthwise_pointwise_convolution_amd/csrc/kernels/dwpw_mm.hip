@@ -429,6 +429,7 @@ int occ_dwpw_mm() {
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
 #define FCM_V_DWPW_MMC(...)
+#define FCM_V_B2B_MM(...)
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC)                              \
     template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>(const KArgs&, int, void*); \
     template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>();
@@ -438,5 +439,6 @@ int occ_dwpw_mm() {
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
 #undef FCM_V_DWPW_MMC
+#undef FCM_V_B2B_MM
 
 }  // namespace fcm

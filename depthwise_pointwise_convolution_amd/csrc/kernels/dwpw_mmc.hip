@@ -392,6 +392,7 @@ int occ_dwpw_mmc() {
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
 #define FCM_V_DWPW_MM(...)
+#define FCM_V_B2B_MM(...)
 #define FCM_V_DWPW_MMC(name, dt, CT, S, KT, OCC)                                 \
     template int launch_dwpw_mmc<CT, S, KT, OCC>(const KArgs&, int, void*); \
     template int occ_dwpw_mmc<CT, S, KT, OCC>();
@@ -401,5 +402,6 @@ int occ_dwpw_mmc() {
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
 #undef FCM_V_DWPW_MMC
+#undef FCM_V_B2B_MM
 
 }  // namespace fcm

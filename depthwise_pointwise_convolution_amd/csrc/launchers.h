@@ -27,6 +27,11 @@ int launch_dwpw_mmc(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int KT, int OCC>
 int occ_dwpw_mmc();
 
+template <typename T, int S, int OCC>
+int launch_b2b_mm(const KArgs& a, int grid, void* stream);
+template <typename T, int S, int OCC>
+int occ_b2b_mm();
+
 template <typename T, int S, int TH, int TW, int K1, int KT, int CC>
 int launch_b2b_mfma(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int TW, int K1, int KT, int CC>

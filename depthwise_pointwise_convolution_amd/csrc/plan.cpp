@@ -44,12 +44,14 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC},
 #define FCM_V_DWPW_MMC(name, dt, CT, S, KT, OCC) \
     {#name, VK_DWPW_MMC, dt, S, 4, 16, KT, 64, 0, 2, 0, OCC},
+#define FCM_V_B2B_MM(name, dt, CT, S, OCC) {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
 #undef FCM_V_DWPW_MMC
+#undef FCM_V_B2B_MM
 };
 const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -105,7 +107,8 @@ int variant_lds_bytes(const VariantDesc& v) {
     case VK_DWPW32:
         return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 1) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4;
     case VK_DWPW_MM:
-    case VK_DWPW_MMC: {
+    case VK_DWPW_MMC:
+    case VK_B2B_MM: {
         // input tile (or chunk) buffers and as many intermediate tiles
         const int slots = IH * IW * (v.cc / 8);
         const int slots_p = (slots + 255) / 256 * 256;
@@ -139,6 +142,12 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         (void)MBW;
         return nks * kbw * 4 + v.kt / 8 + (cbw == 1 ? 20 : cbw * 5 + 20) + cbw * 8 +
                2 * ((slots + 255) / 256) + 16 + kbw * 4 + 24 + 16;
+    }
+    case VK_B2B_MM: {
+        // per wave: 18 resident 3x3 operands, 8 resident 1x1 operands, 32 epilogue-2
+        // constants, input-operand offsets, the direct-load plan, accumulators
+        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
+        return 72 + 32 + 32 + 8 + 18 + 2 * ((slots + 255) / 256) + 32 + 16 + 20;
     }
     case VK_DWPW_MMC: {
         // per wave: accumulators and two sets of per-chunk pointwise operands of its
@@ -222,7 +231,9 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
     const int want = p.kind == FCM_KIND_B2B ? VK_B2B : (p.dtype == FCM_F32 ? VK_DWPW32 : VK_DWPW);
-    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC) ? VK_DWPW : v.vkind;
+    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC) ? VK_DWPW
+                     : v.vkind == VK_B2B_MM                           ? VK_B2B
+                                                                      : v.vkind;
     if (kind != want || v.dtype != p.dtype) {
         if (why) *why = "variant is for another module kind or storage type";
         return false;
@@ -235,7 +246,11 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         if (why) *why = "register-resident pointwise weights need C <= channel chunk";
         return false;
     }
-    if (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC) {
+    if (v.vkind == VK_B2B_MM && (p.C > 64 || p.K1 > 64 || p.K > 64)) {
+        if (why) *why = "matrix-core back-to-back variant takes at most 64 channels per layer";
+        return false;
+    }
+    if (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC || v.vkind == VK_B2B_MM) {
         if (v.vkind == VK_DWPW_MM && p.C > v.cc) {
             if (why) *why = "matrix-core depthwise variant needs C <= its channel chunk";
             return false;
@@ -284,7 +299,8 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ);
     int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd);
     // the workgroups per CU the kernel's register allocation was tuned for
-    if (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC) occ = std::min(occ, v.occ);
+    if (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC || v.vkind == VK_B2B_MM)
+        occ = std::min(occ, v.occ);
     if (lds > d.lds_bytes_per_wg) occ = 0;
     r.wgs_per_cu = occ;
     const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);
@@ -333,7 +349,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     const double lane_ops_per_s = d.valu_f32_flops / 2.0;
     double t_mat, t_vec;
     const double epi_ops = 3.0 * ((double)n1 * ktiles + p.K);
-    if (v.vkind == VK_B2B) {
+    if (v.vkind == VK_B2B || v.vkind == VK_B2B_MM) {
         t_mat = 2.0 * P * pad_px * ((double)v.k1 * 9 * p.C * ktiles + (double)v.k1 * p.K) /
                 d.mfma_f16_flops;
         t_vec = P * pad_px * epi_ops / lane_ops_per_s;

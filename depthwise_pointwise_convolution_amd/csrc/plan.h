@@ -7,7 +7,7 @@
 
 namespace fcm {
 
-enum VKind { VK_DWPW = 0, VK_DWPW32 = 1, VK_B2B = 2, VK_DWPW_MM = 3, VK_DWPW_MMC = 4 };
+enum VKind { VK_DWPW = 0, VK_DWPW32 = 1, VK_B2B = 2, VK_DWPW_MM = 3, VK_DWPW_MMC = 4, VK_B2B_MM = 5 };
 
 struct VariantDesc {
     const char* name;
