@@ -247,7 +247,7 @@ def main(argv=None) -> int:
     if args.variant is None and not args.no_tune and args.mode != "copy":
         # measured choice of variant and grid (untimed, before the benchmark proper)
         with torch.cuda.stream(stream):
-            mod.tune(x0, ys[0], iters=20, stream=stream)
+            mod.tune(xs, ys, iters=2 * nsets, stream=stream)
         torch.cuda.synchronize()
     plan = mod.plan
     vname = fcm_variant_name(plan.variant)

@@ -118,8 +118,8 @@ def lib() -> ctypes.CDLL:
             L.fcm_pack_weights.argtypes = [P(fcm_plan_t), vp, vp, vp, vp, vp]
             L.fcm_dwpw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
             L.fcm_b2b_conv_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
-            L.fcm_tune.argtypes = [P(fcm_problem), P(fcm_device_spec), vp, vp, fp, fp, vp, fp,
-                                   fp, vp, vp, _i32, P(fcm_plan_t)]
+            L.fcm_tune.argtypes = [P(fcm_problem), P(fcm_device_spec), _i32, P(vp), vp, fp, fp,
+                                   vp, fp, fp, P(vp), vp, _i32, P(fcm_plan_t)]
             L.fcm_dw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
             L.fcm_pw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
             L.fcm_conv_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
@@ -245,10 +245,17 @@ def fcm_b2b_conv_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y, stream=No
 
 def fcm_tune(prob, x, w1, scale1, bias1, w2, scale2, bias2, y, iters=20, spec=None,
              stream=None) -> "fcm_plan_t":
+    """x, y: one tensor each, or equal-length sequences of tensors to rotate over."""
+    xs = list(x) if isinstance(x, (list, tuple)) else [x]
+    ys = list(y) if isinstance(y, (list, tuple)) else [y]
+    if len(xs) != len(ys):
+        raise ValueError("x and y need the same number of tensors")
+    xa = (ctypes.c_void_p * len(xs))(*[_ptr(t) for t in xs])
+    ya = (ctypes.c_void_p * len(ys))(*[_ptr(t) for t in ys])
     out = fcm_plan_t()
-    _check(lib().fcm_tune(ctypes.byref(prob), ctypes.byref(spec) if spec else None, _ptr(x),
-                          _ptr(w1), _ptr(scale1), _ptr(bias1), _ptr(w2), _ptr(scale2),
-                          _ptr(bias2), _ptr(y), _stream(stream), int(iters), ctypes.byref(out)),
+    _check(lib().fcm_tune(ctypes.byref(prob), ctypes.byref(spec) if spec else None, len(xs),
+                          xa, _ptr(w1), _ptr(scale1), _ptr(bias1), _ptr(w2), _ptr(scale2),
+                          _ptr(bias2), ya, _stream(stream), int(iters), ctypes.byref(out)),
            "fcm_tune")
     return out
 

@@ -352,18 +352,23 @@ fcm_status fcm_b2b_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w
     return launch_fused(plan, a, stream);
 }
 
-fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, const void* x,
-                    const void* w1, const float* scale1, const float* bias1, const void* w2,
-                    const float* scale2, const float* bias2, void* y, void* stream,
-                    int32_t iters, fcm_plan_t* out) {
+fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_t nsets,
+                    const void* const* x, const void* w1, const float* scale1,
+                    const float* bias1, const void* w2, const float* scale2,
+                    const float* bias2, void* const* y, void* stream, int32_t iters,
+                    fcm_plan_t* out) {
     if (!out) return fail(FCM_ERR_INVALID_ARG, "plan output pointer is NULL");
     if (iters <= 0) return fail(FCM_ERR_INVALID_ARG, "iters must be positive");
+    if (nsets < 1 || !x || !y) return fail(FCM_ERR_INVALID_ARG, "need nsets >= 1 and x, y arrays");
     fcm_plan_t first;
     FCM_TRY(fcm_plan(prob, spec, &first));  // validates the problem
+    int call = 0;
     auto run = [&](const fcm_plan_t* pl) {
+        const int i = call++ % nsets;
         return prob->kind == FCM_KIND_DWPW
-                   ? fcm_dwpw_fwd(pl, x, w1, scale1, bias1, w2, scale2, bias2, y, stream)
-                   : fcm_b2b_conv_fwd(pl, x, w1, scale1, bias1, w2, scale2, bias2, y, stream);
+                   ? fcm_dwpw_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i], stream)
+                   : fcm_b2b_conv_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i],
+                                      stream);
     };
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {

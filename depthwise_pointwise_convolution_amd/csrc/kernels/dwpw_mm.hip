@@ -196,6 +196,12 @@ void dwpw_mm_kernel(KArgs a) {
     };
 
     // ---- per-wave constants ----------------------------------------------------------
+    // All constant loads are issued first, unconditionally (clamped addresses, absent
+    // epilogue arrays read from another valid tensor), then the first two tiles' input,
+    // and only then are the loaded values used: the wait for the constants does not
+    // also wait for the input (vector-memory operations complete in issue order), and
+    // the two latencies overlap.
+    //
     // depthwise: this wave owns channel blocks cb = wave + 4j.  Matrix operand of block
     // cb and tap pair tp, lane (l%16, l/16): row = channel 16cb + l%16, reduction index
     // 8(l/16) + e = (tap 2tp + (l/16)/2, channel 16cb + 8((l/16)&1) + e); non-zero only
@@ -203,6 +209,57 @@ void dwpw_mm_kernel(KArgs a) {
     // of the last pair is empty (zero weights).
     const bool dw_active = (lr >> 3) == (lg & 1);
     const int dw_e = lr & 7;
+    const float* s1p = a.s1 ? a.s1 : (const float*)a.w2;
+    const float* b1p = a.b1 ? a.b1 : (const float*)a.w2;
+    const float* s2p = a.s2 ? a.s2 : (const float*)a.w2;
+    const float* b2p = a.b2 ? a.b2 : (const float*)a.w2;
+    uint16_t wdr[CBW][NTP];
+    float s1l[CBW][4], b1l[CBW][4];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+        const int cb = wave + 4 * j;
+#pragma unroll
+        for (int tp = 0; tp < NTP; ++tp) {
+            const int t = 2 * tp + (lg >> 1), c = cb * 16 + lr;
+            wdr[j][tp] = __builtin_bit_cast(uint16_t,
+                                            wdw[(t < 9 ? t : 0) * a.C + (c < a.C ? c : 0)]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = cb * 16 + lg * 4 + i, cc = c < a.C ? c : 0;
+            s1l[j][i] = s1p[cc];
+            b1l[j][i] = b1p[cc];
+        }
+    }
+    // pointwise A operand of this wave's slice for reduction step ks, block kb: row
+    // kperm<KW>(kb, l%16) of the slice, reduction channels 32ks + 4(l/16) + [0,4) and
+    // 32ks + 16 + 4(l/16) + [0,4) (the order the depthwise result is stored in)
+    uint2 wlo[NKS][KBW], whi[NKS][KBW];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+            const int ko = kw0 + kperm<KW>(kb, lr), c = ks * 32 + lg * 4;
+            const T* row = wpw + (int64_t)(ko < a.K ? ko : 0) * a.C;
+            wlo[ks][kb] = *reinterpret_cast<const uint2*>(row + (c < a.C ? c : 0));
+            whi[ks][kb] = *reinterpret_cast<const uint2*>(row + (c + 16 < a.C ? c + 16 : 0));
+        }
+    // epilogue-2 constants of the lane's output channels kw0 + (KW/4)(l/16) + [0,KW/4)
+    float s2r[KW / 4], b2r[KW / 4];
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) {
+        const int k = kw0 + lg * (KW / 4) + i, kk = k < a.K ? k : 0;
+        s2r[i] = s2p[kk];
+        b2r[i] = b2p[kk];
+    }
+
+    // the first two tiles' input
+    Pos cur = split(L / a.num_ktiles);
+    Pos nxt = advance(cur);
+    issue_tile(cur, std::integral_constant<int, 0>{});
+    issue_tile(nxt, std::integral_constant<int, 1>{});
+
+    // now the loaded values are used
     uint32_t wdc[CBW][NTP];
     float s1r[CBW][4], b1r[CBW][4];
 #pragma unroll
@@ -212,18 +269,14 @@ void dwpw_mm_kernel(KArgs a) {
         for (int tp = 0; tp < NTP; ++tp) {
             const int t = 2 * tp + (lg >> 1), c = cb * 16 + lr;
             const bool ok = dw_active && t < 9 && c < a.C;
-            const uint16_t h = __builtin_bit_cast(uint16_t, wdw[ok ? t * a.C + c : 0]);
-            const uint32_t v = ok ? (uint32_t)h : 0u;
+            const uint32_t v = ok ? (uint32_t)wdr[j][tp] : 0u;
             wdc[j][tp] = (dw_e & 1) ? (v << 16) : v;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = cb * 16 + lg * 4 + i;
-            const bool ok = c < a.C;
-            const float sv = a.s1 ? a.s1[ok ? c : 0] : 1.0f;
-            const float bv = a.b1 ? a.b1[ok ? c : 0] : 0.0f;
-            s1r[j][i] = ok ? sv : 1.0f;
-            b1r[j][i] = ok ? bv : 0.0f;
+            const bool ok = cb * 16 + lg * 4 + i < a.C;
+            s1r[j][i] = (a.s1 && ok) ? s1l[j][i] : 1.0f;
+            b1r[j][i] = (a.b1 && ok) ? b1l[j][i] : 0.0f;
         }
     }
     auto dw_operand = [&](uint32_t v) {
@@ -237,9 +290,6 @@ void dwpw_mm_kernel(KArgs a) {
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) wdf[tp] = dw_operand(wdc[0][tp]);
     }
-    // pointwise A operand of this wave's slice for reduction step ks, block kb: row
-    // kperm<KW>(kb, l%16) of the slice, reduction channels 32ks + 4(l/16) + [0,4) and
-    // 32ks + 16 + 4(l/16) + [0,4) (the order the depthwise result is stored in)
     u32x4 wa[NKS][KBW];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -247,22 +297,14 @@ void dwpw_mm_kernel(KArgs a) {
         for (int kb = 0; kb < KBW; ++kb) {
             const int ko = kw0 + kperm<KW>(kb, lr), c = ks * 32 + lg * 4;
             const bool ok_lo = ko < a.K && c < a.C, ok_hi = ko < a.K && c + 16 < a.C;
-            const T* row = wpw + (int64_t)(ko < a.K ? ko : 0) * a.C;
-            const uint2 lo = *reinterpret_cast<const uint2*>(row + (ok_lo ? c : 0));
-            const uint2 hi = *reinterpret_cast<const uint2*>(row + (ok_hi ? c + 16 : 0));
-            wa[ks][kb] = u32x4{ok_lo ? lo.x : 0u, ok_lo ? lo.y : 0u, ok_hi ? hi.x : 0u,
-                               ok_hi ? hi.y : 0u};
+            wa[ks][kb] = u32x4{ok_lo ? wlo[ks][kb].x : 0u, ok_lo ? wlo[ks][kb].y : 0u,
+                               ok_hi ? whi[ks][kb].x : 0u, ok_hi ? whi[ks][kb].y : 0u};
         }
-    // epilogue-2 constants of the lane's output channels kw0 + (KW/4)(l/16) + [0,KW/4)
-    float s2r[KW / 4], b2r[KW / 4];
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
-        const int k = kw0 + lg * (KW / 4) + i;
-        const bool ok = k < a.K;
-        const float sv = a.s2 ? a.s2[ok ? k : 0] : 1.0f;
-        const float bv = a.b2 ? a.b2[ok ? k : 0] : 0.0f;
-        s2r[i] = ok ? sv : 1.0f;
-        b2r[i] = ok ? bv : 0.0f;
+        const bool ok = kw0 + lg * (KW / 4) + i < a.K;
+        s2r[i] = (a.s2 && ok) ? s2r[i] : 1.0f;
+        b2r[i] = (a.b2 && ok) ? b2r[i] : 0.0f;
     }
     // LDS byte offsets of this lane's depthwise operand reads in output row 0, block
     // cb = wave, per tap pair (row r adds r * ROW_BYTES, block cb + 4j adds 128j bytes:
@@ -378,10 +420,6 @@ void dwpw_mm_kernel(KArgs a) {
     // into xs[P]; phase A of tile i+1 (xs[1-P] -> tls[1-P]); phase B of tile i (tls[P]).
     // Vector-memory operations issued after tile i+1's loads: none before step 0, the
     // NST stores of step i-1 before step i.
-    Pos cur = split(L / a.num_ktiles);
-    Pos nxt = advance(cur);
-    issue_tile(cur, std::integral_constant<int, 0>{});
-    issue_tile(nxt, std::integral_constant<int, 1>{});
     mm::wait_vmcnt<R>();
     __builtin_amdgcn_s_barrier();
     if (cur.n < a.N) phase_a(X0, T0, 0);

@@ -50,8 +50,11 @@ class FcmModule:
 
     def tune(self, x, y=None, iters: int = 20, stream=None) -> None:
         """Replace the plan by the fastest measured variant and grid (fcm_tune); the
-        packed weights serve every variant of the module kind."""
-        y = self.new_output(x.device) if y is None else y
+        packed weights serve every variant of the module kind.  x (and y) may be lists
+        of tensors to rotate over."""
+        if y is None:
+            y = ([self.new_output(t.device) for t in x] if isinstance(x, (list, tuple))
+                 else self.new_output(x.device))
         self.plan = fcm_tune(self.prob, x, self.w1p, self.s1, self.b1, self.w2p, self.s2,
                              self.b2, y, iters, stream=stream)
 

@@ -154,17 +154,20 @@ fcm_status fcm_plan_variant(const fcm_problem* prob, const fcm_device_spec* spec
 /* Measured selection (the profiling step of the TVM conv2d profiler page: every
  * candidate kernel is compiled once, run on the device, and the fastest is kept).
  * Runs every fused variant able to take `prob`, at persistent grids of 1, 2, 3 and 4
- * workgroups per CU (as far as its occupancy allows), `iters` times each on `stream`
- * with the caller's tensors -- laid out as for fcm_dwpw_fwd / fcm_b2b_conv_fwd
- * (weights packed by fcm_pack_weights); y is overwritten -- and writes the plan of
- * the fastest to *out, with out->grid the chosen grid and out->tuned_us its mean
- * time per call.  Synchronises `stream`.  Allocates no device memory.
- * Errors: FCM_ERR_INVALID_ARG / FCM_ERR_UNSUPPORTED as fcm_plan and the *_fwd
- * calls; FCM_ERR_HIP if a launch or an event fails. */
-fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, const void* x,
-                    const void* w1, const float* scale1, const float* bias1, const void* w2,
-                    const float* scale2, const float* bias2, void* y, void* stream,
-                    int32_t iters, fcm_plan_t* out);
+ * workgroups per CU (as far as its occupancy allows), `iters` times each on `stream`,
+ * rotating over `nsets` input/output pairs x[i], y[i] (laid out as for fcm_dwpw_fwd /
+ * fcm_b2b_conv_fwd; several pairs whose total exceeds the 256 MB Infinity Cache make
+ * the candidates stream from HBM as in a real network) with the shared filters and
+ * epilogue arrays (weights packed by fcm_pack_weights); every y[i] is overwritten.
+ * Writes the plan of the fastest to *out, with out->grid the chosen grid and
+ * out->tuned_us its mean time per call.  Synchronises `stream`.  Allocates no device
+ * memory.  Errors: FCM_ERR_INVALID_ARG / FCM_ERR_UNSUPPORTED as fcm_plan and the *_fwd
+ * calls (also for nsets < 1 or NULL arrays); FCM_ERR_HIP if a launch or an event fails. */
+fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_t nsets,
+                    const void* const* x, const void* w1, const float* scale1,
+                    const float* bias1, const void* w2, const float* scale2,
+                    const float* bias2, void* const* y, void* stream, int32_t iters,
+                    fcm_plan_t* out);
 
 /* Number of fused kernel variants compiled into the library, and a short name for
  * one of them ("" if out of range). */

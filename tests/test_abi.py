@@ -220,9 +220,15 @@ def test_forward_calls_reject_bad_arguments_before_any_hip_call():
         assert L.fcm_dwpw_fwd(ctypes.byref(q), *args) == F.FCM_ERR_INVALID_ARG, field
     # tuning: NULL output and non-positive iteration counts
     prob = _problem(F, wl)
-    assert L.fcm_tune(ctypes.byref(prob), None, *args, 5, None) == F.FCM_ERR_INVALID_ARG
+    xs = (ctypes.c_void_p * 1)(0x1000)
+    ys = (ctypes.c_void_p * 1)(0x1000)
+    rest = [fake, nul, nul, fake, nul, nul]
+    assert L.fcm_tune(ctypes.byref(prob), None, 1, xs, *rest, ys, None, 5,
+                      None) == F.FCM_ERR_INVALID_ARG
     out = F.fcm_plan_t()
-    assert L.fcm_tune(ctypes.byref(prob), None, *args, 0,
+    assert L.fcm_tune(ctypes.byref(prob), None, 1, xs, *rest, ys, None, 0,
+                      ctypes.byref(out)) == F.FCM_ERR_INVALID_ARG
+    assert L.fcm_tune(ctypes.byref(prob), None, 0, xs, *rest, ys, None, 5,
                       ctypes.byref(out)) == F.FCM_ERR_INVALID_ARG
 
 
