@@ -4,7 +4,10 @@
 
 Each translation unit is compiled to an object under ``_build/`` in parallel and
 the objects are linked into ``depthwise_pointwise_convolution_amd/libfcm.so``.
-Device code is built for gfx950 only, with packed fp32 arithmetic disabled.
+Device code is built for gfx950 only, with packed fp32 arithmetic disabled.  Every
+kernel source is also compiled to gfx950 assembly, which isa_check.py inspects; the
+library is refused if a store of more than 64 bits is directly followed by a write of
+its data registers (see isa_check.py).
 """
 from __future__ import annotations
 
@@ -24,7 +27,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 SOURCES = [
     ("kernels/dwpw.hip", True),
     ("kernels/dwpw_mm.hip", True),
-    ("kernels/dwpw_mmc.hip", True),
+    ("kernels/dwpw_mmw.hip", True),
     ("kernels/b2b_mm.hip", True),
     ("kernels/lbl.hip", True),
     ("kernels/b2b.hip", True),
@@ -65,10 +68,36 @@ def _compile(src: str, device: bool, verbose: bool) -> str:
     return obj
 
 
+def _check_isa(src: str) -> list:
+    """gfx950 assembly of one kernel source, checked by isa_check."""
+    try:
+        from .isa_check import store_data_overwrites
+    except ImportError:  # loaded by path rather than as part of the package
+        sys.path.insert(0, PKG)
+        from isa_check import store_data_overwrites
+    os.makedirs(BUILD, exist_ok=True)
+    asm = os.path.join(BUILD, src.replace("/", "_") + ".s")
+    cmd = [_hipcc()] + _flags(True) + ["--cuda-device-only", "-S", os.path.join(CSRC, src),
+                                        "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} to assembly failed:\n{r.stderr}")
+    with open(asm) as f:
+        return [(src,) + hit for hit in store_data_overwrites(f.read())]
+
+
 def build(jobs: int = 0, verbose: bool = False) -> str:
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    kernels = [s for s, dev in SOURCES if s.startswith("kernels/")]
     with cf.ThreadPoolExecutor(jobs) as ex:
+        checks = [ex.submit(_check_isa, k) for k in kernels]
         objs = list(ex.map(lambda s: _compile(s[0], s[1], verbose), SOURCES))
+        hits = [h for c in checks for h in c.result()]
+    if hits:
+        src, fn, reader, writer = hits[0]
+        raise RuntimeError(f"{len(hits)} store(s) of more than 64 bits would have their data "
+                           f"registers rewritten by the next instruction, e.g. in {src} {fn}:"
+                           f"\n  {reader}\n  {writer}")
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

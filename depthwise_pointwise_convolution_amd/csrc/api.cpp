@@ -47,16 +47,16 @@ const VariantImpl kImpls[] = {
     {launch_b2b_mfma<CT, S, TH, TW, K1, KT, CC>, occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>},
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
     {launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>},
-#define FCM_V_DWPW_MMC(name, dt, CT, S, KT, OCC) \
-    {launch_dwpw_mmc<CT, S, KT, OCC>, occ_dwpw_mmc<CT, S, KT, OCC>},
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC) {launch_b2b_mm<CT, S, OCC>, occ_b2b_mm<CT, S, OCC>},
+#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, OCC) \
+    {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, OCC>, occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
-#undef FCM_V_DWPW_MMC
 #undef FCM_V_B2B_MM
+#undef FCM_V_DWPW_MMW
 };
 static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
 
@@ -280,8 +280,9 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                              "16-byte aligned");
         const char* s = (const char*)w2_src;
         const char* d = (const char*)w2_dst;
-        const int64_t nb = plan->w2_packed_bytes;
-        if (s < d + nb && d < s + nb) return fail(FCM_ERR_INVALID_ARG, "w2 buffers overlap");
+        const int64_t ns = (int64_t)p.K * (p.kind == FCM_KIND_B2B ? p.K1 : p.C) * e;
+        const int64_t nd = plan->w2_packed_bytes;
+        if (s < d + nd && d < s + ns) return fail(FCM_ERR_INVALID_ARG, "w2 buffers overlap");
     }
     if (w1_src) {
         int rc;
@@ -294,7 +295,10 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                          hipGetErrorString((hipError_t)rc));
     }
     if (w2_src) {
-        const int rc = launch_copy(w2_src, w2_dst, plan->w2_packed_bytes, stream);
+        const int64_t plain = (int64_t)p.K * (p.kind == FCM_KIND_B2B ? p.K1 : p.C) * e;
+        int rc = launch_copy(w2_src, w2_dst, plain, stream);
+        if (rc == 0 && plan->w2_packed_bytes > plain)
+            rc = launch_pack_pw_blocked(w2_src, (char*)w2_dst + plain, p.K, p.C, stream);
         if (rc != 0)
             return fail(FCM_ERR_HIP, std::string("weight copy failed: ") +
                                          hipGetErrorString((hipError_t)rc));

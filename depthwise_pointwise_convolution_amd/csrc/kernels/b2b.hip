@@ -283,14 +283,14 @@ int launch_conv_lbl(int dtype, int stride, const KArgs& a, void* stream) {
     template int launch_b2b_mfma<CT, S, TH, TW, K1, KT, CC>(const KArgs&, int, void*); \
     template int occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>();
 #define FCM_V_DWPW_MM(...)
-#define FCM_V_DWPW_MMC(...)
 #define FCM_V_B2B_MM(...)
+#define FCM_V_DWPW_MMW(...)
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
-#undef FCM_V_DWPW_MMC
 #undef FCM_V_B2B_MM
+#undef FCM_V_DWPW_MMW
 
 }  // namespace fcm

@@ -243,11 +243,13 @@ void b2b_mm_kernel(KArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[4 * kb + i] = epilogue(acc[kb][i], sc[i], bi[i], act2);
         }
+        // whole offsets in the vector operand, scalar offset 0 (see dwpw_mm.hip)
         const bool ok = t.oh0 + wave < a.Ho && t.ow0 + lr < a.Wo;
-        const int srow = ok ? t.out_base + wave * out_row : 0;
-        __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, ok ? st0 : mm::kOob, srow, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o + 8), ry, ok ? st1 : mm::kOob, srow,
-                                               0);
+        const uint32_t row = (uint32_t)(t.out_base + wave * out_row);
+        __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry,
+                                               ok && st0 != mm::kOob ? row + st0 : mm::kOob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o + 8), ry,
+                                               ok && st1 != mm::kOob ? row + st1 : mm::kOob, 0, 0);
     };
 
     // ---- software-pipelined tile loop (see dwpw_mm.hip): step i waits for tile i+1's
@@ -302,16 +304,16 @@ int occ_b2b_mm() {
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
 #define FCM_V_DWPW_MM(...)
-#define FCM_V_DWPW_MMC(...)
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC)                                   \
     template int launch_b2b_mm<CT, S, OCC>(const KArgs&, int, void*); \
     template int occ_b2b_mm<CT, S, OCC>();
+#define FCM_V_DWPW_MMW(...)
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
-#undef FCM_V_DWPW_MMC
 #undef FCM_V_B2B_MM
+#undef FCM_V_DWPW_MMW
 
 }  // namespace fcm

@@ -301,14 +301,14 @@ int occ_dwpw_f32() {
     template int occ_dwpw_f32<S, TH, TW, KT, CC>();
 #define FCM_V_B2B(...)
 #define FCM_V_DWPW_MM(...)
-#define FCM_V_DWPW_MMC(...)
 #define FCM_V_B2B_MM(...)
+#define FCM_V_DWPW_MMW(...)
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
-#undef FCM_V_DWPW_MMC
 #undef FCM_V_B2B_MM
+#undef FCM_V_DWPW_MMW
 
 }  // namespace fcm

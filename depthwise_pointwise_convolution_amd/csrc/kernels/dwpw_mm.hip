@@ -383,16 +383,19 @@ void dwpw_mm_kernel(KArgs a) {
         for (int mb = 0; mb < TH; ++mb)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) bfr[mb][ks] = src[(mb * NKS + ks) * 64 + lane];
+        // reduction step outermost, so that each accumulator is updated in place
         f32x4 acc[TH][KBW];
 #pragma unroll
         for (int mb = 0; mb < TH; ++mb)
 #pragma unroll
-            for (int kb = 0; kb < KBW; ++kb) {
-                acc[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < KBW; ++kb) acc[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < TH; ++mb)
+#pragma unroll
+                for (int kb = 0; kb < KBW; ++kb)
                     acc[mb][kb] = mfma<T>(wa[ks][kb], bfr[mb][ks], acc[mb][kb]);
-            }
         const uint32_t voff = t.ow0 + lr < a.Wo ? st_lane : mm::kOob;
 #pragma unroll
         for (int mb = 0; mb < TH; ++mb) {
@@ -408,8 +411,13 @@ void dwpw_mm_kernel(KArgs a) {
                     o[4 + i] = epilogue(acc[mb][kb + 1][i], s2r[kb * 4 + 4 + i],
                                         b2r[kb * 4 + 4 + i], act2);
                 }
-                __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, v + kb * 4 * sizeof(T),
-                                                       srow, 0);
+                // the whole offset goes in the vector operand (scalar offset 0): with a
+                // register scalar offset the compiler omits the wait state that a store
+                // of more than 64 bits needs before its data registers are rewritten
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    pack16<T>(o), ry,
+                    v == mm::kOob ? mm::kOob : (uint32_t)srow + v + kb * 4 * (uint32_t)sizeof(T),
+                    0, 0);
             }
         }
     };
@@ -466,17 +474,17 @@ int occ_dwpw_mm() {
 #define FCM_V_DWPW(...)
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
-#define FCM_V_DWPW_MMC(...)
 #define FCM_V_B2B_MM(...)
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC)                              \
     template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>(const KArgs&, int, void*); \
     template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>();
+#define FCM_V_DWPW_MMW(...)
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
-#undef FCM_V_DWPW_MMC
 #undef FCM_V_B2B_MM
+#undef FCM_V_DWPW_MMW
 
 }  // namespace fcm

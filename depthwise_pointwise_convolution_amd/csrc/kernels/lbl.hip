@@ -236,6 +236,29 @@ int launch_pack_conv(int elem_bytes, const void* src, void* dst, int K1, int C, 
     return (int)hipGetLastError();
 }
 
+// Blocked copy of [K][C] pointwise filters (layout in plan.h, pw_blocked_elems): one
+// thread per 16-bit destination element, zero where the row or channel does not exist.
+__global__ void pack_pw_blocked_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                       int K, int C, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int e = (int)(i & 7), lane = (int)((i >> 3) & 63), h = (int)((i >> 9) & 1);
+    const int64_t blk = i >> 10;  // g * S32 + s
+    const int S32 = (C + 31) / 32;
+    const int g = (int)(blk / S32), sl = (int)(blk % S32);
+    const int lg = lane >> 4, r = lane & 15;
+    const int k = 32 * g + 8 * (r >> 2) + 4 * h + (r & 3), c = 32 * sl + 8 * lg + e;
+    dst[i] = (k < K && c < C) ? src[(int64_t)k * C + c] : (uint16_t)0;
+}
+
+int launch_pack_pw_blocked(const void* src, void* dst, int K, int C, void* stream) {
+    const int64_t total = (int64_t)((K + 31) / 32 * 32) * ((C + 31) / 32 * 32);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(pack_pw_blocked_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                       0, (hipStream_t)stream, (const uint16_t*)src, (uint16_t*)dst, K, C, total);
+    return (int)hipGetLastError();
+}
+
 int launch_copy(const void* src, void* dst, long long bytes, void* stream) {
     return (int)hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDevice,
                                (hipStream_t)stream);

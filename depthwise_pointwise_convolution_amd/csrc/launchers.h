@@ -22,10 +22,10 @@ int launch_dwpw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int TW, int KT, int CC, int OCC>
 int occ_dwpw_mm();
 
-template <typename T, int S, int KT, int OCC>
-int launch_dwpw_mmc(const KArgs& a, int grid, void* stream);
-template <typename T, int S, int KT, int OCC>
-int occ_dwpw_mmc();
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int OCC>
+int launch_dwpw_mmw(const KArgs& a, int grid, void* stream);
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int OCC>
+int occ_dwpw_mmw();
 
 template <typename T, int S, int OCC>
 int launch_b2b_mm(const KArgs& a, int grid, void* stream);
@@ -48,6 +48,7 @@ int launch_conv_lbl(int dtype, int stride, const KArgs& a, void* stream);
 int launch_pack_dw(int elem_bytes, const void* src, void* dst, int C, int RS, void* stream);
 int launch_pack_conv(int elem_bytes, const void* src, void* dst, int K1, int C, int RS,
                      void* stream);
+int launch_pack_pw_blocked(const void* src, void* dst, int K, int C, void* stream);
 int launch_copy(const void* src, void* dst, long long bytes, void* stream);
 
 }  // namespace fcm

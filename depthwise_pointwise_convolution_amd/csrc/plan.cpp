@@ -35,23 +35,24 @@ namespace fcm {
 
 const VariantDesc kVariants[] = {
 #define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES, OCC) \
-    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0, 0, OCC},
+    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0, 0, OCC, 4, 0},
 #define FCM_V_DWPW32(name, S, TH, TW, KT, CC) \
-    {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 0, 1},
+    {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 0, 1, 4, 0},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
-    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, 0, K1, 1},
+    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, 0, K1, 1, 4, 0},
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
-    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC},
-#define FCM_V_DWPW_MMC(name, dt, CT, S, KT, OCC) \
-    {#name, VK_DWPW_MMC, dt, S, 4, 16, KT, 64, 0, 2, 0, OCC},
-#define FCM_V_B2B_MM(name, dt, CT, S, OCC) {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC},
+    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, 4, 0},
+#define FCM_V_B2B_MM(name, dt, CT, S, OCC) \
+    {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC, 4, 0},
+#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, OCC) \
+    {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, 8, CMAX},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
-#undef FCM_V_DWPW_MMC
 #undef FCM_V_B2B_MM
+#undef FCM_V_DWPW_MMW
 };
 const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -107,13 +108,21 @@ int variant_lds_bytes(const VariantDesc& v) {
     case VK_DWPW32:
         return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 1) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4;
     case VK_DWPW_MM:
-    case VK_DWPW_MMC:
     case VK_B2B_MM: {
         // input tile (or chunk) buffers and as many intermediate tiles
         const int slots = IH * IW * (v.cc / 8);
         const int slots_p = (slots + 255) / 256 * 256;
         const int tls = v.th * (v.cc / 32) * 64 * 16;
         return v.nbuf * (slots_p * 16 + tls);
+    }
+    case VK_DWPW_MMW: {
+        // three input chunk buffers (rounded to whole 512-thread load rounds), two
+        // intermediate chunks of 16-pixel blocks, epilogue-2 constants of the K tile
+        const int slots = IH * IW * (v.cc / 8);
+        const int slots_p = (slots + 511) / 512 * 512;
+        const int mb = (P + 15) / 16;
+        return v.nbuf * slots_p * 16 + 2 * mb * (v.cc / 32) * 64 * 16 + 2 * v.kt * 4 +
+               v.cmax * (9 * 2 + 2 * 4);
     }
     default:
         return IH * IW * (v.cc + 8) * e + 2 * v.k1 * 4 + 2 * v.kt * 4;
@@ -149,13 +158,14 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
         return 72 + 32 + 32 + 8 + 18 + 2 * ((slots + 255) / 256) + 32 + 16 + 20;
     }
-    case VK_DWPW_MMC: {
-        // per wave: accumulators and two sets of per-chunk pointwise operands of its
-        // KT/4 output channels, their epilogue constants, two sets of depthwise operands,
-        // the direct-load plan, staging and addressing
-        const int kbw = v.kt / 64;
+    case VK_DWPW_MMW: {
+        // per wave: accumulators of its KT/8 output channels for every 16-pixel block,
+        // two sets of pointwise operands, depthwise operands and operand offsets, the
+        // direct-load plan, staging and addressing
+        const int mb = (P + 15) / 16, kbw = v.kt / 128;
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
-        return 16 * kbw + 16 * kbw + v.kt / 8 + 26 + 20 + 2 * ((slots + 255) / 256) + 32 + 24;
+        return 4 * mb * kbw + 16 * kbw + 28 + 5 * (mb / 2) + 2 * ((slots + 511) / 512) + 36 +
+               24;
     }
     default: {
         const int KB1 = v.k1 / 16, KB2 = v.kt / 16, KS2 = v.k1 / 32;
@@ -231,7 +241,8 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
     const int want = p.kind == FCM_KIND_B2B ? VK_B2B : (p.dtype == FCM_F32 ? VK_DWPW32 : VK_DWPW);
-    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC) ? VK_DWPW
+    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMW)
+                         ? VK_DWPW
                      : v.vkind == VK_B2B_MM                           ? VK_B2B
                                                                       : v.vkind;
     if (kind != want || v.dtype != p.dtype) {
@@ -250,12 +261,17 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         if (why) *why = "matrix-core back-to-back variant takes at most 64 channels per layer";
         return false;
     }
-    if (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC || v.vkind == VK_B2B_MM) {
+    if (v.vkind == VK_DWPW_MM || v.vkind == VK_B2B_MM || v.vkind == VK_DWPW_MMW) {
         if (v.vkind == VK_DWPW_MM && p.C > v.cc) {
             if (why) *why = "matrix-core depthwise variant needs C <= its channel chunk";
             return false;
         }
-        if (v.vkind == VK_DWPW_MMC && p.C % 64 != 0) {
+        if (v.cmax > 0 && p.C > v.cmax) {
+            if (why) *why = "wide matrix-core variant keeps at most its compiled channel count "
+                            "of depthwise filters in LDS";
+            return false;
+        }
+        if (v.vkind == VK_DWPW_MMW && p.C % 64 != 0) {
             if (why) *why = "chunked matrix-core variant needs C a multiple of 64";
             return false;
         }
@@ -295,12 +311,14 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     const int lds = variant_lds_bytes(v);
     int vg = variant_vgpr_estimate(v);
     vg = (vg + 7) / 8 * 8;
+    // workgroups per CU: a workgroup puts waves/4 waves on each of the 4 SIMDs
+    const int wps = std::max(v.waves / 4, 1);
     int occ_lds = lds > 0 ? d.lds_bytes_per_cu / lds : 8;
-    int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ);
-    int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd);
+    int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ) / wps;
+    int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd / wps);
     // the workgroups per CU the kernel's register allocation was tuned for
-    if (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMC || v.vkind == VK_B2B_MM)
-        occ = std::min(occ, v.occ);
+    if (v.vkind == VK_DWPW_MM || v.vkind == VK_B2B_MM || v.vkind == VK_DWPW_MMW)
+        occ = std::min(occ, std::max(v.occ / wps, 1));
     if (lds > d.lds_bytes_per_wg) occ = 0;
     r.wgs_per_cu = occ;
     const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);
@@ -356,7 +374,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     } else if (v.vkind == VK_DWPW) {
         t_mat = 2.0 * P * pad_px * (double)p.C * p.K / d.mfma_f16_flops;
         t_vec = P * pad_px * (9.0 * p.C * ktiles + epi_ops) / lane_ops_per_s;
-    } else if (v.vkind == VK_DWPW_MMC) {
+    } else if (v.vkind == VK_DWPW_MMW) {
         // block-diagonal depthwise products (320 flop-equivalents per channel and
         // pixel) recomputed for every K tile
         t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * p.C * ktiles) / d.mfma_f16_flops;
@@ -528,7 +546,7 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     pl.tile_w = v.tw;
     pl.k_tile = v.kt;
     pl.c_chunk = v.cc;
-    pl.waves_per_wg = 4;
+    pl.waves_per_wg = v.waves;
     pl.wgs_per_cu = be.wgs_per_cu;
     pl.num_tiles = be.num_tiles;
     pl.grid = be.grid;
@@ -538,13 +556,17 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     pl.w1_packed_bytes =
         (int64_t)(p->kind == FCM_KIND_B2B ? (int64_t)p->K1 * p->R * p->S * p->C
                                           : (int64_t)p->R * p->S * p->C) * e;
+    // DWPW, 16-bit storage: [K][C] followed by the same filters in 32 x 32 blocks in
+    // matrix-operand order (pw_blocked_elems), read by the wide-layer kernel
     pl.w2_packed_bytes = (int64_t)p->K * n1 * e;
+    if (p->kind == FCM_KIND_DWPW && p->dtype != FCM_F32)
+        pl.w2_packed_bytes += pw_blocked_elems(p->K, p->C) * e;
     pl.workspace_bytes = (int64_t)p->N * Ho * Wo * n1 * e;
     const int64_t x_bytes = (int64_t)p->N * p->H * p->W * p->C * e;
     const int64_t y_bytes = (int64_t)p->N * Ho * Wo * p->K * e;
     // epilogue arrays are counted as passed: scale and bias for both layers
     const int64_t epi = (int64_t)4 * 2 * (n1 + p->K);
-    pl.alg_bytes_fused = x_bytes + y_bytes + pl.w1_packed_bytes + pl.w2_packed_bytes + epi;
+    pl.alg_bytes_fused = x_bytes + y_bytes + pl.w1_packed_bytes + (int64_t)p->K * n1 * e + epi;
     pl.alg_bytes_unfused = pl.alg_bytes_fused + 2 * pl.workspace_bytes;
     pl.pred_bytes_fused = be.pred;
     int64_t pu = 0;

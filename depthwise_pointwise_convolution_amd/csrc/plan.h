@@ -1,13 +1,22 @@
 // plan.h -- the gfx950 FusePlanner (host only, no HIP dependency).
 #pragma once
 
+#include <stdint.h>
+
 #include <string>
 
 #include "../../include/fcm.h"
 
 namespace fcm {
 
-enum VKind { VK_DWPW = 0, VK_DWPW32 = 1, VK_B2B = 2, VK_DWPW_MM = 3, VK_DWPW_MMC = 4, VK_B2B_MM = 5 };
+enum VKind {
+    VK_DWPW = 0,
+    VK_DWPW32 = 1,
+    VK_B2B = 2,
+    VK_DWPW_MM = 3,
+    VK_B2B_MM = 5,
+    VK_DWPW_MMW = 6
+};
 
 struct VariantDesc {
     const char* name;
@@ -21,6 +30,8 @@ struct VariantDesc {
     int nbuf;    // input tile buffers in LDS (matrix-core DW only)
     int k1;      // back-to-back: intermediate channels compiled in (0 otherwise)
     int occ;     // waves per SIMD the kernel is compiled to allow (register budget)
+    int waves;   // waves per workgroup
+    int cmax;    // largest C the variant takes (0: no limit)
 };
 
 extern const VariantDesc kVariants[];
@@ -42,6 +53,15 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why);
 // Fill *out for problem p with variant `forced` (or the cheapest one if forced < 0).
 fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int forced,
                         fcm_plan_t* out, std::string* err);
+
+// Elements of the blocked copy of [K][C] pointwise filters: K and C rounded up to
+// multiples of 32, zero filled.  Block (g, s, h) of 64 lanes x 8 elements holds, for
+// lane l = 16 * lg + r and element e, filter [32g + 8(r/4) + 4h + r%4][32s + 8lg + e]:
+// the A operand of one v_mfma_f32_16x16x32 for output rows 32g.. and input channels
+// 32s.., in one contiguous kilobyte.  Blocks are ordered (g, s, h).
+inline int64_t pw_blocked_elems(int K, int C) {
+    return (int64_t)((K + 31) / 32 * 32) * ((C + 31) / 32 * 32);
+}
 
 // Output extent of a convolution.
 inline int conv_out(int in, int pad, int filt, int stride) {

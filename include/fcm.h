@@ -178,7 +178,10 @@ const char* fcm_variant_name(int32_t variant);
  * inference", FCM paper Sec. III-B): converts PyTorch-layout filters into the
  * layouts the kernels read.
  *   DWPW: w1_src depthwise [C][R][S]      -> w1_dst [R*S][C]      (channel fastest)
- *         w2_src pointwise [K][C]         -> w2_dst [K][C]        (copied as is)
+ *         w2_src pointwise [K][C]         -> w2_dst [K][C]        (copied as is), and for
+ *                                            fp16/bf16 followed by the same filters in
+ *                                            32x32 blocks in matrix-operand order (K and C
+ *                                            rounded up to multiples of 32, zero filled)
  *   B2B:  w1_src standard  [K1][C][R][S]  -> w1_dst [K1][R*S][C]  (channel fastest)
  *         w2_src 1x1       [K][K1]        -> w2_dst [K][K1]
  * Sizes in bytes are plan->w1_packed_bytes / w2_packed_bytes.  Either pair may be
@@ -187,7 +190,8 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                             const void* w2_src, void* w2_dst, void* stream);
 
 /* Fused DW -> PW module (FCM DWPW).  x: [N][H][W][C]; w_dw: packed [R*S][C];
- * w_pw: packed [K][C]; scale1/bias1: [C] or NULL; scale2/bias2: [K] or NULL;
+ * w_pw: as fcm_pack_weights writes it (plan->w2_packed_bytes: [K][C], then for fp16/bf16
+ * the blocked copy); scale1/bias1: [C] or NULL; scale2/bias2: [K] or NULL;
  * y: [N][Ho][Wo][K].  plan->prob.kind must be FCM_KIND_DWPW. */
 fcm_status fcm_dwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
                         const float* scale1, const float* bias1, const void* w_pw,

@@ -71,6 +71,8 @@ CASES_INT = [
     ("dwpw", "bf16", 2, 11, 17, 128, 128, None, 1, 1, "none", "relu", False),
     ("dwpw", "f16", 1, 13, 15, 256, 512, None, 2, 1, "relu6", "relu6", True),
     ("dwpw", "f16", 2, 7, 7, 1024, 1024, None, 1, 1, "relu6", "relu6", True),
+    ("dwpw", "bf16", 2, 10, 13, 192, 136, None, 2, 1, "relu", "relu6", True),
+    ("dwpw", "f16", 3, 2, 3, 64, 72, None, 1, 1, "none", "relu", True),
     ("dwpw", "bf16", 2, 12, 10, 40, 24, None, 2, 0, "relu", "none", True),
     ("dwpw", "f32", 1, 16, 16, 32, 32, None, 1, 1, "none", "none", False),
     ("dwpw", "f32", 2, 9, 13, 40, 72, None, 2, 1, "relu6", "relu", True),
@@ -101,6 +103,33 @@ def test_integer_probes_bit_exact_every_variant(case):
         assert bad.size == 0, f"variant {v}: {len(bad)} mismatches, first {bad[:3].tolist()}"
     got, _ = run_gpu(wl, inp, path="unfused")
     assert np.array_equal(got, ref), "layer-by-layer path"
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_integer_exact_every_variant(name):
+    """Every variant able to run the full-size workload, on exact integer inputs with the
+    activations switched off (a clamp could hide a wrong value), into an output filled
+    with NaN first: every element must be written, and equal the oracle's bit for bit."""
+    import dataclasses
+    import torch
+    from depthwise_pointwise_convolution_amd.module import TORCH_DTYPES, from_workload
+    wl = dataclasses.replace(fcm_inputs.WORKLOADS[name], act1="none", act2="none")
+    inp = int_inputs(wl, seed=11)
+    ref = oracle_full(wl, inp)
+    x = torch.from_numpy(inp["x"]).to(TORCH_DTYPES[wl.dtype]).cuda()
+    variants = all_variants_for(wl)
+    assert variants
+    for v in variants:
+        _log(f"case {name} exact variant {v}")
+        mod = from_workload(wl, inp, device="cuda", variant=v)
+        y = mod.new_output("cuda")
+        for rep in range(2):
+            y.fill_(float("nan"))
+            mod.fused(x, y)
+            got = y.double().cpu().numpy()
+            bad = np.argwhere(~(got == ref))
+            assert bad.size == 0, (f"variant {v} run {rep}: {len(bad)} wrong or unwritten, "
+                                   f"first {bad[:4].tolist()}")
 
 
 def _random_cases(n, seed):
