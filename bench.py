@@ -35,6 +35,9 @@ COPY_BYTES = 256 * 1024 * 1024   # plain copy used to calibrate the byte counter
 COPY_STEPS = 5                   # copies a calibration run makes (--mode copy --steps 5)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["depthwise_pointwise_convolution_amd/csrc/kernels/dwpw_mm.hip",
+                  "depthwise_pointwise_convolution_amd/csrc/kernels/dwpw_mmw.hip",
+                  "depthwise_pointwise_convolution_amd/csrc/kernels/b2b_mm.hip",
+                  "depthwise_pointwise_convolution_amd/csrc/kernels/mm_common.h",
                   "depthwise_pointwise_convolution_amd/csrc/kernels/dwpw.hip",
                   "depthwise_pointwise_convolution_amd/csrc/kernels/stages.h",
                   "depthwise_pointwise_convolution_amd/csrc/kernels/common.h",

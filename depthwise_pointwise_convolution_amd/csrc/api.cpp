@@ -48,8 +48,9 @@ const VariantImpl kImpls[] = {
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
     {launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>},
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC) {launch_b2b_mm<CT, S, OCC>, occ_b2b_mm<CT, S, OCC>},
-#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, OCC) \
-    {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, OCC>, occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, OCC>},
+#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
+    {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>,           \
+     occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32

@@ -1,5 +1,5 @@
 // dwpw_mmw.hip -- fused depthwise 3x3 -> pointwise 1x1 on the gfx950 matrix cores for
-// wide layers (C a multiple of 64, K up to 512 per workgroup): 8 waves per workgroup,
+// layers with C a multiple of 64 (K up to 512 per workgroup): NW = 4 or 8 waves,
 // the input channels streamed in 64-channel chunks with two chunks in flight, the
 // pointwise accumulators held in registers across the chunks (output stationary, FCM
 // paper "Fusing Depthwise and Pointwise Convolutions for Efficient Inference on GPUs",
@@ -42,10 +42,11 @@
 
 namespace fcm {
 
-template <typename T, int S, int TH, int TW, int KT, int CMAX, int OCC>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void dwpw_mmw_kernel(KArgs a) {
-    constexpr int NW = 8, NT = 64 * NW, CC = 64, NB = 3;
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    constexpr int NT = 64 * NW, CC = 64, NB = 3;
     constexpr int NPX = TH * TW, MB = (NPX + 15) / 16;
     constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3, NPIX = IH * IW;
     constexpr int CH = CC / 8;  // 16-byte pieces per pixel
@@ -61,6 +62,8 @@ void dwpw_mmw_kernel(KArgs a) {
     constexpr int NST = MB * (KBW / 2);  // buffer stores per lane per finished tile
     static_assert(R + NST < 64 && 2 * R < 64, "vmcnt range");
     static_assert(CMAX % 64 == 0, "whole chunks");
+    // registers allow the depthwise operands of the next step to be held across phase B
+    constexpr bool PREA = MB * KBW <= 16;
 
     __shared__ __attribute__((aligned(16))) u32x4 xs[NB * SLOTS_P];
     __shared__ __attribute__((aligned(16))) u32x4 tl0[MB * NKS * 64];
@@ -258,41 +261,59 @@ void dwpw_mmw_kernel(KArgs a) {
     const uint32_t tls_w =
         (uint32_t)(((2 * (cbw & 1) + (lg >> 1)) * 16 + lr) * 16 + (lg & 1) * 8);
 
-    // phase A of one step: xs chunk c -> intermediate chunk
-    auto phase_a = [&](const u32x4* src, u32x4* dst, int c) {
+    // phase A of one step: xs chunk c -> intermediate chunk, in two halves: the LDS
+    // reads (operands of the depthwise products) and the products, epilogue 1 and the
+    // intermediate writes, so that the reads can be in flight during phase B
+    struct AIn {
+        uint32_t h[NTP];
+        f32x4 s, b;
+        u32x4 xv[NTP][PPW];
+    };
+    auto phase_a_load = [&](const u32x4* src, int c, AIn& in) {
         const char* xb = reinterpret_cast<const char*>(src);
         const int cb = c * 4 + cbw;
+#pragma unroll
+        for (int tp = 0; tp < NTP; ++tp) {
+            const int t = 2 * tp + (lg >> 1);
+            in.h[tp] = wds16[(t < 9 ? t : 0) * CMAX + cb * 16 + lr];
+        }
+        in.s = *reinterpret_cast<const f32x4*>(s1s + cb * 16 + lg * 4);
+        in.b = *reinterpret_cast<const f32x4*>(b1s + cb * 16 + lg * 4);
+#pragma unroll
+        for (int tp = 0; tp < NTP; ++tp)
+#pragma unroll
+            for (int j = 0; j < PPW; ++j)
+                in.xv[tp][j] = *reinterpret_cast<const u32x4*>(xb + xoff[j][tp]);
+    };
+    auto phase_a_compute = [&](const AIn& in, u32x4* dst) {
         u32x4 wf[NTP];
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
             const int t = 2 * tp + (lg >> 1);
-            const uint32_t h = wds16[(t < 9 ? t : 0) * CMAX + cb * 16 + lr];
-            const uint32_t v = (dw_active && t < 9) ? h : 0u;
+            const uint32_t v = (dw_active && t < 9) ? in.h[tp] : 0u;
             wf[tp] = dw_operand((dw_e & 1) ? (v << 16) : v);
         }
-        const f32x4 s1v = *reinterpret_cast<const f32x4*>(s1s + cb * 16 + lg * 4);
-        const f32x4 b1v = *reinterpret_cast<const f32x4*>(b1s + cb * 16 + lg * 4);
         f32x4 d[PPW];
 #pragma unroll
         for (int j = 0; j < PPW; ++j) d[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tp = 0; tp < NTP; ++tp) {
-            u32x4 xv[PPW];
+        for (int tp = 0; tp < NTP; ++tp)
 #pragma unroll
-            for (int j = 0; j < PPW; ++j)
-                xv[j] = *reinterpret_cast<const u32x4*>(xb + xoff[j][tp]);
-#pragma unroll
-            for (int j = 0; j < PPW; ++j) d[j] = mfma<T>(wf[tp], xv[j], d[j]);
-        }
+            for (int j = 0; j < PPW; ++j) d[j] = mfma<T>(wf[tp], in.xv[tp][j], d[j]);
 #pragma unroll
         for (int j = 0; j < PPW; ++j) {
             const int mb = (wave >> 2) + j * (NW / 4);
             float v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = epilogue(d[j][i], s1v[i], b1v[i], act1);
+            for (int i = 0; i < 4; ++i) v[i] = epilogue(d[j][i], in.s[i], in.b[i], act1);
             *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
                                       ((mb * NKS + (cbw >> 1)) * 64) * 16 + tls_w) = pack8<T>(v);
         }
+    };
+    auto phase_a = [&](const u32x4* src, u32x4* dst, int c) {
+        AIn in;
+        phase_a_load(src, c, in);
+        phase_a_compute(in, dst);
     };
     // phase B of one step: acc += pointwise filters x intermediate chunk
     f32x4 acc[MB][KBW];
@@ -379,14 +400,26 @@ void dwpw_mmw_kernel(KArgs a) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own intermediate writes done
         __builtin_amdgcn_s_barrier();
         const Step n3 = next(nn);
-        load_pw(nx, pwo1);
+        if (nch > 1) load_pw(nx, pwo1);  // (one chunk: the operands never change)
         const int xa = xi == 2 ? 0 : xi + 1;
         issue_chunk(n3, xs + xi * SLOTS_P);
-        if (nx.t.n < a.N) phase_a(xs + xa * SLOTS_P, par ? tl0 : tl1, nx.c);
-        phase_b(par ? tl1 : tl0, pwo0);
+        // phase A runs even for a step past the last tile (its chunk was zero-filled and
+        // its intermediate is never read); with few accumulators its LDS reads are
+        // issued before phase B and consumed after it
+        if constexpr (PREA) {
+            AIn ain;
+            phase_a_load(xs + xa * SLOTS_P, nx.c, ain);
+            __builtin_amdgcn_sched_barrier(0);  // (keep the order: reads, B, A)
+            phase_b(par ? tl1 : tl0, pwo0);
+            __builtin_amdgcn_sched_barrier(0);
+            phase_a_compute(ain, par ? tl0 : tl1);
+        } else {
+            phase_a(xs + xa * SLOTS_P, par ? tl0 : tl1, nx.c);
+            phase_b(par ? tl1 : tl0, pwo0);
+        }
         stored = cur.c == nch - 1;
         if (stored) finish(cur.t);
-        pwo0 = pwo1;
+        if (nch > 1) pwo0 = pwo1;
         cur = nx;
         nx = nn;
         nn = n3;
@@ -397,18 +430,18 @@ void dwpw_mmw_kernel(KArgs a) {
     mm::wait_vmcnt<0>();
 }
 
-template <typename T, int S, int TH, int TW, int KT, int CMAX, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
 int launch_dwpw_mmw(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((dwpw_mmw_kernel<T, S, TH, TW, KT, CMAX, OCC>), dim3(grid), dim3(512), 0,
+    hipLaunchKernelGGL((dwpw_mmw_kernel<T, S, TH, TW, KT, CMAX, NW, OCC>), dim3(grid), dim3(64 * NW), 0,
                        (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
-template <typename T, int S, int TH, int TW, int KT, int CMAX, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
 int occ_dwpw_mmw() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dwpw_mmw_kernel<T, S, TH, TW, KT, CMAX, OCC>,
-                                                     512, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dwpw_mmw_kernel<T, S, TH, TW, KT, CMAX, NW, OCC>,
+                                                     64 * NW, 0) != hipSuccess)
         return 0;
     return n;
 }
@@ -418,9 +451,9 @@ int occ_dwpw_mmw() {
 #define FCM_V_B2B(...)
 #define FCM_V_DWPW_MM(...)
 #define FCM_V_B2B_MM(...)
-#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, OCC)                              \
-    template int launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, OCC>(const KArgs&, int, void*); \
-    template int occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, OCC>();
+#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC)                        \
+    template int launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>(const KArgs&, int, void*); \
+    template int occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>();
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32

@@ -44,8 +44,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, 4, 0},
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC) \
     {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC, 4, 0},
-#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, OCC) \
-    {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, 8, CMAX},
+#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
+    {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -118,8 +118,9 @@ int variant_lds_bytes(const VariantDesc& v) {
     case VK_DWPW_MMW: {
         // three input chunk buffers (rounded to whole 512-thread load rounds), two
         // intermediate chunks of 16-pixel blocks, epilogue-2 constants of the K tile
+        const int nt = 64 * v.waves;
         const int slots = IH * IW * (v.cc / 8);
-        const int slots_p = (slots + 511) / 512 * 512;
+        const int slots_p = (slots + nt - 1) / nt * nt;
         const int mb = (P + 15) / 16;
         return v.nbuf * slots_p * 16 + 2 * mb * (v.cc / 32) * 64 * 16 + 2 * v.kt * 4 +
                v.cmax * (9 * 2 + 2 * 4);
@@ -162,10 +163,10 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         // per wave: accumulators of its KT/8 output channels for every 16-pixel block,
         // two sets of pointwise operands, depthwise operands and operand offsets, the
         // direct-load plan, staging and addressing
-        const int mb = (P + 15) / 16, kbw = v.kt / 128;
+        const int mb = (P + 15) / 16, kbw = v.kt / (16 * v.waves), nt = 64 * v.waves;
+        const int ppw = mb * 4 / v.waves;
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
-        return 4 * mb * kbw + 16 * kbw + 28 + 5 * (mb / 2) + 2 * ((slots + 511) / 512) + 36 +
-               24;
+        return 4 * mb * kbw + 16 * kbw + 28 + 5 * ppw + 2 * ((slots + nt - 1) / nt) + 36 + 24;
     }
     default: {
         const int KB1 = v.k1 / 16, KB2 = v.kt / 16, KS2 = v.k1 / 32;
