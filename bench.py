@@ -34,24 +34,24 @@ MALL_BYTES = 256 * 1024 * 1024   # Infinity Cache
 COPY_BYTES = 256 * 1024 * 1024   # plain copy used to calibrate the byte counters
 COPY_STEPS = 5                   # copies a calibration run makes (--mode copy --steps 5)
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["depthwise_pointwise_convolution_amd/csrc/kernels/dwpw_mm.hip",
-                  "depthwise_pointwise_convolution_amd/csrc/kernels/dwpw_mmw.hip",
-                  "depthwise_pointwise_convolution_amd/csrc/kernels/b2b_mm.hip",
-                  "depthwise_pointwise_convolution_amd/csrc/kernels/mm_common.h",
-                  "depthwise_pointwise_convolution_amd/csrc/kernels/dwpw.hip",
-                  "depthwise_pointwise_convolution_amd/csrc/kernels/stages.h",
-                  "depthwise_pointwise_convolution_amd/csrc/kernels/common.h",
-                  "depthwise_pointwise_convolution_amd/csrc/variants.def"]
+KDIR = "depthwise_pointwise_convolution_amd/csrc/kernels/"
+# source file of each fused kernel family (by variant-name prefix) and the headers they share
+KERNEL_FILES = [("mmw_", "dwpw_mmw.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
+                ("dwpw_", "dwpw.hip"), ("b2b_", "b2b.hip")]
+SHARED_SOURCES = ["mm_common.h", "stages.h", "common.h"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(variant: str) -> str:
+    """Hash of the sources a variant's kernel is compiled from: a change there makes its
+    stored counter figures stale."""
+    own = next(f for prefix, f in KERNEL_FILES if variant.startswith(prefix))
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for p in [own] + SHARED_SOURCES:
+        with open(os.path.join(ROOT, KDIR, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -64,7 +64,7 @@ def measured_traffic(workload: str, variant: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_hash():
+    if t.get("kernel_source_sha") != kernel_source_hash(variant):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -109,8 +109,7 @@ def summarize_pmc(workload: str, kernel: str, last: int, fetch_csv: str, write_c
             "fetch_kib": fetch, "write_kib": write, "copy_fetch_kib": cf, "copy_write_kib": cw,
             "copy_bytes": copy_bytes, "scale_fetch": k_fetch, "scale_write": k_write,
             "hbm_read_bytes_per_launch": int(read_b), "hbm_write_bytes_per_launch": int(write_b),
-            "hbm_bytes_per_launch": int(read_b + write_b),
-            "kernel_source_sha": kernel_source_hash()}
+            "hbm_bytes_per_launch": int(read_b + write_b)}
 
 
 def time_graph(fn_list, steps, warmup, torch, stream):
@@ -213,6 +212,7 @@ def main(argv=None) -> int:
         t = summarize_pmc(args.workload, args.kernel, args.steps, *args.summarize_pmc,
                           copy_bytes=COPY_BYTES)
         t["variant"] = args.variant_name
+        t["kernel_source_sha"] = kernel_source_hash(args.variant_name)
         path = os.path.join(PROFILES, f"traffic_{args.variant_name}_{args.workload}.json")
         with open(path, "w") as f:
             json.dump(t, f, indent=1)

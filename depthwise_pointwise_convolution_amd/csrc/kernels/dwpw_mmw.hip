@@ -62,8 +62,6 @@ void dwpw_mmw_kernel(KArgs a) {
     constexpr int NST = MB * (KBW / 2);  // buffer stores per lane per finished tile
     static_assert(R + NST < 64 && 2 * R < 64, "vmcnt range");
     static_assert(CMAX % 64 == 0, "whole chunks");
-    // registers allow the depthwise operands of the next step to be held across phase B
-    constexpr bool PREA = MB * KBW <= 16;
 
     __shared__ __attribute__((aligned(16))) u32x4 xs[NB * SLOTS_P];
     __shared__ __attribute__((aligned(16))) u32x4 tl0[MB * NKS * 64];
@@ -261,9 +259,8 @@ void dwpw_mmw_kernel(KArgs a) {
     const uint32_t tls_w =
         (uint32_t)(((2 * (cbw & 1) + (lg >> 1)) * 16 + lr) * 16 + (lg & 1) * 8);
 
-    // phase A of one step: xs chunk c -> intermediate chunk, in two halves: the LDS
-    // reads (operands of the depthwise products) and the products, epilogue 1 and the
-    // intermediate writes, so that the reads can be in flight during phase B
+    // phase A of one step: xs chunk c -> intermediate chunk (the LDS reads of the
+    // depthwise operands, then the products, epilogue 1 and the intermediate writes)
     struct AIn {
         uint32_t h[NTP];
         f32x4 s, b;
@@ -404,19 +401,9 @@ void dwpw_mmw_kernel(KArgs a) {
         const int xa = xi == 2 ? 0 : xi + 1;
         issue_chunk(n3, xs + xi * SLOTS_P);
         // phase A runs even for a step past the last tile (its chunk was zero-filled and
-        // its intermediate is never read); with few accumulators its LDS reads are
-        // issued before phase B and consumed after it
-        if constexpr (PREA) {
-            AIn ain;
-            phase_a_load(xs + xa * SLOTS_P, nx.c, ain);
-            __builtin_amdgcn_sched_barrier(0);  // (keep the order: reads, B, A)
-            phase_b(par ? tl1 : tl0, pwo0);
-            __builtin_amdgcn_sched_barrier(0);
-            phase_a_compute(ain, par ? tl0 : tl1);
-        } else {
-            phase_a(xs + xa * SLOTS_P, par ? tl0 : tl1, nx.c);
-            phase_b(par ? tl1 : tl0, pwo0);
-        }
+        // its intermediate is never read)
+        phase_a(xs + xa * SLOTS_P, par ? tl0 : tl1, nx.c);
+        phase_b(par ? tl1 : tl0, pwo0);
         stored = cur.c == nch - 1;
         if (stored) finish(cur.t);
         if (nch > 1) pwo0 = pwo1;
