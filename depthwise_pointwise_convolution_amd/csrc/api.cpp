@@ -272,8 +272,9 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                              "16-byte aligned");
         const char* s = (const char*)w1_src;
         const char* d = (const char*)w1_dst;
-        const int64_t nb = plan->w1_packed_bytes;
-        if (s < d + nb && d < s + nb) return fail(FCM_ERR_INVALID_ARG, "w1 buffers overlap");
+        const int64_t ns = (int64_t)(p.kind == FCM_KIND_B2B ? p.K1 : 1) * p.R * p.S * p.C * e;
+        const int64_t nd = plan->w1_packed_bytes;
+        if (s < d + nd && d < s + ns) return fail(FCM_ERR_INVALID_ARG, "w1 buffers overlap");
     }
     if (w2_src) {
         if (!aligned(w2_src, e) || !aligned(w2_dst, 16))
@@ -287,10 +288,14 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
     }
     if (w1_src) {
         int rc;
-        if (p.kind == FCM_KIND_DWPW)
+        if (p.kind == FCM_KIND_DWPW) {
             rc = launch_pack_dw(e, w1_src, w1_dst, p.C, p.R * p.S, stream);
-        else
+        } else {
             rc = launch_pack_conv(e, w1_src, w1_dst, p.K1, p.C, p.R * p.S, stream);
+            const int64_t plain = (int64_t)p.K1 * p.R * p.S * p.C * e;
+            if (rc == 0 && plan->w1_packed_bytes > plain)
+                rc = launch_pack_conv_blocked(w1_src, (char*)w1_dst + plain, p.K1, p.C, stream);
+        }
         if (rc != 0)
             return fail(FCM_ERR_HIP, std::string("weight packing failed: ") +
                                          hipGetErrorString((hipError_t)rc));
@@ -299,7 +304,8 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
         const int64_t plain = (int64_t)p.K * (p.kind == FCM_KIND_B2B ? p.K1 : p.C) * e;
         int rc = launch_copy(w2_src, w2_dst, plain, stream);
         if (rc == 0 && plan->w2_packed_bytes > plain)
-            rc = launch_pack_pw_blocked(w2_src, (char*)w2_dst + plain, p.K, p.C, stream);
+            rc = launch_pack_pw_blocked(w2_src, (char*)w2_dst + plain, p.K,
+                                        p.kind == FCM_KIND_B2B ? p.K1 : p.C, stream);
         if (rc != 0)
             return fail(FCM_ERR_HIP, std::string("weight copy failed: ") +
                                          hipGetErrorString((hipError_t)rc));

@@ -35,7 +35,6 @@ void b2b_mm_kernel(KArgs a) {
     constexpr int NKS2 = K1T / 32;       // reduction steps of the 1x1 conv
     constexpr int KB2 = KT / 16;         // 16-channel output blocks of a wave's row
     constexpr int NST = 2;               // stores per lane per step
-    constexpr uint32_t ROW_BYTES = (uint32_t)S * IW * CH * 16;
 
     __shared__ __attribute__((aligned(16))) u32x4 xs0[SLOTS_P];
     __shared__ __attribute__((aligned(16))) u32x4 xs1[SLOTS_P];
@@ -136,17 +135,31 @@ void b2b_mm_kernel(KArgs a) {
         }
     };
 
+    // the first two tiles' input goes out before anything else, so that its latency
+    // overlaps that of the resident operands below
+    Pos cur = split(L);
+    Pos nxt = advance(cur);
+    issue_tile(cur, std::integral_constant<int, 0>{});
+    issue_tile(nxt, std::integral_constant<int, 1>{});
+
     // ---- resident operands -------------------------------------------------------------
-    // 3x3 filters of intermediate channels [16w, 16w+16), packed [K1][9][C]: operand of
-    // reduction step ks = (tap ks/2, channel half ks%2), lane (l%16, l/16): channel
-    // 16w + l%16, input channels 32(ks%2) + 8(l/16) + [0,8)
+    // 3x3 filters of intermediate channels [16w, 16w+16): operand of reduction step
+    // ks = (tap ks/2, channel half ks%2) is block (w, ks/2, ks%2) of the blocked copy
+    // after the plain [K1][9][C] array (one contiguous kilobyte, zero where the channel
+    // does not exist); lane (l%16, l/16): channel 16w + l%16, input channels
+    // 32(ks%2) + 8(l/16) + [0,8)
+    const u32x4* __restrict__ w1b =
+        reinterpret_cast<const u32x4*>(w1 + (int64_t)a.K1 * 9 * a.C);
+    // a wave whose 16 channels lie past K1 gets zero operands: its intermediate channels
+    // are then exactly 0, which the clamped 1x1 operands below rely on
+    const bool w1live = 16 * wave < a.K1;
+    const int w1g = w1live ? wave : 0;
     u32x4 wa1[NK1];
 #pragma unroll
-    for (int ks = 0; ks < NK1; ++ks) {
-        const int k1 = 16 * wave + lr, t = ks >> 1, c = 32 * (ks & 1) + 8 * lg;
-        const bool ok = k1 < a.K1 && c < a.C;
-        const u32x4 v = ld16(w1 + ((int64_t)(ok ? k1 : 0) * 9 + t) * a.C + (ok ? c : 0));
-        wa1[ks] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < NK1; ++ks) wa1[ks] = w1b[(w1g * NK1 + ks) * 64 + lane];
+    if (!w1live) {
+#pragma unroll
+        for (int ks = 0; ks < NK1; ++ks) wa1[ks] = u32x4{0u, 0u, 0u, 0u};
     }
     float s1r[4], b1r[4];
 #pragma unroll
@@ -158,20 +171,21 @@ void b2b_mm_kernel(KArgs a) {
         s1r[i] = ok ? sv : 1.0f;
         b1r[i] = ok ? bv : 0.0f;
     }
-    // 1x1 filters, [K][K1]: operand of step ks2, block kb: row kperm<64>(kb, l%16),
-    // intermediate channels 32ks2 + 4(l/16) + [0,4) and 32ks2 + 16 + 4(l/16) + [0,4)
+    // 1x1 filters: operand of step ks2, block kb is block (kb/2, ks2, kb%2) of the
+    // blocked copy after the plain [K][K1] array: row 32(kb/2) + 8(r/4) + 4(kb%2) + r%4 for
+    // lane row r, intermediate channels 32ks2 + 8(l/16) + [0,8).  Blocks past K or K1 are
+    // clamped to existing ones: their rows are never stored, and the intermediate channels
+    // they would multiply are zero.
+    const u32x4* __restrict__ w2b = reinterpret_cast<const u32x4*>(w2 + (int64_t)a.K * a.K1);
+    const int g2max = (a.K + 31) / 32 - 1, s2max = (a.K1 + 31) / 32 - 1;
+    const int s32_2 = s2max + 1;
     u32x4 wa2[NKS2][KB2];
 #pragma unroll
     for (int ks2 = 0; ks2 < NKS2; ++ks2)
 #pragma unroll
         for (int kb = 0; kb < KB2; ++kb) {
-            const int ko = kperm<KT>(kb, lr), c = ks2 * 32 + lg * 4;
-            const bool ok_lo = ko < a.K && c < a.K1, ok_hi = ko < a.K && c + 16 < a.K1;
-            const T* row = w2 + (int64_t)(ko < a.K ? ko : 0) * a.K1;
-            const uint2 lo = *reinterpret_cast<const uint2*>(row + (ok_lo ? c : 0));
-            const uint2 hi = *reinterpret_cast<const uint2*>(row + (ok_hi ? c + 16 : 0));
-            wa2[ks2][kb] = u32x4{ok_lo ? lo.x : 0u, ok_lo ? lo.y : 0u, ok_hi ? hi.x : 0u,
-                                 ok_hi ? hi.y : 0u};
+            const int g = min(kb >> 1, g2max), sl = min(ks2, s2max);
+            wa2[ks2][kb] = w2b[((g * s32_2 + sl) * 2 + (kb & 1)) * 64 + lane];
         }
     // epilogue-2 constants in LDS (read back four at a time per use: registers are
     // the scarce resource of this kernel)
@@ -185,36 +199,51 @@ void b2b_mm_kernel(KArgs a) {
     }
     const float* const S2 = s2s;
     const float* const B2 = b2s;
-    // LDS byte offsets of the lane's 3x3 input operand in output row 0, per step
-    uint32_t xoff[NK1];
+    // LDS byte offsets of the lane's 3x3 input operand in input row 0, per filter column
+    // dw and channel half (input row ir adds ir * IN_ROW_BYTES)
+    constexpr uint32_t IN_ROW_BYTES = (uint32_t)IW * CH * 16;
+    uint32_t xoff[3][2];
 #pragma unroll
-    for (int ks = 0; ks < NK1; ++ks) {
-        const int t = ks >> 1, col = lr * S + t % 3;
-        const int p = (t / 3) * IW + col;
-        const int q = 4 * (ks & 1) + lg;
-        xoff[ks] = (uint32_t)(p * CH + (q ^ (col & 7))) * 16u;
-    }
-    const uint32_t tls_w = (uint32_t)lane * 16u + (uint32_t)(wave & 1) * 8u;
-    // store offsets of the lane's two 8-channel runs within a pixel row (kOob when the
-    // run lies beyond K)
-    const uint32_t st0 = 16 * lg < a.K ? (uint32_t)(lr * a.K + 16 * lg) * (uint32_t)es : mm::kOob;
+    for (int dw = 0; dw < 3; ++dw)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = lr * S + dw, q = 4 * h + lg;
+            xoff[dw][h] = (uint32_t)(col * CH + (q ^ (col & 7))) * 16u;
+        }
+    // intermediate: conv1 output rows 4(l/16)+i of wave w's 16 channels are channels
+    // 16(w%2) + 4(l/16) + i of 32-channel slice w/2, i.e. lane group 2(w%2) + (l/16)/2,
+    // bytes 8((l/16)%2)..+7 of its 16-byte operand (the 1x1 operand's natural order)
+    const uint32_t tls_w =
+        (uint32_t)(((2 * (wave & 1) + (lg >> 1)) * 16 + lr) * 16 + (lg & 1) * 8);
+    // store offsets of the lane's two 8-channel runs (output channels 8(l/16) and
+    // 32 + 8(l/16)) within a pixel row (kOob when the run lies beyond K)
+    const uint32_t st0 = 8 * lg < a.K ? (uint32_t)(lr * a.K + 8 * lg) * (uint32_t)es : mm::kOob;
     const uint32_t st1 =
-        16 * lg + 8 < a.K ? (uint32_t)(lr * a.K + 16 * lg + 8) * (uint32_t)es : mm::kOob;
+        32 + 8 * lg < a.K ? (uint32_t)(lr * a.K + 32 + 8 * lg) * (uint32_t)es : mm::kOob;
 
     auto phase_a = [&](const u32x4* src, u32x4* dst) {
         const char* xb = reinterpret_cast<const char*>(src);
         f32x4 d[TH];
 #pragma unroll
         for (int r = 0; r < TH; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // walk the input rows: the operand of input row ir, filter column dw and channel
+        // half h is read once and used by every output row r = (ir - dh) / S it feeds
+        // (filter row dh), instead of once per (output row, tap)
 #pragma unroll
-        for (int ks = 0; ks < NK1; ++ks) {
-            u32x4 xv[TH];
+        for (int ir = 0; ir < IH; ++ir)
 #pragma unroll
-            for (int r = 0; r < TH; ++r)
-                xv[r] = *reinterpret_cast<const u32x4*>(xb + xoff[ks] + r * ROW_BYTES);
+            for (int dw = 0; dw < 3; ++dw)
 #pragma unroll
-            for (int r = 0; r < TH; ++r) d[r] = mfma<T>(wa1[ks], xv[r], d[r]);
-        }
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 xv =
+                        *reinterpret_cast<const u32x4*>(xb + xoff[dw][h] + ir * IN_ROW_BYTES);
+#pragma unroll
+                    for (int dh = 0; dh < 3; ++dh) {
+                        const int r = (ir - dh) / S;
+                        if (ir - dh >= 0 && (ir - dh) % S == 0 && r < TH)
+                            d[r] = mfma<T>(wa1[(dh * 3 + dw) * 2 + h], xv, d[r]);
+                    }
+                }
 #pragma unroll
         for (int r = 0; r < TH; ++r) {
             float v[4];
@@ -234,12 +263,14 @@ void b2b_mm_kernel(KArgs a) {
 #pragma unroll
             for (int kb = 0; kb < KB2; ++kb) acc[kb] = mfma<T>(wa2[ks2][kb], bfr, acc[kb]);
         }
-        // lane holds output channels 16(l/16) + 4kb + [0,4) of pixel l%16 in row w
+        // lane holds output channels 32(kb/2) + 8(l/16) + 4(kb%2) + [0,4) of pixel l%16
+        // in row w: runs of 8 at 8(l/16) (kb 0, 1) and 32 + 8(l/16) (kb 2, 3)
         float o[16];
 #pragma unroll
         for (int kb = 0; kb < KB2; ++kb) {
-            const f32x4 sc = *reinterpret_cast<const f32x4*>(S2 + 16 * lg + 4 * kb);
-            const f32x4 bi = *reinterpret_cast<const f32x4*>(B2 + 16 * lg + 4 * kb);
+            const int ch = 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1);
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(S2 + ch);
+            const f32x4 bi = *reinterpret_cast<const f32x4*>(B2 + ch);
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[4 * kb + i] = epilogue(acc[kb][i], sc[i], bi[i], act2);
         }
@@ -254,12 +285,9 @@ void b2b_mm_kernel(KArgs a) {
 
     // ---- software-pipelined tile loop (see dwpw_mm.hip): step i waits for tile i+1's
     // input (only step i-1's NST stores were issued after it), barrier, requests tile
-    // i+2, phase A of tile i+1, phase B of tile i
-    Pos cur = split(L);
-    Pos nxt = advance(cur);
-    issue_tile(cur, std::integral_constant<int, 0>{});
-    issue_tile(nxt, std::integral_constant<int, 1>{});
-    mm::wait_vmcnt<R>();
+    // i+2, phase A of tile i+1, phase B of tile i.  (The first two tiles were requested
+    // before the resident operands: both latencies overlap.)
+    mm::wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (cur.n < a.N) phase_a(X0, T0);
     auto step_fn = [&](auto par, bool first) {

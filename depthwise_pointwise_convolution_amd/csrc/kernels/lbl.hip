@@ -259,6 +259,31 @@ int launch_pack_pw_blocked(const void* src, void* dst, int K, int C, void* strea
     return (int)hipGetLastError();
 }
 
+// Blocked copy of 3x3 filters from the PyTorch layout [K1][C][3][3] (layout in plan.h,
+// conv_blocked_elems): one thread per 16-bit destination element, zero where the
+// intermediate or input channel does not exist.
+__global__ void pack_conv_blocked_kernel(const uint16_t* __restrict__ src,
+                                         uint16_t* __restrict__ dst, int K1, int C, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int e = (int)(i & 7), lane = (int)((i >> 3) & 63);
+    const int64_t blk = i >> 9;  // (g * 9 + t) * S32 + s
+    const int S32 = (C + 63) / 64 * 2;
+    const int s = (int)(blk % S32), t = (int)((blk / S32) % 9), g = (int)(blk / S32 / 9);
+    const int lg = lane >> 4, r = lane & 15;
+    const int k1 = 16 * g + r, c = 32 * s + 8 * lg + e;
+    dst[i] = (k1 < K1 && c < C) ? src[((int64_t)k1 * C + c) * 9 + t] : (uint16_t)0;
+}
+
+int launch_pack_conv_blocked(const void* src, void* dst, int K1, int C, void* stream) {
+    const int64_t total = (int64_t)((K1 + 15) / 16 * 16) * 9 * ((C + 63) / 64 * 64);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(pack_conv_blocked_kernel, dim3((unsigned)((total + 255) / 256)),
+                       dim3(256), 0, (hipStream_t)stream, (const uint16_t*)src, (uint16_t*)dst,
+                       K1, C, total);
+    return (int)hipGetLastError();
+}
+
 int launch_copy(const void* src, void* dst, long long bytes, void* stream) {
     return (int)hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDevice,
                                (hipStream_t)stream);

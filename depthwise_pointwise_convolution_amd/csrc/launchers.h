@@ -49,6 +49,7 @@ int launch_pack_dw(int elem_bytes, const void* src, void* dst, int C, int RS, vo
 int launch_pack_conv(int elem_bytes, const void* src, void* dst, int K1, int C, int RS,
                      void* stream);
 int launch_pack_pw_blocked(const void* src, void* dst, int K, int C, void* stream);
+int launch_pack_conv_blocked(const void* src, void* dst, int K1, int C, void* stream);
 int launch_copy(const void* src, void* dst, long long bytes, void* stream);
 
 }  // namespace fcm

@@ -557,17 +557,22 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     pl.w1_packed_bytes =
         (int64_t)(p->kind == FCM_KIND_B2B ? (int64_t)p->K1 * p->R * p->S * p->C
                                           : (int64_t)p->R * p->S * p->C) * e;
-    // DWPW, 16-bit storage: [K][C] followed by the same filters in 32 x 32 blocks in
-    // matrix-operand order (pw_blocked_elems), read by the wide-layer kernel
     pl.w2_packed_bytes = (int64_t)p->K * n1 * e;
-    if (p->kind == FCM_KIND_DWPW && p->dtype != FCM_F32)
-        pl.w2_packed_bytes += pw_blocked_elems(p->K, p->C) * e;
+    if (p->dtype != FCM_F32) {
+        // 16-bit storage: the 1x1 filters again in 32 x 32 blocks in matrix-operand order
+        // (pw_blocked_elems), and for B2B the 3x3 filters in 16 x 32 blocks
+        // (conv_blocked_elems), each after the plain array
+        pl.w2_packed_bytes += pw_blocked_elems(p->K, n1) * e;
+        if (p->kind == FCM_KIND_B2B) pl.w1_packed_bytes += conv_blocked_elems(p->K1, p->C) * e;
+    }
     pl.workspace_bytes = (int64_t)p->N * Ho * Wo * n1 * e;
     const int64_t x_bytes = (int64_t)p->N * p->H * p->W * p->C * e;
     const int64_t y_bytes = (int64_t)p->N * Ho * Wo * p->K * e;
     // epilogue arrays are counted as passed: scale and bias for both layers
     const int64_t epi = (int64_t)4 * 2 * (n1 + p->K);
-    pl.alg_bytes_fused = x_bytes + y_bytes + pl.w1_packed_bytes + (int64_t)p->K * n1 * e + epi;
+    const int64_t w1_bytes = (int64_t)(p->kind == FCM_KIND_B2B ? (int64_t)p->K1 * p->R * p->S * p->C
+                                                               : (int64_t)p->R * p->S * p->C) * e;
+    pl.alg_bytes_fused = x_bytes + y_bytes + w1_bytes + (int64_t)p->K * n1 * e + epi;
     pl.alg_bytes_unfused = pl.alg_bytes_fused + 2 * pl.workspace_bytes;
     pl.pred_bytes_fused = be.pred;
     int64_t pu = 0;

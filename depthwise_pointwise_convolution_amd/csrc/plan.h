@@ -63,6 +63,15 @@ inline int64_t pw_blocked_elems(int K, int C) {
     return (int64_t)((K + 31) / 32 * 32) * ((C + 31) / 32 * 32);
 }
 
+// Elements of the blocked copy of 3x3 filters [K1][9][C] (16-bit storage): K1 rounded up
+// to a multiple of 16, C to a multiple of 64.  Block (g, t, s) of 64 lanes x 8 elements
+// holds, for lane l = 16 * lg + r and element e, filter [16g + r][tap t][32s + 8lg + e]:
+// the A operand of one v_mfma_f32_16x16x32 for intermediate channels 16g.. and input
+// channels 32s.. of tap t, in one contiguous kilobyte.  Blocks are ordered (g, t, s).
+inline int64_t conv_blocked_elems(int K1, int C) {
+    return (int64_t)((K1 + 15) / 16 * 16) * 9 * ((C + 63) / 64 * 64);
+}
+
 // Output extent of a convolution.
 inline int conv_out(int in, int pad, int filt, int stride) {
     return (in + 2 * pad - filt) / stride + 1;

@@ -182,8 +182,12 @@ const char* fcm_variant_name(int32_t variant);
  *                                            fp16/bf16 followed by the same filters in
  *                                            32x32 blocks in matrix-operand order (K and C
  *                                            rounded up to multiples of 32, zero filled)
- *   B2B:  w1_src standard  [K1][C][R][S]  -> w1_dst [K1][R*S][C]  (channel fastest)
- *         w2_src 1x1       [K][K1]        -> w2_dst [K][K1]
+ *   B2B:  w1_src standard  [K1][C][R][S]  -> w1_dst [K1][R*S][C]  (channel fastest), and
+ *                                            for fp16/bf16 followed by the same filters in
+ *                                            16x32 blocks in matrix-operand order (K1
+ *                                            rounded up to 16, C to 64, zero filled)
+ *         w2_src 1x1       [K][K1]        -> w2_dst [K][K1], and for fp16/bf16 followed by
+ *                                            32x32 blocks as for DWPW
  * Sizes in bytes are plan->w1_packed_bytes / w2_packed_bytes.  Either pair may be
  * NULL to skip it.  Source and destination must not overlap. */
 fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1_dst,
@@ -198,7 +202,9 @@ fcm_status fcm_dwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
                         const float* scale2, const float* bias2, void* y, void* stream);
 
 /* Fused standard 3x3 conv -> 1x1 conv (back-to-back).  x: [N][H][W][C];
- * w1: packed [K1][R*S][C]; w2: packed [K][K1]; scale1/bias1: [K1] or NULL;
+ * w1, w2: as fcm_pack_weights writes them (plan->w1_packed_bytes / w2_packed_bytes: the
+ * plain [K1][R*S][C] and [K][K1] arrays, then for fp16/bf16 their blocked copies);
+ * scale1/bias1: [K1] or NULL;
  * scale2/bias2: [K] or NULL; y: [N][Ho][Wo][K].  plan->prob.kind must be
  * FCM_KIND_B2B. */
 fcm_status fcm_b2b_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
