@@ -231,19 +231,23 @@ void dwpw_mm_kernel(KArgs a) {
             b1l[j][i] = b1p[cc];
         }
     }
-    // pointwise A operand of this wave's slice for reduction step ks, block kb: row
-    // kperm<KW>(kb, l%16) of the slice, reduction channels 32ks + 4(l/16) + [0,4) and
-    // 32ks + 16 + 4(l/16) + [0,4) (the order the depthwise result is stored in)
-    uint2 wlo[NKS][KBW], whi[NKS][KBW];
+    // pointwise A operand of this wave's 32-channel slice for reduction step ks, block
+    // kb: block (kw0/32, ks, kb) of the blocked copy after the plain [K][C] array (one
+    // contiguous kilobyte; row kperm<32>(kb, l%16) of the slice, reduction channels
+    // 32ks + 8(l/16) + [0,8), the order the depthwise result is stored in).  Blocks past
+    // K or C are clamped to existing ones: their rows are never stored, and the
+    // intermediate channels they would multiply are zero.
+    static_assert(KW == 32, "one 32-channel block group per wave");
+    const u32x4* __restrict__ wpb = reinterpret_cast<const u32x4*>(wpw + (int64_t)a.K * a.C);
+    u32x4 wa[NKS][KBW];
+    {
+        const int g = min(kw0 >> 5, (a.K + 31) / 32 - 1), s32 = (a.C + 31) / 32;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) {
-            const int ko = kw0 + kperm<KW>(kb, lr), c = ks * 32 + lg * 4;
-            const T* row = wpw + (int64_t)(ko < a.K ? ko : 0) * a.C;
-            wlo[ks][kb] = *reinterpret_cast<const uint2*>(row + (c < a.C ? c : 0));
-            whi[ks][kb] = *reinterpret_cast<const uint2*>(row + (c + 16 < a.C ? c + 16 : 0));
-        }
+            for (int kb = 0; kb < KBW; ++kb)
+                wa[ks][kb] = wpb[((g * s32 + min(ks, s32 - 1)) * 2 + kb) * 64 + lane];
+    }
     // epilogue-2 constants of the lane's output channels kw0 + (KW/4)(l/16) + [0,KW/4)
     float s2r[KW / 4], b2r[KW / 4];
 #pragma unroll
@@ -290,16 +294,6 @@ void dwpw_mm_kernel(KArgs a) {
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) wdf[tp] = dw_operand(wdc[0][tp]);
     }
-    u32x4 wa[NKS][KBW];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) {
-            const int ko = kw0 + kperm<KW>(kb, lr), c = ks * 32 + lg * 4;
-            const bool ok_lo = ko < a.K && c < a.C, ok_hi = ko < a.K && c + 16 < a.C;
-            wa[ks][kb] = u32x4{ok_lo ? wlo[ks][kb].x : 0u, ok_lo ? wlo[ks][kb].y : 0u,
-                               ok_hi ? whi[ks][kb].x : 0u, ok_hi ? whi[ks][kb].y : 0u};
-        }
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
         const bool ok = kw0 + lg * (KW / 4) + i < a.K;
@@ -319,7 +313,11 @@ void dwpw_mm_kernel(KArgs a) {
         const int q = 2 * wave + (lg & 1);
         xoff[tp] = (uint32_t)(p * CH + (q ^ (col & 7))) * 16u;
     }
-    const uint32_t tls_w = (uint32_t)lane * 16u + (uint32_t)(wave & 1) * 8u;
+    // intermediate: depthwise rows 4(l/16)+i of channel block cb are channels
+    // 16(cb%2) + 4(l/16) + i of slice cb/2, i.e. lane group 2(cb%2) + (l/16)/2, bytes
+    // 8((l/16)%2)..+7 of its 16-byte operand (cb % 2 == wave % 2 for every block)
+    const uint32_t tls_w =
+        (uint32_t)(((2 * (wave & 1) + (lg >> 1)) * 16 + lr) * 16 + (lg & 1) * 8);
     // store offset of the lane's first output channel within a pixel row of the tile
     // (kOob when the channel does not exist); the pixel row enters as a scalar offset
     const int kl = kw0 + lg * (KW / 4);
