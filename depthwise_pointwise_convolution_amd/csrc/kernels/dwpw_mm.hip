@@ -196,11 +196,14 @@ void dwpw_mm_kernel(KArgs a) {
     };
 
     // ---- per-wave constants ----------------------------------------------------------
-    // All constant loads are issued first, unconditionally (clamped addresses, absent
-    // epilogue arrays read from another valid tensor), then the first two tiles' input,
-    // and only then are the loaded values used: the wait for the constants does not
-    // also wait for the input (vector-memory operations complete in issue order), and
-    // the two latencies overlap.
+    // The first tile's input is requested first (it comes from HBM, the constants from
+    // L2), then all constants, unconditionally (clamped addresses, absent epilogue
+    // arrays read from another valid tensor), then the second tile's input, and only
+    // then are the loaded values used: the wait for the constants does not also wait
+    // for the second tile (vector-memory operations complete in issue order).
+    Pos cur = split(L / a.num_ktiles);
+    Pos nxt = advance(cur);
+    issue_tile(cur, std::integral_constant<int, 0>{});
     //
     // depthwise: this wave owns channel blocks cb = wave + 4j.  Matrix operand of block
     // cb and tap pair tp, lane (l%16, l/16): row = channel 16cb + l%16, reduction index
@@ -257,10 +260,7 @@ void dwpw_mm_kernel(KArgs a) {
         b2r[i] = b2p[kk];
     }
 
-    // the first two tiles' input
-    Pos cur = split(L / a.num_ktiles);
-    Pos nxt = advance(cur);
-    issue_tile(cur, std::integral_constant<int, 0>{});
+    // the second tile's input
     issue_tile(nxt, std::integral_constant<int, 1>{});
 
     // now the loaded values are used
