@@ -287,13 +287,12 @@ void dwpw_mm_kernel(KArgs a) {
         const int w = dw_e >> 1;
         return u32x4{w == 0 ? v : 0u, w == 1 ? v : 0u, w == 2 ? v : 0u, w == 3 ? v : 0u};
     };
-    // with one block per wave the expanded operands stay in registers for the whole
-    // kernel; with more they are expanded per block and step
-    u32x4 wdf[CBW == 1 ? NTP : 1];
-    if constexpr (CBW == 1) {
+    // the expanded operands stay in registers for the whole kernel
+    u32x4 wdf[CBW][NTP];
 #pragma unroll
-        for (int tp = 0; tp < NTP; ++tp) wdf[tp] = dw_operand(wdc[0][tp]);
-    }
+    for (int j = 0; j < CBW; ++j)
+#pragma unroll
+        for (int tp = 0; tp < NTP; ++tp) wdf[j][tp] = dw_operand(wdc[j][tp]);
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
         const bool ok = kw0 + lg * (KW / 4) + i < a.K;
@@ -324,27 +323,24 @@ void dwpw_mm_kernel(KArgs a) {
     const uint32_t st_lane =
         kl < a.K ? (uint32_t)(lr * a.K + kl) * (uint32_t)sizeof(T) : mm::kOob;
 
+    // Two forms of the tile loop, chosen once per launch: the general one, and one for
+    // layers whose epilogue 1 is the identity (no scale, no bias, no activation) and
+    // whose epilogue 2 has no scale (a CIFAR-style block: bias and activation after the
+    // pointwise layer only).  The second skips epilogue 1 and starts the pointwise
+    // accumulators at the bias, so that epilogue 2 is the activation alone (a quarter of
+    // the vector instructions of a step fewer).  (Instantiating all four combinations made
+    // the general form slower.)
+    const bool id1 = !a.s1 && !a.b1 && a.act1 == 0;
+    const bool bias_init2 = !a.s2;
+
     // phase A of one tile: depthwise on the matrix cores, this wave's channel blocks
     // for all TH rows; epilogue 1; 8 bytes per lane into the intermediate tile, where
     // they form half of a pointwise B operand
-    auto phase_a = [&](const u32x4* src, u32x4* dst, int salt) {
+    auto phase_a = [&](const u32x4* src, u32x4* dst, auto identity1) {
         const char* xb = reinterpret_cast<const char*>(src);
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
-            u32x4 wf[NTP];
-#pragma unroll
-            for (int tp = 0; tp < NTP; ++tp) {
-                if constexpr (CBW == 1) {
-                    wf[tp] = wdf[tp];
-                } else {
-                    // expanded per step: the empty statement takes a loop-variant input,
-                    // so the optimiser cannot hoist all blocks' expanded operands out of
-                    // the loop, while the scheduler may still move it
-                    uint32_t v = wdc[j][tp];
-                    asm("" : "+v"(v) : "s"(salt));
-                    wf[tp] = dw_operand(v);
-                }
-            }
+            const u32x4* wf = wdf[j];
             const int cb = wave + 4 * j;
             // tap pairs outer, rows inner: TH independent accumulation chains, so a
             // product never waits for the previous one of its own chain
@@ -365,7 +361,10 @@ void dwpw_mm_kernel(KArgs a) {
             for (int r = 0; r < TH; ++r) {
                 float o[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = epilogue(d[r][i], s1r[j][i], b1r[j][i], act1);
+                for (int i = 0; i < 4; ++i)
+                    o[i] = decltype(identity1)::value
+                               ? d[r][i]
+                               : epilogue(d[r][i], s1r[j][i], b1r[j][i], act1);
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
                                           ((r * NKS + (cb >> 1)) * 64) * 16 + tls_w) =
                     pack8<T>(o);
@@ -375,7 +374,8 @@ void dwpw_mm_kernel(KArgs a) {
     // phase B of one tile: pointwise on the matrix cores, this wave's KW output
     // channels for all TH rows, epilogue 2, 16-byte stores; always NST stores per lane
     // (rows or lanes outside the output get the out-of-range offset)
-    auto phase_b = [&](const u32x4* src, const Pos& t) {
+    auto phase_b = [&](const u32x4* src, const Pos& t, auto from_bias) {
+        constexpr bool FB = decltype(from_bias)::value;
         u32x4 bfr[TH][NKS];
 #pragma unroll
         for (int mb = 0; mb < TH; ++mb)
@@ -386,7 +386,10 @@ void dwpw_mm_kernel(KArgs a) {
 #pragma unroll
         for (int mb = 0; mb < TH; ++mb)
 #pragma unroll
-            for (int kb = 0; kb < KBW; ++kb) acc[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < KBW; ++kb)
+                acc[mb][kb] = FB ? f32x4{b2r[kb * 4], b2r[kb * 4 + 1], b2r[kb * 4 + 2],
+                                         b2r[kb * 4 + 3]}
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -405,9 +408,14 @@ void dwpw_mm_kernel(KArgs a) {
                 float o[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    o[i] = epilogue(acc[mb][kb][i], s2r[kb * 4 + i], b2r[kb * 4 + i], act2);
-                    o[4 + i] = epilogue(acc[mb][kb + 1][i], s2r[kb * 4 + 4 + i],
-                                        b2r[kb * 4 + 4 + i], act2);
+                    if constexpr (FB) {
+                        o[i] = __builtin_amdgcn_fmed3f(acc[mb][kb][i], act2.lo, act2.hi);
+                        o[4 + i] = __builtin_amdgcn_fmed3f(acc[mb][kb + 1][i], act2.lo, act2.hi);
+                    } else {
+                        o[i] = epilogue(acc[mb][kb][i], s2r[kb * 4 + i], b2r[kb * 4 + i], act2);
+                        o[4 + i] = epilogue(acc[mb][kb + 1][i], s2r[kb * 4 + 4 + i],
+                                            b2r[kb * 4 + 4 + i], act2);
+                    }
                 }
                 // the whole offset goes in the vector operand (scalar offset 0): with a
                 // register scalar offset the compiler omits the wait state that a store
@@ -428,26 +436,30 @@ void dwpw_mm_kernel(KArgs a) {
     // NST stores of step i-1 before step i.
     mm::wait_vmcnt<R>();
     __builtin_amdgcn_s_barrier();
-    if (cur.n < a.N) phase_a(X0, T0, 0);
-    auto step_fn = [&](auto par, bool first) {
-        constexpr int P = decltype(par)::value;
-        if (first) mm::wait_vmcnt<0>(); else mm::wait_vmcnt<NST>();
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own intermediate writes done
-        __builtin_amdgcn_s_barrier();
-        const Pos nn = advance(nxt);
-        issue_tile(nn, std::integral_constant<int, P>{});
-        if (nxt.n < a.N) phase_a(P == 0 ? X1 : X0, P == 0 ? T1 : T0, nxt.tw);
-        phase_b(P == 0 ? T0 : T1, cur);
-        cur = nxt;
-        nxt = nn;
+    auto run = [&](auto identity1, auto from_bias) {
+        if (cur.n < a.N) phase_a(X0, T0, identity1);
+        auto step_fn = [&](auto par, bool first) {
+            constexpr int P = decltype(par)::value;
+            if (first) mm::wait_vmcnt<0>(); else mm::wait_vmcnt<NST>();
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own intermediate writes done
+            __builtin_amdgcn_s_barrier();
+            const Pos nn = advance(nxt);
+            issue_tile(nn, std::integral_constant<int, P>{});
+            if (nxt.n < a.N) phase_a(P == 0 ? X1 : X0, P == 0 ? T1 : T0, identity1);
+            phase_b(P == 0 ? T0 : T1, cur, from_bias);
+            cur = nxt;
+            nxt = nn;
+        };
+        bool first = true;
+        while (cur.n < a.N) {
+            step_fn(std::integral_constant<int, 0>{}, first);
+            first = false;
+            if (cur.n >= a.N) break;
+            step_fn(std::integral_constant<int, 1>{}, false);
+        }
     };
-    bool first = true;
-    while (cur.n < a.N) {
-        step_fn(std::integral_constant<int, 0>{}, first);
-        first = false;
-        if (cur.n >= a.N) break;
-        step_fn(std::integral_constant<int, 1>{}, false);
-    }
+    if (id1 && bias_init2) run(std::true_type{}, std::true_type{});
+    else run(std::false_type{}, std::false_type{});
     // loads of tiles past the end may still be in flight into LDS: drain them before
     // the workgroup's LDS can be handed to another workgroup
     mm::wait_vmcnt<0>();
