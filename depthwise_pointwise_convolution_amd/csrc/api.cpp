@@ -45,8 +45,8 @@ const VariantImpl kImpls[] = {
     {launch_dwpw_f32<S, TH, TW, KT, CC>, occ_dwpw_f32<S, TH, TW, KT, CC>},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
     {launch_b2b_mfma<CT, S, TH, TW, K1, KT, CC>, occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>},
-#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
-    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>},
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC) \
+    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC>},
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC) {launch_b2b_mm<CT, S, OCC>, occ_b2b_mm<CT, S, OCC>},
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
     {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>,           \

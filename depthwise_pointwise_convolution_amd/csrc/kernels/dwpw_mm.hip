@@ -17,19 +17,22 @@
 // the depthwise filters.  Products of two 16-bit values are exact in fp32 and the
 // accumulation is fp32, as in the vector version.
 //
-// Work split of a 4x16-pixel tile over the 4 waves of a workgroup:
-//   phase A  wave w computes the depthwise layer of output row w (16 pixels, all CC
-//            channels).  The result lands in the matrix unit's output layout -- lane
+// Work split of a 4x16-pixel tile over the NW = 4 or 8 waves of a workgroup; wave w
+// works on channel group g = w % 4 and on rows RW * (w / 4) .. + RW - 1 (RW = 16 / NW):
+//   phase A  wave w computes the depthwise layer of channel blocks g, g + 4, ... of
+//            its rows.  The result lands in the matrix unit's output layout -- lane
 //            (l%16, l/16) holds channels 16*cb + 4*(l/16) + [0,4) of pixel l%16 -- and
 //            two channel blocks give a lane 8 channels of its pixel: exactly the B
 //            operand of the pointwise product when its reduction index is permuted the
 //            same way.  After epilogue 1 and rounding to the storage type, each lane
-//            writes its 16 bytes to the LDS intermediate tile (one contiguous 1 KB
-//            block per wave and 32 channels, no bank conflicts).
-//   phase B  wave w computes output channels [KT/4*w, KT/4*(w+1)) of the tile for all
-//            four rows, reading the intermediate back as ready-made B operands.  Its
-//            pointwise weights (the A operands) and epilogue-2 constants stay in
-//            registers for the whole kernel.
+//            writes its 8 bytes to the LDS intermediate tile (contiguous 1 KB operand
+//            blocks, no bank conflicts).
+//   phase B  wave w computes output channels [KT/4*g, KT/4*(g+1)) of its rows,
+//            reading the intermediate back as ready-made B operands.  Its pointwise
+//            weights (the A operands) and epilogue-2 constants stay in registers for
+//            the whole kernel.
+// Eight waves pay off where the tile buffers leave room for one workgroup per CU (128
+// channels): two waves per SIMD instead of one.
 // The intermediate thus lives only in LDS (the commBuffer of the page's design) and
 // never reaches HBM.
 //
@@ -56,11 +59,14 @@
 namespace fcm {
 
 
-template <typename T, int S, int TH, int TW, int KT, int CC, int OCC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void dwpw_mm_kernel(KArgs a) {
-    constexpr int NT = 256;
+    constexpr int NT = 64 * NW;
     static_assert(TH == 4 && TW == 16, "4 rows of 16 pixels per tile");
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    // wave w works on channel / output group w % 4 and rows RW * (w / 4) .. + RW - 1
+    constexpr int RW = TH * 4 / NW;
     constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3, NPIX = IH * IW;
     constexpr int CH = CC / 8;  // 16-byte chunks per pixel
     static_assert(CH == 8 || CH == 16, "swizzle needs 8 or 16 chunks per pixel");
@@ -73,7 +79,7 @@ void dwpw_mm_kernel(KArgs a) {
     constexpr int KW = KT / 4;    // pointwise output channels per wave
     constexpr int KBW = KW / 16;  // 16-channel output blocks per wave
     static_assert(KT % 128 == 0, "each wave stores 16-byte runs of 8 output channels");
-    constexpr int NST = TH * (KBW / 2);  // buffer stores per lane per step
+    constexpr int NST = RW * (KBW / 2);  // buffer stores per lane per step
     static_assert(NST < 64, "vmcnt range");
     constexpr uint32_t ROW_BYTES = (uint32_t)S * IW * CH * 16;  // one output row down
 
@@ -90,12 +96,13 @@ void dwpw_mm_kernel(KArgs a) {
     u32x4* const T1 = tl1;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int og = wave & 3, row0 = RW * (wave >> 2);
     const int lr = lane & 15, lg = lane >> 4;
     const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int G = gridDim.x;
     const int L = xcd_logical_id(blockIdx.x, G);
     const int k0 = (L % a.num_ktiles) * KT;
-    const int kw0 = k0 + wave * KW;  // this wave's output channels
+    const int kw0 = k0 + og * KW;  // this wave's output channels
     const T* __restrict__ wdw = (const T*)a.w1;
     const T* __restrict__ wpw = (const T*)a.w2;
     // one buffer resource per tensor (the host guarantees whole tensors below 2 GiB)
@@ -205,7 +212,7 @@ void dwpw_mm_kernel(KArgs a) {
     Pos nxt = advance(cur);
     issue_tile(cur, std::integral_constant<int, 0>{});
     //
-    // depthwise: this wave owns channel blocks cb = wave + 4j.  Matrix operand of block
+    // depthwise: this wave owns channel blocks cb = og + 4j.  Matrix operand of block
     // cb and tap pair tp, lane (l%16, l/16): row = channel 16cb + l%16, reduction index
     // 8(l/16) + e = (tap 2tp + (l/16)/2, channel 16cb + 8((l/16)&1) + e); non-zero only
     // where that channel is the row's, i.e. one 16-bit element per lane.  The tenth tap
@@ -220,7 +227,7 @@ void dwpw_mm_kernel(KArgs a) {
     float s1l[CBW][4], b1l[CBW][4];
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
-        const int cb = wave + 4 * j;
+        const int cb = og + 4 * j;
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
             const int t = 2 * tp + (lg >> 1), c = cb * 16 + lr;
@@ -268,7 +275,7 @@ void dwpw_mm_kernel(KArgs a) {
     float s1r[CBW][4], b1r[CBW][4];
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
-        const int cb = wave + 4 * j;
+        const int cb = og + 4 * j;
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
             const int t = 2 * tp + (lg >> 1), c = cb * 16 + lr;
@@ -300,7 +307,7 @@ void dwpw_mm_kernel(KArgs a) {
         b2r[i] = (a.b2 && ok) ? b2r[i] : 0.0f;
     }
     // LDS byte offsets of this lane's depthwise operand reads in output row 0, block
-    // cb = wave, per tap pair (row r adds r * ROW_BYTES, block cb + 4j adds 128j bytes:
+    // cb = og, per tap pair (row r adds r * ROW_BYTES, block cb + 4j adds 128j bytes:
     // bit 3 of the chunk index is untouched by the swizzle).  The empty tenth tap
     // reads the first tap's pixel (finite data times a zero weight).
     uint32_t xoff[NTP];
@@ -309,14 +316,14 @@ void dwpw_mm_kernel(KArgs a) {
         const int t0 = 2 * tp + (lg >> 1), t = t0 < 9 ? t0 : 0;
         const int col = lr * S + t % 3;
         const int p = (t / 3) * IW + col;
-        const int q = 2 * wave + (lg & 1);
+        const int q = 2 * og + (lg & 1);
         xoff[tp] = (uint32_t)(p * CH + (q ^ (col & 7))) * 16u;
     }
     // intermediate: depthwise rows 4(l/16)+i of channel block cb are channels
     // 16(cb%2) + 4(l/16) + i of slice cb/2, i.e. lane group 2(cb%2) + (l/16)/2, bytes
-    // 8((l/16)%2)..+7 of its 16-byte operand (cb % 2 == wave % 2 for every block)
+    // 8((l/16)%2)..+7 of its 16-byte operand (cb % 2 == og % 2 for every block)
     const uint32_t tls_w =
-        (uint32_t)(((2 * (wave & 1) + (lg >> 1)) * 16 + lr) * 16 + (lg & 1) * 8);
+        (uint32_t)(((2 * (og & 1) + (lg >> 1)) * 16 + lr) * 16 + (lg & 1) * 8);
     // store offset of the lane's first output channel within a pixel row of the tile
     // (kOob when the channel does not exist); the pixel row enters as a scalar offset
     const int kl = kw0 + lg * (KW / 4);
@@ -334,31 +341,31 @@ void dwpw_mm_kernel(KArgs a) {
     const bool bias_init2 = !a.s2;
 
     // phase A of one tile: depthwise on the matrix cores, this wave's channel blocks
-    // for all TH rows; epilogue 1; 8 bytes per lane into the intermediate tile, where
+    // for its RW rows; epilogue 1; 8 bytes per lane into the intermediate tile, where
     // they form half of a pointwise B operand
     auto phase_a = [&](const u32x4* src, u32x4* dst, auto identity1) {
-        const char* xb = reinterpret_cast<const char*>(src);
+        const char* xb = reinterpret_cast<const char*>(src) + row0 * ROW_BYTES;
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
             const u32x4* wf = wdf[j];
-            const int cb = wave + 4 * j;
-            // tap pairs outer, rows inner: TH independent accumulation chains, so a
+            const int cb = og + 4 * j;
+            // tap pairs outer, rows inner: RW independent accumulation chains, so a
             // product never waits for the previous one of its own chain
-            f32x4 d[TH];
+            f32x4 d[RW];
 #pragma unroll
-            for (int r = 0; r < TH; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < RW; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int tp = 0; tp < NTP; ++tp) {
-                u32x4 xv[TH];
+                u32x4 xv[RW];
 #pragma unroll
-                for (int r = 0; r < TH; ++r)
+                for (int r = 0; r < RW; ++r)
                     xv[r] = *reinterpret_cast<const u32x4*>(xb + xoff[tp] + r * ROW_BYTES +
                                                             j * 128);
 #pragma unroll
-                for (int r = 0; r < TH; ++r) d[r] = mfma<T>(wf[tp], xv[r], d[r]);
+                for (int r = 0; r < RW; ++r) d[r] = mfma<T>(wf[tp], xv[r], d[r]);
             }
 #pragma unroll
-            for (int r = 0; r < TH; ++r) {
+            for (int r = 0; r < RW; ++r) {
                 float o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -366,25 +373,26 @@ void dwpw_mm_kernel(KArgs a) {
                                ? d[r][i]
                                : epilogue(d[r][i], s1r[j][i], b1r[j][i], act1);
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
-                                          ((r * NKS + (cb >> 1)) * 64) * 16 + tls_w) =
+                                          (((row0 + r) * NKS + (cb >> 1)) * 64) * 16 + tls_w) =
                     pack8<T>(o);
             }
         }
     };
     // phase B of one tile: pointwise on the matrix cores, this wave's KW output
-    // channels for all TH rows, epilogue 2, 16-byte stores; always NST stores per lane
+    // channels for its RW rows, epilogue 2, 16-byte stores; always NST stores per lane
     // (rows or lanes outside the output get the out-of-range offset)
     auto phase_b = [&](const u32x4* src, const Pos& t, auto from_bias) {
         constexpr bool FB = decltype(from_bias)::value;
-        u32x4 bfr[TH][NKS];
+        u32x4 bfr[RW][NKS];
 #pragma unroll
-        for (int mb = 0; mb < TH; ++mb)
+        for (int mb = 0; mb < RW; ++mb)
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) bfr[mb][ks] = src[(mb * NKS + ks) * 64 + lane];
+            for (int ks = 0; ks < NKS; ++ks)
+                bfr[mb][ks] = src[((row0 + mb) * NKS + ks) * 64 + lane];
         // reduction step outermost, so that each accumulator is updated in place
-        f32x4 acc[TH][KBW];
+        f32x4 acc[RW][KBW];
 #pragma unroll
-        for (int mb = 0; mb < TH; ++mb)
+        for (int mb = 0; mb < RW; ++mb)
 #pragma unroll
             for (int kb = 0; kb < KBW; ++kb)
                 acc[mb][kb] = FB ? f32x4{b2r[kb * 4], b2r[kb * 4 + 1], b2r[kb * 4 + 2],
@@ -393,16 +401,16 @@ void dwpw_mm_kernel(KArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int mb = 0; mb < TH; ++mb)
+            for (int mb = 0; mb < RW; ++mb)
 #pragma unroll
                 for (int kb = 0; kb < KBW; ++kb)
                     acc[mb][kb] = mfma<T>(wa[ks][kb], bfr[mb][ks], acc[mb][kb]);
         const uint32_t voff = t.ow0 + lr < a.Wo ? st_lane : mm::kOob;
 #pragma unroll
-        for (int mb = 0; mb < TH; ++mb) {
-            const bool row_ok = t.oh0 + mb < a.Ho;
+        for (int mb = 0; mb < RW; ++mb) {
+            const bool row_ok = t.oh0 + row0 + mb < a.Ho;
             const uint32_t v = row_ok ? voff : mm::kOob;
-            const int srow = row_ok ? t.out_base + mb * out_row : 0;
+            const int srow = row_ok ? t.out_base + (row0 + mb) * out_row : 0;
 #pragma unroll
             for (int kb = 0; kb < KBW; kb += 2) {
                 float o[8];
@@ -465,18 +473,18 @@ void dwpw_mm_kernel(KArgs a) {
     mm::wait_vmcnt<0>();
 }
 
-template <typename T, int S, int TH, int TW, int KT, int CC, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC>
 int launch_dwpw_mm(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((dwpw_mm_kernel<T, S, TH, TW, KT, CC, OCC>), dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL((dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC>), dim3(grid), dim3(64 * NW), 0,
                        (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
-template <typename T, int S, int TH, int TW, int KT, int CC, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC>
 int occ_dwpw_mm() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, dwpw_mm_kernel<T, S, TH, TW, KT, CC, OCC>, 256, 0) != hipSuccess)
+            &n, dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC>, 64 * NW, 0) != hipSuccess)
         return 0;
     return n;
 }
@@ -485,9 +493,9 @@ int occ_dwpw_mm() {
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
 #define FCM_V_B2B_MM(...)
-#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC)                              \
-    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>(const KArgs&, int, void*); \
-    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, OCC>();
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC)                              \
+    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC>(const KArgs&, int, void*); \
+    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC>();
 #define FCM_V_DWPW_MMW(...)
 #include "../variants.def"
 #undef FCM_V_DWPW

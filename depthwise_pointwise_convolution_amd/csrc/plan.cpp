@@ -40,8 +40,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 0, 1, 4, 0},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
     {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, 0, K1, 1, 4, 0},
-#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, OCC) \
-    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, 4, 0},
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC) \
+    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, NW, 0},
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC) \
     {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC, 4, 0},
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
@@ -109,9 +109,11 @@ int variant_lds_bytes(const VariantDesc& v) {
         return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 1) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4;
     case VK_DWPW_MM:
     case VK_B2B_MM: {
-        // input tile (or chunk) buffers and as many intermediate tiles
+        // input tile (or chunk) buffers and as many intermediate tiles (one direct-load
+        // round is one 16-byte piece per thread)
+        const int nt = 64 * v.waves;
         const int slots = IH * IW * (v.cc / 8);
-        const int slots_p = (slots + 255) / 256 * 256;
+        const int slots_p = (slots + nt - 1) / nt * nt;
         const int tls = v.th * (v.cc / 32) * 64 * 16;
         return v.nbuf * (slots_p * 16 + tls);
     }
@@ -146,12 +148,13 @@ int variant_vgpr_estimate(const VariantDesc& v) {
     case VK_DWPW_MM: {
         // per wave: pointwise operands of its KT/4 output channels and their epilogue
         // constants, its depthwise operands and epilogue-1 constants, the direct-load
-        // plan, accumulators, staging and addressing
-        const int cbw = v.cc / 64, nks = v.cc / 32, kbw = v.kt / 64;
+        // plan, accumulators of its rows, staging and addressing
+        const int cbw = v.cc / 64, nks = v.cc / 32, kbw = v.kt / 64, nt = 64 * v.waves;
+        const int rw = v.th * 4 / v.waves;
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * (v.cc / 8);
         (void)MBW;
-        return nks * kbw * 4 + v.kt / 8 + (cbw == 1 ? 20 : cbw * 5 + 20) + cbw * 8 +
-               2 * ((slots + 255) / 256) + 16 + kbw * 4 + 24 + 16;
+        return nks * kbw * 4 + v.kt / 8 + cbw * 20 + cbw * 8 + 2 * ((slots + nt - 1) / nt) +
+               rw * 4 + rw * kbw * 4 + 24 + 16;
     }
     case VK_B2B_MM: {
         // per wave: 18 resident 3x3 operands, 8 resident 1x1 operands, 32 epilogue-2
