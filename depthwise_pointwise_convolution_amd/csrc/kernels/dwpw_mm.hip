@@ -81,7 +81,9 @@ void dwpw_mm_kernel(KArgs a) {
     static_assert(KT % 128 == 0, "each wave stores 16-byte runs of 8 output channels");
     constexpr int NST = RW * (KBW / 2);  // buffer stores per lane per step
     static_assert(NST < 64, "vmcnt range");
-    constexpr uint32_t ROW_BYTES = (uint32_t)S * IW * CH * 16;  // one output row down
+    constexpr uint32_t IROW_BYTES = (uint32_t)IW * CH * 16;  // one input row down
+    constexpr uint32_t ROW_BYTES = S * IROW_BYTES;             // one output row down
+    constexpr int IHW = (RW - 1) * S + 3;  // input rows under a wave's RW output rows
 
     // separate arrays per buffer: the compiler then sees that reading one buffer does
     // not depend on the direct loads still in flight into the other
@@ -212,11 +214,16 @@ void dwpw_mm_kernel(KArgs a) {
     Pos nxt = advance(cur);
     issue_tile(cur, std::integral_constant<int, 0>{});
     //
-    // depthwise: this wave owns channel blocks cb = og + 4j.  Matrix operand of block
-    // cb and tap pair tp, lane (l%16, l/16): row = channel 16cb + l%16, reduction index
-    // 8(l/16) + e = (tap 2tp + (l/16)/2, channel 16cb + 8((l/16)&1) + e); non-zero only
-    // where that channel is the row's, i.e. one 16-bit element per lane.  The tenth tap
-    // of the last pair is empty (zero weights).
+    // depthwise: this wave owns channel blocks cb = og + 4j.  The nine taps (dh, dw),
+    // numbered 3 dh + dw, are paired as (dh,0)+(dh,1) for dh = 0, 1, 2, then
+    // (0,2)+(1,2), then (2,2) with an empty tenth tap (zero weights): with this pairing
+    // the matrix operand of every pair depends on one input row only (the dw = 2
+    // pairs on two consecutive rows), so one LDS read serves all the output rows that
+    // use it.  Matrix operand of block cb and pair tp, lane (l%16, l/16): row = channel
+    // 16cb + l%16, reduction index 8(l/16) + e = (tap pair_tap(tp, (l/16)/2), channel
+    // 16cb + 8((l/16)&1) + e); non-zero only where that channel is the row's, i.e. one
+    // 16-bit element per lane.
+    auto pair_tap = [](int tp, int hh) { return tp < 3 ? 3 * tp + hh : tp == 3 ? 3 * hh + 2 : 8 + hh; };
     const bool dw_active = (lr >> 3) == (lg & 1);
     const int dw_e = lr & 7;
     const float* s1p = a.s1 ? a.s1 : (const float*)a.w2;
@@ -230,7 +237,7 @@ void dwpw_mm_kernel(KArgs a) {
         const int cb = og + 4 * j;
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
-            const int t = 2 * tp + (lg >> 1), c = cb * 16 + lr;
+            const int t = pair_tap(tp, lg >> 1), c = cb * 16 + lr;
             wdr[j][tp] = __builtin_bit_cast(uint16_t,
                                             wdw[(t < 9 ? t : 0) * a.C + (c < a.C ? c : 0)]);
         }
@@ -278,7 +285,7 @@ void dwpw_mm_kernel(KArgs a) {
         const int cb = og + 4 * j;
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
-            const int t = 2 * tp + (lg >> 1), c = cb * 16 + lr;
+            const int t = pair_tap(tp, lg >> 1), c = cb * 16 + lr;
             const bool ok = dw_active && t < 9 && c < a.C;
             const uint32_t v = ok ? (uint32_t)wdr[j][tp] : 0u;
             wdc[j][tp] = (dw_e & 1) ? (v << 16) : v;
@@ -306,19 +313,20 @@ void dwpw_mm_kernel(KArgs a) {
         s2r[i] = (a.s2 && ok) ? s2r[i] : 1.0f;
         b2r[i] = (a.b2 && ok) ? b2r[i] : 0.0f;
     }
-    // LDS byte offsets of this lane's depthwise operand reads in output row 0, block
-    // cb = og, per tap pair (row r adds r * ROW_BYTES, block cb + 4j adds 128j bytes:
-    // bit 3 of the chunk index is untouched by the swizzle).  The empty tenth tap
-    // reads the first tap's pixel (finite data times a zero weight).
-    uint32_t xoff[NTP];
-#pragma unroll
-    for (int tp = 0; tp < NTP; ++tp) {
-        const int t0 = 2 * tp + (lg >> 1), t = t0 < 9 ? t0 : 0;
-        const int col = lr * S + t % 3;
-        const int p = (t / 3) * IW + col;
-        const int q = 2 * og + (lg & 1);
-        xoff[tp] = (uint32_t)(p * CH + (q ^ (col & 7))) * 16u;
-    }
+    // LDS byte offsets of this lane's depthwise operand reads from input row 0 of the
+    // tile, block cb = og (input row ir adds ir * IROW_BYTES, block cb + 4j adds 128j
+    // bytes: bit 3 of the chunk index is untouched by the swizzle): xo_p for the
+    // (dh,0)+(dh,1) pairs (column lr*S + (l/16)/2), xo_q for the dw = 2 pairs (column
+    // lr*S + 2, the upper lane half one row down), xo_qc the same without the row step
+    // (for the window's last row, where only the (2,2) pair uses the read: the upper
+    // half then meets zero weights and must only stay inside the tile).
+    const int q_ch = 2 * og + (lg & 1), hh = lg >> 1;
+    auto lds_off = [&](int row, int col) {
+        return (uint32_t)((row * IW + col) * CH + (q_ch ^ (col & 7))) * 16u;
+    };
+    const uint32_t xo_p = lds_off(0, lr * S + hh);
+    const uint32_t xo_q = lds_off(hh, lr * S + 2);
+    const uint32_t xo_qc = lds_off(0, lr * S + 2);
     // intermediate: depthwise rows 4(l/16)+i of channel block cb are channels
     // 16(cb%2) + 4(l/16) + i of slice cb/2, i.e. lane group 2(cb%2) + (l/16)/2, bytes
     // 8((l/16)%2)..+7 of its 16-byte operand (cb % 2 == og % 2 for every block)
@@ -349,20 +357,27 @@ void dwpw_mm_kernel(KArgs a) {
         for (int j = 0; j < CBW; ++j) {
             const u32x4* wf = wdf[j];
             const int cb = og + 4 * j;
-            // tap pairs outer, rows inner: RW independent accumulation chains, so a
-            // product never waits for the previous one of its own chain
+            // input rows outer: each operand read once, then applied to every output row
+            // that uses it (RW independent accumulation chains)
             f32x4 d[RW];
 #pragma unroll
             for (int r = 0; r < RW; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int tp = 0; tp < NTP; ++tp) {
-                u32x4 xv[RW];
+            for (int ir = 0; ir < IHW; ++ir) {
+                const u32x4 bp =
+                    *reinterpret_cast<const u32x4*>(xb + xo_p + ir * IROW_BYTES + j * 128);
 #pragma unroll
-                for (int r = 0; r < RW; ++r)
-                    xv[r] = *reinterpret_cast<const u32x4*>(xb + xoff[tp] + r * ROW_BYTES +
-                                                            j * 128);
-#pragma unroll
-                for (int r = 0; r < RW; ++r) d[r] = mfma<T>(wf[tp], xv[r], d[r]);
+                for (int dh = 0; dh < 3; ++dh)
+                    if (ir >= dh && (ir - dh) % S == 0 && (ir - dh) / S < RW)
+                        d[(ir - dh) / S] = mfma<T>(wf[dh], bp, d[(ir - dh) / S]);
+                const bool q0 = ir % S == 0 && ir / S < RW;
+                const bool q1 = ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW;
+                if (q0 || q1) {
+                    const u32x4 bq = *reinterpret_cast<const u32x4*>(
+                        xb + (ir + 1 < IHW ? xo_q : xo_qc) + ir * IROW_BYTES + j * 128);
+                    if (q0) d[ir / S] = mfma<T>(wf[3], bq, d[ir / S]);
+                    if (q1) d[(ir - 2) / S] = mfma<T>(wf[4], bq, d[(ir - 2) / S]);
+                }
             }
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
