@@ -154,9 +154,10 @@ void dwpw_mm_kernel(KArgs a) {
     };
 
     // ---- direct-load plan (tile invariant) ---------------------------------------------
-    // LDS slot s holds chunk q of window pixel p = s / CH with s % CH = q ^ (column & 7):
-    // the 16 lanes of an operand read (consecutive columns, same chunk) then fall in
-    // distinct bank groups, and moving down a row moves every slot by a constant.
+    // LDS slot s holds chunk q of window pixel p = s / CH with s % CH = q ^ (column &
+    // (CH - 1)): the 16 lanes of an operand read (consecutive columns, same chunk) then
+    // fall in distinct bank groups (a pixel is CH 16-byte chunks, so without the swizzle
+    // they would all share one), and moving down a row moves every slot by a constant.
     // dl_off: byte offset of the slot's source relative to the window origin (kOob for
     // padding slots); dl_pos: the slot's window row and column.
     uint32_t dl_off[R];
@@ -165,7 +166,7 @@ void dwpw_mm_kernel(KArgs a) {
     for (int r = 0; r < R; ++r) {
         const int s = r * NT + tid;
         const int p = s / CH, ihl = p / IW, iwl = p % IW;
-        const int q = (s % CH) ^ (iwl & 7);
+        const int q = (s % CH) ^ (iwl & (CH - 1));
         const bool real = s < SLOTS && q * 8 < a.C;
         dl_off[r] = real ? (uint32_t)((ihl * a.W + iwl) * a.C + q * 8) * (uint32_t)sizeof(T)
                          : mm::kOob;
@@ -314,19 +315,23 @@ void dwpw_mm_kernel(KArgs a) {
         b2r[i] = (a.b2 && ok) ? b2r[i] : 0.0f;
     }
     // LDS byte offsets of this lane's depthwise operand reads from input row 0 of the
-    // tile, block cb = og (input row ir adds ir * IROW_BYTES, block cb + 4j adds 128j
-    // bytes: bit 3 of the chunk index is untouched by the swizzle): xo_p for the
+    // tile, block cb = og + 4j (input row ir adds ir * IROW_BYTES): xo_p for the
     // (dh,0)+(dh,1) pairs (column lr*S + (l/16)/2), xo_q for the dw = 2 pairs (column
     // lr*S + 2, the upper lane half one row down), xo_qc the same without the row step
     // (for the window's last row, where only the (2,2) pair uses the read: the upper
     // half then meets zero weights and must only stay inside the tile).
-    const int q_ch = 2 * og + (lg & 1), hh = lg >> 1;
-    auto lds_off = [&](int row, int col) {
-        return (uint32_t)((row * IW + col) * CH + (q_ch ^ (col & 7))) * 16u;
+    const int hh = lg >> 1;
+    auto lds_off = [&](int j, int row, int col) {
+        const int q = 2 * (og + 4 * j) + (lg & 1);
+        return (uint32_t)((row * IW + col) * CH + (q ^ (col & (CH - 1)))) * 16u;
     };
-    const uint32_t xo_p = lds_off(0, lr * S + hh);
-    const uint32_t xo_q = lds_off(hh, lr * S + 2);
-    const uint32_t xo_qc = lds_off(0, lr * S + 2);
+    uint32_t xo_p[CBW], xo_q[CBW], xo_qc[CBW];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+        xo_p[j] = lds_off(j, 0, lr * S + hh);
+        xo_q[j] = lds_off(j, hh, lr * S + 2);
+        xo_qc[j] = lds_off(j, 0, lr * S + 2);
+    }
     // intermediate: depthwise rows 4(l/16)+i of channel block cb are channels
     // 16(cb%2) + 4(l/16) + i of slice cb/2, i.e. lane group 2(cb%2) + (l/16)/2, bytes
     // 8((l/16)%2)..+7 of its 16-byte operand (cb % 2 == og % 2 for every block)
@@ -365,7 +370,7 @@ void dwpw_mm_kernel(KArgs a) {
 #pragma unroll
             for (int ir = 0; ir < IHW; ++ir) {
                 const u32x4 bp =
-                    *reinterpret_cast<const u32x4*>(xb + xo_p + ir * IROW_BYTES + j * 128);
+                    *reinterpret_cast<const u32x4*>(xb + xo_p[j] + ir * IROW_BYTES);
 #pragma unroll
                 for (int dh = 0; dh < 3; ++dh)
                     if (ir >= dh && (ir - dh) % S == 0 && (ir - dh) / S < RW)
@@ -374,7 +379,7 @@ void dwpw_mm_kernel(KArgs a) {
                 const bool q1 = ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW;
                 if (q0 || q1) {
                     const u32x4 bq = *reinterpret_cast<const u32x4*>(
-                        xb + (ir + 1 < IHW ? xo_q : xo_qc) + ir * IROW_BYTES + j * 128);
+                        xb + (ir + 1 < IHW ? xo_q[j] : xo_qc[j]) + ir * IROW_BYTES);
                     if (q0) d[ir / S] = mfma<T>(wf[3], bq, d[ir / S]);
                     if (q1) d[(ir - 2) / S] = mfma<T>(wf[4], bq, d[(ir - 2) / S]);
                 }
