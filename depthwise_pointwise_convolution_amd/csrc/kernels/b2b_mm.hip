@@ -22,6 +22,27 @@
 
 namespace fcm {
 
+// Matrix products of the 3x3 convolution that use input row IR of the tile window:
+// six operands (three filter columns, two channel halves), each applied to every output
+// row r = (IR - dh) / S it feeds.
+template <int S, int TH, int IR>
+__device__ constexpr int b2b_row_products() {
+    int n = 0;
+    for (int dh = 0; dh < 3; ++dh)
+        if (IR - dh >= 0 && (IR - dh) % S == 0 && (IR - dh) / S < TH) n += 6;
+    return n;
+}
+// Scheduling groups for phase A (compiler scheduling hints only, no effect on results):
+// the six LDS operand reads of row IR + 1, then the products of row IR, for every row,
+// so that each row's reads are in flight while the previous row's products run.
+template <int S, int TH, int IR, int IH>
+__device__ __forceinline__ void b2b_sched_rows() {
+    if constexpr (IR + 1 < IH) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    if constexpr (b2b_row_products<S, TH, IR>() > 0)
+        __builtin_amdgcn_sched_group_barrier(0x008, b2b_row_products<S, TH, IR>(), 0);
+    if constexpr (IR + 1 < IH) b2b_sched_rows<S, TH, IR + 1, IH>();
+}
+
 template <typename T, int S, int OCC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void b2b_mm_kernel(KArgs a) {
@@ -228,22 +249,36 @@ void b2b_mm_kernel(KArgs a) {
         for (int r = 0; r < TH; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         // walk the input rows: the operand of input row ir, filter column dw and channel
         // half h is read once and used by every output row r = (ir - dh) / S it feeds
-        // (filter row dh), instead of once per (output row, tap)
-#pragma unroll
-        for (int ir = 0; ir < IH; ++ir)
+        // (filter row dh), instead of once per (output row, tap).  The six operands of
+        // row ir + 1 are requested before the products of row ir, so the LDS latency
+        // overlaps matrix work instead of stalling it.
+        u32x4 xv[2][6];
+        auto load_row = [&](int ir, u32x4* o) {
 #pragma unroll
             for (int dw = 0; dw < 3; ++dw)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const u32x4 xv =
+                for (int h = 0; h < 2; ++h)
+                    o[dw * 2 + h] =
                         *reinterpret_cast<const u32x4*>(xb + xoff[dw][h] + ir * IN_ROW_BYTES);
+        };
+        load_row(0, xv[0]);
+#pragma unroll
+        for (int ir = 0; ir < IH; ++ir) {
+            if (ir + 1 < IH) load_row(ir + 1, xv[(ir + 1) & 1]);
+#pragma unroll
+            for (int dw = 0; dw < 3; ++dw)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int dh = 0; dh < 3; ++dh) {
                         const int r = (ir - dh) / S;
                         if (ir - dh >= 0 && (ir - dh) % S == 0 && r < TH)
-                            d[r] = mfma<T>(wa1[(dh * 3 + dw) * 2 + h], xv, d[r]);
+                            d[r] = mfma<T>(wa1[(dh * 3 + dw) * 2 + h], xv[ir & 1][dw * 2 + h],
+                                           d[r]);
                     }
-                }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // row 0's reads
+        b2b_sched_rows<S, TH, 0, IH>();
 #pragma unroll
         for (int r = 0; r < TH; ++r) {
             float v[4];
