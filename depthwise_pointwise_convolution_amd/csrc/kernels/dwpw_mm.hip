@@ -356,33 +356,51 @@ void dwpw_mm_kernel(KArgs a) {
     // phase A of one tile: depthwise on the matrix cores, this wave's channel blocks
     // for its RW rows; epilogue 1; 8 bytes per lane into the intermediate tile, where
     // they form half of a pointwise B operand
+    // operand reads of one input row of the window: the (dh,0)+(dh,1) operand always,
+    // the dw = 2 operand when a (0,2)+(1,2) or (2,2) product uses the row
+    auto q_used = [](int ir) {
+        return (ir % S == 0 && ir / S < RW) || (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW);
+    };
+    constexpr int NQ = [] {
+        int n = 0;
+        for (int ir = 0; ir < IHW; ++ir)
+            n += (ir % S == 0 && ir / S < RW) || (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW);
+        return n;
+    }();
     auto phase_a = [&](const u32x4* src, u32x4* dst, auto identity1) {
         const char* xb = reinterpret_cast<const char*>(src) + row0 * ROW_BYTES;
+        // every operand of the window is requested first, then the products run (the
+        // scheduling groups below keep that order), so the LDS latency is paid once per
+        // phase instead of once per product
+        u32x4 bp[CBW][IHW], bq[CBW][IHW];
+#pragma unroll
+        for (int j = 0; j < CBW; ++j)
+#pragma unroll
+            for (int ir = 0; ir < IHW; ++ir) {
+                bp[j][ir] = *reinterpret_cast<const u32x4*>(xb + xo_p[j] + ir * IROW_BYTES);
+                if (q_used(ir))
+                    bq[j][ir] = *reinterpret_cast<const u32x4*>(
+                        xb + (ir + 1 < IHW ? xo_q[j] : xo_qc[j]) + ir * IROW_BYTES);
+            }
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
             const u32x4* wf = wdf[j];
             const int cb = og + 4 * j;
-            // input rows outer: each operand read once, then applied to every output row
-            // that uses it (RW independent accumulation chains)
+            // input rows outer: each operand applied to every output row that uses it
+            // (RW independent accumulation chains)
             f32x4 d[RW];
 #pragma unroll
             for (int r = 0; r < RW; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ir = 0; ir < IHW; ++ir) {
-                const u32x4 bp =
-                    *reinterpret_cast<const u32x4*>(xb + xo_p[j] + ir * IROW_BYTES);
 #pragma unroll
                 for (int dh = 0; dh < 3; ++dh)
                     if (ir >= dh && (ir - dh) % S == 0 && (ir - dh) / S < RW)
-                        d[(ir - dh) / S] = mfma<T>(wf[dh], bp, d[(ir - dh) / S]);
-                const bool q0 = ir % S == 0 && ir / S < RW;
-                const bool q1 = ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW;
-                if (q0 || q1) {
-                    const u32x4 bq = *reinterpret_cast<const u32x4*>(
-                        xb + (ir + 1 < IHW ? xo_q[j] : xo_qc[j]) + ir * IROW_BYTES);
-                    if (q0) d[ir / S] = mfma<T>(wf[3], bq, d[ir / S]);
-                    if (q1) d[(ir - 2) / S] = mfma<T>(wf[4], bq, d[(ir - 2) / S]);
-                }
+                        d[(ir - dh) / S] = mfma<T>(wf[dh], bp[j][ir], d[(ir - dh) / S]);
+                if (ir % S == 0 && ir / S < RW)
+                    d[ir / S] = mfma<T>(wf[3], bq[j][ir], d[ir / S]);
+                if (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW)
+                    d[(ir - 2) / S] = mfma<T>(wf[4], bq[j][ir], d[(ir - 2) / S]);
             }
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
@@ -397,6 +415,8 @@ void dwpw_mm_kernel(KArgs a) {
                     pack8<T>(o);
             }
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, CBW * (IHW + NQ), 0);  // operand reads
+        __builtin_amdgcn_sched_group_barrier(0x008, CBW * RW * 5, 0);      // products
     };
     // phase B of one tile: pointwise on the matrix cores, this wave's KW output
     // channels for its RW rows, epilogue 2, 16-byte stores; always NST stores per lane
@@ -425,6 +445,9 @@ void dwpw_mm_kernel(KArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < KBW; ++kb)
                     acc[mb][kb] = mfma<T>(wa[ks][kb], bfr[mb][ks], acc[mb][kb]);
+        // all intermediate reads first, then the products
+        __builtin_amdgcn_sched_group_barrier(0x100, RW * NKS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, RW * NKS * KBW, 0);
         const uint32_t voff = t.ow0 + lr < a.Wo ? st_lane : mm::kOob;
 #pragma unroll
         for (int mb = 0; mb < RW; ++mb) {
