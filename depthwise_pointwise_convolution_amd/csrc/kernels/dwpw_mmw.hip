@@ -62,6 +62,8 @@ void dwpw_mmw_kernel(KArgs a) {
     constexpr int NST = MB * (KBW / 2);  // buffer stores per lane per finished tile
     static_assert(R + NST < 64 && 2 * R < 64, "vmcnt range");
     static_assert(CMAX % 64 == 0, "whole chunks");
+    // phase B's operands can be read before phase A when its accumulators leave room
+    constexpr bool EARLY_B = MB * KBW <= 8;
 
     __shared__ __attribute__((aligned(16))) u32x4 xs[NB * SLOTS_P];
     __shared__ __attribute__((aligned(16))) u32x4 tl0[MB * NKS * 64];
@@ -320,16 +322,26 @@ void dwpw_mmw_kernel(KArgs a) {
         for (int kb = 0; kb < KBW; ++kb) acc[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     // (reduction step outermost: the two updates of an accumulator are MB * KBW matrix
     // instructions apart and each one reads and writes it in place)
-    auto phase_b = [&](const u32x4* src, const PwOps& o) {
+    // the intermediate operands of phase B (read before phase A writes the other
+    // intermediate buffer, so that the reads can be issued early)
+    struct BIn {
+        u32x4 v[MB][NKS];
+    };
+    auto phase_b_load = [&](const u32x4* src, BIn& bfr) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const u32x4 bfr = src[(mb * NKS + ks) * 64 + lane];
+            for (int mb = 0; mb < MB; ++mb) bfr.v[mb][ks] = src[(mb * NKS + ks) * 64 + lane];
+    };
+    auto phase_b = [&](const BIn& in, const PwOps& o) {
+        const auto& bfr = in.v;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int kb = 0; kb < KBW; ++kb)
-                    acc[mb][kb] = mfma<T>(o.w[ks][kb], bfr, acc[mb][kb]);
-            }
+                    acc[mb][kb] = mfma<T>(o.w[ks][kb], bfr[mb][ks], acc[mb][kb]);
     };
     // epilogue 2 and the tile's stores: always NST per lane; pixels past the tile or the
     // output, and 8-channel runs past K, get the out-of-range offset
@@ -402,8 +414,24 @@ void dwpw_mmw_kernel(KArgs a) {
         issue_chunk(n3, xs + xi * SLOTS_P);
         // phase A runs even for a step past the last tile (its chunk was zero-filled and
         // its intermediate is never read)
+        // scheduling groups for the step: the LDS operand reads of a phase before its
+        // products; where registers allow (EARLY_B), phase B's intermediate operands
+        // (written in the previous step) are read before phase A as well
+        BIn bfr;
+        if constexpr (EARLY_B) phase_b_load(par ? tl1 : tl0, bfr);
         phase_a(xs + xa * SLOTS_P, par ? tl0 : tl1, nx.c);
-        phase_b(par ? tl1 : tl0, pwo0);
+        if constexpr (!EARLY_B) phase_b_load(par ? tl1 : tl0, bfr);
+        phase_b(bfr, pwo0);
+        if constexpr (EARLY_B) {
+            __builtin_amdgcn_sched_group_barrier(0x100, NTP + 2 + NTP * PPW + MB * NKS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NTP * PPW, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MB * KBW * NKS, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x100, NTP + 2 + NTP * PPW, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NTP * PPW, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, MB * NKS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MB * KBW * NKS, 0);
+        }
         stored = cur.c == nch - 1;
         if (stored) finish(cur.t);
         if (nch > 1) pwo0 = pwo1;
