@@ -91,21 +91,61 @@ void dwpw_mmw_kernel(KArgs a) {
     const int out_img = a.Ho * a.Wo * a.K * es, out_row = a.Wo * a.K * es;
 
     // epilogue-2 constants of the workgroup's K tile (read back per finished tile), the
-    // depthwise filters and the epilogue-1 constants of every channel
-    for (int i = tid; i < KT; i += NT) {
-        const int k = k0 + i;
-        const bool ok = k < a.K;
-        s2s[i] = (a.s2 && ok) ? a.s2[k] : 1.0f;
-        b2s[i] = (a.b2 && ok) ? a.b2[k] : 0.0f;
-    }
-    for (int i = tid; i < 9 * (a.C / 8); i += NT) {
-        const int t = i / (a.C / 8), c8 = i - t * (a.C / 8);
-        wds[t * (CMAX / 8) + c8] = reinterpret_cast<const u32x4*>(wdw)[i];
-    }
-    for (int i = tid; i < a.C; i += NT) {
-        s1s[i] = a.s1 ? a.s1[i] : 1.0f;
-        b1s[i] = a.b1 ? a.b1[i] : 0.0f;
-    }
+    // depthwise filters and the epilogue-1 constants of every channel.  Every load is
+    // issued before the first LDS write (fixed per-thread counts, masked past the end),
+    // so the copy costs one memory latency rather than one per loop round; the writes
+    // come after the prologue has requested the first chunks and operands.
+    constexpr int I2 = (KT + NT - 1) / NT, IW9 = (9 * CMAX / 8 + NT - 1) / NT;
+    constexpr int I1 = (CMAX + NT - 1) / NT;
+    const int nw = 9 * (a.C / 8);
+    float s2v[I2], b2v[I2], s1v[I1], b1v[I1];
+    u32x4 wv[IW9];
+    auto write_constants = [&]() {
+#pragma unroll
+        for (int r = 0; r < I2; ++r) {
+            const int i = tid + r * NT;
+            if (i < KT) {
+                s2s[i] = s2v[r];
+                b2s[i] = b2v[r];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < IW9; ++r) {
+            const int i = tid + r * NT;
+            if (i < nw) {
+                const int t = i / (a.C / 8), c8 = i - t * (a.C / 8);
+                wds[t * (CMAX / 8) + c8] = wv[r];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < I1; ++r) {
+            const int i = tid + r * NT;
+            if (i < a.C) {
+                s1s[i] = s1v[r];
+                b1s[i] = b1v[r];
+            }
+        }
+    };
+    auto load_constants = [&]() {
+#pragma unroll
+        for (int r = 0; r < I2; ++r) {
+            const int i = tid + r * NT, k = k0 + i;
+            const bool ok = i < KT && k < a.K;
+            s2v[r] = (a.s2 && ok) ? a.s2[k] : 1.0f;
+            b2v[r] = (a.b2 && ok) ? a.b2[k] : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < IW9; ++r) {
+            const int i = tid + r * NT;
+            wv[r] = i < nw ? reinterpret_cast<const u32x4*>(wdw)[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int r = 0; r < I1; ++r) {
+            const int i = tid + r * NT;
+            s1v[r] = (a.s1 && i < a.C) ? a.s1[i] : 1.0f;
+            b1v[r] = (a.b1 && i < a.C) ? a.b1[i] : 0.0f;
+        }
+    };
 
     // ---- (tile, chunk) walk --------------------------------------------------------
     const int pstep = G / a.num_ktiles;
@@ -384,10 +424,12 @@ void dwpw_mmw_kernel(KArgs a) {
     const Step s1 = next(s0);
     const Step s2 = next(s1);
     PwOps pwo0, pwo1;
+    load_constants();
     load_pw(s0, pwo0);
     issue_chunk(s0, xs);
     issue_chunk(s1, xs + SLOTS_P);
     issue_chunk(s2, xs + 2 * SLOTS_P);
+    write_constants();
     mm::wait_vmcnt<2 * R>();  // chunk 0 and the operands; chunks 1, 2 stay in flight
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS constants written
     __builtin_amdgcn_s_barrier();
