@@ -1,5 +1,5 @@
-"""Seeded synthetic workloads for the fused depthwise->pointwise module and the
-3x3->1x1 back-to-back pair.
+"""Seeded synthetic workloads for the fused depthwise->pointwise module, the
+pointwise->depthwise module and the 3x3->1x1 back-to-back pair.
 
 This module only describes shapes and draws random numbers: it holds none of the
 method's arithmetic and imports neither the HIP library nor the oracle, so both sides
@@ -10,10 +10,12 @@ order X, first-layer weights, scale1, bias1, second-layer weights, scale2, bias2
 narrowed to float32 and from there to the storage type with torch's round-to-nearest-
 even casts.  The narrowed values *are* the inputs: both the oracle and the GPU see the
 same numbers.  Weight layouts are PyTorch's: depthwise [C, 3, 3], pointwise [K, C],
-standard conv [K1, C, 3, 3], second conv [K, K1].
+standard conv [K1, C, 3, 3], second conv [K, K1]; for the pointwise->depthwise module
+the first layer is pointwise [K1, C] and the second depthwise [K1, 3, 3] (K = K1).
 
-The five workloads stand in for the layer shapes the pages evaluate (MobileNet-style
-depthwise-separable blocks, the forum's CIFAR network, ResNet-style 3x3 -> 1x1 pairs);
+The workloads stand in for the layer shapes the pages evaluate (MobileNet-style
+depthwise-separable blocks, the forum's CIFAR network, ResNet-style 3x3 -> 1x1 pairs,
+MobileNetV2-style inverted-residual expansions for the pointwise->depthwise module);
 no dataset or trained weight is involved.
 """
 from __future__ import annotations
@@ -29,14 +31,15 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "dwpw" or "b2b"
+    kind: str            # "dwpw", "b2b" or "pwdw"
     dtype: str           # "f32" | "f16" | "bf16"
     N: int
     H: int
     W: int
     C: int
-    K: int               # output channels of the final 1x1 conv
-    K1: int              # b2b: output channels of the 3x3 conv; dwpw: == C
+    K: int               # output channels of the module (pwdw: == K1)
+    K1: int              # b2b: output channels of the 3x3 conv; dwpw: == C;
+                         # pwdw: output channels of the pointwise layer
     stride: int = 1
     pad: int = 1
     R: int = 3
@@ -103,6 +106,18 @@ WORKLOADS = {
         w_dist=("normal", 0.0, 0.05), seed=5,
         description="Back-to-back: conv 3x3 p1 64->64 + scale_bias_relu, conv 1x1 "
                     "64->64 + scale_bias_relu, fp16, N=32 56x56"),
+    "pwdw_f16_32x56x56_c24_k144": Workload(
+        "pwdw_f16_32x56x56_c24_k144", "pwdw", "f16", N=32, H=56, W=56, C=24, K=144, K1=144,
+        act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
+        x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=6,
+        description="PW->DW module (MobileNetV2-style expansion): PW 24->144 + "
+                    "scale/bias+ReLU6, DW 3x3 s1 + scale/bias+ReLU6, fp16, N=32 56x56"),
+    "pwdw_f16_32x112x112_c16_k96_s2": Workload(
+        "pwdw_f16_32x112x112_c16_k96_s2", "pwdw", "f16", N=32, H=112, W=112, C=16, K=96,
+        K1=96, stride=2, act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True,
+        bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=7,
+        description="Downsampling PW->DW module: PW 16->96 + scale/bias+ReLU6, DW 3x3 s2 "
+                    "+ scale/bias+ReLU6, fp16, N=32 112x112 -> 56x56"),
 }
 
 
@@ -139,12 +154,18 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> dict:
     if wl.kind == "dwpw":
         w1 = _draw(rng, wl.w_dist, (wl.C, wl.R, wl.S))
         n1 = wl.C
+    elif wl.kind == "pwdw":
+        w1 = _draw(rng, wl.w_dist, (wl.K1, wl.C))
+        n1 = wl.K1
     else:
         w1 = _draw(rng, wl.w_dist, (wl.K1, wl.C, wl.R, wl.S))
         n1 = wl.K1
     s1 = _draw(rng, wl.scale_dist, (n1,)) if wl.scale1 else None
     b1 = _draw(rng, wl.bias_dist, (n1,)) if wl.bias1 else None
-    w2 = _draw(rng, wl.w_dist, (wl.K, n1))
+    if wl.kind == "pwdw":
+        w2 = _draw(rng, wl.w_dist, (wl.K1, wl.R, wl.S))
+    else:
+        w2 = _draw(rng, wl.w_dist, (wl.K, n1))
     s2 = _draw(rng, wl.scale_dist, (wl.K,)) if wl.scale2 else None
     b2 = _draw(rng, wl.bias_dist, (wl.K,)) if wl.bias2 else None
     out = {

@@ -1,4 +1,5 @@
-"""CPU oracle for the fused depthwise->pointwise module and the 3x3->1x1 pair.
+"""CPU oracle for the fused depthwise->pointwise module, the pointwise->depthwise
+module and the 3x3->1x1 pair.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code with
@@ -16,6 +17,7 @@ the storage type):
 * ``w_pw``   [K, C]               pointwise filters
 * ``w1``     [K1, C, R, S]        first (standard) conv of the back-to-back pair
 * ``w2``     [K, K1]              second (1x1) conv of the pair
+* PW->DW module: ``w_pw`` [K1, C] then ``w_dw`` [K1, R, S]; output channels K1
 * ``scale*``/``bias*`` per channel, or ``None`` (identity)
 """
 from __future__ import annotations
@@ -87,6 +89,14 @@ def _load():
             lib.fcm_oracle_dwpw_at.restype = ctypes.c_int
             lib.fcm_oracle_b2b_at.argtypes = mod_b2b + [ip, i64, dp]
             lib.fcm_oracle_b2b_at.restype = ctypes.c_int
+            # x, N, H, W, C, w_pw, K1, scale1, bias1, act1, w_dw, R, S, sh, sw, ph, pw,
+            # scale2, bias2, act2, dtype
+            mod_pd = [dp, i32, i32, i32, i32, dp, i32, dp, dp, ci, dp] + [i32] * 6 + \
+                [dp, dp, ci, ci]
+            lib.fcm_oracle_pwdw.argtypes = mod_pd + [dp, dp]
+            lib.fcm_oracle_pwdw.restype = ctypes.c_int
+            lib.fcm_oracle_pwdw_at.argtypes = mod_pd + [ip, i64, dp]
+            lib.fcm_oracle_pwdw_at.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -262,3 +272,52 @@ def b2b_at(x, w1, w2, pix, stride=(1, 1), pad=(1, 1), scale1=None, bias1=None,
     """Rows y[n, oh, ow, :] of :func:`b2b` at the listed output pixels only."""
     return _module_at(_load().fcm_oracle_b2b_at, x, w1, w2, pix, stride, pad, scale1,
                       bias1, act1, scale2, bias2, act2, dtype, False)
+
+
+# ---------------------------------------------------------------------------------
+# the pointwise -> depthwise module
+# ---------------------------------------------------------------------------------
+def _pwdw_args(x, w_pw, w_dw, stride, pad, scale1, bias1, act1, scale2, bias2, act2, dtype):
+    x, wp, wd = _f64(x), _f64(w_pw), _f64(w_dw)
+    N, H, W, C = x.shape
+    K1, Cw = wp.shape
+    K1d, R, S = wd.shape
+    assert Cw == C and K1d == K1
+    s1 = None if scale1 is None else _f64(scale1)
+    b1 = None if bias1 is None else _f64(bias1)
+    s2 = None if scale2 is None else _f64(scale2)
+    b2 = None if bias2 is None else _f64(bias2)
+    keep = (x, wp, wd, s1, b1, s2, b2)
+    args = [_p(x), N, H, W, C, _p(wp), K1, _p(s1), _p(b1), ACTS[act1], _p(wd), R, S,
+            stride[0], stride[1], pad[0], pad[1], _p(s2), _p(b2), ACTS[act2], DTYPES[dtype]]
+    return args, keep, (N, H, W, C, K1, R, S)
+
+
+def pwdw(x, w_pw, w_dw, stride=(1, 1), pad=(1, 1), scale1=None, bias1=None, act1="none",
+         scale2=None, bias2=None, act2="none", dtype="f32", return_t=False):
+    """Layer-by-layer PW conv -> epilogue -> round -> DW conv -> epilogue -> round.
+    ``w_pw`` [K1, C], ``w_dw`` [K1, R, S]; returns y [N, Ho, Wo, K1] (and the rounded
+    intermediate [N, H, W, K1] with ``return_t``)."""
+    args, keep, (N, H, W, C, K1, R, S) = _pwdw_args(x, w_pw, w_dw, stride, pad, scale1, bias1,
+                                                     act1, scale2, bias2, act2, dtype)
+    Ho, Wo = out_size(H, pad[0], R, stride[0]), out_size(W, pad[1], S, stride[1])
+    t = np.empty((N, H, W, K1), np.float64) if return_t else None
+    y = np.empty((N, Ho, Wo, K1), np.float64)
+    rc = _load().fcm_oracle_pwdw(*args, _p(t), _p(y))
+    del keep
+    if rc != 0:
+        raise MemoryError("oracle could not allocate the intermediate")
+    return (y, t) if return_t else y
+
+
+def pwdw_at(x, w_pw, w_dw, pix, stride=(1, 1), pad=(1, 1), scale1=None, bias1=None,
+            act1="none", scale2=None, bias2=None, act2="none", dtype="f32"):
+    """Rows y[n, oh, ow, :] of :func:`pwdw` at the listed output pixels only."""
+    args, keep, (N, H, W, C, K1, R, S) = _pwdw_args(x, w_pw, w_dw, stride, pad, scale1, bias1,
+                                                     act1, scale2, bias2, act2, dtype)
+    pix = np.ascontiguousarray(pix, dtype=np.int32).reshape(-1, 3)
+    y = np.empty((pix.shape[0], K1), np.float64)
+    _load().fcm_oracle_pwdw_at(*args, pix.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                               pix.shape[0], _p(y))
+    del keep
+    return y

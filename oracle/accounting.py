@@ -47,13 +47,16 @@ def sizes(wl) -> dict:
     Ho, Wo = wl.Ho, wl.Wo
     n1 = wl.C if wl.kind == "dwpw" else wl.K1
     x = wl.N * wl.H * wl.W * wl.C
-    t = wl.N * Ho * Wo * n1
     y = wl.N * Ho * Wo * wl.K
-    if wl.kind == "dwpw":
-        w1 = wl.C * wl.R * wl.S
+    if wl.kind == "pwdw":
+        # the intermediate is the pointwise layer's output, at the input resolution
+        t = wl.N * wl.H * wl.W * n1
+        w1 = wl.K1 * wl.C
+        w2 = wl.K1 * wl.R * wl.S
     else:
-        w1 = wl.K1 * wl.C * wl.R * wl.S
-    w2 = wl.K * n1
+        t = wl.N * Ho * Wo * n1
+        w1 = wl.C * wl.R * wl.S if wl.kind == "dwpw" else wl.K1 * wl.C * wl.R * wl.S
+        w2 = wl.K * n1
     epi = 4 * (n1 * (int(wl.scale1) + int(wl.bias1)) + wl.K * (int(wl.scale2) + int(wl.bias2)))
     return {"x": x * e, "t": t * e, "y": y * e, "w1": w1 * e, "w2": w2 * e, "epi": epi,
             "elem": e, "pixels_out": wl.N * Ho * Wo}
@@ -72,6 +75,8 @@ def flops(wl) -> int:
     P = wl.N * wl.Ho * wl.Wo
     if wl.kind == "dwpw":
         return 2 * P * wl.C * wl.R * wl.S + 2 * P * wl.C * wl.K
+    if wl.kind == "pwdw":
+        return 2 * wl.N * wl.H * wl.W * wl.C * wl.K1 + 2 * P * wl.K1 * wl.R * wl.S
     return 2 * P * wl.K1 * wl.C * wl.R * wl.S + 2 * P * wl.K1 * wl.K
 
 
@@ -159,6 +164,28 @@ def dwpw_gma(dw_ifms_d: int, dw_overlap: int, dw_ifms_sz: int, dw_weights_sz: in
             * _ceil_div(pw_weights_sz, pw_weights_tile_sz)
             + n_out_tiles * (pw_weights_sz + dw_weights_sz)
             + pw_ofms_sz)
+
+
+def pwdw_redundancy(H: int, W: int, tile_h: int, tile_w: int, stride: int = 1,
+                    pad: int = 1, filt: int = 3) -> float:
+    """Redundant pointwise work of a tiled PW->DW module (the _R of PWDW_R, FCM paper
+    Sec. II-D and Table II): every output tile of tile_h x tile_w depthwise outputs
+    recomputes the intermediate over its whole input window, clipped to the image, so
+    the pointwise layer runs on sum(window pixels) instead of H * W pixels.  Returns
+    sum(window pixels) / (H * W) - 1; zero when one tile covers the whole plane (the
+    PWDW case without redundancy)."""
+    Ho = (H + 2 * pad - filt) // stride + 1
+    Wo = (W + 2 * pad - filt) // stride + 1
+
+    def inside(n_out, tile, n_in):
+        tot = 0
+        for t in range(_ceil_div(n_out, tile)):
+            lo = t * tile * stride - pad
+            hi = lo + (min(tile, n_out - t * tile) - 1) * stride + filt
+            tot += max(0, min(hi, n_in) - max(lo, 0))
+        return tot
+
+    return inside(Ho, tile_h, H) * inside(Wo, tile_w, W) / (H * W) - 1.0
 
 
 def brute_force_overlap(ch_w: int, ch_h: int, tile_w: int, tile_h: int, filt: int,

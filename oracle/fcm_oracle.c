@@ -13,6 +13,10 @@
  *                       ("Fusing Depthwise and Pointwise Convolutions for Efficient
  *                       Inference on GPUs", Sec. II-B, Fig. 2);
  *   pointwise conv   -- a 1x1 filter spanning all channels (same section);
+ *   PW -> DW module  -- the pointwise layer first, then the depthwise layer over its
+ *                       output (the PWDW / PWDW_R fusion cases, FCM paper Sec. II-D,
+ *                       Fig. 3(b), and Sec. III); the depthwise layer's zero padding
+ *                       pads the intermediate, not the module's input;
  *   standard conv    -- the first layer of the back-to-back pair, [N,H,W,C] x
  *                       [K,C,R,S] ("Fusing two back-to-back convolutions", the
  *                       CONV1/CONV2 example);
@@ -323,6 +327,63 @@ int fcm_oracle_b2b_at(const double* x, int N, int H, int W, int C, const double*
         pw_row(t, K1, w2, K, yr);
         epilogue_row(yr, K, scale2, bias2, act2);
         fcm_oracle_round_array(yr, K, dtype);
+        free(t);
+    }
+    return 0;
+}
+
+
+/* PW -> DW module, layer by layer (FCM paper Sec. II-D, Fig. 3(b), PWDW_R):
+ *   t = round(act1(scale1 * (x . w_pw^T) + bias1))   over every input pixel,
+ *   y = round(act2(scale2 * dw(t, w_dw) + bias2)),
+ * w_pw [K1][C], w_dw [K1][R][S]; the depthwise layer's padding is zeros around t. */
+int fcm_oracle_pwdw(const double* x, int N, int H, int W, int C, const double* w_pw, int K1,
+                    const double* scale1, const double* bias1, int act1, const double* w_dw,
+                    int R, int S, int sh, int sw, int ph, int pw, const double* scale2,
+                    const double* bias2, int act2, int dtype, double* t_out, double* y) {
+    int Ho = out_size(H, ph, R, sh), Wo = out_size(W, pw, S, sw);
+    int64_t M = (int64_t)N * H * W;
+    double* t = t_out ? t_out : (double*)malloc(sizeof(double) * (size_t)(M * K1));
+    if (!t) return -1;
+    fcm_oracle_pw(x, M, C, w_pw, K1, t);
+    fcm_oracle_epilogue(t, M, K1, scale1, bias1, act1);
+    fcm_oracle_round_array(t, M * K1, dtype);
+    fcm_oracle_dw(t, N, H, W, K1, w_dw, R, S, sh, sw, ph, pw, y);
+    int64_t Mo = (int64_t)N * Ho * Wo;
+    fcm_oracle_epilogue(y, Mo, K1, scale2, bias2, act2);
+    fcm_oracle_round_array(y, Mo * K1, dtype);
+    if (!t_out) free(t);
+    return 0;
+}
+
+/* The PW -> DW module at listed output pixels only: every intermediate value the
+ * pixel's window reads is recomputed from the input (exactly the redundant
+ * computation of the PWDW_R case), window positions outside the image contribute
+ * nothing. */
+int fcm_oracle_pwdw_at(const double* x, int N, int H, int W, int C, const double* w_pw,
+                       int K1, const double* scale1, const double* bias1, int act1,
+                       const double* w_dw, int R, int S, int sh, int sw, int ph, int pw,
+                       const double* scale2, const double* bias2, int act2, int dtype,
+                       const int32_t* pix /* [P][3] */, int64_t P, double* y_rows) {
+    (void)N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < P; ++i) {
+        int n = pix[3 * i], oh = pix[3 * i + 1], ow = pix[3 * i + 2];
+        double* t = (double*)malloc(sizeof(double) * (size_t)K1);
+        if (!t) continue;
+        double* yr = y_rows + i * K1;
+        for (int k = 0; k < K1; ++k) yr[k] = 0.0;
+        for (int r = 0; r < R; ++r)
+            for (int s = 0; s < S; ++s) {
+                int ih = oh * sh - ph + r, iw = ow * sw - pw + s;
+                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;
+                pw_row(x + (((int64_t)n * H + ih) * W + iw) * C, C, w_pw, K1, t);
+                epilogue_row(t, K1, scale1, bias1, act1);
+                fcm_oracle_round_array(t, K1, dtype);
+                for (int k = 0; k < K1; ++k) yr[k] += t[k] * w_dw[((int64_t)k * R + r) * S + s];
+            }
+        epilogue_row(yr, K1, scale2, bias2, act2);
+        fcm_oracle_round_array(yr, K1, dtype);
         free(t);
     }
     return 0;

@@ -301,6 +301,174 @@ def test_sampled_rows_equal_full_outputs():
 
 
 # ---------------------------------------------------------------------------------
+# the pointwise -> depthwise module
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,stride,pad", [("f32", 1, 1), ("f16", 1, 1), ("bf16", 1, 1),
+                                              ("f16", 2, 1), ("f16", 1, 0)])
+def test_pwdw_module_is_layer_by_layer_pipeline(dtype, stride, pad):
+    rng = _rng(31 + stride + 3 * pad)
+    N, H, W, C, K1 = 2, 7, 6, 8, 24
+    x = oracle.round_to(rng.standard_normal((N, H, W, C)), dtype)
+    wp = oracle.round_to(rng.standard_normal((K1, C)) * 0.3, dtype)
+    wd = oracle.round_to(rng.standard_normal((K1, 3, 3)) * 0.3, dtype)
+    s1, b1 = rng.uniform(0.5, 1.5, K1), rng.standard_normal(K1) * 0.1
+    s2, b2 = rng.uniform(0.5, 1.5, K1), rng.standard_normal(K1) * 0.1
+    y, t = oracle.pwdw(x, wp, wd, (stride, stride), (pad, pad), s1, b1, "relu6", s2, b2,
+                       "relu", dtype, return_t=True)
+    # reference pipeline from library routines: 1x1 conv2d, then a grouped conv2d whose
+    # zero padding surrounds the rounded intermediate; rounding by numpy/torch casts
+    tr = _torch_round(np.clip(_torch_conv(x, wp[:, :, None, None], 1, 0) * s1 + b1, 0, 6),
+                      dtype)
+    yr = _torch_round(np.maximum(_torch_dw(tr, wd, stride, pad) * s2 + b2, 0), dtype)
+    ulp = {"f32": 2.0 ** -23, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[dtype]
+    assert t.shape == (N, H, W, K1) and y.shape == yr.shape
+    assert np.all(np.abs(t - tr) <= ulp * np.abs(tr) + 1e-30)
+    assert np.all(np.abs(y - yr) <= 2 * ulp * np.maximum(np.abs(yr), 1e-3) + 1e-30)
+    assert np.mean(y == yr) > 0.97
+
+
+def test_pwdw_brute_force_tiny():
+    # the definition written out with Python loops on a 3x4 image
+    rng = _rng(32)
+    N, H, W, C, K1 = 1, 3, 4, 3, 2
+    x = rng.standard_normal((N, H, W, C))
+    wp = rng.standard_normal((K1, C))
+    wd = rng.standard_normal((K1, 3, 3))
+    b1 = rng.standard_normal(K1)
+    y = oracle.pwdw(x, wp, wd, bias1=b1, act1="relu", dtype="f32")
+    t = np.zeros((H, W, K1))
+    for h in range(H):
+        for w in range(W):
+            for k in range(K1):
+                v = sum(x[0, h, w, c] * wp[k, c] for c in range(C)) + b1[k]
+                t[h, w, k] = float(np.float32(max(v, 0.0)))
+    for oh in range(H):
+        for ow in range(W):
+            for k in range(K1):
+                acc = 0.0
+                for r in range(3):
+                    for s_ in range(3):
+                        ih, iw = oh - 1 + r, ow - 1 + s_
+                        if 0 <= ih < H and 0 <= iw < W:
+                            acc += t[ih, iw, k] * wd[k, r, s_]
+                assert abs(y[0, oh, ow, k] - float(np.float32(acc))) <= 1e-6 * max(1, abs(acc))
+
+
+def test_pwdw_padding_surrounds_the_intermediate():
+    # x = 0: the intermediate is round(relu(bias1)) at every pixel, and with all-ones
+    # depthwise filters each output counts the window positions inside the image
+    # (4 in a corner, 6 on an edge, 9 inside); padding the module's input instead would
+    # give 9 everywhere
+    N, H, W, C, K1 = 1, 5, 6, 8, 16
+    b1 = np.linspace(0.1, 1.6, K1)
+    y = oracle.pwdw(np.zeros((N, H, W, C)), np.ones((K1, C)), np.ones((K1, 3, 3)),
+                    bias1=b1, act1="relu", dtype="f16")
+    t = oracle.round_to(b1, "f16")
+    count = np.full((H, W), 9.0)
+    count[0, :] -= 3
+    count[-1, :] -= 3
+    count[:, 0] -= 3
+    count[:, -1] -= 3
+    count[0, 0] = count[0, -1] = count[-1, 0] = count[-1, -1] = 4
+    expect = oracle.round_to(count[:, :, None] * t[None, None, :], "f16")
+    assert np.array_equal(y[0], expect)
+
+
+def test_pwdw_identity_depthwise_returns_the_intermediate():
+    rng = _rng(33)
+    x = oracle.round_to(rng.standard_normal((2, 5, 4, 8)), "bf16")
+    wp = oracle.round_to(rng.standard_normal((16, 8)) * 0.4, "bf16")
+    wd = np.zeros((16, 3, 3))
+    wd[:, 1, 1] = 1.0
+    y, t = oracle.pwdw(x, wp, wd, scale1=rng.uniform(0.5, 1.5, 16),
+                       bias1=rng.standard_normal(16) * 0.1, act1="relu6", dtype="bf16",
+                       return_t=True)
+    assert np.array_equal(y, t)
+    # and an identity pointwise layer hands the input to the depthwise layer unchanged
+    wd2 = oracle.round_to(rng.standard_normal((8, 3, 3)), "bf16")
+    y2, t2 = oracle.pwdw(x, np.eye(8), wd2, dtype="bf16", return_t=True)
+    assert np.array_equal(t2, x)
+    assert np.array_equal(y2, oracle.round_to(_torch_dw(x, wd2, 1, 1), "bf16"))
+
+
+def test_pwdw_stride2_is_stride1_subsampled():
+    rng = _rng(34)
+    x = oracle.round_to(rng.standard_normal((1, 9, 8, 8)), "f16")
+    wp = oracle.round_to(rng.standard_normal((16, 8)) * 0.3, "f16")
+    wd = oracle.round_to(rng.standard_normal((16, 3, 3)) * 0.3, "f16")
+    kw = dict(bias1=rng.standard_normal(16) * 0.1, act1="relu6", scale2=rng.uniform(
+        0.5, 1.5, 16), act2="relu", dtype="f16")
+    y1 = oracle.pwdw(x, wp, wd, (1, 1), (1, 1), **kw)
+    y2 = oracle.pwdw(x, wp, wd, (2, 2), (1, 1), **kw)
+    assert np.array_equal(y2, y1[:, ::2, ::2, :])
+
+
+def test_pwdw_sampled_rows_equal_full_outputs():
+    for name in ("pwdw_f16_32x56x56_c24_k144", "pwdw_f16_32x112x112_c16_k96_s2"):
+        wl = fcm_inputs.WORKLOADS[name].replace(N=2, H=11, W=19)
+        inp = fcm_inputs.make_inputs(wl)
+        kw = dict(stride=(wl.stride,) * 2, pad=(1, 1), scale1=inp["scale1"],
+                  bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],
+                  act2=wl.act2, dtype=wl.dtype)
+        full = oracle.pwdw(inp["x"], inp["w1"], inp["w2"], **kw)
+        pix = fcm_inputs.sample_pixels(wl, 40)
+        rows = oracle.pwdw_at(inp["x"], inp["w1"], inp["w2"], pix, **kw)
+        assert np.array_equal(rows, full[pix[:, 0], pix[:, 1], pix[:, 2]])
+
+
+def _brute_force_recompute(H, W, th, tw, stride, pad=1, filt=3):
+    # count, pixel by pixel, how many output tiles' windows need each intermediate
+    # value (windows clipped to the image)
+    Ho = (H + 2 * pad - filt) // stride + 1
+    Wo = (W + 2 * pad - filt) // stride + 1
+    need = np.zeros((H, W), np.int64)
+    for t0 in range(0, Ho, th):
+        for u0 in range(0, Wo, tw):
+            m = np.zeros((H, W), bool)
+            for oh in range(t0, min(t0 + th, Ho)):
+                for ow in range(u0, min(u0 + tw, Wo)):
+                    for r in range(filt):
+                        for s_ in range(filt):
+                            ih, iw = oh * stride - pad + r, ow * stride - pad + s_
+                            if 0 <= ih < H and 0 <= iw < W:
+                                m[ih, iw] = True
+            need += m
+    return need
+
+
+@pytest.mark.parametrize("H,W,th,tw,stride", [(56, 56, 8, 16, 1), (17, 23, 4, 16, 1),
+                                              (112, 112, 4, 16, 2), (9, 9, 3, 5, 2),
+                                              (14, 14, 14, 14, 1)])
+def test_pwdw_redundancy_equals_brute_force(H, W, th, tw, stride):
+    need = _brute_force_recompute(H, W, th, tw, stride)
+    expect = need.sum() / (H * W) - 1.0
+    assert abs(accounting.pwdw_redundancy(H, W, th, tw, stride) - expect) < 1e-12
+
+
+def test_page_pwdw_without_tiling_has_no_redundancy():
+    # Table II: the PWDW cases (no spatial tiling) recompute nothing
+    g = _golden()["pwdw_no_redundant_compute"]
+    for H, W, s in [(56, 56, 1), (28, 28, 2), (7, 7, 1)]:
+        Ho, Wo = (H - 1) // s + 1, (W - 1) // s + 1
+        assert accounting.pwdw_redundancy(H, W, Ho, Wo, s) == g["pwdw_redundancy"]
+        assert _brute_force_recompute(H, W, Ho, Wo, s).max() == 1
+
+
+def test_pwdw_accounting_closed_forms():
+    wl = fcm_inputs.WORKLOADS["pwdw_f16_32x56x56_c24_k144"]
+    s = accounting.sizes(wl)
+    # the intermediate is the pointwise layer's output at the input resolution
+    assert s["t"] == 32 * 56 * 56 * 144 * 2
+    assert accounting.alg_bytes(wl) == (32 * 56 * 56 * 24 * 2 + 32 * 56 * 56 * 144 * 2 +
+                                        144 * 24 * 2 + 144 * 9 * 2 + 4 * 4 * 144)
+    assert accounting.alg_bytes(wl, False) - accounting.alg_bytes(wl) == 2 * s["t"]
+    assert accounting.flops(wl) == 2 * 32 * 56 * 56 * (24 * 144 + 144 * 9)
+    wl2 = fcm_inputs.WORKLOADS["pwdw_f16_32x112x112_c16_k96_s2"]
+    assert (wl2.Ho, wl2.Wo) == (56, 56)
+    assert accounting.sizes(wl2)["t"] == 32 * 112 * 112 * 96 * 2
+
+
+# ---------------------------------------------------------------------------------
 # the pages' own facts
 # ---------------------------------------------------------------------------------
 def _golden():
