@@ -29,6 +29,7 @@ SOURCES = [
     ("kernels/dwpw_mm.hip", True),
     ("kernels/dwpw_mmw.hip", True),
     ("kernels/b2b_mm.hip", True),
+    ("kernels/pwdw_mm.hip", True),
     ("kernels/lbl.hip", True),
     ("kernels/b2b.hip", True),
     ("api.cpp", True),

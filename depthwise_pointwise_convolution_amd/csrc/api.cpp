@@ -51,6 +51,8 @@ const VariantImpl kImpls[] = {
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
     {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>,           \
      occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>},
+#define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
+    {launch_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>, occ_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -58,6 +60,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_DWPW_MM
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
+#undef FCM_V_PWDW_MM
 };
 static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
 
@@ -162,7 +165,7 @@ void set_tiles(KArgs* a, int th, int tw, int kt, int kdim) {
 
 fcm_status launch_fused(const fcm_plan_t* plan, KArgs& a, void* stream) {
     const VariantDesc& v = kVariants[plan->variant];
-    set_tiles(&a, v.th, v.tw, v.kt, plan->prob.K);
+    set_tiles(&a, v.th, v.tw, v.kt, plan->prob.K);  // (PWDW: K == K1)
     int cus = 0, per_cu = 0;
     FCM_TRY(device_capacity(plan->variant, &cus, &per_cu));
     // persistent grid within what the GPU holds at once (measured occupancy) and the
@@ -272,7 +275,9 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                              "16-byte aligned");
         const char* s = (const char*)w1_src;
         const char* d = (const char*)w1_dst;
-        const int64_t ns = (int64_t)(p.kind == FCM_KIND_B2B ? p.K1 : 1) * p.R * p.S * p.C * e;
+        const int64_t ns = p.kind == FCM_KIND_PWDW
+                               ? (int64_t)p.K1 * p.C * e
+                               : (int64_t)(p.kind == FCM_KIND_B2B ? p.K1 : 1) * p.R * p.S * p.C * e;
         const int64_t nd = plan->w1_packed_bytes;
         if (s < d + nd && d < s + ns) return fail(FCM_ERR_INVALID_ARG, "w1 buffers overlap");
     }
@@ -282,9 +287,22 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                              "16-byte aligned");
         const char* s = (const char*)w2_src;
         const char* d = (const char*)w2_dst;
-        const int64_t ns = (int64_t)p.K * (p.kind == FCM_KIND_B2B ? p.K1 : p.C) * e;
+        const int64_t ns = p.kind == FCM_KIND_PWDW
+                               ? (int64_t)p.K1 * p.R * p.S * e
+                               : (int64_t)p.K * (p.kind == FCM_KIND_B2B ? p.K1 : p.C) * e;
         const int64_t nd = plan->w2_packed_bytes;
         if (s < d + nd && d < s + ns) return fail(FCM_ERR_INVALID_ARG, "w2 buffers overlap");
+    }
+    if (p.kind == FCM_KIND_PWDW) {
+        // first layer: pointwise [K1][C] copied as is; second: depthwise [K1][R*S] ->
+        // [R*S][K1]
+        int rc = 0;
+        if (w1_src) rc = launch_copy(w1_src, w1_dst, (int64_t)p.K1 * p.C * e, stream);
+        if (rc == 0 && w2_src) rc = launch_pack_dw(e, w2_src, w2_dst, p.K1, p.R * p.S, stream);
+        if (rc != 0)
+            return fail(FCM_ERR_HIP, std::string("weight packing failed: ") +
+                                         hipGetErrorString((hipError_t)rc));
+        return ok();
     }
     if (w1_src) {
         int rc;
@@ -363,6 +381,31 @@ fcm_status fcm_b2b_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w
     return launch_fused(plan, a, stream);
 }
 
+fcm_status fcm_pwdw_fwd(const fcm_plan_t* plan, const void* x, const void* w_pw,
+                        const float* scale1, const float* bias1, const void* w_dw,
+                        const float* scale2, const float* bias2, void* y, void* stream) {
+    FCM_TRY(check_plan(plan, FCM_KIND_PWDW));
+    FCM_TRY(check_variant(plan));
+    FCM_TRY(need(x, "x", 16));
+    FCM_TRY(need(w_pw, "w_pw", 16));
+    FCM_TRY(need(w_dw, "w_dw", 16));
+    FCM_TRY(need(y, "y", 16));
+    FCM_TRY(optional(scale1, "scale1"));
+    FCM_TRY(optional(bias1, "bias1"));
+    FCM_TRY(optional(scale2, "scale2"));
+    FCM_TRY(optional(bias2, "bias2"));
+    KArgs a = base_args(plan);
+    a.x = x;
+    a.w1 = w_pw;
+    a.s1 = scale1;
+    a.b1 = bias1;
+    a.w2 = w_dw;
+    a.s2 = scale2;
+    a.b2 = bias2;
+    a.y = y;
+    return launch_fused(plan, a, stream);
+}
+
 fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_t nsets,
                     const void* const* x, const void* w1, const float* scale1,
                     const float* bias1, const void* w2, const float* scale2,
@@ -376,10 +419,15 @@ fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_
     int call = 0;
     auto run = [&](const fcm_plan_t* pl) {
         const int i = call++ % nsets;
-        return prob->kind == FCM_KIND_DWPW
-                   ? fcm_dwpw_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i], stream)
-                   : fcm_b2b_conv_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i],
-                                      stream);
+        switch (prob->kind) {
+        case FCM_KIND_DWPW:
+            return fcm_dwpw_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i], stream);
+        case FCM_KIND_PWDW:
+            return fcm_pwdw_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i], stream);
+        default:
+            return fcm_b2b_conv_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i],
+                                    stream);
+        }
     };
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
@@ -401,7 +449,7 @@ fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_
         if (st != FCM_OK) break;
         const int64_t ptiles = (int64_t)prob->N * ((pv.Ho + vd.th - 1) / vd.th) *
                                ((pv.Wo + vd.tw - 1) / vd.tw);
-        const int ktiles = (prob->K + vd.kt - 1) / vd.kt;
+        const int ktiles = (prob->K + vd.kt - 1) / vd.kt;  // (PWDW: K == K1)
         int64_t last_grid = -1;
         for (int w = 1; w <= std::min(4, per_cu) && st == FCM_OK; ++w) {
             const int64_t g = persistent_grid(ptiles, ktiles, (int64_t)cus * w);
@@ -442,13 +490,20 @@ fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_
 
 fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
                       const float* scale1, const float* bias1, void* t, void* stream) {
-    FCM_TRY(check_plan(plan, FCM_KIND_DWPW));
+    if (!plan) return fail(FCM_ERR_INVALID_ARG, "plan is NULL");
+    FCM_TRY(check_plan(plan, plan->prob.kind == FCM_KIND_PWDW ? FCM_KIND_PWDW : FCM_KIND_DWPW));
     FCM_TRY(need(x, "x", 16));
     FCM_TRY(need(w_dw, "w_dw", 16));
     FCM_TRY(need(t, "t", 16));
     FCM_TRY(optional(scale1, "scale1"));
     FCM_TRY(optional(bias1, "bias1"));
     KArgs a = base_args(plan);
+    if (plan->prob.kind == FCM_KIND_PWDW) {
+        // the second layer of a PW->DW module: depthwise over the K1-channel
+        // intermediate with the module's second epilogue
+        a.C = plan->prob.K1;
+        a.act1 = plan->prob.act2;
+    }
     a.x = x;
     a.w1 = w_dw;
     a.s1 = scale1;
@@ -474,6 +529,14 @@ fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
     KArgs a = base_args(plan);
     // the 1x1 layer reads the intermediate as its input: [N*Ho*Wo][C or K1]
     if (plan->prob.kind == FCM_KIND_B2B) a.C = plan->prob.K1;
+    if (plan->prob.kind == FCM_KIND_PWDW) {
+        // the first layer of a PW->DW module: every input pixel, C -> K1, with the
+        // module's first epilogue
+        a.Ho = plan->prob.H;
+        a.Wo = plan->prob.W;
+        a.K = plan->prob.K1;
+        a.act2 = plan->prob.act1;
+    }
     a.x = t;
     a.w2 = w_pw;
     a.s2 = scale2;

@@ -1,0 +1,423 @@
+// pwdw_mm.hip -- fused pointwise 1x1 -> depthwise 3x3 module (PWDW_R) with both
+// convolutions on the gfx950 matrix cores (16-bit storage, C <= CMAX input channels).
+//
+// The PW->DW fusion case of "Fusing Depthwise and Pointwise Convolutions for Efficient
+// Inference on GPUs" (Sec. II-D, Fig. 3(b); Sec. III) expands the channels with a
+// pointwise layer and filters each expanded channel with a depthwise 3x3 stencil, the
+// first half of an inverted-residual block.  The intermediate never reaches HBM; the
+// price is that a tile of depthwise outputs needs the intermediate over its whole input
+// window, so the pointwise layer is recomputed on the halo that neighbouring tiles share
+// (the "_R", redundant computation, of Table II).  When one tile covers the whole plane
+// nothing is recomputed (the PWDW case).
+//
+// Work of a workgroup: one TH x 16 tile of output pixels and KT = NW * BPW * 16 of the
+// expanded channels; wave w owns the 16-channel blocks w * BPW .. + BPW - 1 of that
+// slice, for both layers, so no barrier separates them.
+//   pointwise  T^T[c][p] = sum_ci Wpw[c][ci] * X[p][ci] over every 16-pixel block of the
+//              input window (IH x IW pixels, row-major): one v_mfma_f32_16x16x32 per
+//              16 channels x 16 pixels x 32 input channels.  The X operand (16 bytes of a
+//              window pixel per lane) is read once per pixel block for all of the wave's
+//              channel blocks.  The result arrives as 4 channels of one pixel per lane;
+//              epilogue 1 is applied, window pixels outside the image are set to zero
+//              (the depthwise layer's zero padding surrounds the intermediate, not the
+//              module's input), and the rounded values go to the wave's LDS tile.
+//   depthwise  the block-diagonal matrix form: A = the 16-channel filter diagonal for
+//              two taps, B = 16 bytes of the LDS intermediate per lane; the taps are
+//              paired by input row ((dh,0)+(dh,1) for each dh, (0,2)+(1,2), (2,2) with
+//              an empty tenth tap), so one B operand read serves every output row that
+//              uses its input row.  Epilogue 2, 8-byte buffer stores.
+// The intermediate tile of a channel block is stored [window row][chunk][column], 16
+// bytes per (pixel, 8 channels): the 16 lanes of a depthwise operand read (consecutive
+// output columns) then read consecutive 16-byte slots, free of bank conflicts at stride
+// 1, and the row offset of every read is a compile-time constant.
+//
+// The input window arrives by direct global->LDS loads (buffer_load_dwordx4 ... lds)
+// into two buffers: the next tile's window is requested at the start of a step and has
+// the whole step to arrive.  Chunk q of window pixel p sits at chunk position
+// q ^ ((p / (16 / NCH)) % NCH), so the 16 lanes of a pointwise operand read (16
+// consecutive window pixels, same chunk) fall in distinct bank groups.  Out-of-image
+// pixels and channels past C come back as zeros from the buffer range check; stores of
+// pixels outside the output get an out-of-range offset and are dropped, so every wave
+// issues the same number of memory instructions per step and the wait for the next
+// window counts them exactly.
+#include <type_traits>
+
+#include "mm_common.h"
+
+namespace fcm {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void pwdw_mm_kernel(KArgs a) {
+    constexpr int TW = 16;
+    constexpr int NT = 64 * NW;
+    constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3, NP = IH * IW;
+    constexpr int NPB = (NP + 15) / 16;  // 16-pixel blocks of the window
+    constexpr int NCH = CMAX / 8;        // 16-byte chunks per window pixel in LDS
+    static_assert(NCH == 4 || NCH == 8, "32 or 64 input channels");
+    constexpr int NKC = CMAX / 32;       // reduction steps of the pointwise product
+    constexpr int SLOTS = NPB * 16 * NCH;
+    constexpr int R = (SLOTS + NT - 1) / NT;  // direct-load rounds per window
+    constexpr int SLOTS_P = R * NT;
+    constexpr int KT = NW * BPW * 16;    // expanded channels of one workgroup
+    constexpr int NST = BPW * TH;        // buffer stores per lane per step
+    static_assert(NST < 64, "vmcnt range");
+    static_assert(NPB <= 32, "window validity fits one 32-bit mask");
+    // intermediate tile of one channel block: (IH + 1) rows (the extra row takes the
+    // pixels of the last, partial pixel block) x 2 chunks x IW columns x 16 bytes
+    constexpr int TROW = 2 * IW * 16;
+    constexpr int TREG = (IH + 1) * TROW;
+    constexpr int IHW = IH;              // input rows under the tile's TH output rows
+    (void)KT;
+
+    __shared__ __attribute__((aligned(16))) u32x4 xs0[SLOTS_P];
+    __shared__ __attribute__((aligned(16))) u32x4 xs1[SLOTS_P];
+    __shared__ __attribute__((aligned(16))) u32x4 tl[NW * BPW * TREG / 16];
+    u32x4* const X0 = xs0;
+    u32x4* const X1 = xs1;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    char* const tbase = reinterpret_cast<char*>(tl) + wave * BPW * TREG;
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
+    const int G = gridDim.x;
+    const int L = xcd_logical_id(blockIdx.x, G);
+    const int cb0 = (L % a.num_ktiles) * (NW * BPW) + wave * BPW;  // first owned block
+    const T* __restrict__ wpw = (const T*)a.w1;  // [K1][C]
+    const T* __restrict__ wdw = (const T*)a.w2;  // [9][K1]
+    const int es = (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rx = mm::rsrc(a.x, (uint32_t)(a.N * a.H * a.W * a.C * es));
+    const __amdgpu_buffer_rsrc_t ry = mm::rsrc(a.y, (uint32_t)(a.N * a.Ho * a.Wo * a.K1 * es));
+    const int in_img = a.H * a.W * a.C * es, in_row = a.W * a.C * es;
+    const int out_img = a.Ho * a.Wo * a.K1 * es, out_row = a.Wo * a.K1 * es;
+
+    // ---- tile walk: tiles pt0, pt0 + pstep, ... as (image, tile row, tile column),
+    // advanced by mixed-radix addition -------------------------------------------------
+    const int pstep = G / a.num_ktiles;
+    using Pos = mm::TilePos;
+    auto derive = [&](Pos& p) {
+        p.oh0 = p.th * TH;
+        p.ow0 = p.tw * TW;
+        p.ih0 = p.oh0 * S - a.pad_h;
+        p.iw0 = p.ow0 * S - a.pad_w;
+        p.in_base = p.n * in_img + p.ih0 * in_row + p.iw0 * a.C * es;
+        p.out_base = p.n * out_img + p.oh0 * out_row + p.ow0 * a.K1 * es;
+    };
+    auto split = [&](int t) {
+        Pos p;
+        const int per_img = a.tiles_h * a.tiles_w;
+        p.n = t / per_img;
+        const int rem = t - p.n * per_img;
+        p.th = rem / a.tiles_w;
+        p.tw = rem - p.th * a.tiles_w;
+        derive(p);
+        return p;
+    };
+    const Pos step = split(pstep);
+    auto advance = [&](Pos p) {
+        p.tw += step.tw;
+        if (p.tw >= a.tiles_w) {
+            p.tw -= a.tiles_w;
+            ++p.th;
+        }
+        p.th += step.th;
+        if (p.th >= a.tiles_h) {
+            p.th -= a.tiles_h;
+            ++p.n;
+        }
+        p.n += step.n;
+        derive(p);
+        return p;
+    };
+
+    // ---- direct-load plan (tile invariant) ------------------------------------------
+    // LDS slot s holds chunk position s % NCH of window pixel p = s / NCH, i.e. input
+    // chunk q = (s % NCH) ^ ((p / (16 / NCH)) % NCH).  dl_off: byte offset of the source
+    // from the window origin (kOob for pixels past the window and chunks past C);
+    // dl_pos: the pixel's window row and column.
+    uint32_t dl_off[R];
+    int dl_pos[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int s = r * NT + tid;
+        const int p = s / NCH, wr = p / IW, wc = p % IW;
+        const int q = (s % NCH) ^ ((p / (16 / NCH)) & (NCH - 1));
+        const bool real = p < NP && q * 8 < a.C;
+        dl_off[r] = real ? (uint32_t)((wr * a.W + wc) * a.C + q * 8) * (uint32_t)es : mm::kOob;
+        dl_pos[r] = real ? (wr << 16) | wc : 0;
+    }
+    // always R loads per lane (a tile past the end loads nothing), so waits are exact
+    auto issue_tile = [&](const Pos& t, auto buf) __attribute__((always_inline)) {
+        u32x4* dst = decltype(buf)::value == 0 ? X0 : X1;
+        const bool live = t.n < a.N;
+        const bool inside = live && t.ih0 >= 0 && t.iw0 >= 0 && t.ih0 + IH <= a.H &&
+                            t.iw0 + IW <= a.W;
+        if (inside) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t off = dl_off[r];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(dst + r * NT + wave * 64), 16,
+                    off, t.in_base, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int ih = t.ih0 + (dl_pos[r] >> 16), iw = t.iw0 + (dl_pos[r] & 0xffff);
+                const bool ok = live && dl_off[r] != mm::kOob && (unsigned)ih < (unsigned)a.H &&
+                                (unsigned)iw < (unsigned)a.W;
+                const uint32_t off = ok ? (uint32_t)(t.in_base + (int)dl_off[r]) : mm::kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(dst + r * NT + wave * 64), 16,
+                    off, 0, 0, 0);
+            }
+        }
+    };
+
+    Pos cur = split(L / a.num_ktiles);
+    issue_tile(cur, std::integral_constant<int, 0>{});
+
+    // ---- per-wave constants (requested after the first window) ----------------------
+    // pointwise A operand of block j, reduction step kc, lane (l%16, l/16): row =
+    // expanded channel 16 cb + l%16, reduction index 8(l/16) + e = input channel
+    // 32 kc + 8(l/16) + e: 16 contiguous bytes of the [K1][C] filters (zero past C/K1)
+    u32x4 apw[BPW][NKC];
+    // depthwise A operand of block j and tap pair tp: row = channel 16 cb + l%16,
+    // reduction index 8(l/16) + e = (tap pair_tap(tp, (l/16)/2), channel 8((l/16)&1) + e);
+    // non-zero only where that channel is the row's: one 16-bit element per lane
+    auto pair_tap = [](int tp, int hh) { return tp < 3 ? 3 * tp + hh : tp == 3 ? 3 * hh + 2 : 8 + hh; };
+    const bool dw_active = (lr >> 3) == (lg & 1);
+    uint16_t wdr[BPW][5];
+    float s1r[BPW][4], b1r[BPW][4], s2r[BPW][4], b2r[BPW][4];
+    const float* s1p = a.s1 ? a.s1 : (const float*)a.w1;
+    const float* b1p = a.b1 ? a.b1 : (const float*)a.w1;
+    const float* s2p = a.s2 ? a.s2 : (const float*)a.w1;
+    const float* b2p = a.b2 ? a.b2 : (const float*)a.w1;
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int c = (cb0 + j) * 16 + lr;
+        const int cc = c < a.K1 ? c : 0;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            const int ci = 32 * kc + 8 * lg;
+            const int cic = ci < a.C ? ci : 0;
+            apw[j][kc] = *reinterpret_cast<const u32x4*>(wpw + (int64_t)cc * a.C + cic);
+        }
+#pragma unroll
+        for (int tp = 0; tp < 5; ++tp) {
+            const int t = pair_tap(tp, lg >> 1);
+            wdr[j][tp] = __builtin_bit_cast(uint16_t, wdw[(t < 9 ? t : 0) * a.K1 + cc]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = (cb0 + j) * 16 + 4 * lg + i, kk = k < a.K1 ? k : 0;
+            s1r[j][i] = s1p[kk];
+            b1r[j][i] = b1p[kk];
+            s2r[j][i] = s2p[kk];
+            b2r[j][i] = b2p[kk];
+        }
+    }
+    mm::wait_vmcnt<0>();  // first window and constants
+    u32x4 adw[BPW][5];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int c = (cb0 + j) * 16 + lr;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            const bool ok = c < a.K1 && 32 * kc + 8 * lg < a.C;
+            if (!ok) apw[j][kc] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int tp = 0; tp < 5; ++tp) {
+            const int t = pair_tap(tp, lg >> 1);
+            const bool ok = dw_active && t < 9 && c < a.K1;
+            const uint32_t v = ok ? (uint32_t)wdr[j][tp] : 0u;
+            const uint32_t h = (lr & 1) ? (v << 16) : v;
+            const int w = (lr & 7) >> 1;
+            adw[j][tp] = u32x4{w == 0 ? h : 0u, w == 1 ? h : 0u, w == 2 ? h : 0u, w == 3 ? h : 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = (cb0 + j) * 16 + 4 * lg + i < a.K1;
+            s1r[j][i] = (a.s1 && ok) ? s1r[j][i] : 1.0f;
+            b1r[j][i] = (a.b1 && ok) ? b1r[j][i] : 0.0f;
+            s2r[j][i] = (a.s2 && ok) ? s2r[j][i] : 1.0f;
+            b2r[j][i] = (a.b2 && ok) ? b2r[j][i] : 0.0f;
+        }
+    }
+
+    // ---- per-lane offsets (tile invariant) -------------------------------------------
+    // pointwise X operand of window block pb, step kc: pixel 16 pb + l%16, chunk
+    // 4 kc + l/16 (the swizzle term does not depend on pb)
+    uint32_t xo[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+        const int q = 4 * kc + lg;
+        xo[kc] = (uint32_t)(lr * NCH + (q ^ ((lr / (16 / NCH)) & (NCH - 1)))) * 16u;
+    }
+    // intermediate write of window block pb: pixel p = 16 pb + l%16 at (row, column)
+    // (p / IW, p % IW) -- pixels past the window go to the spare row IH -- channels
+    // 4(l/16) .. + 3 of the block = chunk (l/16)/2, bytes 8((l/16)&1) .. + 7;
+    // wpos: the pixel's window row and column (row IH for the spare pixels)
+    uint32_t two[NPB];
+    int wpos[NPB];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+        const int p = 16 * pb + lr;
+        const int wr = p < NP ? p / IW : IH, wc = p < NP ? p % IW : (p - NP);
+        two[pb] = (uint32_t)(wr * TROW + ((lg >> 1) * IW + wc) * 16 + (lg & 1) * 8);
+        wpos[pb] = (wr << 16) | wc;
+    }
+    // depthwise B operand reads: lane (l%16, l/16) reads chunk (l/16)&1 of column
+    // l%16 * S + dw; the (dh,0)+(dh,1) pairs take dw = (l/16)/2 from one input row, the
+    // dw = 2 pairs take column + 2 from two consecutive rows ((l/16)/2 rows down)
+    const int hh = lg >> 1, ch = lg & 1;
+    const uint32_t rd_p = (uint32_t)((ch * IW + lr * S + hh) * 16);
+    const uint32_t rd_q = (uint32_t)(hh * TROW + (ch * IW + lr * S + 2) * 16);
+    const uint32_t rd_qc = (uint32_t)((ch * IW + lr * S + 2) * 16);
+    // output store offset of the lane's 4 channels within a pixel row of the tile
+    // (the channel block and row enter per store)
+    const uint32_t st_lane = (uint32_t)(lr * a.K1 + 4 * lg) * (uint32_t)es;
+
+    // which window rows a dw = 2 pair reads
+    auto q_used = [](int ir) {
+        return (ir % S == 0 && ir / S < TH) || (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < TH);
+    };
+
+    // one step: pointwise over the window of tile t (from buffer src) into the wave's
+    // intermediate tiles, depthwise over them, epilogues, stores
+    auto compute = [&](const u32x4* src, const Pos& t) __attribute__((always_inline)) {
+        // window validity of every pixel block for this lane (bit pb)
+        uint32_t valid = 0;
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) {
+            const int ih = t.ih0 + (wpos[pb] >> 16), iw = t.iw0 + (wpos[pb] & 0xffff);
+            const bool ok = (wpos[pb] >> 16) < IH && (unsigned)ih < (unsigned)a.H &&
+                            (unsigned)iw < (unsigned)a.W;
+            valid |= ok ? (1u << pb) : 0u;
+        }
+        const char* xb = reinterpret_cast<const char*>(src);
+        // pointwise layer over the window
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) {
+            u32x4 bx[NKC];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+                bx[kc] = *reinterpret_cast<const u32x4*>(xb + pb * 16 * NCH * 16 + xo[kc]);
+            const bool ok = (valid >> pb) & 1u;
+#pragma unroll
+            for (int j = 0; j < BPW; ++j) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) acc = mfma<T>(apw[j][kc], bx[kc], acc);
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    o[i] = ok ? epilogue(acc[i], s1r[j][i], b1r[j][i], act1) : 0.0f;
+                *reinterpret_cast<uint2*>(tbase + j * TREG + two[pb]) = pack8<T>(o);
+            }
+        }
+        // depthwise layer, block by block
+        const uint32_t voff_col = t.ow0 + lr < a.Wo ? st_lane : mm::kOob;
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            const char* tb = tbase + j * TREG;
+            f32x4 d[TH];
+#pragma unroll
+            for (int r = 0; r < TH; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ir = 0; ir < IHW; ++ir) {
+                const u32x4 bp = *reinterpret_cast<const u32x4*>(tb + ir * TROW + rd_p);
+                u32x4 bq = bp;
+                if (q_used(ir))
+                    bq = *reinterpret_cast<const u32x4*>(tb + ir * TROW +
+                                                         (ir + 1 < IHW ? rd_q : rd_qc));
+#pragma unroll
+                for (int dh = 0; dh < 3; ++dh)
+                    if (ir >= dh && (ir - dh) % S == 0 && (ir - dh) / S < TH)
+                        d[(ir - dh) / S] = mfma<T>(adw[j][dh], bp, d[(ir - dh) / S]);
+                if (ir % S == 0 && ir / S < TH) d[ir / S] = mfma<T>(adw[j][3], bq, d[ir / S]);
+                if (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < TH)
+                    d[(ir - 2) / S] = mfma<T>(adw[j][4], bq, d[(ir - 2) / S]);
+            }
+            // this lane's 4 channels exist (K1 is a multiple of 8, so a group of 4 is
+            // all in or all out)
+            const bool ch_ok = (cb0 + j) * 16 + 4 * lg < a.K1;
+#pragma unroll
+            for (int r = 0; r < TH; ++r) {
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = epilogue(d[r][i], s2r[j][i], b2r[j][i], act2);
+                const bool row_ok = ch_ok && t.oh0 + r < a.Ho && voff_col != mm::kOob;
+                const uint32_t v =
+                    row_ok ? (uint32_t)(t.out_base + r * out_row + (cb0 + j) * 16 * es) + voff_col
+                           : mm::kOob;
+                // the whole offset in the vector operand, scalar offset 0
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack8<T>(o)), ry, v,
+                                                      0, 0);
+            }
+        }
+    };
+
+    // ---- tile loop --------------------------------------------------------------------
+    // Step i (buffer P = i % 2): wait for tile i's window (the memory operations issued
+    // after its loads are the NST stores of step i-1); barrier (every wave's share of
+    // the window has landed, and every wave is done with step i-1, so buffer 1-P is
+    // free); request tile i+1 into buffer 1-P; compute tile i from buffer P.
+    auto step_fn = [&](auto par, bool first) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        if (!first) mm::wait_vmcnt<NST>();
+        __builtin_amdgcn_s_barrier();
+        const Pos nxt = advance(cur);
+        issue_tile(nxt, std::integral_constant<int, 1 - P>{});
+        compute(P == 0 ? X0 : X1, cur);
+        cur = nxt;
+    };
+    bool first = true;
+    while (cur.n < a.N) {
+        step_fn(std::integral_constant<int, 0>{}, first);
+        first = false;
+        if (cur.n >= a.N) break;
+        step_fn(std::integral_constant<int, 1>{}, false);
+    }
+    // loads of the tile past the end may still be in flight into LDS
+    mm::wait_vmcnt<0>();
+}
+
+template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
+int launch_pwdw_mm(const KArgs& a, int grid, void* stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((pwdw_mm_kernel<T, S, TH, CMAX, NW, BPW, OCC>), dim3(grid), dim3(64 * NW),
+                       0, (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
+int occ_pwdw_mm() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, pwdw_mm_kernel<T, S, TH, CMAX, NW, BPW, OCC>, 64 * NW, 0) != hipSuccess)
+        return 0;
+    return n;
+}
+
+#define FCM_V_DWPW(...)
+#define FCM_V_DWPW32(...)
+#define FCM_V_B2B(...)
+#define FCM_V_B2B_MM(...)
+#define FCM_V_DWPW_MM(...)
+#define FCM_V_DWPW_MMW(...)
+#define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC)                                \
+    template int launch_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>(const KArgs&, int, void*); \
+    template int occ_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>();
+#include "../variants.def"
+#undef FCM_V_DWPW
+#undef FCM_V_DWPW32
+#undef FCM_V_B2B
+#undef FCM_V_DWPW_MM
+#undef FCM_V_B2B_MM
+#undef FCM_V_DWPW_MMW
+#undef FCM_V_PWDW_MM
+
+}  // namespace fcm

@@ -35,17 +35,19 @@ namespace fcm {
 
 const VariantDesc kVariants[] = {
 #define FCM_V_DWPW(name, dt, CT, S, TH, TW, KT, CC, WRES, OCC) \
-    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0, 0, OCC, 4, 0},
+    {#name, VK_DWPW, dt, S, TH, TW, KT, CC, WRES ? 1 : 0, 0, 0, OCC, 4, 0, 0},
 #define FCM_V_DWPW32(name, S, TH, TW, KT, CC) \
-    {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 0, 1, 4, 0},
+    {#name, VK_DWPW32, FCM_F32, S, TH, TW, KT, CC, 0, 0, 0, 1, 4, 0, 0},
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
-    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, 0, K1, 1, 4, 0},
+    {#name, VK_B2B, dt, S, TH, TW, KT, CC, 1, 0, K1, 1, 4, 0, 0},
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC) \
-    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, NW, 0},
+    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, NW, 0, 0},
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC) \
-    {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC, 4, 0},
+    {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC, 4, 0, 0},
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
-    {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX},
+    {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0},
+#define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
+    {#name, VK_PWDW_MM, dt, S, TH, 16, NW * BPW * 16, CMAX, 1, 2, 0, OCC, NW, CMAX, BPW},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -53,6 +55,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_DWPW_MM
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
+#undef FCM_V_PWDW_MM
 };
 const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -127,6 +130,16 @@ int variant_lds_bytes(const VariantDesc& v) {
         return v.nbuf * slots_p * 16 + 2 * mb * (v.cc / 32) * 64 * 16 + 2 * v.kt * 4 +
                v.cmax * (9 * 2 + 2 * 4);
     }
+    case VK_PWDW_MM: {
+        // two input-window buffers (whole load rounds of 16-pixel blocks) and one
+        // intermediate tile per owned channel block: (IH + 1) rows x 2 chunks x IW
+        // columns x 16 bytes
+        const int nt = 64 * v.waves;
+        const int npb = (IH * IW + 15) / 16;
+        const int slots = npb * 16 * (v.cmax / 8);
+        const int slots_p = (slots + nt - 1) / nt * nt;
+        return 2 * slots_p * 16 + v.waves * v.bpw * (IH + 1) * 2 * IW * 16;
+    }
     default:
         return IH * IW * (v.cc + 8) * e + 2 * v.k1 * 4 + 2 * v.kt * 4;
     }
@@ -171,6 +184,16 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
         return 4 * mb * kbw + 16 * kbw + 28 + 5 * ppw + 2 * ((slots + nt - 1) / nt) + 36 + 24;
     }
+    case VK_PWDW_MM: {
+        // per owned block: pointwise operands, five depthwise operands, both epilogues'
+        // constants; window offsets and positions per pixel block, the direct-load plan,
+        // the output rows' accumulators, operands in flight, addressing
+        const int IH = (v.th - 1) * v.stride + 3, IW = 15 * v.stride + 3;
+        const int npb = (IH * IW + 15) / 16, nt = 64 * v.waves;
+        const int slots = npb * 16 * (v.cmax / 8);
+        return v.bpw * (4 * (v.cmax / 32) + 20 + 16) + 2 * npb + 2 * ((slots + nt - 1) / nt) +
+               4 * v.th + 16 + 48;
+    }
     default: {
         const int KB1 = v.k1 / 16, KB2 = v.kt / 16, KS2 = v.k1 / 32;
         return 40 + MBW * KB1 * 4 + KS2 * KB2 * 4 + KB2 * 4 + MBW * 4 + 24;
@@ -183,7 +206,7 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         *err = "problem pointer is NULL";
         return FCM_ERR_INVALID_ARG;
     }
-    if (p->kind != FCM_KIND_DWPW && p->kind != FCM_KIND_B2B) {
+    if (p->kind != FCM_KIND_DWPW && p->kind != FCM_KIND_B2B && p->kind != FCM_KIND_PWDW) {
         *err = "unknown kind";
         return FCM_ERR_INVALID_ARG;
     }
@@ -204,6 +227,10 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
     }
     if (p->kind == FCM_KIND_DWPW && p->K1 != p->C) {
         *err = "a depthwise layer keeps the channel count: K1 must equal C";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->kind == FCM_KIND_PWDW && p->K != p->K1) {
+        *err = "the depthwise layer of a PW->DW module keeps the channel count: K must equal K1";
         return FCM_ERR_INVALID_ARG;
     }
     if (p->pad_h >= p->R || p->pad_w >= p->S) {
@@ -240,10 +267,36 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         *err = "the back-to-back kernels need 16-bit storage (fp16 or bf16)";
         return FCM_ERR_UNSUPPORTED;
     }
+    if (p->kind == FCM_KIND_PWDW && p->dtype == FCM_F32) {
+        *err = "the PW->DW kernels need 16-bit storage (fp16 or bf16)";
+        return FCM_ERR_UNSUPPORTED;
+    }
     return FCM_OK;
 }
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
+    if ((v.vkind == VK_PWDW_MM) != (p.kind == FCM_KIND_PWDW) || v.dtype != p.dtype) {
+        if (why) *why = "variant is for another module kind or storage type";
+        return false;
+    }
+    if (v.vkind == VK_PWDW_MM) {
+        if (v.stride != p.stride_h) {
+            if (why) *why = "variant is compiled for another stride";
+            return false;
+        }
+        if (p.C > v.cmax) {
+            if (why) *why = "PW->DW variant stages at most its compiled input channel count";
+            return false;
+        }
+        const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
+        const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
+        if ((int64_t)p.N * p.H * p.W * p.C * 2 >= ((int64_t)1 << 31) ||
+            (int64_t)p.N * Ho * Wo * p.K1 * 2 >= ((int64_t)1 << 31)) {
+            if (why) *why = "PW->DW variant addresses whole tensors below 2 GiB";
+            return false;
+        }
+        return true;
+    }
     const int want = p.kind == FCM_KIND_B2B ? VK_B2B : (p.dtype == FCM_F32 ? VK_DWPW32 : VK_DWPW);
     const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMW)
                          ? VK_DWPW
@@ -417,6 +470,108 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     return r;
 }
 
+// PW->DW module (FCM paper Sec. II-D, Fig. 3(b); Eq. 4).  The pointwise layer runs on
+// every tile's whole input window (clipped to the image), so the intermediate on the
+// windows' overlap is computed once per tile that needs it; the depthwise layer runs
+// once per output pixel.
+Estimate estimate_pwdw(const VariantDesc& v, const fcm_problem& p, const fcm_device_spec& d,
+                       int Ho, int Wo) {
+    Estimate r{};
+    const int e = elem_bytes(p.dtype);
+    const int lds = variant_lds_bytes(v);
+    int vg = (variant_vgpr_estimate(v) + 7) / 8 * 8;
+    const int wps = std::max(v.waves / 4, 1);
+    const int occ_lds = lds > 0 ? d.lds_bytes_per_cu / lds : 8;
+    const int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ) / wps;
+    int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd / wps);
+    occ = std::min(occ, std::max(v.occ / wps, 1));
+    if (lds > d.lds_bytes_per_wg) occ = 0;
+    r.wgs_per_cu = occ;
+    const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);
+    const int64_t ptiles = (int64_t)p.N * tiles_h * tiles_w;
+    const int ktiles = (int)cdiv(p.K1, v.kt);
+    r.num_tiles = (int)std::min<int64_t>(ptiles * ktiles, INT32_MAX);
+    const int64_t grid = persistent_grid(ptiles, ktiles, (int64_t)d.num_cus * std::max(occ, 1));
+    r.grid = (int)grid;
+
+    // input windows: the exact clipped footprint, once per channel slice
+    const int64_t win = halo_pixels(Ho, Wo, p.H, p.W, v.th, v.tw, p.stride_h, p.pad_h, p.pad_w);
+    const int64_t x_reads = win * p.N * p.C * e * ktiles;
+    const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K1 * e;
+    const int kt = std::min(v.kt, p.K1);
+    const int64_t w_slice = (int64_t)kt * p.C * e + 9LL * kt * e + 4LL * 4 * kt;
+    r.pred = x_reads + y_bytes + grid * w_slice;
+    // pointwise pixels computed per pixel of the intermediate (1 = no recomputation)
+    r.waste = (double)win / ((double)p.H * p.W) *
+              ((double)tiles_h * v.th * tiles_w * v.tw) / ((double)Ho * Wo);
+
+    const double alg = (double)p.N * p.H * p.W * p.C * e + (double)y_bytes +
+                       (double)p.K1 * p.C * e + 9.0 * p.K1 * e;
+    // window pixels the pointwise layer runs on (each K slice for its own channels)
+    const double pw_px = (double)win * p.N;
+    const double out_px = (double)p.N * tiles_h * v.th * tiles_w * v.tw;
+    const double c_pad = (double)cdiv(p.C, 32) * 32;
+    // matrix work as executed: the pointwise product padded to 32 input channels, the
+    // block-diagonal depthwise product (320 flop-equivalents per channel and pixel)
+    const double t_mat = (pw_px * 2.0 * c_pad * p.K1 + out_px * 320.0 * p.K1) / d.mfma_f16_flops;
+    // vector work: an epilogue (fma, clamp, conversion) per intermediate and output value
+    const double t_vec = 3.0 * p.K1 * (pw_px + out_px) / (d.valu_f32_flops / 2.0);
+    const double t_hbm = alg / d.hbm_bytes_per_s;
+    const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);
+    const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
+    r.t_us = std::max(std::max(t_hbm, t_l2), std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+
+    // Eq. 4 as printed, plus the module's own output write (the OFMs are written once):
+    // the PW input with its overlap (Eq. 1 over the input plane with the tile extents in
+    // input pixels, times the PW input depth) once per weight tile of whichever layer
+    // has more, PW filters once per output tile, DW filters once per spatial tile.
+    const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, 3,
+                                       p.stride_h);
+    const double ifm = (double)p.N * p.H * p.W * p.C * e;
+    const double w_pw = (double)p.K1 * p.C * e, w_pw_tile = (double)kt * p.C * e;
+    const double w_dw = 9.0 * p.K1 * e, w_dw_tile = 9.0 * kt * e;
+    const double ofm = (double)y_bytes, ofm_tile = (double)v.th * v.tw * kt * e;
+    const bool fits = lds <= d.lds_bytes_per_wg && occ > 0;
+    const bool enough = r.num_tiles >= d.num_cus;
+    r.feasible = fits && enough;
+    if (!r.feasible) {
+        r.gma = INFINITY;
+    } else {
+        r.gma = (2.0 * p.C * overlap * p.N * e + ifm) *
+                    std::max(ceil(w_pw / w_pw_tile), ceil(w_dw / w_dw_tile)) +
+                ceil(ofm / ofm_tile) * w_pw +
+                ceil((double)Ho * Wo / ((double)v.th * v.tw)) * w_dw + ofm;
+    }
+    return r;
+}
+
+// Layer-by-layer PW->DW: the 1x1 kernel over every input pixel writes the intermediate,
+// the depthwise kernel reads it back.  Bytes with the baseline kernels' tilings, and
+// Eq. 2 (PW) + Eq. 3 (DW).
+void estimate_unfused_pwdw(const fcm_problem& p, int Ho, int Wo, int64_t* pred, double* gma) {
+    const int e = elem_bytes(p.dtype);
+    const int64_t x_bytes = (int64_t)p.N * p.H * p.W * p.C * e;
+    const int64_t t_bytes = (int64_t)p.N * p.H * p.W * p.K1 * e;
+    const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K1 * e;
+    const int64_t w_pw = (int64_t)p.K1 * p.C * e;
+    const int mt = lbl::PW_MT16, kt = lbl::PW_KT16;
+    const int64_t m = (int64_t)p.N * p.H * p.W;
+    const int64_t first = x_bytes * cdiv(p.K1, kt) + cdiv(m, mt) * w_pw + t_bytes;
+    const int th = lbl::DW_TH, tw = lbl::DW_TW, cc = lbl::DW_CC16;
+    const int64_t halo = halo_pixels(Ho, Wo, p.H, p.W, th, tw, p.stride_h, p.pad_h, p.pad_w);
+    const int64_t tiles_px = (int64_t)p.N * cdiv(Ho, th) * cdiv(Wo, tw);
+    const int64_t second = halo * p.N * p.K1 * e + tiles_px * cdiv(p.K1, cc) * 9LL * cc * e +
+                           y_bytes;
+    *pred = first + second;
+    const double g1 = ceil((double)w_pw / ((double)std::min(kt, p.K1) * p.C * e)) * x_bytes +
+                      (double)t_bytes +
+                      ceil((double)t_bytes / ((double)mt * std::min(kt, p.K1) * e)) * w_pw;
+    const double overlap = eq1_overlap(p.W, p.H, tw * p.stride_w, th * p.stride_h, 3, p.stride_h);
+    const double g2 = 2.0 * p.K1 * overlap * p.N * e + (double)t_bytes + (double)y_bytes +
+                      ceil((double)Ho * Wo / (double)(th * tw)) * 9.0 * p.K1 * e;
+    *gma = g1 + g2;
+}
+
 // Layer-by-layer bytes with the baseline kernels' fixed tilings, and the pages'
 // Eq. 3 (first layer) + Eq. 2 (1x1 layer) estimate.
 void estimate_unfused(const fcm_problem& p, const fcm_device_spec& d, int Ho, int Wo,
@@ -506,7 +661,8 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         if (forced >= 0 && i != forced) continue;
         const VariantDesc& v = kVariants[i];
         if (!variant_runs(v, *p, forced >= 0 ? &why : nullptr)) continue;
-        Estimate e = estimate(v, *p, d, Ho, Wo);
+        Estimate e = p->kind == FCM_KIND_PWDW ? estimate_pwdw(v, *p, d, Ho, Wo)
+                                              : estimate(v, *p, d, Ho, Wo);
         if (e.wgs_per_cu <= 0) {
             if (forced >= 0) why = "variant's LDS or registers exceed the device budget";
             continue;
@@ -556,6 +712,30 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     pl.grid = be.grid;
     pl.lds_bytes = variant_lds_bytes(v);
     const int e = elem_bytes(p->dtype);
+    if (p->kind == FCM_KIND_PWDW) {
+        // first layer: pointwise [K1][C] as is; second: depthwise [R*S][K1]
+        pl.w1_packed_bytes = (int64_t)p->K1 * p->C * e;
+        pl.w2_packed_bytes = (int64_t)p->R * p->S * p->K1 * e;
+        pl.workspace_bytes = (int64_t)p->N * p->H * p->W * p->K1 * e;
+        const int64_t x_bytes = (int64_t)p->N * p->H * p->W * p->C * e;
+        const int64_t y_bytes = (int64_t)p->N * Ho * Wo * p->K1 * e;
+        pl.alg_bytes_fused = x_bytes + y_bytes + pl.w1_packed_bytes + pl.w2_packed_bytes +
+                             (int64_t)4 * 2 * (p->K1 + p->K1);
+        pl.alg_bytes_unfused = pl.alg_bytes_fused + 2 * pl.workspace_bytes;
+        pl.pred_bytes_fused = be.pred;
+        int64_t pu = 0;
+        double gu = 0;
+        estimate_unfused_pwdw(*p, Ho, Wo, &pu, &gu);
+        pl.pred_bytes_unfused = pu;
+        pl.gma_paper_fused = be.gma;
+        pl.gma_paper_unfused = gu;
+        pl.fuse = (be.gma < gu) ? 1 : 0;
+        pl.pred_us_fused = be.t_us;
+        pl.flops = 2.0 * p->N * p->H * p->W * p->C * p->K1 +
+                   2.0 * p->N * Ho * Wo * p->K1 * p->R * p->S;
+        *out = pl;
+        return FCM_OK;
+    }
     const int n1 = p->kind == FCM_KIND_B2B ? p->K1 : p->C;
     pl.w1_packed_bytes =
         (int64_t)(p->kind == FCM_KIND_B2B ? (int64_t)p->K1 * p->R * p->S * p->C

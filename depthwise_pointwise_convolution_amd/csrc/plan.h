@@ -15,7 +15,8 @@ enum VKind {
     VK_B2B = 2,
     VK_DWPW_MM = 3,
     VK_B2B_MM = 5,
-    VK_DWPW_MMW = 6
+    VK_DWPW_MMW = 6,
+    VK_PWDW_MM = 7
 };
 
 struct VariantDesc {
@@ -32,6 +33,7 @@ struct VariantDesc {
     int occ;     // waves per SIMD the kernel is compiled to allow (register budget)
     int waves;   // waves per workgroup
     int cmax;    // largest C the variant takes (0: no limit)
+    int bpw;     // PW->DW: 16-channel blocks per wave (0 otherwise)
 };
 
 extern const VariantDesc kVariants[];

@@ -9,14 +9,16 @@ from typing import Optional
 import torch
 
 from . import (fcm_b2b_conv_fwd, fcm_conv_fwd, fcm_dw_fwd, fcm_dwpw_fwd, fcm_pack_weights,
-               fcm_plan, fcm_plan_variant, fcm_pw_fwd, fcm_tune, problem, FCM_KIND_B2B)
+               fcm_plan, fcm_plan_variant, fcm_pw_fwd, fcm_pwdw_fwd, fcm_tune, problem,
+               FCM_KIND_B2B, FCM_KIND_PWDW)
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
 class FcmModule:
-    """w1: depthwise [C,3,3] or standard [K1,C,3,3]; w2: [K,C] or [K,K1] (torch, on
-    the GPU, storage dtype); scale/bias: float32 per-channel tensors or None."""
+    """w1: depthwise [C,3,3], standard [K1,C,3,3] or (PW->DW) pointwise [K1,C]; w2:
+    [K,C], [K,K1] or (PW->DW) depthwise [K1,3,3] (torch, on the GPU, storage dtype);
+    scale/bias: float32 per-channel tensors or None."""
 
     def __init__(self, kind: str, dtype: str, N: int, H: int, W: int, C: int, K: int,
                  K1: Optional[int], stride: int, pad: int, act1: str, act2: str, w1, w2,
@@ -38,13 +40,16 @@ class FcmModule:
         self.out_shape = (N, self.plan.Ho, self.plan.Wo, K)
         self.t_shape = (N, self.plan.Ho, self.plan.Wo, C if K1 is None else K1)
         self.b2b = self.prob.kind == FCM_KIND_B2B
+        self.pwdw = self.prob.kind == FCM_KIND_PWDW
+        if self.pwdw:  # the intermediate is the pointwise layer's output
+            self.t_shape = (N, H, W, K1)
 
     def new_output(self, device) -> torch.Tensor:
         return torch.empty(self.out_shape, dtype=self.tdtype, device=device)
 
     def fused(self, x, y=None, stream=None) -> torch.Tensor:
         y = self.new_output(x.device) if y is None else y
-        fn = fcm_b2b_conv_fwd if self.b2b else fcm_dwpw_fwd
+        fn = fcm_b2b_conv_fwd if self.b2b else fcm_pwdw_fwd if self.pwdw else fcm_dwpw_fwd
         fn(self.plan, x, self.w1p, self.s1, self.b1, self.w2p, self.s2, self.b2, y, stream)
         return y
 
@@ -60,12 +65,18 @@ class FcmModule:
 
     def first_layer(self, x, t=None, stream=None) -> torch.Tensor:
         t = torch.empty(self.t_shape, dtype=self.tdtype, device=x.device) if t is None else t
+        if self.pwdw:
+            fcm_pw_fwd(self.plan, x, self.w1p, self.s1, self.b1, t, stream)
+            return t
         fn = fcm_conv_fwd if self.b2b else fcm_dw_fwd
         fn(self.plan, x, self.w1p, self.s1, self.b1, t, stream)
         return t
 
     def second_layer(self, t, y=None, stream=None) -> torch.Tensor:
         y = self.new_output(t.device) if y is None else y
+        if self.pwdw:
+            fcm_dw_fwd(self.plan, t, self.w2p, self.s2, self.b2, y, stream)
+            return y
         fcm_pw_fwd(self.plan, t, self.w2p, self.s2, self.b2, y, stream)
         return y
 

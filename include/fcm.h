@@ -9,8 +9,13 @@
  * pair of a standard 3x3 convolution followed by a 1x1 convolution ("Fusing two
  * back-to-back convolutions", the CONV1/CONV2 example); the second convolution must
  * be 1x1 so that every workgroup's input to it is produced by that workgroup alone
- * (same discussion).  Each convolution is followed by a per-channel scale, bias and
- * ReLU/ReLU6 epilogue (conv -> normalisation -> activation, FCM paper Sec. III-A).
+ * (same discussion).  The PW->DW module (the PWDW / PWDW_R fusion case, FCM paper
+ * Sec. II-D, Fig. 3(b), and Sec. III) runs the other order: a pointwise layer expands
+ * the channels and a depthwise 3x3 layer filters its output, the intermediate again
+ * kept on chip; a tile of outputs recomputes the intermediate over its whole input
+ * window, the overlap with neighbouring tiles included.  Each convolution is followed
+ * by a per-channel scale, bias and ReLU/ReLU6 epilogue (conv -> normalisation ->
+ * activation, FCM paper Sec. III-A).
  * Unfused layer-by-layer entry points, with the same stage code, serve as the
  * baseline the FCM paper compares against (Sec. V-C) and as the fallback when a plan
  * says not to fuse (Sec. IV).
@@ -61,7 +66,8 @@ typedef enum { FCM_ACT_NONE = 0, FCM_ACT_RELU = 1, FCM_ACT_RELU6 = 2 } fcm_act;
 
 typedef enum {
     FCM_KIND_DWPW = 0, /* depthwise RxS conv (C -> C) then pointwise 1x1 (C -> K) */
-    FCM_KIND_B2B = 1   /* standard RxS conv (C -> K1) then 1x1 conv (K1 -> K) */
+    FCM_KIND_B2B = 1,  /* standard RxS conv (C -> K1) then 1x1 conv (K1 -> K) */
+    FCM_KIND_PWDW = 2  /* pointwise 1x1 (C -> K1) then depthwise RxS conv (K1 -> K1) */
 } fcm_kind;
 
 /* The problem, in the pages' terms: NHWC input feature maps, per-channel depthwise
@@ -72,10 +78,12 @@ typedef struct {
     int32_t dtype;    /* fcm_dtype of activations and weights */
     int32_t N, H, W;  /* input batch and spatial extent */
     int32_t C;        /* input channels */
-    int32_t K1;       /* B2B: output channels of the first conv.  DWPW: must equal C */
-    int32_t K;        /* output channels of the final 1x1 conv */
-    int32_t R, S;     /* first conv's filter height/width (only 3x3 has kernels) */
-    int32_t stride_h, stride_w, pad_h, pad_w; /* first conv; the 1x1 is stride 1 */
+    int32_t K1;       /* B2B: output channels of the first conv.  DWPW: must equal C.
+                         PWDW: output channels of the pointwise layer */
+    int32_t K;        /* output channels of the module (PWDW: must equal K1) */
+    int32_t R, S;     /* the RxS conv's filter height/width (only 3x3 has kernels) */
+    int32_t stride_h, stride_w, pad_h, pad_w; /* of the RxS conv (the first layer for
+                         DWPW and B2B, the second for PWDW); the 1x1 is stride 1 */
     int32_t act1, act2; /* fcm_act after the first / second conv */
 } fcm_problem;
 
@@ -141,9 +149,9 @@ fcm_status fcm_query_device_spec(int device, fcm_device_spec* out);
  * with the pages' rule (fewer estimated global memory accesses) whether fusing
  * beats the layer-by-layer kernels.  spec == NULL uses the MI355X defaults.
  * Host only; makes no HIP call.  Errors: INVALID_ARG (null pointer, non-positive
- * size, K1 != C for DWPW, padding >= filter), UNSUPPORTED (filter not 3x3, stride
- * not 1 or 2, padding not 0 or 1, a channel count not a multiple of 8, or no variant
- * fits). */
+ * size, K1 != C for DWPW, K != K1 for PWDW, padding >= filter), UNSUPPORTED (filter not
+ * 3x3, stride not 1 or 2, padding not 0 or 1, a channel count not a multiple of 8, fp32
+ * storage for B2B or PWDW, or no variant fits). */
 fcm_status fcm_plan(const fcm_problem* prob, const fcm_device_spec* spec, fcm_plan_t* out);
 
 /* Same, but with the fused kernel variant forced (for tests and on-device tuning).
@@ -156,7 +164,8 @@ fcm_status fcm_plan_variant(const fcm_problem* prob, const fcm_device_spec* spec
  * Runs every fused variant able to take `prob`, at persistent grids of 1, 2, 3 and 4
  * workgroups per CU (as far as its occupancy allows), `iters` times each on `stream`,
  * rotating over `nsets` input/output pairs x[i], y[i] (laid out as for fcm_dwpw_fwd /
- * fcm_b2b_conv_fwd; several pairs whose total exceeds the 256 MB Infinity Cache make
+ * fcm_b2b_conv_fwd / fcm_pwdw_fwd, with w1, w2 the first and second layer's packed
+ * filters and scale1/bias1, scale2/bias2 their epilogues; several pairs whose total exceeds the 256 MB Infinity Cache make
  * the candidates stream from HBM as in a real network) with the shared filters and
  * epilogue arrays (weights packed by fcm_pack_weights); every y[i] is overwritten.
  * Writes the plan of the fastest to *out, with out->grid the chosen grid and
@@ -188,6 +197,8 @@ const char* fcm_variant_name(int32_t variant);
  *                                            rounded up to 16, C to 64, zero filled)
  *         w2_src 1x1       [K][K1]        -> w2_dst [K][K1], and for fp16/bf16 followed by
  *                                            32x32 blocks as for DWPW
+ *   PWDW: w1_src pointwise [K1][C]        -> w1_dst [K1][C]       (copied as is)
+ *         w2_src depthwise [K1][R][S]     -> w2_dst [R*S][K1]     (channel fastest)
  * Sizes in bytes are plan->w1_packed_bytes / w2_packed_bytes.  Either pair may be
  * NULL to skip it.  Source and destination must not overlap. */
 fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1_dst,
@@ -212,13 +223,27 @@ fcm_status fcm_b2b_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w
                             const float* scale2, const float* bias2, void* y,
                             void* stream);
 
+/* Fused PW -> DW module (FCM PWDW_R; PWDW when one tile covers the plane).
+ * x: [N][H][W][C]; w_pw: packed [K1][C]; scale1/bias1: [K1] or NULL (epilogue of the
+ * pointwise layer); w_dw: packed [R*S][K1]; scale2/bias2: [K1] or NULL (epilogue of the
+ * depthwise layer); y: [N][Ho][Wo][K1].  The depthwise layer's zero padding surrounds
+ * the intermediate.  plan->prob.kind must be FCM_KIND_PWDW. */
+fcm_status fcm_pwdw_fwd(const fcm_plan_t* plan, const void* x, const void* w_pw,
+                        const float* scale1, const float* bias1, const void* w_dw,
+                        const float* scale2, const float* bias2, void* y, void* stream);
+
 /* Layer-by-layer baseline, first layer of a DWPW plan: depthwise conv + epilogue 1,
- * writing the intermediate t: [N][Ho][Wo][C] (plan->workspace_bytes bytes). */
+ * writing the intermediate t: [N][Ho][Wo][C] (plan->workspace_bytes bytes).
+ * For a PWDW plan: the second layer, depthwise conv + epilogue (scale/bias [K1]) over
+ * the intermediate x = t: [N][H][W][K1], writing y: [N][Ho][Wo][K1]. */
 fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
                       const float* scale1, const float* bias1, void* t, void* stream);
 
 /* Layer-by-layer baseline, second layer of a DWPW or B2B plan: 1x1 conv + epilogue 2
- * reading the intermediate t: [N][Ho][Wo][C or K1], writing y: [N][Ho][Wo][K]. */
+ * reading the intermediate t: [N][Ho][Wo][C or K1], writing y: [N][Ho][Wo][K].
+ * For a PWDW plan: the first layer, 1x1 conv + epilogue (scale/bias [K1]) over the
+ * input t = x: [N][H][W][C] with the packed [K1][C] filters, writing the intermediate
+ * y: [N][H][W][K1] (plan->workspace_bytes bytes). */
 fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
                       const float* scale2, const float* bias2, void* y, void* stream);
 

@@ -32,12 +32,12 @@ def oracle_kwargs(wl, inp) -> dict:
 
 
 def oracle_full(wl, inp) -> np.ndarray:
-    fn = oracle.dwpw if wl.kind == "dwpw" else oracle.b2b
+    fn = {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw}[wl.kind]
     return fn(inp["x"], inp["w1"], inp["w2"], **oracle_kwargs(wl, inp))
 
 
 def oracle_rows(wl, inp, pix) -> np.ndarray:
-    fn = oracle.dwpw_at if wl.kind == "dwpw" else oracle.b2b_at
+    fn = {"dwpw": oracle.dwpw_at, "b2b": oracle.b2b_at, "pwdw": oracle.pwdw_at}[wl.kind]
     return fn(inp["x"], inp["w1"], inp["w2"], pix, **oracle_kwargs(wl, inp))
 
 
@@ -64,6 +64,8 @@ def int_inputs(wl, seed: int) -> dict:
     bit whatever its summation order."""
     rng = np.random.default_rng(seed)
     x = rng.integers(-2, 3, size=(wl.N, wl.H, wl.W, wl.C)).astype(np.float64)
+    if wl.kind == "pwdw":
+        return _int_inputs_pwdw(wl, rng, x)
     n1 = wl.C if wl.kind == "dwpw" else wl.K1
     if wl.kind == "dwpw":
         w1 = rng.integers(-1, 2, size=(wl.C, 3, 3)).astype(np.float64)
@@ -87,6 +89,26 @@ def int_inputs(wl, seed: int) -> dict:
     s2 = rng.choice([1.0, 2.0], size=wl.K) if wl.scale2 else None
     b2 = rng.integers(-2, 3, size=wl.K).astype(np.float64) if wl.bias2 else None
     return {"x": x, "w1": w1, "w2": w2, "scale1": s1, "bias1": b1, "scale2": s2, "bias2": b2}
+
+
+def _int_inputs_pwdw(wl, rng, x) -> dict:
+    """PW->DW module: at most 6 non-zero pointwise filter taps of +-1 per expanded
+    channel (|intermediate| <= 2*(2*6)+2 = 26) and at most 4 non-zero depthwise taps
+    (|output| <= 2*(4*26)+2 = 210): every value an integer below 256."""
+    w1 = np.zeros((wl.K1, wl.C))
+    for k in range(wl.K1):
+        idx = rng.choice(wl.C, size=min(6, wl.C), replace=False)
+        w1[k, idx] = rng.choice([-1.0, 1.0], size=idx.size)
+    s1 = rng.choice([1.0, 2.0], size=wl.K1) if wl.scale1 else None
+    b1 = rng.integers(-2, 3, size=wl.K1).astype(np.float64) if wl.bias1 else None
+    w2 = np.zeros((wl.K1, 9))
+    for k in range(wl.K1):
+        idx = rng.choice(9, size=4, replace=False)
+        w2[k, idx] = rng.choice([-1.0, 1.0], size=4)
+    s2 = rng.choice([1.0, 2.0], size=wl.K1) if wl.scale2 else None
+    b2 = rng.integers(-2, 3, size=wl.K1).astype(np.float64) if wl.bias2 else None
+    return {"x": x, "w1": w1, "w2": w2.reshape(wl.K1, 3, 3), "scale1": s1, "bias1": b1,
+            "scale2": s2, "bias2": b2}
 
 
 def all_variants_for(wl):
@@ -113,6 +135,8 @@ REDUCED = {
     "down_f16_64x56x56_c256_k512_s2": dict(N=2, H=57, W=45),
     "late_f16_64x7x7_c1024": dict(N=3),
     "b2b_f16_32x56x56_c64": dict(N=2, H=23, W=37),
+    "pwdw_f16_32x56x56_c24_k144": dict(N=2, H=29, W=37),
+    "pwdw_f16_32x112x112_c16_k96_s2": dict(N=2, H=45, W=57),
 }
 
 

@@ -36,7 +36,7 @@ def header_functions():
 
 def test_header_declares_the_boundary_calls():
     names = header_functions()
-    for required in ("fcm_plan", "fcm_dwpw_fwd", "fcm_b2b_conv_fwd", "fcm_tune",
+    for required in ("fcm_plan", "fcm_dwpw_fwd", "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_tune",
                      "fcm_pack_weights", "fcm_dw_fwd", "fcm_pw_fwd", "fcm_conv_fwd"):
         assert required in names
 
@@ -90,7 +90,9 @@ def test_plan_integers_match_oracle_accounting(name):
     assert pl.alg_bytes_unfused == acct.alg_bytes(full, fused=False)
     n1 = wl.C if wl.kind == "dwpw" else wl.K1
     e = acct.ELEM_BYTES[wl.dtype]
-    assert pl.workspace_bytes == wl.N * wl.Ho * wl.Wo * n1 * e
+    assert pl.workspace_bytes == acct.sizes(wl)["t"]
+    if wl.kind != "pwdw":
+        assert pl.workspace_bytes == wl.N * wl.Ho * wl.Wo * n1 * e
     assert pl.flops == acct.flops(wl)
     # tiling and launch shape are self-consistent
     name_v = F.fcm_variant_name(pl.variant)
@@ -182,6 +184,52 @@ def test_invalid_problems_are_rejected_on_the_host(change, status):
     assert ei.value.status == getattr(F, "FCM_ERR_" + status), ei.value
 
 
+def test_pwdw_problems_are_checked_on_the_host():
+    F = _lib()
+    # the depthwise layer keeps the pointwise layer's channel count
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_plan(F.problem("pwdw", "f16", 2, 16, 16, 24, 96, 144), _spec(F))
+    assert ei.value.status == F.FCM_ERR_INVALID_ARG
+    # 16-bit storage only
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_plan(F.problem("pwdw", "f32", 2, 16, 16, 24, 144, 144), _spec(F))
+    assert ei.value.status == F.FCM_ERR_UNSUPPORTED
+    # more input channels than any PW->DW variant stages
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_plan(F.problem("pwdw", "f16", 2, 16, 16, 128, 144, 144), _spec(F))
+    assert ei.value.status == F.FCM_ERR_UNSUPPORTED
+    # a DWPW plan cannot run the PW->DW entry point, nor the reverse
+    import ctypes
+    L = F.lib()
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake, fake, None, None, fake, None, None, fake, None]
+    dw = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["mbv1_f16_8x112x112_c64_k128"]), _spec(F))
+    pd = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["pwdw_f16_32x56x56_c24_k144"]), _spec(F))
+    assert L.fcm_pwdw_fwd(ctypes.byref(dw), *args) == F.FCM_ERR_INVALID_ARG
+    assert L.fcm_dwpw_fwd(ctypes.byref(pd), *args) == F.FCM_ERR_INVALID_ARG
+    assert L.fcm_conv_fwd(ctypes.byref(pd), fake, fake, None, None, fake, None) == \
+        F.FCM_ERR_INVALID_ARG
+
+
+def test_pwdw_plan_counts_the_recomputed_windows():
+    # the planner's bytes requested from the memory hierarchy include every tile's whole
+    # input window (clipped), the oracle's redundancy accounting in bytes
+    F = _lib()
+    wl = fcm_inputs.WORKLOADS["pwdw_f16_32x56x56_c24_k144"]
+    pl = F.fcm_plan(_problem(F, wl), _spec(F))
+    red = acct.pwdw_redundancy(wl.H, wl.W, pl.tile_h, pl.tile_w, wl.stride)
+    ktiles = math.ceil(wl.K1 / pl.k_tile)
+    x_reads = round((1 + red) * wl.N * wl.H * wl.W) * wl.C * 2 * ktiles
+    y = wl.N * wl.Ho * wl.Wo * wl.K1 * 2
+    rest = pl.pred_bytes_fused - x_reads - y
+    w_slice = min(pl.k_tile, wl.K1) * (wl.C + 9) * 2 + 16 * min(pl.k_tile, wl.K1)
+    assert rest == pl.grid * w_slice
+    # the paper-model estimate (Eq. 4 plus the output write) is finite and below the
+    # layer-by-layer one, which moves the intermediate twice
+    assert 0 < pl.gma_paper_fused < pl.gma_paper_unfused
+    assert pl.fuse == 1
+
+
 def test_b2b_needs_16bit_storage_and_small_filters():
     F = _lib()
     prob = F.problem("b2b", "f32", 1, 16, 16, 64, 64, 64, stride=1, pad=1)
@@ -243,7 +291,9 @@ def test_forced_variants_cover_every_compiled_kernel():
         for dt in ("f16", "bf16", "f32") for c, k in ((64, 128), (128, 128), (64, 64))
         for s in (1, 2)] + [
         fcm_inputs.Workload("b", "b2b", dt, N=2, H=17, W=23, C=64, K=64, K1=k1, stride=s)
-        for dt in ("f16", "bf16") for k1 in (32, 64, 128) for s in (1, 2)]
+        for dt in ("f16", "bf16") for k1 in (32, 64, 128) for s in (1, 2)] + [
+        fcm_inputs.Workload("p", "pwdw", dt, N=2, H=17, W=23, C=c, K=k1, K1=k1, stride=s)
+        for dt in ("f16", "bf16") for c in (24, 64) for k1 in (96, 144) for s in (1, 2)]
     for wl in shapes:
         prob = _problem(F, wl)
         for v in range(F.fcm_num_variants()):

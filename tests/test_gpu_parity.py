@@ -79,6 +79,12 @@ CASES_INT = [
     ("b2b", "f16", 2, 9, 19, 64, 64, 64, 1, 1, "relu", "relu", True),
     ("b2b", "bf16", 1, 10, 9, 32, 48, 32, 1, 0, "none", "relu", True),
     ("b2b", "f16", 1, 11, 12, 40, 24, 96, 2, 1, "relu6", "none", True),
+    ("pwdw", "f16", 2, 9, 21, 24, 144, 144, 1, 1, "relu6", "relu6", True),
+    ("pwdw", "bf16", 1, 11, 17, 64, 48, 48, 1, 1, "none", "relu", False),
+    ("pwdw", "f16", 2, 13, 15, 16, 96, 96, 2, 1, "relu", "relu6", True),
+    ("pwdw", "bf16", 1, 10, 9, 40, 40, 40, 2, 0, "relu6", "none", True),
+    ("pwdw", "f16", 1, 3, 2, 8, 24, 24, 1, 1, "none", "none", True),
+    ("pwdw", "f16", 2, 17, 33, 32, 200, 200, 1, 1, "none", "relu", True),
 ]
 
 
@@ -162,6 +168,54 @@ def test_random_small_shapes(wl):
         assert err <= TOL[wl.dtype], (path, err)
 
 
+def _random_pwdw_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        C = int(rng.choice([8, 16, 24, 32, 40, 64]))
+        K1 = int(rng.choice([8, 16, 24, 48, 96, 136, 144]))
+        out.append(fcm_inputs.Workload(
+            f"pd{i}", "pwdw", str(rng.choice(["f16", "bf16"])), N=int(rng.integers(1, 3)),
+            H=int(rng.integers(1, 24)), W=int(rng.integers(1, 40)), C=C, K=K1, K1=K1,
+            stride=int(rng.integers(1, 3)), pad=int(rng.integers(0, 2)),
+            act1=str(rng.choice(["none", "relu", "relu6"])),
+            act2=str(rng.choice(["none", "relu", "relu6"])), scale1=bool(rng.random() < .5),
+            bias1=bool(rng.random() < .5), scale2=bool(rng.random() < .5),
+            bias2=bool(rng.random() < .5), seed=int(rng.integers(1 << 30))))
+    return [w for w in out if w.H + 2 * w.pad >= 3 and w.W + 2 * w.pad >= 3]
+
+
+@pytest.mark.parametrize("wl", _random_pwdw_cases(16, 8), ids=lambda w: w.name)
+def test_random_small_shapes_pwdw(wl):
+    inp = fcm_inputs.make_inputs(wl)
+    ref = oracle_full(wl, inp)
+    for path in ("fused", "unfused"):
+        _log(f"case {wl} {path}")
+        got, _ = run_gpu(wl, inp, path=path)
+        err = rel_err(got, ref)
+        assert err <= TOL[wl.dtype], (path, err)
+
+
+def test_pwdw_output_guard_bands_and_every_output_written():
+    import torch
+    from depthwise_pointwise_convolution_amd.module import from_workload
+    wl = reduced("pwdw_f16_32x56x56_c24_k144")
+    inp = fcm_inputs.make_inputs(wl)
+    x = torch.from_numpy(inp["x"]).half().cuda()
+    for v in all_variants_for(wl):
+        _log(f"case pwdw guard bands variant {v}")
+        mod = from_workload(wl, inp, variant=v)
+        n = int(np.prod(mod.out_shape))
+        guard = 4096
+        buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
+        y = buf[guard:guard + n].view(mod.out_shape)
+        mod.fused(x, y)
+        torch.cuda.synchronize()
+        b = buf.cpu()
+        assert torch.isnan(b[:guard]).all() and torch.isnan(b[guard + n:]).all()
+        assert not torch.isnan(b[guard:guard + n]).any()
+
+
 def test_output_guard_bands_and_every_output_written():
     import torch
     from depthwise_pointwise_convolution_amd.module import from_workload
@@ -213,9 +267,10 @@ def test_device_argument_errors_enqueue_nothing():
 @pytest.mark.parametrize("H,W,stride,pad", [(1, 1, 1, 1), (2, 3, 2, 1), (3, 3, 1, 0),
                                              (5, 2, 2, 0), (1, 40, 1, 1)])
 def test_degenerate_extents(H, W, stride, pad):
-    for dtype in ("f16", "f32"):
-        wl = fcm_inputs.Workload("deg", "dwpw", dtype, N=1, H=H, W=W, C=8, K=8, K1=8,
-                                 stride=stride, pad=pad, bias2=True, seed=H * 7 + W)
+    for kind, dtype in (("dwpw", "f16"), ("dwpw", "f32"), ("pwdw", "f16")):
+        wl = fcm_inputs.Workload("deg", kind, dtype, N=1, H=H, W=W, C=8, K=8, K1=8,
+                                 stride=stride, pad=pad, bias1=kind == "pwdw", bias2=True,
+                                 act1="relu" if kind == "pwdw" else "none", seed=H * 7 + W)
         if H + 2 * pad < 3 or W + 2 * pad < 3:
             continue
         inp = fcm_inputs.make_inputs(wl)
