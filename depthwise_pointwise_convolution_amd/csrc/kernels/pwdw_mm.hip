@@ -278,7 +278,8 @@ void pwdw_mm_kernel(KArgs a) {
     const uint32_t rd_q = (uint32_t)(hh * TROW + (ch * IW + lr * S + 2) * 16);
     const uint32_t rd_qc = (uint32_t)((ch * IW + lr * S + 2) * 16);
     // output store offset of the lane's 4 channels within a pixel row of the tile
-    // (the channel block and row enter per store)
+    // (the channel block and row enter per store; K1 is a multiple of 8, so the 4
+    // channels of a lane exist all or none)
     const uint32_t st_lane = (uint32_t)(lr * a.K1 + 4 * lg) * (uint32_t)es;
 
     // which window rows a dw = 2 pair reads
@@ -299,64 +300,100 @@ void pwdw_mm_kernel(KArgs a) {
             valid |= ok ? (1u << pb) : 0u;
         }
         const char* xb = reinterpret_cast<const char*>(src);
-        // pointwise layer over the window
-#pragma unroll
-        for (int pb = 0; pb < NPB; ++pb) {
-            u32x4 bx[NKC];
+        // The reads of each phase run ahead of their products: the pointwise layer
+        // requests window block pb + PDX while it multiplies block pb, the depthwise
+        // layer requests input row ir + PDR while it multiplies row ir.  Scheduling
+        // barriers fence every step, so the compiler cannot sink a read next to its use
+        // (it otherwise pays the LDS latency once per read, with few waves to hide it).
+        constexpr int PDX = NPB < 2 ? NPB : 2;
+        constexpr int PDR = IHW < 2 ? IHW : 2;
+        u32x4 bx[NPB][NKC];
+        auto read_x = [&](int pb) __attribute__((always_inline)) {
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
-                bx[kc] = *reinterpret_cast<const u32x4*>(xb + pb * 16 * NCH * 16 + xo[kc]);
+                bx[pb][kc] = *reinterpret_cast<const u32x4*>(xb + pb * 16 * NCH * 16 + xo[kc]);
+        };
+        // pointwise layer over the window
+#pragma unroll
+        for (int pb = 0; pb < PDX; ++pb) read_x(pb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) {
+            if (pb + PDX < NPB) read_x(pb + PDX);
+            // the activation's clamp, narrowed to [0, 0] for pixels outside the image:
+            // their intermediate is the depthwise layer's zero padding
             const bool ok = (valid >> pb) & 1u;
+            const float lo = ok ? act1.lo : 0.0f, hi = ok ? act1.hi : 0.0f;
 #pragma unroll
             for (int j = 0; j < BPW; ++j) {
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kc = 0; kc < NKC; ++kc) acc = mfma<T>(apw[j][kc], bx[kc], acc);
+                for (int kc = 0; kc < NKC; ++kc) acc = mfma<T>(apw[j][kc], bx[pb][kc], acc);
                 float o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    o[i] = ok ? epilogue(acc[i], s1r[j][i], b1r[j][i], act1) : 0.0f;
+                    o[i] = __builtin_amdgcn_fmed3f(__builtin_fmaf(acc[i], s1r[j][i], b1r[j][i]),
+                                                   lo, hi);
                 *reinterpret_cast<uint2*>(tbase + j * TREG + two[pb]) = pack8<T>(o);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // depthwise layer, block by block
-        const uint32_t voff_col = t.ow0 + lr < a.Wo ? st_lane : mm::kOob;
+        // depthwise layer, block by block.  Store offsets: a per-lane part (column and
+        // channels within the tile row; kLaneOob when the lane's pixel or channels do not
+        // exist) plus a wave-uniform row part (kRowOob past the last output row).  Any
+        // sum with an out-of-range part is at least 1 GiB, past the output tensor (the
+        // planner keeps it below 1 GiB), so the store is dropped; keeping the lane
+        // condition out of the row term leaves the compiler no divergent branch around
+        // a store, which would confuse its own count of the memory operations in flight.
+        constexpr uint32_t kLaneOob = 0x40000000u, kRowOob = 0x80000000u;
+        const bool col_ok = t.ow0 + lr < a.Wo;
+        uint32_t stv[BPW];
+#pragma unroll
+        for (int j = 0; j < BPW; ++j)
+            stv[j] = (col_ok && (cb0 + j) * 16 + 4 * lg < a.K1)
+                         ? st_lane + (uint32_t)((cb0 + j) * 16 * es)
+                         : kLaneOob;
+        u32x4 bp[BPW][IHW], bq[BPW][IHW];
+        auto read_row = [&](int j, int ir) __attribute__((always_inline)) {
+            const char* tb = tbase + j * TREG;
+            bp[j][ir] = *reinterpret_cast<const u32x4*>(tb + ir * TROW + rd_p);
+            if (q_used(ir))
+                bq[j][ir] = *reinterpret_cast<const u32x4*>(tb + ir * TROW +
+                                                            (ir + 1 < IHW ? rd_q : rd_qc));
+        };
+#pragma unroll
+        for (int ir = 0; ir < PDR; ++ir) read_row(0, ir);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
-            const char* tb = tbase + j * TREG;
             f32x4 d[TH];
 #pragma unroll
             for (int r = 0; r < TH; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ir = 0; ir < IHW; ++ir) {
-                const u32x4 bp = *reinterpret_cast<const u32x4*>(tb + ir * TROW + rd_p);
-                u32x4 bq = bp;
-                if (q_used(ir))
-                    bq = *reinterpret_cast<const u32x4*>(tb + ir * TROW +
-                                                         (ir + 1 < IHW ? rd_q : rd_qc));
+                // the next rows' reads (the next block's first rows near the end)
+                if (ir + PDR < IHW) read_row(j, ir + PDR);
+                else if (j + 1 < BPW) read_row(j + 1, ir + PDR - IHW);
 #pragma unroll
                 for (int dh = 0; dh < 3; ++dh)
                     if (ir >= dh && (ir - dh) % S == 0 && (ir - dh) / S < TH)
-                        d[(ir - dh) / S] = mfma<T>(adw[j][dh], bp, d[(ir - dh) / S]);
-                if (ir % S == 0 && ir / S < TH) d[ir / S] = mfma<T>(adw[j][3], bq, d[ir / S]);
+                        d[(ir - dh) / S] = mfma<T>(adw[j][dh], bp[j][ir], d[(ir - dh) / S]);
+                if (ir % S == 0 && ir / S < TH)
+                    d[ir / S] = mfma<T>(adw[j][3], bq[j][ir], d[ir / S]);
                 if (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < TH)
-                    d[(ir - 2) / S] = mfma<T>(adw[j][4], bq, d[(ir - 2) / S]);
+                    d[(ir - 2) / S] = mfma<T>(adw[j][4], bq[j][ir], d[(ir - 2) / S]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // this lane's 4 channels exist (K1 is a multiple of 8, so a group of 4 is
-            // all in or all out)
-            const bool ch_ok = (cb0 + j) * 16 + 4 * lg < a.K1;
 #pragma unroll
             for (int r = 0; r < TH; ++r) {
                 float o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] = epilogue(d[r][i], s2r[j][i], b2r[j][i], act2);
-                const bool row_ok = ch_ok && t.oh0 + r < a.Ho && voff_col != mm::kOob;
-                const uint32_t v =
-                    row_ok ? (uint32_t)(t.out_base + r * out_row + (cb0 + j) * 16 * es) + voff_col
-                           : mm::kOob;
+                const uint32_t row = t.oh0 + r < a.Ho ? (uint32_t)(t.out_base + r * out_row)
+                                                      : kRowOob;
                 // the whole offset in the vector operand, scalar offset 0
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack8<T>(o)), ry, v,
-                                                      0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack8<T>(o)), ry,
+                                                      stv[j] + row, 0, 0);
             }
         }
     };

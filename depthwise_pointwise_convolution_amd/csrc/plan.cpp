@@ -291,8 +291,8 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
         const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
         if ((int64_t)p.N * p.H * p.W * p.C * 2 >= ((int64_t)1 << 31) ||
-            (int64_t)p.N * Ho * Wo * p.K1 * 2 >= ((int64_t)1 << 31)) {
-            if (why) *why = "PW->DW variant addresses whole tensors below 2 GiB";
+            (int64_t)p.N * Ho * Wo * p.K1 * 2 >= ((int64_t)1 << 30)) {
+            if (why) *why = "PW->DW variant addresses inputs below 2 GiB and outputs below 1 GiB";
             return false;
         }
         return true;
