@@ -25,14 +25,14 @@ from typing import Optional
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
 
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
     kind: str            # "dwpw", "b2b" or "pwdw"
-    dtype: str           # "f32" | "f16" | "bf16"
+    dtype: str           # "f32" | "f16" | "bf16" | "i8"
     N: int
     H: int
     W: int
@@ -106,6 +106,13 @@ WORKLOADS = {
         w_dist=("normal", 0.0, 0.05), seed=5,
         description="Back-to-back: conv 3x3 p1 64->64 + scale_bias_relu, conv 1x1 "
                     "64->64 + scale_bias_relu, fp16, N=32 56x56"),
+    "mbv1i8_i8_8x112x112_c32_k64": Workload(
+        "mbv1i8_i8_8x112x112_c32_k64", "dwpw", "i8", N=8, H=112, W=112, C=32, K=64, K1=32,
+        act1="relu", act2="relu", scale1=True, bias1=True, scale2=True, bias2=True,
+        x_dist=("int", -64, 63), w_dist=("int", -127, 127),
+        scale_dist=("uniform", 0.002, 0.006), bias_dist=("normal", 0.0, 8.0), seed=8,
+        description="INT8 DWPW (MobileNetV1 layers 2-3): DW 3x3 s1 C=32 + requantize+ReLU, "
+                    "PW 32->64 + requantize+ReLU, int8 with int32 sums, N=8 112x112"),
     "pwdw_f16_32x56x56_c24_k144": Workload(
         "pwdw_f16_32x56x56_c24_k144", "pwdw", "f16", N=32, H=56, W=56, C=24, K=144, K1=144,
         act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
@@ -139,7 +146,10 @@ def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
 
 
 def _narrow(a: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 -> float32 -> storage type (torch RNE casts); returned as float64."""
+    """float64 -> float32 -> storage type (torch RNE casts); returned as float64.  int8:
+    the nearest integer, saturated."""
+    if dtype == "i8":
+        return np.clip(np.rint(a), -128, 127).astype(np.float64)
     import torch
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
@@ -186,7 +196,8 @@ def to_torch(a: Optional[np.ndarray], dtype: str, device=None):
     if a is None:
         return None
     import torch
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "i8": torch.int8}[dtype]
     t = torch.from_numpy(np.ascontiguousarray(a)).to(tdt)
     return t.to(device) if device is not None else t
 

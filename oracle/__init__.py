@@ -19,6 +19,10 @@ the storage type):
 * ``w2``     [K, K1]              second (1x1) conv of the pair
 * PW->DW module: ``w_pw`` [K1, C] then ``w_dw`` [K1, R, S]; output channels K1
 * ``scale*``/``bias*`` per channel, or ``None`` (identity)
+
+``dtype="i8"`` is the INT8 module: integer operands, exact sums, and at each storage
+point the binary32 requantization fmaf(scale, acc, bias) -> activation clamp -> nearest
+integer (ties to even) -> saturation to [-128, 127] (see fcm_oracle.c).
 """
 from __future__ import annotations
 
@@ -33,7 +37,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "fcm_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
 ACTS = {"none": 0, "relu": 1, "relu6": 2}
 
 _lock = threading.Lock()

@@ -30,7 +30,7 @@ from __future__ import annotations
 
 import math
 
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
 INF = float("inf")
 
 

@@ -35,7 +35,14 @@
  *   - zero padding; output size floor((H + 2p - R)/s) + 1;
  *   - epilogue y = act(scale[c]*acc + bias[c]); a NULL scale means 1, a NULL bias 0;
  *   - rounding to binary16 / bfloat16 / binary32 is IEEE round-to-nearest-even,
- *     implemented below from the format definitions (not with a library cast).
+ *     implemented below from the format definitions (not with a library cast);
+ *   - INT8 storage (FCM paper Sec. III-B: int8 operands, four-way int8 dot products
+ *     with 32-bit accumulation, results packed to 8 bits before they are written):
+ *     the sums are exact integers; the epilogue is evaluated in binary32 -- one fused
+ *     multiply-add v = fmaf(scale, acc, bias), the activation's clamp -- and v is
+ *     rounded to the nearest integer (ties to even) and saturated to [-128, 127].
+ *     Because a floating-point step decides an integer code here, the oracle takes it
+ *     in the same precision as the kernels (binary32 FMA, then round-to-nearest-even).
  *
  * Layouts (PyTorch's, independent of the GPU library's packed layouts):
  *   activations NHWC [N][H][W][C]; depthwise weights [C][R][S]; pointwise weights
@@ -64,6 +71,7 @@ int fcm_oracle_threads(void) {
 #define ORACLE_F32 0
 #define ORACLE_F16 1
 #define ORACLE_BF16 2
+#define ORACLE_I8 3
 
 #define ACT_NONE 0
 #define ACT_RELU 1
@@ -95,10 +103,19 @@ static double round_binary(double v, int mant, int emin, int emax) {
     return copysign(r, v);
 }
 
+/* Nearest int8 code: round to the nearest integer, ties to even, then saturate. */
+static double round_i8(double v) {
+    double r = rint(v); /* default rounding mode: to nearest, ties to even */
+    if (r < -128.0) r = -128.0;
+    if (r > 127.0) r = 127.0;
+    return r;
+}
+
 double fcm_oracle_round(double v, int dtype) {
     switch (dtype) {
     case ORACLE_F16: return round_binary(v, 10, -14, 15);
     case ORACLE_BF16: return round_binary(v, 7, -126, 127);
+    case ORACLE_I8: return round_i8(v);
     default: return round_binary(v, 23, -126, 127);
     }
 }
@@ -211,6 +228,33 @@ static void pw_row(const double* t, int C, const double* w, int K, double* y) {
     }
 }
 
+/* One pixel's C values leave a layer: normalisation + activation, then rounding to the
+ * storage type.  Floating-point storage: the epilogue in double precision, one rounding.
+ * INT8: the epilogue in binary32 (fmaf, clamp), then the nearest int8 code. */
+static void store_row(double* a, int C, const double* scale, const double* bias, int act,
+                      int dtype) {
+    if (dtype != ORACLE_I8) {
+        epilogue_row(a, C, scale, bias, act);
+        fcm_oracle_round_array(a, C, dtype);
+        return;
+    }
+    for (int c = 0; c < C; ++c) {
+        float acc = (float)a[c]; /* exact: |acc| < 2^24 for int8 operands */
+        float sc = scale ? (float)scale[c] : 1.0f;
+        float bi = bias ? (float)bias[c] : 0.0f;
+        float v = fmaf(sc, acc, bi);
+        if (act == ACT_RELU || act == ACT_RELU6) v = v > 0.0f ? v : 0.0f;
+        if (act == ACT_RELU6) v = v < 6.0f ? v : 6.0f;
+        a[c] = round_i8((double)v);
+    }
+}
+
+static void store_rows(double* a, int64_t M, int C, const double* scale, const double* bias,
+                       int act, int dtype) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) store_row(a + m * C, C, scale, bias, act, dtype);
+}
+
 /* Per-channel normalisation + activation in place over a [M][C] array. */
 void fcm_oracle_epilogue(double* a, int64_t M, int C, const double* scale,
                          const double* bias, int act) {
@@ -233,11 +277,9 @@ int fcm_oracle_dwpw(const double* x, int N, int H, int W, int C, const double* w
     double* t = t_out ? t_out : (double*)malloc(sizeof(double) * (size_t)(M * C));
     if (!t) return -1;
     fcm_oracle_dw(x, N, H, W, C, w_dw, R, S, sh, sw, ph, pw, t);
-    fcm_oracle_epilogue(t, M, C, scale1, bias1, act1);
-    fcm_oracle_round_array(t, M * C, dtype);
+    store_rows(t, M, C, scale1, bias1, act1, dtype);
     fcm_oracle_pw(t, M, C, w_pw, K, y);
-    fcm_oracle_epilogue(y, M, K, scale2, bias2, act2);
-    fcm_oracle_round_array(y, M * K, dtype);
+    store_rows(y, M, K, scale2, bias2, act2, dtype);
     if (!t_out) free(t);
     return 0;
 }
@@ -255,8 +297,7 @@ int fcm_oracle_b2b(const double* x, int N, int H, int W, int C, const double* w1
     fcm_oracle_epilogue(t, M, K1, scale1, bias1, act1);
     fcm_oracle_round_array(t, M * K1, dtype);
     fcm_oracle_pw(t, M, K1, w2, K, y);
-    fcm_oracle_epilogue(y, M, K, scale2, bias2, act2);
-    fcm_oracle_round_array(y, M * K, dtype);
+    store_rows(y, M, K, scale2, bias2, act2, dtype);
     if (!t_out) free(t);
     return 0;
 }
@@ -287,12 +328,10 @@ int fcm_oracle_dwpw_at(const double* x, int N, int H, int W, int C, const double
                 }
             t[c] = acc;
         }
-        epilogue_row(t, C, scale1, bias1, act1);
-        fcm_oracle_round_array(t, C, dtype);
+        store_row(t, C, scale1, bias1, act1, dtype);
         double* yr = y_rows + i * K;
         pw_row(t, C, w_pw, K, yr);
-        epilogue_row(yr, K, scale2, bias2, act2);
-        fcm_oracle_round_array(yr, K, dtype);
+        store_row(yr, K, scale2, bias2, act2, dtype);
         free(t);
     }
     return 0;
@@ -325,8 +364,7 @@ int fcm_oracle_b2b_at(const double* x, int N, int H, int W, int C, const double*
         fcm_oracle_round_array(t, K1, dtype);
         double* yr = y_rows + i * K;
         pw_row(t, K1, w2, K, yr);
-        epilogue_row(yr, K, scale2, bias2, act2);
-        fcm_oracle_round_array(yr, K, dtype);
+        store_row(yr, K, scale2, bias2, act2, dtype);
         free(t);
     }
     return 0;

@@ -301,6 +301,78 @@ def test_sampled_rows_equal_full_outputs():
 
 
 # ---------------------------------------------------------------------------------
+# INT8: exact integer sums, binary32 requantization
+# ---------------------------------------------------------------------------------
+def _requant_ref(acc, scale, bias, act):
+    """Integer sums (exact in float64) -> v = scale*acc + bias computed exactly in
+    float64 (dyadic scale and bias keep it exact), rounded once to binary32 (what one
+    fused multiply-add gives) -> clamp -> nearest integer with ties to even (numpy's
+    rint) -> saturate."""
+    v = (acc * scale + bias).astype(np.float32)
+    if act in ("relu", "relu6"):
+        v = np.maximum(v, np.float32(0))
+    if act == "relu6":
+        v = np.minimum(v, np.float32(6))
+    return np.clip(np.rint(v.astype(np.float64)), -128, 127)
+
+
+@pytest.mark.parametrize("stride,act1,act2", [(1, "relu", "relu"), (2, "none", "relu6"),
+                                              (1, "relu6", "none")])
+def test_i8_dwpw_is_the_integer_pipeline(stride, act1, act2):
+    rng = _rng(40 + stride)
+    N, H, W, C, K = 2, 9, 11, 16, 24
+    x = rng.integers(-128, 128, (N, H, W, C)).astype(np.float64)
+    wd = rng.integers(-127, 128, (C, 3, 3)).astype(np.float64)
+    wp = rng.integers(-127, 128, (K, C)).astype(np.float64)
+    # dyadic scales and biases: scale*acc + bias is exact in float64, so rounding it to
+    # binary32 once is exactly what a fused multiply-add in binary32 returns
+    s1 = rng.integers(1, 4096, C) / 2.0 ** 17
+    b1 = rng.integers(-64, 64, C) / 8.0
+    s2 = rng.integers(1, 4096, K) / 2.0 ** 19
+    b2 = rng.integers(-64, 64, K) / 8.0
+    y, t = oracle.dwpw(x, wd, wp, (stride, stride), (1, 1), s1, b1, act1, s2, b2, act2, "i8",
+                       return_t=True)
+    acc1 = _torch_dw(x, wd, stride, 1)
+    assert np.all(acc1 == np.rint(acc1)) and np.abs(acc1).max() < 2 ** 24
+    tr = _requant_ref(acc1, s1, b1, act1)
+    acc2 = _torch_conv(tr, wp[:, :, None, None], 1, 0)
+    yr = _requant_ref(acc2, s2, b2, act2)
+    assert np.array_equal(t, tr)
+    assert np.array_equal(y, yr)
+    # the codes really reach the int8 range's ends where the activation allows it
+    if act1 != "relu6":
+        assert t.max() == 127 or t.min() == -128
+
+
+def test_i8_rounding_ties_to_even_and_saturates():
+    # identity filters and scale 1/2: every intermediate is x/2 exactly, so odd inputs
+    # sit on a tie; scale 2 on the output saturates the large codes
+    x = np.arange(-127, 128, dtype=np.float64).reshape(1, 1, 255, 1)
+    wd = np.zeros((1, 3, 3))
+    wd[0, 1, 1] = 1
+    y1, t = oracle.dwpw(x, wd, np.eye(1), scale1=np.array([0.5]), dtype="i8", return_t=True)
+    half = x / 2
+    expect = np.where(np.abs(half - np.trunc(half)) == 0.5,
+                      2 * np.round(half / 2), np.round(half))   # ties to the even neighbour
+    assert np.array_equal(t, expect)
+    assert np.array_equal(t.ravel()[[0, 1, 2, 125, 126, 127, 128, 129]],
+                          [-64, -63, -62, -1, 0, 0, 0, 1])
+    y2 = oracle.dwpw(x, wd, np.eye(1), scale1=np.array([4.0]), dtype="i8")
+    assert y2.min() == -128 and y2.max() == 127
+    assert np.array_equal(y2.ravel(), np.clip(4 * x.ravel(), -128, 127))
+
+
+def test_i8_inputs_are_integer_codes():
+    wl = fcm_inputs.WORKLOADS["mbv1i8_i8_8x112x112_c32_k64"].replace(N=1, H=8, W=8)
+    inp = fcm_inputs.make_inputs(wl)
+    for k in ("x", "w1", "w2"):
+        a = inp[k]
+        assert np.all(a == np.rint(a)) and a.min() >= -128 and a.max() <= 127
+    assert accounting.alg_bytes(fcm_inputs.WORKLOADS["mbv1i8_i8_8x112x112_c32_k64"]) == (
+        8 * 112 * 112 * (32 + 64) + 9 * 32 + 64 * 32 + 4 * 2 * (32 + 64))
+
+
+# ---------------------------------------------------------------------------------
 # the pointwise -> depthwise module
 # ---------------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,stride,pad", [("f32", 1, 1), ("f16", 1, 1), ("bf16", 1, 1),
