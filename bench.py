@@ -36,7 +36,7 @@ COPY_STEPS = 5                   # copies a calibration run makes (--mode copy -
 PROFILES = os.path.join(ROOT, "profiles")
 KDIR = "depthwise_pointwise_convolution_amd/csrc/kernels/"
 # source file of each fused kernel family (by variant-name prefix) and the headers they share
-KERNEL_FILES = [("mmw_", "dwpw_mmw.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
+KERNEL_FILES = [("dwpw_i8_", "dwpw_i8.hip"), ("mmw_", "dwpw_mmw.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
                 ("dwpw_", "dwpw.hip"), ("b2b_", "b2b.hip"), ("pwdw_", "pwdw_mm.hip")]
 SHARED_SOURCES = ["mm_common.h", "stages.h", "common.h"]
 

@@ -27,12 +27,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfcm.so")
 
 FCM_OK, FCM_ERR_INVALID_ARG, FCM_ERR_UNSUPPORTED, FCM_ERR_HIP = 0, 1, 2, 3
-FCM_F32, FCM_F16, FCM_BF16 = 0, 1, 2
+FCM_F32, FCM_F16, FCM_BF16, FCM_I8 = 0, 1, 2, 3
 FCM_ACT_NONE, FCM_ACT_RELU, FCM_ACT_RELU6 = 0, 1, 2
 FCM_KIND_DWPW, FCM_KIND_B2B, FCM_KIND_PWDW = 0, 1, 2
 FCM_PLAN_VERSION = 2
 
-DTYPE_CODES = {"f32": FCM_F32, "f16": FCM_F16, "bf16": FCM_BF16}
+DTYPE_CODES = {"f32": FCM_F32, "f16": FCM_F16, "bf16": FCM_BF16, "i8": FCM_I8}
 ACT_CODES = {"none": FCM_ACT_NONE, "relu": FCM_ACT_RELU, "relu6": FCM_ACT_RELU6}
 KIND_CODES = {"dwpw": FCM_KIND_DWPW, "b2b": FCM_KIND_B2B, "pwdw": FCM_KIND_PWDW}
 

@@ -53,6 +53,7 @@ const VariantImpl kImpls[] = {
      occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>},
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {launch_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>, occ_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>},
+#define FCM_V_DWPW_I8(name, S, OCC) {launch_dwpw_i8<S, OCC>, occ_dwpw_i8<S, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -61,6 +62,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_PWDW_MM
+#undef FCM_V_DWPW_I8
 };
 static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
 
@@ -264,7 +266,7 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
     if (!plan) return fail(FCM_ERR_INVALID_ARG, "plan is NULL");
     FCM_TRY(check_plan(plan, plan->prob.kind));
     const fcm_problem& p = plan->prob;
-    const int e = p.dtype == FCM_F32 ? 4 : 2;
+    const int e = p.dtype == FCM_F32 ? 4 : p.dtype == FCM_I8 ? 1 : 2;
     if ((w1_src == nullptr) != (w1_dst == nullptr))
         return fail(FCM_ERR_INVALID_ARG, "w1_src and w1_dst must both be given or both NULL");
     if ((w2_src == nullptr) != (w2_dst == nullptr))
@@ -292,6 +294,15 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                : (int64_t)p.K * (p.kind == FCM_KIND_B2B ? p.K1 : p.C) * e;
         const int64_t nd = plan->w2_packed_bytes;
         if (s < d + nd && d < s + ns) return fail(FCM_ERR_INVALID_ARG, "w2 buffers overlap");
+    }
+    if (p.dtype == FCM_I8) {
+        // int8 DW->PW: depthwise [C][R*S] -> [R*S][C]; pointwise [K][C] copied, then the
+        // blocked copy in the int8 matrix-operand order
+        const int rc = launch_pack_i8(w1_src, w1_dst, w2_src, w2_dst, p.C, p.K, stream);
+        if (rc != 0)
+            return fail(FCM_ERR_HIP, std::string("weight packing failed: ") +
+                                         hipGetErrorString((hipError_t)rc));
+        return ok();
     }
     if (p.kind == FCM_KIND_PWDW) {
         // first layer: pointwise [K1][C] copied as is; second: depthwise [K1][R*S] ->
@@ -510,7 +521,9 @@ fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
     a.b1 = bias1;
     a.y = t;
     set_tiles(&a, lbl::DW_TH, lbl::DW_TW, 1, 1);
-    const int rc = launch_dw_lbl(plan->prob.dtype, plan->prob.stride_h, a, stream);
+    const int rc = plan->prob.dtype == FCM_I8
+                       ? launch_dw_lbl_i8(plan->prob.stride_h, a, stream)
+                       : launch_dw_lbl(plan->prob.dtype, plan->prob.stride_h, a, stream);
     if (rc != 0)
         return fail(FCM_ERR_HIP,
                     std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)rc));
@@ -544,7 +557,8 @@ fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
     a.y = y;
     const int kt = plan->prob.dtype == FCM_F32 ? lbl::PW_KT32 : lbl::PW_KT16;
     a.num_ktiles = (plan->prob.K + kt - 1) / kt;
-    const int rc = launch_pw_lbl(plan->prob.dtype, a, stream);
+    const int rc = plan->prob.dtype == FCM_I8 ? launch_pw_lbl_i8(a, stream)
+                                              : launch_pw_lbl(plan->prob.dtype, a, stream);
     if (rc != 0)
         return fail(FCM_ERR_HIP,
                     std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)rc));

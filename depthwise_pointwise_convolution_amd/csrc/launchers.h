@@ -32,6 +32,16 @@ int launch_pwdw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
 int occ_pwdw_mm();
 
+template <int S, int OCC>
+int launch_dwpw_i8(const KArgs& a, int grid, void* stream);
+template <int S, int OCC>
+int occ_dwpw_i8();
+// INT8 layer-by-layer baselines and weight packing (dwpw_i8.hip)
+int launch_dw_lbl_i8(int stride, const KArgs& a, void* stream);
+int launch_pw_lbl_i8(const KArgs& a, void* stream);
+int launch_pack_i8(const void* w_dw, void* dw_dst, const void* w_pw, void* pw_dst, int C, int K,
+                   void* stream);
+
 template <typename T, int S, int OCC>
 int launch_b2b_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int OCC>

@@ -48,6 +48,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0},
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {#name, VK_PWDW_MM, dt, S, TH, 16, NW * BPW * 16, CMAX, 1, 2, 0, OCC, NW, CMAX, BPW},
+#define FCM_V_DWPW_I8(name, S, OCC) \
+    {#name, VK_DWPW_I8, FCM_I8, S, 4, 16, 64, 64, 1, 2, 0, OCC, 4, 64, 0},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -56,12 +58,13 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_PWDW_MM
+#undef FCM_V_DWPW_I8
 };
 const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
 namespace {
 
-int elem_bytes(int dtype) { return dtype == FCM_F32 ? 4 : 2; }
+int elem_bytes(int dtype) { return dtype == FCM_F32 ? 4 : dtype == FCM_I8 ? 1 : 2; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Rows (or columns) of the input that the halo window of output tile `t` (extent
@@ -130,6 +133,13 @@ int variant_lds_bytes(const VariantDesc& v) {
         return v.nbuf * slots_p * 16 + 2 * mb * (v.cc / 32) * 64 * 16 + 2 * v.kt * 4 +
                v.cmax * (9 * 2 + 2 * 4);
     }
+    case VK_DWPW_I8: {
+        // two input tile buffers (16-byte chunks of 16 channels, whole 256-thread load
+        // rounds) and two 4-row intermediate tiles of 1 KB per row
+        const int slots = IH * IW * 4;
+        const int slots_p = (slots + 255) / 256 * 256;
+        return 2 * slots_p * 16 + 2 * 4 * 1024;
+    }
     case VK_PWDW_MM: {
         // two input-window buffers (whole load rounds of 16-pixel blocks) and one
         // intermediate tile per owned channel block: (IH + 1) rows x 2 chunks x IW
@@ -184,6 +194,12 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
         return 4 * mb * kbw + 16 * kbw + 28 + 5 * ppw + 2 * ((slots + nt - 1) / nt) + 36 + 24;
     }
+    case VK_DWPW_I8: {
+        // depthwise and pointwise operands, both epilogues' constants (4 + 16 channels),
+        // the direct-load plan, operands of the input rows, accumulators, addressing
+        const int IH = (v.th - 1) * v.stride + 3, IW = 15 * v.stride + 3;
+        return 12 + 16 + 8 + 32 + 2 * ((IH * IW * 4 + 255) / 256) + 4 * IH + 16 + 16 + 40;
+    }
     case VK_PWDW_MM: {
         // per owned block: pointwise operands, five depthwise operands, both epilogues'
         // constants; window offsets and positions per pixel block, the direct-load plan,
@@ -210,7 +226,7 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         *err = "unknown kind";
         return FCM_ERR_INVALID_ARG;
     }
-    if (p->dtype < FCM_F32 || p->dtype > FCM_BF16) {
+    if (p->dtype < FCM_F32 || p->dtype > FCM_I8) {
         *err = "unknown dtype";
         return FCM_ERR_INVALID_ARG;
     }
@@ -271,10 +287,40 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         *err = "the PW->DW kernels need 16-bit storage (fp16 or bf16)";
         return FCM_ERR_UNSUPPORTED;
     }
+    if (p->dtype == FCM_I8 && p->kind != FCM_KIND_DWPW) {
+        *err = "int8 storage is provided for the DW->PW module only";
+        return FCM_ERR_UNSUPPORTED;
+    }
+    if (p->dtype == FCM_I8 && (p->C % 16 || p->K % 16)) {
+        *err = "int8 kernels need channel counts that are multiples of 16 (16-byte vectors)";
+        return FCM_ERR_UNSUPPORTED;
+    }
     return FCM_OK;
 }
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
+    if (v.vkind == VK_DWPW_I8 || p.dtype == FCM_I8) {
+        if (v.vkind != VK_DWPW_I8 || p.dtype != FCM_I8 || p.kind != FCM_KIND_DWPW) {
+            if (why) *why = "variant is for another module kind or storage type";
+            return false;
+        }
+        if (v.stride != p.stride_h) {
+            if (why) *why = "variant is compiled for another stride";
+            return false;
+        }
+        if (p.C > 64) {
+            if (why) *why = "int8 variant stages at most 64 input channels";
+            return false;
+        }
+        const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
+        const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
+        if ((int64_t)p.N * p.H * p.W * p.C >= ((int64_t)1 << 31) ||
+            (int64_t)p.N * Ho * Wo * p.K >= ((int64_t)1 << 30)) {
+            if (why) *why = "int8 variant addresses inputs below 2 GiB and outputs below 1 GiB";
+            return false;
+        }
+        return true;
+    }
     if ((v.vkind == VK_PWDW_MM) != (p.kind == FCM_KIND_PWDW) || v.dtype != p.dtype) {
         if (why) *why = "variant is for another module kind or storage type";
         return false;
@@ -436,6 +482,13 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
         // pixel) recomputed for every K tile
         t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * p.C * ktiles) / d.mfma_f16_flops;
         t_vec = P * pad_px * (epi_ops + 1.25 * p.C * ktiles) / lane_ops_per_s;
+    } else if (v.vkind == VK_DWPW_I8) {
+        // int8 matrix rate is twice the fp16 one; the block-diagonal depthwise product is
+        // 3 16x16x64 instructions per 16 channels x 16 pixels (384 op-equivalents per
+        // channel and pixel), the pointwise reduction padded to 64 channels; vector work:
+        // about five operations per requantized value
+        t_mat = P * pad_px * (2.0 * 64 * p.K + 384.0 * 64 * ktiles) / (2.0 * d.mfma_f16_flops);
+        t_vec = P * pad_px * 5.0 * ((double)n1 * ktiles + p.K) / lane_ops_per_s;
     } else if (v.vkind == VK_DWPW_MM) {
         t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * v.cc * ktiles) / d.mfma_f16_flops;
         // operand expansion when a wave owns several depthwise channel blocks
@@ -741,7 +794,10 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         (int64_t)(p->kind == FCM_KIND_B2B ? (int64_t)p->K1 * p->R * p->S * p->C
                                           : (int64_t)p->R * p->S * p->C) * e;
     pl.w2_packed_bytes = (int64_t)p->K * n1 * e;
-    if (p->dtype != FCM_F32) {
+    if (p->dtype == FCM_I8) {
+        // int8: the 1x1 filters again in 64 x 64 blocks in the int8 matrix-operand order
+        pl.w2_packed_bytes += (int64_t)((p->K + 63) / 64) * 64 * 64;
+    } else if (p->dtype != FCM_F32) {
         // 16-bit storage: the 1x1 filters again in 32 x 32 blocks in matrix-operand order
         // (pw_blocked_elems), and for B2B the 3x3 filters in 16 x 32 blocks
         // (conv_blocked_elems), each after the plain array

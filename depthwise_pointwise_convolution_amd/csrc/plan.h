@@ -16,7 +16,8 @@ enum VKind {
     VK_DWPW_MM = 3,
     VK_B2B_MM = 5,
     VK_DWPW_MMW = 6,
-    VK_PWDW_MM = 7
+    VK_PWDW_MM = 7,
+    VK_DWPW_I8 = 8
 };
 
 struct VariantDesc {

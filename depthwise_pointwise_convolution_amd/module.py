@@ -12,7 +12,8 @@ from . import (fcm_b2b_conv_fwd, fcm_conv_fwd, fcm_dw_fwd, fcm_dwpw_fwd, fcm_pac
                fcm_plan, fcm_plan_variant, fcm_pw_fwd, fcm_pwdw_fwd, fcm_tune, problem,
                FCM_KIND_B2B, FCM_KIND_PWDW)
 
-TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+                "i8": torch.int8}
 
 
 class FcmModule:

@@ -26,7 +26,11 @@
  *  - Convolution is cross-correlation (no filter flip) with zero padding.
  *  - Activations and weights share one storage type (fcm_dtype); accumulation and
  *    the epilogue are fp32; each layer's output is rounded to the storage type with
- *    round-to-nearest-even.
+ *    round-to-nearest-even.  FCM_I8 (DWPW only; FCM paper Sec. III-B: int8 operands,
+ *    32-bit accumulation, results packed to 8 bits before they are written): exact
+ *    int32 sums; each layer's output is v = fmaf(scale, acc, bias) in fp32, clamped to
+ *    the activation's range, rounded to the nearest integer (ties to even) and
+ *    saturated to [-128, 127].
  *  - Epilogue of a layer with n output channels: out[c] = act(scale[c]*acc[c] +
  *    bias[c]) with fp32 arrays scale[n], bias[n] in device memory; a NULL scale means
  *    1 and a NULL bias means 0.
@@ -60,7 +64,7 @@ typedef enum {
     FCM_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
 } fcm_status;
 
-typedef enum { FCM_F32 = 0, FCM_F16 = 1, FCM_BF16 = 2 } fcm_dtype;
+typedef enum { FCM_F32 = 0, FCM_F16 = 1, FCM_BF16 = 2, FCM_I8 = 3 } fcm_dtype;
 
 typedef enum { FCM_ACT_NONE = 0, FCM_ACT_RELU = 1, FCM_ACT_RELU6 = 2 } fcm_act;
 
@@ -151,7 +155,8 @@ fcm_status fcm_query_device_spec(int device, fcm_device_spec* out);
  * Host only; makes no HIP call.  Errors: INVALID_ARG (null pointer, non-positive
  * size, K1 != C for DWPW, K != K1 for PWDW, padding >= filter), UNSUPPORTED (filter not
  * 3x3, stride not 1 or 2, padding not 0 or 1, a channel count not a multiple of 8, fp32
- * storage for B2B or PWDW, or no variant fits). */
+ * storage for B2B or PWDW, int8 storage other than DWPW or with C or K not a multiple
+ * of 16, or no variant fits). */
 fcm_status fcm_plan(const fcm_problem* prob, const fcm_device_spec* spec, fcm_plan_t* out);
 
 /* Same, but with the fused kernel variant forced (for tests and on-device tuning).
@@ -197,6 +202,9 @@ const char* fcm_variant_name(int32_t variant);
  *                                            rounded up to 16, C to 64, zero filled)
  *         w2_src 1x1       [K][K1]        -> w2_dst [K][K1], and for fp16/bf16 followed by
  *                                            32x32 blocks as for DWPW
+ *   DWPW in FCM_I8: w1 as above; w2 [K][C] copied, then 64 x 64 blocks (K tile of 64
+ *         output channels, four 16-row operands) in the int8 matrix-operand order
+ *         (K rounded up to 64, C <= 64, zero filled)
  *   PWDW: w1_src pointwise [K1][C]        -> w1_dst [K1][C]       (copied as is)
  *         w2_src depthwise [K1][R][S]     -> w2_dst [R*S][K1]     (channel fastest)
  * Sizes in bytes are plan->w1_packed_bytes / w2_packed_bytes.  Either pair may be

@@ -230,6 +230,25 @@ def test_pwdw_plan_counts_the_recomputed_windows():
     assert pl.fuse == 1
 
 
+def test_i8_problems_are_checked_on_the_host():
+    F = _lib()
+    for kind, C, K, K1 in (("b2b", 64, 64, 64), ("pwdw", 32, 64, 64)):
+        with pytest.raises(F.FcmError) as ei:
+            F.fcm_plan(F.problem(kind, "i8", 1, 16, 16, C, K, K1), _spec(F))
+        assert ei.value.status == F.FCM_ERR_UNSUPPORTED
+    for C, K in ((24, 64), (32, 40)):  # 16-byte int8 vectors
+        with pytest.raises(F.FcmError) as ei:
+            F.fcm_plan(F.problem("dwpw", "i8", 1, 16, 16, C, K), _spec(F))
+        assert ei.value.status == F.FCM_ERR_UNSUPPORTED
+    with pytest.raises(F.FcmError) as ei:  # more channels than the int8 kernel stages
+        F.fcm_plan(F.problem("dwpw", "i8", 1, 16, 16, 128, 64), _spec(F))
+    assert ei.value.status == F.FCM_ERR_UNSUPPORTED
+    pl = F.fcm_plan(F.problem("dwpw", "i8", 8, 112, 112, 32, 64), _spec(F))
+    assert F.fcm_variant_name(pl.variant).startswith("dwpw_i8")
+    # int8 filters: 9 x C depthwise, K x C plain + 64 x 64 blocks per 64 output channels
+    assert pl.w1_packed_bytes == 9 * 32 and pl.w2_packed_bytes == 64 * 32 + 64 * 64
+
+
 def test_b2b_needs_16bit_storage_and_small_filters():
     F = _lib()
     prob = F.problem("b2b", "f32", 1, 16, 16, 64, 64, 64, stride=1, pad=1)
@@ -293,7 +312,9 @@ def test_forced_variants_cover_every_compiled_kernel():
         fcm_inputs.Workload("b", "b2b", dt, N=2, H=17, W=23, C=64, K=64, K1=k1, stride=s)
         for dt in ("f16", "bf16") for k1 in (32, 64, 128) for s in (1, 2)] + [
         fcm_inputs.Workload("p", "pwdw", dt, N=2, H=17, W=23, C=c, K=k1, K1=k1, stride=s)
-        for dt in ("f16", "bf16") for c in (24, 64) for k1 in (96, 144) for s in (1, 2)]
+        for dt in ("f16", "bf16") for c in (24, 64) for k1 in (96, 144) for s in (1, 2)] + [
+        fcm_inputs.Workload("q", "dwpw", "i8", N=2, H=17, W=23, C=c, K=k, K1=c, stride=s)
+        for c in (32, 64) for k in (64, 112) for s in (1, 2)]
     for wl in shapes:
         prob = _problem(F, wl)
         for v in range(F.fcm_num_variants()):

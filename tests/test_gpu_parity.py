@@ -79,6 +79,9 @@ CASES_INT = [
     ("b2b", "f16", 2, 9, 19, 64, 64, 64, 1, 1, "relu", "relu", True),
     ("b2b", "bf16", 1, 10, 9, 32, 48, 32, 1, 0, "none", "relu", True),
     ("b2b", "f16", 1, 11, 12, 40, 24, 96, 2, 1, "relu6", "none", True),
+    ("dwpw", "i8", 2, 9, 21, 32, 64, None, 1, 1, "relu", "relu", True),
+    ("dwpw", "i8", 1, 13, 15, 64, 128, None, 2, 1, "none", "relu6", True),
+    ("dwpw", "i8", 2, 7, 7, 16, 48, None, 1, 0, "relu6", "none", False),
     ("pwdw", "f16", 2, 9, 21, 24, 144, 144, 1, 1, "relu6", "relu6", True),
     ("pwdw", "bf16", 1, 11, 17, 64, 48, 48, 1, 1, "none", "relu", False),
     ("pwdw", "f16", 2, 13, 15, 16, 96, 96, 2, 1, "relu", "relu6", True),
@@ -130,7 +133,9 @@ def test_full_size_integer_exact_every_variant(name):
         mod = from_workload(wl, inp, device="cuda", variant=v)
         y = mod.new_output("cuda")
         for rep in range(2):
-            y.fill_(float("nan"))
+            # NaN marks unwritten floats; int8 outputs get two different fill codes, so an
+            # unwritten element differs from the expected value in at least one run
+            y.fill_(float("nan") if wl.dtype != "i8" else (85 if rep == 0 else -86))
             mod.fused(x, y)
             got = y.double().cpu().numpy()
             bad = np.argwhere(~(got == ref))
@@ -166,6 +171,34 @@ def test_random_small_shapes(wl):
         got, _ = run_gpu(wl, inp, path=path)
         err = rel_err(got, ref)
         assert err <= TOL[wl.dtype], (path, err)
+
+
+def _random_i8_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        out.append(fcm_inputs.Workload(
+            f"q{i}", "dwpw", "i8", N=int(rng.integers(1, 3)), H=int(rng.integers(1, 24)),
+            W=int(rng.integers(1, 40)), C=int(rng.choice([16, 32, 48, 64])),
+            K=int(rng.choice([16, 32, 64, 80, 128])), K1=0, stride=int(rng.integers(1, 3)),
+            pad=int(rng.integers(0, 2)), act1=str(rng.choice(["none", "relu", "relu6"])),
+            act2=str(rng.choice(["none", "relu", "relu6"])), scale1=bool(rng.random() < .7),
+            bias1=bool(rng.random() < .7), scale2=bool(rng.random() < .7),
+            bias2=bool(rng.random() < .7), x_dist=("int", -128, 127),
+            w_dist=("int", -127, 127), scale_dist=("uniform", 0.001, 0.01),
+            bias_dist=("normal", 0.0, 8.0), seed=int(rng.integers(1 << 30))))
+    return [w.replace(K1=w.C) for w in out if w.H + 2 * w.pad >= 3 and w.W + 2 * w.pad >= 3]
+
+
+@pytest.mark.parametrize("wl", _random_i8_cases(16, 9), ids=lambda w: w.name)
+def test_random_small_shapes_i8(wl):
+    inp = fcm_inputs.make_inputs(wl)
+    ref = oracle_full(wl, inp)
+    for path in ("fused", "unfused"):
+        _log(f"case {wl} {path}")
+        got, _ = run_gpu(wl, inp, path=path)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, (path, len(bad), bad[:3].tolist())
 
 
 def _random_pwdw_cases(n, seed):
