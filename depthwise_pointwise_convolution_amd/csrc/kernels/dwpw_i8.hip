@@ -394,34 +394,47 @@ __global__ __launch_bounds__(256) void dw_lbl_i8_kernel(KArgs a) {
     ((uint32_t*)a.y)[pix * C4 + c4] = q8::pack4(o[0], o[1], o[2], o[3]);
 }
 
-// Pointwise: one thread per (pixel, 4 output channels); four-way int8 dot products with
-// 32-bit accumulation over C (the pages' dp4a); requantized; 4 bytes stored.
-// t: [M][C], w: [K][C] (plain), y: [M][K], M = N * Ho * Wo.
+// Pointwise: one thread per (pixel, 16 output channels); the workgroup's 16 filters are
+// staged in LDS (every lane reads the same word: a broadcast); four-way int8 dot
+// products with 32-bit accumulation over C (the pages' dp4a), the pixel's channels read
+// 16 bytes at a time; requantized; one 16-byte store.  t: [M][C], w: [K][C] (plain),
+// y: [M][K], M = N * Ho * Wo; blockIdx.y = group of 16 output channels; C <= 1024.
 __global__ __launch_bounds__(256) void pw_lbl_i8_kernel(KArgs a) {
-    const int K4 = a.K / 4, C4 = a.C / 4;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    __shared__ uint32_t ws[16 * 256];
+    const int C4 = a.C / 4, kg = blockIdx.y;
     const int64_t M = (int64_t)a.N * a.Ho * a.Wo;
-    if (idx >= M * K4) return;
-    const int k4 = (int)(idx % K4);
-    const int64_t m = idx / K4;
-    const uint32_t* __restrict__ t = (const uint32_t*)a.x + m * C4;
-    const uint32_t* __restrict__ w = (const uint32_t*)a.w2;
-    int32_t acc[4] = {0, 0, 0, 0};
-    for (int c = 0; c < C4; ++c) {
-        const int tv = (int)t[c];
+    const uint32_t* __restrict__ w = (const uint32_t*)a.w2 + (int64_t)16 * kg * C4;
+    for (int i = threadIdx.x; i < 16 * C4; i += 256) ws[i] = w[i];
+    __syncthreads();
+    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (m >= M) return;
+    const u32x4* __restrict__ t = (const u32x4*)((const uint32_t*)a.x + m * C4);
+    int32_t acc[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[i] = __builtin_amdgcn_sdot4(tv, (int)w[(int64_t)(4 * k4 + i) * C4 + c], acc[i],
-                                            false);
+    for (int k = 0; k < 16; ++k) acc[k] = 0;
+    for (int c16 = 0; c16 < C4 / 4; ++c16) {
+        const u32x4 tv = t[c16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                acc[k] = __builtin_amdgcn_sdot4((int)tv[j], (int)ws[k * C4 + 4 * c16 + j], acc[k],
+                                                false);
     }
     const q8::Bounds bd = q8::bounds(a.act2);
     uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int k = 4 * k4 + i;
-        o[i] = q8::requant(acc[i], a.s2 ? a.s2[k] : 1.0f, a.b2 ? a.b2[k] : 0.0f, bd.lo, bd.hi);
+    for (int q = 0; q < 4; ++q) {
+        uint32_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = 16 * kg + 4 * q + i;
+            v[i] = q8::requant(acc[4 * q + i], a.s2 ? a.s2[k] : 1.0f, a.b2 ? a.b2[k] : 0.0f,
+                               bd.lo, bd.hi);
+        }
+        o[q] = q8::pack4(v[0], v[1], v[2], v[3]);
     }
-    ((uint32_t*)a.y)[m * K4 + k4] = q8::pack4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<u32x4*>((int8_t*)a.y + m * a.K + 16 * kg) = u32x4{o[0], o[1], o[2], o[3]};
 }
 
 int launch_dw_lbl_i8(int stride, const KArgs& a, void* stream) {
@@ -436,10 +449,11 @@ int launch_dw_lbl_i8(int stride, const KArgs& a, void* stream) {
 }
 
 int launch_pw_lbl_i8(const KArgs& a, void* stream) {
-    const int64_t total = (int64_t)a.N * a.Ho * a.Wo * (a.K / 4);
+    if (a.C > 1024) return (int)hipErrorInvalidValue;
+    const int64_t M = (int64_t)a.N * a.Ho * a.Wo;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(pw_lbl_i8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       (hipStream_t)stream, a);
+    hipLaunchKernelGGL(pw_lbl_i8_kernel, dim3((unsigned)((M + 255) / 256), (unsigned)(a.K / 16)),
+                       dim3(256), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 
