@@ -31,7 +31,7 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "dwpw", "b2b" or "pwdw"
+    kind: str            # "dwpw", "b2b", "pwdw" or "pwpw"
     dtype: str           # "f32" | "f16" | "bf16" | "i8"
     N: int
     H: int
@@ -113,6 +113,12 @@ WORKLOADS = {
         scale_dist=("uniform", 0.002, 0.006), bias_dist=("normal", 0.0, 8.0), seed=8,
         description="INT8 DWPW (MobileNetV1 layers 2-3): DW 3x3 s1 C=32 + requantize+ReLU, "
                     "PW 32->64 + requantize+ReLU, int8 with int32 sums, N=8 112x112"),
+    "pwpw_f16_32x56x56_c64_k32_k64": Workload(
+        "pwpw_f16_32x56x56_c64_k32_k64", "pwpw", "f16", N=32, H=56, W=56, C=64, K=64, K1=32,
+        R=1, S=1, pad=0, act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True,
+        bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=9,
+        description="PW->PW module (bottleneck pair): PW 64->32 + scale/bias+ReLU6, "
+                    "PW 32->64 + scale/bias+ReLU6, fp16, N=32 56x56"),
     "pwdw_f16_32x56x56_c24_k144": Workload(
         "pwdw_f16_32x56x56_c24_k144", "pwdw", "f16", N=32, H=56, W=56, C=24, K=144, K1=144,
         act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True, bias2=True,
@@ -164,7 +170,7 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> dict:
     if wl.kind == "dwpw":
         w1 = _draw(rng, wl.w_dist, (wl.C, wl.R, wl.S))
         n1 = wl.C
-    elif wl.kind == "pwdw":
+    elif wl.kind in ("pwdw", "pwpw"):
         w1 = _draw(rng, wl.w_dist, (wl.K1, wl.C))
         n1 = wl.K1
     else:

@@ -101,6 +101,10 @@ def _load():
             lib.fcm_oracle_pwdw.restype = ctypes.c_int
             lib.fcm_oracle_pwdw_at.argtypes = mod_pd + [ip, i64, dp]
             lib.fcm_oracle_pwdw_at.restype = ctypes.c_int
+            # x, M, C, w1, K1, scale1, bias1, act1, w2, K, scale2, bias2, act2, dtype, t, y
+            lib.fcm_oracle_pwpw.argtypes = [dp, i64, i32, dp, i32, dp, dp, ci, dp, i32, dp, dp,
+                                            ci, ci, dp, dp]
+            lib.fcm_oracle_pwpw.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -325,3 +329,36 @@ def pwdw_at(x, w_pw, w_dw, pix, stride=(1, 1), pad=(1, 1), scale1=None, bias1=No
                                pix.shape[0], _p(y))
     del keep
     return y
+
+
+# ---------------------------------------------------------------------------------
+# the pointwise -> pointwise module
+# ---------------------------------------------------------------------------------
+def pwpw(x, w1, w2, scale1=None, bias1=None, act1="none", scale2=None, bias2=None,
+         act2="none", dtype="f32", return_t=False, **_):
+    """Layer-by-layer PW conv -> epilogue -> round -> PW conv -> epilogue -> round over
+    every pixel of x [..., C]; w1 [K1, C], w2 [K, K1].  (Stride and padding keywords are
+    accepted and ignored: a 1x1 layer has neither.)"""
+    x, w1, w2 = _f64(x), _f64(w1), _f64(w2)
+    C = x.shape[-1]
+    K1, C1 = w1.shape
+    K, K1b = w2.shape
+    assert C1 == C and K1b == K1
+    M = x.size // C
+    t = np.empty(x.shape[:-1] + (K1,), np.float64)
+    y = np.empty(x.shape[:-1] + (K,), np.float64)
+    arrs = [None if a is None else _f64(a) for a in (scale1, bias1, scale2, bias2)]
+    rc = _load().fcm_oracle_pwpw(_p(x), M, C, _p(w1), K1, _p(arrs[0]), _p(arrs[1]), ACTS[act1],
+                                 _p(w2), K, _p(arrs[2]), _p(arrs[3]), ACTS[act2], DTYPES[dtype],
+                                 _p(t), _p(y))
+    if rc != 0:
+        raise MemoryError("oracle could not allocate the intermediate")
+    return (y, t) if return_t else y
+
+
+def pwpw_at(x, w1, w2, pix, **kw):
+    """Rows y[n, h, w, :] of :func:`pwpw` at the listed pixels (each pixel is
+    independent, so this is the module on those pixels alone)."""
+    x = _f64(x)
+    pix = np.asarray(pix).reshape(-1, 3)
+    return pwpw(x[pix[:, 0], pix[:, 1], pix[:, 2]], w1, w2, **kw)

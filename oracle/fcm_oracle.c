@@ -17,6 +17,8 @@
  *                       output (the PWDW / PWDW_R fusion cases, FCM paper Sec. II-D,
  *                       Fig. 3(b), and Sec. III); the depthwise layer's zero padding
  *                       pads the intermediate, not the module's input;
+ *   PW -> PW module  -- two pointwise layers (the PWPW fusion case, FCM paper Sec. III,
+ *                       Table II): pixel by pixel, so a tile needs no halo;
  *   standard conv    -- the first layer of the back-to-back pair, [N,H,W,C] x
  *                       [K,C,R,S] ("Fusing two back-to-back convolutions", the
  *                       CONV1/CONV2 example);
@@ -424,5 +426,22 @@ int fcm_oracle_pwdw_at(const double* x, int N, int H, int W, int C, const double
         fcm_oracle_round_array(yr, K1, dtype);
         free(t);
     }
+    return 0;
+}
+
+
+/* PW -> PW module, layer by layer, over M pixels: t = store(x . w1^T), y = store(t . w2^T),
+ * w1 [K1][C], w2 [K][K1]; store = epilogue + rounding to the storage type. */
+int fcm_oracle_pwpw(const double* x, int64_t M, int C, const double* w1, int K1,
+                    const double* scale1, const double* bias1, int act1, const double* w2,
+                    int K, const double* scale2, const double* bias2, int act2, int dtype,
+                    double* t_out, double* y) {
+    double* t = t_out ? t_out : (double*)malloc(sizeof(double) * (size_t)(M * K1));
+    if (!t) return -1;
+    fcm_oracle_pw(x, M, C, w1, K1, t);
+    store_rows(t, M, K1, scale1, bias1, act1, dtype);
+    fcm_oracle_pw(t, M, K1, w2, K, y);
+    store_rows(y, M, K, scale2, bias2, act2, dtype);
+    if (!t_out) free(t);
     return 0;
 }

@@ -373,6 +373,50 @@ def test_i8_inputs_are_integer_codes():
 
 
 # ---------------------------------------------------------------------------------
+# the pointwise -> pointwise module
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_pwpw_module_is_layer_by_layer_pipeline(dtype):
+    rng = _rng(50)
+    x = oracle.round_to(rng.standard_normal((2, 5, 7, 24)), dtype)
+    w1 = oracle.round_to(rng.standard_normal((40, 24)) * 0.3, dtype)
+    w2 = oracle.round_to(rng.standard_normal((16, 40)) * 0.3, dtype)
+    s1, b1 = rng.uniform(0.5, 1.5, 40), rng.standard_normal(40) * 0.1
+    s2, b2 = rng.uniform(0.5, 1.5, 16), rng.standard_normal(16) * 0.1
+    y, t = oracle.pwpw(x, w1, w2, s1, b1, "relu6", s2, b2, "relu", dtype, return_t=True)
+    tr = _torch_round(np.clip(_torch_conv(x, w1[:, :, None, None], 1, 0) * s1 + b1, 0, 6), dtype)
+    yr = _torch_round(np.maximum(_torch_conv(tr, w2[:, :, None, None], 1, 0) * s2 + b2, 0), dtype)
+    ulp = {"f32": 2.0 ** -23, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[dtype]
+    assert np.all(np.abs(t - tr) <= ulp * np.abs(tr) + 1e-30)
+    assert np.all(np.abs(y - yr) <= 2 * ulp * np.maximum(np.abs(yr), 1e-3) + 1e-30)
+    assert np.mean(y == yr) > 0.97
+
+
+def test_pwpw_identity_first_layer_is_one_pointwise_layer():
+    rng = _rng(51)
+    x = oracle.round_to(rng.standard_normal((1, 4, 6, 16)), "f16")
+    w2 = oracle.round_to(rng.standard_normal((8, 16)) * 0.3, "f16")
+    b2 = rng.standard_normal(8) * 0.1
+    y, t = oracle.pwpw(x, np.eye(16), w2, bias2=b2, act2="relu", dtype="f16", return_t=True)
+    assert np.array_equal(t, x)
+    assert np.array_equal(y, oracle.round_to(np.maximum(oracle.pw(x, w2) + b2, 0), "f16"))
+    # and the module is a per-pixel map: any subset of pixels gives the same rows
+    pix = np.array([[0, 3, 5], [0, 0, 0], [0, 2, 1]])
+    assert np.array_equal(oracle.pwpw_at(x, np.eye(16), w2, pix, bias2=b2, act2="relu",
+                                         dtype="f16"), y[pix[:, 0], pix[:, 1], pix[:, 2]])
+
+
+def test_pwpw_accounting_closed_forms():
+    wl = fcm_inputs.WORKLOADS["pwpw_f16_32x56x56_c64_k32_k64"]
+    s = accounting.sizes(wl)
+    P = 32 * 56 * 56
+    assert (wl.Ho, wl.Wo) == (56, 56)
+    assert s["t"] == P * 32 * 2
+    assert accounting.alg_bytes(wl) == P * (64 + 64) * 2 + (32 * 64 + 64 * 32) * 2 + 4 * 2 * (32 + 64)
+    assert accounting.flops(wl) == 2 * P * (64 * 32 + 32 * 64)
+
+
+# ---------------------------------------------------------------------------------
 # the pointwise -> depthwise module
 # ---------------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,stride,pad", [("f32", 1, 1), ("f16", 1, 1), ("bf16", 1, 1),
