@@ -8,6 +8,7 @@ kernels.  The functions carry the C ABI's names (see ``include/fcm.h``):
     fcm_dwpw_fwd(plan, x, w_dw, scale1, bias1, w_pw, scale2, bias2, y)
     fcm_b2b_conv_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y)
     fcm_pwdw_fwd(plan, x, w_pw, scale1, bias1, w_dw, scale2, bias2, y)
+    fcm_pwpw_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y)
     fcm_dw_fwd / fcm_pw_fwd / fcm_conv_fwd   (layer-by-layer baselines)
 
 Tensor arguments are torch tensors on the GPU (or raw integer device addresses, or
@@ -29,12 +30,13 @@ LIB_PATH = os.path.join(PKG, "libfcm.so")
 FCM_OK, FCM_ERR_INVALID_ARG, FCM_ERR_UNSUPPORTED, FCM_ERR_HIP = 0, 1, 2, 3
 FCM_F32, FCM_F16, FCM_BF16, FCM_I8 = 0, 1, 2, 3
 FCM_ACT_NONE, FCM_ACT_RELU, FCM_ACT_RELU6 = 0, 1, 2
-FCM_KIND_DWPW, FCM_KIND_B2B, FCM_KIND_PWDW = 0, 1, 2
+FCM_KIND_DWPW, FCM_KIND_B2B, FCM_KIND_PWDW, FCM_KIND_PWPW = 0, 1, 2, 3
 FCM_PLAN_VERSION = 2
 
 DTYPE_CODES = {"f32": FCM_F32, "f16": FCM_F16, "bf16": FCM_BF16, "i8": FCM_I8}
 ACT_CODES = {"none": FCM_ACT_NONE, "relu": FCM_ACT_RELU, "relu6": FCM_ACT_RELU6}
-KIND_CODES = {"dwpw": FCM_KIND_DWPW, "b2b": FCM_KIND_B2B, "pwdw": FCM_KIND_PWDW}
+KIND_CODES = {"dwpw": FCM_KIND_DWPW, "b2b": FCM_KIND_B2B, "pwdw": FCM_KIND_PWDW,
+              "pwpw": FCM_KIND_PWPW}
 
 
 class FcmError(RuntimeError):
@@ -88,7 +90,8 @@ class fcm_plan_t(ctypes.Structure):
 EXPORTS = ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan", "fcm_plan_variant",
            "fcm_num_variants", "fcm_variant_name", "fcm_pack_weights", "fcm_dwpw_fwd",
            "fcm_tune",
-           "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_dw_fwd", "fcm_pw_fwd", "fcm_conv_fwd",
+           "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_pwpw_fwd", "fcm_dw_fwd", "fcm_pw_fwd",
+           "fcm_conv_fwd",
            "fcm_status_str",
            "fcm_last_error")
 
@@ -121,6 +124,7 @@ def lib() -> ctypes.CDLL:
             L.fcm_dwpw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
             L.fcm_b2b_conv_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
             L.fcm_pwdw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
+            L.fcm_pwpw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
             L.fcm_tune.argtypes = [P(fcm_problem), P(fcm_device_spec), _i32, P(vp), vp, fp, fp,
                                    vp, fp, fp, P(vp), vp, _i32, P(fcm_plan_t)]
             L.fcm_dw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
@@ -132,8 +136,8 @@ def lib() -> ctypes.CDLL:
             L.fcm_last_error.argtypes = []
             for name in ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan",
                          "fcm_plan_variant", "fcm_pack_weights", "fcm_dwpw_fwd",
-                         "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_dw_fwd", "fcm_pw_fwd",
-                         "fcm_conv_fwd"):
+                         "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_pwpw_fwd", "fcm_dw_fwd",
+                         "fcm_pw_fwd", "fcm_conv_fwd"):
                 getattr(L, name).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -252,6 +256,12 @@ def fcm_pwdw_fwd(plan, x, w_pw, scale1, bias1, w_dw, scale2, bias2, y, stream=No
     _check(lib().fcm_pwdw_fwd(ctypes.byref(plan), _ptr(x), _ptr(w_pw), _ptr(scale1),
                               _ptr(bias1), _ptr(w_dw), _ptr(scale2), _ptr(bias2), _ptr(y),
                               _stream(stream)), "fcm_pwdw_fwd")
+
+
+def fcm_pwpw_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y, stream=None):
+    _check(lib().fcm_pwpw_fwd(ctypes.byref(plan), _ptr(x), _ptr(w1), _ptr(scale1),
+                              _ptr(bias1), _ptr(w2), _ptr(scale2), _ptr(bias2), _ptr(y),
+                              _stream(stream)), "fcm_pwpw_fwd")
 
 
 def fcm_tune(prob, x, w1, scale1, bias1, w2, scale2, bias2, y, iters=20, spec=None,

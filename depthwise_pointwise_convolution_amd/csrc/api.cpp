@@ -54,6 +54,7 @@ const VariantImpl kImpls[] = {
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {launch_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>, occ_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>},
 #define FCM_V_DWPW_I8(name, S, OCC) {launch_dwpw_i8<S, OCC>, occ_dwpw_i8<S, OCC>},
+#define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) {launch_pwpw_mm<CT, PB, OCC>, occ_pwpw_mm<CT, PB, OCC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -63,6 +64,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_PWDW_MM
 #undef FCM_V_DWPW_I8
+#undef FCM_V_PWPW_MM
 };
 static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
 
@@ -168,6 +170,11 @@ void set_tiles(KArgs* a, int th, int tw, int kt, int kdim) {
 fcm_status launch_fused(const fcm_plan_t* plan, KArgs& a, void* stream) {
     const VariantDesc& v = kVariants[plan->variant];
     set_tiles(&a, v.th, v.tw, v.kt, plan->prob.K);  // (PWDW: K == K1)
+    if (plan->prob.kind == FCM_KIND_PWPW) {
+        // tiles of th x tw consecutive pixels of the flattened N x H x W extent
+        const int64_t M = (int64_t)plan->prob.N * plan->prob.H * plan->prob.W;
+        a.num_ptiles = (int)((M + v.th * v.tw - 1) / (v.th * v.tw));
+    }
     int cus = 0, per_cu = 0;
     FCM_TRY(device_capacity(plan->variant, &cus, &per_cu));
     // persistent grid within what the GPU holds at once (measured occupancy) and the
@@ -295,6 +302,19 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
         const int64_t nd = plan->w2_packed_bytes;
         if (s < d + nd && d < s + ns) return fail(FCM_ERR_INVALID_ARG, "w2 buffers overlap");
     }
+    if (p.kind == FCM_KIND_PWPW) {
+        int rc = 0;
+        if (w1_src) rc = launch_copy(w1_src, w1_dst, (int64_t)p.K1 * p.C * e, stream);
+        if (rc == 0 && w2_src) {
+            const int64_t plain = (int64_t)p.K * p.K1 * e;
+            rc = launch_copy(w2_src, w2_dst, plain, stream);
+            if (rc == 0) rc = launch_pack_pw_blocked(w2_src, (char*)w2_dst + plain, p.K, p.K1, stream);
+        }
+        if (rc != 0)
+            return fail(FCM_ERR_HIP, std::string("weight packing failed: ") +
+                                         hipGetErrorString((hipError_t)rc));
+        return ok();
+    }
     if (p.dtype == FCM_I8) {
         // int8 DW->PW: depthwise [C][R*S] -> [R*S][C]; pointwise [K][C] copied, then the
         // blocked copy in the int8 matrix-operand order
@@ -417,6 +437,31 @@ fcm_status fcm_pwdw_fwd(const fcm_plan_t* plan, const void* x, const void* w_pw,
     return launch_fused(plan, a, stream);
 }
 
+fcm_status fcm_pwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
+                        const float* scale1, const float* bias1, const void* w2,
+                        const float* scale2, const float* bias2, void* y, void* stream) {
+    FCM_TRY(check_plan(plan, FCM_KIND_PWPW));
+    FCM_TRY(check_variant(plan));
+    FCM_TRY(need(x, "x", 16));
+    FCM_TRY(need(w1, "w1", 16));
+    FCM_TRY(need(w2, "w2", 16));
+    FCM_TRY(need(y, "y", 16));
+    FCM_TRY(optional(scale1, "scale1"));
+    FCM_TRY(optional(bias1, "bias1"));
+    FCM_TRY(optional(scale2, "scale2"));
+    FCM_TRY(optional(bias2, "bias2"));
+    KArgs a = base_args(plan);
+    a.x = x;
+    a.w1 = w1;
+    a.s1 = scale1;
+    a.b1 = bias1;
+    a.w2 = w2;
+    a.s2 = scale2;
+    a.b2 = bias2;
+    a.y = y;
+    return launch_fused(plan, a, stream);
+}
+
 fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_t nsets,
                     const void* const* x, const void* w1, const float* scale1,
                     const float* bias1, const void* w2, const float* scale2,
@@ -435,6 +480,8 @@ fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_
             return fcm_dwpw_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i], stream);
         case FCM_KIND_PWDW:
             return fcm_pwdw_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i], stream);
+        case FCM_KIND_PWPW:
+            return fcm_pwpw_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i], stream);
         default:
             return fcm_b2b_conv_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, y[i],
                                     stream);
@@ -458,8 +505,10 @@ fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_
         int cus = 0, per_cu = 0;
         st = device_capacity(v, &cus, &per_cu);
         if (st != FCM_OK) break;
-        const int64_t ptiles = (int64_t)prob->N * ((pv.Ho + vd.th - 1) / vd.th) *
-                               ((pv.Wo + vd.tw - 1) / vd.tw);
+        const int64_t ptiles =
+            prob->kind == FCM_KIND_PWPW
+                ? ((int64_t)prob->N * prob->H * prob->W + vd.th * vd.tw - 1) / (vd.th * vd.tw)
+                : (int64_t)prob->N * ((pv.Ho + vd.th - 1) / vd.th) * ((pv.Wo + vd.tw - 1) / vd.tw);
         const int ktiles = (prob->K + vd.kt - 1) / vd.kt;  // (PWDW: K == K1)
         int64_t last_grid = -1;
         for (int w = 1; w <= std::min(4, per_cu) && st == FCM_OK; ++w) {
@@ -541,7 +590,7 @@ fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
     FCM_TRY(optional(bias2, "bias2"));
     KArgs a = base_args(plan);
     // the 1x1 layer reads the intermediate as its input: [N*Ho*Wo][C or K1]
-    if (plan->prob.kind == FCM_KIND_B2B) a.C = plan->prob.K1;
+    if (plan->prob.kind == FCM_KIND_B2B || plan->prob.kind == FCM_KIND_PWPW) a.C = plan->prob.K1;
     if (plan->prob.kind == FCM_KIND_PWDW) {
         // the first layer of a PW->DW module: every input pixel, C -> K1, with the
         // module's first epilogue
@@ -567,6 +616,29 @@ fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
 
 fcm_status fcm_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
                         const float* scale1, const float* bias1, void* t, void* stream) {
+    if (plan && plan->prob.kind == FCM_KIND_PWPW) {
+        // the first 1x1 layer of a PW->PW module: C -> K1 over every pixel, epilogue 1
+        FCM_TRY(check_plan(plan, FCM_KIND_PWPW));
+        FCM_TRY(need(x, "x", 16));
+        FCM_TRY(need(w1, "w1", 16));
+        FCM_TRY(need(t, "t", 16));
+        FCM_TRY(optional(scale1, "scale1"));
+        FCM_TRY(optional(bias1, "bias1"));
+        KArgs a = base_args(plan);
+        a.x = x;
+        a.w2 = w1;
+        a.s2 = scale1;
+        a.b2 = bias1;
+        a.act2 = plan->prob.act1;
+        a.K = plan->prob.K1;
+        a.y = t;
+        a.num_ktiles = (plan->prob.K1 + lbl::PW_KT16 - 1) / lbl::PW_KT16;
+        const int rc = launch_pw_lbl(plan->prob.dtype, a, stream);
+        if (rc != 0)
+            return fail(FCM_ERR_HIP,
+                        std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)rc));
+        return ok();
+    }
     FCM_TRY(check_plan(plan, FCM_KIND_B2B));
     FCM_TRY(need(x, "x", 16));
     FCM_TRY(need(w1, "w1", 16));

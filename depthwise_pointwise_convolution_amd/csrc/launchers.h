@@ -32,6 +32,11 @@ int launch_pwdw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
 int occ_pwdw_mm();
 
+template <typename T, int PB, int OCC>
+int launch_pwpw_mm(const KArgs& a, int grid, void* stream);
+template <typename T, int PB, int OCC>
+int occ_pwpw_mm();
+
 template <int S, int OCC>
 int launch_dwpw_i8(const KArgs& a, int grid, void* stream);
 template <int S, int OCC>

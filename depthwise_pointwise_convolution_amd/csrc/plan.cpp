@@ -50,6 +50,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_PWDW_MM, dt, S, TH, 16, NW * BPW * 16, CMAX, 1, 2, 0, OCC, NW, CMAX, BPW},
 #define FCM_V_DWPW_I8(name, S, OCC) \
     {#name, VK_DWPW_I8, FCM_I8, S, 4, 16, 64, 64, 1, 2, 0, OCC, 4, 64, 0},
+#define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) \
+    {#name, VK_PWPW_MM, dt, 1, PB, 16, 64, 64, 1, 2, 64, OCC, 4, 64, 0},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -59,6 +61,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_PWDW_MM
 #undef FCM_V_DWPW_I8
+#undef FCM_V_PWPW_MM
 };
 const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -133,6 +136,11 @@ int variant_lds_bytes(const VariantDesc& v) {
         return v.nbuf * slots_p * 16 + 2 * mb * (v.cc / 32) * 64 * 16 + 2 * v.kt * 4 +
                v.cmax * (9 * 2 + 2 * 4);
     }
+    case VK_PWPW_MM: {
+        // two input tiles of th x 16 pixels x 64 channels, two intermediate tiles of
+        // th x 16 pixels x 64 channels
+        return 2 * v.th * 16 * 64 * e + 2 * v.th * 16 * 64 * e;
+    }
     case VK_DWPW_I8: {
         // two input tile buffers (16-byte chunks of 16 channels, whole 256-thread load
         // rounds) and two 4-row intermediate tiles of 1 KB per row
@@ -194,6 +202,11 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
         return 4 * mb * kbw + 16 * kbw + 28 + 5 * ppw + 2 * ((slots + nt - 1) / nt) + 36 + 24;
     }
+    case VK_PWPW_MM: {
+        // first-layer operands, 8 second-layer operands, 4 + 16 epilogue constants, the
+        // direct-load plan, operands and accumulators of the tile, addressing
+        return 8 + 32 + 8 + 32 + v.th * 2 / 4 * 8 + v.th * 8 + (v.th / 4) * 16 + 40;
+    }
     case VK_DWPW_I8: {
         // depthwise and pointwise operands, both epilogues' constants (4 + 16 channels),
         // the direct-load plan, operands of the input rows, accumulators, addressing
@@ -222,7 +235,8 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         *err = "problem pointer is NULL";
         return FCM_ERR_INVALID_ARG;
     }
-    if (p->kind != FCM_KIND_DWPW && p->kind != FCM_KIND_B2B && p->kind != FCM_KIND_PWDW) {
+    if (p->kind != FCM_KIND_DWPW && p->kind != FCM_KIND_B2B && p->kind != FCM_KIND_PWDW &&
+        p->kind != FCM_KIND_PWPW) {
         *err = "unknown kind";
         return FCM_ERR_INVALID_ARG;
     }
@@ -263,6 +277,28 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         *err = "tensor element counts must stay below 2^31";
         return FCM_ERR_UNSUPPORTED;
     }
+    if (p->kind == FCM_KIND_PWPW) {
+        // two 1x1 layers: no filter extent, stride or padding to choose
+        if (p->R != 1 || p->S != 1 || p->stride_h != 1 || p->stride_w != 1 || p->pad_h != 0 ||
+            p->pad_w != 0) {
+            *err = "a PW->PW module is two 1x1 layers: R = S = 1, stride 1, no padding";
+            return FCM_ERR_INVALID_ARG;
+        }
+        if (p->C % 8 || p->K % 8 || p->K1 % 8) {
+            *err = "channel counts must be multiples of 8 (16-byte NHWC vectors)";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        if (p->dtype == FCM_F32 || p->dtype == FCM_I8) {
+            *err = "the PW->PW kernels need 16-bit storage (fp16 or bf16)";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        const int64_t big = (int64_t)1 << 31;
+        if ((int64_t)p->N * p->H * p->W * std::max(std::max(p->C, p->K), p->K1) >= big) {
+            *err = "tensor element counts must stay below 2^31";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        return FCM_OK;
+    }
     if (p->R != 3 || p->S != 3) {
         *err = "only 3x3 first-layer filters have kernels";
         return FCM_ERR_UNSUPPORTED;
@@ -299,6 +335,22 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
 }
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
+    if (v.vkind == VK_PWPW_MM || p.kind == FCM_KIND_PWPW) {
+        if (v.vkind != VK_PWPW_MM || p.kind != FCM_KIND_PWPW || v.dtype != p.dtype) {
+            if (why) *why = "variant is for another module kind or storage type";
+            return false;
+        }
+        if (p.C > 64 || p.K1 > 64) {
+            if (why) *why = "PW->PW variant takes at most 64 input and 64 intermediate channels";
+            return false;
+        }
+        const int64_t M = (int64_t)p.N * p.H * p.W;
+        if (M * p.C * 2 >= ((int64_t)1 << 31) || M * p.K * 2 >= ((int64_t)1 << 30)) {
+            if (why) *why = "PW->PW variant addresses inputs below 2 GiB and outputs below 1 GiB";
+            return false;
+        }
+        return true;
+    }
     if (v.vkind == VK_DWPW_I8 || p.dtype == FCM_I8) {
         if (v.vkind != VK_DWPW_I8 || p.dtype != FCM_I8 || p.kind != FCM_KIND_DWPW) {
             if (why) *why = "variant is for another module kind or storage type";
@@ -598,6 +650,55 @@ Estimate estimate_pwdw(const VariantDesc& v, const fcm_problem& p, const fcm_dev
     return r;
 }
 
+// PW->PW module: tiles of th x 16 consecutive pixels, both layers on the matrix cores, the
+// first layer recomputed once per 64-channel output tile; Eq. 2 for each layer with the
+// intermediate removed from the global-memory accesses (FCM paper Sec. IV-B).
+Estimate estimate_pwpw(const VariantDesc& v, const fcm_problem& p, const fcm_device_spec& d) {
+    Estimate r{};
+    const int e = elem_bytes(p.dtype);
+    const int lds = variant_lds_bytes(v);
+    const int vg = (variant_vgpr_estimate(v) + 7) / 8 * 8;
+    const int occ_lds = lds > 0 ? d.lds_bytes_per_cu / lds : 8;
+    const int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ);
+    int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd);
+    occ = std::min(occ, std::max(v.occ, 1));
+    if (lds > d.lds_bytes_per_wg) occ = 0;
+    r.wgs_per_cu = occ;
+    const int64_t M = (int64_t)p.N * p.H * p.W;
+    const int mp = v.th * v.tw;
+    const int64_t ptiles = cdiv(M, mp);
+    const int ktiles = (int)cdiv(p.K, v.kt);
+    r.num_tiles = (int)std::min<int64_t>(ptiles * ktiles, INT32_MAX);
+    const int64_t grid = persistent_grid(ptiles, ktiles, (int64_t)d.num_cus * std::max(occ, 1));
+    r.grid = (int)grid;
+    const int64_t x_bytes = M * p.C * e, y_bytes = M * p.K * e;
+    const int64_t w_bytes = ((int64_t)p.K1 * p.C + (int64_t)std::min(v.kt, p.K) * p.K1) * e;
+    r.pred = x_bytes * ktiles + y_bytes + grid * (w_bytes + 4LL * 2 * (p.K1 + v.kt));
+    r.waste = (double)ktiles * ((double)ptiles * mp / (double)M);
+    const double alg = (double)x_bytes + y_bytes + ((double)p.K1 * p.C + (double)p.K * p.K1) * e;
+    const double t_mat = (double)ptiles * mp *
+                         (2.0 * 64 * 64 * ktiles + 2.0 * 64 * std::min(v.kt, p.K) * ktiles) /
+                         d.mfma_f16_flops;
+    const double t_vec = (double)ptiles * mp * 3.0 * (64.0 * ktiles + p.K) /
+                         (d.valu_f32_flops / 2.0);
+    const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
+    r.t_us = std::max(std::max(alg / d.hbm_bytes_per_s, (double)r.pred / (4.0 * d.hbm_bytes_per_s)),
+                      std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+    const bool fits = lds <= d.lds_bytes_per_wg && occ > 0;
+    r.feasible = fits && r.num_tiles >= d.num_cus;
+    if (!r.feasible) {
+        r.gma = INFINITY;
+    } else {
+        // first layer's input once per weight tile of the second layer, the first
+        // layer's filters once per output tile, the second layer's likewise, output once
+        const double w1 = (double)p.K1 * p.C * e, w2 = (double)p.K * p.K1 * e;
+        const double ofm_tile = (double)mp * std::min(v.kt, p.K) * e;
+        r.gma = (double)x_bytes * ceil(w2 / ((double)std::min(v.kt, p.K) * p.K1 * e)) +
+                ceil((double)y_bytes / ofm_tile) * (w1 + w2) + (double)y_bytes;
+    }
+    return r;
+}
+
 // Layer-by-layer PW->DW: the 1x1 kernel over every input pixel writes the intermediate,
 // the depthwise kernel reads it back.  Bytes with the baseline kernels' tilings, and
 // Eq. 2 (PW) + Eq. 3 (DW).
@@ -714,8 +815,9 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         if (forced >= 0 && i != forced) continue;
         const VariantDesc& v = kVariants[i];
         if (!variant_runs(v, *p, forced >= 0 ? &why : nullptr)) continue;
-        Estimate e = p->kind == FCM_KIND_PWDW ? estimate_pwdw(v, *p, d, Ho, Wo)
-                                              : estimate(v, *p, d, Ho, Wo);
+        Estimate e = p->kind == FCM_KIND_PWDW   ? estimate_pwdw(v, *p, d, Ho, Wo)
+                     : p->kind == FCM_KIND_PWPW ? estimate_pwpw(v, *p, d)
+                                                : estimate(v, *p, d, Ho, Wo);
         if (e.wgs_per_cu <= 0) {
             if (forced >= 0) why = "variant's LDS or registers exceed the device budget";
             continue;
@@ -765,6 +867,31 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     pl.grid = be.grid;
     pl.lds_bytes = variant_lds_bytes(v);
     const int e = elem_bytes(p->dtype);
+    if (p->kind == FCM_KIND_PWPW) {
+        // first layer [K1][C] as is; second [K][K1] and its blocked copy
+        const int64_t M = (int64_t)p->N * p->H * p->W;
+        pl.w1_packed_bytes = (int64_t)p->K1 * p->C * e;
+        pl.w2_packed_bytes = ((int64_t)p->K * p->K1 + pw_blocked_elems(p->K, p->K1)) * e;
+        pl.workspace_bytes = M * p->K1 * e;
+        pl.alg_bytes_fused = M * p->C * e + M * p->K * e + (int64_t)p->K1 * p->C * e +
+                             (int64_t)p->K * p->K1 * e + (int64_t)4 * 2 * (p->K1 + p->K);
+        pl.alg_bytes_unfused = pl.alg_bytes_fused + 2 * pl.workspace_bytes;
+        pl.pred_bytes_fused = be.pred;
+        // layer by layer: each 1x1 layer with the baseline's tiling (Eq. 2 for each)
+        const int mt = lbl::PW_MT16, kt = lbl::PW_KT16;
+        const int64_t l1 = M * p->C * e * cdiv(p->K1, kt) + cdiv(M, mt) * p->K1 * p->C * e +
+                           pl.workspace_bytes;
+        const int64_t l2 = pl.workspace_bytes * cdiv(p->K, kt) + cdiv(M, mt) * p->K * p->K1 * e +
+                           M * p->K * e;
+        pl.pred_bytes_unfused = l1 + l2;
+        pl.gma_paper_fused = be.gma;
+        pl.gma_paper_unfused = (double)(l1 + l2);
+        pl.fuse = (be.gma < pl.gma_paper_unfused) ? 1 : 0;
+        pl.pred_us_fused = be.t_us;
+        pl.flops = 2.0 * M * p->C * p->K1 + 2.0 * M * p->K1 * p->K;
+        *out = pl;
+        return FCM_OK;
+    }
     if (p->kind == FCM_KIND_PWDW) {
         // first layer: pointwise [K1][C] as is; second: depthwise [R*S][K1]
         pl.w1_packed_bytes = (int64_t)p->K1 * p->C * e;

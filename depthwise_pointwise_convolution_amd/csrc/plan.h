@@ -17,7 +17,8 @@ enum VKind {
     VK_B2B_MM = 5,
     VK_DWPW_MMW = 6,
     VK_PWDW_MM = 7,
-    VK_DWPW_I8 = 8
+    VK_DWPW_I8 = 8,
+    VK_PWPW_MM = 9
 };
 
 struct VariantDesc {

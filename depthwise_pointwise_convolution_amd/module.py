@@ -9,8 +9,8 @@ from typing import Optional
 import torch
 
 from . import (fcm_b2b_conv_fwd, fcm_conv_fwd, fcm_dw_fwd, fcm_dwpw_fwd, fcm_pack_weights,
-               fcm_plan, fcm_plan_variant, fcm_pw_fwd, fcm_pwdw_fwd, fcm_tune, problem,
-               FCM_KIND_B2B, FCM_KIND_PWDW)
+               fcm_plan, fcm_plan_variant, fcm_pw_fwd, fcm_pwdw_fwd, fcm_pwpw_fwd, fcm_tune,
+               problem, FCM_KIND_B2B, FCM_KIND_PWDW, FCM_KIND_PWPW)
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
                 "i8": torch.int8}
@@ -24,8 +24,8 @@ class FcmModule:
     def __init__(self, kind: str, dtype: str, N: int, H: int, W: int, C: int, K: int,
                  K1: Optional[int], stride: int, pad: int, act1: str, act2: str, w1, w2,
                  scale1=None, bias1=None, scale2=None, bias2=None,
-                 variant: Optional[int] = None, stream=None):
-        self.prob = problem(kind, dtype, N, H, W, C, K, K1, stride=stride, pad=pad,
+                 variant: Optional[int] = None, stream=None, R: int = 3, S: int = 3):
+        self.prob = problem(kind, dtype, N, H, W, C, K, K1, R=R, S=S, stride=stride, pad=pad,
                             act1=act1, act2=act2)
         self.plan = fcm_plan(self.prob) if variant is None else fcm_plan_variant(self.prob,
                                                                                  variant)
@@ -44,13 +44,17 @@ class FcmModule:
         self.pwdw = self.prob.kind == FCM_KIND_PWDW
         if self.pwdw:  # the intermediate is the pointwise layer's output
             self.t_shape = (N, H, W, K1)
+        # a PW->PW module runs its layers through the first-conv / 1x1 entry points
+        self.pwpw = self.prob.kind == FCM_KIND_PWPW
+        self.b2b = self.b2b or self.pwpw
 
     def new_output(self, device) -> torch.Tensor:
         return torch.empty(self.out_shape, dtype=self.tdtype, device=device)
 
     def fused(self, x, y=None, stream=None) -> torch.Tensor:
         y = self.new_output(x.device) if y is None else y
-        fn = fcm_b2b_conv_fwd if self.b2b else fcm_pwdw_fwd if self.pwdw else fcm_dwpw_fwd
+        fn = (fcm_pwpw_fwd if self.pwpw else fcm_b2b_conv_fwd if self.b2b else
+              fcm_pwdw_fwd if self.pwdw else fcm_dwpw_fwd)
         fn(self.plan, x, self.w1p, self.s1, self.b1, self.w2p, self.s2, self.b2, y, stream)
         return y
 
@@ -97,4 +101,4 @@ def from_workload(wl, tensors: dict, device="cuda", variant=None) -> "FcmModule"
                      wl.act2, dev(tensors["w1"], tdt), dev(tensors["w2"], tdt),
                      dev(tensors["scale1"], torch.float32), dev(tensors["bias1"], torch.float32),
                      dev(tensors["scale2"], torch.float32), dev(tensors["bias2"], torch.float32),
-                     variant=variant)
+                     variant=variant, R=wl.R, S=wl.S)

@@ -13,7 +13,9 @@
  * Sec. II-D, Fig. 3(b), and Sec. III) runs the other order: a pointwise layer expands
  * the channels and a depthwise 3x3 layer filters its output, the intermediate again
  * kept on chip; a tile of outputs recomputes the intermediate over its whole input
- * window, the overlap with neighbouring tiles included.  Each convolution is followed
+ * window, the overlap with neighbouring tiles included.  The PW->PW module (the PWPW
+ * fusion case, FCM paper Sec. III, Table II) chains two 1x1 layers per pixel.  Each
+ * convolution is followed
  * by a per-channel scale, bias and ReLU/ReLU6 epilogue (conv -> normalisation ->
  * activation, FCM paper Sec. III-A).
  * Unfused layer-by-layer entry points, with the same stage code, serve as the
@@ -71,7 +73,9 @@ typedef enum { FCM_ACT_NONE = 0, FCM_ACT_RELU = 1, FCM_ACT_RELU6 = 2 } fcm_act;
 typedef enum {
     FCM_KIND_DWPW = 0, /* depthwise RxS conv (C -> C) then pointwise 1x1 (C -> K) */
     FCM_KIND_B2B = 1,  /* standard RxS conv (C -> K1) then 1x1 conv (K1 -> K) */
-    FCM_KIND_PWDW = 2  /* pointwise 1x1 (C -> K1) then depthwise RxS conv (K1 -> K1) */
+    FCM_KIND_PWDW = 2, /* pointwise 1x1 (C -> K1) then depthwise RxS conv (K1 -> K1) */
+    FCM_KIND_PWPW = 3  /* pointwise 1x1 (C -> K1) then pointwise 1x1 (K1 -> K); R = S = 1,
+                          stride 1, no padding */
 } fcm_kind;
 
 /* The problem, in the pages' terms: NHWC input feature maps, per-channel depthwise
@@ -205,6 +209,7 @@ const char* fcm_variant_name(int32_t variant);
  *   DWPW in FCM_I8: w1 as above; w2 [K][C] copied, then 64 x 64 blocks (K tile of 64
  *         output channels, four 16-row operands) in the int8 matrix-operand order
  *         (K rounded up to 64, C <= 64, zero filled)
+ *   PWPW: w1_src [K1][C] copied as is; w2_src [K][K1] copied, then blocked as for DWPW
  *   PWDW: w1_src pointwise [K1][C]        -> w1_dst [K1][C]       (copied as is)
  *         w2_src depthwise [K1][R][S]     -> w2_dst [R*S][K1]     (channel fastest)
  * Sizes in bytes are plan->w1_packed_bytes / w2_packed_bytes.  Either pair may be
@@ -240,6 +245,14 @@ fcm_status fcm_pwdw_fwd(const fcm_plan_t* plan, const void* x, const void* w_pw,
                         const float* scale1, const float* bias1, const void* w_dw,
                         const float* scale2, const float* bias2, void* y, void* stream);
 
+/* Fused PW -> PW module (FCM PWPW).  x: [N][H][W][C]; w1: packed [K1][C] (copied as
+ * is); scale1/bias1: [K1] or NULL; w2: packed [K][K1], then for fp16/bf16 its blocked
+ * copy (as for DWPW's pointwise filters); scale2/bias2: [K] or NULL; y: [N][H][W][K].
+ * plan->prob.kind must be FCM_KIND_PWPW. */
+fcm_status fcm_pwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
+                        const float* scale1, const float* bias1, const void* w2,
+                        const float* scale2, const float* bias2, void* y, void* stream);
+
 /* Layer-by-layer baseline, first layer of a DWPW plan: depthwise conv + epilogue 1,
  * writing the intermediate t: [N][Ho][Wo][C] (plan->workspace_bytes bytes).
  * For a PWDW plan: the second layer, depthwise conv + epilogue (scale/bias [K1]) over
@@ -256,7 +269,8 @@ fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
                       const float* scale2, const float* bias2, void* y, void* stream);
 
 /* Layer-by-layer baseline, first layer of a B2B plan: standard conv + epilogue 1,
- * writing t: [N][Ho][Wo][K1]. */
+ * writing t: [N][Ho][Wo][K1].  For a PWPW plan: the first 1x1 layer + epilogue 1 with the
+ * packed [K1][C] filters, writing t: [N][H][W][K1] (the second layer is fcm_pw_fwd). */
 fcm_status fcm_conv_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
                         const float* scale1, const float* bias1, void* t, void* stream);
 

@@ -33,12 +33,14 @@ def oracle_kwargs(wl, inp) -> dict:
 
 
 def oracle_full(wl, inp) -> np.ndarray:
-    fn = {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw}[wl.kind]
+    fn = {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw,
+          "pwpw": oracle.pwpw}[wl.kind]
     return fn(inp["x"], inp["w1"], inp["w2"], **oracle_kwargs(wl, inp))
 
 
 def oracle_rows(wl, inp, pix) -> np.ndarray:
-    fn = {"dwpw": oracle.dwpw_at, "b2b": oracle.b2b_at, "pwdw": oracle.pwdw_at}[wl.kind]
+    fn = {"dwpw": oracle.dwpw_at, "b2b": oracle.b2b_at, "pwdw": oracle.pwdw_at,
+          "pwpw": oracle.pwpw_at}[wl.kind]
     return fn(inp["x"], inp["w1"], inp["w2"], pix, **oracle_kwargs(wl, inp))
 
 
@@ -68,7 +70,13 @@ def int_inputs(wl, seed: int) -> dict:
     if wl.kind == "pwdw":
         return _int_inputs_pwdw(wl, rng, x)
     n1 = wl.C if wl.kind == "dwpw" else wl.K1
-    if wl.kind == "dwpw":
+    if wl.kind == "pwpw":
+        w1 = np.zeros((wl.K1, wl.C))
+        for k in range(wl.K1):
+            idx = rng.choice(wl.C, size=min(6, wl.C), replace=False)
+            w1[k, idx] = rng.choice([-1.0, 1.0], size=idx.size)
+        acc1 = 6 * 2
+    elif wl.kind == "dwpw":
         w1 = rng.integers(-1, 2, size=(wl.C, 3, 3)).astype(np.float64)
         acc1 = 9 * 2       # |first-layer sum| <= 9 taps * |x|
     else:
@@ -116,8 +124,8 @@ def all_variants_for(wl):
     """Indices of every compiled variant able to run the workload."""
     import depthwise_pointwise_convolution_amd as F
     p = F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
-                  None if wl.kind == "dwpw" else wl.K1, stride=wl.stride, pad=wl.pad,
-                  act1=wl.act1, act2=wl.act2)
+                  None if wl.kind == "dwpw" else wl.K1, R=wl.R, S=wl.S, stride=wl.stride,
+                  pad=wl.pad, act1=wl.act1, act2=wl.act2)
     out = []
     for v in range(F.fcm_num_variants()):
         try:
@@ -138,6 +146,7 @@ REDUCED = {
     "b2b_f16_32x56x56_c64": dict(N=2, H=23, W=37),
     "pwdw_f16_32x56x56_c24_k144": dict(N=2, H=29, W=37),
     "mbv1i8_i8_8x112x112_c32_k64": dict(N=2, H=29, W=37),
+    "pwpw_f16_32x56x56_c64_k32_k64": dict(N=2, H=29, W=37),
     "pwdw_f16_32x112x112_c16_k96_s2": dict(N=2, H=45, W=57),
 }
 

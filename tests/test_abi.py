@@ -69,8 +69,8 @@ def test_library_has_no_undefined_own_symbols():
 
 def _problem(F, wl):
     return F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
-                     None if wl.kind == "dwpw" else wl.K1, stride=wl.stride, pad=wl.pad,
-                     act1=wl.act1, act2=wl.act2)
+                     None if wl.kind == "dwpw" else wl.K1, R=wl.R, S=wl.S, stride=wl.stride,
+                     pad=wl.pad, act1=wl.act1, act2=wl.act2)
 
 
 def _spec(F):
@@ -97,7 +97,10 @@ def test_plan_integers_match_oracle_accounting(name):
     # tiling and launch shape are self-consistent
     name_v = F.fcm_variant_name(pl.variant)
     assert name_v
-    ptiles = wl.N * math.ceil(wl.Ho / pl.tile_h) * math.ceil(wl.Wo / pl.tile_w)
+    if wl.kind == "pwpw":  # runs of tile_h x tile_w consecutive pixels (no spatial tiles)
+        ptiles = math.ceil(wl.N * wl.H * wl.W / (pl.tile_h * pl.tile_w))
+    else:
+        ptiles = wl.N * math.ceil(wl.Ho / pl.tile_h) * math.ceil(wl.Wo / pl.tile_w)
     ktiles = math.ceil(wl.K / pl.k_tile)
     assert pl.num_tiles == ptiles * ktiles
     assert pl.grid % ktiles == 0 and 0 < pl.grid <= max(pl.num_tiles, ktiles)
@@ -314,7 +317,9 @@ def test_forced_variants_cover_every_compiled_kernel():
         fcm_inputs.Workload("p", "pwdw", dt, N=2, H=17, W=23, C=c, K=k1, K1=k1, stride=s)
         for dt in ("f16", "bf16") for c in (24, 64) for k1 in (96, 144) for s in (1, 2)] + [
         fcm_inputs.Workload("q", "dwpw", "i8", N=2, H=17, W=23, C=c, K=k, K1=c, stride=s)
-        for c in (32, 64) for k in (64, 112) for s in (1, 2)]
+        for c in (32, 64) for k in (64, 112) for s in (1, 2)] + [
+        fcm_inputs.Workload("r", "pwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=k1, R=1, S=1, pad=0)
+        for dt in ("f16", "bf16") for c in (32, 64) for k1 in (32, 64) for k in (64, 136)]
     for wl in shapes:
         prob = _problem(F, wl)
         for v in range(F.fcm_num_variants()):

@@ -82,6 +82,9 @@ CASES_INT = [
     ("dwpw", "i8", 2, 9, 21, 32, 64, None, 1, 1, "relu", "relu", True),
     ("dwpw", "i8", 1, 13, 15, 64, 128, None, 2, 1, "none", "relu6", True),
     ("dwpw", "i8", 2, 7, 7, 16, 48, None, 1, 0, "relu6", "none", False),
+    ("pwpw", "f16", 2, 9, 21, 64, 64, 32, 1, 0, "relu6", "relu6", True),
+    ("pwpw", "bf16", 1, 11, 17, 40, 136, 56, 1, 0, "none", "relu", True),
+    ("pwpw", "f16", 3, 5, 7, 24, 24, 64, 1, 0, "relu", "none", False),
     ("pwdw", "f16", 2, 9, 21, 24, 144, 144, 1, 1, "relu6", "relu6", True),
     ("pwdw", "bf16", 1, 11, 17, 64, 48, 48, 1, 1, "none", "relu", False),
     ("pwdw", "f16", 2, 13, 15, 16, 96, 96, 2, 1, "relu", "relu6", True),
@@ -93,9 +96,11 @@ CASES_INT = [
 
 def _int_workload(case):
     kind, dtype, N, H, W, C, K, K1, stride, pad, act1, act2, epi = case
+    rs = 1 if kind == "pwpw" else 3
     return fcm_inputs.Workload("int", kind, dtype, N=N, H=H, W=W, C=C, K=K,
                                K1=C if K1 is None else K1, stride=stride, pad=pad, act1=act1,
-                               act2=act2, scale1=epi, bias1=epi, scale2=epi, bias2=epi)
+                               act2=act2, scale1=epi, bias1=epi, scale2=epi, bias2=epi, R=rs,
+                               S=rs)
 
 
 @pytest.mark.parametrize("case", CASES_INT, ids=lambda c: "-".join(map(str, c[:10])))
