@@ -37,7 +37,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KDIR = "depthwise_pointwise_convolution_amd/csrc/kernels/"
 # source file of each fused kernel family (by variant-name prefix) and the headers they share
 KERNEL_FILES = [("dwpw_i8_", "dwpw_i8.hip"), ("mmw_", "dwpw_mmw.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
-                ("dwpw_", "dwpw.hip"), ("b2b_", "b2b.hip"), ("pwdw_", "pwdw_mm.hip")]
+                ("dwpw_", "dwpw.hip"), ("b2b_", "b2b.hip"), ("pwdw_", "pwdw_mm.hip"),
+                ("pwpw_", "pwpw_mm.hip")]
 SHARED_SOURCES = ["mm_common.h", "stages.h", "common.h"]
 
 
@@ -169,7 +170,8 @@ def cpu_baseline(wl, budget_s: float):
     t_all = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw}[wl.kind](
+        {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw,
+         "pwpw": oracle.pwpw}[wl.kind](
             inp["x"], inp["w1"], inp["w2"], **kw)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_all >= budget_s or len(times) >= 50:
