@@ -86,8 +86,21 @@ class fcm_plan_t(ctypes.Structure):
         return d
 
 
+FCM_LAYER_DW, FCM_LAYER_PW = 0, 1
+
+
+class fcm_layer(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in ("type", "C", "K", "stride", "act")]
+
+
+class fcm_chain_group(ctypes.Structure):
+    _fields_ = [("first", _i32), ("count", _i32), ("kind", _i32), ("variant", _i32),
+                ("gma", _f64)]
+
+
 # every symbol include/fcm.h declares
 EXPORTS = ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan", "fcm_plan_variant",
+           "fcm_plan_chain",
            "fcm_num_variants", "fcm_variant_name", "fcm_pack_weights", "fcm_dwpw_fwd",
            "fcm_tune",
            "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_pwpw_fwd", "fcm_dw_fwd", "fcm_pw_fwd",
@@ -116,6 +129,10 @@ def lib() -> ctypes.CDLL:
             L.fcm_plan.argtypes = [P(fcm_problem), P(fcm_device_spec), P(fcm_plan_t)]
             L.fcm_plan_variant.argtypes = [P(fcm_problem), P(fcm_device_spec), _i32,
                                            P(fcm_plan_t)]
+            L.fcm_plan_chain.argtypes = [P(fcm_layer), _i32, _i32, _i32, _i32, _i32,
+                                         P(fcm_device_spec), P(fcm_chain_group), P(_i32),
+                                         P(_f64), P(_f64)]
+            L.fcm_plan_chain.restype = ctypes.c_int
             L.fcm_num_variants.restype = _i32
             L.fcm_num_variants.argtypes = []
             L.fcm_variant_name.restype = ctypes.c_char_p
@@ -213,6 +230,28 @@ def fcm_plan_variant(prob: fcm_problem, variant: int,
     _check(lib().fcm_plan_variant(ctypes.byref(prob), ctypes.byref(spec) if spec else None,
                                   variant, ctypes.byref(out)), "fcm_plan_variant")
     return out
+
+
+def fcm_plan_chain(layers, N: int, H: int, W: int, dtype="f16",
+                   spec: Optional[fcm_device_spec] = None):
+    """FusePlanner over a chain of layers given as (type, C, K, stride, act) tuples with type
+    "dw" or "pw".  Returns (groups, gma_chain, gma_layer_by_layer); each group is a dict
+    with first, count, kind (-1: a single layer), variant and gma."""
+    n = len(layers)
+    arr = (fcm_layer * n)()
+    for i, (t, C, K, s, act) in enumerate(layers):
+        arr[i].type = {"dw": FCM_LAYER_DW, "pw": FCM_LAYER_PW}[t] if isinstance(t, str) else t
+        arr[i].C, arr[i].K, arr[i].stride = C, K, s
+        arr[i].act = ACT_CODES[act] if isinstance(act, str) else act
+    out = (fcm_chain_group * n)()
+    ng, gc, gl = _i32(), _f64(), _f64()
+    _check(lib().fcm_plan_chain(arr, n, N, H, W,
+                                DTYPE_CODES[dtype] if isinstance(dtype, str) else dtype,
+                                ctypes.byref(spec) if spec else None, out, ctypes.byref(ng),
+                                ctypes.byref(gc), ctypes.byref(gl)), "fcm_plan_chain")
+    groups = [{"first": out[i].first, "count": out[i].count, "kind": out[i].kind,
+               "variant": out[i].variant, "gma": out[i].gma} for i in range(ng.value)]
+    return groups, gc.value, gl.value
 
 
 def fcm_num_variants() -> int:

@@ -261,6 +261,18 @@ fcm_status fcm_plan_variant(const fcm_problem* prob, const fcm_device_spec* spec
     return s == FCM_OK ? ok() : fail(s, err);
 }
 
+fcm_status fcm_plan_chain(const fcm_layer* layers, int32_t n, int32_t N, int32_t H, int32_t W,
+                          int32_t dtype, const fcm_device_spec* spec, fcm_chain_group* groups,
+                          int32_t* ngroups, double* gma_chain, double* gma_layer_by_layer) {
+    std::string err;
+    int ng = 0;
+    const fcm_status s = plan_chain(layers, n, N, H, W, dtype, spec, groups, &ng, gma_chain,
+                                    gma_layer_by_layer, &err);
+    if (s != FCM_OK) return fail(s, err);
+    *ngroups = ng;
+    return ok();
+}
+
 int32_t fcm_num_variants(void) { return kNumVariants; }
 
 const char* fcm_variant_name(int32_t variant) {

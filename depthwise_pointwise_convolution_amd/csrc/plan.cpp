@@ -28,6 +28,8 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <cmath>
+#include <vector>
 
 #include "lbl_tiles.h"
 
@@ -956,6 +958,154 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
                    ? 2.0 * P * p->K1 * p->C * p->R * p->S + 2.0 * P * p->K1 * p->K
                    : 2.0 * P * p->C * p->R * p->S + 2.0 * P * p->C * p->K;
     *out = pl;
+    return FCM_OK;
+}
+
+namespace {
+
+// Layer-by-layer estimate of one layer alone (the pages' Eq. 3 for a depthwise layer,
+// Eq. 2 for a pointwise layer), with the baseline kernels' tilings.
+double single_layer_gma(const fcm_layer& l, int N, int H, int W, int e) {
+    if (l.type == FCM_LAYER_DW) {
+        const int Ho = conv_out(H, 1, 3, l.stride), Wo = conv_out(W, 1, 3, l.stride);
+        const int th = lbl::DW_TH, tw = lbl::DW_TW;
+        const double ifm = (double)N * H * W * l.C * e, ofm = (double)N * Ho * Wo * l.C * e;
+        const double overlap = eq1_overlap(W, H, tw * l.stride, th * l.stride, 3, l.stride);
+        return 2.0 * l.C * overlap * N * e + ifm + ofm +
+               ceil((double)Ho * Wo / (double)(th * tw)) * 9.0 * l.C * e;
+    }
+    const int mt = e == 4 ? lbl::PW_MT32 : lbl::PW_MT16, kt = e == 4 ? lbl::PW_KT32 : lbl::PW_KT16;
+    const double ifm = (double)N * H * W * l.C * e, ofm = (double)N * H * W * l.K * e;
+    const double w = (double)l.K * l.C * e;
+    return ceil(w / ((double)std::min(kt, l.K) * l.C * e)) * ifm + ofm +
+           ceil(ofm / ((double)mt * std::min(kt, l.K) * e)) * w;
+}
+
+}  // namespace
+
+fcm_status plan_chain(const fcm_layer* layers, int n, int N, int H, int W, int dtype,
+                      const fcm_device_spec* spec, fcm_chain_group* groups, int* ngroups,
+                      double* gma_chain, double* gma_lbl, std::string* err) {
+    if (!layers || !groups || !ngroups || !gma_chain || !gma_lbl) {
+        *err = "NULL argument";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (n < 1 || N <= 0 || H <= 0 || W <= 0) {
+        *err = "need at least one layer and a positive input extent";
+        return FCM_ERR_INVALID_ARG;
+    }
+    const int e = elem_bytes(dtype);
+    // per-layer input extents, validity
+    std::vector<int> hin(n + 1), win(n + 1);
+    hin[0] = H;
+    win[0] = W;
+    for (int i = 0; i < n; ++i) {
+        const fcm_layer& l = layers[i];
+        if (l.type != FCM_LAYER_DW && l.type != FCM_LAYER_PW) {
+            *err = "unknown layer type at layer " + std::to_string(i);
+            return FCM_ERR_INVALID_ARG;
+        }
+        if (l.C <= 0 || l.K <= 0 || (i > 0 && l.C != layers[i - 1].K)) {
+            *err = "channel counts do not chain at layer " + std::to_string(i);
+            return FCM_ERR_INVALID_ARG;
+        }
+        if (l.type == FCM_LAYER_DW && (l.K != l.C || (l.stride != 1 && l.stride != 2))) {
+            *err = "a depthwise layer keeps its channels and has stride 1 or 2 (layer " +
+                   std::to_string(i) + ")";
+            return FCM_ERR_INVALID_ARG;
+        }
+        if (l.type == FCM_LAYER_PW && l.stride != 1) {
+            *err = "a pointwise layer has stride 1 (layer " + std::to_string(i) + ")";
+            return FCM_ERR_INVALID_ARG;
+        }
+        if (l.C % 8 || l.K % 8) {
+            *err = "channel counts must be multiples of 8 (layer " + std::to_string(i) + ")";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        hin[i + 1] = l.type == FCM_LAYER_DW ? conv_out(hin[i], 1, 3, l.stride) : hin[i];
+        win[i + 1] = l.type == FCM_LAYER_DW ? conv_out(win[i], 1, 3, l.stride) : win[i];
+    }
+    // candidate modules for each pair (i, i+1)
+    std::vector<double> single(n), pair(n, INFINITY);
+    std::vector<int> pkind(n, -1), pvar(n, -1);
+    for (int i = 0; i < n; ++i) single[i] = single_layer_gma(layers[i], N, hin[i], win[i], e);
+    for (int i = 0; i + 1 < n; ++i) {
+        const fcm_layer &a = layers[i], &b = layers[i + 1];
+        fcm_problem p;
+        memset(&p, 0, sizeof(p));
+        p.dtype = dtype;
+        p.N = N;
+        p.H = hin[i];
+        p.W = win[i];
+        p.act1 = a.act;
+        p.act2 = b.act;
+        if (a.type == FCM_LAYER_DW && b.type == FCM_LAYER_PW) {
+            p.kind = FCM_KIND_DWPW;
+            p.C = p.K1 = a.C;
+            p.K = b.K;
+            p.R = p.S = 3;
+            p.stride_h = p.stride_w = a.stride;
+            p.pad_h = p.pad_w = 1;
+        } else if (a.type == FCM_LAYER_PW && b.type == FCM_LAYER_DW) {
+            p.kind = FCM_KIND_PWDW;
+            p.C = a.C;
+            p.K1 = p.K = a.K;
+            p.R = p.S = 3;
+            p.stride_h = p.stride_w = b.stride;
+            p.pad_h = p.pad_w = 1;
+        } else if (a.type == FCM_LAYER_PW && b.type == FCM_LAYER_PW) {
+            p.kind = FCM_KIND_PWPW;
+            p.C = a.C;
+            p.K1 = a.K;
+            p.K = b.K;
+            p.R = p.S = 1;
+            p.stride_h = p.stride_w = 1;
+        } else {
+            continue;  // DW -> DW: no module
+        }
+        fcm_plan_t pl;
+        std::string e2;
+        if (plan_problem(&p, spec, -1, &pl, &e2) != FCM_OK) continue;  // no kernel
+        if (!std::isfinite(pl.gma_paper_fused)) continue;               // infeasible tiling
+        pair[i] = pl.gma_paper_fused;
+        pkind[i] = p.kind;
+        pvar[i] = pl.variant;
+    }
+    // dynamic program: best[i] = cheapest schedule of layers 0 .. i-1 (then fewest groups)
+    std::vector<double> best(n + 1, INFINITY);
+    std::vector<int> cnt(n + 1, 0), take(n + 1, 1);
+    best[0] = 0.0;
+    for (int i = 1; i <= n; ++i) {
+        best[i] = best[i - 1] + single[i - 1];
+        cnt[i] = cnt[i - 1] + 1;
+        take[i] = 1;
+        if (i >= 2 && std::isfinite(pair[i - 2])) {
+            const double c = best[i - 2] + pair[i - 2];
+            if (c < best[i] || (c == best[i] && cnt[i - 2] + 1 < cnt[i])) {
+                best[i] = c;
+                cnt[i] = cnt[i - 2] + 1;
+                take[i] = 2;
+            }
+        }
+    }
+    // read the schedule back
+    std::vector<fcm_chain_group> sched;
+    for (int i = n; i > 0; i -= take[i]) {
+        fcm_chain_group g;
+        g.count = take[i];
+        g.first = i - take[i];
+        g.kind = take[i] == 2 ? pkind[i - 2] : -1;
+        g.variant = take[i] == 2 ? pvar[i - 2] : -1;
+        g.gma = take[i] == 2 ? pair[i - 2] : single[i - 1];
+        sched.push_back(g);
+    }
+    std::reverse(sched.begin(), sched.end());
+    for (size_t k = 0; k < sched.size(); ++k) groups[k] = sched[k];
+    *ngroups = (int)sched.size();
+    *gma_chain = best[n];
+    double lbl_total = 0.0;
+    for (int i = 0; i < n; ++i) lbl_total += single[i];
+    *gma_lbl = lbl_total;
     return FCM_OK;
 }
 

@@ -54,6 +54,11 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err);
 // Whether variant v can run problem p (kind, type, stride, channel limits).
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why);
 
+// FusePlanner over a chain of layers (see fcm_plan_chain in fcm.h).
+fcm_status plan_chain(const fcm_layer* layers, int n, int N, int H, int W, int dtype,
+                      const fcm_device_spec* spec, fcm_chain_group* groups, int* ngroups,
+                      double* gma_chain, double* gma_lbl, std::string* err);
+
 // Fill *out for problem p with variant `forced` (or the cheapest one if forced < 0).
 fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int forced,
                         fcm_plan_t* out, std::string* err);

@@ -187,6 +187,42 @@ fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_
                     const float* bias2, void* const* y, void* stream, int32_t iters,
                     fcm_plan_t* out);
 
+/* A layer of a chain (a linear network of depthwise and pointwise layers, MobileNet-style;
+ * FCM paper Sec. IV, Fig. 4): shapes only. */
+typedef enum { FCM_LAYER_DW = 0, FCM_LAYER_PW = 1 } fcm_layer_type;
+typedef struct {
+    int32_t type;   /* fcm_layer_type: depthwise 3x3 (padding 1) or pointwise 1x1 */
+    int32_t C, K;   /* input / output channels (depthwise: K == C) */
+    int32_t stride; /* depthwise: 1 or 2; pointwise: 1 */
+    int32_t act;    /* fcm_act after the layer's scale/bias */
+} fcm_layer;
+
+/* One group of the chain's schedule: a single layer run by itself, or two consecutive
+ * layers run as one fused module. */
+typedef struct {
+    int32_t first;   /* index of the group's first layer */
+    int32_t count;   /* 1 (layer by layer) or 2 (a fused module) */
+    int32_t kind;    /* fcm_kind of the module; -1 for a single layer */
+    int32_t variant; /* the module's planned kernel variant; -1 for a single layer */
+    double gma;      /* estimated global memory accesses of the group, bytes */
+} fcm_chain_group;
+
+/* FusePlanner over a chain (FCM paper Sec. IV): for each pair of consecutive layers that
+ * forms a module with a kernel here (DW->PW, PW->DW, PW->PW; the pair's plan must be
+ * feasible), the fused estimate of fcm_plan (Eq. 4 style) competes with the two layers'
+ * layer-by-layer estimates (Eq. 3 for a depthwise layer, Eq. 2 for a pointwise layer, with
+ * the baseline kernels' tilings); a dynamic program over the chain picks the partition into
+ * single layers and fused pairs with the fewest estimated accesses (ties: fewer groups).
+ * The chain's input is N x H x W with layers[0].C channels; a layer's output extent is the
+ * next layer's input.  groups (capacity n) receives the schedule in order, *ngroups its
+ * length, *gma_chain its total and *gma_layer_by_layer the total with every layer alone.
+ * spec == NULL uses the MI355X defaults.  Host only.  Errors: INVALID_ARG (NULL outputs,
+ * n < 1, consecutive layers whose channel counts do not chain, a depthwise layer with
+ * K != C), UNSUPPORTED (a layer the library could not run alone: see fcm_plan). */
+fcm_status fcm_plan_chain(const fcm_layer* layers, int32_t n, int32_t N, int32_t H, int32_t W,
+                          int32_t dtype, const fcm_device_spec* spec, fcm_chain_group* groups,
+                          int32_t* ngroups, double* gma_chain, double* gma_layer_by_layer);
+
 /* Number of fused kernel variants compiled into the library, and a short name for
  * one of them ("" if out of range). */
 int32_t fcm_num_variants(void);

@@ -8,6 +8,8 @@ import math
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import fcm_inputs
@@ -331,3 +333,129 @@ def test_forced_variants_cover_every_compiled_kernel():
                 assert F.lib().fcm_last_error()
     assert used == set(range(F.fcm_num_variants())), sorted(set(range(
         F.fcm_num_variants())) - used)
+
+
+# ---------------------------------------------------------------------------------
+# FusePlanner over a chain of layers
+# ---------------------------------------------------------------------------------
+def _pair_problem(F, a, b, N, H, W, dtype):
+    """The module two consecutive layers form (None: no module kind for DW -> DW)."""
+    (ta, Ca, Ka, sa, aa), (tb, Cb, Kb, sb, ab) = a, b
+    if ta == "dw" and tb == "pw":
+        return F.problem("dwpw", dtype, N, H, W, Ca, Kb, Ca, stride=sa, pad=1, act1=aa, act2=ab)
+    if ta == "pw" and tb == "dw":
+        return F.problem("pwdw", dtype, N, H, W, Ca, Ka, Ka, stride=sb, pad=1, act1=aa, act2=ab)
+    if ta == "pw" and tb == "pw":
+        return F.problem("pwpw", dtype, N, H, W, Ca, Kb, Ka, R=1, S=1, stride=1, pad=0,
+                         act1=aa, act2=ab)
+    return None
+
+
+def _brute_force_chain(F, layers, N, H, W, dtype):
+    """Every partition of the chain into single layers and consecutive pairs, each single
+    layer priced by a one-layer chain and each pair by its own plan (when a kernel can run
+    it and its estimate is finite); returns the minimum total."""
+    n = len(layers)
+    exts = [(H, W)]
+    for t, C, K, s, act in layers:
+        h, w = exts[-1]
+        exts.append(((h - 1) // s + 1, (w - 1) // s + 1) if t == "dw" else (h, w))
+    single = [F.fcm_plan_chain([l], N, *exts[i], dtype)[1] for i, l in enumerate(layers)]
+    pair = []
+    for i in range(n - 1):
+        p = _pair_problem(F, layers[i], layers[i + 1], N, *exts[i], dtype)
+        cost = math.inf
+        if p is not None:
+            try:
+                pl = F.fcm_plan(p)
+                cost = pl.gma_paper_fused
+            except F.FcmError:
+                pass
+        pair.append(cost)
+    best = math.inf
+
+    def walk(i, acc):
+        nonlocal best
+        if i == n:
+            best = min(best, acc)
+            return
+        walk(i + 1, acc + single[i])
+        if i + 1 < n and math.isfinite(pair[i]):
+            walk(i + 2, acc + pair[i])
+    walk(0, 0.0)
+    return best, single, pair
+
+
+def _random_chain(rng, n):
+    layers, C = [], int(rng.choice([16, 24, 32, 64]))
+    for i in range(n):
+        if i > 0 and layers[-1][0] == "dw" or rng.random() < 0.5:
+            K = int(rng.choice([16, 24, 32, 48, 64, 96, 144]))
+            layers.append(("pw", C, K, 1, str(rng.choice(["relu6", "none"]))))
+            C = K
+        else:
+            layers.append(("dw", C, C, int(rng.choice([1, 2])), "relu6"))
+    return layers
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_chain_planner_is_the_optimal_partition(seed):
+    F = _lib()
+    rng = np.random.default_rng(seed)
+    layers = _random_chain(rng, int(rng.integers(3, 9)))
+    N, H, W = 8, 56, 56
+    groups, total, lbl = F.fcm_plan_chain(layers, N, H, W, "f16")
+    best, single, pair = _brute_force_chain(F, layers, N, H, W, "f16")
+    assert total == pytest.approx(best, rel=1e-12)
+    assert lbl == pytest.approx(sum(single), rel=1e-12)
+    # the groups tile the chain in order and carry their own estimates
+    i = 0
+    for g in groups:
+        assert g["first"] == i and g["count"] in (1, 2)
+        assert g["gma"] == pytest.approx(single[i] if g["count"] == 1 else pair[i], rel=1e-12)
+        assert (g["kind"] == -1) == (g["count"] == 1)
+        i += g["count"]
+    assert i == len(layers)
+    assert sum(g["gma"] for g in groups) == pytest.approx(total, rel=1e-12)
+
+
+def test_chain_planner_on_a_mobilenet_v1_body():
+    # MobileNetV1 after its first convolution (Mob_v1, the FCM paper's Table II network),
+    # 112 x 112 input, fp16: every depthwise layer is followed by a pointwise one
+    F = _lib()
+    body = [("dw", 32, 32, 1, "relu6"), ("pw", 32, 64, 1, "relu6"),
+            ("dw", 64, 64, 2, "relu6"), ("pw", 64, 128, 1, "relu6"),
+            ("dw", 128, 128, 1, "relu6"), ("pw", 128, 128, 1, "relu6"),
+            ("dw", 128, 128, 2, "relu6"), ("pw", 128, 256, 1, "relu6"),
+            ("dw", 256, 256, 1, "relu6"), ("pw", 256, 256, 1, "relu6")]
+    groups, total, lbl = F.fcm_plan_chain(body, 8, 112, 112, "f16")
+    assert total < lbl
+    fused = [g for g in groups if g["count"] == 2]
+    assert fused and all(g["kind"] in (F.FCM_KIND_DWPW, F.FCM_KIND_PWDW, F.FCM_KIND_PWPW)
+                         for g in fused)
+    # a fused group satisfies both FusePlanner constraints: its tiles fit the on-chip
+    # memory and there are at least as many output tiles as compute units
+    exts = [(112, 112)]
+    for t, C, K, s_, act in body:
+        h, w = exts[-1]
+        exts.append(((h - 1) // s_ + 1, (w - 1) // s_ + 1) if t == "dw" else (h, w))
+    for g in fused:
+        i = g["first"]
+        pl = F.fcm_plan_variant(_pair_problem(F, body[i], body[i + 1], 8, *exts[i], "f16"),
+                                g["variant"], _spec(F))
+        assert pl.num_tiles >= _spec(F).num_cus and math.isfinite(pl.gma_paper_fused)
+    # the late 28 x 28 pairs have fewer output tiles than compute units at batch 8, so
+    # they stay layer by layer; at batch 64 the same layers fuse
+    assert [g["count"] for g in groups if g["first"] >= 6] == [1, 1, 1, 1]
+    g64, t64, l64 = F.fcm_plan_chain(body[6:], 64, 56, 56, "f16")
+    assert any(g["count"] == 2 for g in g64) and t64 < l64
+
+
+def test_chain_planner_rejects_broken_chains():
+    F = _lib()
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_plan_chain([("pw", 32, 64, 1, "none"), ("dw", 32, 32, 1, "none")], 1, 8, 8)
+    assert ei.value.status == F.FCM_ERR_INVALID_ARG
+    with pytest.raises(F.FcmError) as ei:
+        F.fcm_plan_chain([("dw", 32, 64, 1, "none")], 1, 8, 8)
+    assert ei.value.status == F.FCM_ERR_INVALID_ARG
