@@ -9,7 +9,7 @@ Every tensor is drawn in float64 from ``numpy.random.default_rng(seed)`` in the 
 order X, first-layer weights, scale1, bias1, second-layer weights, scale2, bias2, then
 narrowed to float32 and from there to the storage type with torch's round-to-nearest-
 even casts.  The narrowed values *are* the inputs: both the oracle and the GPU see the
-same numbers.  Weight layouts are PyTorch's: depthwise [C, 3, 3], pointwise [K, C],
+same numbers.  Weight layouts are PyTorch's: depthwise [C*mult, R, S], pointwise [K, C],
 standard conv [K1, C, 3, 3], second conv [K, K1]; for the pointwise->depthwise module
 the first layer is pointwise [K1, C] and the second depthwise [K1, 3, 3] (K = K1).
 
@@ -44,6 +44,8 @@ class Workload:
     pad: int = 1
     R: int = 3
     S: int = 3
+    dil: int = 1          # dwpw: dilation of the depthwise taps
+    mult: int = 1         # dwpw: depth multiplier (K1 == C * mult)
     act1: str = "none"
     act2: str = "none"
     scale1: bool = False  # whether a per-channel scale / bias array is passed
@@ -59,11 +61,11 @@ class Workload:
 
     @property
     def Ho(self) -> int:
-        return (self.H + 2 * self.pad - self.R) // self.stride + 1
+        return (self.H + 2 * self.pad - (self.R - 1) * self.dil - 1) // self.stride + 1
 
     @property
     def Wo(self) -> int:
-        return (self.W + 2 * self.pad - self.S) // self.stride + 1
+        return (self.W + 2 * self.pad - (self.S - 1) * self.dil - 1) // self.stride + 1
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -168,8 +170,8 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> dict:
     rng = np.random.default_rng(wl.seed if seed is None else seed)
     x = _draw(rng, wl.x_dist, (wl.N, wl.H, wl.W, wl.C))
     if wl.kind == "dwpw":
-        w1 = _draw(rng, wl.w_dist, (wl.C, wl.R, wl.S))
-        n1 = wl.C
+        w1 = _draw(rng, wl.w_dist, (wl.C * wl.mult, wl.R, wl.S))
+        n1 = wl.C * wl.mult
     elif wl.kind in ("pwdw", "pwpw"):
         w1 = _draw(rng, wl.w_dist, (wl.K1, wl.C))
         n1 = wl.K1

@@ -105,6 +105,13 @@ def _load():
             lib.fcm_oracle_pwpw.argtypes = [dp, i64, i32, dp, i32, dp, dp, ci, dp, i32, dp, dp,
                                             ci, ci, dp, dp]
             lib.fcm_oracle_pwpw.restype = ctypes.c_int
+            # x, N, H, W, C, w, R, S, sh, sw, ph, pw, dh, dw, M, t
+            lib.fcm_oracle_dw_gen.argtypes = [dp, i32, i32, i32, i32, dp] + [i32] * 9 + [dp]
+            # x, N, H, W, C, w_dw, R, S, sh, sw, ph, pw, dh, dw, M, scale1, bias1, act1,
+            # w_pw, K, scale2, bias2, act2, dtype, t, y
+            lib.fcm_oracle_dwpw_gen.argtypes = [dp, i32, i32, i32, i32, dp] + [i32] * 9 + \
+                [dp, dp, ci, dp, i32, dp, dp, ci, ci, dp, dp]
+            lib.fcm_oracle_dwpw_gen.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -362,3 +369,53 @@ def pwpw_at(x, w1, w2, pix, **kw):
     x = _f64(x)
     pix = np.asarray(pix).reshape(-1, 3)
     return pwpw(x[pix[:, 0], pix[:, 1], pix[:, 2]], w1, w2, **kw)
+
+
+# ---------------------------------------------------------------------------------
+# generalised depthwise layer: R x S filters, dilation, depth multiplier
+# (PyTorch forum "Using optimised depthwise convolutions": nn.Conv2d(in_chans,
+# in_chans * k, kernel_size, groups=in_chans), and the SeparableConv2d listing's
+# dilation argument)
+# ---------------------------------------------------------------------------------
+def dw_gen(x, w_dw, stride=(1, 1), pad=(1, 1), dilation=(1, 1)) -> np.ndarray:
+    """Depthwise layer with w_dw [C*M][R][S]: output channel j reads input channel j // M."""
+    x, w = _f64(x), _f64(w_dw)
+    N, H, W, C = x.shape
+    CM, R, S = w.shape
+    assert CM % C == 0
+    M = CM // C
+    Ho = out_size(H, pad[0], (R - 1) * dilation[0] + 1, stride[0])
+    Wo = out_size(W, pad[1], (S - 1) * dilation[1] + 1, stride[1])
+    t = np.empty((N, Ho, Wo, CM), np.float64)
+    _load().fcm_oracle_dw_gen(_p(x), N, H, W, C, _p(w), R, S, stride[0], stride[1], pad[0],
+                              pad[1], dilation[0], dilation[1], M, _p(t))
+    return t
+
+
+def dwpw_gen(x, w_dw, w_pw, stride=(1, 1), pad=(1, 1), dilation=(1, 1), scale1=None,
+             bias1=None, act1="none", scale2=None, bias2=None, act2="none", dtype="f32",
+             return_t=False):
+    """Layer by layer: generalised DW (w_dw [C*M][R][S]) -> epilogue -> round ->
+    PW (w_pw [K][C*M]) -> epilogue -> round."""
+    x, w1, w2 = _f64(x), _f64(w_dw), _f64(w_pw)
+    N, H, W, C = x.shape
+    CM, R, S = w1.shape
+    assert CM % C == 0
+    M = CM // C
+    K, CMw = w2.shape
+    assert CMw == CM
+    Ho = out_size(H, pad[0], (R - 1) * dilation[0] + 1, stride[0])
+    Wo = out_size(W, pad[1], (S - 1) * dilation[1] + 1, stride[1])
+    t = np.empty((N, Ho, Wo, CM), np.float64) if return_t else None
+    y = np.empty((N, Ho, Wo, K), np.float64)
+    s1 = None if scale1 is None else _f64(scale1)
+    b1 = None if bias1 is None else _f64(bias1)
+    s2 = None if scale2 is None else _f64(scale2)
+    b2 = None if bias2 is None else _f64(bias2)
+    rc = _load().fcm_oracle_dwpw_gen(
+        _p(x), N, H, W, C, _p(w1), R, S, stride[0], stride[1], pad[0], pad[1], dilation[0],
+        dilation[1], M, _p(s1), _p(b1), ACTS[act1], _p(w2), K, _p(s2), _p(b2), ACTS[act2],
+        DTYPES[dtype], _p(t), _p(y))
+    if rc != 0:
+        raise MemoryError("oracle could not allocate the intermediate")
+    return (y, t) if return_t else y

@@ -45,7 +45,8 @@ def sizes(wl) -> dict:
     """Element counts and byte sizes of every tensor of one invocation."""
     e = ELEM_BYTES[wl.dtype]
     Ho, Wo = wl.Ho, wl.Wo
-    n1 = wl.C if wl.kind == "dwpw" else wl.K1
+    # a depthwise layer with depth multiplier m has C*m outputs (one filter per output)
+    n1 = wl.C * wl.mult if wl.kind == "dwpw" else wl.K1
     x = wl.N * wl.H * wl.W * wl.C
     y = wl.N * Ho * Wo * wl.K
     if wl.kind == "pwdw":
@@ -55,7 +56,7 @@ def sizes(wl) -> dict:
         w2 = wl.K1 * wl.R * wl.S
     else:
         t = wl.N * Ho * Wo * n1
-        w1 = wl.C * wl.R * wl.S if wl.kind == "dwpw" else wl.K1 * wl.C * wl.R * wl.S
+        w1 = n1 * wl.R * wl.S if wl.kind == "dwpw" else wl.K1 * wl.C * wl.R * wl.S
         w2 = wl.K * n1
     epi = 4 * (n1 * (int(wl.scale1) + int(wl.bias1)) + wl.K * (int(wl.scale2) + int(wl.bias2)))
     return {"x": x * e, "t": t * e, "y": y * e, "w1": w1 * e, "w2": w2 * e, "epi": epi,
@@ -74,7 +75,8 @@ def flops(wl) -> int:
     """Multiply-adds counted as 2 flops; the epilogue is not counted."""
     P = wl.N * wl.Ho * wl.Wo
     if wl.kind == "dwpw":
-        return 2 * P * wl.C * wl.R * wl.S + 2 * P * wl.C * wl.K
+        n1 = wl.C * wl.mult
+        return 2 * P * n1 * wl.R * wl.S + 2 * P * n1 * wl.K
     if wl.kind == "pwdw":
         return 2 * wl.N * wl.H * wl.W * wl.C * wl.K1 + 2 * P * wl.K1 * wl.R * wl.S
     return 2 * P * wl.K1 * wl.C * wl.R * wl.S + 2 * P * wl.K1 * wl.K

@@ -19,6 +19,11 @@
  *                       pads the intermediate, not the module's input;
  *   PW -> PW module  -- two pointwise layers (the PWPW fusion case, FCM paper Sec. III,
  *                       Table II): pixel by pixel, so a tile needs no halo;
+ *   generalised DW   -- any R x S filter, a dilation and a depth multiplier m (PyTorch
+ *                       forum "Using optimised depthwise convolutions": the depthwise
+ *                       layer with in_chans * k outputs, groups = in_chans, and the
+ *                       SeparableConv2d listing's dilation); output channel j reads input
+ *                       channel j / m;
  *   standard conv    -- the first layer of the back-to-back pair, [N,H,W,C] x
  *                       [K,C,R,S] ("Fusing two back-to-back convolutions", the
  *                       CONV1/CONV2 example);
@@ -442,6 +447,62 @@ int fcm_oracle_pwpw(const double* x, int64_t M, int C, const double* w1, int K1,
     store_rows(t, M, K1, scale1, bias1, act1, dtype);
     fcm_oracle_pw(t, M, K1, w2, K, y);
     store_rows(y, M, K, scale2, bias2, act2, dtype);
+    if (!t_out) free(t);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Generalised depthwise layer: any R x S filter, dilation and depth multiplier.    */
+/* The PyTorch forum thread "Using optimised depthwise convolutions" defines the     */
+/* depthwise layer as nn.Conv2d(in_chans, in_chans * k, kernel_size,                 */
+/* groups = in_chans) -- k filters per input channel, any filter size -- and its      */
+/* SeparableConv2d listing passes a dilation to that layer.  With groups = C, output  */
+/* channel j belongs to group j / k, i.e. reads input channel j / k; a dilation d     */
+/* spaces the filter taps d pixels apart.                                            */
+/* ------------------------------------------------------------------------------ */
+
+/* t[n][oh][ow][c*M + i] = sum_{r,s} x[n][oh*sh - ph + r*dh][ow*sw - pw + s*dw][c] *
+ * w[c*M + i][r][s], x = 0 outside the image; w is [C*M][R][S], t has C*M channels. */
+void fcm_oracle_dw_gen(const double* x, int N, int H, int W, int C, const double* w, int R,
+                       int S, int sh, int sw, int ph, int pw, int dh, int dw, int M,
+                       double* t) {
+    int Ho = out_size(H, ph, (R - 1) * dh + 1, sh), Wo = out_size(W, pw, (S - 1) * dw + 1, sw);
+    int CM = C * M;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int n = 0; n < N; ++n)
+        for (int oh = 0; oh < Ho; ++oh)
+            for (int ow = 0; ow < Wo; ++ow)
+                for (int j = 0; j < CM; ++j) {
+                    int c = j / M;
+                    double acc = 0.0;
+                    for (int r = 0; r < R; ++r)
+                        for (int s = 0; s < S; ++s) {
+                            int ih = oh * sh - ph + r * dh, iw = ow * sw - pw + s * dw;
+                            if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;
+                            acc += x[(((int64_t)n * H + ih) * W + iw) * C + c] *
+                                   w[((int64_t)j * R + r) * S + s];
+                        }
+                    t[(((int64_t)n * Ho + oh) * Wo + ow) * CM + j] = acc;
+                }
+}
+
+/* DW -> PW module with the generalised depthwise layer, layer by layer: the C*M
+ * depthwise outputs are stored (epilogue 1, rounding), then the pointwise layer
+ * w_pw [K][C*M] and epilogue 2. */
+int fcm_oracle_dwpw_gen(const double* x, int N, int H, int W, int C, const double* w_dw,
+                        int R, int S, int sh, int sw, int ph, int pw, int dh, int dw, int M,
+                        const double* scale1, const double* bias1, int act1,
+                        const double* w_pw, int K, const double* scale2, const double* bias2,
+                        int act2, int dtype, double* t_out, double* y) {
+    int Ho = out_size(H, ph, (R - 1) * dh + 1, sh), Wo = out_size(W, pw, (S - 1) * dw + 1, sw);
+    int64_t P = (int64_t)N * Ho * Wo;
+    int CM = C * M;
+    double* t = t_out ? t_out : (double*)malloc(sizeof(double) * (size_t)(P * CM));
+    if (!t) return -1;
+    fcm_oracle_dw_gen(x, N, H, W, C, w_dw, R, S, sh, sw, ph, pw, dh, dw, M, t);
+    store_rows(t, P, CM, scale1, bias1, act1, dtype);
+    fcm_oracle_pw(t, P, CM, w_pw, K, y);
+    store_rows(y, P, K, scale2, bias2, act2, dtype);
     if (!t_out) free(t);
     return 0;
 }
