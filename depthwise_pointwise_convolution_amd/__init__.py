@@ -31,7 +31,7 @@ FCM_OK, FCM_ERR_INVALID_ARG, FCM_ERR_UNSUPPORTED, FCM_ERR_HIP = 0, 1, 2, 3
 FCM_F32, FCM_F16, FCM_BF16, FCM_I8 = 0, 1, 2, 3
 FCM_ACT_NONE, FCM_ACT_RELU, FCM_ACT_RELU6 = 0, 1, 2
 FCM_KIND_DWPW, FCM_KIND_B2B, FCM_KIND_PWDW, FCM_KIND_PWPW = 0, 1, 2, 3
-FCM_PLAN_VERSION = 2
+FCM_PLAN_VERSION = 3
 
 DTYPE_CODES = {"f32": FCM_F32, "f16": FCM_F16, "bf16": FCM_BF16, "i8": FCM_I8}
 ACT_CODES = {"none": FCM_ACT_NONE, "relu": FCM_ACT_RELU, "relu6": FCM_ACT_RELU6}
@@ -52,7 +52,8 @@ _i32, _i64, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
 
 class fcm_problem(ctypes.Structure):
     _fields_ = [(n, _i32) for n in ("kind", "dtype", "N", "H", "W", "C", "K1", "K", "R", "S",
-                                    "stride_h", "stride_w", "pad_h", "pad_w", "act1", "act2")]
+                                    "stride_h", "stride_w", "pad_h", "pad_w", "act1", "act2",
+                                    "dil_h", "dil_w", "mult")]
 
 
 class fcm_device_spec(ctypes.Structure):
@@ -188,15 +189,18 @@ def _stream(stream) -> Optional[int]:
 # host-side calls
 # ------------------------------------------------------------------------------------
 def problem(kind="dwpw", dtype="f16", N=1, H=1, W=1, C=8, K=8, K1=None, R=3, S=3,
-            stride=1, pad=1, act1="none", act2="none") -> fcm_problem:
-    """Build an fcm_problem; K1 defaults to C (depthwise first layer).  For the
-    PW->DW module ("pwdw") K1 is the pointwise layer's output and K must equal it."""
+            stride=1, pad=1, act1="none", act2="none", dilation=1, mult=1) -> fcm_problem:
+    """Build an fcm_problem; K1 defaults to C*mult (depthwise first layer).  For the
+    PW->DW module ("pwdw") K1 is the pointwise layer's output and K must equal it.
+    dilation / mult: the depthwise layer's tap spacing and depth multiplier (DWPW)."""
     p = fcm_problem()
     p.kind = KIND_CODES[kind] if isinstance(kind, str) else kind
     p.dtype = DTYPE_CODES[dtype] if isinstance(dtype, str) else dtype
     p.N, p.H, p.W, p.C, p.K = N, H, W, C, K
-    p.K1 = C if K1 is None else K1
+    p.K1 = C * mult if K1 is None else K1
     p.R, p.S = R, S
+    dh, dw = (dilation, dilation) if isinstance(dilation, int) else dilation
+    p.dil_h, p.dil_w, p.mult = dh, dw, mult
     sh, sw = (stride, stride) if isinstance(stride, int) else stride
     ph, pw = (pad, pad) if isinstance(pad, int) else pad
     p.stride_h, p.stride_w, p.pad_h, p.pad_w = sh, sw, ph, pw

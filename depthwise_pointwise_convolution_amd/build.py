@@ -32,6 +32,7 @@ SOURCES = [
     ("kernels/pwdw_mm.hip", True),
     ("kernels/dwpw_i8.hip", True),
     ("kernels/pwpw_mm.hip", True),
+    ("kernels/dwpw_gen.hip", True),
     ("kernels/lbl.hip", True),
     ("kernels/b2b.hip", True),
     ("api.cpp", True),

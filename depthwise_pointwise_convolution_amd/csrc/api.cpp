@@ -35,6 +35,7 @@ fcm_status ok() {
 struct VariantImpl {
     launch_fn launch;
     occupancy_fn occupancy;
+    launch_fn lbl_first;  // generalised DW->PW: its layer-by-layer depthwise kernel
 };
 
 const VariantImpl kImpls[] = {
@@ -55,6 +56,10 @@ const VariantImpl kImpls[] = {
     {launch_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>, occ_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>},
 #define FCM_V_DWPW_I8(name, S, OCC) {launch_dwpw_i8<S, OCC>, occ_dwpw_i8<S, OCC>},
 #define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) {launch_pwpw_mm<CT, PB, OCC>, occ_pwpw_mm<CT, PB, OCC>},
+#define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC)    \
+    {launch_dwpw_gen<CT, S, FS, D, M, TH, TW, KT, CC>,                \
+     occ_dwpw_gen<CT, S, FS, D, M, TH, TW, KT, CC>,                   \
+     launch_dw_gen_lbl<CT, S, FS, D, M, TH, TW, KT, CC>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -65,6 +70,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_PWDW_MM
 #undef FCM_V_DWPW_I8
 #undef FCM_V_PWPW_MM
+#undef FCM_V_DWPW_GEN
 };
 static_assert(sizeof(kImpls) / sizeof(kImpls[0]) > 0, "variants");
 
@@ -103,8 +109,10 @@ fcm_status check_plan(const fcm_plan_t* plan, int kind) {
     if (st != FCM_OK) return fail(st, "plan holds an invalid problem: " + err);
     if (plan->prob.kind != kind)
         return fail(FCM_ERR_INVALID_ARG, "plan is for the other module kind");
-    if (plan->Ho != conv_out(plan->prob.H, plan->prob.pad_h, plan->prob.R, plan->prob.stride_h) ||
-        plan->Wo != conv_out(plan->prob.W, plan->prob.pad_w, plan->prob.S, plan->prob.stride_w))
+    if (plan->Ho != conv_out(plan->prob.H, plan->prob.pad_h, prob_ext_h(plan->prob),
+                             plan->prob.stride_h) ||
+        plan->Wo != conv_out(plan->prob.W, plan->prob.pad_w, prob_ext_w(plan->prob),
+                             plan->prob.stride_w))
         return fail(FCM_ERR_INVALID_ARG, "plan output extent does not match its problem");
     return FCM_OK;
 }
@@ -298,7 +306,8 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
         const char* d = (const char*)w1_dst;
         const int64_t ns = p.kind == FCM_KIND_PWDW
                                ? (int64_t)p.K1 * p.C * e
-                               : (int64_t)(p.kind == FCM_KIND_B2B ? p.K1 : 1) * p.R * p.S * p.C * e;
+                               : p.kind == FCM_KIND_B2B ? (int64_t)p.K1 * p.R * p.S * p.C * e
+                                                        : (int64_t)p.R * p.S * p.K1 * e;
         const int64_t nd = plan->w1_packed_bytes;
         if (s < d + nd && d < s + ns) return fail(FCM_ERR_INVALID_ARG, "w1 buffers overlap");
     }
@@ -310,7 +319,7 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
         const char* d = (const char*)w2_dst;
         const int64_t ns = p.kind == FCM_KIND_PWDW
                                ? (int64_t)p.K1 * p.R * p.S * e
-                               : (int64_t)p.K * (p.kind == FCM_KIND_B2B ? p.K1 : p.C) * e;
+                               : (int64_t)p.K * p.K1 * e;  // (DW->PW: K1 = C * mult)
         const int64_t nd = plan->w2_packed_bytes;
         if (s < d + nd && d < s + ns) return fail(FCM_ERR_INVALID_ARG, "w2 buffers overlap");
     }
@@ -350,7 +359,8 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
     if (w1_src) {
         int rc;
         if (p.kind == FCM_KIND_DWPW) {
-            rc = launch_pack_dw(e, w1_src, w1_dst, p.C, p.R * p.S, stream);
+            // [C*mult][R*S] -> [R*S][C*mult] (K1 = C * mult)
+            rc = launch_pack_dw(e, w1_src, w1_dst, p.K1, p.R * p.S, stream);
         } else {
             rc = launch_pack_conv(e, w1_src, w1_dst, p.K1, p.C, p.R * p.S, stream);
             const int64_t plain = (int64_t)p.K1 * p.R * p.S * p.C * e;
@@ -362,11 +372,10 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                          hipGetErrorString((hipError_t)rc));
     }
     if (w2_src) {
-        const int64_t plain = (int64_t)p.K * (p.kind == FCM_KIND_B2B ? p.K1 : p.C) * e;
+        const int64_t plain = (int64_t)p.K * p.K1 * e;
         int rc = launch_copy(w2_src, w2_dst, plain, stream);
         if (rc == 0 && plan->w2_packed_bytes > plain)
-            rc = launch_pack_pw_blocked(w2_src, (char*)w2_dst + plain, p.K,
-                                        p.kind == FCM_KIND_B2B ? p.K1 : p.C, stream);
+            rc = launch_pack_pw_blocked(w2_src, (char*)w2_dst + plain, p.K, p.K1, stream);
         if (rc != 0)
             return fail(FCM_ERR_HIP, std::string("weight copy failed: ") +
                                          hipGetErrorString((hipError_t)rc));
@@ -581,6 +590,20 @@ fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
     a.s1 = scale1;
     a.b1 = bias1;
     a.y = t;
+    if (prob_is_gen(plan->prob)) {
+        // the generalised depthwise layer: the plan's variant names the kernel (filter,
+        // dilation, multiplier, chunk); one workgroup per (tile, chunk)
+        FCM_TRY(check_variant(plan));
+        const VariantDesc& v = kVariants[plan->variant];
+        set_tiles(&a, lbl::DWG_TH, lbl::DWG_TW, 1, 1);
+        const int64_t grid = (int64_t)a.num_ptiles * ((plan->prob.C + v.cc - 1) / v.cc);
+        if (grid > INT32_MAX) return fail(FCM_ERR_UNSUPPORTED, "too many depthwise tiles");
+        const int rc = kImpls[plan->variant].lbl_first(a, (int)grid, stream);
+        if (rc != 0)
+            return fail(FCM_ERR_HIP, std::string("kernel launch failed: ") +
+                                         hipGetErrorString((hipError_t)rc));
+        return ok();
+    }
     set_tiles(&a, lbl::DW_TH, lbl::DW_TW, 1, 1);
     const int rc = plan->prob.dtype == FCM_I8
                        ? launch_dw_lbl_i8(plan->prob.stride_h, a, stream)
@@ -602,7 +625,10 @@ fcm_status fcm_pw_fwd(const fcm_plan_t* plan, const void* t, const void* w_pw,
     FCM_TRY(optional(bias2, "bias2"));
     KArgs a = base_args(plan);
     // the 1x1 layer reads the intermediate as its input: [N*Ho*Wo][C or K1]
-    if (plan->prob.kind == FCM_KIND_B2B || plan->prob.kind == FCM_KIND_PWPW) a.C = plan->prob.K1;
+    // (DW->PW: K1 = C * mult depthwise outputs)
+    if (plan->prob.kind == FCM_KIND_B2B || plan->prob.kind == FCM_KIND_PWPW ||
+        plan->prob.kind == FCM_KIND_DWPW)
+        a.C = plan->prob.K1;
     if (plan->prob.kind == FCM_KIND_PWDW) {
         // the first layer of a PW->DW module: every input pixel, C -> K1, with the
         // module's first epilogue

@@ -37,6 +37,15 @@ int launch_pwpw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int PB, int OCC>
 int occ_pwpw_mm();
 
+// generalised DW->PW (dwpw_gen.hip): fused kernel, occupancy, and the matching
+// layer-by-layer depthwise kernel
+template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC>
+int launch_dwpw_gen(const KArgs& a, int grid, void* stream);
+template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC>
+int occ_dwpw_gen();
+template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC>
+int launch_dw_gen_lbl(const KArgs& a, int grid, void* stream);
+
 template <int S, int OCC>
 int launch_dwpw_i8(const KArgs& a, int grid, void* stream);
 template <int S, int OCC>

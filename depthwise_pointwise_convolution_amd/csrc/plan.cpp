@@ -54,6 +54,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_I8, FCM_I8, S, 4, 16, 64, 64, 1, 2, 0, OCC, 4, 64, 0},
 #define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) \
     {#name, VK_PWPW_MM, dt, 1, PB, 16, 64, 64, 1, 2, 64, OCC, 4, 64, 0},
+#define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC) \
+    {#name, VK_DWPW_GEN, dt, S, TH, TW, KT, CC, 0, 1, 0, 2, 4, 0, 0, FS, D, M},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -64,6 +66,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_PWDW_MM
 #undef FCM_V_DWPW_I8
 #undef FCM_V_PWPW_MM
+#undef FCM_V_DWPW_GEN
 };
 const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -74,9 +77,9 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Rows (or columns) of the input that the halo window of output tile `t` (extent
 // `tile` outputs, stride s, 3 taps, padding pad) covers inside [0, in).
-int64_t window_inside(int t, int tile, int s, int pad, int in) {
+int64_t window_inside(int t, int tile, int s, int pad, int in, int ext = 3) {
     const int64_t lo = (int64_t)t * tile * s - pad;
-    const int64_t hi = lo + (int64_t)(tile - 1) * s + 3;  // exclusive
+    const int64_t hi = lo + (int64_t)(tile - 1) * s + ext;  // exclusive
     const int64_t a = std::max<int64_t>(lo, 0), b = std::min<int64_t>(hi, in);
     return b > a ? b - a : 0;
 }
@@ -84,10 +87,11 @@ int64_t window_inside(int t, int tile, int s, int pad, int in) {
 // Sum over all output tiles of an image of the input pixels their halo windows
 // load (clipped to the image): the exact per-image footprint of a tiled
 // 3x3 stencil, overlaps counted once per tile that loads them.
-int64_t halo_pixels(int Ho, int Wo, int H, int W, int th, int tw, int s, int ph, int pw) {
+int64_t halo_pixels(int Ho, int Wo, int H, int W, int th, int tw, int s, int ph, int pw,
+                    int ext_h = 3, int ext_w = 3) {
     int64_t rows = 0, cols = 0;
-    for (int t = 0; t < cdiv(Ho, th); ++t) rows += window_inside(t, th, s, ph, H);
-    for (int t = 0; t < cdiv(Wo, tw); ++t) cols += window_inside(t, tw, s, pw, W);
+    for (int t = 0; t < cdiv(Ho, th); ++t) rows += window_inside(t, th, s, ph, H, ext_h);
+    for (int t = 0; t < cdiv(Wo, tw); ++t) cols += window_inside(t, tw, s, pw, W, ext_w);
     return rows * cols;
 }
 
@@ -110,6 +114,14 @@ int64_t persistent_grid(int64_t ptiles, int ktiles, int64_t capacity) {
 
 int variant_lds_bytes(const VariantDesc& v) {
     const int e = elem_bytes(v.dtype);
+    if (v.vkind == VK_DWPW_GEN) {
+        // input window chunk, intermediate chunk (C*M channels), fp32 depthwise filters and
+        // epilogue-1 constants of the chunk, epilogue-2 constants of the K tile
+        const int ext = (v.fs - 1) * v.dil + 1, cm = v.cc * v.mult;
+        const int IHg = (v.th - 1) * v.stride + ext, IWg = (v.tw - 1) * v.stride + ext;
+        return IHg * IWg * (v.cc + 8) * e + v.th * v.tw * (cm + 8) * e +
+               v.fs * v.fs * cm * 4 + 2 * cm * 4 + 2 * v.kt * 4;
+    }
     const int IH = (v.th - 1) * v.stride + 3, IW = (v.tw - 1) * v.stride + 3;
     const int P = v.th * v.tw;
     switch (v.vkind) {
@@ -169,6 +181,13 @@ int variant_vgpr_estimate(const VariantDesc& v) {
     const int P = v.th * v.tw;
     const int MBW = P / 64;
     switch (v.vkind) {
+    case VK_DWPW_GEN: {
+        // accumulators, the next chunk's input in flight, one depthwise item's sums
+        const int KB = v.kt / 16, ext = (v.fs - 1) * v.dil + 1;
+        const int slots = ((v.th - 1) * v.stride + ext) * ((v.tw - 1) * v.stride + ext) *
+                          (v.cc / 8);
+        return 40 + MBW * KB * 4 + 4 * ((slots + 255) / 256) + 8 * v.mult + 24;
+    }
     case VK_DWPW: {
         const int KB = v.kt / 16, KS = v.cc / 32;
         const int cg = v.cc / 8;
@@ -257,19 +276,31 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         *err = "sizes, filter extent and strides must be positive, padding non-negative";
         return FCM_ERR_INVALID_ARG;
     }
-    if (p->kind == FCM_KIND_DWPW && p->K1 != p->C) {
-        *err = "a depthwise layer keeps the channel count: K1 must equal C";
+    if (p->dil_h < 0 || p->dil_w < 0 || p->mult < 0) {
+        *err = "dilation and depth multiplier must be non-negative (0 means 1)";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->kind != FCM_KIND_DWPW && (p->dil_h > 1 || p->dil_w > 1 || p->mult > 1)) {
+        *err = "dilation and depth multiplier describe the depthwise layer of a DW->PW module";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->kind == FCM_KIND_DWPW && (int64_t)p->K1 != (int64_t)p->C * prob_mult(*p)) {
+        *err = "a depthwise layer has C * mult outputs: K1 must equal C * mult";
         return FCM_ERR_INVALID_ARG;
     }
     if (p->kind == FCM_KIND_PWDW && p->K != p->K1) {
         *err = "the depthwise layer of a PW->DW module keeps the channel count: K must equal K1";
         return FCM_ERR_INVALID_ARG;
     }
-    if (p->pad_h >= p->R || p->pad_w >= p->S) {
-        *err = "padding must be smaller than the filter";
+    if (p->R > 64 || p->S > 64 || prob_dil_h(*p) > 64 || prob_dil_w(*p) > 64) {
+        *err = "filter extent and dilation must be at most 64";
+        return FCM_ERR_UNSUPPORTED;
+    }
+    if (p->pad_h >= prob_ext_h(*p) || p->pad_w >= prob_ext_w(*p)) {
+        *err = "padding must be smaller than the filter's (dilated) extent";
         return FCM_ERR_INVALID_ARG;
     }
-    if (p->H + 2 * p->pad_h < p->R || p->W + 2 * p->pad_w < p->S) {
+    if (p->H + 2 * p->pad_h < prob_ext_h(*p) || p->W + 2 * p->pad_w < prob_ext_w(*p)) {
         *err = "padded input is smaller than the filter";
         return FCM_ERR_INVALID_ARG;
     }
@@ -297,6 +328,29 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         const int64_t big = (int64_t)1 << 31;
         if ((int64_t)p->N * p->H * p->W * std::max(std::max(p->C, p->K), p->K1) >= big) {
             *err = "tensor element counts must stay below 2^31";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        return FCM_OK;
+    }
+    if (prob_is_gen(*p)) {
+        if (p->R != p->S || (p->R != 3 && p->R != 5 && p->R != 7)) {
+            *err = "generalised depthwise kernels take square 3x3, 5x5 or 7x7 filters";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        if (prob_dil_h(*p) != prob_dil_w(*p)) {
+            *err = "generalised depthwise kernels take the same dilation in both directions";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        if (p->stride_h != p->stride_w || (p->stride_h != 1 && p->stride_h != 2)) {
+            *err = "stride must be 1 or 2 in both directions";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        if (p->dtype != FCM_F16 && p->dtype != FCM_BF16) {
+            *err = "generalised depthwise kernels need 16-bit storage (fp16 or bf16)";
+            return FCM_ERR_UNSUPPORTED;
+        }
+        if (p->C % 8 || p->K % 8 || p->K1 % 8) {
+            *err = "channel counts must be multiples of 8 (16-byte NHWC vectors)";
             return FCM_ERR_UNSUPPORTED;
         }
         return FCM_OK;
@@ -337,6 +391,19 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
 }
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
+    if (v.vkind == VK_DWPW_GEN || prob_is_gen(p)) {
+        if (v.vkind != VK_DWPW_GEN || p.kind != FCM_KIND_DWPW || v.dtype != p.dtype) {
+            if (why) *why = "variant is for another module kind, depthwise form or storage type";
+            return false;
+        }
+        if (v.stride != p.stride_h || v.fs != p.R || v.fs != p.S || v.dil != prob_dil_h(p) ||
+            v.mult != prob_mult(p)) {
+            if (why) *why = "variant is compiled for another stride, filter size, dilation or "
+                            "depth multiplier";
+            return false;
+        }
+        return true;
+    }
     if (v.vkind == VK_PWPW_MM || p.kind == FCM_KIND_PWPW) {
         if (v.vkind != VK_PWPW_MM || p.kind != FCM_KIND_PWPW || v.dtype != p.dtype) {
             if (why) *why = "variant is for another module kind or storage type";
@@ -655,6 +722,100 @@ Estimate estimate_pwdw(const VariantDesc& v, const fcm_problem& p, const fcm_dev
 // PW->PW module: tiles of th x 16 consecutive pixels, both layers on the matrix cores, the
 // first layer recomputed once per 64-channel output tile; Eq. 2 for each layer with the
 // intermediate removed from the global-memory accesses (FCM paper Sec. IV-B).
+// DW->PW module with a generalised depthwise layer (filter FS x FS, dilation D, depth
+// multiplier M; PyTorch forum "Using optimised depthwise convolutions").  The same
+// tiling as the plain module, with the window extent (FS-1)*D + 1 in place of 3 and
+// C*M intermediate channels; the depthwise layer runs on the vector ALU (FS*FS
+// multiply-adds per intermediate value) once per output-channel tile, the pointwise
+// layer on the matrix cores.  Filters are streamed per tile and chunk.
+Estimate estimate_gen(const VariantDesc& v, const fcm_problem& p, const fcm_device_spec& d,
+                      int Ho, int Wo) {
+    Estimate r{};
+    const int e = elem_bytes(p.dtype);
+    const int lds = variant_lds_bytes(v);
+    int vg = (variant_vgpr_estimate(v) + 7) / 8 * 8;
+    int occ = std::min(std::min(lds > 0 ? d.lds_bytes_per_cu / lds : 8,
+                                std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ)),
+                       d.max_waves_per_simd);
+    if (lds > d.lds_bytes_per_wg) occ = 0;
+    r.wgs_per_cu = occ;
+    const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);
+    const int64_t ptiles = (int64_t)p.N * tiles_h * tiles_w;
+    const int ktiles = (int)cdiv(p.K, v.kt);
+    r.num_tiles = (int)std::min<int64_t>(ptiles * ktiles, INT32_MAX);
+    const int64_t grid = persistent_grid(ptiles, ktiles, (int64_t)d.num_cus * std::max(occ, 1));
+    r.grid = (int)grid;
+    const int ext_h = prob_ext_h(p), ext_w = prob_ext_w(p);
+    const int64_t halo =
+        halo_pixels(Ho, Wo, p.H, p.W, v.th, v.tw, p.stride_h, p.pad_h, p.pad_w, ext_h, ext_w);
+    const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K * e;
+    const int64_t w1_bytes = (int64_t)p.R * p.S * p.K1 * e;
+    const int64_t w2_slice = (int64_t)std::min(v.kt, p.K) * p.K1 * e;
+    const int64_t epi = (int64_t)4 * 2 * (p.K1 + v.kt);
+    r.pred = halo * p.N * p.C * e * ktiles + y_bytes + (int64_t)r.num_tiles * (w2_slice + w1_bytes) +
+             grid * epi;
+    const double pad_px = (double)tiles_h * v.th * tiles_w * v.tw / ((double)Ho * Wo);
+    r.waste = (double)ktiles * pad_px;
+    const double P = (double)p.N * Ho * Wo;
+    const double alg = (double)p.N * p.H * p.W * p.C * e + (double)y_bytes + (double)w1_bytes +
+                       (double)p.K * p.K1 * e;
+    const double lane_ops_per_s = d.valu_f32_flops / 2.0;
+    const double t_mat = 2.0 * P * pad_px * (double)p.K1 * p.K / d.mfma_f16_flops;
+    const double t_vec = P * pad_px *
+                         ((double)p.R * p.S * p.K1 * ktiles + 3.0 * ((double)p.K1 * ktiles + p.K)) /
+                         lane_ops_per_s;
+    const double t_hbm = alg / d.hbm_bytes_per_s;
+    const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);
+    const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
+    r.t_us = std::max(std::max(t_hbm, t_l2), std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+    // constructed DW->PW estimate (Eq. 1 with the window extent as the filter size)
+    const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, ext_h,
+                                       p.stride_h);
+    const double ifm = (double)p.N * p.H * p.W * p.C * e;
+    const double w_pw = (double)p.K * p.K1 * e;
+    const double ofm_tile = (double)v.th * v.tw * std::min(v.kt, p.K) * e;
+    const bool fits = lds <= d.lds_bytes_per_wg && occ > 0;
+    const bool enough = r.num_tiles >= d.num_cus;
+    r.feasible = fits && enough;
+    r.gma = r.feasible ? (2.0 * p.C * overlap * p.N * e + ifm) * ceil(w_pw / (double)w2_slice) +
+                             ceil((double)y_bytes / ofm_tile) * (w_pw + (double)w1_bytes) +
+                             (double)y_bytes
+                       : INFINITY;
+    return r;
+}
+
+// Layer-by-layer pair for the generalised module: the depthwise kernel with the
+// variant's chunk (input once per tile, filters once per tile and chunk, intermediate
+// written), then the pointwise baseline over C*M channels.  Eq. 3 + Eq. 2.
+void estimate_unfused_gen(const fcm_problem& p, int cc, int Ho, int Wo, int64_t* pred,
+                          double* gma) {
+    const int e = elem_bytes(p.dtype);
+    const int th = lbl::DWG_TH, tw = lbl::DWG_TW;
+    const int64_t t_bytes = (int64_t)p.N * Ho * Wo * p.K1 * e;
+    const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K * e;
+    const int64_t w2 = (int64_t)p.K * p.K1 * e;
+    const int ext_h = prob_ext_h(p), ext_w = prob_ext_w(p);
+    const int64_t halo =
+        halo_pixels(Ho, Wo, p.H, p.W, th, tw, p.stride_h, p.pad_h, p.pad_w, ext_h, ext_w);
+    const int64_t tiles = (int64_t)p.N * cdiv(Ho, th) * cdiv(Wo, tw);
+    const int64_t first = halo * p.N * p.C * e +
+                          tiles * cdiv(p.C, cc) * (int64_t)p.R * p.S * cc * prob_mult(p) * e +
+                          t_bytes;
+    const int64_t m = (int64_t)p.N * Ho * Wo;
+    const int64_t second =
+        t_bytes * cdiv(p.K, lbl::PW_KT16) + cdiv(m, lbl::PW_MT16) * w2 + y_bytes;
+    *pred = first + second;
+    const double ifm = (double)p.N * p.H * p.W * p.C * e;
+    const double overlap = eq1_overlap(p.W, p.H, tw * p.stride_w, th * p.stride_h, ext_h,
+                                       p.stride_h);
+    const double w1 = (double)p.R * p.S * p.K1 * e;
+    const double g1 = 2.0 * p.C * overlap * p.N * e + ifm + (double)t_bytes +
+                      ceil((double)Ho * Wo / (th * tw)) * p.N * w1;
+    const double g2 = ceil(w2 / ((double)std::min(lbl::PW_KT16, p.K) * p.K1 * e)) * t_bytes +
+                      (double)y_bytes + ceil((double)m / lbl::PW_MT16) * w2;
+    *gma = g1 + g2;
+}
+
 Estimate estimate_pwpw(const VariantDesc& v, const fcm_problem& p, const fcm_device_spec& d) {
     Estimate r{};
     const int e = elem_bytes(p.dtype);
@@ -807,8 +968,8 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         *err = "device spec has a non-positive field";
         return FCM_ERR_INVALID_ARG;
     }
-    const int Ho = conv_out(p->H, p->pad_h, p->R, p->stride_h);
-    const int Wo = conv_out(p->W, p->pad_w, p->S, p->stride_w);
+    const int Ho = conv_out(p->H, p->pad_h, prob_ext_h(*p), p->stride_h);
+    const int Wo = conv_out(p->W, p->pad_w, prob_ext_w(*p), p->stride_w);
 
     int best = -1;
     Estimate be{};
@@ -817,7 +978,8 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         if (forced >= 0 && i != forced) continue;
         const VariantDesc& v = kVariants[i];
         if (!variant_runs(v, *p, forced >= 0 ? &why : nullptr)) continue;
-        Estimate e = p->kind == FCM_KIND_PWDW   ? estimate_pwdw(v, *p, d, Ho, Wo)
+        Estimate e = prob_is_gen(*p)            ? estimate_gen(v, *p, d, Ho, Wo)
+                     : p->kind == FCM_KIND_PWDW ? estimate_pwdw(v, *p, d, Ho, Wo)
                      : p->kind == FCM_KIND_PWPW ? estimate_pwpw(v, *p, d)
                                                 : estimate(v, *p, d, Ho, Wo);
         if (e.wgs_per_cu <= 0) {
@@ -918,10 +1080,11 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         *out = pl;
         return FCM_OK;
     }
-    const int n1 = p->kind == FCM_KIND_B2B ? p->K1 : p->C;
+    // the first layer's outputs: K1 (B2B), C * mult (DW->PW: K1 as validated)
+    const int n1 = p->K1;
     pl.w1_packed_bytes =
         (int64_t)(p->kind == FCM_KIND_B2B ? (int64_t)p->K1 * p->R * p->S * p->C
-                                          : (int64_t)p->R * p->S * p->C) * e;
+                                          : (int64_t)p->R * p->S * p->K1) * e;
     pl.w2_packed_bytes = (int64_t)p->K * n1 * e;
     if (p->dtype == FCM_I8) {
         // int8: the 1x1 filters again in 64 x 64 blocks in the int8 matrix-operand order
@@ -939,13 +1102,16 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     // epilogue arrays are counted as passed: scale and bias for both layers
     const int64_t epi = (int64_t)4 * 2 * (n1 + p->K);
     const int64_t w1_bytes = (int64_t)(p->kind == FCM_KIND_B2B ? (int64_t)p->K1 * p->R * p->S * p->C
-                                                               : (int64_t)p->R * p->S * p->C) * e;
+                                                               : (int64_t)p->R * p->S * p->K1) * e;
     pl.alg_bytes_fused = x_bytes + y_bytes + w1_bytes + (int64_t)p->K * n1 * e + epi;
     pl.alg_bytes_unfused = pl.alg_bytes_fused + 2 * pl.workspace_bytes;
     pl.pred_bytes_fused = be.pred;
     int64_t pu = 0;
     double gu = 0;
-    estimate_unfused(*p, d, Ho, Wo, &pu, &gu);
+    if (prob_is_gen(*p))
+        estimate_unfused_gen(*p, v.cc, Ho, Wo, &pu, &gu);
+    else
+        estimate_unfused(*p, d, Ho, Wo, &pu, &gu);
     pl.pred_bytes_unfused = pu;
     pl.gma_paper_fused = be.gma;
     pl.gma_paper_unfused = gu;
@@ -956,7 +1122,7 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     const double P = (double)p->N * Ho * Wo;
     pl.flops = p->kind == FCM_KIND_B2B
                    ? 2.0 * P * p->K1 * p->C * p->R * p->S + 2.0 * P * p->K1 * p->K
-                   : 2.0 * P * p->C * p->R * p->S + 2.0 * P * p->C * p->K;
+                   : 2.0 * P * p->K1 * p->R * p->S + 2.0 * P * p->K1 * p->K;
     *out = pl;
     return FCM_OK;
 }

@@ -18,7 +18,8 @@ enum VKind {
     VK_DWPW_MMW = 6,
     VK_PWDW_MM = 7,
     VK_DWPW_I8 = 8,
-    VK_PWPW_MM = 9
+    VK_PWPW_MM = 9,
+    VK_DWPW_GEN = 10
 };
 
 struct VariantDesc {
@@ -36,6 +37,9 @@ struct VariantDesc {
     int waves;   // waves per workgroup
     int cmax;    // largest C the variant takes (0: no limit)
     int bpw;     // PW->DW: 16-channel blocks per wave (0 otherwise)
+    int fs;      // generalised DW->PW: filter size, dilation, depth multiplier (0 otherwise)
+    int dil;
+    int mult;
 };
 
 extern const VariantDesc kVariants[];
@@ -79,6 +83,19 @@ inline int64_t pw_blocked_elems(int K, int C) {
 // channels 32s.. of tap t, in one contiguous kilobyte.  Blocks are ordered (g, t, s).
 inline int64_t conv_blocked_elems(int K1, int C) {
     return (int64_t)((K1 + 15) / 16 * 16) * 9 * ((C + 63) / 64 * 64);
+}
+
+// The generalised depthwise fields of a problem (0 means 1) and the input extent of
+// one output's window, (R-1)*dil + 1.
+inline int prob_dil_h(const fcm_problem& p) { return p.dil_h > 0 ? p.dil_h : 1; }
+inline int prob_dil_w(const fcm_problem& p) { return p.dil_w > 0 ? p.dil_w : 1; }
+inline int prob_mult(const fcm_problem& p) { return p.mult > 0 ? p.mult : 1; }
+inline int prob_ext_h(const fcm_problem& p) { return (p.R - 1) * prob_dil_h(p) + 1; }
+inline int prob_ext_w(const fcm_problem& p) { return (p.S - 1) * prob_dil_w(p) + 1; }
+// A DW->PW module whose depthwise layer is not the plain 3x3, undilated, multiplier-1 one.
+inline bool prob_is_gen(const fcm_problem& p) {
+    return p.kind == FCM_KIND_DWPW && (p.R != 3 || p.S != 3 || prob_dil_h(p) != 1 ||
+                                       prob_dil_w(p) != 1 || prob_mult(p) != 1);
 }
 
 // Output extent of a convolution.

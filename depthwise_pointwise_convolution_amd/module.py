@@ -17,16 +17,17 @@ TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat
 
 
 class FcmModule:
-    """w1: depthwise [C,3,3], standard [K1,C,3,3] or (PW->DW) pointwise [K1,C]; w2:
-    [K,C], [K,K1] or (PW->DW) depthwise [K1,3,3] (torch, on the GPU, storage dtype);
+    """w1: depthwise [C*mult,R,S], standard [K1,C,3,3] or (PW->DW) pointwise [K1,C]; w2:
+    [K,C*mult], [K,K1] or (PW->DW) depthwise [K1,3,3] (torch, on the GPU, storage dtype);
     scale/bias: float32 per-channel tensors or None."""
 
     def __init__(self, kind: str, dtype: str, N: int, H: int, W: int, C: int, K: int,
                  K1: Optional[int], stride: int, pad: int, act1: str, act2: str, w1, w2,
                  scale1=None, bias1=None, scale2=None, bias2=None,
-                 variant: Optional[int] = None, stream=None, R: int = 3, S: int = 3):
+                 variant: Optional[int] = None, stream=None, R: int = 3, S: int = 3,
+                 dilation: int = 1, mult: int = 1):
         self.prob = problem(kind, dtype, N, H, W, C, K, K1, R=R, S=S, stride=stride, pad=pad,
-                            act1=act1, act2=act2)
+                            act1=act1, act2=act2, dilation=dilation, mult=mult)
         self.plan = fcm_plan(self.prob) if variant is None else fcm_plan_variant(self.prob,
                                                                                  variant)
         self.dtype = dtype
@@ -39,7 +40,7 @@ class FcmModule:
                          stream)
         self.s1, self.b1, self.s2, self.b2 = scale1, bias1, scale2, bias2
         self.out_shape = (N, self.plan.Ho, self.plan.Wo, K)
-        self.t_shape = (N, self.plan.Ho, self.plan.Wo, C if K1 is None else K1)
+        self.t_shape = (N, self.plan.Ho, self.plan.Wo, self.prob.K1)
         self.b2b = self.prob.kind == FCM_KIND_B2B
         self.pwdw = self.prob.kind == FCM_KIND_PWDW
         if self.pwdw:  # the intermediate is the pointwise layer's output
@@ -101,4 +102,4 @@ def from_workload(wl, tensors: dict, device="cuda", variant=None) -> "FcmModule"
                      wl.act2, dev(tensors["w1"], tdt), dev(tensors["w2"], tdt),
                      dev(tensors["scale1"], torch.float32), dev(tensors["bias1"], torch.float32),
                      dev(tensors["scale2"], torch.float32), dev(tensors["bias2"], torch.float32),
-                     variant=variant, R=wl.R, S=wl.S)
+                     variant=variant, R=wl.R, S=wl.S, dilation=wl.dil, mult=wl.mult)

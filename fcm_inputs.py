@@ -133,6 +133,26 @@ WORKLOADS = {
         bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=7,
         description="Downsampling PW->DW module: PW 16->96 + scale/bias+ReLU6, DW 3x3 s2 "
                     "+ scale/bias+ReLU6, fp16, N=32 112x112 -> 56x56"),
+    # generalised depthwise layers (filter size, dilation, depth multiplier)
+    "dw5_f16_32x28x28_c120_k40": Workload(
+        "dw5_f16_32x28x28_c120_k40", "dwpw", "f16", N=32, H=28, W=28, C=120, K=40, K1=120,
+        R=5, S=5, pad=2, act1="relu", act2="none", scale1=True, bias1=True, scale2=True,
+        bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=10,
+        description="5x5 depthwise block (MobileNetV3-style 28x28 stage): DW 5x5 s1 p2 C=120 "
+                    "+ scale/bias+ReLU, PW 120->40 + scale/bias (linear), fp16, N=32 28x28"),
+    "dil2_f16_8x33x33_c960_k160": Workload(
+        "dil2_f16_8x33x33_c960_k160", "dwpw", "f16", N=8, H=33, W=33, C=960, K=160, K1=960,
+        dil=2, pad=2, act1="relu6", act2="none", scale1=True, bias1=True, scale2=True,
+        bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.05), seed=11,
+        description="Dilated depthwise block (MobileNetV2 backbone at output stride 16): "
+                    "DW 3x3 dilation 2 p2 C=960 + scale/bias+ReLU6, PW 960->160 + "
+                    "scale/bias (linear), fp16, N=8 33x33"),
+    "mult2_f16_8x112x112_c32_k128": Workload(
+        "mult2_f16_8x112x112_c32_k128", "dwpw", "f16", N=8, H=112, W=112, C=32, K=128,
+        K1=64, mult=2, act1="relu6", act2="relu6", scale1=True, bias1=True, scale2=True,
+        bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=12,
+        description="Depth multiplier 2: DW 3x3 s1 C=32 x2 -> 64 + scale/bias+ReLU6, "
+                    "PW 64->128 + scale/bias+ReLU6, fp16, N=8 112x112"),
 }
 
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FCM_PLAN_VERSION 2
+#define FCM_PLAN_VERSION 3
 
 typedef enum {
     FCM_OK = 0,
@@ -93,6 +93,22 @@ typedef struct {
     int32_t stride_h, stride_w, pad_h, pad_w; /* of the RxS conv (the first layer for
                          DWPW and B2B, the second for PWDW); the 1x1 is stride 1 */
     int32_t act1, act2; /* fcm_act after the first / second conv */
+    /* Generalised depthwise layer of a DWPW module (PyTorch forum "Using optimised
+     * depthwise convolutions": the depthwise layer nn.Conv2d(in_chans, in_chans * k,
+     * kernel_size, groups = in_chans), and the dilation its SeparableConv2d listing
+     * passes).  0 means 1, so a zero-initialised problem is the plain module.
+     *  - dil_h, dil_w: spacing of the filter taps; the window of one output spans
+     *    (R-1)*dil_h + 1 rows and (S-1)*dil_w + 1 columns, and Ho, Wo follow from
+     *    that extent;
+     *  - mult: depth multiplier m; the depthwise layer has C*m outputs (K1 must equal
+     *    C*m), output channel j reads input channel j / m, depthwise filters are
+     *    [C*m][R][S] and pointwise filters [K][C*m].
+     * Kernels exist for square R = S in {3, 5, 7}, dil_h = dil_w, 16-bit storage, and
+     * the compiled (stride, filter, dilation, multiplier) combinations; other values
+     * are FCM_ERR_UNSUPPORTED (plain 3x3 problems keep every kernel listed above).
+     * Other kinds require 0 or 1 here (FCM_ERR_INVALID_ARG otherwise). */
+    int32_t dil_h, dil_w;
+    int32_t mult;
 } fcm_problem;
 
 /* What the planner needs to know about the GPU (FusePlanner's inputs: number of

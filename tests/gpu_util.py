@@ -32,13 +32,24 @@ def oracle_kwargs(wl, inp) -> dict:
                 act2=wl.act2, dtype=wl.dtype)
 
 
+def is_gen(wl) -> bool:
+    """A DW->PW workload whose depthwise layer is not the plain 3x3 one."""
+    return wl.kind == "dwpw" and (wl.R != 3 or wl.S != 3 or wl.dil != 1 or wl.mult != 1)
+
+
 def oracle_full(wl, inp) -> np.ndarray:
+    if is_gen(wl):
+        return oracle.dwpw_gen(inp["x"], inp["w1"], inp["w2"],
+                               dilation=(wl.dil, wl.dil), **oracle_kwargs(wl, inp))
     fn = {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw,
           "pwpw": oracle.pwpw}[wl.kind]
     return fn(inp["x"], inp["w1"], inp["w2"], **oracle_kwargs(wl, inp))
 
 
 def oracle_rows(wl, inp, pix) -> np.ndarray:
+    if is_gen(wl):  # the whole output (seconds at the workloads' sizes), then the pixels
+        full = oracle_full(wl, inp)
+        return full[pix[:, 0], pix[:, 1], pix[:, 2]]
     fn = {"dwpw": oracle.dwpw_at, "b2b": oracle.b2b_at, "pwdw": oracle.pwdw_at,
           "pwpw": oracle.pwpw_at}[wl.kind]
     return fn(inp["x"], inp["w1"], inp["w2"], pix, **oracle_kwargs(wl, inp))
@@ -69,8 +80,16 @@ def int_inputs(wl, seed: int) -> dict:
     x = rng.integers(-2, 3, size=(wl.N, wl.H, wl.W, wl.C)).astype(np.float64)
     if wl.kind == "pwdw":
         return _int_inputs_pwdw(wl, rng, x)
-    n1 = wl.C if wl.kind == "dwpw" else wl.K1
-    if wl.kind == "pwpw":
+    n1 = wl.C * wl.mult if wl.kind == "dwpw" else wl.K1
+    if is_gen(wl):
+        # at most 9 non-zero taps of +-1 per filter, whatever its size
+        w1 = np.zeros((n1, wl.R * wl.S))
+        for j in range(n1):
+            idx = rng.choice(wl.R * wl.S, size=min(9, wl.R * wl.S), replace=False)
+            w1[j, idx] = rng.integers(-1, 2, size=idx.size)
+        w1 = w1.reshape(n1, wl.R, wl.S)
+        acc1 = 9 * 2
+    elif wl.kind == "pwpw":
         w1 = np.zeros((wl.K1, wl.C))
         for k in range(wl.K1):
             idx = rng.choice(wl.C, size=min(6, wl.C), replace=False)
@@ -125,7 +144,7 @@ def all_variants_for(wl):
     import depthwise_pointwise_convolution_amd as F
     p = F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
                   None if wl.kind == "dwpw" else wl.K1, R=wl.R, S=wl.S, stride=wl.stride,
-                  pad=wl.pad, act1=wl.act1, act2=wl.act2)
+                  pad=wl.pad, act1=wl.act1, act2=wl.act2, dilation=wl.dil, mult=wl.mult)
     out = []
     for v in range(F.fcm_num_variants()):
         try:
@@ -148,6 +167,9 @@ REDUCED = {
     "mbv1i8_i8_8x112x112_c32_k64": dict(N=2, H=29, W=37),
     "pwpw_f16_32x56x56_c64_k32_k64": dict(N=2, H=29, W=37),
     "pwdw_f16_32x112x112_c16_k96_s2": dict(N=2, H=45, W=57),
+    "dw5_f16_32x28x28_c120_k40": dict(N=2, H=29, W=37),
+    "dil2_f16_8x33x33_c960_k160": dict(N=2, H=21, W=19),
+    "mult2_f16_8x112x112_c32_k128": dict(N=2, H=29, W=37),
 }
 
 

@@ -72,7 +72,7 @@ def test_library_has_no_undefined_own_symbols():
 def _problem(F, wl):
     return F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
                      None if wl.kind == "dwpw" else wl.K1, R=wl.R, S=wl.S, stride=wl.stride,
-                     pad=wl.pad, act1=wl.act1, act2=wl.act2)
+                     pad=wl.pad, act1=wl.act1, act2=wl.act2, dilation=wl.dil, mult=wl.mult)
 
 
 def _spec(F):
@@ -90,7 +90,7 @@ def test_plan_integers_match_oracle_accounting(name):
     full = wl.replace(scale1=True, bias1=True, scale2=True, bias2=True)
     assert pl.alg_bytes_fused == acct.alg_bytes(full, fused=True)
     assert pl.alg_bytes_unfused == acct.alg_bytes(full, fused=False)
-    n1 = wl.C if wl.kind == "dwpw" else wl.K1
+    n1 = wl.C * wl.mult if wl.kind == "dwpw" else wl.K1
     e = acct.ELEM_BYTES[wl.dtype]
     assert pl.workspace_bytes == acct.sizes(wl)["t"]
     if wl.kind != "pwdw":
@@ -321,7 +321,11 @@ def test_forced_variants_cover_every_compiled_kernel():
         fcm_inputs.Workload("q", "dwpw", "i8", N=2, H=17, W=23, C=c, K=k, K1=c, stride=s)
         for c in (32, 64) for k in (64, 112) for s in (1, 2)] + [
         fcm_inputs.Workload("r", "pwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=k1, R=1, S=1, pad=0)
-        for dt in ("f16", "bf16") for c in (32, 64) for k1 in (32, 64) for k in (64, 136)]
+        for dt in ("f16", "bf16") for c in (32, 64) for k1 in (32, 64) for k in (64, 136)] + [
+        fcm_inputs.Workload("g", "dwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=c * m, R=f, S=f,
+                            stride=s, pad=(f - 1) * d // 2, dil=d, mult=m)
+        for dt in ("f16", "bf16") for c, k in ((40, 48), (64, 136)) for s in (1, 2)
+        for f, d, m in ((5, 1, 1), (7, 1, 1), (3, 2, 1), (3, 1, 2))]
     for wl in shapes:
         prob = _problem(F, wl)
         for v in range(F.fcm_num_variants()):
@@ -459,3 +463,76 @@ def test_chain_planner_rejects_broken_chains():
     with pytest.raises(F.FcmError) as ei:
         F.fcm_plan_chain([("dw", 32, 64, 1, "none")], 1, 8, 8)
     assert ei.value.status == F.FCM_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------------
+# generalised depthwise layer (filter size, dilation, depth multiplier)
+# ---------------------------------------------------------------------------------
+def test_generalised_depthwise_problem_rules():
+    F = _lib()
+    spec = _spec(F)
+
+    def status(**kw):
+        base = dict(kind="dwpw", dtype="f16", N=1, H=20, W=20, C=32, K=64, R=5, S=5,
+                    stride=1, pad=2)
+        base.update(kw)
+        try:
+            F.fcm_plan(F.problem(**base), spec)
+            return F.FCM_OK
+        except F.FcmError as e:
+            assert F.lib().fcm_last_error()
+            return e.status
+
+    assert status() == F.FCM_OK
+    assert status(R=3, S=3, dilation=2) == F.FCM_OK
+    assert status(R=3, S=3, pad=1, mult=2) == F.FCM_OK
+    # output extent follows the dilated window: (20 + 4 - 5) + 1
+    pl = F.fcm_plan(F.problem("dwpw", "f16", 1, 20, 20, 32, 64, R=3, S=3, pad=2, dilation=2),
+                    spec)
+    assert (pl.Ho, pl.Wo) == (20, 20)
+    assert F.fcm_plan(F.problem("dwpw", "f16", 1, 20, 20, 32, 64, R=3, S=3, pad=0,
+                                dilation=2), spec).Ho == 16
+    # the depthwise layer has C * mult outputs
+    assert status(R=3, S=3, pad=1, mult=2, K1=32) == F.FCM_ERR_INVALID_ARG
+    # padding below the dilated extent, non-negative fields
+    assert status(R=3, S=3, dilation=2, pad=5) == F.FCM_ERR_INVALID_ARG
+    assert status(dilation=-1) == F.FCM_ERR_INVALID_ARG
+    assert status(mult=-2) == F.FCM_ERR_INVALID_ARG
+    # only the DW->PW module has a generalised depthwise layer
+    assert status(kind="b2b", R=3, S=3, pad=1, K1=64, dilation=2) == F.FCM_ERR_INVALID_ARG
+    assert status(kind="pwdw", R=3, S=3, pad=1, K1=64, mult=2) == F.FCM_ERR_INVALID_ARG
+    # shapes with no kernel
+    assert status(R=9, S=9, pad=4) == F.FCM_ERR_UNSUPPORTED
+    assert status(R=5, S=3, pad=1) == F.FCM_ERR_UNSUPPORTED
+    assert status(dtype="f32") == F.FCM_ERR_UNSUPPORTED
+    assert status(dtype="i8", C=32, K=64) == F.FCM_ERR_UNSUPPORTED
+    assert status(C=36) == F.FCM_ERR_UNSUPPORTED
+    # a valid combination that no variant is compiled for
+    assert status(mult=2) == F.FCM_ERR_UNSUPPORTED
+    # zero-initialised fields are the plain module (all its variants stay available)
+    p = F.problem("dwpw", "f16", 2, 17, 23, 64, 128)
+    p.dil_h = p.dil_w = p.mult = 0
+    assert F.fcm_plan(p, spec).variant == F.fcm_plan(F.problem("dwpw", "f16", 2, 17, 23, 64,
+                                                               128), spec).variant
+
+
+def test_generalised_plan_accounting_and_variant_match():
+    F = _lib()
+    spec = _spec(F)
+    for name in ("dw5_f16_32x28x28_c120_k40", "dil2_f16_8x33x33_c960_k160",
+                 "mult2_f16_8x112x112_c32_k128"):
+        wl = fcm_inputs.WORKLOADS[name]
+        pl = F.fcm_plan(_problem(F, wl), spec)
+        vname = F.fcm_variant_name(pl.variant)
+        assert vname.startswith("gen_"), vname
+        e = acct.ELEM_BYTES[wl.dtype]
+        assert pl.w1_packed_bytes == wl.C * wl.mult * wl.R * wl.S * e
+        # the packed pointwise filters: the plain [K][C*mult] array and its blocked copy
+        k32, c32 = -(-wl.K // 32) * 32, -(-wl.C * wl.mult // 32) * 32
+        assert pl.w2_packed_bytes == (wl.K * wl.C * wl.mult + k32 * c32) * e
+        assert pl.flops == acct.flops(wl)
+        # the fused module moves fewer compulsory bytes than its layers; the Eq.-style
+        # estimate (requests, weights re-read per tile) decides the fuse flag
+        assert pl.alg_bytes_fused < pl.alg_bytes_unfused
+        assert pl.fuse == (1 if pl.gma_paper_fused < pl.gma_paper_unfused else 0)
+        print(name, vname, pl.gma_paper_fused, pl.gma_paper_unfused, pl.fuse)
