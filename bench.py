@@ -38,7 +38,7 @@ KDIR = "depthwise_pointwise_convolution_amd/csrc/kernels/"
 # source file of each fused kernel family (by variant-name prefix) and the headers they share
 KERNEL_FILES = [("dwpw_i8_", "dwpw_i8.hip"), ("mmw_", "dwpw_mmw.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
                 ("dwpw_", "dwpw.hip"), ("b2b_", "b2b.hip"), ("pwdw_", "pwdw_mm.hip"),
-                ("pwpw_", "pwpw_mm.hip")]
+                ("pwpw_", "pwpw_mm.hip"), ("gen_", "dwpw_gen.hip")]
 SHARED_SOURCES = ["mm_common.h", "stages.h", "common.h"]
 
 
@@ -166,13 +166,16 @@ def cpu_baseline(wl, budget_s: float):
     kw = dict(stride=(wl.stride,) * 2, pad=(wl.pad,) * 2, scale1=inp["scale1"],
               bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],
               act2=wl.act2, dtype=wl.dtype)
+    fn = {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw,
+          "pwpw": oracle.pwpw}[wl.kind]
+    if wl.kind == "dwpw" and (wl.R != 3 or wl.S != 3 or wl.dil != 1 or wl.mult != 1):
+        fn = oracle.dwpw_gen  # generalised depthwise layer
+        kw["dilation"] = (wl.dil, wl.dil)
     times = []
     t_all = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw,
-         "pwpw": oracle.pwpw}[wl.kind](
-            inp["x"], inp["w1"], inp["w2"], **kw)
+        fn(inp["x"], inp["w1"], inp["w2"], **kw)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_all >= budget_s or len(times) >= 50:
             break
@@ -319,6 +322,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.description}", "N": wl.N, "H": wl.H,
                    "W": wl.W, "C": wl.C, "K": wl.K, "stride": wl.stride,
+                   "filter": [wl.R, wl.S], "dilation": wl.dil, "depth_multiplier": wl.mult,
                    "kernel_variant": vname, "grid": plan.grid,
                    "selection": "measured (fcm_tune)" if plan.tuned_us > 0 else "analytic plan",
                    "timing": "eager" if args.eager else "hip-graph",

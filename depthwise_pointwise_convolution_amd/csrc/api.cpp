@@ -596,7 +596,9 @@ fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
         FCM_TRY(check_variant(plan));
         const VariantDesc& v = kVariants[plan->variant];
         set_tiles(&a, lbl::DWG_TH, lbl::DWG_TW, 1, 1);
-        const int64_t grid = (int64_t)a.num_ptiles * ((plan->prob.C + v.cc - 1) / v.cc);
+        (void)v;
+        const int64_t grid =
+            (int64_t)a.num_ptiles * ((plan->prob.C + lbl::DWG_CC - 1) / lbl::DWG_CC);
         if (grid > INT32_MAX) return fail(FCM_ERR_UNSUPPORTED, "too many depthwise tiles");
         const int rc = kImpls[plan->variant].lbl_first(a, (int)grid, stream);
         if (rc != 0)

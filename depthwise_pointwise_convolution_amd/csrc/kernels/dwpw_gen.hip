@@ -11,8 +11,10 @@
 // channels and loops over such tiles (persistent grid).  Per tile and per chunk of CC
 // input channels it
 //   1. stages the input window ((TH-1)*S + (FS-1)*D + 1 rows, likewise columns) in LDS
-//      with 16-byte NHWC loads, zero-filled outside the image; the next chunk's loads
-//      are issued before this chunk's arithmetic and stay in flight through it;
+//      with 16-byte NHWC loads, zero-filled outside the image; the input and depthwise
+//      constants of a chunk are requested two chunks ahead (two register sets) and stay
+//      in flight through the arithmetic in between, and a chunk's pointwise operands are
+//      requested before its depthwise stage;
 //   2. runs the depthwise stencil on the vector ALU in fp32: a work item takes 16 bytes
 //      of input channels of one column and VB output rows, and produces the CC*M/CC
 //      outputs of each of those channels (output channel c*M + i reads input channel
@@ -48,6 +50,45 @@ __device__ __forceinline__ void stage_dw_gen_weights(float* wdw_s, float* s1s, f
         b1s[i] = (a.b1 && j < a.K1) ? a.b1[j] : 0.0f;
     }
 }
+
+// The same constants held in registers between their load and their LDS store, so a
+// chunk's filters can be requested one chunk ahead (with its input window) and written
+// to LDS at the start of the chunk: no load-wait-store round trip inside a chunk.
+template <typename T, int FS, int M, int CC, int NT>
+struct DwGenConsts {
+    static constexpr int CM = CC * M, NW = FS * FS * CM;
+    static constexpr int ITW = (NW + NT - 1) / NT, ITE = (CM + NT - 1) / NT;
+    float w[ITW], sc[ITE], bi[ITE];
+
+    __device__ __forceinline__ void load(const T* __restrict__ wg, const KArgs& a, int c0,
+                                         int tid) {
+        const int j0 = c0 * M;
+#pragma unroll
+        for (int i = 0; i < ITW; ++i) {
+            const int v = tid + i * NT;
+            const int t = v / CM, j = j0 + (v - t * CM);
+            w[i] = (v < NW && j < a.K1) ? (float)wg[t * a.K1 + j] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < ITE; ++i) {
+            const int j = j0 + tid + i * NT;
+            const bool in = tid + i * NT < CM && j < a.K1;
+            sc[i] = (a.s1 && in) ? a.s1[j] : 1.0f;
+            bi[i] = (a.b1 && in) ? a.b1[j] : 0.0f;
+        }
+    }
+    __device__ __forceinline__ void store(float* wdw_s, float* s1s, float* b1s, int tid) const {
+#pragma unroll
+        for (int i = 0; i < ITW; ++i)
+            if (tid + i * NT < NW) wdw_s[tid + i * NT] = w[i];
+#pragma unroll
+        for (int i = 0; i < ITE; ++i)
+            if (tid + i * NT < CM) {
+                s1s[tid + i * NT] = sc[i];
+                b1s[tid + i * NT] = bi[i];
+            }
+    }
+};
 
 // Generalised depthwise stencil + epilogue 1 over a TH x TW tile and one CC-channel
 // chunk in LDS.  Work item = (16-byte channel vector cg, output column, VB adjacent
@@ -149,8 +190,13 @@ void dwpw_gen_kernel(KArgs a) {
     const int per_img = a.tiles_h * a.tiles_w;
     const int nchunks = (a.C + CC - 1) / CC;
 
-    HaloTile<T, IH, IW, CC, NT> halo;
-    int pt = L / a.num_ktiles;
+    // The workgroup's steps are its (tile, chunk) pairs in order.  Two register sets
+    // hold the input window and depthwise constants of the next two steps, so every
+    // step's loads are issued two steps before it needs them (a step is short next to
+    // a memory round trip when the chunks are many, as in wide layers).
+    const int first = L / a.num_ktiles;
+    const int my_tiles = first < a.num_ptiles ? (a.num_ptiles - 1 - first) / pstep + 1 : 0;
+    const int nsteps = my_tiles * nchunks;
     auto tile_origin = [&](int t, int* n, int* oh0, int* ow0) {
         *n = t / per_img;
         const int rem = t - *n * per_img;
@@ -158,96 +204,103 @@ void dwpw_gen_kernel(KArgs a) {
         *oh0 = th * TH;
         *ow0 = (rem - th * a.tiles_w) * TW;
     };
-    if (pt < a.num_ptiles) {
-        int n, oh0, ow0;
-        tile_origin(pt, &n, &oh0, &ow0);
-        halo.load(x, a, n, oh0 * S - a.pad_h, ow0 * S - a.pad_w, 0, tid);
-    }
+    HaloTile<T, IH, IW, CC, NT> h0, h1;
+    DwGenConsts<T, FS, M, CC, NT> d0, d1;
+    auto issue = [&](HaloTile<T, IH, IW, CC, NT>& h, DwGenConsts<T, FS, M, CC, NT>& dc,
+                     int st) __attribute__((always_inline)) {
+        if (st < nsteps) {
+            const int ti = st / nchunks, c0 = (st - ti * nchunks) * CC;
+            int n, oh0, ow0;
+            tile_origin(first + ti * pstep, &n, &oh0, &ow0);
+            h.load(x, a, n, oh0 * S - a.pad_h, ow0 * S - a.pad_w, c0, tid);
+            dc.load(wdw, a, c0, tid);
+        }
+    };
+    issue(h0, d0, 0);
+    issue(h1, d1, 1);
     for (int i = tid; i < KT; i += NT) {
         const int k = k0 + i;
         s2s[i] = (a.s2 && k < a.K) ? a.s2[k] : 1.0f;
         b2s[i] = (a.b2 && k < a.K) ? a.b2[k] : 0.0f;
     }
 
-    for (; pt < a.num_ptiles; pt += pstep) {
-        int n, oh0, ow0;
-        tile_origin(pt, &n, &oh0, &ow0);
-        f32x4 acc[MBW][KB];
+    f32x4 acc[MBW][KB];
+    auto step = [&](HaloTile<T, IH, IW, CC, NT>& h, DwGenConsts<T, FS, M, CC, NT>& dc,
+                    int st) __attribute__((always_inline)) {
+        const int ti = st / nchunks, ci = st - ti * nchunks, c0 = ci * CC;
+        if (ci == 0) {
 #pragma unroll
-        for (int mi = 0; mi < MBW; ++mi)
+            for (int mi = 0; mi < MBW; ++mi)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) acc[mi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int ci = 0; ci < nchunks; ++ci) {
-            const int c0 = ci * CC;
-            halo.template store<XS>(xs, tid);
-            stage_dw_gen_weights<T, FS, M, CC, NT>(wdw_s, s1s, b1s, wdw, a, c0, tid);
-            __syncthreads();
-            // the next chunk (or the next tile's first chunk) is requested now; its
-            // loads stay in flight through this chunk's arithmetic
-            {
-                int nt = pt, nc = c0 + CC;
-                if (nc >= a.C) {
-                    nt = pt + pstep;
-                    nc = 0;
-                }
-                if (nt < a.num_ptiles) {
-                    int nn, noh0, now0;
-                    tile_origin(nt, &nn, &noh0, &now0);
-                    halo.load(x, a, nn, noh0 * S - a.pad_h, now0 * S - a.pad_w, nc, tid);
-                }
-            }
-            dw_gen_stage<T, S, FS, D, M, TH, TW, CC, XS, IW, VB, NT>(
-                xs, wdw_s, s1s, b1s, act1, tid, [&](int ohl, int col, int cgm, u32x4 v) {
-                    st16(ts + (ohl * TW + col) * TS + cgm * VN, v);
-                });
-            __syncthreads();
-            const int j0 = c0 * M;
-#pragma unroll
-            for (int mi = 0; mi < MBW; ++mi) {
-                const int row = (wave + 4 * mi) * 16 + lr;
-#pragma unroll
-                for (int ks = 0; ks < KSI; ++ks) {
-                    const u32x4 bfrag = ld16(ts + row * TS + ks * 32 + lg * 8);
-                    const int j = j0 + ks * 32 + lg * 8;
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        const int ko = k0 + kperm<KT>(kb, lr);
-                        const u32x4 afrag = (ko < a.K && j < a.K1)
-                                                ? ld16(wpw + (int64_t)ko * a.K1 + j)
-                                                : u32x4{0u, 0u, 0u, 0u};
-                        acc[mi][kb] = mfma<T>(afrag, bfrag, acc[mi][kb]);
-                    }
-                }
-            }
-            // No barrier here: the next chunk's LDS stores (xs, wdw_s, s1s, b1s) target
-            // data last read before the barrier above, and ts is rewritten only after
-            // the next staging barrier, which a wave reaches only once it is done
-            // reading ts.
+                for (int kb = 0; kb < KB; ++kb) acc[mi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-
+        h.template store<XS>(xs, tid);
+        dc.store(wdw_s, s1s, b1s, tid);
+        __syncthreads();
+        // this chunk's pointwise operands are requested before the depthwise stage, which
+        // hides their latency; then the loads of the step after next reuse h and dc
+        const int j0 = c0 * M;
+        u32x4 wa[KSI][KB];
+#pragma unroll
+        for (int ks = 0; ks < KSI; ++ks) {
+            const int j = j0 + ks * 32 + lg * 8;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int ko = k0 + kperm<KT>(kb, lr);
+                wa[ks][kb] = (ko < a.K && j < a.K1) ? ld16(wpw + (int64_t)ko * a.K1 + j)
+                                                    : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        issue(h, dc, st + 2);
+        dw_gen_stage<T, S, FS, D, M, TH, TW, CC, XS, IW, VB, NT>(
+            xs, wdw_s, s1s, b1s, act1, tid, [&](int ohl, int col, int cgm, u32x4 v) {
+                st16(ts + (ohl * TW + col) * TS + cgm * VN, v);
+            });
+        __syncthreads();
 #pragma unroll
         for (int mi = 0; mi < MBW; ++mi) {
-            const int px = (wave + 4 * mi) * 16 + lr;
-            const int oh = oh0 + px / TW, ow = ow0 + px % TW;
-            if (oh < a.Ho && ow < a.Wo) {
-                T* yp = y + (((int64_t)n * a.Ho + oh) * a.Wo + ow) * a.K + k0;
+            const int row = (wave + 4 * mi) * 16 + lr;
 #pragma unroll
-                for (int kb = 0; kb < KB; kb += 2) {
-                    const int kl = lg * (KT / 4) + kb * 4;
-                    if (k0 + kl < a.K) {
-                        float o[8];
+            for (int ks = 0; ks < KSI; ++ks) {
+                const u32x4 bfrag = ld16(ts + row * TS + ks * 32 + lg * 8);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            o[i] = epilogue(acc[mi][kb][i], s2s[kl + i], b2s[kl + i], act2);
-                            o[4 + i] = epilogue(acc[mi][kb + 1][i], s2s[kl + 4 + i],
-                                                b2s[kl + 4 + i], act2);
+                for (int kb = 0; kb < KB; ++kb)
+                    acc[mi][kb] = mfma<T>(wa[ks][kb], bfrag, acc[mi][kb]);
+            }
+        }
+        // No barrier here: the next step's LDS stores (xs, wdw_s, s1s, b1s) target data
+        // last read before the barrier above, and ts is rewritten only after the next
+        // step's first barrier, which a wave reaches only once it is done reading ts.
+        if (ci == nchunks - 1) {
+            int n, oh0, ow0;
+            tile_origin(first + ti * pstep, &n, &oh0, &ow0);
+#pragma unroll
+            for (int mi = 0; mi < MBW; ++mi) {
+                const int px = (wave + 4 * mi) * 16 + lr;
+                const int oh = oh0 + px / TW, ow = ow0 + px % TW;
+                if (oh < a.Ho && ow < a.Wo) {
+                    T* yp = y + (((int64_t)n * a.Ho + oh) * a.Wo + ow) * a.K + k0;
+#pragma unroll
+                    for (int kb = 0; kb < KB; kb += 2) {
+                        const int kl = lg * (KT / 4) + kb * 4;
+                        if (k0 + kl < a.K) {
+                            float o[8];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                o[i] = epilogue(acc[mi][kb][i], s2s[kl + i], b2s[kl + i], act2);
+                                o[4 + i] = epilogue(acc[mi][kb + 1][i], s2s[kl + 4 + i],
+                                                    b2s[kl + 4 + i], act2);
+                            }
+                            st16(yp + kl, pack16<T>(o));
                         }
-                        st16(yp + kl, pack16<T>(o));
                     }
                 }
             }
         }
+    };
+    for (int st = 0; st < nsteps; st += 2) {
+        step(h0, d0, st);
+        if (st + 1 < nsteps) step(h1, d1, st + 1);
     }
 }
 
@@ -309,12 +362,14 @@ int occ_dwpw_gen() {
     return n;
 }
 // The layer-by-layer depthwise kernel for the variant's (type, stride, filter,
-// dilation, multiplier, chunk); the caller sets tiles_h / tiles_w for lbl::DWG_TH x lbl::DWG_TW
-// tiles and launches num_ptiles * ceil(C / CC) workgroups.
+// dilation, multiplier), with the baseline's own fixed tiling whatever the fused
+// variant's chunk: the caller sets tiles_h / tiles_w for lbl::DWG_TH x lbl::DWG_TW tiles
+// and launches num_ptiles * ceil(C / lbl::DWG_CC) workgroups.
 template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC>
 int launch_dw_gen_lbl(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((dw_gen_lbl_kernel<T, S, FS, D, M, lbl::DWG_TH, lbl::DWG_TW, CC>), dim3(grid),
+    hipLaunchKernelGGL((dw_gen_lbl_kernel<T, S, FS, D, M, lbl::DWG_TH, lbl::DWG_TW, lbl::DWG_CC>),
+                       dim3(grid),
                        dim3(256), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }

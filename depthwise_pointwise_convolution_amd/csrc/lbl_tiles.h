@@ -12,6 +12,7 @@ constexpr int PW_MBW16 = 2;             // 16-pixel blocks per wave (128 pixels 
 constexpr int PW_MT16 = 64 * PW_MBW16;  // pixels per workgroup
 constexpr int PW_KT32 = 64, PW_MT32 = 4;
 constexpr int DWG_TH = 4, DWG_TW = 16;  // generalised depthwise output tile
+constexpr int DWG_CC = 32;              // and its input channels per workgroup
 constexpr int CV_TH = 4, CV_TW = 16, CV_KT = 64, CV_CC = 64;  // 3x3 conv
 }  // namespace lbl
 }  // namespace fcm

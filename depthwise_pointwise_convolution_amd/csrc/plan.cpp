@@ -182,11 +182,14 @@ int variant_vgpr_estimate(const VariantDesc& v) {
     const int MBW = P / 64;
     switch (v.vkind) {
     case VK_DWPW_GEN: {
-        // accumulators, the next chunk's input in flight, one depthwise item's sums
+        // accumulators, the chunk's pointwise operands, the next chunk's input and
+        // depthwise constants in flight, one depthwise item's sums
         const int KB = v.kt / 16, ext = (v.fs - 1) * v.dil + 1;
         const int slots = ((v.th - 1) * v.stride + ext) * ((v.tw - 1) * v.stride + ext) *
                           (v.cc / 8);
-        return 40 + MBW * KB * 4 + 4 * ((slots + 255) / 256) + 8 * v.mult + 24;
+        const int consts = (v.fs * v.fs * v.cc * v.mult + 255) / 256;
+        return 40 + MBW * KB * 4 + (v.cc * v.mult / 32) * KB * 4 + 4 * ((slots + 255) / 256) +
+               consts + 8 * v.mult + 24;
     }
     case VK_DWPW: {
         const int KB = v.kt / 16, KS = v.cc / 32;
@@ -1109,7 +1112,7 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     int64_t pu = 0;
     double gu = 0;
     if (prob_is_gen(*p))
-        estimate_unfused_gen(*p, v.cc, Ho, Wo, &pu, &gu);
+        estimate_unfused_gen(*p, lbl::DWG_CC, Ho, Wo, &pu, &gu);
     else
         estimate_unfused(*p, d, Ho, Wo, &pu, &gu);
     pl.pred_bytes_unfused = pu;
