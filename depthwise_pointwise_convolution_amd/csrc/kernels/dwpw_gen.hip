@@ -2,9 +2,10 @@
 // filter (3, 5 or 7), a dilation D between the taps and a depth multiplier M (M filters
 // per input channel, so the depthwise layer has C*M outputs and the pointwise layer
 // reduces over C*M channels).  The depthwise layer is the one the PyTorch forum thread
-// "Using optimised depthwise convolutions" writes as nn.Conv2d(in_chans, in_chans * k,
-// kernel_size, groups = in_chans), with the dilation its SeparableConv2d listing passes
-// on; the fusion is the FCM paper's DWPW module ("Fusing Depthwise and Pointwise
+// "Using optimised depthwise convolutions" describes: a grouped convolution with one
+// group per input channel, k outputs per group and any filter size, which its
+// separable-convolution module also builds with a dilation; the fusion is the FCM
+// paper's DWPW module ("Fusing Depthwise and Pointwise
 // Convolutions for Efficient Inference on GPUs", Sec. III, Fig. 3(b)).
 //
 // One workgroup (4 waves) owns a TH x TW output tile and a KT-wide slice of the output

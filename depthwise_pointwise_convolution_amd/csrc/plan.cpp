@@ -717,7 +717,7 @@ Estimate estimate_pwdw(const VariantDesc& v, const fcm_problem& p, const fcm_dev
         r.gma = (2.0 * p.C * overlap * p.N * e + ifm) *
                     std::max(ceil(w_pw / w_pw_tile), ceil(w_dw / w_dw_tile)) +
                 ceil(ofm / ofm_tile) * w_pw +
-                ceil((double)Ho * Wo / ((double)v.th * v.tw)) * w_dw + ofm;
+                ceil((double)p.N * Ho * Wo / ((double)v.th * v.tw)) * w_dw + ofm;
     }
     return r;
 }
@@ -813,9 +813,10 @@ void estimate_unfused_gen(const fcm_problem& p, int cc, int Ho, int Wo, int64_t*
                                        p.stride_h);
     const double w1 = (double)p.R * p.S * p.K1 * e;
     const double g1 = 2.0 * p.C * overlap * p.N * e + ifm + (double)t_bytes +
-                      ceil((double)Ho * Wo / (th * tw)) * p.N * w1;
-    const double g2 = ceil(w2 / ((double)std::min(lbl::PW_KT16, p.K) * p.K1 * e)) * t_bytes +
-                      (double)y_bytes + ceil((double)m / lbl::PW_MT16) * w2;
+                      ceil((double)p.N * Ho * Wo / (th * tw)) * w1;
+    const double kt2 = (double)std::min(lbl::PW_KT16, p.K);
+    const double g2 = ceil(w2 / (kt2 * p.K1 * e)) * t_bytes + (double)y_bytes +
+                      ceil((double)y_bytes / ((double)lbl::PW_MT16 * kt2 * e)) * w2;
     *gma = g1 + g2;
 }
 
@@ -888,7 +889,7 @@ void estimate_unfused_pwdw(const fcm_problem& p, int Ho, int Wo, int64_t* pred, 
                       ceil((double)t_bytes / ((double)mt * std::min(kt, p.K1) * e)) * w_pw;
     const double overlap = eq1_overlap(p.W, p.H, tw * p.stride_w, th * p.stride_h, 3, p.stride_h);
     const double g2 = 2.0 * p.K1 * overlap * p.N * e + (double)t_bytes + (double)y_bytes +
-                      ceil((double)Ho * Wo / (double)(th * tw)) * 9.0 * p.K1 * e;
+                      ceil((double)p.N * Ho * Wo / (double)(th * tw)) * 9.0 * p.K1 * e;
     *gma = g1 + g2;
 }
 
@@ -941,7 +942,7 @@ void estimate_unfused(const fcm_problem& p, const fcm_device_spec& d, int Ho, in
              (double)t_bytes + ceil((double)t_bytes / ((double)th * tw * lbl::CV_KT * e)) * w1;
     } else {
         g1 = 2.0 * p.C * overlap * p.N * e + ifm + (double)t_bytes +
-             ceil((double)Ho * Wo / (double)(th * tw)) * 9.0 * p.C * e;
+             ceil((double)p.N * Ho * Wo / (double)(th * tw)) * 9.0 * p.C * e;
     }
     const double g2 = ceil((double)w2 / ((double)std::min(kt, p.K) * n1 * e)) * (double)t_bytes +
                       (double)y_bytes + ceil((double)y_bytes / ((double)mt * std::min(kt, p.K) * e)) *
@@ -1141,7 +1142,7 @@ double single_layer_gma(const fcm_layer& l, int N, int H, int W, int e) {
         const double ifm = (double)N * H * W * l.C * e, ofm = (double)N * Ho * Wo * l.C * e;
         const double overlap = eq1_overlap(W, H, tw * l.stride, th * l.stride, 3, l.stride);
         return 2.0 * l.C * overlap * N * e + ifm + ofm +
-               ceil((double)Ho * Wo / (double)(th * tw)) * 9.0 * l.C * e;
+               ceil((double)N * Ho * Wo / (double)(th * tw)) * 9.0 * l.C * e;
     }
     const int mt = e == 4 ? lbl::PW_MT32 : lbl::PW_MT16, kt = e == 4 ? lbl::PW_KT32 : lbl::PW_KT16;
     const double ifm = (double)N * H * W * l.C * e, ofm = (double)N * H * W * l.K * e;

@@ -86,17 +86,22 @@ typedef struct {
     int32_t dtype;    /* fcm_dtype of activations and weights */
     int32_t N, H, W;  /* input batch and spatial extent */
     int32_t C;        /* input channels */
-    int32_t K1;       /* B2B: output channels of the first conv.  DWPW: must equal C.
-                         PWDW: output channels of the pointwise layer */
+    int32_t K1;       /* B2B: output channels of the first conv.  DWPW: must equal
+                         C * mult (the depthwise layer's outputs).  PWDW: output
+                         channels of the pointwise layer */
     int32_t K;        /* output channels of the module (PWDW: must equal K1) */
-    int32_t R, S;     /* the RxS conv's filter height/width (only 3x3 has kernels) */
+    int32_t R, S;     /* the RxS conv's filter height/width: 3x3 for every module;
+                         the DWPW module also takes 5x5 and 7x7 depthwise filters
+                         (the combinations compiled into the library; any other is
+                         FCM_ERR_UNSUPPORTED) */
     int32_t stride_h, stride_w, pad_h, pad_w; /* of the RxS conv (the first layer for
                          DWPW and B2B, the second for PWDW); the 1x1 is stride 1 */
     int32_t act1, act2; /* fcm_act after the first / second conv */
     /* Generalised depthwise layer of a DWPW module (PyTorch forum "Using optimised
-     * depthwise convolutions": the depthwise layer nn.Conv2d(in_chans, in_chans * k,
-     * kernel_size, groups = in_chans), and the dilation its SeparableConv2d listing
-     * passes).  0 means 1, so a zero-initialised problem is the plain module.
+     * depthwise convolutions": a grouped convolution with one group per input
+     * channel and k outputs per group, any filter size, and the dilation the
+     * thread's separable module gives it).  0 means 1, so a zero-initialised
+     * problem is the plain module.
      *  - dil_h, dil_w: spacing of the filter taps; the window of one output spans
      *    (R-1)*dil_h + 1 rows and (S-1)*dil_w + 1 columns, and Ho, Wo follow from
      *    that extent;

@@ -373,9 +373,9 @@ def pwpw_at(x, w1, w2, pix, **kw):
 
 # ---------------------------------------------------------------------------------
 # generalised depthwise layer: R x S filters, dilation, depth multiplier
-# (PyTorch forum "Using optimised depthwise convolutions": nn.Conv2d(in_chans,
-# in_chans * k, kernel_size, groups=in_chans), and the SeparableConv2d listing's
-# dilation argument)
+# (PyTorch forum "Using optimised depthwise convolutions": a grouped convolution with
+# one group per input channel and k outputs per group, any filter size, and the
+# dilation the thread's separable module gives it)
 # ---------------------------------------------------------------------------------
 def dw_gen(x, w_dw, stride=(1, 1), pad=(1, 1), dilation=(1, 1)) -> np.ndarray:
     """Depthwise layer with w_dw [C*M][R][S]: output channel j reads input channel j // M."""

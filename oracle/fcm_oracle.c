@@ -20,10 +20,10 @@
  *   PW -> PW module  -- two pointwise layers (the PWPW fusion case, FCM paper Sec. III,
  *                       Table II): pixel by pixel, so a tile needs no halo;
  *   generalised DW   -- any R x S filter, a dilation and a depth multiplier m (PyTorch
- *                       forum "Using optimised depthwise convolutions": the depthwise
- *                       layer with in_chans * k outputs, groups = in_chans, and the
- *                       SeparableConv2d listing's dilation); output channel j reads input
- *                       channel j / m;
+ *                       forum "Using optimised depthwise convolutions": a grouped
+ *                       convolution with one group per input channel and k outputs per
+ *                       group, dilated in the thread's separable module); output
+ *                       channel j reads input channel j / m;
  *   standard conv    -- the first layer of the back-to-back pair, [N,H,W,C] x
  *                       [K,C,R,S] ("Fusing two back-to-back convolutions", the
  *                       CONV1/CONV2 example);
@@ -453,10 +453,10 @@ int fcm_oracle_pwpw(const double* x, int64_t M, int C, const double* w1, int K1,
 
 /* ------------------------------------------------------------------------------ */
 /* Generalised depthwise layer: any R x S filter, dilation and depth multiplier.    */
-/* The PyTorch forum thread "Using optimised depthwise convolutions" defines the     */
-/* depthwise layer as nn.Conv2d(in_chans, in_chans * k, kernel_size,                 */
-/* groups = in_chans) -- k filters per input channel, any filter size -- and its      */
-/* SeparableConv2d listing passes a dilation to that layer.  With groups = C, output  */
+/* The PyTorch forum thread "Using optimised depthwise convolutions" describes the   */
+/* depthwise layer as a grouped convolution with one group per input channel and k  */
+/* filters per group, any filter size; its separable module also gives that layer a */
+/* dilation.  With one group per channel (C groups), output                        */
 /* channel j belongs to group j / k, i.e. reads input channel j / k; a dilation d     */
 /* spaces the filter taps d pixels apart.                                            */
 /* ------------------------------------------------------------------------------ */

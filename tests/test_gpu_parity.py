@@ -5,6 +5,8 @@ Bars: bit-exact on integer probes (every step exact, so any index, halo, stride,
 padding, tiling or layout mistake shows); normwise max relative error <= 1e-5 for
 fp32 storage and <= 2e-2 (fp32 accumulation) for fp16/bf16 otherwise.
 """
+import zlib
+
 import numpy as np
 import pytest
 
@@ -106,7 +108,8 @@ def _int_workload(case):
 @pytest.mark.parametrize("case", CASES_INT, ids=lambda c: "-".join(map(str, c[:10])))
 def test_integer_probes_bit_exact_every_variant(case):
     wl = _int_workload(case)
-    inp = int_inputs(wl, seed=sum(map(hash, map(str, case))) % 1000)
+    seed = zlib.crc32(repr(case).encode()) % 1000
+    inp = int_inputs(wl, seed=seed)
     ref = oracle_full(wl, inp)
     variants = all_variants_for(wl)
     assert variants, "no variant runs this problem"
@@ -114,9 +117,10 @@ def test_integer_probes_bit_exact_every_variant(case):
         _log(f"case int {case} variant {v}")
         got, _ = run_gpu(wl, inp, variant=v)
         bad = np.argwhere(got != ref)
-        assert bad.size == 0, f"variant {v}: {len(bad)} mismatches, first {bad[:3].tolist()}"
+        assert bad.size == 0, (f"variant {v} (input seed {seed}): {len(bad)} mismatches, "
+                               f"first {bad[:3].tolist()}")
     got, _ = run_gpu(wl, inp, path="unfused")
-    assert np.array_equal(got, ref), "layer-by-layer path"
+    assert np.array_equal(got, ref), f"layer-by-layer path (input seed {seed})"
 
 
 @pytest.mark.parametrize("name", NAMES)

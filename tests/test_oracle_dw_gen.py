@@ -1,7 +1,7 @@
 """Pins for the oracle's generalised depthwise layer (R x S filters, dilation, depth
-multiplier; PyTorch forum "Using optimised depthwise convolutions": the depthwise layer
-nn.Conv2d(in_chans, in_chans * k, kernel_size, groups=in_chans) and the SeparableConv2d
-listing's dilation argument) and of the DW->PW module built on it.
+multiplier; PyTorch forum "Using optimised depthwise convolutions": a grouped
+convolution with one group per input channel and k outputs per group, any filter size,
+dilated in the thread's separable module) and of the DW->PW module built on it.
 
 Each pin relies on something other than the generalised code itself: the library's
 grouped, dilated convolution; pure-Python loops on tiny inputs; the oracle's plain

@@ -679,3 +679,161 @@ def test_equations_mark_infeasible_tilings_infinite():
     assert accounting.dwpw_gma(8, 0, 10, 1, 1, 1, 10, 10, 100, 4, 99, 1) == float("inf")
     assert accounting.eq4_pwdw_gma(1, 0, 1, 1, 1, 1, 1, 1, 1, 1, 1, 5, 1, 4, 1) == \
         float("inf")
+
+
+# ---------------------------------------------------------------------------------
+# the sampled back-to-back checker (used at full size on the GPU) against the full one
+# ---------------------------------------------------------------------------------
+@pytest.mark.parametrize("stride,pad,H,W", [(1, 1, 9, 20), (2, 0, 11, 13), (2, 1, 10, 17),
+                                            (1, 0, 7, 6)])
+def test_b2b_sampled_rows_equal_full_outputs(stride, pad, H, W):
+    # the back-to-back workload's recipe (channels, epilogues, distributions) on a
+    # reduced plane; the sampled form sums in another order, but every value here is
+    # computed in fp64 and rounded once per storage point, so rows must agree exactly
+    wl = fcm_inputs.WORKLOADS["b2b_f16_32x56x56_c64"].replace(N=2, H=H, W=W, stride=stride,
+                                                             pad=pad)
+    inp = fcm_inputs.make_inputs(wl)
+    kw = dict(stride=(stride, stride), pad=(pad, pad), scale1=inp["scale1"],
+              bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],
+              act2=wl.act2, dtype=wl.dtype)
+    full = oracle.b2b(inp["x"], inp["w1"], inp["w2"], **kw)
+    assert full.shape == (2, wl.Ho, wl.Wo, wl.K)
+    pix = fcm_inputs.sample_pixels(wl, 40)
+    rows = oracle.b2b_at(inp["x"], inp["w1"], inp["w2"], pix, **kw)
+    assert np.array_equal(rows, full[pix[:, 0], pix[:, 1], pix[:, 2]])
+    # and every pixel of one image, so the borders of a stride/pad combination are covered
+    every = np.array([(1, h, w) for h in range(wl.Ho) for w in range(wl.Wo)], np.int32)
+    assert np.array_equal(oracle.b2b_at(inp["x"], inp["w1"], inp["w2"], every, **kw),
+                          full[1].reshape(-1, wl.K))
+
+
+def test_b2b_sampled_rows_match_library_pipeline():
+    # independent of the full C checker: the sampled rows against torch's fp64 conv2d
+    # pipeline with the same storage rounding
+    wl = fcm_inputs.WORKLOADS["b2b_f16_32x56x56_c64"].replace(N=1, H=8, W=9, C=16, K1=24, K=8)
+    inp = fcm_inputs.make_inputs(wl)
+    x = torch.from_numpy(inp["x"]).permute(0, 3, 1, 2)
+    t = F.conv2d(x, torch.from_numpy(inp["w1"]), padding=1)
+    t = t * torch.from_numpy(inp["scale1"])[None, :, None, None] + \
+        torch.from_numpy(inp["bias1"])[None, :, None, None]
+    t = torch.from_numpy(oracle.round_to(t.clamp(min=0).numpy(), "f16"))
+    y = F.conv2d(t, torch.from_numpy(inp["w2"])[:, :, None, None])
+    y = y * torch.from_numpy(inp["scale2"])[None, :, None, None] + \
+        torch.from_numpy(inp["bias2"])[None, :, None, None]
+    y = oracle.round_to(y.clamp(min=0).permute(0, 2, 3, 1).numpy(), "f16")
+    pix = np.array([(0, h, w) for h in range(8) for w in range(9)], np.int32)
+    rows = oracle.b2b_at(inp["x"], inp["w1"], inp["w2"], pix, scale1=inp["scale1"],
+                         bias1=inp["bias1"], act1="relu", scale2=inp["scale2"],
+                         bias2=inp["bias2"], act2="relu", dtype="f16")
+    # fp64 sums in different orders may differ in the last bit before the rounding to
+    # fp16; a flip of one fp16 step is the most that can result
+    ref = y.reshape(-1, 8)
+    assert np.max(np.abs(rows - ref) / np.maximum(np.abs(ref), 2.0 ** -14)) <= 2.0 ** -10
+
+
+# ---------------------------------------------------------------------------------
+# Eq. 4 and the constructed DW->PW estimate against a simulated tiled execution
+# ---------------------------------------------------------------------------------
+def _simulate_module_accesses(kind, H, W, C, n1, K, tile_h, tile_w, ct, filt, e):
+    """Element-by-element count of the global memory accesses (bytes) of a tiled module
+    at stride 1, under the access model the FusePlanner equations describe (FCM paper
+    Sec. IV, Fig. 3): the plane is cut into tile_h x tile_w tiles; a tile's input window
+    reaches (filt - 1) pixels past every border it shares with another tile (so the
+    overlap of each border is fetched by the tiles on both sides of it); the channels
+    that a weight tile produces form one work item per spatial tile.  Each work item
+    loads its window over all C input channels and the weight tile(s) it needs, and
+    writes its output.  kind "dwpw": the channel tile is a slice of ct output channels of
+    the pointwise layer, every work item recomputes the whole depthwise layer (all n1 =
+    C channels: all depthwise filters) and loads its slice of the pointwise filters.
+    kind "pwdw": the channel tile is a slice of ct intermediate channels, carried through
+    both layers: its slice of the pointwise filters and of the depthwise filters.
+    Returns (total bytes, number of work items)."""
+    ext = filt - 1
+    loads = np.zeros((H, W), np.int64)
+    n_sp = 0
+    for y0 in range(0, H, tile_h):
+        for x0 in range(0, W, tile_w):
+            n_sp += 1
+            ya = y0 - (ext if y0 > 0 else 0)
+            yb = min(H, y0 + tile_h) + (ext if y0 + tile_h < H else 0)
+            xa = x0 - (ext if x0 > 0 else 0)
+            xb = min(W, x0 + tile_w) + (ext if x0 + tile_w < W else 0)
+            loads[ya:yb, xa:xb] += 1
+    n_out = K if kind == "dwpw" else n1
+    n_ct = -(-n_out // ct)
+    window_bytes = int(loads.sum()) * C * e            # one pass over every window
+    total = n_ct * window_bytes
+    for c0 in range(0, n_out, ct):
+        cw = min(ct, n_out - c0)
+        if kind == "dwpw":
+            per_item = filt * filt * n1 * e + cw * n1 * e
+        else:
+            per_item = cw * C * e + filt * filt * cw * e
+        total += n_sp * per_item
+    total += H * W * n_out * e                          # the module's output, once
+    return total, n_sp * n_ct
+
+
+@pytest.mark.parametrize("H,W,th,tw", [(12, 12, 12, 4), (12, 12, 3, 12), (10, 16, 10, 4),
+                                       (9, 9, 9, 9)])
+@pytest.mark.parametrize("kind", ["dwpw", "pwdw"])
+def test_fcm_estimates_equal_simulated_accesses_without_channel_split(kind, H, W, th, tw):
+    # tiles split one direction of the plane (Eq. 1 is exact there) and one channel
+    # tile covers every channel: the FCM estimate equals the simulated access count
+    C, n1, K, e, filt = 8, 24, 16, 2, 3
+    if kind == "dwpw":
+        n1 = C
+    ch = K if kind == "dwpw" else n1
+    sim, items = _simulate_module_accesses(kind, H, W, C, n1, K, th, tw, ch, filt, e)
+    ov = accounting.eq1_overlap(W, H, tw, th, filt, filt, 1)
+    ifm = H * W * C * e
+    ofm = H * W * ch * e
+    if kind == "dwpw":
+        est = accounting.dwpw_gma(C, ov * e, ifm, 9 * C * e, K * C * e, K * C * e, ofm,
+                                  th * tw * K * e, 0, items, 1, 1)
+    else:
+        est = accounting.eq4_pwdw_gma(C, ov * e, ifm, n1 * C * e, n1 * C * e, 9 * n1 * e,
+                                      9 * n1 * e, ofm, th * tw * n1 * e, H * W, th * tw, 0,
+                                      items, 1, 1)
+    assert est == sim
+
+
+@pytest.mark.parametrize("ct", [4, 8])
+@pytest.mark.parametrize("kind", ["dwpw", "pwdw"])
+def test_fcm_estimates_charge_whole_filters_per_output_tile(kind, ct):
+    # with the channels split into tiles the printed equations still charge the whole
+    # pointwise filter array per output tile (the literal form); the simulation loads
+    # only each tile's slice, and every other term agrees exactly
+    H, W, th, tw, C, e, filt = 12, 16, 12, 4, 8, 2, 3
+    n1 = C if kind == "dwpw" else 16
+    K = 16
+    ch = K if kind == "dwpw" else n1
+    sim, items = _simulate_module_accesses(kind, H, W, C, n1, K, th, tw, ct, filt, e)
+    ov = accounting.eq1_overlap(W, H, tw, th, filt, filt, 1)
+    ifm, ofm = H * W * C * e, H * W * ch * e
+    if kind == "dwpw":
+        est = accounting.dwpw_gma(C, ov * e, ifm, 9 * C * e, K * C * e, ct * C * e, ofm,
+                                  th * tw * ct * e, 0, items, 1, 1)
+        whole, tile = K * C * e, ct * C * e
+    else:
+        est = accounting.eq4_pwdw_gma(C, ov * e, ifm, n1 * C * e, ct * C * e, 9 * n1 * e,
+                                      9 * ct * e, ofm, th * tw * ct * e, H * W, th * tw, 0,
+                                      items, 1, 1)
+        whole, tile = n1 * C * e, ct * C * e
+    assert est - sim == items * (whole - tile)
+
+
+def test_eq4_weight_tile_count_is_the_larger_layers():
+    # the PW input is re-read once per weight tile of whichever layer needs more tiles
+    base = dict(pw_ifms_d=4, dw_overlap=10, pw_ifms_sz=1000, pw_weights_sz=64,
+                dw_weights_sz=36, dw_ofms_sz=500, dw_ofms_tile_sz=500, dw_ofms_hw=10,
+                dw_ofms_tile_hw=10, tiles_sz_sum=0, n_fcm_ofm_tiles=1, l1_sz=1, n_sms=1)
+    one = accounting.eq4_pwdw_gma(pw_weights_tile_sz=64, dw_weights_tile_sz=36, **base)
+    assert one == (2 * 4 * 10 + 1000) + 64 + 36 + 500
+    pw4 = accounting.eq4_pwdw_gma(pw_weights_tile_sz=16, dw_weights_tile_sz=36, **base)
+    dw3 = accounting.eq4_pwdw_gma(pw_weights_tile_sz=64, dw_weights_tile_sz=12, **base)
+    assert pw4 - one == 3 * (2 * 4 * 10 + 1000)
+    assert dw3 - one == 2 * (2 * 4 * 10 + 1000)
+    # and without the output term added by reading (iii), the value printed on the page
+    assert accounting.eq4_pwdw_gma(pw_weights_tile_sz=64, dw_weights_tile_sz=36,
+                                   include_output=False, **base) == one - 500
