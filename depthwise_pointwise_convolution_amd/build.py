@@ -28,6 +28,7 @@ SOURCES = [
     ("kernels/dwpw.hip", True),
     ("kernels/dwpw_mm.hip", True),
     ("kernels/dwpw_mmw.hip", True),
+    ("kernels/dwpw_ws.hip", True),
     ("kernels/b2b_mm.hip", True),
     ("kernels/pwdw_mm.hip", True),
     ("kernels/dwpw_i8.hip", True),

@@ -52,6 +52,8 @@ const VariantImpl kImpls[] = {
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
     {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>,           \
      occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>},
+#define FCM_V_DWPW_WS(name, dt, CTy, S, TH, TW, CT, KT, NW) \
+    {launch_dwpw_ws<CTy, S, TH, TW, CT, KT, NW>, occ_dwpw_ws<CTy, S, TH, TW, CT, KT, NW>},
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {launch_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>, occ_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>},
 #define FCM_V_DWPW_I8(name, S, OCC) {launch_dwpw_i8<S, OCC>, occ_dwpw_i8<S, OCC>},
@@ -68,6 +70,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_PWDW_MM
+#undef FCM_V_DWPW_WS
 #undef FCM_V_DWPW_I8
 #undef FCM_V_PWPW_MM
 #undef FCM_V_DWPW_GEN

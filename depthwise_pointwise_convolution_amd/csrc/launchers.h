@@ -27,6 +27,11 @@ int launch_dwpw_mmw(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
 int occ_dwpw_mmw();
 
+template <typename T, int S, int TH, int TW, int CT, int KT, int NW>
+int launch_dwpw_ws(const KArgs& a, int grid, void* stream);
+template <typename T, int S, int TH, int TW, int CT, int KT, int NW>
+int occ_dwpw_ws();
+
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
 int launch_pwdw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>

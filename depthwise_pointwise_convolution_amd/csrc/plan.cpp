@@ -48,6 +48,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC, 4, 0, 0},
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
     {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0},
+#define FCM_V_DWPW_WS(name, dt, CTy, S, TH, TW, CT, KT, NW) \
+    {#name, VK_DWPW_WS, dt, S, TH, TW, KT, CT, 1, 2, 0, NW / 4, NW, CT, 0},
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {#name, VK_PWDW_MM, dt, S, TH, 16, NW * BPW * 16, CMAX, 1, 2, 0, OCC, NW, CMAX, BPW},
 #define FCM_V_DWPW_I8(name, S, OCC) \
@@ -64,6 +66,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_PWDW_MM
+#undef FCM_V_DWPW_WS
 #undef FCM_V_DWPW_I8
 #undef FCM_V_PWPW_MM
 #undef FCM_V_DWPW_GEN
@@ -150,6 +153,16 @@ int variant_lds_bytes(const VariantDesc& v) {
         return v.nbuf * slots_p * 16 + 2 * mb * (v.cc / 32) * 64 * 16 + 2 * v.kt * 4 +
                v.cmax * (9 * 2 + 2 * 4);
     }
+    case VK_DWPW_WS: {
+        // three input windows (whole direct-load rounds of the depthwise half of the
+        // waves, plus one wave's landing slots for the partial round) and three
+        // intermediate blocks of 16 pixels x cc channels
+        const int nt = 64 * (v.waves / 2);
+        const int slots = IH * IW * (v.cc / 8);
+        const int rf = slots / nt, rem = slots - rf * nt;
+        const int slots_b = rf * nt + (rem + 63) / 64 * 64 + (rem > 0 ? 64 : 0);
+        return 3 * slots_b * 16 + 3 * (v.cc / 32) * 1024;
+    }
     case VK_PWPW_MM: {
         // two input tiles of th x 16 pixels x 64 channels, two intermediate tiles of
         // th x 16 pixels x 64 channels
@@ -225,6 +238,20 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         const int ppw = mb * 4 / v.waves;
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
         return 4 * mb * kbw + 16 * kbw + 28 + 5 * ppw + 2 * ((slots + nt - 1) / nt) + 36 + 24;
+    }
+    case VK_DWPW_WS: {
+        // the larger of the two roles: a pointwise wave holds its output channels'
+        // operands over all cc inputs, one step's intermediate operands, accumulators and
+        // epilogue constants; a depthwise wave its channel blocks' diagonal operands (5 x 4
+        // registers each), epilogue constants, two blocks' window operands and the
+        // direct-load plan
+        const int npw = v.waves / 2, kbw = v.kt / (16 * npw), nks = v.cc / 32;
+        const int cbw = v.cc / 16 / npw;
+        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * (v.cc / 8);
+        const int r = (slots + 64 * npw - 1) / (64 * npw);
+        const int pw_regs = nks * kbw * 4 + 4 * nks + 4 * kbw + 4 * kbw * 2 + 24;
+        const int dw_regs = 20 * cbw + 8 * cbw + 40 + r + (r + 1) / 2 + 10 + 24;
+        return pw_regs > dw_regs ? pw_regs : dw_regs;
     }
     case VK_PWPW_MM: {
         // first-layer operands, 8 second-layer operands, 4 + 16 epilogue constants, the
@@ -468,7 +495,7 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         return true;
     }
     const int want = p.kind == FCM_KIND_B2B ? VK_B2B : (p.dtype == FCM_F32 ? VK_DWPW32 : VK_DWPW);
-    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMW)
+    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMW || v.vkind == VK_DWPW_WS)
                          ? VK_DWPW
                      : v.vkind == VK_B2B_MM                           ? VK_B2B
                                                                       : v.vkind;
@@ -488,7 +515,13 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         if (why) *why = "matrix-core back-to-back variant takes at most 64 channels per layer";
         return false;
     }
-    if (v.vkind == VK_DWPW_MM || v.vkind == VK_B2B_MM || v.vkind == VK_DWPW_MMW) {
+    if (v.vkind == VK_DWPW_WS && p.C != v.cc) {
+        if (why) *why = "register-resident wide variant is compiled for exactly its channel "
+                        "count";
+        return false;
+    }
+    if (v.vkind == VK_DWPW_MM || v.vkind == VK_B2B_MM || v.vkind == VK_DWPW_MMW ||
+        v.vkind == VK_DWPW_WS) {
         if (v.vkind == VK_DWPW_MM && p.C > v.cc) {
             if (why) *why = "matrix-core depthwise variant needs C <= its channel chunk";
             return false;
@@ -544,7 +577,8 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ) / wps;
     int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd / wps);
     // the workgroups per CU the kernel's register allocation was tuned for
-    if (v.vkind == VK_DWPW_MM || v.vkind == VK_B2B_MM || v.vkind == VK_DWPW_MMW)
+    if (v.vkind == VK_DWPW_MM || v.vkind == VK_B2B_MM || v.vkind == VK_DWPW_MMW ||
+        v.vkind == VK_DWPW_WS)
         occ = std::min(occ, std::max(v.occ / wps, 1));
     if (lds > d.lds_bytes_per_wg) occ = 0;
     r.wgs_per_cu = occ;
@@ -606,6 +640,10 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
         // pixel) recomputed for every K tile
         t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * p.C * ktiles) / d.mfma_f16_flops;
         t_vec = P * pad_px * (epi_ops + 1.25 * p.C * ktiles) / lane_ops_per_s;
+    } else if (v.vkind == VK_DWPW_WS) {
+        // the block-diagonal depthwise products run once per pixel and K tile
+        t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * p.C * ktiles) / d.mfma_f16_flops;
+        t_vec = P * pad_px * epi_ops / lane_ops_per_s;
     } else if (v.vkind == VK_DWPW_I8) {
         // int8 matrix rate is twice the fp16 one; the block-diagonal depthwise product is
         // 3 16x16x64 instructions per 16 channels x 16 pixels (384 op-equivalents per

@@ -19,7 +19,8 @@ enum VKind {
     VK_PWDW_MM = 7,
     VK_DWPW_I8 = 8,
     VK_PWPW_MM = 9,
-    VK_DWPW_GEN = 10
+    VK_DWPW_GEN = 10,
+    VK_DWPW_WS = 11
 };
 
 struct VariantDesc {
