@@ -249,37 +249,9 @@ void dwpw_ws_kernel(KArgs a) {
                 }
             }
         };
-        // resident depthwise operands of the wave's channel blocks cb = CBW wave + j: lane
-        // (l%16, l/16) holds reduction index 8(l/16) + e = (tap 2tp + (l/16)/2, channel
-        // 16cb + 8((l/16)&1) + e); the one non-zero element (channel 16cb + l%16) sits at
-        // e = l%8 of lanes whose channel half matches.  Epilogue-1 constants of the lane's
-        // depthwise rows 4(l/16)..+3 of each block.
-        const T* __restrict__ wdw = (const T*)a.w1;
-        const bool dw_active = (lr >> 3) == (lg & 1);
-        const int dw_e = lr & 7;
+        // resident depthwise operands and epilogue-1 constants (filled in the prologue)
         u32x4 dwa[CBW][NTP];
         f32x4 e1s[CBW], e1b[CBW];
-#pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-#pragma unroll
-            for (int tp = 0; tp < NTP; ++tp) {
-                const int t = 2 * tp + (lg >> 1);
-                const int c = 16 * (CBW * wave + j) + lr;
-                const uint16_t h = (dw_active && t < 9)
-                                       ? reinterpret_cast<const uint16_t*>(wdw)[t * CT + c]
-                                       : (uint16_t)0;
-                const uint32_t v = (dw_e & 1) ? ((uint32_t)h << 16) : (uint32_t)h;
-                const int w = dw_e >> 1;
-                dwa[j][tp] = u32x4{w == 0 ? v : 0u, w == 1 ? v : 0u, w == 2 ? v : 0u,
-                                   w == 3 ? v : 0u};
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = 16 * (CBW * wave + j) + 4 * lg + i;
-                e1s[j][i] = a.s1 ? a.s1[c] : 1.0f;
-                e1b[j][i] = a.b1 ? a.b1[c] : 0.0f;
-            }
-        }
         // LDS byte offsets of the lane's window reads relative to a channel block's piece:
         // pixel of (output pixel lr, tap 2tp + lg/2), piece 2cb + (lg&1) swizzled with the
         // pixel's sw
@@ -337,12 +309,51 @@ void dwpw_ws_kernel(KArgs a) {
             }
         };
 
-        // prologue: windows of steps 0, 1, 2 (the resident operands were requested
-        // before them); window 0 and the operands are in once at most two windows'
-        // loads are outstanding; the depthwise layer of step 0
+        // prologue: the window of step 0, then the resident operands, then the windows of
+        // steps 1 and 2.  The operands are complete before the later windows are
+        // requested: the compiler's wait for them counts every load issued before it, so
+        // it would otherwise also wait for those windows (at launch, when every
+        // workgroup requests its first windows at once, that wait is the longest).
         issue_window(b0, xs0);
+        asm volatile("" ::: "memory");
+        // resident depthwise operands of the wave's channel blocks cb = CBW wave + j: lane
+        // (l%16, l/16) holds reduction index 8(l/16) + e = (tap 2tp + (l/16)/2, channel
+        // 16cb + 8((l/16)&1) + e); the one non-zero element (channel 16cb + l%16) sits at
+        // e = l%8 of lanes whose channel half matches.  Epilogue-1 constants of the lane's
+        // depthwise rows 4(l/16)..+3 of each block.
+        const T* __restrict__ wdw = (const T*)a.w1;
+        const bool dw_active = (lr >> 3) == (lg & 1);
+        const int dw_e = lr & 7;
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) {
+#pragma unroll
+            for (int tp = 0; tp < NTP; ++tp) {
+                const int t = 2 * tp + (lg >> 1);
+                const int c = 16 * (CBW * wave + j) + lr;
+                const uint16_t h = (dw_active && t < 9)
+                                       ? reinterpret_cast<const uint16_t*>(wdw)[t * CT + c]
+                                       : (uint16_t)0;
+                const uint32_t v = (dw_e & 1) ? ((uint32_t)h << 16) : (uint32_t)h;
+                const int w = dw_e >> 1;
+                dwa[j][tp] = u32x4{w == 0 ? v : 0u, w == 1 ? v : 0u, w == 2 ? v : 0u,
+                                   w == 3 ? v : 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 16 * (CBW * wave + j) + 4 * lg + i;
+                e1s[j][i] = a.s1 ? a.s1[c] : 1.0f;
+                e1b[j][i] = a.b1 ? a.b1[c] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) {
+#pragma unroll
+            for (int tp = 0; tp < NTP; ++tp) asm volatile("" : "+v"(dwa[j][tp]));
+            asm volatile("" : "+v"(e1s[j]), "+v"(e1b[j]));
+        }
         issue_window(b0 + bstep, xs1);
         issue_window(b0 + 2 * bstep, xs2);
+        // window 0 is in once at most the last two windows' loads are outstanding
         mm::wait_vmcnt<2 * R>();
         __builtin_amdgcn_s_barrier();
         dw_step(xs0, tl0);

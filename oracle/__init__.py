@@ -65,6 +65,8 @@ def _load():
             i32, i64 = ctypes.c_int32, ctypes.c_int64
             lib.fcm_oracle_threads.restype = ctypes.c_int
             lib.fcm_oracle_threads.argtypes = []
+            lib.fcm_oracle_set_threads.restype = None
+            lib.fcm_oracle_set_threads.argtypes = [ctypes.c_int]
             lib.fcm_oracle_round.restype = ctypes.c_double
             lib.fcm_oracle_round.argtypes = [ctypes.c_double, ctypes.c_int]
             lib.fcm_oracle_round_array.argtypes = [dp, i64, ctypes.c_int]
@@ -119,6 +121,11 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle's loops run on."""
     return int(_load().fcm_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run the oracle's later loops on n OpenMP threads."""
+    _load().fcm_oracle_set_threads(int(n))
 
 
 def _f64(a):

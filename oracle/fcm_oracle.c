@@ -75,6 +75,15 @@ int fcm_oracle_threads(void) {
 #endif
 }
 
+/* Sets the threads later OpenMP loops use (for timing the checker on one core). */
+void fcm_oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 #define ORACLE_F32 0
 #define ORACLE_F16 1
 #define ORACLE_BF16 2
