@@ -103,6 +103,13 @@ def _load():
             lib.fcm_oracle_pwdw.restype = ctypes.c_int
             lib.fcm_oracle_pwdw_at.argtypes = mod_pd + [ip, i64, dp]
             lib.fcm_oracle_pwdw_at.restype = ctypes.c_int
+            # the PW -> DW arguments up to act2, then w3, K, scale3, bias3, act3, residual,
+            # dtype, and (t1, t2, y) or (pix, P, y_rows)
+            mod_pdp = mod_pd[:-1] + [dp, i32, dp, dp, ci, ci, ci]
+            lib.fcm_oracle_pwdwpw.argtypes = mod_pdp + [dp, dp, dp]
+            lib.fcm_oracle_pwdwpw.restype = ctypes.c_int
+            lib.fcm_oracle_pwdwpw_at.argtypes = mod_pdp + [ip, i64, dp]
+            lib.fcm_oracle_pwdwpw_at.restype = ctypes.c_int
             # x, M, C, w1, K1, scale1, bias1, act1, w2, K, scale2, bias2, act2, dtype, t, y
             lib.fcm_oracle_pwpw.argtypes = [dp, i64, i32, dp, i32, dp, dp, ci, dp, i32, dp, dp,
                                             ci, ci, dp, dp]
@@ -342,6 +349,67 @@ def pwdw_at(x, w_pw, w_dw, pix, stride=(1, 1), pad=(1, 1), scale1=None, bias1=No
     _load().fcm_oracle_pwdw_at(*args, pix.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                pix.shape[0], _p(y))
     del keep
+    return y
+
+
+# ---------------------------------------------------------------------------------
+# the pointwise -> depthwise -> pointwise module (inverted-residual block)
+# ---------------------------------------------------------------------------------
+def _pwdwpw_args(x, w1, w2, w3, stride, pad, scale1, bias1, act1, scale2, bias2, act2,
+                 scale3, bias3, act3, residual, dtype):
+    args, keep, dims = _pwdw_args(x, w1, w2, stride, pad, scale1, bias1, act1, scale2, bias2,
+                                  act2, dtype)
+    w3 = _f64(w3)
+    K, K1b = w3.shape
+    assert K1b == dims[4]
+    s3 = None if scale3 is None else _f64(scale3)
+    b3 = None if bias3 is None else _f64(bias3)
+    args = args[:-1] + [_p(w3), K, _p(s3), _p(b3), ACTS[act3], int(bool(residual)),
+                        DTYPES[dtype]]
+    return args, keep + (w3, s3, b3), dims + (K,)
+
+
+def pwdwpw(x, w1, w2, w3, stride=(1, 1), pad=(1, 1), scale1=None, bias1=None, act1="none",
+           scale2=None, bias2=None, act2="none", scale3=None, bias3=None, act3="none",
+           residual=False, dtype="f32", return_t=False):
+    """Layer by layer: PW (w1 [K1, C]) -> epilogue 1 -> round -> DW (w2 [K1, R, S]) ->
+    epilogue 2 -> round -> PW (w3 [K, K1]) -> epilogue 3 (+ the input pixel when
+    ``residual``) -> round.  Returns y [N, Ho, Wo, K] (and the two rounded
+    intermediates with ``return_t``)."""
+    args, keep, (N, H, W, C, K1, R, S, K) = _pwdwpw_args(
+        x, w1, w2, w3, stride, pad, scale1, bias1, act1, scale2, bias2, act2, scale3, bias3,
+        act3, residual, dtype)
+    Ho, Wo = out_size(H, pad[0], R, stride[0]), out_size(W, pad[1], S, stride[1])
+    t1 = np.empty((N, H, W, K1), np.float64) if return_t else None
+    t2 = np.empty((N, Ho, Wo, K1), np.float64) if return_t else None
+    y = np.empty((N, Ho, Wo, K), np.float64)
+    rc = _load().fcm_oracle_pwdwpw(*args, _p(t1), _p(t2), _p(y))
+    del keep
+    if rc == -2:
+        raise ValueError("the shortcut needs an unchanged extent and K == C; int8 storage "
+                         "is not defined for this module")
+    if rc != 0:
+        raise MemoryError("oracle could not allocate the intermediate")
+    return (y, t1, t2) if return_t else y
+
+
+def pwdwpw_at(x, w1, w2, w3, pix, stride=(1, 1), pad=(1, 1), scale1=None, bias1=None,
+              act1="none", scale2=None, bias2=None, act2="none", scale3=None, bias3=None,
+              act3="none", residual=False, dtype="f32"):
+    """Rows y[n, oh, ow, :] of :func:`pwdwpw` at the listed output pixels only."""
+    args, keep, (N, H, W, C, K1, R, S, K) = _pwdwpw_args(
+        x, w1, w2, w3, stride, pad, scale1, bias1, act1, scale2, bias2, act2, scale3, bias3,
+        act3, residual, dtype)
+    pix = np.ascontiguousarray(pix, dtype=np.int32).reshape(-1, 3)
+    y = np.empty((pix.shape[0], K), np.float64)
+    rc = _load().fcm_oracle_pwdwpw_at(*args, pix.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      pix.shape[0], _p(y))
+    del keep
+    if rc == -2:
+        raise ValueError("the shortcut needs an unchanged extent and K == C; int8 storage "
+                         "is not defined for this module")
+    if rc != 0:
+        raise MemoryError("oracle could not allocate the intermediate")
     return y
 
 

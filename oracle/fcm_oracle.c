@@ -19,6 +19,11 @@
  *                       pads the intermediate, not the module's input;
  *   PW -> PW module  -- two pointwise layers (the PWPW fusion case, FCM paper Sec. III,
  *                       Table II): pixel by pixel, so a tile needs no halo;
+ *   PW -> DW -> PW   -- the three convolutional layers of an inverted-residual block
+ *                       (FCM paper Sec. II-B, Fig. 4): the PW -> DW module followed by
+ *                       a third, pointwise layer; with the block's identity shortcut
+ *                       the input pixel is added after the third layer's activation,
+ *                       before its one rounding;
  *   generalised DW   -- any R x S filter, a dilation and a depth multiplier m (PyTorch
  *                       forum "Using optimised depthwise convolutions": a grouped
  *                       convolution with one group per input channel and k outputs per
@@ -457,6 +462,83 @@ int fcm_oracle_pwpw(const double* x, int64_t M, int C, const double* w1, int K1,
     fcm_oracle_pw(t, M, K1, w2, K, y);
     store_rows(y, M, K, scale2, bias2, act2, dtype);
     if (!t_out) free(t);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* PW -> DW -> PW: the three convolutional layers of an inverted-residual block     */
+/* (FCM paper Sec. II-B; Fig. 4 shows two such blocks in sequence).                 */
+/* ------------------------------------------------------------------------------ */
+
+/* Third layer of one output pixel, in place of its K1 depthwise outputs t2 (already
+ * rounded): y[k] = round(act3(scale3[k] * sum_c t2[c] * w3[k][c] + bias3[k]) + xs[k]),
+ * xs the shortcut row (the module's input at the same pixel) or NULL.  The shortcut
+ * joins after the activation and before the single rounding. */
+static void pw3_row(const double* t2, int K1, const double* w3, int K, const double* scale3,
+                    const double* bias3, int act3, const double* xs, int dtype, double* y) {
+    pw_row(t2, K1, w3, K, y);
+    epilogue_row(y, K, scale3, bias3, act3);
+    if (xs)
+        for (int k = 0; k < K; ++k) y[k] += xs[k];
+    fcm_oracle_round_array(y, K, dtype);
+}
+
+/* The module layer by layer:
+ *   t1 = round(act1(scale1 * (x . w1^T) + bias1))          [N][H][W][K1]
+ *   t2 = round(act2(scale2 * dw(t1, w2) + bias2))          [N][Ho][Wo][K1]
+ *   y  = round(act3(scale3 * (t2 . w3^T) + bias3) [+ x])   [N][Ho][Wo][K]
+ * w1 [K1][C], w2 [K1][R][S], w3 [K][K1].  residual != 0 adds the input pixel (the
+ * block's identity shortcut); it needs Ho == H, Wo == W and K == C (else -2).
+ * Floating-point storage only (-2 for int8). */
+int fcm_oracle_pwdwpw(const double* x, int N, int H, int W, int C, const double* w1, int K1,
+                      const double* scale1, const double* bias1, int act1, const double* w2,
+                      int R, int S, int sh, int sw, int ph, int pw, const double* scale2,
+                      const double* bias2, int act2, const double* w3, int K,
+                      const double* scale3, const double* bias3, int act3, int residual,
+                      int dtype, double* t1_out, double* t2_out, double* y) {
+    int Ho = out_size(H, ph, R, sh), Wo = out_size(W, pw, S, sw);
+    if (dtype == ORACLE_I8) return -2;
+    if (residual && (Ho != H || Wo != W || K != C)) return -2;
+    int64_t Mo = (int64_t)N * Ho * Wo;
+    double* t2 = t2_out ? t2_out : (double*)malloc(sizeof(double) * (size_t)(Mo * K1));
+    if (!t2) return -1;
+    int rc = fcm_oracle_pwdw(x, N, H, W, C, w1, K1, scale1, bias1, act1, w2, R, S, sh, sw, ph,
+                             pw, scale2, bias2, act2, dtype, t1_out, t2);
+    if (rc == 0) {
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < Mo; ++m)
+            pw3_row(t2 + m * K1, K1, w3, K, scale3, bias3, act3, residual ? x + m * C : NULL,
+                    dtype, y + m * K);
+    }
+    if (!t2_out) free(t2);
+    return rc;
+}
+
+/* The module at listed output pixels only: the first two layers as fcm_oracle_pwdw_at
+ * (every intermediate value the pixel's window reads recomputed from the input), then
+ * the third layer and the shortcut of that pixel. */
+int fcm_oracle_pwdwpw_at(const double* x, int N, int H, int W, int C, const double* w1,
+                         int K1, const double* scale1, const double* bias1, int act1,
+                         const double* w2, int R, int S, int sh, int sw, int ph, int pw,
+                         const double* scale2, const double* bias2, int act2,
+                         const double* w3, int K, const double* scale3, const double* bias3,
+                         int act3, int residual, int dtype, const int32_t* pix /* [P][3] */,
+                         int64_t P, double* y_rows) {
+    int Ho = out_size(H, ph, R, sh), Wo = out_size(W, pw, S, sw);
+    if (dtype == ORACLE_I8) return -2;
+    if (residual && (Ho != H || Wo != W || K != C)) return -2;
+    double* t2 = (double*)malloc(sizeof(double) * (size_t)(P * K1 + 1));
+    if (!t2) return -1;
+    fcm_oracle_pwdw_at(x, N, H, W, C, w1, K1, scale1, bias1, act1, w2, R, S, sh, sw, ph, pw,
+                       scale2, bias2, act2, dtype, pix, P, t2);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < P; ++i) {
+        int n = pix[3 * i], oh = pix[3 * i + 1], ow = pix[3 * i + 2];
+        const double* xs =
+            residual ? x + (((int64_t)n * H + oh) * W + ow) * C : NULL;
+        pw3_row(t2 + i * K1, K1, w3, K, scale3, bias3, act3, xs, dtype, y_rows + i * K);
+    }
+    free(t2);
     return 0;
 }
 
