@@ -40,7 +40,8 @@ COPY_STEPS = 5                   # copies a calibration run makes (--mode copy -
 PROFILES = os.path.join(ROOT, "profiles")
 KDIR = "depthwise_pointwise_convolution_amd/csrc/kernels/"
 # source file of each fused kernel family (by variant-name prefix) and the headers they share
-KERNEL_FILES = [("dwpw_i8_", "dwpw_i8.hip"), ("ws_", "dwpw_ws.hip"), ("mmw_", "dwpw_mmw.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
+KERNEL_FILES = [("dwpw_i8_", "dwpw_i8.hip"), ("ws_", "dwpw_ws.hip"), ("pwdwpw_", "pwdwpw_mm.hip"),
+                ("mmw_", "dwpw_mmw.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
                 ("dwpw_", "dwpw.hip"), ("b2b_", "b2b.hip"), ("pwdw_", "pwdw_mm.hip"),
                 ("pwpw_", "pwpw_mm.hip"), ("gen_", "dwpw_gen.hip")]
 SHARED_SOURCES = ["mm_common.h", "stages.h", "common.h"]
@@ -177,6 +178,9 @@ def _oracle_call(wl):
     kw = dict(stride=(wl.stride,) * 2, pad=(wl.pad,) * 2, scale1=inp["scale1"],
               bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],
               act2=wl.act2, dtype=wl.dtype)
+    if wl.kind == "pwdwpw":
+        kw.update(scale3=inp["scale3"], bias3=inp["bias3"], act3=wl.act3, residual=wl.residual)
+        return lambda: oracle.pwdwpw(inp["x"], inp["w1"], inp["w2"], inp["w3"], **kw)
     fn = {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw,
           "pwpw": oracle.pwpw}[wl.kind]
     if wl.kind == "dwpw" and (wl.R != 3 or wl.S != 3 or wl.dil != 1 or wl.mult != 1):

@@ -9,7 +9,8 @@ kernels.  The functions carry the C ABI's names (see ``include/fcm.h``):
     fcm_b2b_conv_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y)
     fcm_pwdw_fwd(plan, x, w_pw, scale1, bias1, w_dw, scale2, bias2, y)
     fcm_pwpw_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y)
-    fcm_dw_fwd / fcm_pw_fwd / fcm_conv_fwd   (layer-by-layer baselines)
+    fcm_pwdwpw_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3, y)
+    fcm_dw_fwd / fcm_pw_fwd / fcm_conv_fwd / fcm_pwdwpw_lbl   (layer-by-layer baselines)
 
 Tensor arguments are torch tensors on the GPU (or raw integer device addresses, or
 None where the ABI allows NULL); PyTorch only provides device memory and the stream
@@ -30,13 +31,13 @@ LIB_PATH = os.path.join(PKG, "libfcm.so")
 FCM_OK, FCM_ERR_INVALID_ARG, FCM_ERR_UNSUPPORTED, FCM_ERR_HIP = 0, 1, 2, 3
 FCM_F32, FCM_F16, FCM_BF16, FCM_I8 = 0, 1, 2, 3
 FCM_ACT_NONE, FCM_ACT_RELU, FCM_ACT_RELU6 = 0, 1, 2
-FCM_KIND_DWPW, FCM_KIND_B2B, FCM_KIND_PWDW, FCM_KIND_PWPW = 0, 1, 2, 3
-FCM_PLAN_VERSION = 3
+FCM_KIND_DWPW, FCM_KIND_B2B, FCM_KIND_PWDW, FCM_KIND_PWPW, FCM_KIND_PWDWPW = 0, 1, 2, 3, 4
+FCM_PLAN_VERSION = 4
 
 DTYPE_CODES = {"f32": FCM_F32, "f16": FCM_F16, "bf16": FCM_BF16, "i8": FCM_I8}
 ACT_CODES = {"none": FCM_ACT_NONE, "relu": FCM_ACT_RELU, "relu6": FCM_ACT_RELU6}
 KIND_CODES = {"dwpw": FCM_KIND_DWPW, "b2b": FCM_KIND_B2B, "pwdw": FCM_KIND_PWDW,
-              "pwpw": FCM_KIND_PWPW}
+              "pwpw": FCM_KIND_PWPW, "pwdwpw": FCM_KIND_PWDWPW}
 
 
 class FcmError(RuntimeError):
@@ -53,7 +54,7 @@ _i32, _i64, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
 class fcm_problem(ctypes.Structure):
     _fields_ = [(n, _i32) for n in ("kind", "dtype", "N", "H", "W", "C", "K1", "K", "R", "S",
                                     "stride_h", "stride_w", "pad_h", "pad_w", "act1", "act2",
-                                    "dil_h", "dil_w", "mult")]
+                                    "dil_h", "dil_w", "mult", "act3", "residual")]
 
 
 class fcm_device_spec(ctypes.Structure):
@@ -105,7 +106,7 @@ EXPORTS = ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan", "fcm_
            "fcm_num_variants", "fcm_variant_name", "fcm_pack_weights", "fcm_dwpw_fwd",
            "fcm_tune",
            "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_pwpw_fwd", "fcm_dw_fwd", "fcm_pw_fwd",
-           "fcm_conv_fwd",
+           "fcm_conv_fwd", "fcm_pwdwpw_fwd", "fcm_pwdwpw_lbl", "fcm_tune_pwdwpw",
            "fcm_status_str",
            "fcm_last_error")
 
@@ -145,6 +146,13 @@ def lib() -> ctypes.CDLL:
             L.fcm_pwpw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, vp]
             L.fcm_tune.argtypes = [P(fcm_problem), P(fcm_device_spec), _i32, P(vp), vp, fp, fp,
                                    vp, fp, fp, P(vp), vp, _i32, P(fcm_plan_t)]
+            L.fcm_pwdwpw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, fp, fp,
+                                         vp, vp]
+            L.fcm_pwdwpw_lbl.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, fp, fp,
+                                         vp, vp, vp, vp]
+            L.fcm_tune_pwdwpw.argtypes = [P(fcm_problem), P(fcm_device_spec), _i32, P(vp), vp,
+                                          fp, fp, vp, fp, fp, vp, fp, fp, P(vp), vp, _i32,
+                                          P(fcm_plan_t)]
             L.fcm_dw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
             L.fcm_pw_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
             L.fcm_conv_fwd.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, vp]
@@ -155,7 +163,8 @@ def lib() -> ctypes.CDLL:
             for name in ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan",
                          "fcm_plan_variant", "fcm_pack_weights", "fcm_dwpw_fwd",
                          "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_pwpw_fwd", "fcm_dw_fwd",
-                         "fcm_pw_fwd", "fcm_conv_fwd"):
+                         "fcm_pw_fwd", "fcm_conv_fwd", "fcm_pwdwpw_fwd", "fcm_pwdwpw_lbl",
+                         "fcm_tune_pwdwpw", "fcm_tune"):
                 getattr(L, name).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -189,9 +198,12 @@ def _stream(stream) -> Optional[int]:
 # host-side calls
 # ------------------------------------------------------------------------------------
 def problem(kind="dwpw", dtype="f16", N=1, H=1, W=1, C=8, K=8, K1=None, R=3, S=3,
-            stride=1, pad=1, act1="none", act2="none", dilation=1, mult=1) -> fcm_problem:
+            stride=1, pad=1, act1="none", act2="none", dilation=1, mult=1, act3="none",
+            residual=False) -> fcm_problem:
     """Build an fcm_problem; K1 defaults to C*mult (depthwise first layer).  For the
-    PW->DW module ("pwdw") K1 is the pointwise layer's output and K must equal it.
+    PW->DW module ("pwdw") K1 is the pointwise layer's output and K must equal it; for the
+    PW->DW->PW module ("pwdwpw") K1 is the expansion's output, K the projection's, act3
+    the projection's activation and residual the identity shortcut.
     dilation / mult: the depthwise layer's tap spacing and depth multiplier (DWPW)."""
     p = fcm_problem()
     p.kind = KIND_CODES[kind] if isinstance(kind, str) else kind
@@ -206,6 +218,8 @@ def problem(kind="dwpw", dtype="f16", N=1, H=1, W=1, C=8, K=8, K1=None, R=3, S=3
     p.stride_h, p.stride_w, p.pad_h, p.pad_w = sh, sw, ph, pw
     p.act1 = ACT_CODES[act1] if isinstance(act1, str) else act1
     p.act2 = ACT_CODES[act2] if isinstance(act2, str) else act2
+    p.act3 = ACT_CODES[act3] if isinstance(act3, str) else act3
+    p.residual = int(bool(residual))
     return p
 
 
@@ -305,6 +319,40 @@ def fcm_pwpw_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y, stream=None):
     _check(lib().fcm_pwpw_fwd(ctypes.byref(plan), _ptr(x), _ptr(w1), _ptr(scale1),
                               _ptr(bias1), _ptr(w2), _ptr(scale2), _ptr(bias2), _ptr(y),
                               _stream(stream)), "fcm_pwpw_fwd")
+
+
+def fcm_pwdwpw_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3, y,
+                   stream=None):
+    _check(lib().fcm_pwdwpw_fwd(ctypes.byref(plan), _ptr(x), _ptr(w1), _ptr(scale1),
+                                _ptr(bias1), _ptr(w2), _ptr(scale2), _ptr(bias2), _ptr(w3),
+                                _ptr(scale3), _ptr(bias3), _ptr(y), _stream(stream)),
+           "fcm_pwdwpw_fwd")
+
+
+def fcm_pwdwpw_lbl(plan, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3, t1, t2,
+                   y, stream=None):
+    _check(lib().fcm_pwdwpw_lbl(ctypes.byref(plan), _ptr(x), _ptr(w1), _ptr(scale1),
+                                _ptr(bias1), _ptr(w2), _ptr(scale2), _ptr(bias2), _ptr(w3),
+                                _ptr(scale3), _ptr(bias3), _ptr(t1), _ptr(t2), _ptr(y),
+                                _stream(stream)), "fcm_pwdwpw_lbl")
+
+
+def fcm_tune_pwdwpw(prob, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3, y,
+                    iters=20, spec=None, stream=None) -> "fcm_plan_t":
+    """As :func:`fcm_tune`, for the PW->DW->PW module."""
+    xs = list(x) if isinstance(x, (list, tuple)) else [x]
+    ys = list(y) if isinstance(y, (list, tuple)) else [y]
+    if len(xs) != len(ys):
+        raise ValueError("x and y need the same number of tensors")
+    xa = (ctypes.c_void_p * len(xs))(*[_ptr(t) for t in xs])
+    ya = (ctypes.c_void_p * len(ys))(*[_ptr(t) for t in ys])
+    out = fcm_plan_t()
+    _check(lib().fcm_tune_pwdwpw(ctypes.byref(prob), ctypes.byref(spec) if spec else None,
+                                 len(xs), xa, _ptr(w1), _ptr(scale1), _ptr(bias1), _ptr(w2),
+                                 _ptr(scale2), _ptr(bias2), _ptr(w3), _ptr(scale3),
+                                 _ptr(bias3), ya, _stream(stream), int(iters),
+                                 ctypes.byref(out)), "fcm_tune_pwdwpw")
+    return out
 
 
 def fcm_tune(prob, x, w1, scale1, bias1, w2, scale2, bias2, y, iters=20, spec=None,

@@ -31,6 +31,7 @@ SOURCES = [
     ("kernels/dwpw_ws.hip", True),
     ("kernels/b2b_mm.hip", True),
     ("kernels/pwdw_mm.hip", True),
+    ("kernels/pwdwpw_mm.hip", True),
     ("kernels/dwpw_i8.hip", True),
     ("kernels/pwpw_mm.hip", True),
     ("kernels/dwpw_gen.hip", True),

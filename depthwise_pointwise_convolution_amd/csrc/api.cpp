@@ -56,6 +56,9 @@ const VariantImpl kImpls[] = {
     {launch_dwpw_ws<CTy, S, TH, TW, CT, KT, NW>, occ_dwpw_ws<CTy, S, TH, TW, CT, KT, NW>},
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {launch_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>, occ_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>},
+#define FCM_V_PWDWPW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, KB, OCC)   \
+    {launch_pwdwpw_mm<CT, S, TH, CMAX, NW, BPW, KB, OCC>,                \
+     occ_pwdwpw_mm<CT, S, TH, CMAX, NW, BPW, KB, OCC>},
 #define FCM_V_DWPW_I8(name, S, OCC) {launch_dwpw_i8<S, OCC>, occ_dwpw_i8<S, OCC>},
 #define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) {launch_pwpw_mm<CT, PB, OCC>, occ_pwpw_mm<CT, PB, OCC>},
 #define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC)    \
@@ -70,6 +73,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_PWDW_MM
+#undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS
 #undef FCM_V_DWPW_I8
 #undef FCM_V_PWPW_MM
@@ -168,6 +172,8 @@ KArgs base_args(const fcm_plan_t* plan) {
     a.pad_w = p.pad_w;
     a.act1 = p.act1;
     a.act2 = p.act2;
+    a.act3 = p.act3;
+    a.residual = p.residual;
     return a;
 }
 
@@ -199,6 +205,78 @@ fcm_status launch_fused(const fcm_plan_t* plan, KArgs& a, void* stream) {
     return ok();
 }
 
+}  // namespace
+}  // namespace fcm
+
+namespace fcm {
+namespace {
+// Measured selection shared by fcm_tune and fcm_tune_pwdwpw: `run` launches the module
+// with a candidate plan on the next input/output pair.
+template <typename Run>
+fcm_status tune_impl(const fcm_problem* prob, const fcm_device_spec* spec, int32_t iters,
+                     void* stream, fcm_plan_t* out, Run&& run) {
+    fcm_plan_t first;
+    FCM_TRY(fcm_plan(prob, spec, &first));  // validates the problem
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return fail(FCM_ERR_HIP, "hipEventCreate failed");
+    }
+    fcm_status st = FCM_OK;
+    fcm_plan_t best = first;
+    double best_us = 0.0;
+    for (int v = 0; v < kNumVariants && st == FCM_OK; ++v) {
+        fcm_plan_t pv;
+        std::string err;
+        if (plan_problem(prob, spec, v, &pv, &err) != FCM_OK) continue;
+        const VariantDesc& vd = kVariants[v];
+        std::string why;
+        if (!variant_runs(vd, pv.prob, &why)) continue;
+        int cus = 0, per_cu = 0;
+        st = device_capacity(v, &cus, &per_cu);
+        if (st != FCM_OK) break;
+        const int64_t ptiles =
+            prob->kind == FCM_KIND_PWPW
+                ? ((int64_t)prob->N * prob->H * prob->W + vd.th * vd.tw - 1) / (vd.th * vd.tw)
+                : (int64_t)prob->N * ((pv.Ho + vd.th - 1) / vd.th) * ((pv.Wo + vd.tw - 1) / vd.tw);
+        const int ktiles = (prob->K + vd.kt - 1) / vd.kt;  // (PWDW: K == K1)
+        int64_t last_grid = -1;
+        for (int w = 1; w <= std::min(4, per_cu) && st == FCM_OK; ++w) {
+            const int64_t g = persistent_grid(ptiles, ktiles, (int64_t)cus * w);
+            if (g == last_grid) continue;
+            last_grid = g;
+            fcm_plan_t cand = pv;
+            cand.grid = (int32_t)g;
+            cand.wgs_per_cu = w;
+            for (int i = 0; i < 2 && st == FCM_OK; ++i) st = run(&cand);  // warm-up
+            if (st != FCM_OK) break;
+            if (hipEventRecord(e0, (hipStream_t)stream) != hipSuccess) {
+                st = fail(FCM_ERR_HIP, "hipEventRecord failed");
+                break;
+            }
+            for (int i = 0; i < iters && st == FCM_OK; ++i) st = run(&cand);
+            if (st != FCM_OK) break;
+            float ms = 0.f;
+            if (hipEventRecord(e1, (hipStream_t)stream) != hipSuccess ||
+                hipEventSynchronize(e1) != hipSuccess ||
+                hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+                st = fail(FCM_ERR_HIP, "timing events failed");
+                break;
+            }
+            const double us = 1e3 * ms / iters;
+            if (best_us == 0.0 || us < best_us) {
+                best_us = us;
+                best = cand;
+            }
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != FCM_OK) return st;
+    best.tuned_us = best_us;
+    *out = best;
+    return ok();
+}
 }  // namespace
 }  // namespace fcm
 
@@ -307,7 +385,7 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                              "16-byte aligned");
         const char* s = (const char*)w1_src;
         const char* d = (const char*)w1_dst;
-        const int64_t ns = p.kind == FCM_KIND_PWDW
+        const int64_t ns = prob_has_expansion(p)
                                ? (int64_t)p.K1 * p.C * e
                                : p.kind == FCM_KIND_B2B ? (int64_t)p.K1 * p.R * p.S * p.C * e
                                                         : (int64_t)p.R * p.S * p.K1 * e;
@@ -320,7 +398,7 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                              "16-byte aligned");
         const char* s = (const char*)w2_src;
         const char* d = (const char*)w2_dst;
-        const int64_t ns = p.kind == FCM_KIND_PWDW
+        const int64_t ns = prob_has_expansion(p)
                                ? (int64_t)p.K1 * p.R * p.S * e
                                : (int64_t)p.K * p.K1 * e;  // (DW->PW: K1 = C * mult)
         const int64_t nd = plan->w2_packed_bytes;
@@ -348,9 +426,9 @@ fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1
                                          hipGetErrorString((hipError_t)rc));
         return ok();
     }
-    if (p.kind == FCM_KIND_PWDW) {
+    if (prob_has_expansion(p)) {
         // first layer: pointwise [K1][C] copied as is; second: depthwise [K1][R*S] ->
-        // [R*S][K1]
+        // [R*S][K1] (PW->DW->PW: the projection's filters are not packed)
         int rc = 0;
         if (w1_src) rc = launch_copy(w1_src, w1_dst, (int64_t)p.K1 * p.C * e, stream);
         if (rc == 0 && w2_src) rc = launch_pack_dw(e, w2_src, w2_dst, p.K1, p.R * p.S, stream);
@@ -486,6 +564,104 @@ fcm_status fcm_pwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
     return launch_fused(plan, a, stream);
 }
 
+fcm_status fcm_pwdwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
+                          const float* scale1, const float* bias1, const void* w2,
+                          const float* scale2, const float* bias2, const void* w3,
+                          const float* scale3, const float* bias3, void* y, void* stream) {
+    FCM_TRY(check_plan(plan, FCM_KIND_PWDWPW));
+    FCM_TRY(check_variant(plan));
+    FCM_TRY(need(x, "x", 16));
+    FCM_TRY(need(w1, "w1", 16));
+    FCM_TRY(need(w2, "w2", 16));
+    FCM_TRY(need(w3, "w3", 16));
+    FCM_TRY(need(y, "y", 16));
+    FCM_TRY(optional(scale1, "scale1"));
+    FCM_TRY(optional(bias1, "bias1"));
+    FCM_TRY(optional(scale2, "scale2"));
+    FCM_TRY(optional(bias2, "bias2"));
+    FCM_TRY(optional(scale3, "scale3"));
+    FCM_TRY(optional(bias3, "bias3"));
+    KArgs a = base_args(plan);
+    a.x = x;
+    a.w1 = w1;
+    a.s1 = scale1;
+    a.b1 = bias1;
+    a.w2 = w2;
+    a.s2 = scale2;
+    a.b2 = bias2;
+    a.w3 = w3;
+    a.s3 = scale3;
+    a.b3 = bias3;
+    a.y = y;
+    return launch_fused(plan, a, stream);
+}
+
+fcm_status fcm_pwdwpw_lbl(const fcm_plan_t* plan, const void* x, const void* w1,
+                          const float* scale1, const float* bias1, const void* w2,
+                          const float* scale2, const float* bias2, const void* w3,
+                          const float* scale3, const float* bias3, void* t1, void* t2, void* y,
+                          void* stream) {
+    FCM_TRY(check_plan(plan, FCM_KIND_PWDWPW));
+    FCM_TRY(need(x, "x", 16));
+    FCM_TRY(need(w1, "w1", 16));
+    FCM_TRY(need(w2, "w2", 16));
+    FCM_TRY(need(w3, "w3", 16));
+    FCM_TRY(need(t1, "t1", 16));
+    FCM_TRY(need(t2, "t2", 16));
+    FCM_TRY(need(y, "y", 16));
+    FCM_TRY(optional(scale1, "scale1"));
+    FCM_TRY(optional(bias1, "bias1"));
+    FCM_TRY(optional(scale2, "scale2"));
+    FCM_TRY(optional(bias2, "bias2"));
+    FCM_TRY(optional(scale3, "scale3"));
+    FCM_TRY(optional(bias3, "bias3"));
+    const fcm_problem& p = plan->prob;
+    auto launched = [](int rc) {
+        return rc == 0 ? ok()
+                       : fail(FCM_ERR_HIP, std::string("kernel launch failed: ") +
+                                               hipGetErrorString((hipError_t)rc));
+    };
+    // expansion: every input pixel, C -> K1, epilogue 1
+    KArgs a = base_args(plan);
+    a.Ho = p.H;
+    a.Wo = p.W;
+    a.K = p.K1;
+    a.act2 = p.act1;
+    a.x = x;
+    a.w2 = w1;
+    a.s2 = scale1;
+    a.b2 = bias1;
+    a.y = t1;
+    a.residual = 0;
+    a.num_ktiles = (p.K1 + lbl::PW_KT16 - 1) / lbl::PW_KT16;
+    FCM_TRY(launched(launch_pw_lbl(p.dtype, a, stream)));
+    // depthwise over the K1-channel expansion, epilogue 2
+    a = base_args(plan);
+    a.C = p.K1;
+    a.act1 = p.act2;
+    a.x = t1;
+    a.w1 = w2;
+    a.s1 = scale2;
+    a.b1 = bias2;
+    a.y = t2;
+    a.residual = 0;
+    set_tiles(&a, lbl::DW_TH, lbl::DW_TW, 1, 1);
+    FCM_TRY(launched(launch_dw_lbl(p.dtype, p.stride_h, a, stream)));
+    // projection K1 -> K, epilogue 3, the shortcut
+    a = base_args(plan);
+    a.C = p.K1;
+    a.act2 = p.act3;
+    a.x = t2;
+    a.w2 = w3;
+    a.s2 = scale3;
+    a.b2 = bias3;
+    a.res = p.residual ? x : nullptr;
+    a.y = y;
+    a.num_ktiles = (p.K + lbl::PW_KT16 - 1) / lbl::PW_KT16;
+    return launched(launch_pw_lbl(p.dtype, a, stream));
+}
+
+
 fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_t nsets,
                     const void* const* x, const void* w1, const float* scale1,
                     const float* bias1, const void* w2, const float* scale2,
@@ -494,8 +670,8 @@ fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_
     if (!out) return fail(FCM_ERR_INVALID_ARG, "plan output pointer is NULL");
     if (iters <= 0) return fail(FCM_ERR_INVALID_ARG, "iters must be positive");
     if (nsets < 1 || !x || !y) return fail(FCM_ERR_INVALID_ARG, "need nsets >= 1 and x, y arrays");
-    fcm_plan_t first;
-    FCM_TRY(fcm_plan(prob, spec, &first));  // validates the problem
+    if (prob && prob->kind == FCM_KIND_PWDWPW)
+        return fail(FCM_ERR_INVALID_ARG, "a PW->DW->PW module is tuned with fcm_tune_pwdwpw");
     int call = 0;
     auto run = [&](const fcm_plan_t* pl) {
         const int i = call++ % nsets;
@@ -511,65 +687,27 @@ fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_
                                     stream);
         }
     };
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
-        if (e0) (void)hipEventDestroy(e0);
-        return fail(FCM_ERR_HIP, "hipEventCreate failed");
-    }
-    fcm_status st = FCM_OK;
-    fcm_plan_t best = first;
-    double best_us = 0.0;
-    for (int v = 0; v < kNumVariants && st == FCM_OK; ++v) {
-        fcm_plan_t pv;
-        std::string err;
-        if (plan_problem(prob, spec, v, &pv, &err) != FCM_OK) continue;
-        const VariantDesc& vd = kVariants[v];
-        std::string why;
-        if (!variant_runs(vd, pv.prob, &why)) continue;
-        int cus = 0, per_cu = 0;
-        st = device_capacity(v, &cus, &per_cu);
-        if (st != FCM_OK) break;
-        const int64_t ptiles =
-            prob->kind == FCM_KIND_PWPW
-                ? ((int64_t)prob->N * prob->H * prob->W + vd.th * vd.tw - 1) / (vd.th * vd.tw)
-                : (int64_t)prob->N * ((pv.Ho + vd.th - 1) / vd.th) * ((pv.Wo + vd.tw - 1) / vd.tw);
-        const int ktiles = (prob->K + vd.kt - 1) / vd.kt;  // (PWDW: K == K1)
-        int64_t last_grid = -1;
-        for (int w = 1; w <= std::min(4, per_cu) && st == FCM_OK; ++w) {
-            const int64_t g = persistent_grid(ptiles, ktiles, (int64_t)cus * w);
-            if (g == last_grid) continue;
-            last_grid = g;
-            fcm_plan_t cand = pv;
-            cand.grid = (int32_t)g;
-            cand.wgs_per_cu = w;
-            for (int i = 0; i < 2 && st == FCM_OK; ++i) st = run(&cand);  // warm-up
-            if (st != FCM_OK) break;
-            if (hipEventRecord(e0, (hipStream_t)stream) != hipSuccess) {
-                st = fail(FCM_ERR_HIP, "hipEventRecord failed");
-                break;
-            }
-            for (int i = 0; i < iters && st == FCM_OK; ++i) st = run(&cand);
-            if (st != FCM_OK) break;
-            float ms = 0.f;
-            if (hipEventRecord(e1, (hipStream_t)stream) != hipSuccess ||
-                hipEventSynchronize(e1) != hipSuccess ||
-                hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
-                st = fail(FCM_ERR_HIP, "timing events failed");
-                break;
-            }
-            const double us = 1e3 * ms / iters;
-            if (best_us == 0.0 || us < best_us) {
-                best_us = us;
-                best = cand;
-            }
-        }
-    }
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
-    if (st != FCM_OK) return st;
-    best.tuned_us = best_us;
-    *out = best;
-    return ok();
+    return tune_impl(prob, spec, iters, stream, out, run);
+}
+
+fcm_status fcm_tune_pwdwpw(const fcm_problem* prob, const fcm_device_spec* spec, int32_t nsets,
+                           const void* const* x, const void* w1, const float* scale1,
+                           const float* bias1, const void* w2, const float* scale2,
+                           const float* bias2, const void* w3, const float* scale3,
+                           const float* bias3, void* const* y, void* stream, int32_t iters,
+                           fcm_plan_t* out) {
+    if (!out) return fail(FCM_ERR_INVALID_ARG, "plan output pointer is NULL");
+    if (iters <= 0) return fail(FCM_ERR_INVALID_ARG, "iters must be positive");
+    if (nsets < 1 || !x || !y) return fail(FCM_ERR_INVALID_ARG, "need nsets >= 1 and x, y arrays");
+    if (!prob || prob->kind != FCM_KIND_PWDWPW)
+        return fail(FCM_ERR_INVALID_ARG, "fcm_tune_pwdwpw takes a PW->DW->PW problem");
+    int call = 0;
+    auto run = [&](const fcm_plan_t* pl) {
+        const int i = call++ % nsets;
+        return fcm_pwdwpw_fwd(pl, x[i], w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3,
+                              y[i], stream);
+    };
+    return tune_impl(prob, spec, iters, stream, out, run);
 }
 
 fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,

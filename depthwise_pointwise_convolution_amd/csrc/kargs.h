@@ -15,9 +15,14 @@ struct KArgs {
     const float* s2;   // epilogue 2 scale / bias (nullable)
     const float* b2;
     void* y;           // output feature maps
+    const void* w3;    // third layer's filters [K][K1] (PW->DW->PW module; else unused)
+    const float* s3;   // epilogue 3 scale / bias (nullable)
+    const float* b3;
+    const void* res;   // shortcut input added after the last epilogue (nullable)
     int N, H, W, C, K1, K, Ho, Wo;
     int pad_h, pad_w;
-    int act1, act2;
+    int act1, act2, act3;
+    int residual;      // PW->DW->PW module: add the input pixel after epilogue 3
     int tiles_h, tiles_w;  // pixel tiles per image
     int num_ptiles;        // N * tiles_h * tiles_w (or flattened pixel tiles)
     int num_ktiles;        // output-channel tiles

@@ -112,6 +112,14 @@ __global__ __launch_bounds__(256) void pw_lbl_kernel(KArgs a) {
                         o[4 + i] =
                             epilogue(acc[mi][kb + 1][i], s2s[kl + 4 + i], b2s[kl + 4 + i], act2);
                     }
+                    if (a.res) {
+                        // shortcut: the same pixel and channels of a [M][K] tensor, added
+                        // after the activation, before the one rounding
+                        float rv[8];
+                        unpack16<T>(ld16((const T*)a.res + m * a.K + k0 + kl), rv);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) o[i] += rv[i];
+                    }
                     st16(y + m * a.K + k0 + kl, pack16<T>(o));
                 }
             }

@@ -37,6 +37,11 @@ int launch_pwdw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
 int occ_pwdw_mm();
 
+template <typename T, int S, int TH, int CMAX, int NW, int BPW, int KB, int OCC>
+int launch_pwdwpw_mm(const KArgs& a, int grid, void* stream);
+template <typename T, int S, int TH, int CMAX, int NW, int BPW, int KB, int OCC>
+int occ_pwdwpw_mm();
+
 template <typename T, int PB, int OCC>
 int launch_pwpw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int PB, int OCC>

@@ -52,6 +52,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_WS, dt, S, TH, TW, KT, CT, 1, 2, 0, NW / 4, NW, CT, 0},
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {#name, VK_PWDW_MM, dt, S, TH, 16, NW * BPW * 16, CMAX, 1, 2, 0, OCC, NW, CMAX, BPW},
+#define FCM_V_PWDWPW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, KB, OCC) \
+    {#name, VK_PWDWPW_MM, dt, S, TH, 16, KB * 16, CMAX, 1, 2, NW * BPW * 16, OCC, NW, CMAX, BPW},
 #define FCM_V_DWPW_I8(name, S, OCC) \
     {#name, VK_DWPW_I8, FCM_I8, S, 4, 16, 64, 64, 1, 2, 0, OCC, 4, 64, 0},
 #define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) \
@@ -66,6 +68,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_PWDW_MM
+#undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS
 #undef FCM_V_DWPW_I8
 #undef FCM_V_PWPW_MM
@@ -163,6 +166,18 @@ int variant_lds_bytes(const VariantDesc& v) {
         const int slots_b = rf * nt + (rem + 63) / 64 * 64 + (rem > 0 ? 64 : 0);
         return 3 * slots_b * 16 + 3 * (v.cc / 32) * 1024;
     }
+    case VK_PWDWPW_MM: {
+        // two input-window buffers (whole load rounds of 16-pixel blocks), one expansion
+        // tile per expanded-channel block ((IH + 1) rows x 2 chunks x IW x 16 bytes), and
+        // the depthwise tile: th x 16 pixels x (k1 + 8) channels
+        const int nt = 64 * v.waves;
+        const int iw = 15 * v.stride + 3;
+        const int np = IH * iw, npb = (np + 15) / 16;
+        const int slots = npb * 16 * (v.cmax / 8);
+        const int slots_p = (slots + nt - 1) / nt * nt;
+        const int nb = v.k1 / 16;
+        return 2 * slots_p * 16 + nb * (IH + 1) * 2 * iw * 16 + v.th * 16 * (v.k1 + 8) * 2;
+    }
     case VK_PWPW_MM: {
         // two input tiles of th x 16 pixels x 64 channels, two intermediate tiles of
         // th x 16 pixels x 64 channels
@@ -253,6 +268,18 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         const int dw_regs = 20 * cbw + 8 * cbw + 40 + r + (r + 1) / 2 + 10 + 24;
         return pw_regs > dw_regs ? pw_regs : dw_regs;
     }
+    case VK_PWDWPW_MM: {
+        // expansion, depthwise and projection operands (the projection's for every
+        // output block), the three epilogues' constants, the reads in flight, the
+        // depthwise accumulators of the tile's rows, per-pixel-block offsets, the
+        // direct-load plan and addressing
+        const int bpw = v.bpw, nkc = v.cmax / 32, nk3 = v.k1 / 32, kb = v.kt / 16;
+        const int iw = 15 * v.stride + 3, ih = (v.th - 1) * v.stride + 3;
+        const int npb = (ih * iw + 15) / 16;
+        const int slots = npb * 16 * (v.cmax / 8), nt = 64 * v.waves;
+        return 4 * bpw * nkc + 20 * bpw + 16 * bpw + 4 * kb * nk3 + 8 * kb + 12 * nkc +
+               16 * bpw + 4 * v.th + 2 * npb + 2 * ((slots + nt - 1) / nt) + 4 * nk3 + 30;
+    }
     case VK_PWPW_MM: {
         // first-layer operands, 8 second-layer operands, 4 + 16 epilogue constants, the
         // direct-load plan, operands and accumulators of the tile, addressing
@@ -287,8 +314,17 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         return FCM_ERR_INVALID_ARG;
     }
     if (p->kind != FCM_KIND_DWPW && p->kind != FCM_KIND_B2B && p->kind != FCM_KIND_PWDW &&
-        p->kind != FCM_KIND_PWPW) {
+        p->kind != FCM_KIND_PWPW && p->kind != FCM_KIND_PWDWPW) {
         *err = "unknown kind";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->kind != FCM_KIND_PWDWPW && (p->act3 != 0 || p->residual != 0)) {
+        *err = "act3 and residual describe the third layer of a PW->DW->PW module";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->act3 < FCM_ACT_NONE || p->act3 > FCM_ACT_RELU6 || p->residual < 0 ||
+        p->residual > 1) {
+        *err = "unknown third activation, or residual not 0 or 1";
         return FCM_ERR_INVALID_ARG;
     }
     if (p->dtype < FCM_F32 || p->dtype > FCM_I8) {
@@ -320,6 +356,14 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
     }
     if (p->kind == FCM_KIND_PWDW && p->K != p->K1) {
         *err = "the depthwise layer of a PW->DW module keeps the channel count: K must equal K1";
+        return FCM_ERR_INVALID_ARG;
+    }
+    if (p->kind == FCM_KIND_PWDWPW && p->residual &&
+        (p->K != p->C ||
+         conv_out(p->H, p->pad_h, p->R, p->stride_h) != p->H ||
+         conv_out(p->W, p->pad_w, p->S, p->stride_w) != p->W || p->stride_h != 1 ||
+         p->stride_w != 1)) {
+        *err = "the identity shortcut needs stride 1, K == C and an unchanged extent";
         return FCM_ERR_INVALID_ARG;
     }
     if (p->R > 64 || p->S > 64 || prob_dil_h(*p) > 64 || prob_dil_w(*p) > 64) {
@@ -409,6 +453,10 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         *err = "the PW->DW kernels need 16-bit storage (fp16 or bf16)";
         return FCM_ERR_UNSUPPORTED;
     }
+    if (p->kind == FCM_KIND_PWDWPW && (p->dtype == FCM_F32 || p->dtype == FCM_I8)) {
+        *err = "the PW->DW->PW kernels need 16-bit storage (fp16 or bf16)";
+        return FCM_ERR_UNSUPPORTED;
+    }
     if (p->dtype == FCM_I8 && p->kind != FCM_KIND_DWPW) {
         *err = "int8 storage is provided for the DW->PW module only";
         return FCM_ERR_UNSUPPORTED;
@@ -468,6 +516,30 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         if ((int64_t)p.N * p.H * p.W * p.C >= ((int64_t)1 << 31) ||
             (int64_t)p.N * Ho * Wo * p.K >= ((int64_t)1 << 30)) {
             if (why) *why = "int8 variant addresses inputs below 2 GiB and outputs below 1 GiB";
+            return false;
+        }
+        return true;
+    }
+    if (v.vkind == VK_PWDWPW_MM || p.kind == FCM_KIND_PWDWPW) {
+        if (v.vkind != VK_PWDWPW_MM || p.kind != FCM_KIND_PWDWPW || v.dtype != p.dtype) {
+            if (why) *why = "variant is for another module kind or storage type";
+            return false;
+        }
+        if (v.stride != p.stride_h) {
+            if (why) *why = "variant is compiled for another stride";
+            return false;
+        }
+        if (p.C > v.cmax || p.K1 > v.k1 || p.K > v.kt) {
+            if (why) *why = "PW->DW->PW variant holds at most its compiled input, expanded and "
+                            "output channel counts";
+            return false;
+        }
+        const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
+        const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
+        if ((int64_t)p.N * p.H * p.W * p.C * 2 >= ((int64_t)1 << 31) ||
+            (int64_t)p.N * Ho * Wo * p.K * 2 >= ((int64_t)1 << 30)) {
+            if (why) *why = "PW->DW->PW variant addresses inputs below 2 GiB and outputs below "
+                            "1 GiB";
             return false;
         }
         return true;
@@ -760,6 +832,101 @@ Estimate estimate_pwdw(const VariantDesc& v, const fcm_problem& p, const fcm_dev
     return r;
 }
 
+// PW->DW->PW module (the three layers of an inverted-residual block): the PW->DW tiling
+// (the expansion recomputed on every tile's input window, the depthwise layer once per
+// output pixel) with all K1 expanded channels in one workgroup, then the projection on
+// the depthwise tile.  No estimate for three layers is printed on the pages; the Eq.-style
+// figure takes Eq. 4's form: the input with its overlap once (a single weight tile), the
+// three layers' filters once per output tile, the output once.
+void estimate_unfused_pwdw(const fcm_problem& p, int Ho, int Wo, int64_t* pred, double* gma);
+
+Estimate estimate_pwdwpw(const VariantDesc& v, const fcm_problem& p, const fcm_device_spec& d,
+                         int Ho, int Wo) {
+    Estimate r{};
+    const int e = elem_bytes(p.dtype);
+    const int lds = variant_lds_bytes(v);
+    const int vg = (variant_vgpr_estimate(v) + 7) / 8 * 8;
+    const int wps = std::max((v.waves + 3) / 4, 1);
+    const int occ_lds = lds > 0 ? d.lds_bytes_per_cu / lds : 8;
+    const int occ_vgpr = std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ) / wps;
+    int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd / wps);
+    if (lds > d.lds_bytes_per_wg) occ = 0;
+    r.wgs_per_cu = occ;
+    const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);
+    const int64_t ptiles = (int64_t)p.N * tiles_h * tiles_w;
+    r.num_tiles = (int)std::min<int64_t>(ptiles, INT32_MAX);
+    const int64_t grid = persistent_grid(ptiles, 1, (int64_t)d.num_cus * std::max(occ, 1));
+    r.grid = (int)grid;
+
+    const int64_t win = halo_pixels(Ho, Wo, p.H, p.W, v.th, v.tw, p.stride_h, p.pad_h, p.pad_w);
+    const int64_t x_reads = win * p.N * p.C * e;
+    const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K * e;
+    const int64_t w_all = ((int64_t)p.K1 * p.C + 9LL * p.K1 + (int64_t)p.K * p.K1) * e +
+                          4LL * 2 * (2 * p.K1 + p.K);
+    r.pred = x_reads + y_bytes + grid * w_all;
+    r.waste = (double)win / ((double)p.H * p.W) *
+              ((double)tiles_h * v.th * tiles_w * v.tw) / ((double)Ho * Wo) *
+              ((double)v.k1 / p.K1);
+
+    const double alg = (double)p.N * p.H * p.W * p.C * e + (double)y_bytes + (double)w_all;
+    const double pw_px = (double)win * p.N;
+    const double out_px = (double)p.N * tiles_h * v.th * tiles_w * v.tw;
+    const double c_pad = (double)cdiv(p.C, 32) * 32;
+    // matrix work as executed: the expansion padded to 32 input channels over the
+    // window, the block-diagonal depthwise product (320 flop-equivalents per channel and
+    // pixel), the projection over the held channels and its 16-channel output blocks
+    const double t_mat = (pw_px * 2.0 * c_pad * v.k1 + out_px * 320.0 * v.k1 +
+                          out_px * 2.0 * v.k1 * (double)cdiv(p.K, 16) * 16) /
+                         d.mfma_f16_flops;
+    const double t_vec = 3.0 * ((double)v.k1 * (pw_px + out_px) + (double)p.K * out_px) /
+                         (d.valu_f32_flops / 2.0);
+    const double t_hbm = alg / d.hbm_bytes_per_s;
+    const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);
+    const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
+    r.t_us = std::max(std::max(t_hbm, t_l2), std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+
+    const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, 3,
+                                       p.stride_h);
+    const double ifm = (double)p.N * p.H * p.W * p.C * e;
+    const double w1 = (double)p.K1 * p.C * e, w2 = 9.0 * p.K1 * e, w3 = (double)p.K * p.K1 * e;
+    const double ofm = (double)y_bytes, ofm_tile = (double)v.th * v.tw * p.K * e;
+    const bool fits = lds <= d.lds_bytes_per_wg && occ > 0;
+    const bool enough = r.num_tiles >= d.num_cus;
+    r.feasible = fits && enough;
+    r.gma = r.feasible ? (2.0 * p.C * overlap * p.N * e + ifm) +
+                             ceil(ofm / ofm_tile) * (w1 + w2 + w3) + ofm
+                       : INFINITY;
+    return r;
+}
+
+// Layer-by-layer PW->DW->PW: the expansion over every input pixel writes t1, the
+// depthwise kernel reads it and writes t2, the projection reads t2 (and the input again
+// for the shortcut) and writes the output.  Bytes with the baseline kernels' tilings,
+// and Eq. 2 (expansion) + Eq. 3 (depthwise) + Eq. 2 (projection).
+void estimate_unfused_pwdwpw(const fcm_problem& p, int Ho, int Wo, int64_t* pred, double* gma) {
+    int64_t pu = 0;
+    double gu = 0;
+    // the first two layers are the PW->DW module's layer-by-layer pair with its output
+    // (the depthwise layer's K1 channels) as the intermediate t2
+    fcm_problem q = p;
+    q.kind = FCM_KIND_PWDW;
+    q.K = p.K1;
+    estimate_unfused_pwdw(q, Ho, Wo, &pu, &gu);
+    const int e = elem_bytes(p.dtype);
+    const int64_t t2 = (int64_t)p.N * Ho * Wo * p.K1 * e;
+    const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K * e;
+    const int64_t w3 = (int64_t)p.K * p.K1 * e;
+    const int64_t m = (int64_t)p.N * Ho * Wo;
+    const int mt = lbl::PW_MT16, kt = lbl::PW_KT16;
+    const int64_t res = p.residual ? (int64_t)p.N * p.H * p.W * p.C * e : 0;
+    const int64_t third = t2 * cdiv(p.K, kt) + cdiv(m, mt) * w3 + y_bytes + res;
+    *pred = pu + third;
+    const double g3 = ceil((double)w3 / ((double)std::min(kt, p.K) * p.K1 * e)) * (double)t2 +
+                      (double)y_bytes + (double)res +
+                      ceil((double)y_bytes / ((double)mt * std::min(kt, p.K) * e)) * (double)w3;
+    *gma = gu + g3;
+}
+
 // PW->PW module: tiles of th x 16 consecutive pixels, both layers on the matrix cores, the
 // first layer recomputed once per 64-channel output tile; Eq. 2 for each layer with the
 // intermediate removed from the global-memory accesses (FCM paper Sec. IV-B).
@@ -1020,8 +1187,9 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         if (forced >= 0 && i != forced) continue;
         const VariantDesc& v = kVariants[i];
         if (!variant_runs(v, *p, forced >= 0 ? &why : nullptr)) continue;
-        Estimate e = prob_is_gen(*p)            ? estimate_gen(v, *p, d, Ho, Wo)
-                     : p->kind == FCM_KIND_PWDW ? estimate_pwdw(v, *p, d, Ho, Wo)
+        Estimate e = prob_is_gen(*p)              ? estimate_gen(v, *p, d, Ho, Wo)
+                     : p->kind == FCM_KIND_PWDW   ? estimate_pwdw(v, *p, d, Ho, Wo)
+                     : p->kind == FCM_KIND_PWDWPW ? estimate_pwdwpw(v, *p, d, Ho, Wo)
                      : p->kind == FCM_KIND_PWPW ? estimate_pwpw(v, *p, d)
                                                 : estimate(v, *p, d, Ho, Wo);
         if (e.wgs_per_cu <= 0) {
@@ -1095,6 +1263,36 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         pl.fuse = (be.gma < pl.gma_paper_unfused) ? 1 : 0;
         pl.pred_us_fused = be.t_us;
         pl.flops = 2.0 * M * p->C * p->K1 + 2.0 * M * p->K1 * p->K;
+        *out = pl;
+        return FCM_OK;
+    }
+    if (p->kind == FCM_KIND_PWDWPW) {
+        // expansion [K1][C] as is; depthwise [R*S][K1]; the projection's [K][K1] filters
+        // are read unpacked
+        pl.w1_packed_bytes = (int64_t)p->K1 * p->C * e;
+        pl.w2_packed_bytes = (int64_t)p->R * p->S * p->K1 * e;
+        const int64_t t1 = (int64_t)p->N * p->H * p->W * p->K1 * e;
+        const int64_t t2 = (int64_t)p->N * Ho * Wo * p->K1 * e;
+        pl.workspace_bytes = t1 + t2;
+        const int64_t x_bytes = (int64_t)p->N * p->H * p->W * p->C * e;
+        const int64_t y_bytes = (int64_t)p->N * Ho * Wo * p->K * e;
+        pl.alg_bytes_fused = x_bytes + y_bytes + pl.w1_packed_bytes + pl.w2_packed_bytes +
+                             (int64_t)p->K * p->K1 * e + (int64_t)4 * 2 * (2 * p->K1 + p->K);
+        // layer by layer: each intermediate written and read back, and the shortcut
+        // reads the input a second time
+        pl.alg_bytes_unfused = pl.alg_bytes_fused + 2 * (t1 + t2) + (p->residual ? x_bytes : 0);
+        pl.pred_bytes_fused = be.pred;
+        int64_t pu = 0;
+        double gu = 0;
+        estimate_unfused_pwdwpw(*p, Ho, Wo, &pu, &gu);
+        pl.pred_bytes_unfused = pu;
+        pl.gma_paper_fused = be.gma;
+        pl.gma_paper_unfused = gu;
+        pl.fuse = (be.gma < gu) ? 1 : 0;
+        pl.pred_us_fused = be.t_us;
+        pl.flops = 2.0 * p->N * p->H * p->W * p->C * p->K1 +
+                   2.0 * p->N * Ho * Wo * p->K1 * p->R * p->S +
+                   2.0 * p->N * Ho * Wo * p->K1 * p->K;
         *out = pl;
         return FCM_OK;
     }

@@ -20,7 +20,8 @@ enum VKind {
     VK_DWPW_I8 = 8,
     VK_PWPW_MM = 9,
     VK_DWPW_GEN = 10,
-    VK_DWPW_WS = 11
+    VK_DWPW_WS = 11,
+    VK_PWDWPW_MM = 12
 };
 
 struct VariantDesc {
@@ -33,11 +34,12 @@ struct VariantDesc {
     int cc;      // input channels per LDS pass
     int wres;    // pointwise weights resident in registers
     int nbuf;    // input tile buffers in LDS (matrix-core DW only)
-    int k1;      // back-to-back: intermediate channels compiled in (0 otherwise)
+    int k1;      // back-to-back: intermediate channels compiled in; PW->DW->PW: expanded
+                 // channels one workgroup holds (0 otherwise)
     int occ;     // waves per SIMD the kernel is compiled to allow (register budget)
     int waves;   // waves per workgroup
     int cmax;    // largest C the variant takes (0: no limit)
-    int bpw;     // PW->DW: 16-channel blocks per wave (0 otherwise)
+    int bpw;     // PW->DW and PW->DW->PW: 16-channel blocks per wave (0 otherwise)
     int fs;      // generalised DW->PW: filter size, dilation, depth multiplier (0 otherwise)
     int dil;
     int mult;
@@ -93,6 +95,11 @@ inline int prob_dil_w(const fcm_problem& p) { return p.dil_w > 0 ? p.dil_w : 1; 
 inline int prob_mult(const fcm_problem& p) { return p.mult > 0 ? p.mult : 1; }
 inline int prob_ext_h(const fcm_problem& p) { return (p.R - 1) * prob_dil_h(p) + 1; }
 inline int prob_ext_w(const fcm_problem& p) { return (p.S - 1) * prob_dil_w(p) + 1; }
+// The depthwise layer's input and output channels: K1 for PW->DW and PW->DW->PW (the
+// expanded channels), C for the other modules' first layer.
+inline bool prob_has_expansion(const fcm_problem& p) {
+    return p.kind == FCM_KIND_PWDW || p.kind == FCM_KIND_PWDWPW;
+}
 // A DW->PW module whose depthwise layer is not the plain 3x3, undilated, multiplier-1 one.
 inline bool prob_is_gen(const fcm_problem& p) {
     return p.kind == FCM_KIND_DWPW && (p.R != 3 || p.S != 3 || prob_dil_h(p) != 1 ||

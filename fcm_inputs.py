@@ -6,16 +6,19 @@ method's arithmetic and imports neither the HIP library nor the oracle, so both 
 can take their inputs from it.
 
 Every tensor is drawn in float64 from ``numpy.random.default_rng(seed)`` in the fixed
-order X, first-layer weights, scale1, bias1, second-layer weights, scale2, bias2, then
+order X, first-layer weights, scale1, bias1, second-layer weights, scale2, bias2 (and for
+the three-layer module the projection's weights, scale3, bias3), then
 narrowed to float32 and from there to the storage type with torch's round-to-nearest-
 even casts.  The narrowed values *are* the inputs: both the oracle and the GPU see the
 same numbers.  Weight layouts are PyTorch's: depthwise [C*mult, R, S], pointwise [K, C],
 standard conv [K1, C, 3, 3], second conv [K, K1]; for the pointwise->depthwise module
-the first layer is pointwise [K1, C] and the second depthwise [K1, 3, 3] (K = K1).
+the first layer is pointwise [K1, C] and the second depthwise [K1, 3, 3] (K = K1); the
+three-layer module adds the projection [K, K1].
 
 The workloads stand in for the layer shapes the pages evaluate (MobileNet-style
 depthwise-separable blocks, the forum's CIFAR network, ResNet-style 3x3 -> 1x1 pairs,
-MobileNetV2-style inverted-residual expansions for the pointwise->depthwise module);
+MobileNetV2-style inverted-residual expansions for the pointwise->depthwise module and
+whole inverted-residual blocks for the three-layer module);
 no dataset or trained weight is involved.
 """
 from __future__ import annotations
@@ -31,7 +34,7 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "dwpw", "b2b", "pwdw" or "pwpw"
+    kind: str            # "dwpw", "b2b", "pwdw", "pwpw" or "pwdwpw"
     dtype: str           # "f32" | "f16" | "bf16" | "i8"
     N: int
     H: int
@@ -39,7 +42,7 @@ class Workload:
     C: int
     K: int               # output channels of the module (pwdw: == K1)
     K1: int              # b2b: output channels of the 3x3 conv; dwpw: == C;
-                         # pwdw: output channels of the pointwise layer
+                         # pwdw, pwdwpw: output channels of the (first) pointwise layer
     stride: int = 1
     pad: int = 1
     R: int = 3
@@ -52,6 +55,10 @@ class Workload:
     bias1: bool = False
     scale2: bool = False
     bias2: bool = False
+    act3: str = "none"    # pwdwpw: the projection's activation, scale / bias, and whether
+    scale3: bool = False  # the identity shortcut adds the input pixel
+    bias3: bool = False
+    residual: bool = False
     x_dist: tuple = ("normal", 0.0, 1.0)
     w_dist: tuple = ("normal", 0.0, 0.1)
     scale_dist: tuple = ("uniform", 0.5, 1.5)
@@ -133,6 +140,23 @@ WORKLOADS = {
         bias2=True, x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=7,
         description="Downsampling PW->DW module: PW 16->96 + scale/bias+ReLU6, DW 3x3 s2 "
                     "+ scale/bias+ReLU6, fp16, N=32 112x112 -> 56x56"),
+    # the three layers of an inverted-residual block (PW -> DW -> PW)
+    "pwdwpw_f16_32x56x56_c24_k144_k24": Workload(
+        "pwdwpw_f16_32x56x56_c24_k144_k24", "pwdwpw", "f16", N=32, H=56, W=56, C=24, K=24,
+        K1=144, act1="relu6", act2="relu6", act3="none", residual=True, scale1=True,
+        bias1=True, scale2=True, bias2=True, scale3=True, bias3=True,
+        x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=13,
+        description="Inverted-residual block (MobileNetV2-style 56x56 stage): PW 24->144 + "
+                    "scale/bias+ReLU6, DW 3x3 s1 + scale/bias+ReLU6, PW 144->24 + "
+                    "scale/bias (linear), identity shortcut, fp16, N=32 56x56"),
+    "pwdwpw_f16_32x112x112_c16_k96_k24_s2": Workload(
+        "pwdwpw_f16_32x112x112_c16_k96_k24_s2", "pwdwpw", "f16", N=32, H=112, W=112, C=16,
+        K=24, K1=96, stride=2, act1="relu6", act2="relu6", act3="none", scale1=True,
+        bias1=True, scale2=True, bias2=True, scale3=True, bias3=True,
+        x_dist=("normal", 0.0, 1.0), w_dist=("normal", 0.0, 0.1), seed=14,
+        description="Downsampling inverted-residual block: PW 16->96 + scale/bias+ReLU6, "
+                    "DW 3x3 s2 + scale/bias+ReLU6, PW 96->24 + scale/bias (linear), fp16, "
+                    "N=32 112x112 -> 56x56"),
     # generalised depthwise layers (filter size, dilation, depth multiplier)
     "dw5_f16_32x28x28_c120_k40": Workload(
         "dw5_f16_32x28x28_c120_k40", "dwpw", "f16", N=32, H=28, W=28, C=120, K=40, K1=120,
@@ -192,7 +216,7 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> dict:
     if wl.kind == "dwpw":
         w1 = _draw(rng, wl.w_dist, (wl.C * wl.mult, wl.R, wl.S))
         n1 = wl.C * wl.mult
-    elif wl.kind in ("pwdw", "pwpw"):
+    elif wl.kind in ("pwdw", "pwpw", "pwdwpw"):
         w1 = _draw(rng, wl.w_dist, (wl.K1, wl.C))
         n1 = wl.K1
     else:
@@ -200,12 +224,18 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> dict:
         n1 = wl.K1
     s1 = _draw(rng, wl.scale_dist, (n1,)) if wl.scale1 else None
     b1 = _draw(rng, wl.bias_dist, (n1,)) if wl.bias1 else None
-    if wl.kind == "pwdw":
+    if wl.kind in ("pwdw", "pwdwpw"):
         w2 = _draw(rng, wl.w_dist, (wl.K1, wl.R, wl.S))
     else:
         w2 = _draw(rng, wl.w_dist, (wl.K, n1))
-    s2 = _draw(rng, wl.scale_dist, (wl.K,)) if wl.scale2 else None
-    b2 = _draw(rng, wl.bias_dist, (wl.K,)) if wl.bias2 else None
+    n2 = wl.K1 if wl.kind == "pwdwpw" else wl.K
+    s2 = _draw(rng, wl.scale_dist, (n2,)) if wl.scale2 else None
+    b2 = _draw(rng, wl.bias_dist, (n2,)) if wl.bias2 else None
+    w3 = s3 = b3 = None
+    if wl.kind == "pwdwpw":
+        w3 = _draw(rng, wl.w_dist, (wl.K, wl.K1))
+        s3 = _draw(rng, wl.scale_dist, (wl.K,)) if wl.scale3 else None
+        b3 = _draw(rng, wl.bias_dist, (wl.K,)) if wl.bias3 else None
     out = {
         "x": _narrow(x, wl.dtype),
         "w1": _narrow(w1, wl.dtype),
@@ -215,6 +245,10 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> dict:
         "scale2": None if s2 is None else _narrow(s2, "f32"),
         "bias2": None if b2 is None else _narrow(b2, "f32"),
     }
+    if wl.kind == "pwdwpw":
+        out["w3"] = _narrow(w3, wl.dtype)
+        out["scale3"] = None if s3 is None else _narrow(s3, "f32")
+        out["bias3"] = None if b3 is None else _narrow(b3, "f32")
     return out
 
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FCM_PLAN_VERSION 3
+#define FCM_PLAN_VERSION 4
 
 typedef enum {
     FCM_OK = 0,
@@ -74,8 +74,13 @@ typedef enum {
     FCM_KIND_DWPW = 0, /* depthwise RxS conv (C -> C) then pointwise 1x1 (C -> K) */
     FCM_KIND_B2B = 1,  /* standard RxS conv (C -> K1) then 1x1 conv (K1 -> K) */
     FCM_KIND_PWDW = 2, /* pointwise 1x1 (C -> K1) then depthwise RxS conv (K1 -> K1) */
-    FCM_KIND_PWPW = 3  /* pointwise 1x1 (C -> K1) then pointwise 1x1 (K1 -> K); R = S = 1,
+    FCM_KIND_PWPW = 3, /* pointwise 1x1 (C -> K1) then pointwise 1x1 (K1 -> K); R = S = 1,
                           stride 1, no padding */
+    FCM_KIND_PWDWPW = 4 /* the three layers of an inverted-residual block (FCM paper
+                          Sec. II-B: PW-DW-PW; Fig. 4): pointwise 1x1 expansion (C -> K1),
+                          depthwise RxS conv (K1 -> K1, the stride and padding below),
+                          pointwise 1x1 projection (K1 -> K), each with its epilogue, and
+                          optionally the block's identity shortcut (`residual`) */
 } fcm_kind;
 
 /* The problem, in the pages' terms: NHWC input feature maps, per-channel depthwise
@@ -114,6 +119,14 @@ typedef struct {
      * Other kinds require 0 or 1 here (FCM_ERR_INVALID_ARG otherwise). */
     int32_t dil_h, dil_w;
     int32_t mult;
+    /* PW->DW->PW module only (other kinds require 0 here, FCM_ERR_INVALID_ARG otherwise):
+     *  - act3: fcm_act after the projection's scale/bias (an inverted residual's linear
+     *    bottleneck is FCM_ACT_NONE);
+     *  - residual: 1 adds the module's input pixel to its output after act3, before the
+     *    single rounding to the storage type (the block's identity shortcut); needs
+     *    stride 1, K == C and an output extent equal to the input's. */
+    int32_t act3;
+    int32_t residual;
 } fcm_problem;
 
 /* What the planner needs to know about the GPU (FusePlanner's inputs: number of
@@ -178,10 +191,11 @@ fcm_status fcm_query_device_spec(int device, fcm_device_spec* out);
  * with the pages' rule (fewer estimated global memory accesses) whether fusing
  * beats the layer-by-layer kernels.  spec == NULL uses the MI355X defaults.
  * Host only; makes no HIP call.  Errors: INVALID_ARG (null pointer, non-positive
- * size, K1 != C for DWPW, K != K1 for PWDW, padding >= filter), UNSUPPORTED (filter not
- * 3x3, stride not 1 or 2, padding not 0 or 1, a channel count not a multiple of 8, fp32
- * storage for B2B or PWDW, int8 storage other than DWPW or with C or K not a multiple
- * of 16, or no variant fits). */
+ * size, K1 != C for DWPW, K != K1 for PWDW, padding >= filter, act3 or residual set for
+ * a kind other than PWDWPW, a shortcut whose shapes do not match), UNSUPPORTED (filter
+ * not 3x3, stride not 1 or 2, padding not 0 or 1, a channel count not a multiple of 8,
+ * fp32 storage for B2B, PWDW or PWDWPW, int8 storage other than DWPW or with C or K
+ * not a multiple of 16, or no variant fits). */
 fcm_status fcm_plan(const fcm_problem* prob, const fcm_device_spec* spec, fcm_plan_t* out);
 
 /* Same, but with the fused kernel variant forced (for tests and on-device tuning).
@@ -269,6 +283,8 @@ const char* fcm_variant_name(int32_t variant);
  *   PWPW: w1_src [K1][C] copied as is; w2_src [K][K1] copied, then blocked as for DWPW
  *   PWDW: w1_src pointwise [K1][C]        -> w1_dst [K1][C]       (copied as is)
  *         w2_src depthwise [K1][R][S]     -> w2_dst [R*S][K1]     (channel fastest)
+ *   PWDWPW: w1 and w2 as for PWDW; the projection's [K][K1] filters are read as
+ *         PyTorch stores them ([K][K1][1][1]), with no packing
  * Sizes in bytes are plan->w1_packed_bytes / w2_packed_bytes.  Either pair may be
  * NULL to skip it.  Source and destination must not overlap. */
 fcm_status fcm_pack_weights(const fcm_plan_t* plan, const void* w1_src, void* w1_dst,
@@ -309,6 +325,43 @@ fcm_status fcm_pwdw_fwd(const fcm_plan_t* plan, const void* x, const void* w_pw,
 fcm_status fcm_pwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
                         const float* scale1, const float* bias1, const void* w2,
                         const float* scale2, const float* bias2, void* y, void* stream);
+
+/* Fused PW -> DW -> PW module (the inverted-residual block).  x: [N][H][W][C];
+ * w1: packed [K1][C] expansion filters; scale1/bias1: [K1] or NULL; w2: packed
+ * [R*S][K1] depthwise filters; scale2/bias2: [K1] or NULL; w3: [K][K1] projection
+ * filters (PyTorch layout, not packed); scale3/bias3: [K] or NULL; y: [N][Ho][Wo][K].
+ * With plan->prob.residual the input pixel is added after epilogue 3 (x must then also
+ * be the shortcut: stride 1, K == C).  The two intermediates stay on chip.  All tensor
+ * pointers 16-byte aligned, epilogue arrays 4-byte aligned; y must not overlap x.
+ * plan->prob.kind must be FCM_KIND_PWDWPW.  Errors: INVALID_ARG (plan/pointer checks),
+ * HIP (launch failure). */
+fcm_status fcm_pwdwpw_fwd(const fcm_plan_t* plan, const void* x, const void* w1,
+                          const float* scale1, const float* bias1, const void* w2,
+                          const float* scale2, const float* bias2, const void* w3,
+                          const float* scale3, const float* bias3, void* y, void* stream);
+
+/* Layer-by-layer baseline of the PW -> DW -> PW module: the pointwise kernel writes the
+ * expansion t1: [N][H][W][K1], the depthwise kernel reads it and writes t2:
+ * [N][Ho][Wo][K1], the pointwise kernel reads t2 and writes y (adding x for the
+ * shortcut).  t1 and t2 are caller buffers (plan->workspace_bytes in total: t1's bytes
+ * then t2's).  Same arguments and errors as fcm_pwdwpw_fwd otherwise. */
+fcm_status fcm_pwdwpw_lbl(const fcm_plan_t* plan, const void* x, const void* w1,
+                          const float* scale1, const float* bias1, const void* w2,
+                          const float* scale2, const float* bias2, const void* w3,
+                          const float* scale3, const float* bias3, void* t1, void* t2, void* y,
+                          void* stream);
+
+/* fcm_tune for the PW -> DW -> PW module: every fused variant able to take `prob`
+ * (kind FCM_KIND_PWDWPW) at each persistent grid, timed over the nsets pairs x[i], y[i]
+ * with the three layers' filters and epilogues as fcm_pwdwpw_fwd takes them.  Writes
+ * the fastest plan to *out (out->tuned_us its mean time per call); synchronises
+ * `stream`; allocates no device memory.  Errors as fcm_tune. */
+fcm_status fcm_tune_pwdwpw(const fcm_problem* prob, const fcm_device_spec* spec, int32_t nsets,
+                           const void* const* x, const void* w1, const float* scale1,
+                           const float* bias1, const void* w2, const float* scale2,
+                           const float* bias2, const void* w3, const float* scale3,
+                           const float* bias3, void* const* y, void* stream, int32_t iters,
+                           fcm_plan_t* out);
 
 /* Layer-by-layer baseline, first layer of a DWPW plan: depthwise conv + epilogue 1,
  * writing the intermediate t: [N][Ho][Wo][C] (plan->workspace_bytes bytes).

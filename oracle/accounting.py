@@ -49,6 +49,15 @@ def sizes(wl) -> dict:
     n1 = wl.C * wl.mult if wl.kind == "dwpw" else wl.K1
     x = wl.N * wl.H * wl.W * wl.C
     y = wl.N * Ho * Wo * wl.K
+    if wl.kind == "pwdwpw":
+        # two intermediates: the expansion at the input resolution, the depthwise output
+        # at the output resolution; three filter arrays and three epilogues
+        t = wl.N * wl.H * wl.W * n1 + wl.N * Ho * Wo * n1
+        epi = 4 * (n1 * (int(wl.scale1) + int(wl.bias1) + int(wl.scale2) + int(wl.bias2))
+                   + wl.K * (int(wl.scale3) + int(wl.bias3)))
+        return {"x": x * e, "t": t * e, "y": y * e, "w1": wl.K1 * wl.C * e,
+                "w2": wl.K1 * wl.R * wl.S * e, "w3": wl.K * wl.K1 * e, "epi": epi, "elem": e,
+                "pixels_out": wl.N * Ho * Wo}
     if wl.kind == "pwdw":
         # the intermediate is the pointwise layer's output, at the input resolution
         t = wl.N * wl.H * wl.W * n1
@@ -64,10 +73,15 @@ def sizes(wl) -> dict:
 
 
 def alg_bytes(wl, fused: bool = True) -> int:
+    """Fused: input, output, filters and epilogue arrays once.  Layer by layer: each
+    intermediate also written and read back, and (three-layer module with the identity
+    shortcut) the input read a second time by the last layer."""
     s = sizes(wl)
-    b = s["x"] + s["y"] + s["w1"] + s["w2"] + s["epi"]
+    b = s["x"] + s["y"] + s["w1"] + s["w2"] + s.get("w3", 0) + s["epi"]
     if not fused:
         b += 2 * s["t"]
+        if wl.kind == "pwdwpw" and wl.residual:
+            b += s["x"]
     return b
 
 
@@ -79,6 +93,9 @@ def flops(wl) -> int:
         return 2 * P * n1 * wl.R * wl.S + 2 * P * n1 * wl.K
     if wl.kind == "pwdw":
         return 2 * wl.N * wl.H * wl.W * wl.C * wl.K1 + 2 * P * wl.K1 * wl.R * wl.S
+    if wl.kind == "pwdwpw":
+        return (2 * wl.N * wl.H * wl.W * wl.C * wl.K1 + 2 * P * wl.K1 * wl.R * wl.S
+                + 2 * P * wl.K1 * wl.K)
     return 2 * P * wl.K1 * wl.C * wl.R * wl.S + 2 * P * wl.K1 * wl.K
 
 
@@ -166,6 +183,21 @@ def dwpw_gma(dw_ifms_d: int, dw_overlap: int, dw_ifms_sz: int, dw_weights_sz: in
             * _ceil_div(pw_weights_sz, pw_weights_tile_sz)
             + n_out_tiles * (pw_weights_sz + dw_weights_sz)
             + pw_ofms_sz)
+
+
+def pwdwpw_gma(pw_ifms_d: int, dw_overlap: int, pw_ifms_sz: int, w1_sz: int, w2_sz: int,
+               w3_sz: int, ofms_sz: int, ofms_tile_sz: int, tiles_sz_sum: int,
+               n_fcm_ofm_tiles: int, l1_sz: int, n_sms: int) -> float:
+    """Three-layer PW->DW->PW module.  The pages print no estimate for three layers; this
+    one takes Eq. 4's form for a module whose workgroup holds every expanded channel (a
+    single weight tile): the first layer's input with the depthwise overlap once, the
+    three layers' filters once per output tile, the intermediates free, the output once."""
+    if l1_sz < tiles_sz_sum:
+        return INF
+    if n_fcm_ofm_tiles < n_sms:
+        return INF
+    return ((2 * pw_ifms_d * dw_overlap + pw_ifms_sz)
+            + _ceil_div(ofms_sz, ofms_tile_sz) * (w1_sz + w2_sz + w3_sz) + ofms_sz)
 
 
 def pwdw_redundancy(H: int, W: int, tile_h: int, tile_w: int, stride: int = 1,

@@ -27,9 +27,18 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 def oracle_kwargs(wl, inp) -> dict:
-    return dict(stride=(wl.stride, wl.stride), pad=(wl.pad, wl.pad), scale1=inp["scale1"],
-                bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],
-                act2=wl.act2, dtype=wl.dtype)
+    kw = dict(stride=(wl.stride, wl.stride), pad=(wl.pad, wl.pad), scale1=inp["scale1"],
+              bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],
+              act2=wl.act2, dtype=wl.dtype)
+    if wl.kind == "pwdwpw":
+        kw.update(scale3=inp.get("scale3"), bias3=inp.get("bias3"), act3=wl.act3,
+                  residual=wl.residual)
+    return kw
+
+
+def final_act(wl) -> str:
+    """The activation of the module's last layer."""
+    return wl.act3 if wl.kind == "pwdwpw" else wl.act2
 
 
 def is_gen(wl) -> bool:
@@ -41,6 +50,8 @@ def oracle_full(wl, inp) -> np.ndarray:
     if is_gen(wl):
         return oracle.dwpw_gen(inp["x"], inp["w1"], inp["w2"],
                                dilation=(wl.dil, wl.dil), **oracle_kwargs(wl, inp))
+    if wl.kind == "pwdwpw":
+        return oracle.pwdwpw(inp["x"], inp["w1"], inp["w2"], inp["w3"], **oracle_kwargs(wl, inp))
     fn = {"dwpw": oracle.dwpw, "b2b": oracle.b2b, "pwdw": oracle.pwdw,
           "pwpw": oracle.pwpw}[wl.kind]
     return fn(inp["x"], inp["w1"], inp["w2"], **oracle_kwargs(wl, inp))
@@ -50,6 +61,9 @@ def oracle_rows(wl, inp, pix) -> np.ndarray:
     if is_gen(wl):  # the whole output (seconds at the workloads' sizes), then the pixels
         full = oracle_full(wl, inp)
         return full[pix[:, 0], pix[:, 1], pix[:, 2]]
+    if wl.kind == "pwdwpw":
+        return oracle.pwdwpw_at(inp["x"], inp["w1"], inp["w2"], inp["w3"], pix,
+                                **oracle_kwargs(wl, inp))
     fn = {"dwpw": oracle.dwpw_at, "b2b": oracle.b2b_at, "pwdw": oracle.pwdw_at,
           "pwpw": oracle.pwpw_at}[wl.kind]
     return fn(inp["x"], inp["w1"], inp["w2"], pix, **oracle_kwargs(wl, inp))
@@ -80,6 +94,8 @@ def int_inputs(wl, seed: int) -> dict:
     x = rng.integers(-2, 3, size=(wl.N, wl.H, wl.W, wl.C)).astype(np.float64)
     if wl.kind == "pwdw":
         return _int_inputs_pwdw(wl, rng, x)
+    if wl.kind == "pwdwpw":
+        return _int_inputs_pwdwpw(wl, rng, x)
     n1 = wl.C * wl.mult if wl.kind == "dwpw" else wl.K1
     if is_gen(wl):
         # at most 9 non-zero taps of +-1 per filter, whatever its size
@@ -139,12 +155,40 @@ def _int_inputs_pwdw(wl, rng, x) -> dict:
             "scale2": s2, "bias2": b2}
 
 
+def _int_inputs_pwdwpw(wl, rng, x) -> dict:
+    """PW->DW->PW module: 2 non-zero expansion taps of +-1 per expanded channel
+    (|t1| <= 2*4+2 = 10), 3 non-zero depthwise taps (|t2| <= 2*30+2 = 62), 2 non-zero
+    projection taps with scale 1 (|y| <= 124+2, plus 2 for the shortcut): every value an
+    integer below 256, exact in every storage type."""
+    w1 = np.zeros((wl.K1, wl.C))
+    for k in range(wl.K1):
+        idx = rng.choice(wl.C, size=min(2, wl.C), replace=False)
+        w1[k, idx] = rng.choice([-1.0, 1.0], size=idx.size)
+    s1 = rng.choice([1.0, 2.0], size=wl.K1) if wl.scale1 else None
+    b1 = rng.integers(-2, 3, size=wl.K1).astype(np.float64) if wl.bias1 else None
+    w2 = np.zeros((wl.K1, 9))
+    for k in range(wl.K1):
+        idx = rng.choice(9, size=3, replace=False)
+        w2[k, idx] = rng.choice([-1.0, 1.0], size=3)
+    s2 = rng.choice([1.0, 2.0], size=wl.K1) if wl.scale2 else None
+    b2 = rng.integers(-2, 3, size=wl.K1).astype(np.float64) if wl.bias2 else None
+    w3 = np.zeros((wl.K, wl.K1))
+    for k in range(wl.K):
+        idx = rng.choice(wl.K1, size=min(2, wl.K1), replace=False)
+        w3[k, idx] = rng.choice([-1.0, 1.0], size=idx.size)
+    s3 = np.ones(wl.K) if wl.scale3 else None
+    b3 = rng.integers(-2, 3, size=wl.K).astype(np.float64) if wl.bias3 else None
+    return {"x": x, "w1": w1, "w2": w2.reshape(wl.K1, 3, 3), "scale1": s1, "bias1": b1,
+            "scale2": s2, "bias2": b2, "w3": w3, "scale3": s3, "bias3": b3}
+
+
 def all_variants_for(wl):
     """Indices of every compiled variant able to run the workload."""
     import depthwise_pointwise_convolution_amd as F
     p = F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
                   None if wl.kind == "dwpw" else wl.K1, R=wl.R, S=wl.S, stride=wl.stride,
-                  pad=wl.pad, act1=wl.act1, act2=wl.act2, dilation=wl.dil, mult=wl.mult)
+                  pad=wl.pad, act1=wl.act1, act2=wl.act2, dilation=wl.dil, mult=wl.mult,
+                  act3=wl.act3, residual=wl.residual)
     out = []
     for v in range(F.fcm_num_variants()):
         try:
@@ -170,6 +214,8 @@ REDUCED = {
     "dw5_f16_32x28x28_c120_k40": dict(N=2, H=29, W=37),
     "dil2_f16_8x33x33_c960_k160": dict(N=2, H=21, W=19),
     "mult2_f16_8x112x112_c32_k128": dict(N=2, H=29, W=37),
+    "pwdwpw_f16_32x56x56_c24_k144_k24": dict(N=2, H=29, W=37),
+    "pwdwpw_f16_32x112x112_c16_k96_k24_s2": dict(N=2, H=45, W=57),
 }
 
 

@@ -72,7 +72,8 @@ def test_library_has_no_undefined_own_symbols():
 def _problem(F, wl):
     return F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
                      None if wl.kind == "dwpw" else wl.K1, R=wl.R, S=wl.S, stride=wl.stride,
-                     pad=wl.pad, act1=wl.act1, act2=wl.act2, dilation=wl.dil, mult=wl.mult)
+                     pad=wl.pad, act1=wl.act1, act2=wl.act2, dilation=wl.dil, mult=wl.mult,
+                     act3=wl.act3, residual=wl.residual)
 
 
 def _spec(F):
@@ -87,13 +88,14 @@ def test_plan_integers_match_oracle_accounting(name):
     assert pl.version == F.FCM_PLAN_VERSION
     assert (pl.Ho, pl.Wo) == (wl.Ho, wl.Wo)
     # the library counts every epilogue array (its callers may pass any of them)
-    full = wl.replace(scale1=True, bias1=True, scale2=True, bias2=True)
+    full = wl.replace(scale1=True, bias1=True, scale2=True, bias2=True, scale3=True,
+                      bias3=True)
     assert pl.alg_bytes_fused == acct.alg_bytes(full, fused=True)
     assert pl.alg_bytes_unfused == acct.alg_bytes(full, fused=False)
     n1 = wl.C * wl.mult if wl.kind == "dwpw" else wl.K1
     e = acct.ELEM_BYTES[wl.dtype]
     assert pl.workspace_bytes == acct.sizes(wl)["t"]
-    if wl.kind != "pwdw":
+    if wl.kind not in ("pwdw", "pwdwpw"):
         assert pl.workspace_bytes == wl.N * wl.Ho * wl.Wo * n1 * e
     assert pl.flops == acct.flops(wl)
     # tiling and launch shape are self-consistent
@@ -325,7 +327,9 @@ def test_forced_variants_cover_every_compiled_kernel():
         fcm_inputs.Workload("g", "dwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=c * m, R=f, S=f,
                             stride=s, pad=(f - 1) * d // 2, dil=d, mult=m)
         for dt in ("f16", "bf16") for c, k in ((40, 48), (64, 136)) for s in (1, 2)
-        for f, d, m in ((5, 1, 1), (7, 1, 1), (3, 2, 1), (3, 1, 2))]
+        for f, d, m in ((5, 1, 1), (7, 1, 1), (3, 2, 1), (3, 1, 2))] + [
+        fcm_inputs.Workload("i", "pwdwpw", dt, N=2, H=17, W=23, C=24, K=24, K1=k1, stride=s)
+        for dt in ("f16", "bf16") for k1 in (96, 144) for s in (1, 2)]
     for wl in shapes:
         prob = _problem(F, wl)
         for v in range(F.fcm_num_variants()):
@@ -565,6 +569,10 @@ def _paper_fused(wl, pl, spec):
                              kt * wl.K1 * e, y, th * tw * kt * e, **feas)
     ext = (wl.R - 1) * wl.dil + 1
     ov = acct.eq1_overlap(wl.W, wl.H, tw * wl.stride, th * wl.stride, ext, ext, wl.stride)
+    if wl.kind == "pwdwpw":
+        y = wl.N * wl.Ho * wl.Wo * wl.K * e
+        return acct.pwdwpw_gma(wl.C, ov * wl.N * e, ifm, wl.K1 * wl.C * e, 9 * wl.K1 * e,
+                               wl.K * wl.K1 * e, y, th * tw * wl.K * e, **feas)
     if wl.kind == "pwdw":
         kt = min(pl.k_tile, wl.K1)
         y = wl.N * wl.Ho * wl.Wo * wl.K1 * e
@@ -596,14 +604,19 @@ def _paper_unfused(wl, spec):
     if wl.kind == "pwpw":
         M = wl.N * wl.H * wl.W
         return pw_layer(wl.C, wl.K1, M) + pw_layer(wl.K1, wl.K, M)
-    if wl.kind == "pwdw":
+    if wl.kind in ("pwdw", "pwdwpw"):
         M = wl.N * wl.H * wl.W
         th, tw = t["DW_TH"], t["DW_TW"]
         ov = acct.eq1_overlap(wl.W, wl.H, tw * wl.stride, th * wl.stride, 3, 3, wl.stride)
         tsz = M * wl.K1 * e
         dw = acct.eq3_dw_gma(wl.K1, ov * wl.N * e, tsz, wl.N * wl.Ho * wl.Wo * wl.K1 * e,
                              wl.N * wl.Ho * wl.Wo, th * tw, 9 * wl.K1 * e, 0, 0, 0, 1, **big)
-        return pw_layer(wl.C, wl.K1, M) + dw
+        if wl.kind == "pwdw":
+            return pw_layer(wl.C, wl.K1, M) + dw
+        # the projection over the depthwise output, and the input read again for the
+        # shortcut
+        res = ifm if wl.residual else 0
+        return pw_layer(wl.C, wl.K1, M) + dw + pw_layer(wl.K1, wl.K, wl.N * wl.Ho * wl.Wo) + res
     P = wl.N * wl.Ho * wl.Wo
     n1 = wl.C * wl.mult if wl.kind == "dwpw" else wl.K1
     tsz = P * n1 * e
