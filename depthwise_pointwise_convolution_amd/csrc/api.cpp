@@ -298,21 +298,7 @@ const char* fcm_last_error(void) { return g_last_error.c_str(); }
 
 fcm_status fcm_default_device_spec(fcm_device_spec* out) {
     if (!out) return fail(FCM_ERR_INVALID_ARG, "spec output pointer is NULL");
-    memset(out, 0, sizeof(*out));
-    out->num_cus = 256;
-    out->num_xcds = 8;
-    out->simds_per_cu = 4;
-    out->wave_size = 64;
-    out->max_waves_per_simd = 8;
-    out->vgprs_per_simd_lane = 512;
-    out->lds_bytes_per_cu = 160 * 1024;
-    out->lds_bytes_per_wg = 160 * 1024;
-    out->l2_bytes_per_xcd = 4LL * 1024 * 1024;
-    out->hbm_bytes_per_s = 8.0e12;
-    out->mfma_f16_flops = 2.5e15;
-    out->mfma_f32_flops = 157.3e12;
-    // 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz, no packed fp32 math
-    out->valu_f32_flops = 256.0 * 4 * 16 * 2 * 2.4e9;
+    default_spec(out);
     return ok();
 }
 

@@ -28,6 +28,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <cmath>
 #include <vector>
 
@@ -79,6 +80,20 @@ const int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 namespace {
 
 int elem_bytes(int dtype) { return dtype == FCM_F32 ? 4 : dtype == FCM_I8 ? 1 : 2; }
+
+// Product of sizes for the range checks, saturated at 2^61 (the checks compare it with
+// bounds far below, and an unvalidated problem may hold sizes whose product overflows);
+// 0 if any factor is not positive.
+int64_t sat_mul(std::initializer_list<int64_t> xs) {
+    const int64_t cap = (int64_t)1 << 61;
+    int64_t r = 1;
+    for (int64_t x : xs) {
+        if (x <= 0) return 0;
+        if (r > cap / x) return cap;
+        r *= x;
+    }
+    return r;
+}
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Rows (or columns) of the input that the halo window of output tile `t` (extent
@@ -116,6 +131,24 @@ int64_t persistent_grid(int64_t ptiles, int ktiles, int64_t capacity) {
     const int64_t work = ptiles * ktiles;
     const int64_t g = std::min(work, std::max<int64_t>(capacity, ktiles));
     return std::max<int64_t>(g / ktiles, 1) * ktiles;
+}
+
+void default_spec(fcm_device_spec* out) {
+    memset(out, 0, sizeof(*out));
+    out->num_cus = 256;
+    out->num_xcds = 8;
+    out->simds_per_cu = 4;
+    out->wave_size = 64;
+    out->max_waves_per_simd = 8;
+    out->vgprs_per_simd_lane = 512;
+    out->lds_bytes_per_cu = 160 * 1024;
+    out->lds_bytes_per_wg = 160 * 1024;
+    out->l2_bytes_per_xcd = 4LL * 1024 * 1024;
+    out->hbm_bytes_per_s = 8.0e12;
+    out->mfma_f16_flops = 2.5e15;
+    out->mfma_f32_flops = 157.3e12;
+    // 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz, no packed fp32 math
+    out->valu_f32_flops = 256.0 * 4 * 16 * 2 * 2.4e9;
 }
 
 int variant_lds_bytes(const VariantDesc& v) {
@@ -379,8 +412,8 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
         return FCM_ERR_INVALID_ARG;
     }
     const int64_t big = (int64_t)1 << 31;
-    if ((int64_t)p->N * p->H * p->W * p->C >= big || (int64_t)p->N * p->H * p->W * p->K >= big ||
-        (int64_t)p->N * p->H * p->W * p->K1 >= big) {
+    if (sat_mul({p->N, p->H, p->W, p->C}) >= big || sat_mul({p->N, p->H, p->W, p->K}) >= big ||
+        sat_mul({p->N, p->H, p->W, p->K1}) >= big) {
         *err = "tensor element counts must stay below 2^31";
         return FCM_ERR_UNSUPPORTED;
     }
@@ -400,7 +433,7 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
             return FCM_ERR_UNSUPPORTED;
         }
         const int64_t big = (int64_t)1 << 31;
-        if ((int64_t)p->N * p->H * p->W * std::max(std::max(p->C, p->K), p->K1) >= big) {
+        if (sat_mul({p->N, p->H, p->W, std::max(std::max(p->C, p->K), p->K1)}) >= big) {
             *err = "tensor element counts must stay below 2^31";
             return FCM_ERR_UNSUPPORTED;
         }
@@ -491,8 +524,8 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
             if (why) *why = "PW->PW variant takes at most 64 input and 64 intermediate channels";
             return false;
         }
-        const int64_t M = (int64_t)p.N * p.H * p.W;
-        if (M * p.C * 2 >= ((int64_t)1 << 31) || M * p.K * 2 >= ((int64_t)1 << 30)) {
+        const int64_t M = sat_mul({p.N, p.H, p.W});
+        if (sat_mul({M, p.C, 2}) >= ((int64_t)1 << 31) || sat_mul({M, p.K, 2}) >= ((int64_t)1 << 30)) {
             if (why) *why = "PW->PW variant addresses inputs below 2 GiB and outputs below 1 GiB";
             return false;
         }
@@ -513,8 +546,8 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         }
         const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
         const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
-        if ((int64_t)p.N * p.H * p.W * p.C >= ((int64_t)1 << 31) ||
-            (int64_t)p.N * Ho * Wo * p.K >= ((int64_t)1 << 30)) {
+        if (sat_mul({p.N, p.H, p.W, p.C}) >= ((int64_t)1 << 31) ||
+            sat_mul({p.N, Ho, Wo, p.K}) >= ((int64_t)1 << 30)) {
             if (why) *why = "int8 variant addresses inputs below 2 GiB and outputs below 1 GiB";
             return false;
         }
@@ -536,8 +569,8 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         }
         const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
         const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
-        if ((int64_t)p.N * p.H * p.W * p.C * 2 >= ((int64_t)1 << 31) ||
-            (int64_t)p.N * Ho * Wo * p.K * 2 >= ((int64_t)1 << 30)) {
+        if (sat_mul({p.N, p.H, p.W, p.C, 2}) >= ((int64_t)1 << 31) ||
+            sat_mul({p.N, Ho, Wo, p.K, 2}) >= ((int64_t)1 << 30)) {
             if (why) *why = "PW->DW->PW variant addresses inputs below 2 GiB and outputs below "
                             "1 GiB";
             return false;
@@ -559,8 +592,8 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         }
         const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
         const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
-        if ((int64_t)p.N * p.H * p.W * p.C * 2 >= ((int64_t)1 << 31) ||
-            (int64_t)p.N * Ho * Wo * p.K1 * 2 >= ((int64_t)1 << 30)) {
+        if (sat_mul({p.N, p.H, p.W, p.C, 2}) >= ((int64_t)1 << 31) ||
+            sat_mul({p.N, Ho, Wo, p.K1, 2}) >= ((int64_t)1 << 30)) {
             if (why) *why = "PW->DW variant addresses inputs below 2 GiB and outputs below 1 GiB";
             return false;
         }
@@ -610,8 +643,8 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
         const int Wo = conv_out(p.W, p.pad_w, p.S, p.stride_w);
         const int64_t e = p.dtype == FCM_F32 ? 4 : 2;
-        if ((int64_t)p.N * p.H * p.W * p.C * e >= ((int64_t)1 << 31) ||
-            (int64_t)p.N * Ho * Wo * p.K * e >= ((int64_t)1 << 31)) {
+        if (sat_mul({p.N, p.H, p.W, p.C, e}) >= ((int64_t)1 << 31) ||
+            sat_mul({p.N, Ho, Wo, p.K, e}) >= ((int64_t)1 << 31)) {
             if (why) *why = "matrix-core depthwise variant addresses whole tensors below 2 GiB";
             return false;
         }
@@ -1170,7 +1203,7 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     if (spec) {
         d = *spec;
     } else {
-        fcm_default_device_spec(&d);
+        default_spec(&d);
     }
     if (d.num_cus <= 0 || d.lds_bytes_per_cu <= 0 || d.lds_bytes_per_wg <= 0 ||
         d.vgprs_per_simd_lane <= 0 || d.max_waves_per_simd <= 0) {

@@ -45,6 +45,10 @@ struct VariantDesc {
     int mult;
 };
 
+// MI355X published figures (256 CUs, 160 KB LDS per CU, 8 TB/s HBM, 2.5 PFLOP/s dense
+// fp16/bf16 matrix rate, ...); host only.
+void default_spec(fcm_device_spec* out);
+
 extern const VariantDesc kVariants[];
 extern const int kNumVariants;
 
@@ -108,7 +112,8 @@ inline bool prob_is_gen(const fcm_problem& p) {
 
 // Output extent of a convolution.
 inline int conv_out(int in, int pad, int filt, int stride) {
-    return (in + 2 * pad - filt) / stride + 1;
+    // (64-bit: an unvalidated problem may hold sizes whose sum overflows an int)
+    return (int)(((int64_t)in + 2 * (int64_t)pad - filt) / stride + 1);
 }
 
 }  // namespace fcm
