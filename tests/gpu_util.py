@@ -26,6 +26,34 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return num / den if den > 0 else num
 
 
+MANTISSA = {"f32": 23, "f16": 10, "bf16": 7}
+
+
+def ulp(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the storage type's values at |a| (normal range; subnormal spacing below
+    the smallest normal)."""
+    m = MANTISSA[dtype]
+    emin = {"f32": -126, "f16": -14, "bf16": -126}[dtype]
+    e = np.floor(np.log2(np.maximum(np.abs(a), 2.0 ** emin)))
+    return 2.0 ** (e - m)
+
+
+def elementwise_excess(got: np.ndarray, ref: np.ndarray, dtype: str, n_ulp: float = 4.0,
+                       floor_ulps: float = 1.0) -> float:
+    """Largest |got - ref| / (n_ulp * ulp(ref) + floor_ulps * ulp(max|ref|)) over the
+    elements: <= 1 means every element is within a few units of the storage type of the
+    oracle's value, plus a floor of one unit at the output's largest magnitude (an
+    intermediate value can round to the neighbouring storage value when the fp32 and fp64
+    sums straddle a rounding boundary, which moves an output by a fraction of that unit)."""
+    if ref.size == 0 or dtype not in ("f16", "bf16"):
+        # (fp32 storage: the normwise 1e-5 bar; the fp32 sums of the kernels and the fp64
+        # sums of the oracle differ by more than a few output units where terms cancel)
+        return 0.0
+    top = float(np.max(np.abs(ref)))
+    tol = n_ulp * ulp(ref, dtype) + floor_ulps * (ulp(np.array(top), dtype) if top > 0 else 0.0)
+    return float(np.max(np.abs(got - ref) / np.maximum(tol, 1e-300)))
+
+
 def oracle_kwargs(wl, inp) -> dict:
     kw = dict(stride=(wl.stride, wl.stride), pad=(wl.pad, wl.pad), scale1=inp["scale1"],
               bias1=inp["bias1"], act1=wl.act1, scale2=inp["scale2"], bias2=inp["bias2"],

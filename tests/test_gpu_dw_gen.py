@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import fcm_inputs
-from gpu_util import (TOL, all_variants_for, gpu_available, int_inputs, oracle_full, rel_err,
+from gpu_util import (TOL, all_variants_for, elementwise_excess, gpu_available, int_inputs,
+                      oracle_full, rel_err,
                       run_gpu)
 
 pytestmark = [pytest.mark.gpu,
@@ -99,3 +100,5 @@ def test_gen_random_small_shapes(wl):
         err = rel_err(got, ref)
         assert np.all(np.isfinite(got))
         assert err <= TOL[wl.dtype], (path, err)
+        ex = elementwise_excess(got, ref, wl.dtype)
+        assert ex <= 1.0, (path, "elementwise", ex)
