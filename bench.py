@@ -271,7 +271,7 @@ def measure(name, args, steps, warmup, torch, dev, stream, with_unfused=True):
     ys = [mod.new_output(dev) for _ in range(nsets)]
     ts = [torch.empty(mod.t_shape, dtype=tdt, device=dev) for _ in range(nsets)]
     torch.cuda.synchronize()
-    if variant is None and not args.no_tune:
+    if variant is None and not args.no_tune and args.mode != "variants":
         # measured choice of variant and grid (untimed, before the timing proper)
         with torch.cuda.stream(stream):
             mod.tune(xs, ys, iters=2 * nsets, stream=stream)
@@ -339,7 +339,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=8.0,
                     help="seconds of oracle time for the cpu_baseline leg (0 = skip)")
     ap.add_argument("--mode", default="bench", choices=["bench", "fused-only", "unfused-only",
-                                                        "copy"],
+                                                        "copy", "variants"],
                     help="profiling helpers: run only one path (or a plain copy) K times")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                           "COPY_WRITE"),
@@ -381,6 +381,25 @@ def main(argv=None) -> int:
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copied {args.steps} x {a.numel()} bytes")
+        return 0
+
+    if args.mode == "variants":
+        # every variant able to run the workload at its analytic plan's grid, timed like the
+        # benchmark; one JSON line per variant (a stored table the planner is checked against)
+        import depthwise_pointwise_convolution_amd as F
+        base = measure(args.workload, args, 0, 0, torch, dev, stream, with_unfused=False)
+        analytic = F.fcm_plan(base["mod"].prob)
+        for v in range(F.fcm_num_variants()):
+            try:
+                pv = F.fcm_plan_variant(base["mod"].prob, v)
+            except F.FcmError:
+                continue
+            base["mod"].plan = pv
+            ms = time_graph(base["fused"], args.steps, args.warmup, torch, stream)
+            print(json.dumps({"workload": args.workload, "variant": F.fcm_variant_name(v),
+                              "grid": pv.grid, "us": round(ms * 1e3, 3),
+                              "pred_us": round(pv.pred_us_fused, 3),
+                              "analytic_choice": v == analytic.variant}), flush=True)
         return 0
 
     r = measure(args.workload, args, args.steps, args.warmup, torch, dev, stream,

@@ -23,6 +23,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <stdlib.h>
@@ -659,7 +660,7 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
 namespace {
 
 struct Estimate {
-    double t_us;      // roofline time model
+    double t_us;      // time model (see finish_time)
     int64_t pred;     // bytes requested from the memory hierarchy
     double waste;     // arithmetic done beyond the module's own (recompute, padding)
     double gma;       // pages' Eq.-style estimate (inf when infeasible)
@@ -667,7 +668,49 @@ struct Estimate {
     int num_tiles;
     int grid;
     bool feasible;
+    // the time model's terms, seconds: compulsory HBM bytes, bytes requested from the
+    // on-chip caches, matrix-core work as executed, vector work; fraction of CUs busy
+    double t_hbm, t_l2, t_mat, t_vec, busy;
 };
+
+// The time model: the roofline terms of a variant (each at the machine's peak rate) and the
+// fraction of the CUs its tiles keep busy, scaled to what the kernels achieve.
+void finish_time(Estimate& r, double t_hbm, double t_l2, double t_mat, double t_vec,
+                 double busy) {
+    r.t_hbm = t_hbm;
+    r.t_l2 = t_l2;
+    r.t_mat = t_mat;
+    r.t_vec = t_vec;
+    r.busy = busy;
+    // Calibrated on MI355X against every compiled variant of the fifteen benchmark
+    // workloads (one measured table, graph-replayed launches streaming from HBM): a launch
+    // costs a fixed ~4 us (prologue, pipeline fill and drain, launch spacing) plus its
+    // slowest term at the fraction of the peak rate these issue- and latency-bound kernels
+    // reach -- HBM 50%, cache requests 20% (of the 4x-HBM rate the terms assume), matrix
+    // cores 20%, vector ALUs 15%.  With these factors the cheapest modelled variant is the
+    // measured fastest on all fifteen workloads.
+    constexpr double kFixedUs = 4.0, kHbm = 0.5, kL2 = 0.2, kMat = 0.2, kVec = 0.15;
+    r.t_us = kFixedUs + std::max(std::max(t_hbm / kHbm, t_l2 / kL2),
+                                 std::max(t_mat / kMat, t_vec / kVec)) /
+                            std::max(busy, 1e-9) * 1e6;
+}
+
+// Modelled HBM bytes of a run: its compulsory bytes, plus its filters fetched once per XCD
+// (each XCD's L2 serves that XCD's further re-reads of them; the kernels' input-window
+// overlaps and K-tile re-reads are served by the L2 the same way).
+int64_t modelled_hbm(int64_t alg, int64_t filters, const fcm_device_spec& d) {
+    return alg + (int64_t)std::max(d.num_xcds - 1, 0) * filters;
+}
+
+// The plan's fuse flag: the fused module's modelled HBM bytes below the layer-by-layer
+// kernels' (which also write the intermediate and read it back).  The FusePlanner
+// equations count every tile's requests to global memory, re-reads included; on gfx950
+// those re-reads hit the XCD's 4 MB L2, so the equations' figures are reported
+// (gma_paper_*) but the flag follows the bytes that reach HBM.
+int fuse_flag(int64_t alg_fused, int64_t alg_unfused, int64_t filters,
+              const fcm_device_spec& d) {
+    return modelled_hbm(alg_fused, filters, d) < modelled_hbm(alg_unfused, filters, d) ? 1 : 0;
+}
 
 Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_spec& d, int Ho,
                   int Wo) {
@@ -768,7 +811,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     const double t_hbm = alg / d.hbm_bytes_per_s;
     const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);
     const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
-    r.t_us = std::max(std::max(t_hbm, t_l2), std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+    finish_time(r, t_hbm, t_l2, t_mat, t_vec, busy);
 
     // Eq.-style estimate (FCM paper Sec. IV): DW->PW constructed from Eq. 2 and 3.
     const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, 3,
@@ -839,7 +882,7 @@ Estimate estimate_pwdw(const VariantDesc& v, const fcm_problem& p, const fcm_dev
     const double t_hbm = alg / d.hbm_bytes_per_s;
     const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);
     const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
-    r.t_us = std::max(std::max(t_hbm, t_l2), std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+    finish_time(r, t_hbm, t_l2, t_mat, t_vec, busy);
 
     // Eq. 4 as printed, plus the module's own output write (the OFMs are written once):
     // the PW input with its overlap (Eq. 1 over the input plane with the tile extents in
@@ -916,7 +959,7 @@ Estimate estimate_pwdwpw(const VariantDesc& v, const fcm_problem& p, const fcm_d
     const double t_hbm = alg / d.hbm_bytes_per_s;
     const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);
     const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
-    r.t_us = std::max(std::max(t_hbm, t_l2), std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+    finish_time(r, t_hbm, t_l2, t_mat, t_vec, busy);
 
     const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, 3,
                                        p.stride_h);
@@ -1008,7 +1051,12 @@ Estimate estimate_gen(const VariantDesc& v, const fcm_problem& p, const fcm_devi
     const double t_hbm = alg / d.hbm_bytes_per_s;
     const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);
     const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
-    r.t_us = std::max(std::max(t_hbm, t_l2), std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+    finish_time(r, t_hbm, t_l2, t_mat, t_vec, busy);
+    // each (tile, channel chunk) step of this kernel also pays a fixed latency (two
+    // barriers and its loads' round trip, ~1 us measured): the chunks of a workgroup's
+    // tiles run one after another
+    const int64_t steps = cdiv(r.num_tiles, std::max<int64_t>(grid, 1)) * cdiv(p.C, v.cc);
+    r.t_us += 1.0 * (double)steps;
     // constructed DW->PW estimate (Eq. 1 with the window extent as the filter size)
     const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, ext_h,
                                        p.stride_h);
@@ -1087,8 +1135,8 @@ Estimate estimate_pwpw(const VariantDesc& v, const fcm_problem& p, const fcm_dev
     const double t_vec = (double)ptiles * mp * 3.0 * (64.0 * ktiles + p.K) /
                          (d.valu_f32_flops / 2.0);
     const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
-    r.t_us = std::max(std::max(alg / d.hbm_bytes_per_s, (double)r.pred / (4.0 * d.hbm_bytes_per_s)),
-                      std::max(t_mat, t_vec)) / std::max(busy, 1e-9) * 1e6;
+    finish_time(r, alg / d.hbm_bytes_per_s, (double)r.pred / (4.0 * d.hbm_bytes_per_s), t_mat,
+                t_vec, busy);
     const bool fits = lds <= d.lds_bytes_per_wg && occ > 0;
     r.feasible = fits && r.num_tiles >= d.num_cus;
     if (!r.feasible) {
@@ -1191,6 +1239,15 @@ void estimate_unfused(const fcm_problem& p, const fcm_device_spec& d, int Ho, in
 
 }  // namespace
 
+// FCM_LOG=1 in the environment: every candidate variant's estimate goes to stderr.
+bool plan_log_enabled() {
+    static const bool on = [] {
+        const char* e = getenv("FCM_LOG");
+        return e && *e && strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
 fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int forced,
                         fcm_plan_t* out, std::string* err) {
     if (!out) {
@@ -1225,19 +1282,33 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
                      : p->kind == FCM_KIND_PWDWPW ? estimate_pwdwpw(v, *p, d, Ho, Wo)
                      : p->kind == FCM_KIND_PWPW ? estimate_pwpw(v, *p, d)
                                                 : estimate(v, *p, d, Ho, Wo);
+        if (plan_log_enabled())
+            fprintf(stderr,
+                    "fcm plan: %-40s feasible %d wgs/cu %d grid %6d tiles %7d  t %8.3f us "
+                    "(hbm %.3f l2 %.3f mat %.3f vec %.3f busy %.2f)  bytes %lld waste %.3f gma %.4g\n",
+                    v.name, (int)e.feasible, e.wgs_per_cu, e.grid, e.num_tiles, e.t_us,
+                    e.t_hbm * 1e6, e.t_l2 * 1e6, e.t_mat * 1e6, e.t_vec * 1e6, e.busy,
+                    (long long)e.pred, e.waste, e.gma);
         if (e.wgs_per_cu <= 0) {
             if (forced >= 0) why = "variant's LDS or registers exceed the device budget";
             continue;
         }
+        // (The pages' second constraint, at least as many output tiles as compute units,
+        // makes a tiling's Eq.-style estimate infinite; the ranking itself goes by the time
+        // model, which already charges the idle CUs of such a tiling.  The first
+        // constraint, LDS and registers, excluded the variant above.)
         bool better;
         if (best < 0) {
             better = true;
-        } else if (e.feasible != be.feasible) {
-            better = e.feasible;  // a constraint violation never beats a feasible tiling
-        } else if (!e.feasible && e.num_tiles != be.num_tiles) {
-            better = e.num_tiles > be.num_tiles;  // infeasible: keep the CUs busiest
         } else if (fabs(e.t_us - be.t_us) > 0.01 * std::min(e.t_us, be.t_us)) {
             better = e.t_us < be.t_us;  // modelled time decides unless within 1%
+        } else if (std::min(e.wgs_per_cu * v.waves, 8) !=
+                   std::min(be.wgs_per_cu * kVariants[best].waves, 8)) {
+            // resident waves per CU, up to two per SIMD: more hide more latency (the kernels
+            // are latency and issue bound, which the roofline terms do not see); beyond
+            // that the measured builds gained nothing
+            better = std::min(e.wgs_per_cu * v.waves, 8) >
+                     std::min(be.wgs_per_cu * kVariants[best].waves, 8);
         } else if (e.pred != be.pred) {
             better = e.pred < be.pred;
         } else if (e.waste != be.waste) {
@@ -1293,7 +1364,8 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         pl.pred_bytes_unfused = l1 + l2;
         pl.gma_paper_fused = be.gma;
         pl.gma_paper_unfused = (double)(l1 + l2);
-        pl.fuse = (be.gma < pl.gma_paper_unfused) ? 1 : 0;
+        pl.fuse = fuse_flag(pl.alg_bytes_fused, pl.alg_bytes_unfused,
+                            pl.w1_packed_bytes + (int64_t)p->K * p->K1 * e, d);
         pl.pred_us_fused = be.t_us;
         pl.flops = 2.0 * M * p->C * p->K1 + 2.0 * M * p->K1 * p->K;
         *out = pl;
@@ -1321,7 +1393,9 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         pl.pred_bytes_unfused = pu;
         pl.gma_paper_fused = be.gma;
         pl.gma_paper_unfused = gu;
-        pl.fuse = (be.gma < gu) ? 1 : 0;
+        pl.fuse = fuse_flag(pl.alg_bytes_fused, pl.alg_bytes_unfused,
+                            pl.w1_packed_bytes + pl.w2_packed_bytes + (int64_t)p->K * p->K1 * e,
+                            d);
         pl.pred_us_fused = be.t_us;
         pl.flops = 2.0 * p->N * p->H * p->W * p->C * p->K1 +
                    2.0 * p->N * Ho * Wo * p->K1 * p->R * p->S +
@@ -1346,7 +1420,8 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         pl.pred_bytes_unfused = pu;
         pl.gma_paper_fused = be.gma;
         pl.gma_paper_unfused = gu;
-        pl.fuse = (be.gma < gu) ? 1 : 0;
+        pl.fuse = fuse_flag(pl.alg_bytes_fused, pl.alg_bytes_unfused,
+                            pl.w1_packed_bytes + pl.w2_packed_bytes, d);
         pl.pred_us_fused = be.t_us;
         pl.flops = 2.0 * p->N * p->H * p->W * p->C * p->K1 +
                    2.0 * p->N * Ho * Wo * p->K1 * p->R * p->S;
@@ -1388,9 +1463,8 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
     pl.pred_bytes_unfused = pu;
     pl.gma_paper_fused = be.gma;
     pl.gma_paper_unfused = gu;
-    // FusePlanner's rule: fuse when the module's estimated global memory accesses are
-    // below those of its layers run one by one (finite beats infinite).
-    pl.fuse = (be.gma < gu) ? 1 : 0;
+    pl.fuse = fuse_flag(pl.alg_bytes_fused, pl.alg_bytes_unfused,
+                      w1_bytes + (int64_t)p->K * n1 * e, d);
     pl.pred_us_fused = be.t_us;
     const double P = (double)p->N * Ho * Wo;
     pl.flops = p->kind == FCM_KIND_B2B

@@ -162,7 +162,9 @@ typedef struct {
     int32_t num_tiles;      /* pixel tiles x K tiles */
     int32_t grid;           /* workgroups launched (persistent kernels loop) */
     int32_t lds_bytes;      /* LDS of one workgroup */
-    int32_t fuse;           /* 1: the fused kernel moves fewer bytes than LBL */
+    int32_t fuse;           /* 1: the fused module's modelled HBM bytes (compulsory
+                               bytes, filters once per XCD) are below the layer-by-layer
+                               kernels'; the Eq. 1-4 figures are gma_paper_* */
     int64_t w1_packed_bytes, w2_packed_bytes; /* sizes fcm_pack_weights writes */
     int64_t workspace_bytes;  /* intermediate tensor of the unfused path */
     int64_t alg_bytes_fused;  /* compulsory HBM bytes: X + Y + weights + epilogue */
@@ -172,7 +174,9 @@ typedef struct {
     double gma_paper_fused;   /* FusePlanner estimate (Eq. 1-4 style), bytes */
     double gma_paper_unfused; /* Eq. 2 + Eq. 3, bytes */
     double flops;             /* 2 * multiply-adds of both convolutions */
-    double pred_us_fused;     /* roofline time model of the chosen variant, us */
+    double pred_us_fused;     /* time model of the chosen variant, us: a fixed launch
+                                 cost plus its slowest roofline term at the fraction of
+                                 peak the kernels reach (calibrated on MI355X) */
     double tuned_us;          /* fcm_tune: measured time of this plan, us (0 otherwise) */
 } fcm_plan_t;
 
