@@ -18,8 +18,8 @@
 // When the whole pointwise weight slice fits in registers (C <= CC) it is loaded
 // once per workgroup and kept there for every tile (local weight stationary).
 //
-// The fp32 variant (no fp32 16x16x32 matrix instruction) does the pointwise stage
-// on the VALU from the same LDS intermediate.
+// The fp32 variant contracts the same kind of LDS intermediate (in fp32) with the
+// fp32 matrix instruction, four reduction channels per instruction.
 #include "stages.h"
 
 namespace fcm {
@@ -176,29 +176,38 @@ void dwpw_mfma_kernel(KArgs a) {
     }
 }
 
-// fp32 storage: depthwise stage as above (4 channels per 16-byte vector), pointwise
-// contraction on the VALU from the LDS intermediate.  Thread t owns output channel
-// k0 + t % KT for P*KT/256 pixels of the tile.
+// fp32 storage: depthwise stage as above (4 channels per 16-byte vector) into an fp32
+// LDS intermediate, pointwise contraction on the matrix cores with the fp32 instruction
+// v_mfma_f32_16x16x4_f32 (the FP32 FCMs of the FCM paper, Sec. III-B).  Wave w owns the
+// 16-pixel blocks w, w + 4, ... of the tile and all KT output channels of the slice.
+// One 16-byte LDS read per lane supplies the pixel operand of four consecutive
+// instructions: for a slab of 16 channels, instruction j takes channel 4 * g + j from
+// lane group g = l / 16 (and the same channel of the weight operand), so the four
+// instructions together reduce over the slab's 16 channels.
 template <int S, int TH, int TW, int KT, int CC>
 __global__ __launch_bounds__(256) void dwpw_f32_kernel(KArgs a) {
     typedef float T;
     constexpr int NT = 256;
     constexpr int VN = 4;
     constexpr int P = TH * TW;
+    static_assert(P % 64 == 0, "tile must give each wave whole 16-pixel blocks");
+    constexpr int MBW = P / 64;  // 16-pixel blocks per wave
     constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3;
-    constexpr int XS = CC + 4, TS = CC + 1;
-    static_assert(NT % KT == 0 && (P * KT) % NT == 0, "tile sizes");
-    constexpr int PG = NT / KT;           // pixel groups
-    constexpr int PPT = P * KT / NT;      // pixels per thread
+    // row stride of the intermediate: 36 floats = 4 mod 64 banks times an odd factor,
+    // so the 16 rows x 4 lane groups of an operand read hit 64 distinct banks
+    constexpr int XS = CC + 4, TS = CC + 4;
+    static_assert(KT % 16 == 0 && CC % 16 == 0, "tile sizes");
+    constexpr int KB = KT / 16, NSL = CC / 16;
     constexpr int VB = DwBlocking<TH, TW, CC / VN, NT>::VB;
 
     __shared__ __attribute__((aligned(16))) T xs[IH * IW * XS];
-    __shared__ float ts[P * TS];
+    __shared__ __attribute__((aligned(16))) float ts[P * TS];
     __shared__ __attribute__((aligned(16))) float wdw_s[9 * CC];
     __shared__ float s1s[CC], b1s[CC];
+    __shared__ float s2s[KT], b2s[KT];
 
-    const int tid = threadIdx.x;
-
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
     const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int G = gridDim.x;
     const int L = xcd_logical_id(blockIdx.x, G);
@@ -208,10 +217,11 @@ __global__ __launch_bounds__(256) void dwpw_f32_kernel(KArgs a) {
     const T* __restrict__ wdw = (const T*)a.w1;
     const T* __restrict__ wpw = (const T*)a.w2;
     T* __restrict__ y = (T*)a.y;
-    const int kl = tid % KT, pg = tid / KT;
-    const int k = k0 + kl;
-    const float sc2 = (a.s2 && k < a.K) ? a.s2[k] : 1.0f;
-    const float bi2 = (a.b2 && k < a.K) ? a.b2[k] : 0.0f;
+    for (int i = tid; i < KT; i += NT) {
+        const int k = k0 + i;
+        s2s[i] = (a.s2 && k < a.K) ? a.s2[k] : 1.0f;
+        b2s[i] = (a.b2 && k < a.K) ? a.b2[k] : 0.0f;
+    }
 
     const int per_img = a.tiles_h * a.tiles_w;
     for (int pt = L / a.num_ktiles; pt < a.num_ptiles; pt += pstep) {
@@ -219,39 +229,68 @@ __global__ __launch_bounds__(256) void dwpw_f32_kernel(KArgs a) {
         const int rem = pt - n * per_img;
         const int th = rem / a.tiles_w, tw = rem - th * a.tiles_w;
         const int oh0 = th * TH, ow0 = tw * TW;
-        float acc[PPT];
+        f32x4 acc[MBW][KB];
 #pragma unroll
-        for (int i = 0; i < PPT; ++i) acc[i] = 0.0f;
+        for (int mi = 0; mi < MBW; ++mi)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) acc[mi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int c0 = 0; c0 < a.C; c0 += CC) {
             __syncthreads();  // previous chunk's readers of xs / ts are done
             stage_input<T, IH, IW, CC, XS, NT>(xs, x, a, n, oh0 * S - a.pad_h,
                                                ow0 * S - a.pad_w, c0, tid);
             stage_dw_weights<T, CC, NT>(wdw_s, s1s, b1s, wdw, a, c0, tid);
+            // this chunk's weight operands: row kperm(kb, lr) of the slice, channels
+            // c0 + 16 * sl + 4 * lg .. + 3 (zeros beyond K or C)
+            u32x4 wa[NSL][KB];
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int ko = k0 + kperm<KT>(kb, lr), c = c0 + sl * 16 + lg * 4;
+                    wa[sl][kb] = (ko < a.K && c < a.C) ? ld16(wpw + (int64_t)ko * a.C + c)
+                                                       : u32x4{0u, 0u, 0u, 0u};
+                }
             __syncthreads();
             dw_stage<T, S, TH, TW, CC, XS, IW, VB, NT>(
                 xs, wdw_s, s1s, b1s, act1, tid, [&](int ohl, int col, int cg, u32x4 v) {
-                    float f[4];
-                    unpack16<float>(v, f);
-                    float* d = ts + (ohl * TW + col) * TS + cg * VN;
-                    d[0] = f[0]; d[1] = f[1]; d[2] = f[2]; d[3] = f[3];
+                    st16(ts + (ohl * TW + col) * TS + cg * VN, v);
                 });
             __syncthreads();
-            const int cn = (a.C - c0) < CC ? (a.C - c0) : CC;
-            for (int c = 0; c < cn; ++c) {
-                const float wv = k < a.K ? wpw[(int64_t)k * a.C + c0 + c] : 0.0f;
 #pragma unroll
-                for (int i = 0; i < PPT; ++i)
-                    acc[i] = __builtin_fmaf(ts[(pg + i * PG) * TS + c], wv, acc[i]);
+            for (int mi = 0; mi < MBW; ++mi) {
+                const int row = (wave + 4 * mi) * 16 + lr;
+#pragma unroll
+                for (int sl = 0; sl < NSL; ++sl) {
+                    const f32x4 bv = __builtin_bit_cast(f32x4, ld16(ts + row * TS + sl * 16 + lg * 4));
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const f32x4 av = __builtin_bit_cast(f32x4, wa[sl][kb]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[mi][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                av[j], bv[j], acc[mi][kb], 0, 0, 0);
+                    }
+                }
             }
         }
-        if (k < a.K) {
+        // lane (lr, lg) holds channels lg * KT/4 + 4 * kb + i of pixel row lr
 #pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                const int px = pg + i * PG;
-                const int oh = oh0 + px / TW, ow = ow0 + px % TW;
-                if (oh < a.Ho && ow < a.Wo)
-                    y[(((int64_t)n * a.Ho + oh) * a.Wo + ow) * a.K + k] =
-                        epilogue(acc[i], sc2, bi2, act2);
+        for (int mi = 0; mi < MBW; ++mi) {
+            const int px = (wave + 4 * mi) * 16 + lr;
+            const int oh = oh0 + px / TW, ow = ow0 + px % TW;
+            if (oh < a.Ho && ow < a.Wo) {
+                T* yp = y + (((int64_t)n * a.Ho + oh) * a.Wo + ow) * a.K + k0;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int kl = lg * (KT / 4) + kb * 4;
+                    if (k0 + kl < a.K) {
+                        f32x4 o;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            o[i] = epilogue(acc[mi][kb][i], s2s[kl + i], b2s[kl + i], act2);
+                        st16(yp + kl, __builtin_bit_cast(u32x4, o));
+                    }
+                }
             }
         }
     }

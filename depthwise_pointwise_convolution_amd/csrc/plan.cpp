@@ -169,7 +169,8 @@ int variant_lds_bytes(const VariantDesc& v) {
         return IH * IW * (v.cc + 8) * e + P * (v.cc + 8) * e + 9 * v.cc * 4 + 2 * v.cc * 4 +
                2 * v.kt * 4;
     case VK_DWPW32:
-        return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 1) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4;
+        return IH * IW * (v.cc + 4) * 4 + P * (v.cc + 4) * 4 + 9 * v.cc * 4 + 2 * v.cc * 4 +
+               2 * v.kt * 4;
     case VK_DWPW_MM:
     case VK_B2B_MM: {
         // input tile (or chunk) buffers and as many intermediate tiles (one direct-load
@@ -261,7 +262,9 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         return 40 + MBW * KB * 4 + (v.wres ? KS * KB * 4 : 12) + vb * 8 + 24;
     }
     case VK_DWPW32:
-        return 64 + P * v.kt / 256 + 24;
+        // accumulators of the wave's pixel blocks, the chunk's weight operands, the
+        // depthwise work item, staging and addressing
+        return 40 + MBW * (v.kt / 16) * 4 + (v.cc / 16) * (v.kt / 16) * 4 + 24 + 24;
     case VK_DWPW_MM: {
         // per wave: pointwise operands of its KT/4 output channels and their epilogue
         // constants, its depthwise operands and epilogue-1 constants, the direct-load
@@ -805,8 +808,9 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
         t_vec = P * pad_px * (epi_ops + (v.cc > 64 ? 1.25 * v.cc * ktiles : 0.0)) /
                 lane_ops_per_s;
     } else {
-        t_mat = 0.0;
-        t_vec = P * pad_px * (9.0 * p.C * ktiles + (double)p.C * p.K + epi_ops) / lane_ops_per_s;
+        // fp32: pointwise products on the fp32 matrix instruction, depthwise on the VALU
+        t_mat = 2.0 * P * pad_px * (double)p.C * p.K / d.mfma_f32_flops;
+        t_vec = P * pad_px * (9.0 * p.C * ktiles + epi_ops) / lane_ops_per_s;
     }
     const double t_hbm = alg / d.hbm_bytes_per_s;
     const double t_l2 = (double)r.pred / (4.0 * d.hbm_bytes_per_s);

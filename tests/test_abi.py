@@ -69,6 +69,24 @@ def test_library_has_no_undefined_own_symbols():
     assert F.fcm_num_variants() > 0
 
 
+def test_fp32_pointwise_stage_runs_on_the_matrix_cores():
+    # the fp32 kernel's pointwise products are fp32 matrix instructions: every compiled
+    # instance holds v_mfma_f32_16x16x4_f32 (from the gfx950 assembly build.py keeps)
+    import re
+    asm_path = os.path.join(ROOT, "depthwise_pointwise_convolution_amd", "_build",
+                            "kernels_dwpw.hip.s")
+    if not os.path.exists(asm_path):
+        pytest.skip("library assembly not built here")
+    asm = open(asm_path).read()
+    bodies = []
+    for m in re.finditer(r"^(_ZN3fcm15dwpw_f32_kernel\S*):", asm, re.M):
+        end = asm.find(".Lfunc_end", m.end())
+        bodies.append(asm[m.end():end])
+    assert len(bodies) == 2
+    for b in bodies:
+        assert len(re.findall(r"\bv_mfma_f32_16x16x4_?f32\b", b)) >= 16
+
+
 def _problem(F, wl):
     return F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
                      None if wl.kind == "dwpw" else wl.K1, R=wl.R, S=wl.S, stride=wl.stride,
