@@ -29,6 +29,7 @@ SOURCES = [
     ("kernels/dwpw_mm.hip", True),
     ("kernels/dwpw_mmw.hip", True),
     ("kernels/dwpw_ws.hip", True),
+    ("kernels/dwpw_wsl.hip", True),
     ("kernels/b2b_mm.hip", True),
     ("kernels/pwdw_mm.hip", True),
     ("kernels/pwdwpw_mm.hip", True),

@@ -54,6 +54,8 @@ const VariantImpl kImpls[] = {
      occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>},
 #define FCM_V_DWPW_WS(name, dt, CTy, S, TH, TW, CT, KT, NW) \
     {launch_dwpw_ws<CTy, S, TH, TW, CT, KT, NW>, occ_dwpw_ws<CTy, S, TH, TW, CT, KT, NW>},
+#define FCM_V_DWPW_WSL(name, dt, CT, S, TH, TW, KT, CMAX, NW) \
+    {launch_dwpw_wsl<CT, S, TH, TW, KT, CMAX, NW>, occ_dwpw_wsl<CT, S, TH, TW, KT, CMAX, NW>},
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {launch_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>, occ_pwdw_mm<CT, S, TH, CMAX, NW, BPW, OCC>},
 #define FCM_V_PWDWPW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, KB, OCC)   \
@@ -75,6 +77,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_PWDW_MM
 #undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS
+#undef FCM_V_DWPW_WSL
 #undef FCM_V_DWPW_I8
 #undef FCM_V_PWPW_MM
 #undef FCM_V_DWPW_GEN

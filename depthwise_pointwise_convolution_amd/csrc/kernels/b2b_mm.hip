@@ -284,8 +284,8 @@ void b2b_mm_kernel(KArgs a) {
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = epilogue(d[r][i], s1r[i], b1r[i], act1);
-            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
-                                      ((r * NKS2 + (wave >> 1)) * 64) * 16 + tls_w) = pack8<T>(v);
+            st8(reinterpret_cast<char*>(dst) + ((r * NKS2 + (wave >> 1)) * 64) * 16 + tls_w,
+                pack8<T>(v));
         }
     };
     auto phase_b = [&](const u32x4* src, const Pos& t) {

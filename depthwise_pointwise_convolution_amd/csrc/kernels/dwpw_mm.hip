@@ -410,9 +410,9 @@ void dwpw_mm_kernel(KArgs a) {
                     o[i] = decltype(identity1)::value
                                ? d[r][i]
                                : epilogue(d[r][i], s1r[j][i], b1r[j][i], act1);
-                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
-                                          (((row0 + r) * NKS + (cb >> 1)) * 64) * 16 + tls_w) =
-                    pack8<T>(o);
+                st8(reinterpret_cast<char*>(dst) + (((row0 + r) * NKS + (cb >> 1)) * 64) * 16 +
+                        tls_w,
+                    pack8<T>(o));
             }
         }
         __builtin_amdgcn_sched_group_barrier(0x100, CBW * (IHW + NQ), 0);  // operand reads

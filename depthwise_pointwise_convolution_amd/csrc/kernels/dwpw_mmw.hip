@@ -260,9 +260,11 @@ void dwpw_mmw_kernel(KArgs a) {
     struct PwOps {
         u32x4 w[NKS][KBW];
     };
-    const u32x4* __restrict__ wpb =
-        reinterpret_cast<const u32x4*>(wpw + (int64_t)a.K * a.C);
+    // (buffer loads with a 32-bit offset: the destination registers are written by the
+    // load alone, so reusing them for the next step's operands waits for nothing)
     const int s32 = a.C / 32, g32 = (a.K + 31) / 32;
+    const __amdgpu_buffer_rsrc_t rw =
+        mm::rsrc(wpw + (int64_t)a.K * a.C, (uint32_t)(g32 * 32 * a.C * es));
     auto load_pw = [&](const Step& st, PwOps& o) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
@@ -270,7 +272,9 @@ void dwpw_mmw_kernel(KArgs a) {
             for (int kb = 0; kb < KBW; ++kb) {
                 const int g = min((kw0 >> 5) + (kb >> 1), g32 - 1);
                 const int blk = (g * s32 + 2 * st.c + ks) * 2 + (kb & 1);
-                o.w[ks][kb] = wpb[blk * 64 + lane];
+                o.w[ks][kb] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rw, (uint32_t)(blk * 64 + lane) * 16u, 0, 0));
             }
     };
     auto dw_operand = [&](uint32_t v) {
@@ -345,8 +349,8 @@ void dwpw_mmw_kernel(KArgs a) {
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = epilogue(d[j][i], in.s[i], in.b[i], act1);
-            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
-                                      ((mb * NKS + (cbw >> 1)) * 64) * 16 + tls_w) = pack8<T>(v);
+            mm::lds_st8(mm::lds_addr(dst) + ((mb * NKS + (cbw >> 1)) * 64) * 16 + tls_w,
+                        pack8<T>(v));
         }
     };
     auto phase_a = [&](const u32x4* src, u32x4* dst, int c) {
@@ -434,24 +438,29 @@ void dwpw_mmw_kernel(KArgs a) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS constants written
     __builtin_amdgcn_s_barrier();
     if (s0.t.n < a.N) phase_a(xs, tl0, s0.c);
+    mm::wait_vmcnt<R>();  // chunk 1 (chunk 2 stays in flight)
 
     // ---- pipelined steps ---------------------------------------------------------------
-    // step s (P = s % 2, xi = s % 3): wait for chunk s+1 and the operands loaded in
-    // step s-1 (only chunk s+2's loads and the previous step's stores, if it finished
-    // a tile, were issued after them); barrier; pointwise operands of step s+1; input
-    // chunk of step s+3 into xs[xi]; phase A of s+1 from xs[(xi+1)%3] into tl[1-P];
-    // phase B of s from tl[P]; if s ends its tile, epilogue 2 and stores.  One loop
-    // body (no unrolling by parity): the accumulators stay in the same registers, so
-    // every matrix instruction of a chain reads and writes its accumulator in place.
+    // step s (P = s % 2, xi = s % 3): barrier (chunk s+1 and the operands of step s were
+    // waited for at the end of step s-1: only chunk s+2's loads and step s-1's stores, if
+    // it finished a tile, were issued after them); pointwise operands of step s+1 into the
+    // other operand set; input chunk of step s+3 into xs[xi]; phase A of s+1 from
+    // xs[(xi+1)%3] into tl[1-P]; phase B of s from tl[P]; if s ends its tile, epilogue 2
+    // and stores.  The loop runs two steps per round, so the two operand sets and the
+    // two intermediate buffers are named at compile time and alternate without register
+    // copies (a copy of the operands just requested would wait for those loads); the
+    // accumulators stay in the same registers, so every matrix instruction of a chain
+    // reads and writes its accumulator in place.
     Step cur = s0, nx = s1, nn = s2;
-    int xi = 0, par = 0;
-    bool stored = false;
-    while (cur.t.n < a.N) {
-        if (stored) mm::wait_vmcnt<R + NST>(); else mm::wait_vmcnt<R>();
+    int xi = 0;
+    auto step = [&](auto parc, const PwOps& use, PwOps& fill) {
+        constexpr int par = decltype(parc)::value;
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own intermediate writes done
         __builtin_amdgcn_s_barrier();
         const Step n3 = next(nn);
-        if (nch > 1) load_pw(nx, pwo1);  // (one chunk: the operands never change)
+        // (every step issues the same loads, so the compiler's count of the loads in
+        // flight is the same on every path; with one chunk they repeat the same operands)
+        load_pw(nx, fill);
         const int xa = xi == 2 ? 0 : xi + 1;
         issue_chunk(n3, xs + xi * SLOTS_P);
         // phase A runs even for a step past the last tile (its chunk was zero-filled and
@@ -463,7 +472,7 @@ void dwpw_mmw_kernel(KArgs a) {
         if constexpr (EARLY_B) phase_b_load(par ? tl1 : tl0, bfr);
         phase_a(xs + xa * SLOTS_P, par ? tl0 : tl1, nx.c);
         if constexpr (!EARLY_B) phase_b_load(par ? tl1 : tl0, bfr);
-        phase_b(bfr, pwo0);
+        phase_b(bfr, use);
         if constexpr (EARLY_B) {
             __builtin_amdgcn_sched_group_barrier(0x100, NTP + 2 + NTP * PPW + MB * NKS, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, NTP * PPW, 0);
@@ -474,15 +483,33 @@ void dwpw_mmw_kernel(KArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x100, MB * NKS, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, MB * KBW * NKS, 0);
         }
-        stored = cur.c == nch - 1;
-        if (stored) finish(cur.t);
-        if (nch > 1) pwo0 = pwo1;
+        // the wait for the next step sits on the branch that issued (or skipped) the
+        // stores, so the compiler's own count of the loads in flight stays exact on
+        // every path
+        if (cur.c == nch - 1) {
+            finish(cur.t);
+            mm::wait_vmcnt<R + NST>();
+        } else {
+            mm::wait_vmcnt<R>();
+        }
         cur = nx;
         nx = nn;
         nn = n3;
         xi = xa;
-        par ^= 1;
+    };
+    // the workgroup's step count, known up front: a loop of step pairs and at most one
+    // more step, with no exit test between the two steps of a pair (an exit test there
+    // lets the compiler merge the two steps into one loop body entered either way, and
+    // its count of the loads in flight then has to cover paths that never run)
+    const int t_first = L / a.num_ktiles;
+    const int n_tiles = t_first < a.num_ptiles ? (a.num_ptiles - 1 - t_first) / pstep + 1 : 0;
+    const int n_steps = n_tiles * nch;
+    int si = 0;
+    for (; si + 2 <= n_steps; si += 2) {
+        step(std::integral_constant<int, 0>{}, pwo0, pwo1);
+        step(std::integral_constant<int, 1>{}, pwo1, pwo0);
     }
+    if (si < n_steps) step(std::integral_constant<int, 0>{}, pwo0, pwo1);
     // chunks of steps past the end may still be in flight into LDS
     mm::wait_vmcnt<0>();
 }

@@ -44,41 +44,6 @@ namespace fcm {
 namespace ws {
 // (The statements below are gfx950 assembly; the host compilation pass of this source
 // only needs the functions to exist.)
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-#if __HIP_DEVICE_COMPILE__
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-#else
-    (void)p;
-    return 0;
-#endif
-}
-// Ten 16-byte LDS reads issued back to back, waited for within the same statement.  The
-// compiler does not see these reads as LDS accesses, so it adds no wait for the direct
-// global->LDS loads in flight (which it cannot always tell apart from them); the
-// kernel's own waits and barriers order the reads after the loads of the window they
-// read.
-__device__ __forceinline__ void lds_read10(const uint32_t (&ad)[10], u32x4 (&o)[10]) {
-#if __HIP_DEVICE_COMPILE__
-    asm volatile(
-        "ds_read_b128 %0, %10\n\t"
-        "ds_read_b128 %1, %11\n\t"
-        "ds_read_b128 %2, %12\n\t"
-        "ds_read_b128 %3, %13\n\t"
-        "ds_read_b128 %4, %14\n\t"
-        "ds_read_b128 %5, %15\n\t"
-        "ds_read_b128 %6, %16\n\t"
-        "ds_read_b128 %7, %17\n\t"
-        "ds_read_b128 %8, %18\n\t"
-        "ds_read_b128 %9, %19\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
-          "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
-          "v"(ad[7]), "v"(ad[8]), "v"(ad[9])
-        : "memory");
-#endif
-}
 // Four 16-byte LDS reads at base + 1024 i, likewise.
 __device__ __forceinline__ void lds_read4k(uint32_t base, u32x4 (&o)[4]) {
 #if __HIP_DEVICE_COMPILE__
@@ -273,7 +238,7 @@ void dwpw_ws_kernel(KArgs a) {
         // the depthwise layer of one block: window buffer src -> intermediate buffer dst,
         // two channel blocks (two independent product chains) at a time
         auto dw_step = [&](const u32x4* src, u32x4* dst) {
-            const uint32_t xb = ws::lds_addr(src), tb = ws::lds_addr(dst);
+            const uint32_t xb = mm::lds_addr(src), tb = mm::lds_addr(dst);
 #pragma unroll
             for (int j0 = 0; j0 < CBW; j0 += 2) {
                 uint32_t ad[10];
@@ -285,7 +250,7 @@ void dwpw_ws_kernel(KArgs a) {
                         ad[j * NTP + tp] = xb + xoff[tp] + ((q ^ xsw[tp]) << 4);
                 }
                 u32x4 xr[10];
-                ws::lds_read10(ad, xr);
+                mm::lds_read10(ad, xr);
                 f32x4 d[2];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) d[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -416,7 +381,7 @@ void dwpw_ws_kernel(KArgs a) {
         // pixels past the output and 8-channel runs past K get the out-of-range offset,
         // whose stores are dropped)
         auto pw_step = [&](const u32x4* src, int b) {
-            const uint32_t tb = ws::lds_addr(src) + lane * 16u;
+            const uint32_t tb = mm::lds_addr(src) + lane * 16u;
             u32x4 bv[NKS];
 #pragma unroll
             for (int k4 = 0; k4 < NKS; k4 += 4) {

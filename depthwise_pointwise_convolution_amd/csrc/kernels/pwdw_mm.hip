@@ -46,8 +46,6 @@
 
 namespace fcm {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void pwdw_mm_kernel(KArgs a) {
@@ -334,7 +332,7 @@ void pwdw_mm_kernel(KArgs a) {
                 for (int i = 0; i < 4; ++i)
                     o[i] = __builtin_amdgcn_fmed3f(__builtin_fmaf(acc[i], s1r[j][i], b1r[j][i]),
                                                    lo, hi);
-                *reinterpret_cast<uint2*>(tbase + j * TREG + two[pb]) = pack8<T>(o);
+                st8(tbase + j * TREG + two[pb], pack8<T>(o));
             }
             __builtin_amdgcn_sched_barrier(0);
         }

@@ -44,15 +44,6 @@
 
 namespace fcm {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// An 8-byte LDS store as one vector value (a store of the two-field struct is split and
-// re-merged by the compiler, which then no longer knows which LDS array it writes and
-// waits for the direct loads in flight before it).
-__device__ __forceinline__ void st8(char* p, uint2 v) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{v.x, v.y};
-}
-
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int KB, int OCC>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void pwdwpw_mm_kernel(KArgs a) {

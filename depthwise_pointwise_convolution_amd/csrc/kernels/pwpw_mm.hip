@@ -201,8 +201,8 @@ void pwpw_mm_kernel(KArgs a) {
             float o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = epilogue(d[pb][i], s1r[i], b1r[i], act1);
-            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(dst) +
-                                      ((pb * NKS + (wave >> 1)) * 64) * 16 + tls_w) = pack8<T>(o);
+            st8(reinterpret_cast<char*>(dst) + ((pb * NKS + (wave >> 1)) * 64) * 16 + tls_w,
+                pack8<T>(o));
         }
     };
     auto phase_b = [&](const u32x4* src, int t) __attribute__((always_inline)) {

@@ -32,6 +32,11 @@ int launch_dwpw_ws(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int TW, int CT, int KT, int NW>
 int occ_dwpw_ws();
 
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW>
+int launch_dwpw_wsl(const KArgs& a, int grid, void* stream);
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW>
+int occ_dwpw_wsl();
+
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>
 int launch_pwdw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int OCC>

@@ -52,6 +52,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0},
 #define FCM_V_DWPW_WS(name, dt, CTy, S, TH, TW, CT, KT, NW) \
     {#name, VK_DWPW_WS, dt, S, TH, TW, KT, CT, 1, 2, 0, NW / 4, NW, CT, 0},
+#define FCM_V_DWPW_WSL(name, dt, CT, S, TH, TW, KT, CMAX, NW) \
+    {#name, VK_DWPW_WSL, dt, S, TH, TW, KT, 64, 0, 4, 0, NW / 4, NW, CMAX, 0},
 #define FCM_V_PWDW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, OCC) \
     {#name, VK_PWDW_MM, dt, S, TH, 16, NW * BPW * 16, CMAX, 1, 2, 0, OCC, NW, CMAX, BPW},
 #define FCM_V_PWDWPW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, KB, OCC) \
@@ -72,6 +74,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_PWDW_MM
 #undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS
+#undef FCM_V_DWPW_WSL
 #undef FCM_V_DWPW_I8
 #undef FCM_V_PWPW_MM
 #undef FCM_V_DWPW_GEN
@@ -191,6 +194,17 @@ int variant_lds_bytes(const VariantDesc& v) {
         return v.nbuf * slots_p * 16 + 2 * mb * (v.cc / 32) * 64 * 16 + 2 * v.kt * 4 +
                v.cmax * (9 * 2 + 2 * 4);
     }
+    case VK_DWPW_WSL: {
+        // four input windows (whole load rounds of the depthwise waves), two
+        // intermediate slices of 16-pixel blocks, epilogue-2 constants of the K tile,
+        // depthwise filters and epilogue-1 constants of every channel
+        const int nt = 32 * v.waves;
+        const int slots = IH * IW * (v.cc / 8);
+        const int slots_p = (slots + nt - 1) / nt * nt;
+        const int mb = (P + 15) / 16;
+        return v.nbuf * slots_p * 16 + 2 * mb * (v.cc / 32) * 64 * 16 + 2 * v.kt * 4 +
+               v.cmax * (9 * 2 + 2 * 4);
+    }
     case VK_DWPW_WS: {
         // three input windows (whole direct-load rounds of the depthwise half of the
         // waves, plus one wave's landing slots for the partial round) and three
@@ -290,6 +304,20 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         const int ppw = mb * 4 / v.waves;
         const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
         return 4 * mb * kbw + 16 * kbw + 28 + 5 * ppw + 2 * ((slots + nt - 1) / nt) + 36 + 24;
+    }
+    case VK_DWPW_WSL: {
+        // the larger of the two roles: a pointwise wave holds its KT/4 output channels'
+        // accumulators for every pixel block, two sets of one step's filters and the step's
+        // intermediate operands; a depthwise wave every pixel block's window operands, the
+        // diagonal operand, accumulators, read offsets and the direct-load plan
+        const int half = v.waves / 2;
+        const int mb = (P + 15) / 16, kbw = v.kt / (16 * half), nks = v.cc / 32;
+        const int mbw = mb * 4 / half;
+        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
+        const int r = (slots + 64 * half - 1) / (64 * half);
+        const int pw_regs = 4 * mb * kbw + 2 * 4 * nks * kbw + 4 * mb * nks + 24;
+        const int dw_regs = 20 * mbw + 4 + 4 * mbw + 5 * mbw + 3 * r + 8 + 30;
+        return std::max(pw_regs, dw_regs) + 16;
     }
     case VK_DWPW_WS: {
         // the larger of the two roles: a pointwise wave holds its output channels'
@@ -604,7 +632,8 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         return true;
     }
     const int want = p.kind == FCM_KIND_B2B ? VK_B2B : (p.dtype == FCM_F32 ? VK_DWPW32 : VK_DWPW);
-    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMW || v.vkind == VK_DWPW_WS)
+    const int kind = (v.vkind == VK_DWPW_MM || v.vkind == VK_DWPW_MMW || v.vkind == VK_DWPW_WS ||
+                      v.vkind == VK_DWPW_WSL)
                          ? VK_DWPW
                      : v.vkind == VK_B2B_MM                           ? VK_B2B
                                                                       : v.vkind;
@@ -630,7 +659,7 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         return false;
     }
     if (v.vkind == VK_DWPW_MM || v.vkind == VK_B2B_MM || v.vkind == VK_DWPW_MMW ||
-        v.vkind == VK_DWPW_WS) {
+        v.vkind == VK_DWPW_WS || v.vkind == VK_DWPW_WSL) {
         if (v.vkind == VK_DWPW_MM && p.C > v.cc) {
             if (why) *why = "matrix-core depthwise variant needs C <= its channel chunk";
             return false;
@@ -640,7 +669,7 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
                             "of depthwise filters in LDS";
             return false;
         }
-        if (v.vkind == VK_DWPW_MMW && p.C % 64 != 0) {
+        if ((v.vkind == VK_DWPW_MMW || v.vkind == VK_DWPW_WSL) && p.C % 64 != 0) {
             if (why) *why = "chunked matrix-core variant needs C a multiple of 64";
             return false;
         }
@@ -729,7 +758,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     int occ = std::min(std::min(occ_lds, occ_vgpr), d.max_waves_per_simd / wps);
     // the workgroups per CU the kernel's register allocation was tuned for
     if (v.vkind == VK_DWPW_MM || v.vkind == VK_B2B_MM || v.vkind == VK_DWPW_MMW ||
-        v.vkind == VK_DWPW_WS)
+        v.vkind == VK_DWPW_WS || v.vkind == VK_DWPW_WSL)
         occ = std::min(occ, std::max(v.occ / wps, 1));
     if (lds > d.lds_bytes_per_wg) occ = 0;
     r.wgs_per_cu = occ;
@@ -786,7 +815,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     } else if (v.vkind == VK_DWPW) {
         t_mat = 2.0 * P * pad_px * (double)p.C * p.K / d.mfma_f16_flops;
         t_vec = P * pad_px * (9.0 * p.C * ktiles + epi_ops) / lane_ops_per_s;
-    } else if (v.vkind == VK_DWPW_MMW) {
+    } else if (v.vkind == VK_DWPW_MMW || v.vkind == VK_DWPW_WSL) {
         // block-diagonal depthwise products (320 flop-equivalents per channel and
         // pixel) recomputed for every K tile
         t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * p.C * ktiles) / d.mfma_f16_flops;
@@ -1301,11 +1330,17 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         // makes a tiling's Eq.-style estimate infinite; the ranking itself goes by the time
         // model, which already charges the idle CUs of such a tiling.  The first
         // constraint, LDS and registers, excluded the variant above.)
+        auto specialised = [](int vk) { return vk == VK_DWPW_WS || vk == VK_DWPW_WSL; };
         bool better;
         if (best < 0) {
             better = true;
         } else if (fabs(e.t_us - be.t_us) > 0.01 * std::min(e.t_us, be.t_us)) {
             better = e.t_us < be.t_us;  // modelled time decides unless within 1%
+        } else if (specialised(v.vkind) != specialised(kVariants[best].vkind)) {
+            // wave-specialised builds run the two layers' instruction streams on
+            // different waves of a SIMD, which overlaps them; the roofline terms are the
+            // same
+            better = specialised(v.vkind);
         } else if (std::min(e.wgs_per_cu * v.waves, 8) !=
                    std::min(be.wgs_per_cu * kVariants[best].waves, 8)) {
             // resident waves per CU, up to two per SIMD: more hide more latency (the kernels

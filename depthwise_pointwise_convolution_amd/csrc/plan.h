@@ -21,7 +21,8 @@ enum VKind {
     VK_PWPW_MM = 9,
     VK_DWPW_GEN = 10,
     VK_DWPW_WS = 11,
-    VK_PWDWPW_MM = 12
+    VK_PWDWPW_MM = 12,
+    VK_DWPW_WSL = 13
 };
 
 struct VariantDesc {
