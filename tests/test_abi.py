@@ -87,6 +87,45 @@ def test_fp32_pointwise_stage_runs_on_the_matrix_cores():
         assert len(re.findall(r"\bv_mfma_f32_16x16x4_?f32\b", b)) >= 16
 
 
+def test_no_full_memory_wait_before_lds_access_in_matrix_core_kernels():
+    # the matrix-core kernels keep direct global->LDS loads in flight across their steps;
+    # a wait for every vector-memory operation right before an LDS access (which the
+    # compiler inserts when it cannot tell an LDS access from those loads) would expose a
+    # full memory latency per step.  Checked on the gfx950 assembly build.py keeps.
+    import re
+    build = os.path.join(ROOT, "depthwise_pointwise_convolution_amd", "_build")
+    files = ["dwpw_mm", "dwpw_mmw", "dwpw_ws", "dwpw_wsl", "b2b_mm", "pwdw_mm", "pwdwpw_mm",
+             "pwpw_mm", "dwpw_i8"]
+    paths = [os.path.join(build, f"kernels_{f}.hip.s") for f in files]
+    if not all(os.path.exists(p) for p in paths):
+        pytest.skip("library assembly not built here")
+    found = []
+    for path in paths:
+        asm = open(path).read()
+        for m in re.finditer(r"^(_ZN3fcm\S+):", asm, re.M):
+            if "lbl" in m.group(1) or "pack" in m.group(1):
+                continue
+            end = asm.find(".Lfunc_end", m.end())
+            ins = [l.split(";")[0].strip() for l in asm[m.end():end].splitlines()]
+            ins = [l for l in ins if l and (not l.startswith(".") or l.startswith(".LBB"))]
+            # loop bodies: spans closed by a branch back to an earlier label that does not
+            # just end the program (a step that runs once, such as a tail step after the
+            # loop, may wait)
+            label = {l[:-1]: i for i, l in enumerate(ins) if l.startswith(".LBB")}
+            loops = []
+            for i, l in enumerate(ins):
+                t = l.split()
+                if t[0] in ("s_branch",) or t[0].startswith("s_cbranch"):
+                    j = label.get(t[-1], i + 1)
+                    if j < i and not any(x.startswith("s_endpgm") for x in ins[j + 1:j + 3]):
+                        loops.append((j, i))
+            for i, (a, b) in enumerate(zip(ins, ins[1:])):
+                if (a.startswith("s_waitcnt") and "vmcnt(0)" in a and b.startswith("ds_") and
+                        any(lo <= i <= hi for lo, hi in loops)):
+                    found.append((os.path.basename(path), m.group(1)[:60], b))
+    assert found == [], found[:5]
+
+
 def _problem(F, wl):
     return F.problem(wl.kind, wl.dtype, wl.N, wl.H, wl.W, wl.C, wl.K,
                      None if wl.kind == "dwpw" else wl.K1, R=wl.R, S=wl.S, stride=wl.stride,
