@@ -61,9 +61,9 @@ int occ_dwpw_gen();
 template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC>
 int launch_dw_gen_lbl(const KArgs& a, int grid, void* stream);
 
-template <int S, int OCC>
+template <int S, int OCC, int CMAX>
 int launch_dwpw_i8(const KArgs& a, int grid, void* stream);
-template <int S, int OCC>
+template <int S, int OCC, int CMAX>
 int occ_dwpw_i8();
 // INT8 layer-by-layer baselines and weight packing (dwpw_i8.hip)
 int launch_dw_lbl_i8(int stride, const KArgs& a, void* stream);

@@ -58,8 +58,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_PWDW_MM, dt, S, TH, 16, NW * BPW * 16, CMAX, 1, 2, 0, OCC, NW, CMAX, BPW},
 #define FCM_V_PWDWPW_MM(name, dt, CT, S, TH, CMAX, NW, BPW, KB, OCC) \
     {#name, VK_PWDWPW_MM, dt, S, TH, 16, KB * 16, CMAX, 1, 2, NW * BPW * 16, OCC, NW, CMAX, BPW},
-#define FCM_V_DWPW_I8(name, S, OCC) \
-    {#name, VK_DWPW_I8, FCM_I8, S, 4, 16, 64, 64, 1, 2, 0, OCC, 4, 64, 0},
+#define FCM_V_DWPW_I8(name, S, OCC, CMAX) \
+    {#name, VK_DWPW_I8, FCM_I8, S, 4, 16, 64, 64, 1, 2, 0, OCC, 4, CMAX, 0},
 #define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) \
     {#name, VK_PWPW_MM, dt, 1, PB, 16, 64, 64, 1, 2, 64, OCC, 4, 64, 0},
 #define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC) \
@@ -235,9 +235,11 @@ int variant_lds_bytes(const VariantDesc& v) {
     case VK_DWPW_I8: {
         // two input tile buffers (16-byte chunks of 16 channels, whole 256-thread load
         // rounds) and two 4-row intermediate tiles of 1 KB per row
+        // (the sliced build: depthwise filters [9][cmax] bytes and epilogue-1 constants
+        // of every channel as well)
         const int slots = IH * IW * 4;
         const int slots_p = (slots + 255) / 256 * 256;
-        return 2 * slots_p * 16 + 2 * 4 * 1024;
+        return 2 * slots_p * 16 + 2 * 4 * 1024 + (v.cmax > 64 ? v.cmax * (9 + 8) : 0);
     }
     case VK_PWDW_MM: {
         // two input-window buffers (whole load rounds of 16-pixel blocks) and one
@@ -353,8 +355,10 @@ int variant_vgpr_estimate(const VariantDesc& v) {
     case VK_DWPW_I8: {
         // depthwise and pointwise operands, both epilogues' constants (4 + 16 channels),
         // the direct-load plan, operands of the input rows, accumulators, addressing
+        // (the sliced build: two operand sets, and the accumulators live across steps)
         const int IH = (v.th - 1) * v.stride + 3, IW = 15 * v.stride + 3;
-        return 12 + 16 + 8 + 32 + 2 * ((IH * IW * 4 + 255) / 256) + 4 * IH + 16 + 16 + 40;
+        return 12 + 16 + 8 + 32 + 2 * ((IH * IW * 4 + 255) / 256) + 4 * IH + 16 + 16 + 40 +
+               (v.cmax > 64 ? 16 + 8 : 0);
     }
     case VK_PWDW_MM: {
         // per owned block: pointwise operands, five depthwise operands, both epilogues'
@@ -572,8 +576,15 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
             if (why) *why = "variant is compiled for another stride";
             return false;
         }
-        if (p.C > 64) {
-            if (why) *why = "int8 variant stages at most 64 input channels";
+        if (p.C > v.cmax) {
+            if (why) *why = v.cmax == 64 ? "single-pass int8 variant takes at most 64 input channels"
+                                         : "sliced int8 variant stages at most its compiled "
+                                           "channel count of depthwise filters in LDS";
+            return false;
+        }
+        if (v.cmax > 64 && p.C <= 64) {
+            if (why) *why = "sliced int8 variant is for more than 64 input channels (one slice "
+                            "is the single-pass kernel's case)";
             return false;
         }
         const int Ho = conv_out(p.H, p.pad_h, p.R, p.stride_h);
@@ -829,7 +840,9 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
         // 3 16x16x64 instructions per 16 channels x 16 pixels (384 op-equivalents per
         // channel and pixel), the pointwise reduction padded to 64 channels; vector work:
         // about five operations per requantized value
-        t_mat = P * pad_px * (2.0 * 64 * p.K + 384.0 * 64 * ktiles) / (2.0 * d.mfma_f16_flops);
+        // (the reduction is padded to whole 64-channel slices)
+        const double c64 = 64.0 * (double)cdiv(p.C, 64);
+        t_mat = P * pad_px * (2.0 * c64 * p.K + 384.0 * c64 * ktiles) / (2.0 * d.mfma_f16_flops);
         t_vec = P * pad_px * 5.0 * ((double)n1 * ktiles + p.K) / lane_ops_per_s;
     } else if (v.vkind == VK_DWPW_MM) {
         t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * v.cc * ktiles) / d.mfma_f16_flops;
@@ -1474,8 +1487,9 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
                                           : (int64_t)p->R * p->S * p->K1) * e;
     pl.w2_packed_bytes = (int64_t)p->K * n1 * e;
     if (p->dtype == FCM_I8) {
-        // int8: the 1x1 filters again in 64 x 64 blocks in the int8 matrix-operand order
-        pl.w2_packed_bytes += (int64_t)((p->K + 63) / 64) * 64 * 64;
+        // int8: the 1x1 filters again in 64 x 64 blocks (k tile, 64-channel slice) in the
+        // int8 matrix-operand order
+        pl.w2_packed_bytes += (int64_t)((p->K + 63) / 64) * ((p->C + 63) / 64) * 64 * 64;
     } else if (p->dtype != FCM_F32) {
         // 16-bit storage: the 1x1 filters again in 32 x 32 blocks in matrix-operand order
         // (pw_blocked_elems), and for B2B the 3x3 filters in 16 x 32 blocks

@@ -309,13 +309,19 @@ def test_i8_problems_are_checked_on_the_host():
         with pytest.raises(F.FcmError) as ei:
             F.fcm_plan(F.problem("dwpw", "i8", 1, 16, 16, C, K), _spec(F))
         assert ei.value.status == F.FCM_ERR_UNSUPPORTED
-    with pytest.raises(F.FcmError) as ei:  # more channels than the int8 kernel stages
-        F.fcm_plan(F.problem("dwpw", "i8", 1, 16, 16, 128, 64), _spec(F))
+    with pytest.raises(F.FcmError) as ei:  # more channels than the sliced kernel stages
+        F.fcm_plan(F.problem("dwpw", "i8", 1, 16, 16, 1040, 64), _spec(F))
     assert ei.value.status == F.FCM_ERR_UNSUPPORTED
     pl = F.fcm_plan(F.problem("dwpw", "i8", 8, 112, 112, 32, 64), _spec(F))
-    assert F.fcm_variant_name(pl.variant).startswith("dwpw_i8")
-    # int8 filters: 9 x C depthwise, K x C plain + 64 x 64 blocks per 64 output channels
+    assert F.fcm_variant_name(pl.variant).startswith("dwpw_i8_")
+    # int8 filters: 9 x C depthwise, K x C plain + 64 x 64 blocks per (64 output channels,
+    # 64-channel slice)
     assert pl.w1_packed_bytes == 9 * 32 and pl.w2_packed_bytes == 64 * 32 + 64 * 64
+    # wider layers run in 64-channel slices (a partial last slice included)
+    for C, K in ((96, 48), (256, 128), (960, 160)):
+        pl = F.fcm_plan(F.problem("dwpw", "i8", 2, 14, 14, C, K), _spec(F))
+        assert F.fcm_variant_name(pl.variant).startswith("dwpw_i8c_")
+        assert pl.w2_packed_bytes == K * C + -(-K // 64) * -(-C // 64) * 64 * 64
 
 
 def test_b2b_needs_16bit_storage_and_small_filters():
@@ -383,7 +389,7 @@ def test_forced_variants_cover_every_compiled_kernel():
         fcm_inputs.Workload("p", "pwdw", dt, N=2, H=17, W=23, C=c, K=k1, K1=k1, stride=s)
         for dt in ("f16", "bf16") for c in (24, 64) for k1 in (96, 144) for s in (1, 2)] + [
         fcm_inputs.Workload("q", "dwpw", "i8", N=2, H=17, W=23, C=c, K=k, K1=c, stride=s)
-        for c in (32, 64) for k in (64, 112) for s in (1, 2)] + [
+        for c in (32, 64, 96, 256) for k in (64, 112) for s in (1, 2)] + [
         fcm_inputs.Workload("r", "pwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=k1, R=1, S=1, pad=0)
         for dt in ("f16", "bf16") for c in (32, 64) for k1 in (32, 64) for k in (64, 136)] + [
         fcm_inputs.Workload("g", "dwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=c * m, R=f, S=f,

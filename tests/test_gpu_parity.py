@@ -90,6 +90,10 @@ CASES_INT = [
     ("dwpw", "i8", 2, 9, 21, 32, 64, None, 1, 1, "relu", "relu", True),
     ("dwpw", "i8", 1, 13, 15, 64, 128, None, 2, 1, "none", "relu6", True),
     ("dwpw", "i8", 2, 7, 7, 16, 48, None, 1, 0, "relu6", "none", False),
+    # wider int8 layers in 64-channel slices: four whole slices, and partial last slices
+    ("dwpw", "i8", 2, 9, 21, 256, 128, None, 1, 1, "relu", "relu6", True),
+    ("dwpw", "i8", 1, 10, 13, 96, 48, None, 2, 1, "none", "relu", True),
+    ("dwpw", "i8", 2, 7, 9, 144, 64, None, 1, 0, "relu6", "none", False),
     ("pwpw", "f16", 2, 9, 21, 64, 64, 32, 1, 0, "relu6", "relu6", True),
     ("pwpw", "bf16", 1, 11, 17, 40, 136, 56, 1, 0, "none", "relu", True),
     ("pwpw", "f16", 3, 5, 7, 24, 24, 64, 1, 0, "relu", "none", False),
