@@ -63,7 +63,8 @@ const VariantImpl kImpls[] = {
      occ_pwdwpw_mm<CT, S, TH, CMAX, NW, BPW, KB, OCC>},
 #define FCM_V_DWPW_I8(name, S, OCC, CMAX) \
     {launch_dwpw_i8<S, OCC, CMAX>, occ_dwpw_i8<S, OCC, CMAX>},
-#define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) {launch_pwpw_mm<CT, PB, OCC>, occ_pwpw_mm<CT, PB, OCC>},
+#define FCM_V_PWPW_MM(name, dt, CT, PB, OCC, CMAX, KT) \
+    {launch_pwpw_mm<CT, PB, OCC, CMAX, KT>, occ_pwpw_mm<CT, PB, OCC, CMAX, KT>},
 #define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC)    \
     {launch_dwpw_gen<CT, S, FS, D, M, TH, TW, KT, CC>,                \
      occ_dwpw_gen<CT, S, FS, D, M, TH, TW, KT, CC>,                   \

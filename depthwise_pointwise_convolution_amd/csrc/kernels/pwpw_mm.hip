@@ -1,5 +1,6 @@
 // pwpw_mm.hip -- fused pointwise 1x1 -> pointwise 1x1 (the FCM PWPW module) on the gfx950
-// matrix cores, 16-bit storage, C <= 64 input and K1 <= 64 intermediate channels.
+// matrix cores, 16-bit storage: a single-pass kernel for C <= 64 input and K1 <= 64
+// intermediate channels, and a wide kernel (further down) for C <= CMAX and any K1.
 //
 // The PWPW fusion case of "Fusing Depthwise and Pointwise Convolutions for Efficient
 // Inference on GPUs" (Sec. III, Table II) chains two 1x1 layers: two GEMMs over the
@@ -273,20 +274,233 @@ void pwpw_mm_kernel(KArgs a) {
     mm::wait_vmcnt<0>();
 }
 
-template <typename T, int PB, int OCC>
+// Wide PW->PW (MobileNetV2-style bottleneck pairs such as 24 -> 144 -> 24 and
+// 96 -> 576 -> 96): C <= CMAX input channels, any number of intermediate channels in
+// 64-channel slices, KT = 64 or 128 output channels per workgroup.  Four waves, tiles of
+// 64 consecutive pixels; the whole input tile (all C channels) sits in LDS, the next
+// tile's by direct global->LDS loads during the current one.  Per intermediate slice j:
+//   phase A  wave w: intermediate channels 64j + 16w .. +15 of the four pixel blocks,
+//            reduced over C in 32-channel steps (first-layer filters from the plain
+//            [K1][C] array, 16 bytes per lane and step), epilogue 1, rounding, 8-byte
+//            writes of the slice into an LDS buffer in the second layer's operand order
+//            (two buffers, alternating by slice);
+//   phase B  wave w: pixel block w, the workgroup's KT output channels: the slice's two
+//            32-channel reduction steps accumulated in registers across the slices
+//            (blocked filter copy, as in the single-pass kernel).
+// One barrier per slice (after phase A); both layers' filters of a slice are requested
+// at its start, so the second layer's arrive behind phase A.  After the last slice,
+// epilogue 2 and 16-byte stores.  Channels past C or K1 come out as zeros (zero-filled
+// input chunks, zero filters), so a partial last slice needs no special case.
+template <typename T, int CMAX, int KT, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void pwpw_wide_kernel(KArgs a) {
+    constexpr int NT = 256, PB = 4, MP = PB * 16, CH = 8;
+    constexpr int NSL = CMAX / 64;              // 64-channel slices of the input tile
+    constexpr int SLOTS = NSL * MP * CH;
+    constexpr int R = SLOTS / NT;               // direct-load rounds per tile
+    static_assert(CMAX % 64 == 0 && SLOTS % NT == 0, "whole slices and load rounds");
+    constexpr int NKC = CMAX / 32;              // first-layer reduction steps (at most)
+    constexpr int NKS = 2;                      // second-layer reduction steps per slice
+    constexpr int KBW = KT / 16;                // 16-channel output blocks per wave
+    static_assert(KT == 64 || KT == 128, "64 or 128 output channels per workgroup");
+
+    __shared__ __attribute__((aligned(16))) u32x4 xs0[SLOTS];
+    __shared__ __attribute__((aligned(16))) u32x4 xs1[SLOTS];
+    __shared__ __attribute__((aligned(16))) u32x4 tl0[PB * NKS * 64];
+    __shared__ __attribute__((aligned(16))) u32x4 tl1[PB * NKS * 64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
+    const int G = gridDim.x;
+    const int L = xcd_logical_id(blockIdx.x, G);
+    const int k0 = (L % a.num_ktiles) * KT;
+    const int es = (int)sizeof(T);
+    const int64_t M = (int64_t)a.N * a.H * a.W;
+    const __amdgpu_buffer_rsrc_t rx = mm::rsrc(a.x, (uint32_t)(M * a.C * es));
+    const __amdgpu_buffer_rsrc_t ry = mm::rsrc(a.y, (uint32_t)(M * a.K * es));
+    const int ntiles = a.num_ptiles;
+    const int pstep = G / a.num_ktiles;
+    const int nkc = (a.C + 31) / 32;   // first-layer reduction steps of this problem
+    const int nj = (a.K1 + 63) / 64;   // intermediate slices
+
+    // ---- direct-load plan: slot s = (slice sl, pixel p, chunk position) holds input
+    // chunk q = position ^ ((p >> 1) & 7) of the slice; chunks past C load zero
+    uint32_t dl_off[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int s = r * NT + tid;
+        const int sl = s / (MP * CH), p = (s / CH) % MP;
+        const int q = (s % CH) ^ ((p >> 1) & 7);
+        const int c = sl * 64 + q * 8;
+        dl_off[r] = c < a.C ? (uint32_t)((p * a.C + c) * es) : mm::kOob;
+    }
+    auto issue_tile = [&](int t, u32x4* dst) __attribute__((always_inline)) {
+        const bool live = t < ntiles;
+        const int base = live ? t * MP * a.C * es : 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t off = live ? dl_off[r] : mm::kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void*)(dst + r * NT + wave * 64), 16, off,
+                base, 0, 0);
+        }
+    };
+
+    // ---- per-lane constants ------------------------------------------------------------
+    const T* __restrict__ w1 = (const T*)a.w1;
+    const u32x4* __restrict__ wpb =
+        reinterpret_cast<const u32x4*>((const T*)a.w2 + (int64_t)a.K * a.K1);
+    const int s32 = (a.K1 + 31) / 32, g32n = (a.K + 31) / 32;
+    // epilogue-2 constants of the lane's output channels k0 + 32 g + 8(l/16) + j
+    float s2r[KT / 32][8], b2r[KT / 32][8];
+#pragma unroll
+    for (int g = 0; g < KT / 32; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int k = k0 + 32 * g + 8 * lg + j;
+            const bool ok = k < a.K;
+            s2r[g][j] = (a.s2 && ok) ? a.s2[k] : 1.0f;
+            b2r[g][j] = (a.b2 && ok) ? a.b2[k] : 0.0f;
+        }
+    // phase A operand read of step kc: pixel 16pb + l%16, chunk 4(kc%2) + l/16 of slice
+    // kc/2 (pixel blocks add 16 * CH * 16 bytes, slices MP * CH * 16)
+    uint32_t xo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = 4 * h + lg;
+        xo[h] = (uint32_t)((lr * CH + (q ^ ((lr >> 1) & 7))) * 16);
+    }
+    const uint32_t tls_w = (uint32_t)(((2 * (wave & 1) + (lg >> 1)) * 16 + lr) * 16 + (lg & 1) * 8);
+    constexpr uint32_t kLaneOob = 0x40000000u, kRowOob = 0x80000000u;
+    uint32_t st_lane[KT / 32];
+#pragma unroll
+    for (int g = 0; g < KT / 32; ++g)
+        st_lane[g] = k0 + 32 * g + 8 * lg < a.K ? (uint32_t)((lr * a.K + k0 + 32 * g + 8 * lg) * es)
+                                                : kLaneOob;
+
+    // one tile: slices of the intermediate, then epilogue 2 and the stores
+    auto tile = [&](int t, const u32x4* xsrc) __attribute__((always_inline)) {
+        const char* xb = reinterpret_cast<const char*>(xsrc);
+        f32x4 acc[KBW];
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < nj; ++j) {
+            // both layers' filters of the slice
+            const int c1 = 64 * j + 16 * wave + lr;
+            u32x4 a1[NKC];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                const int ci = 32 * kc + 8 * lg;
+                a1[kc] = (kc < nkc && c1 < a.K1 && ci < a.C)
+                             ? *reinterpret_cast<const u32x4*>(w1 + (int64_t)c1 * a.C + ci)
+                             : u32x4{0u, 0u, 0u, 0u};
+            }
+            u32x4 wa[NKS][KBW];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < KBW; ++kb) {
+                    const int g = min(k0 / 32 + kb / 2, g32n - 1);
+                    wa[ks][kb] = wpb[((g * s32 + min(2 * j + ks, s32 - 1)) * 2 + (kb & 1)) * 64 + lane];
+                }
+            float s1r[4], b1r[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 64 * j + 16 * wave + 4 * lg + i;
+                const bool ok = c < a.K1;
+                s1r[i] = (a.s1 && ok) ? a.s1[c] : 1.0f;
+                b1r[i] = (a.b1 && ok) ? a.b1[c] : 0.0f;
+            }
+            // phase A: the slice of the intermediate for the four pixel blocks
+            f32x4 d[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) d[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                if (kc < nkc) {
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) {
+                        const u32x4 bx = *reinterpret_cast<const u32x4*>(
+                            xb + (kc >> 1) * (MP * CH * 16) + pb * (16 * CH * 16) + xo[kc & 1]);
+                        d[pb] = mfma<T>(a1[kc], bx, d[pb]);
+                    }
+                }
+            }
+            u32x4* tdst = (j & 1) ? tl1 : tl0;
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = epilogue(d[pb][i], s1r[i], b1r[i], act1);
+                st8(reinterpret_cast<char*>(tdst) + ((pb * NKS + (wave >> 1)) * 64) * 16 + tls_w,
+                    pack8<T>(o));
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own intermediate writes done
+            __builtin_amdgcn_s_barrier();
+            // phase B: pixel block `wave`, the slice's two reduction steps
+            u32x4 bfr[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) bfr[ks] = tdst[(wave * NKS + ks) * 64 + lane];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < KBW; ++kb) acc[kb] = mfma<T>(wa[ks][kb], bfr[ks], acc[kb]);
+        }
+        // pixels past the tensor fall past the output's range (below 1 GiB, checked by the
+        // planner) and are dropped
+        const uint32_t pix0 = t < ntiles ? (uint32_t)((t * MP + wave * 16) * a.K * es) : kRowOob;
+#pragma unroll
+        for (int g = 0; g < KT / 32; ++g) {
+            float o[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = epilogue(acc[2 * g][i], s2r[g][i], b2r[g][i], act2);
+                o[4 + i] = epilogue(acc[2 * g + 1][i], s2r[g][4 + i], b2r[g][4 + i], act2);
+            }
+            // the whole offset in the vector operand, scalar offset 0
+            __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, st_lane[g] + pix0, 0, 0);
+        }
+    };
+
+    // ---- tile loop: the next tile's input is requested before the current one runs ---
+    int cur = L / a.num_ktiles;
+    issue_tile(cur, xs0);
+    mm::wait_vmcnt<0>();
+    int par = 0;
+    while (cur < ntiles) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();  // every wave is done with the buffers the next
+                                       // tile's loads and slices overwrite
+        issue_tile(cur + pstep, par ? xs0 : xs1);
+        tile(cur, par ? xs1 : xs0);
+        mm::wait_vmcnt<0>();  // the next tile's input (and this tile's stores)
+        cur += pstep;
+        par ^= 1;
+    }
+}
+
+template <typename T, int PB, int OCC, int CMAX, int KT>
 int launch_pwpw_mm(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((pwpw_mm_kernel<T, PB, OCC>), dim3(grid), dim3(256), 0, (hipStream_t)stream,
-                       a);
+    if constexpr (CMAX == 64)
+        hipLaunchKernelGGL((pwpw_mm_kernel<T, PB, OCC>), dim3(grid), dim3(256), 0,
+                           (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL((pwpw_wide_kernel<T, CMAX, KT, OCC>), dim3(grid), dim3(256), 0,
+                           (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
-template <typename T, int PB, int OCC>
+template <typename T, int PB, int OCC, int CMAX, int KT>
 int occ_pwpw_mm() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pwpw_mm_kernel<T, PB, OCC>, 256, 0) !=
-        hipSuccess)
-        return 0;
-    return n;
+    hipError_t e;
+    if constexpr (CMAX == 64)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pwpw_mm_kernel<T, PB, OCC>, 256, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pwpw_wide_kernel<T, CMAX, KT, OCC>,
+                                                         256, 0);
+    return e == hipSuccess ? n : 0;
 }
 
 #define FCM_V_DWPW(...)
@@ -297,9 +511,9 @@ int occ_pwpw_mm() {
 #define FCM_V_DWPW_MMW(...)
 #define FCM_V_PWDW_MM(...)
 #define FCM_V_DWPW_I8(...)
-#define FCM_V_PWPW_MM(name, dt, CT, PB, OCC)                                  \
-    template int launch_pwpw_mm<CT, PB, OCC>(const KArgs&, int, void*); \
-    template int occ_pwpw_mm<CT, PB, OCC>();
+#define FCM_V_PWPW_MM(name, dt, CT, PB, OCC, CMAX, KT)                                  \
+    template int launch_pwpw_mm<CT, PB, OCC, CMAX, KT>(const KArgs&, int, void*); \
+    template int occ_pwpw_mm<CT, PB, OCC, CMAX, KT>();
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32

@@ -47,9 +47,9 @@ int launch_pwdwpw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int CMAX, int NW, int BPW, int KB, int OCC>
 int occ_pwdwpw_mm();
 
-template <typename T, int PB, int OCC>
+template <typename T, int PB, int OCC, int CMAX, int KT>
 int launch_pwpw_mm(const KArgs& a, int grid, void* stream);
-template <typename T, int PB, int OCC>
+template <typename T, int PB, int OCC, int CMAX, int KT>
 int occ_pwpw_mm();
 
 // generalised DW->PW (dwpw_gen.hip): fused kernel, occupancy, and the matching

@@ -60,8 +60,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_PWDWPW_MM, dt, S, TH, 16, KB * 16, CMAX, 1, 2, NW * BPW * 16, OCC, NW, CMAX, BPW},
 #define FCM_V_DWPW_I8(name, S, OCC, CMAX) \
     {#name, VK_DWPW_I8, FCM_I8, S, 4, 16, 64, 64, 1, 2, 0, OCC, 4, CMAX, 0},
-#define FCM_V_PWPW_MM(name, dt, CT, PB, OCC) \
-    {#name, VK_PWPW_MM, dt, 1, PB, 16, 64, 64, 1, 2, 64, OCC, 4, 64, 0},
+#define FCM_V_PWPW_MM(name, dt, CT, PB, OCC, CMAX, KT) \
+    {#name, VK_PWPW_MM, dt, 1, PB, 16, KT, CMAX, 1, 2, CMAX == 64 ? 64 : 1 << 20, OCC, 4, CMAX, 0},
 #define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC) \
     {#name, VK_DWPW_GEN, dt, S, TH, TW, KT, CC, 0, 1, 0, 2, 4, 0, 0, FS, D, M},
 #include "variants.def"
@@ -228,9 +228,9 @@ int variant_lds_bytes(const VariantDesc& v) {
         return 2 * slots_p * 16 + nb * (IH + 1) * 2 * iw * 16 + v.th * 16 * (v.k1 + 8) * 2;
     }
     case VK_PWPW_MM: {
-        // two input tiles of th x 16 pixels x 64 channels, two intermediate tiles of
+        // two input tiles of th x 16 pixels x cmax channels, two intermediate tiles of
         // th x 16 pixels x 64 channels
-        return 2 * v.th * 16 * 64 * e + 2 * v.th * 16 * 64 * e;
+        return 2 * v.th * 16 * v.cmax * e + 2 * v.th * 16 * 64 * e;
     }
     case VK_DWPW_I8: {
         // two input tile buffers (16-byte chunks of 16 channels, whole 256-thread load
@@ -349,7 +349,12 @@ int variant_vgpr_estimate(const VariantDesc& v) {
     }
     case VK_PWPW_MM: {
         // first-layer operands, 8 second-layer operands, 4 + 16 epilogue constants, the
-        // direct-load plan, operands and accumulators of the tile, addressing
+        // direct-load plan, operands and accumulators of the tile, addressing; the wide
+        // build: a slice's first-layer operands over cmax inputs, its second-layer
+        // operands and accumulators of KT outputs, epilogue-2 constants, the load plan
+        if (v.cmax > 64)
+            return 4 * (v.cmax / 32) + 8 * (v.kt / 16) + 4 * (v.kt / 16) + v.kt / 2 +
+                   v.cmax / 32 + 16 + 40;
         return 8 + 32 + 8 + 32 + v.th * 2 / 4 * 8 + v.th * 8 + (v.th / 4) * 16 + 40;
     }
     case VK_DWPW_I8: {
@@ -556,8 +561,16 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
             if (why) *why = "variant is for another module kind or storage type";
             return false;
         }
-        if (p.C > 64 || p.K1 > 64) {
-            if (why) *why = "PW->PW variant takes at most 64 input and 64 intermediate channels";
+        if (p.C > v.cmax || p.K1 > v.k1) {
+            if (why) *why = v.cmax == 64 ? "single-pass PW->PW variant takes at most 64 input "
+                                           "and 64 intermediate channels"
+                                         : "wide PW->PW variant stages at most its compiled "
+                                           "input channel count";
+            return false;
+        }
+        if (v.cmax > 64 && p.C <= 64 && p.K1 <= 64) {
+            if (why) *why = "wide PW->PW variant is for more than 64 input or intermediate "
+                            "channels (the single-pass kernel's case)";
             return false;
         }
         const int64_t M = sat_mul({p.N, p.H, p.W});
@@ -1172,13 +1185,19 @@ Estimate estimate_pwpw(const VariantDesc& v, const fcm_problem& p, const fcm_dev
     r.grid = (int)grid;
     const int64_t x_bytes = M * p.C * e, y_bytes = M * p.K * e;
     const int64_t w_bytes = ((int64_t)p.K1 * p.C + (int64_t)std::min(v.kt, p.K) * p.K1) * e;
-    r.pred = x_bytes * ktiles + y_bytes + grid * (w_bytes + 4LL * 2 * (p.K1 + v.kt));
+    // (the single-pass build keeps its filters in registers for the workgroup's whole
+    // run; the wide build reads both layers' filters again for every tile)
+    const bool wide = v.cmax > 64;
+    r.pred = x_bytes * ktiles + y_bytes +
+             (wide ? (int64_t)r.num_tiles : grid) * (w_bytes + 4LL * 2 * (p.K1 + v.kt));
     r.waste = (double)ktiles * ((double)ptiles * mp / (double)M);
     const double alg = (double)x_bytes + y_bytes + ((double)p.K1 * p.C + (double)p.K * p.K1) * e;
+    const double c_pad = wide ? 32.0 * cdiv(p.C, 32) : 64.0;
+    const double k1_pad = wide ? 64.0 * cdiv(p.K1, 64) : 64.0;
     const double t_mat = (double)ptiles * mp *
-                         (2.0 * 64 * 64 * ktiles + 2.0 * 64 * std::min(v.kt, p.K) * ktiles) /
+                         (2.0 * c_pad * k1_pad * ktiles + 2.0 * k1_pad * std::min(v.kt, p.K) * ktiles) /
                          d.mfma_f16_flops;
-    const double t_vec = (double)ptiles * mp * 3.0 * (64.0 * ktiles + p.K) /
+    const double t_vec = (double)ptiles * mp * 3.0 * (k1_pad * ktiles + p.K) /
                          (d.valu_f32_flops / 2.0);
     const double busy = std::min(1.0, (double)r.num_tiles / d.num_cus);
     finish_time(r, alg / d.hbm_bytes_per_s, (double)r.pred / (4.0 * d.hbm_bytes_per_s), t_mat,

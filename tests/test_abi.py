@@ -391,7 +391,8 @@ def test_forced_variants_cover_every_compiled_kernel():
         fcm_inputs.Workload("q", "dwpw", "i8", N=2, H=17, W=23, C=c, K=k, K1=c, stride=s)
         for c in (32, 64, 96, 256) for k in (64, 112) for s in (1, 2)] + [
         fcm_inputs.Workload("r", "pwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=k1, R=1, S=1, pad=0)
-        for dt in ("f16", "bf16") for c in (32, 64) for k1 in (32, 64) for k in (64, 136)] + [
+        for dt in ("f16", "bf16") for c, k1 in ((32, 32), (64, 64), (24, 144), (96, 576))
+        for k in (64, 136)] + [
         fcm_inputs.Workload("g", "dwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=c * m, R=f, S=f,
                             stride=s, pad=(f - 1) * d // 2, dil=d, mult=m)
         for dt in ("f16", "bf16") for c, k in ((40, 48), (64, 136)) for s in (1, 2)

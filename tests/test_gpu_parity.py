@@ -97,6 +97,11 @@ CASES_INT = [
     ("pwpw", "f16", 2, 9, 21, 64, 64, 32, 1, 0, "relu6", "relu6", True),
     ("pwpw", "bf16", 1, 11, 17, 40, 136, 56, 1, 0, "none", "relu", True),
     ("pwpw", "f16", 3, 5, 7, 24, 24, 64, 1, 0, "relu", "none", False),
+    # wide bottleneck pairs: intermediate in 64-channel slices (a partial last one), input
+    # channels past one slice, 64 and 128 output channels per workgroup
+    ("pwpw", "f16", 2, 9, 21, 24, 24, 144, 1, 0, "relu6", "none", True),
+    ("pwpw", "bf16", 1, 11, 17, 96, 96, 576, 1, 0, "relu6", "relu", True),
+    ("pwpw", "f16", 2, 7, 9, 160, 40, 200, 1, 0, "none", "relu6", False),
     ("pwdw", "f16", 2, 9, 21, 24, 144, 144, 1, 1, "relu6", "relu6", True),
     ("pwdw", "bf16", 1, 11, 17, 64, 48, 48, 1, 1, "none", "relu", False),
     ("pwdw", "f16", 2, 13, 15, 16, 96, 96, 2, 1, "relu", "relu6", True),
