@@ -313,9 +313,11 @@ void b2b_mm_kernel(KArgs a) {
         const bool ok = t.oh0 + wave < a.Ho && t.ow0 + lr < a.Wo;
         const uint32_t row = (uint32_t)(t.out_base + wave * out_row);
         __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry,
-                                               ok && st0 != mm::kOob ? row + st0 : mm::kOob, 0, 0);
+                                               ok && st0 != mm::kOob ? row + st0 : mm::kOob, 0,
+                                               mm::kStoreStream);
         __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o + 8), ry,
-                                               ok && st1 != mm::kOob ? row + st1 : mm::kOob, 0, 0);
+                                               ok && st1 != mm::kOob ? row + st1 : mm::kOob, 0,
+                                               mm::kStoreStream);
     };
 
     // ---- software-pipelined tile loop (see dwpw_mm.hip): step i waits for tile i+1's

@@ -312,7 +312,8 @@ void dwpw_i8_kernel(KArgs a) {
         const uint32_t lanev = t.ow0 + lr < a.Wo ? st_lane : kLaneOob;
         const uint32_t row = t.oh0 + wave < a.Ho ? (uint32_t)(t.out_base + wave * out_row) : kRowOob;
         // the whole offset in the vector operand, scalar offset 0
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, ry, lanev + row, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, ry, lanev + row, 0,
+                                               mm::kStoreStream);
     };
 
     // ---- software-pipelined tile loop (as in the 16-bit matrix-core kernel) ---------
@@ -638,7 +639,7 @@ void dwpw_i8c_kernel(KArgs a) {
             t.oh0 + wave < a.Ho ? (uint32_t)(t.out_base + wave * out_row) : kRowOob;
         // the whole offset in the vector operand, scalar offset 0
         __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, ry, lanev + row,
-                                               0, 0);
+                                               0, mm::kStoreStream);
         if (done) {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) acc[kb] = i32x4{0, 0, 0, 0};

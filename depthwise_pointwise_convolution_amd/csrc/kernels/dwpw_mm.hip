@@ -474,7 +474,7 @@ void dwpw_mm_kernel(KArgs a) {
                 __builtin_amdgcn_raw_buffer_store_b128(
                     pack16<T>(o), ry,
                     v == mm::kOob ? mm::kOob : (uint32_t)srow + v + kb * 4 * (uint32_t)sizeof(T),
-                    0, 0);
+                    0, mm::kStoreStream);
             }
         }
     };

@@ -414,7 +414,8 @@ void dwpw_ws_kernel(KArgs a) {
                 const bool run_ok = ok && kl < a.K;
                 __builtin_amdgcn_raw_buffer_store_b128(
                     pack16<T>(o), ry,
-                    run_ok ? (uint32_t)t.out_base + v + (uint32_t)(kl * es) : mm::kOob, 0, 0);
+                    run_ok ? (uint32_t)t.out_base + v + (uint32_t)(kl * es) : mm::kOob, 0,
+                    mm::kStoreStream);
             }
         };
         // the prologue's barrier (the depthwise layer of step 0 is not read before the

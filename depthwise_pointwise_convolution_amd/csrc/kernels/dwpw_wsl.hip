@@ -438,7 +438,7 @@ void dwpw_wsl_kernel(KArgs a) {
                     __builtin_amdgcn_raw_buffer_store_b128(
                         pack16<T>(o), ry,
                         run_ok ? (uint32_t)t.out_base + v + (uint32_t)((k0 + kl) * es) : mm::kOob,
-                        0, 0);
+                        0, mm::kStoreStream);
                 }
 #pragma unroll
                 for (int kb = 0; kb < KBW; ++kb) acc[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -243,7 +243,8 @@ void pwpw_mm_kernel(KArgs a) {
                     o[4 + i] = epilogue(acc[mb][2 * g + 1][i], s2r[g][4 + i], b2r[g][4 + i], act2);
                 }
                 // the whole offset in the vector operand, scalar offset 0
-                __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, st_lane[g] + pix0, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, st_lane[g] + pix0, 0,
+                                                       mm::kStoreStream);
             }
         }
     };
@@ -459,7 +460,8 @@ void pwpw_wide_kernel(KArgs a) {
                 o[4 + i] = epilogue(acc[2 * g + 1][i], s2r[g][4 + i], b2r[g][4 + i], act2);
             }
             // the whole offset in the vector operand, scalar offset 0
-            __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, st_lane[g] + pix0, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(pack16<T>(o), ry, st_lane[g] + pix0, 0,
+                                                   mm::kStoreStream);
         }
     };
 
