@@ -65,10 +65,10 @@ const VariantImpl kImpls[] = {
     {launch_dwpw_i8<S, OCC, CMAX>, occ_dwpw_i8<S, OCC, CMAX>},
 #define FCM_V_PWPW_MM(name, dt, CT, PB, OCC, CMAX, KT) \
     {launch_pwpw_mm<CT, PB, OCC, CMAX, KT>, occ_pwpw_mm<CT, PB, OCC, CMAX, KT>},
-#define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC)    \
-    {launch_dwpw_gen<CT, S, FS, D, M, TH, TW, KT, CC>,                \
-     occ_dwpw_gen<CT, S, FS, D, M, TH, TW, KT, CC>,                   \
-     launch_dw_gen_lbl<CT, S, FS, D, M, TH, TW, KT, CC>},
+#define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC, NG) \
+    {launch_dwpw_gen<CT, S, FS, D, M, TH, TW, KT, CC, NG>,                \
+     occ_dwpw_gen<CT, S, FS, D, M, TH, TW, KT, CC, NG>,                   \
+     launch_dw_gen_lbl<CT, S, FS, D, M, TH, TW, KT, CC, NG>},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32

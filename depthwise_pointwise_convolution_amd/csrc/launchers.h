@@ -53,12 +53,13 @@ template <typename T, int PB, int OCC, int CMAX, int KT>
 int occ_pwpw_mm();
 
 // generalised DW->PW (dwpw_gen.hip): fused kernel, occupancy, and the matching
-// layer-by-layer depthwise kernel
-template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC>
+// layer-by-layer depthwise kernel (NG: the fused variant's channel groups, which only
+// tell the instantiations of variants that differ in it apart)
+template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC, int NG>
 int launch_dwpw_gen(const KArgs& a, int grid, void* stream);
-template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC>
+template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC, int NG>
 int occ_dwpw_gen();
-template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC>
+template <typename T, int S, int FS, int D, int M, int TH, int TW, int KT, int CC, int NG>
 int launch_dw_gen_lbl(const KArgs& a, int grid, void* stream);
 
 template <int S, int OCC, int CMAX>

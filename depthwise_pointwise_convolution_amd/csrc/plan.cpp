@@ -62,8 +62,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_I8, FCM_I8, S, 4, 16, 64, 64, 1, 2, 0, OCC, 4, CMAX, 0},
 #define FCM_V_PWPW_MM(name, dt, CT, PB, OCC, CMAX, KT) \
     {#name, VK_PWPW_MM, dt, 1, PB, 16, KT, CMAX, 1, 2, CMAX == 64 ? 64 : 1 << 20, OCC, 4, CMAX, 0},
-#define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC) \
-    {#name, VK_DWPW_GEN, dt, S, TH, TW, KT, CC, 0, 1, 0, 2, 4, 0, 0, FS, D, M},
+#define FCM_V_DWPW_GEN(name, dt, CT, S, FS, D, M, TH, TW, KT, CC, NG) \
+    {#name, VK_DWPW_GEN, dt, S, TH, TW, KT, CC, 0, 1, 0, 2, 4 * NG, 0, 0, FS, D, M},
 #include "variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -160,10 +160,13 @@ int variant_lds_bytes(const VariantDesc& v) {
     if (v.vkind == VK_DWPW_GEN) {
         // input window chunk, intermediate chunk (C*M channels), fp32 depthwise filters and
         // epilogue-1 constants of the chunk, epilogue-2 constants of the K tile
-        const int ext = (v.fs - 1) * v.dil + 1, cm = v.cc * v.mult;
+        // (per channel group), plus the partial sums one group hands to another
+        const int ext = (v.fs - 1) * v.dil + 1, cm = v.cc * v.mult, ng = v.waves / 4;
         const int IHg = (v.th - 1) * v.stride + ext, IWg = (v.tw - 1) * v.stride + ext;
-        return IHg * IWg * (v.cc + 8) * e + v.th * v.tw * (cm + 8) * e +
-               v.fs * v.fs * cm * 4 + 2 * cm * 4 + 2 * v.kt * 4;
+        const int red = ng > 1 ? v.th * v.tw * v.kt * 4 : 16;
+        return ng * (IHg * IWg * (v.cc + 8) * e + v.th * v.tw * (cm + 8) * e +
+                     v.fs * v.fs * cm * 4 + 2 * cm * 4) +
+               2 * v.kt * 4 + red;
     }
     const int IH = (v.th - 1) * v.stride + 3, IW = (v.tw - 1) * v.stride + 3;
     const int P = v.th * v.tw;
@@ -552,6 +555,15 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
             v.mult != prob_mult(p)) {
             if (why) *why = "variant is compiled for another stride, filter size, dilation or "
                             "depth multiplier";
+            return false;
+        }
+        // whole tensors through 32-bit buffer offsets (the output is bounded by the
+        // padded input extent at stride 1)
+        const int64_t e = p.dtype == FCM_F32 ? 4 : 2;
+        if (sat_mul({p.N, p.H, p.W, p.C, e}) >= ((int64_t)1 << 31) ||
+            sat_mul({p.N, (int64_t)p.H + 2 * p.pad_h, (int64_t)p.W + 2 * p.pad_w, p.K, e}) >=
+                ((int64_t)1 << 31)) {
+            if (why) *why = "generalised variant addresses whole tensors below 2 GiB";
             return false;
         }
         return true;
@@ -1077,9 +1089,11 @@ Estimate estimate_gen(const VariantDesc& v, const fcm_problem& p, const fcm_devi
     const int e = elem_bytes(p.dtype);
     const int lds = variant_lds_bytes(v);
     int vg = (variant_vgpr_estimate(v) + 7) / 8 * 8;
+    // workgroups per CU: a workgroup of NG channel groups puts NG waves on each SIMD
+    const int ng = std::max(v.waves / 4, 1);
     int occ = std::min(std::min(lds > 0 ? d.lds_bytes_per_cu / lds : 8,
-                                std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ)),
-                       d.max_waves_per_simd);
+                                std::max(d.vgprs_per_simd_lane / std::max(vg, 1), v.occ) / ng),
+                       d.max_waves_per_simd / ng);
     if (lds > d.lds_bytes_per_wg) occ = 0;
     r.wgs_per_cu = occ;
     const int tiles_h = (int)cdiv(Ho, v.th), tiles_w = (int)cdiv(Wo, v.tw);
@@ -1114,7 +1128,9 @@ Estimate estimate_gen(const VariantDesc& v, const fcm_problem& p, const fcm_devi
     // each (tile, channel chunk) step of this kernel also pays a fixed latency (two
     // barriers and its loads' round trip, ~1 us measured): the chunks of a workgroup's
     // tiles run one after another
-    const int64_t steps = cdiv(r.num_tiles, std::max<int64_t>(grid, 1)) * cdiv(p.C, v.cc);
+    // (the channel groups of a workgroup take a tile's chunks in turn)
+    const int64_t steps =
+        cdiv(r.num_tiles, std::max<int64_t>(grid, 1)) * cdiv(cdiv(p.C, v.cc), ng);
     r.t_us += 1.0 * (double)steps;
     // constructed DW->PW estimate (Eq. 1 with the window extent as the filter size)
     const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, ext_h,

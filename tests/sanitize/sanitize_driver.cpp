@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <random>
 #include <string>
 #include <vector>
@@ -114,7 +115,8 @@ fcm_problem random_problem() {
     p.act2 = pick(-1, 3);
     p.dil_h = p.dil_w = pick(0, 5) ? 0 : pick(-1, 3);
     p.mult = pick(0, 5) ? 0 : pick(-1, 3);
-    if (p.kind == FCM_KIND_DWPW && pick(0, 3)) p.K1 = p.C * (p.mult > 0 ? p.mult : 1);
+    if (p.kind == FCM_KIND_DWPW && pick(0, 3))  // (saturated: C may be drawn huge)
+        p.K1 = (int)std::min<int64_t>((int64_t)p.C * (p.mult > 0 ? p.mult : 1), INT32_MAX);
     if (p.kind == FCM_KIND_PWDW && pick(0, 3)) p.K = p.K1;
     if (p.kind == FCM_KIND_PWPW && pick(0, 3)) {
         p.R = p.S = 1;
