@@ -252,7 +252,7 @@ def roof(plan, wl, us: float) -> dict:
 
 
 def measure(name, args, steps, warmup, torch, dev, stream, with_unfused=True):
-    """Plan (and, unless --no-tune, measure-choose) the fused kernel of one workload,
+    """Plan (and, with --tune, measure-choose) the fused kernel of one workload,
     then time the fused and the layer-by-layer paths over a buffer rotation that
     exceeds the Infinity Cache.  Returns the figures and the module."""
     import fcm_inputs
@@ -271,7 +271,7 @@ def measure(name, args, steps, warmup, torch, dev, stream, with_unfused=True):
     ys = [mod.new_output(dev) for _ in range(nsets)]
     ts = [torch.empty(mod.t_shape, dtype=tdt, device=dev) for _ in range(nsets)]
     torch.cuda.synchronize()
-    if variant is None and not args.no_tune and args.mode != "variants":
+    if variant is None and args.tune and args.mode != "variants":
         # measured choice of variant and grid (untimed, before the timing proper)
         with torch.cuda.stream(stream):
             mod.tune(xs, ys, iters=2 * nsets, stream=stream)
@@ -326,8 +326,12 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--variant", type=int, default=None, help="force a fused kernel variant")
-    ap.add_argument("--no-tune", action="store_true",
-                    help="use the analytic plan instead of the measured choice (fcm_tune)")
+    ap.add_argument("--tune", action="store_true",
+                    help="replace the planner's analytic plan by the measured choice (fcm_tune); "
+                         "the default analytic plan makes every run, profiled or not, use the "
+                         "same kernel")
+    ap.add_argument("--no-tune", dest="tune", action="store_false",
+                    help="the analytic plan (the default)")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--sets", type=int, default=0,
                     help="input/output buffer sets in rotation (0 = enough to exceed the "

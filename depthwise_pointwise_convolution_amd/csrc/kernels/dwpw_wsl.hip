@@ -207,8 +207,11 @@ void dwpw_wsl_kernel(KArgs a) {
         const __amdgpu_buffer_rsrc_t rx =
             mm::rsrc(a.x, (uint32_t)(a.N * a.H * a.W * a.C * es));
         // direct-load plan: slot s holds 16-byte piece q of window pixel p = s / CH,
-        // s % CH = q ^ (column & 7); per lane and round, the offset from the window origin
-        // and, where a tile is a whole map, from the image origin (padding out of range)
+        // s % CH = q ^ ((column - row) & 7); per lane and round, the offset from the window
+        // origin and, where a tile is a whole map, from the image origin (padding out of
+        // range).  (With the column alone in the key, 8 lanes of a depthwise read whose
+        // output pixels wrap from one row of a 7-wide map into the next hit one bank group
+        // twice; column minus row gives them 8 distinct groups in every pixel block.)
         const bool whole = a.tiles_h == 1 && a.tiles_w == 1;
         uint32_t dl_off[R], dl_img[R];
         int dl_pos[R];
@@ -216,7 +219,7 @@ void dwpw_wsl_kernel(KArgs a) {
         for (int r = 0; r < R; ++r) {
             const int s = r * NTD + tid;
             const int p = s / CH, ihl = p / IW, iwl = p % IW;
-            const int q = (s % CH) ^ (iwl & 7);
+            const int q = (s % CH) ^ ((iwl - ihl) & 7);
             const bool real = s < SLOTS;
             dl_off[r] = real ? (uint32_t)((ihl * a.W + iwl) * a.C + q * 8) * (uint32_t)es : mm::kOob;
             dl_pos[r] = real ? (ihl << 16) | iwl : 0;
@@ -277,19 +280,20 @@ void dwpw_wsl_kernel(KArgs a) {
             return u32x4{w == 0 ? v : 0u, w == 1 ? v : 0u, w == 2 ? v : 0u, w == 3 ? v : 0u};
         };
         // LDS byte offsets of the lane's window reads for pixel block j and tap pair tp;
-        // pixels past the tile read pixel 0 (their results are never stored), the empty
-        // tenth tap reads the first tap's pixel
+        // pixels past the tile read the last pixel (their results are never stored; the
+        // same address as the block's last real lane, so no further bank group), the
+        // empty tenth tap reads the first tap's pixel
         uint32_t xoff[MBW][NTP];
 #pragma unroll
         for (int j = 0; j < MBW; ++j) {
-            const int p0 = (jb + j) * 16 + lr, p = p0 < NPX ? p0 : 0;
+            const int p0 = (jb + j) * 16 + lr, p = p0 < NPX ? p0 : NPX - 1;
             const int r = p / TW, c = p % TW;
 #pragma unroll
             for (int tp = 0; tp < NTP; ++tp) {
                 const int t0 = 2 * tp + (lg >> 1), t = t0 < 9 ? t0 : 0;
                 const int ih = r * S + t / 3, iw = c * S + t % 3;
                 const int q = 2 * cbw + (lg & 1);
-                xoff[j][tp] = (uint32_t)((ih * IW + iw) * CH + (q ^ (iw & 7))) * 16u;
+                xoff[j][tp] = (uint32_t)((ih * IW + iw) * CH + (q ^ ((iw - ih) & 7))) * 16u;
             }
         }
         // intermediate: depthwise output rows 4(l/16)+i of channel block cb are channels
