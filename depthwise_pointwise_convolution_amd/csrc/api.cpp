@@ -50,8 +50,11 @@ const VariantImpl kImpls[] = {
     {launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC>},
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC) {launch_b2b_mm<CT, S, OCC>, occ_b2b_mm<CT, S, OCC>},
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
-    {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>,           \
-     occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>},
+    {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, 1>,        \
+     occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, 1>},
+#define FCM_V_DWPW_MMWD(name, dt, CT, S, D, TH, TW, KT, CMAX, NW, OCC) \
+    {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, D>,             \
+     occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, D>},
 #define FCM_V_DWPW_WS(name, dt, CTy, S, TH, TW, CT, KT, NW) \
     {launch_dwpw_ws<CTy, S, TH, TW, CT, KT, NW>, occ_dwpw_ws<CTy, S, TH, TW, CT, KT, NW>},
 #define FCM_V_DWPW_WSL(name, dt, CT, S, TH, TW, KT, CMAX, NW) \
@@ -76,6 +79,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_DWPW_MM
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
+#undef FCM_V_DWPW_MMWD
 #undef FCM_V_PWDW_MM
 #undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS
@@ -727,12 +731,24 @@ fcm_status fcm_dw_fwd(const fcm_plan_t* plan, const void* x, const void* w_dw,
         // dilation, multiplier, chunk); one workgroup per (tile, chunk)
         FCM_TRY(check_variant(plan));
         const VariantDesc& v = kVariants[plan->variant];
+        // the layer-by-layer depthwise kernel depends on (storage type, stride, filter,
+        // dilation, multiplier) only: a plan whose variant has none (a matrix-core variant
+        // for dilated taps) takes that of a generalised variant with the same fields
+        launch_fn lbl_dw = kImpls[plan->variant].lbl_first;
+        for (int i = 0; !lbl_dw && i < kNumVariants; ++i) {
+            const VariantDesc& g = kVariants[i];
+            if (g.vkind == VK_DWPW_GEN && g.dtype == v.dtype && g.stride == v.stride &&
+                g.fs == plan->prob.R && g.dil == prob_dil_h(plan->prob) &&
+                g.mult == prob_mult(plan->prob))
+                lbl_dw = kImpls[i].lbl_first;
+        }
+        if (!lbl_dw)
+            return fail(FCM_ERR_UNSUPPORTED, "no layer-by-layer kernel for this depthwise layer");
         set_tiles(&a, lbl::DWG_TH, lbl::DWG_TW, 1, 1);
-        (void)v;
         const int64_t grid =
             (int64_t)a.num_ptiles * ((plan->prob.C + lbl::DWG_CC - 1) / lbl::DWG_CC);
         if (grid > INT32_MAX) return fail(FCM_ERR_UNSUPPORTED, "too many depthwise tiles");
-        const int rc = kImpls[plan->variant].lbl_first(a, (int)grid, stream);
+        const int rc = lbl_dw(a, (int)grid, stream);
         if (rc != 0)
             return fail(FCM_ERR_HIP, std::string("kernel launch failed: ") +
                                          hipGetErrorString((hipError_t)rc));

@@ -42,13 +42,14 @@
 
 namespace fcm {
 
-template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
+// D: dilation of the depthwise taps (the window then spans (TH-1)S + 2D + 1 rows)
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC, int D>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void dwpw_mmw_kernel(KArgs a) {
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     constexpr int NT = 64 * NW, CC = 64, NB = 3;
     constexpr int NPX = TH * TW, MB = (NPX + 15) / 16;
-    constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3, NPIX = IH * IW;
+    constexpr int IH = (TH - 1) * S + 2 * D + 1, IW = (TW - 1) * S + 2 * D + 1, NPIX = IH * IW;
     constexpr int CH = CC / 8;  // 16-byte pieces per pixel
     constexpr int SLOTS = NPIX * CH;
     constexpr int R = (SLOTS + NT - 1) / NT;  // direct-load rounds per chunk
@@ -294,7 +295,7 @@ void dwpw_mmw_kernel(KArgs a) {
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
             const int t0 = 2 * tp + (lg >> 1), t = t0 < 9 ? t0 : 0;
-            const int ih = r * S + t / 3, iw = c * S + t % 3;
+            const int ih = r * S + (t / 3) * D, iw = c * S + (t % 3) * D;
             const int q = 2 * cbw + (lg & 1);
             xoff[j][tp] = (uint32_t)((ih * IW + iw) * CH + (q ^ (iw & 7))) * 16u;
         }
@@ -514,17 +515,17 @@ void dwpw_mmw_kernel(KArgs a) {
     mm::wait_vmcnt<0>();
 }
 
-template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC, int D>
 int launch_dwpw_mmw(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((dwpw_mmw_kernel<T, S, TH, TW, KT, CMAX, NW, OCC>), dim3(grid), dim3(64 * NW), 0,
+    hipLaunchKernelGGL((dwpw_mmw_kernel<T, S, TH, TW, KT, CMAX, NW, OCC, D>), dim3(grid), dim3(64 * NW), 0,
                        (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
-template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC, int D>
 int occ_dwpw_mmw() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dwpw_mmw_kernel<T, S, TH, TW, KT, CMAX, NW, OCC>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dwpw_mmw_kernel<T, S, TH, TW, KT, CMAX, NW, OCC, D>,
                                                      64 * NW, 0) != hipSuccess)
         return 0;
     return n;
@@ -535,9 +536,12 @@ int occ_dwpw_mmw() {
 #define FCM_V_B2B(...)
 #define FCM_V_DWPW_MM(...)
 #define FCM_V_B2B_MM(...)
-#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC)                        \
-    template int launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>(const KArgs&, int, void*); \
-    template int occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC>();
+#define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC)                           \
+    template int launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, 1>(const KArgs&, int, void*); \
+    template int occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, 1>();
+#define FCM_V_DWPW_MMWD(name, dt, CT, S, D, TH, TW, KT, CMAX, NW, OCC)                        \
+    template int launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, D>(const KArgs&, int, void*); \
+    template int occ_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, D>();
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
@@ -545,5 +549,6 @@ int occ_dwpw_mmw() {
 #undef FCM_V_DWPW_MM
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
+#undef FCM_V_DWPW_MMWD
 
 }  // namespace fcm

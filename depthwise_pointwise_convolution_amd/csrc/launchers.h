@@ -22,9 +22,9 @@ int launch_dwpw_mm(const KArgs& a, int grid, void* stream);
 template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC>
 int occ_dwpw_mm();
 
-template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC, int D>
 int launch_dwpw_mmw(const KArgs& a, int grid, void* stream);
-template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC, int D>
 int occ_dwpw_mmw();
 
 template <typename T, int S, int TH, int TW, int CT, int KT, int NW>

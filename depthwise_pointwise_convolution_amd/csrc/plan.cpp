@@ -50,6 +50,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_B2B_MM, dt, S, 4, 16, 64, 64, 1, 2, 64, OCC, 4, 0, 0},
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
     {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0},
+#define FCM_V_DWPW_MMWD(name, dt, CT, S, D, TH, TW, KT, CMAX, NW, OCC) \
+    {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0, 3, D, 1},
 #define FCM_V_DWPW_WS(name, dt, CTy, S, TH, TW, CT, KT, NW) \
     {#name, VK_DWPW_WS, dt, S, TH, TW, KT, CT, 1, 2, 0, NW / 4, NW, CT, 0},
 #define FCM_V_DWPW_WSL(name, dt, CT, S, TH, TW, KT, CMAX, NW) \
@@ -71,6 +73,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_DWPW_MM
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
+#undef FCM_V_DWPW_MMWD
 #undef FCM_V_PWDW_MM
 #undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS
@@ -168,7 +171,9 @@ int variant_lds_bytes(const VariantDesc& v) {
                      v.fs * v.fs * cm * 4 + 2 * cm * 4) +
                2 * v.kt * 4 + red;
     }
-    const int IH = (v.th - 1) * v.stride + 3, IW = (v.tw - 1) * v.stride + 3;
+    // (a variant compiled for dilated taps spans 2 dil + 1 pixels per window side)
+    const int ext = v.dil > 1 ? 2 * v.dil + 1 : 3;
+    const int IH = (v.th - 1) * v.stride + ext, IW = (v.tw - 1) * v.stride + ext;
     const int P = v.th * v.tw;
     switch (v.vkind) {
     case VK_DWPW:
@@ -306,8 +311,8 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         // two sets of pointwise operands, depthwise operands and operand offsets, the
         // direct-load plan, staging and addressing
         const int mb = (P + 15) / 16, kbw = v.kt / (16 * v.waves), nt = 64 * v.waves;
-        const int ppw = mb * 4 / v.waves;
-        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * 8;
+        const int ppw = mb * 4 / v.waves, ext = v.dil > 1 ? 2 * v.dil + 1 : 3;
+        const int slots = ((v.th - 1) * v.stride + ext) * ((v.tw - 1) * v.stride + ext) * 8;
         return 4 * mb * kbw + 16 * kbw + 28 + 5 * ppw + 2 * ((slots + nt - 1) / nt) + 36 + 24;
     }
     case VK_DWPW_WSL: {
@@ -546,6 +551,31 @@ fcm_status validate_problem(const fcm_problem* p, std::string* err) {
 }
 
 bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) {
+    // the chunked matrix-core variants compiled for dilated 3x3 taps run the generalised
+    // problems with that dilation (and multiplier 1), nothing else
+    const bool dil_mmw = v.vkind == VK_DWPW_MMW && v.dil > 1;
+    if (dil_mmw) {
+        if (!prob_is_gen(p) || v.dtype != p.dtype || p.R != 3 || p.S != 3 ||
+            prob_dil_h(p) != v.dil || prob_dil_w(p) != v.dil || prob_mult(p) != 1 ||
+            v.stride != p.stride_h) {
+            if (why) *why = "dilated matrix-core variant is for a 3x3 depthwise layer with its "
+                            "dilation, multiplier 1, its stride and storage type";
+            return false;
+        }
+        if (p.C % 64 != 0 || p.C > v.cmax) {
+            if (why) *why = "chunked matrix-core variant needs C a multiple of 64 up to its "
+                            "compiled channel count";
+            return false;
+        }
+        const int Ho = conv_out(p.H, p.pad_h, prob_ext_h(p), p.stride_h);
+        const int Wo = conv_out(p.W, p.pad_w, prob_ext_w(p), p.stride_w);
+        if (sat_mul({p.N, p.H, p.W, p.C, 2}) >= ((int64_t)1 << 31) ||
+            sat_mul({p.N, Ho, Wo, p.K, 2}) >= ((int64_t)1 << 31)) {
+            if (why) *why = "matrix-core depthwise variant addresses whole tensors below 2 GiB";
+            return false;
+        }
+        return true;
+    }
     if (v.vkind == VK_DWPW_GEN || prob_is_gen(p)) {
         if (v.vkind != VK_DWPW_GEN || p.kind != FCM_KIND_DWPW || v.dtype != p.dtype) {
             if (why) *why = "variant is for another module kind, depthwise form or storage type";
@@ -805,7 +835,9 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     const int64_t grid = persistent_grid(ptiles, ktiles, (int64_t)d.num_cus * std::max(occ, 1));
     r.grid = (int)grid;
 
-    const int64_t halo = halo_pixels(Ho, Wo, p.H, p.W, v.th, v.tw, p.stride_h, p.pad_h, p.pad_w);
+    // (window extent from the problem: a dilated layer on a variant compiled for it)
+    const int64_t halo = halo_pixels(Ho, Wo, p.H, p.W, v.th, v.tw, p.stride_h, p.pad_h, p.pad_w,
+                                     prob_ext_h(p), prob_ext_w(p));
     const int64_t x_reads = halo * p.N * p.C * e * ktiles;
     const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K * e;
     const int n1 = p.kind == FCM_KIND_B2B ? p.K1 : p.C;
@@ -885,7 +917,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     finish_time(r, t_hbm, t_l2, t_mat, t_vec, busy);
 
     // Eq.-style estimate (FCM paper Sec. IV): DW->PW constructed from Eq. 2 and 3.
-    const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, 3,
+    const double overlap = eq1_overlap(p.W, p.H, v.tw * p.stride_w, v.th * p.stride_h, prob_ext_h(p),
                                        p.stride_h);
     const double ifm = (double)p.N * p.H * p.W * p.C * e;
     const double w_pw = (double)p.K * n1 * e;
@@ -1358,7 +1390,7 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
         if (forced >= 0 && i != forced) continue;
         const VariantDesc& v = kVariants[i];
         if (!variant_runs(v, *p, forced >= 0 ? &why : nullptr)) continue;
-        Estimate e = prob_is_gen(*p)              ? estimate_gen(v, *p, d, Ho, Wo)
+        Estimate e = v.vkind == VK_DWPW_GEN        ? estimate_gen(v, *p, d, Ho, Wo)
                      : p->kind == FCM_KIND_PWDW   ? estimate_pwdw(v, *p, d, Ho, Wo)
                      : p->kind == FCM_KIND_PWDWPW ? estimate_pwdwpw(v, *p, d, Ho, Wo)
                      : p->kind == FCM_KIND_PWPW ? estimate_pwpw(v, *p, d)

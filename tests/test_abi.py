@@ -629,7 +629,9 @@ def test_generalised_plan_accounting_and_variant_match():
         wl = fcm_inputs.WORKLOADS[name]
         pl = F.fcm_plan(_problem(F, wl), spec)
         vname = F.fcm_variant_name(pl.variant)
-        assert vname.startswith("gen_"), vname
+        # (a dilated 3x3 layer with C a multiple of 64 may run on the chunked
+        # matrix-core kernel compiled for its dilation)
+        assert vname.startswith(("gen_", "mmwd_")), vname
         e = acct.ELEM_BYTES[wl.dtype]
         assert pl.w1_packed_bytes == wl.C * wl.mult * wl.R * wl.S * e
         # the packed pointwise filters: the plain [K][C*mult] array and its blocked copy

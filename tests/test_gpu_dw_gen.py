@@ -31,6 +31,7 @@ CASES = [
     ("f16", 1, 15, 17, 72, 64, 7, 1, 1, 1, 3, "relu", "relu", True),
     ("f16", 2, 12, 19, 96, 264, 3, 2, 1, 1, 2, "relu6", "none", True),
     ("f16", 1, 8, 9, 32, 40, 3, 2, 1, 1, 1, "none", "none", True),
+    ("f16", 1, 11, 21, 128, 72, 3, 2, 1, 1, 2, "relu6", "relu", True),
     ("f16", 2, 10, 23, 32, 128, 3, 1, 2, 1, 1, "relu6", "relu6", True),
     ("f16", 1, 17, 13, 48, 72, 3, 1, 2, 2, 1, "relu", "none", True),
     ("bf16", 2, 13, 14, 40, 56, 5, 1, 1, 1, 2, "relu", "relu6", True),
