@@ -52,6 +52,16 @@
 // complete in issue order).  Per-lane offsets are fixed for the whole kernel; the
 // tile's position enters as a scalar offset, so interior tiles need no per-lane
 // address arithmetic at all.
+//
+// Depth multiplier M = 2 (the depthwise layer of the PyTorch forum's "Using optimised
+// depthwise convolutions", with in_chans * 2 outputs: output channel j reads input
+// channel j / 2).  CC then counts intermediate channels, the window holds CC / 2 input
+// channels, and the 16 intermediate channels of a block read 8 input channels, one
+// 16-byte piece per pixel.  A product then takes one input row's three taps in its four
+// 8-channel reduction slots (slot l/16 = tap column, the fourth slot zero-weighted):
+// A[row i][(slot s, channel e)] = w[3 dh + s][16 cb + i] where e == i / 2, else 0.  Each
+// input row is read once per channel block and serves the (up to three) output rows
+// below it, three products per 16 channels x 16 pixels instead of five.
 #include <type_traits>
 
 #include "mm_common.h"
@@ -59,21 +69,22 @@
 namespace fcm {
 
 
-template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void dwpw_mm_kernel(KArgs a) {
     constexpr int NT = 64 * NW;
+    static_assert(M == 1 || M == 2, "depth multiplier 1 or 2");
     static_assert(TH == 4 && TW == 16, "4 rows of 16 pixels per tile");
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     // wave w works on channel / output group w % 4 and rows RW * (w / 4) .. + RW - 1
     constexpr int RW = TH * 4 / NW;
     constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3, NPIX = IH * IW;
-    constexpr int CH = CC / 8;  // 16-byte chunks per pixel
-    static_assert(CH == 8 || CH == 16, "swizzle needs 8 or 16 chunks per pixel");
+    constexpr int CH = CC / (8 * M);  // 16-byte chunks per pixel (CC / M input channels)
+    static_assert(CH == 4 || CH == 8 || CH == 16, "swizzle needs 4, 8 or 16 chunks per pixel");
     constexpr int SLOTS = NPIX * CH;
     constexpr int R = (SLOTS + NT - 1) / NT;  // direct-load rounds per tile
     constexpr int SLOTS_P = R * NT;
-    constexpr int NCB = CC / 16, NKS = CC / 32, NTP = 5;
+    constexpr int NCB = CC / 16, NKS = CC / 32, NTP = M == 1 ? 5 : 3;
     constexpr int CBW = NCB / 4;  // depthwise channel blocks per wave
     static_assert(NCB % 4 == 0, "each wave owns whole channel blocks");
     constexpr int KW = KT / 4;    // pointwise output channels per wave
@@ -154,19 +165,23 @@ void dwpw_mm_kernel(KArgs a) {
     };
 
     // ---- direct-load plan (tile invariant) ---------------------------------------------
-    // LDS slot s holds chunk q of window pixel p = s / CH with s % CH = q ^ (column &
-    // (CH - 1)): the 16 lanes of an operand read (consecutive columns, same chunk) then
-    // fall in distinct bank groups (a pixel is CH 16-byte chunks, so without the swizzle
-    // they would all share one), and moving down a row moves every slot by a constant.
+    // LDS slot s holds chunk q of window pixel p = s / CH with s % CH = q ^ key(column),
+    // key = column & (CH - 1): the 16 lanes of an operand read (consecutive columns, same
+    // chunk) then fall in distinct bank groups (a pixel is CH 16-byte chunks, so without
+    // the swizzle they would all share one), and moving down a row moves every slot by a
+    // constant.  With 4 chunks per pixel two neighbouring pixels fill one 128-byte bank
+    // line, so the key is (column / 2) & 3: 8 consecutive columns then take 8 distinct
+    // 16-byte bank groups.
     // dl_off: byte offset of the slot's source relative to the window origin (kOob for
     // padding slots); dl_pos: the slot's window row and column.
+    auto swz = [](int col) { return CH >= 8 ? col & (CH - 1) : (col >> 1) & (CH - 1); };
     uint32_t dl_off[R];
     int dl_pos[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int s = r * NT + tid;
         const int p = s / CH, ihl = p / IW, iwl = p % IW;
-        const int q = (s % CH) ^ (iwl & (CH - 1));
+        const int q = (s % CH) ^ swz(iwl);
         const bool real = s < SLOTS && q * 8 < a.C;
         dl_off[r] = real ? (uint32_t)((ihl * a.W + iwl) * a.C + q * 8) * (uint32_t)sizeof(T)
                          : mm::kOob;
@@ -224,9 +239,15 @@ void dwpw_mm_kernel(KArgs a) {
     // 16cb + l%16, reduction index 8(l/16) + e = (tap pair_tap(tp, (l/16)/2), channel
     // 16cb + 8((l/16)&1) + e); non-zero only where that channel is the row's, i.e. one
     // 16-bit element per lane.
+    // M = 2: operand tp = dh, lane (l%16, l/16): row = intermediate channel 16cb + l%16,
+    // reduction index 8(l/16) + e = (tap (dh, l/16), input channel 8cb + e) for l/16 < 3
+    // (the fourth slot has zero weights); non-zero only at e = (l%16)/2, the row's input
+    // channel.
     auto pair_tap = [](int tp, int hh) { return tp < 3 ? 3 * tp + hh : tp == 3 ? 3 * hh + 2 : 8 + hh; };
-    const bool dw_active = (lr >> 3) == (lg & 1);
-    const int dw_e = lr & 7;
+    auto lane_tap = [&](int tp) { return M == 1 ? pair_tap(tp, lg >> 1) : lg < 3 ? 3 * tp + lg : 0; };
+    const bool dw_active = M == 1 ? (lr >> 3) == (lg & 1) : lg < 3;
+    const int dw_e = M == 1 ? lr & 7 : lr >> 1;
+    const int C1 = a.C * M;  // intermediate channels
     const float* s1p = a.s1 ? a.s1 : (const float*)a.w2;
     const float* b1p = a.b1 ? a.b1 : (const float*)a.w2;
     const float* s2p = a.s2 ? a.s2 : (const float*)a.w2;
@@ -238,13 +259,13 @@ void dwpw_mm_kernel(KArgs a) {
         const int cb = og + 4 * j;
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
-            const int t = pair_tap(tp, lg >> 1), c = cb * 16 + lr;
+            const int t = lane_tap(tp), c = cb * 16 + lr;
             wdr[j][tp] = __builtin_bit_cast(uint16_t,
-                                            wdw[(t < 9 ? t : 0) * a.C + (c < a.C ? c : 0)]);
+                                            wdw[(t < 9 ? t : 0) * C1 + (c < C1 ? c : 0)]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = cb * 16 + lg * 4 + i, cc = c < a.C ? c : 0;
+            const int c = cb * 16 + lg * 4 + i, cc = c < C1 ? c : 0;
             s1l[j][i] = s1p[cc];
             b1l[j][i] = b1p[cc];
         }
@@ -256,10 +277,10 @@ void dwpw_mm_kernel(KArgs a) {
     // K or C are clamped to existing ones: their rows are never stored, and the
     // intermediate channels they would multiply are zero.
     static_assert(KW == 32, "one 32-channel block group per wave");
-    const u32x4* __restrict__ wpb = reinterpret_cast<const u32x4*>(wpw + (int64_t)a.K * a.C);
+    const u32x4* __restrict__ wpb = reinterpret_cast<const u32x4*>(wpw + (int64_t)a.K * C1);
     u32x4 wa[NKS][KBW];
     {
-        const int g = min(kw0 >> 5, (a.K + 31) / 32 - 1), s32 = (a.C + 31) / 32;
+        const int g = min(kw0 >> 5, (a.K + 31) / 32 - 1), s32 = (C1 + 31) / 32;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -286,14 +307,14 @@ void dwpw_mm_kernel(KArgs a) {
         const int cb = og + 4 * j;
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
-            const int t = pair_tap(tp, lg >> 1), c = cb * 16 + lr;
-            const bool ok = dw_active && t < 9 && c < a.C;
+            const int t = lane_tap(tp), c = cb * 16 + lr;
+            const bool ok = dw_active && t < 9 && c < C1;
             const uint32_t v = ok ? (uint32_t)wdr[j][tp] : 0u;
             wdc[j][tp] = (dw_e & 1) ? (v << 16) : v;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = cb * 16 + lg * 4 + i < a.C;
+            const bool ok = cb * 16 + lg * 4 + i < C1;
             s1r[j][i] = (a.s1 && ok) ? s1l[j][i] : 1.0f;
             b1r[j][i] = (a.b1 && ok) ? b1l[j][i] : 0.0f;
         }
@@ -319,18 +340,25 @@ void dwpw_mm_kernel(KArgs a) {
     // (dh,0)+(dh,1) pairs (column lr*S + (l/16)/2), xo_q for the dw = 2 pairs (column
     // lr*S + 2, the upper lane half one row down), xo_qc the same without the row step
     // (for the window's last row, where only the (2,2) pair uses the read: the upper
-    // half then meets zero weights and must only stay inside the tile).
+    // half then meets zero weights and must only stay inside the tile).  M = 2: one
+    // read per input row, xo_p at column lr*S + l/16 of chunk cb (the zero-weighted
+    // fourth slot reads column lr*S).
     const int hh = lg >> 1;
     auto lds_off = [&](int j, int row, int col) {
-        const int q = 2 * (og + 4 * j) + (lg & 1);
-        return (uint32_t)((row * IW + col) * CH + (q ^ (col & (CH - 1)))) * 16u;
+        const int q = M == 1 ? 2 * (og + 4 * j) + (lg & 1) : og + 4 * j;
+        return (uint32_t)((row * IW + col) * CH + (q ^ swz(col))) * 16u;
     };
     uint32_t xo_p[CBW], xo_q[CBW], xo_qc[CBW];
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
-        xo_p[j] = lds_off(j, 0, lr * S + hh);
-        xo_q[j] = lds_off(j, hh, lr * S + 2);
-        xo_qc[j] = lds_off(j, 0, lr * S + 2);
+        if constexpr (M == 1) {
+            xo_p[j] = lds_off(j, 0, lr * S + hh);
+            xo_q[j] = lds_off(j, hh, lr * S + 2);
+            xo_qc[j] = lds_off(j, 0, lr * S + 2);
+        } else {
+            xo_p[j] = lds_off(j, 0, lr * S + (lg < 3 ? lg : 0));
+            xo_q[j] = xo_qc[j] = xo_p[j];
+        }
     }
     // intermediate: depthwise rows 4(l/16)+i of channel block cb are channels
     // 16(cb%2) + 4(l/16) + i of slice cb/2, i.e. lane group 2(cb%2) + (l/16)/2, bytes
@@ -357,7 +385,8 @@ void dwpw_mm_kernel(KArgs a) {
     // for its RW rows; epilogue 1; 8 bytes per lane into the intermediate tile, where
     // they form half of a pointwise B operand
     // operand reads of one input row of the window: the (dh,0)+(dh,1) operand always,
-    // the dw = 2 operand when a (0,2)+(1,2) or (2,2) product uses the row
+    // the dw = 2 operand when a (0,2)+(1,2) or (2,2) product uses the row (M = 1; with
+    // M = 2 the one read of a row holds all three of its taps)
     auto q_used = [](int ir) {
         return (ir % S == 0 && ir / S < RW) || (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW);
     };
@@ -378,7 +407,7 @@ void dwpw_mm_kernel(KArgs a) {
 #pragma unroll
             for (int ir = 0; ir < IHW; ++ir) {
                 bp[j][ir] = *reinterpret_cast<const u32x4*>(xb + xo_p[j] + ir * IROW_BYTES);
-                if (q_used(ir))
+                if (M == 1 && q_used(ir))
                     bq[j][ir] = *reinterpret_cast<const u32x4*>(
                         xb + (ir + 1 < IHW ? xo_q[j] : xo_qc[j]) + ir * IROW_BYTES);
             }
@@ -387,7 +416,8 @@ void dwpw_mm_kernel(KArgs a) {
             const u32x4* wf = wdf[j];
             const int cb = og + 4 * j;
             // input rows outer: each operand applied to every output row that uses it
-            // (RW independent accumulation chains)
+            // (RW independent accumulation chains); wf[dh] holds the taps (dh, 0) and
+            // (dh, 1) (M = 1) or the whole filter row dh (M = 2)
             f32x4 d[RW];
 #pragma unroll
             for (int r = 0; r < RW; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -397,10 +427,12 @@ void dwpw_mm_kernel(KArgs a) {
                 for (int dh = 0; dh < 3; ++dh)
                     if (ir >= dh && (ir - dh) % S == 0 && (ir - dh) / S < RW)
                         d[(ir - dh) / S] = mfma<T>(wf[dh], bp[j][ir], d[(ir - dh) / S]);
-                if (ir % S == 0 && ir / S < RW)
-                    d[ir / S] = mfma<T>(wf[3], bq[j][ir], d[ir / S]);
-                if (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW)
-                    d[(ir - 2) / S] = mfma<T>(wf[4], bq[j][ir], d[(ir - 2) / S]);
+                if constexpr (M == 1) {
+                    if (ir % S == 0 && ir / S < RW)
+                        d[ir / S] = mfma<T>(wf[3], bq[j][ir], d[ir / S]);
+                    if (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW)
+                        d[(ir - 2) / S] = mfma<T>(wf[4], bq[j][ir], d[(ir - 2) / S]);
+                }
             }
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
@@ -415,8 +447,8 @@ void dwpw_mm_kernel(KArgs a) {
                     pack8<T>(o));
             }
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, CBW * (IHW + NQ), 0);  // operand reads
-        __builtin_amdgcn_sched_group_barrier(0x008, CBW * RW * 5, 0);      // products
+        __builtin_amdgcn_sched_group_barrier(0x100, CBW * (IHW + (M == 1 ? NQ : 0)), 0);  // reads
+        __builtin_amdgcn_sched_group_barrier(0x008, CBW * RW * NTP, 0);  // products
     };
     // phase B of one tile: pointwise on the matrix cores, this wave's KW output
     // channels for its RW rows, epilogue 2, 16-byte stores; always NST stores per lane
@@ -516,18 +548,18 @@ void dwpw_mm_kernel(KArgs a) {
     mm::wait_vmcnt<0>();
 }
 
-template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M>
 int launch_dwpw_mm(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC>), dim3(grid), dim3(64 * NW), 0,
-                       (hipStream_t)stream, a);
+    hipLaunchKernelGGL((dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC, M>), dim3(grid),
+                       dim3(64 * NW), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
-template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M>
 int occ_dwpw_mm() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC>, 64 * NW, 0) != hipSuccess)
+            &n, dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC, M>, 64 * NW, 0) != hipSuccess)
         return 0;
     return n;
 }
@@ -536,15 +568,19 @@ int occ_dwpw_mm() {
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
 #define FCM_V_B2B_MM(...)
-#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC)                              \
-    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC>(const KArgs&, int, void*); \
-    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC>();
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC)                                 \
+    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1>(const KArgs&, int, void*); \
+    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1>();
+#define FCM_V_DWPW_MMM(name, dt, CT, S, M, TH, TW, KT, CC, NW, OCC)                            \
+    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M>(const KArgs&, int, void*); \
+    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M>();
 #define FCM_V_DWPW_MMW(...)
 #include "../variants.def"
 #undef FCM_V_DWPW
 #undef FCM_V_DWPW32
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
+#undef FCM_V_DWPW_MMM
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 

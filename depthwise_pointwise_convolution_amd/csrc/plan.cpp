@@ -52,6 +52,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0},
 #define FCM_V_DWPW_MMWD(name, dt, CT, S, D, TH, TW, KT, CMAX, NW, OCC) \
     {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0, 3, D, 1},
+#define FCM_V_DWPW_MMM(name, dt, CT, S, M, TH, TW, KT, CC, NW, OCC) \
+    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, NW, 0, 0, 3, 1, M},
 #define FCM_V_DWPW_WS(name, dt, CTy, S, TH, TW, CT, KT, NW) \
     {#name, VK_DWPW_WS, dt, S, TH, TW, KT, CT, 1, 2, 0, NW / 4, NW, CT, 0},
 #define FCM_V_DWPW_WSL(name, dt, CT, S, TH, TW, KT, CMAX, NW) \
@@ -74,6 +76,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_DWPW_MMWD
+#undef FCM_V_DWPW_MMM
 #undef FCM_V_PWDW_MM
 #undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS
@@ -186,8 +189,9 @@ int variant_lds_bytes(const VariantDesc& v) {
     case VK_B2B_MM: {
         // input tile (or chunk) buffers and as many intermediate tiles (one direct-load
         // round is one 16-byte piece per thread)
+        // (a depth multiplier m: the window holds cc / m input channels)
         const int nt = 64 * v.waves;
-        const int slots = IH * IW * (v.cc / 8);
+        const int slots = IH * IW * (v.cc / (8 * std::max(v.mult, 1)));
         const int slots_p = (slots + nt - 1) / nt * nt;
         const int tls = v.th * (v.cc / 32) * 64 * 16;
         return v.nbuf * (slots_p * 16 + tls);
@@ -293,12 +297,13 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         // per wave: pointwise operands of its KT/4 output channels and their epilogue
         // constants, its depthwise operands and epilogue-1 constants, the direct-load
         // plan, accumulators of its rows, staging and addressing
+        // (a depth multiplier: three depthwise operands per channel block, not five)
         const int cbw = v.cc / 64, nks = v.cc / 32, kbw = v.kt / 64, nt = 64 * v.waves;
-        const int rw = v.th * 4 / v.waves;
-        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * (v.cc / 8);
+        const int rw = v.th * 4 / v.waves, m = std::max(v.mult, 1);
+        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * (v.cc / (8 * m));
         (void)MBW;
-        return nks * kbw * 4 + v.kt / 8 + cbw * 20 + cbw * 8 + 2 * ((slots + nt - 1) / nt) +
-               rw * 4 + rw * kbw * 4 + 24 + 16;
+        return nks * kbw * 4 + v.kt / 8 + cbw * (m > 1 ? 12 : 20) + cbw * 8 +
+               2 * ((slots + nt - 1) / nt) + rw * 4 + rw * kbw * 4 + 24 + 16;
     }
     case VK_B2B_MM: {
         // per wave: 18 resident 3x3 operands, 8 resident 1x1 operands, 32 epilogue-2
@@ -576,6 +581,30 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         }
         return true;
     }
+    // the matrix-core variants compiled for a depth multiplier run the generalised
+    // problems with an undilated 3x3 layer and that multiplier, C * M intermediate
+    // channels in one pass
+    if (v.vkind == VK_DWPW_MM && v.mult > 1) {
+        if (!prob_is_gen(p) || v.dtype != p.dtype || p.R != 3 || p.S != 3 ||
+            prob_dil_h(p) != 1 || prob_dil_w(p) != 1 || prob_mult(p) != v.mult ||
+            v.stride != p.stride_h) {
+            if (why) *why = "matrix-core multiplier variant is for an undilated 3x3 depthwise "
+                            "layer with its multiplier, its stride and storage type";
+            return false;
+        }
+        if ((int64_t)p.C * v.mult > v.cc) {
+            if (why) *why = "matrix-core multiplier variant needs C * mult <= its channel chunk";
+            return false;
+        }
+        const int Ho = conv_out(p.H, p.pad_h, 3, p.stride_h);
+        const int Wo = conv_out(p.W, p.pad_w, 3, p.stride_w);
+        if (sat_mul({p.N, p.H, p.W, p.C, 2}) >= ((int64_t)1 << 31) ||
+            sat_mul({p.N, Ho, Wo, p.K, 2}) >= ((int64_t)1 << 31)) {
+            if (why) *why = "matrix-core depthwise variant addresses whole tensors below 2 GiB";
+            return false;
+        }
+        return true;
+    }
     if (v.vkind == VK_DWPW_GEN || prob_is_gen(p)) {
         if (v.vkind != VK_DWPW_GEN || p.kind != FCM_KIND_DWPW || v.dtype != p.dtype) {
             if (why) *why = "variant is for another module kind, depthwise form or storage type";
@@ -840,9 +869,10 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
                                      prob_ext_h(p), prob_ext_w(p));
     const int64_t x_reads = halo * p.N * p.C * e * ktiles;
     const int64_t y_bytes = (int64_t)p.N * Ho * Wo * p.K * e;
-    const int n1 = p.kind == FCM_KIND_B2B ? p.K1 : p.C;
+    // (first-layer outputs: K1 for B2B, C * mult for DW->PW)
+    const int n1 = p.kind == FCM_KIND_B2B ? p.K1 : p.C * prob_mult(p);
     const int64_t w1_bytes =
-        (int64_t)(p.kind == FCM_KIND_B2B ? (int64_t)p.K1 * 9 * p.C : 9LL * p.C) * e;
+        (int64_t)(p.kind == FCM_KIND_B2B ? (int64_t)p.K1 * 9 * p.C : 9LL * n1) * e;
     const int64_t w2_slice = (int64_t)std::min(v.kt, p.K) * n1 * e;
     const int64_t epi = (int64_t)4 * 2 * (n1 + v.kt);
     int64_t w_reads;
@@ -902,7 +932,10 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
         t_mat = P * pad_px * (2.0 * c64 * p.K + 384.0 * c64 * ktiles) / (2.0 * d.mfma_f16_flops);
         t_vec = P * pad_px * 5.0 * ((double)n1 * ktiles + p.K) / lane_ops_per_s;
     } else if (v.vkind == VK_DWPW_MM) {
-        t_mat = P * pad_px * (2.0 * p.C * p.K + 320.0 * v.cc * ktiles) / d.mfma_f16_flops;
+        // (with a depth multiplier: 3 instructions per 16 intermediate channels x 16
+        // pixels, 192 flop-equivalents per intermediate channel and pixel)
+        t_mat = P * pad_px * (2.0 * n1 * p.K + (v.mult > 1 ? 192.0 : 320.0) * v.cc * ktiles) /
+                d.mfma_f16_flops;
         // operand expansion when a wave owns several depthwise channel blocks
         t_vec = P * pad_px * (epi_ops + (v.cc > 64 ? 1.25 * v.cc * ktiles : 0.0)) /
                 lane_ops_per_s;

@@ -395,7 +395,7 @@ def test_forced_variants_cover_every_compiled_kernel():
         for k in (64, 136)] + [
         fcm_inputs.Workload("g", "dwpw", dt, N=2, H=17, W=23, C=c, K=k, K1=c * m, R=f, S=f,
                             stride=s, pad=(f - 1) * d // 2, dil=d, mult=m)
-        for dt in ("f16", "bf16") for c, k in ((40, 48), (64, 136)) for s in (1, 2)
+        for dt in ("f16", "bf16") for c, k in ((32, 72), (40, 48), (64, 136)) for s in (1, 2)
         for f, d, m in ((5, 1, 1), (7, 1, 1), (3, 2, 1), (3, 1, 2))] + [
         fcm_inputs.Workload("i", "pwdwpw", dt, N=2, H=17, W=23, C=24, K=24, K1=k1, stride=s)
         for dt in ("f16", "bf16") for k1 in (96, 144) for s in (1, 2)]
@@ -631,7 +631,7 @@ def test_generalised_plan_accounting_and_variant_match():
         vname = F.fcm_variant_name(pl.variant)
         # (a dilated 3x3 layer with C a multiple of 64 may run on the chunked
         # matrix-core kernel compiled for its dilation)
-        assert vname.startswith(("gen_", "mmwd_")), vname
+        assert vname.startswith(("gen_", "mmwd_", "mmm_")), vname
         e = acct.ELEM_BYTES[wl.dtype]
         assert pl.w1_packed_bytes == wl.C * wl.mult * wl.R * wl.S * e
         # the packed pointwise filters: the plain [K][C*mult] array and its blocked copy
