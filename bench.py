@@ -41,7 +41,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KDIR = "depthwise_pointwise_convolution_amd/csrc/kernels/"
 # source file of each fused kernel family (by variant-name prefix) and the headers they share
 KERNEL_FILES = [("dwpw_i8_", "dwpw_i8.hip"), ("wsl_", "dwpw_wsl.hip"), ("ws_", "dwpw_ws.hip"), ("pwdwpw_", "pwdwpw_mm.hip"),
-                ("mmw_", "dwpw_mmw.hip"), ("mmwd_", "dwpw_mmw.hip"), ("mmm_", "dwpw_mm.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
+                ("mmw_", "dwpw_mmw.hip"), ("mmwd_", "dwpw_mmw.hip"), ("mmm_", "dwpw_mm.hip"), ("mmf_", "dwpw_mm.hip"), ("mm_", "dwpw_mm.hip"), ("b2bmm_", "b2b_mm.hip"),
                 ("dwpw_", "dwpw.hip"), ("b2b_", "b2b.hip"), ("pwdw_", "pwdw_mm.hip"),
                 ("pwpw_", "pwpw_mm.hip"), ("gen_", "dwpw_gen.hip")]
 SHARED_SOURCES = ["mm_common.h", "stages.h", "common.h"]

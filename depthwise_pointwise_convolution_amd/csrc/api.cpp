@@ -47,9 +47,14 @@ const VariantImpl kImpls[] = {
 #define FCM_V_B2B(name, dt, CT, S, TH, TW, K1, KT, CC) \
     {launch_b2b_mfma<CT, S, TH, TW, K1, KT, CC>, occ_b2b_mfma<CT, S, TH, TW, K1, KT, CC>},
 #define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC) \
-    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1>},
+    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1, 3>,      \
+     occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1, 3>},
 #define FCM_V_DWPW_MMM(name, dt, CT, S, M, TH, TW, KT, CC, NW, OCC) \
-    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M>, occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M>},
+    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M, 3>,          \
+     occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M, 3>},
+#define FCM_V_DWPW_MMF(name, dt, CT, S, FS, TH, TW, KT, CC, NW, OCC) \
+    {launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1, FS>,          \
+     occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1, FS>},
 #define FCM_V_B2B_MM(name, dt, CT, S, OCC) {launch_b2b_mm<CT, S, OCC>, occ_b2b_mm<CT, S, OCC>},
 #define FCM_V_DWPW_MMW(name, dt, CT, S, TH, TW, KT, CMAX, NW, OCC) \
     {launch_dwpw_mmw<CT, S, TH, TW, KT, CMAX, NW, OCC, 1>,        \
@@ -83,6 +88,7 @@ const VariantImpl kImpls[] = {
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_DWPW_MMWD
 #undef FCM_V_DWPW_MMM
+#undef FCM_V_DWPW_MMF
 #undef FCM_V_PWDW_MM
 #undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS

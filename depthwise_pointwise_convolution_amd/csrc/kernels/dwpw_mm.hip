@@ -62,30 +62,54 @@
 // A[row i][(slot s, channel e)] = w[3 dh + s][16 cb + i] where e == i / 2, else 0.  Each
 // input row is read once per channel block and serves the (up to three) output rows
 // below it, three products per 16 channels x 16 pixels instead of five.
+//
+// Filter size FS = 5 (M = 1; the forum page's depthwise layer with a 5x5 kernel): the
+// taps pair within a filter row, (dh,0)+(dh,1) and (dh,2)+(dh,3), and down the last
+// column, (0,4)+(1,4), (2,4)+(3,4), (4,4) alone: 13 products per 16 channels x 16 pixels.
+// The depthwise operands stay in registers in compact form (one 32-bit word each) and
+// are expanded where used, and phase A runs block by block, so that only one block's
+// operand reads are held at a time.
 #include <type_traits>
 
 #include "mm_common.h"
 
 namespace fcm {
 
+// f(std::integral_constant<int, I>) for I = B .. E - 1: loop indices that are constants
+// (the scheduling-group builtin takes constant instruction counts)
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
-template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M, int FS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void dwpw_mm_kernel(KArgs a) {
     constexpr int NT = 64 * NW;
     static_assert(M == 1 || M == 2, "depth multiplier 1 or 2");
+    static_assert(FS == 3 || (FS == 5 && M == 1), "3x3 filters, or 5x5 with multiplier 1");
     static_assert(TH == 4 && TW == 16, "4 rows of 16 pixels per tile");
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     // wave w works on channel / output group w % 4 and rows RW * (w / 4) .. + RW - 1
     constexpr int RW = TH * 4 / NW;
-    constexpr int IH = (TH - 1) * S + 3, IW = (TW - 1) * S + 3, NPIX = IH * IW;
+    constexpr int IH = (TH - 1) * S + FS, IW = (TW - 1) * S + FS, NPIX = IH * IW;
     constexpr int CH = CC / (8 * M);  // 16-byte chunks per pixel (CC / M input channels)
     static_assert(CH == 4 || CH == 8 || CH == 16, "swizzle needs 4, 8 or 16 chunks per pixel");
     constexpr int SLOTS = NPIX * CH;
     constexpr int R = (SLOTS + NT - 1) / NT;  // direct-load rounds per tile
     constexpr int SLOTS_P = R * NT;
-    constexpr int NCB = CC / 16, NKS = CC / 32, NTP = M == 1 ? 5 : 3;
+    // depthwise operands per channel block: NPR tap pairs per filter row, NQP pairs down
+    // the last column (M = 1); one per filter row (M = 2)
+    constexpr int NPR = FS / 2, NQP = (FS + 1) / 2;
+    constexpr int NCB = CC / 16, NKS = CC / 32, NTP = M == 1 ? FS * NPR + NQP : 3;
     constexpr int CBW = NCB / 4;  // depthwise channel blocks per wave
+    // 5x5 phase A: wave w owns channel blocks w, w + NW, ... for all TH rows (fewer
+    // filter operands per wave than CBW blocks over RW rows)
+    constexpr int CBD = FS == 5 ? NCB / NW : CBW;
+    static_assert(FS == 3 || NCB % NW == 0, "5x5: whole channel blocks per wave");
     static_assert(NCB % 4 == 0, "each wave owns whole channel blocks");
     constexpr int KW = KT / 4;    // pointwise output channels per wave
     constexpr int KBW = KW / 16;  // 16-channel output blocks per wave
@@ -94,7 +118,7 @@ void dwpw_mm_kernel(KArgs a) {
     static_assert(NST < 64, "vmcnt range");
     constexpr uint32_t IROW_BYTES = (uint32_t)IW * CH * 16;  // one input row down
     constexpr uint32_t ROW_BYTES = S * IROW_BYTES;             // one output row down
-    constexpr int IHW = (RW - 1) * S + 3;  // input rows under a wave's RW output rows
+    constexpr int IHW = (RW - 1) * S + FS;  // input rows under a wave's RW output rows
 
     // separate arrays per buffer: the compiler then sees that reading one buffer does
     // not depend on the direct loads still in flight into the other
@@ -110,6 +134,8 @@ void dwpw_mm_kernel(KArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int og = wave & 3, row0 = RW * (wave >> 2);
+    // the depthwise channel block j of this wave
+    auto blk = [&](int j) { return FS == 5 ? wave + NW * j : og + 4 * j; };
     const int lr = lane & 15, lg = lane >> 4;
     const Act act1 = act_bounds(a.act1), act2 = act_bounds(a.act2);
     const int G = gridDim.x;
@@ -243,7 +269,13 @@ void dwpw_mm_kernel(KArgs a) {
     // reduction index 8(l/16) + e = (tap (dh, l/16), input channel 8cb + e) for l/16 < 3
     // (the fourth slot has zero weights); non-zero only at e = (l%16)/2, the row's input
     // channel.
-    auto pair_tap = [](int tp, int hh) { return tp < 3 ? 3 * tp + hh : tp == 3 ? 3 * hh + 2 : 8 + hh; };
+    // (general FS: operand tp < FS * NPR pairs the taps (tp / NPR, 2 (tp % NPR) + hh), the
+    // others the taps (2 (tp - FS * NPR) + hh, FS - 1); FS * FS marks an absent tap)
+    auto pair_tap = [](int tp, int hh) {
+        if (tp < FS * NPR) return (tp / NPR) * FS + 2 * (tp % NPR) + hh;
+        const int dh = 2 * (tp - FS * NPR) + hh;
+        return dh < FS ? dh * FS + FS - 1 : FS * FS;
+    };
     auto lane_tap = [&](int tp) { return M == 1 ? pair_tap(tp, lg >> 1) : lg < 3 ? 3 * tp + lg : 0; };
     const bool dw_active = M == 1 ? (lr >> 3) == (lg & 1) : lg < 3;
     const int dw_e = M == 1 ? lr & 7 : lr >> 1;
@@ -252,16 +284,16 @@ void dwpw_mm_kernel(KArgs a) {
     const float* b1p = a.b1 ? a.b1 : (const float*)a.w2;
     const float* s2p = a.s2 ? a.s2 : (const float*)a.w2;
     const float* b2p = a.b2 ? a.b2 : (const float*)a.w2;
-    uint16_t wdr[CBW][NTP];
-    float s1l[CBW][4], b1l[CBW][4];
+    uint16_t wdr[CBD][NTP];
+    float s1l[CBD][4], b1l[CBD][4];
 #pragma unroll
-    for (int j = 0; j < CBW; ++j) {
-        const int cb = og + 4 * j;
+    for (int j = 0; j < CBD; ++j) {
+        const int cb = blk(j);
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
             const int t = lane_tap(tp), c = cb * 16 + lr;
             wdr[j][tp] = __builtin_bit_cast(uint16_t,
-                                            wdw[(t < 9 ? t : 0) * C1 + (c < C1 ? c : 0)]);
+                                            wdw[(t < FS * FS ? t : 0) * C1 + (c < C1 ? c : 0)]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -300,15 +332,15 @@ void dwpw_mm_kernel(KArgs a) {
     issue_tile(nxt, std::integral_constant<int, 1>{});
 
     // now the loaded values are used
-    uint32_t wdc[CBW][NTP];
-    float s1r[CBW][4], b1r[CBW][4];
+    uint32_t wdc[CBD][NTP];
+    float s1r[CBD][4], b1r[CBD][4];
 #pragma unroll
-    for (int j = 0; j < CBW; ++j) {
-        const int cb = og + 4 * j;
+    for (int j = 0; j < CBD; ++j) {
+        const int cb = blk(j);
 #pragma unroll
         for (int tp = 0; tp < NTP; ++tp) {
             const int t = lane_tap(tp), c = cb * 16 + lr;
-            const bool ok = dw_active && t < 9 && c < C1;
+            const bool ok = dw_active && t < FS * FS && c < C1;
             const uint32_t v = ok ? (uint32_t)wdr[j][tp] : 0u;
             wdc[j][tp] = (dw_e & 1) ? (v << 16) : v;
         }
@@ -323,12 +355,15 @@ void dwpw_mm_kernel(KArgs a) {
         const int w = dw_e >> 1;
         return u32x4{w == 0 ? v : 0u, w == 1 ? v : 0u, w == 2 ? v : 0u, w == 3 ? v : 0u};
     };
-    // the expanded operands stay in registers for the whole kernel
-    u32x4 wdf[CBW][NTP];
+    // the expanded operands stay in registers for the whole kernel (3x3; the thirteen of
+    // a 5x5 filter are expanded where used)
+    u32x4 wdf[CBW][FS == 3 ? NTP : 1];
+    if constexpr (FS == 3) {
 #pragma unroll
-    for (int j = 0; j < CBW; ++j)
+        for (int j = 0; j < CBW; ++j)
 #pragma unroll
-        for (int tp = 0; tp < NTP; ++tp) wdf[j][tp] = dw_operand(wdc[j][tp]);
+            for (int tp = 0; tp < NTP; ++tp) wdf[j][tp] = dw_operand(wdc[j][tp]);
+    }
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
         const bool ok = kw0 + lg * (KW / 4) + i < a.K;
@@ -345,16 +380,19 @@ void dwpw_mm_kernel(KArgs a) {
     // fourth slot reads column lr*S).
     const int hh = lg >> 1;
     auto lds_off = [&](int j, int row, int col) {
-        const int q = M == 1 ? 2 * (og + 4 * j) + (lg & 1) : og + 4 * j;
+        const int q = M == 1 ? 2 * blk(j) + (lg & 1) : blk(j);
         return (uint32_t)((row * IW + col) * CH + (q ^ swz(col))) * 16u;
     };
-    uint32_t xo_p[CBW], xo_q[CBW], xo_qc[CBW];
+    // (FS = 5: xo_p5[j][i] for the (dh,2i)+(dh,2i+1) pairs, xo_q / xo_qc at column lr*S + 4)
+    uint32_t xo_p[CBD], xo_q[CBD], xo_qc[CBD], xo_p5[CBD][NPR];
 #pragma unroll
-    for (int j = 0; j < CBW; ++j) {
+    for (int j = 0; j < CBD; ++j) {
         if constexpr (M == 1) {
             xo_p[j] = lds_off(j, 0, lr * S + hh);
-            xo_q[j] = lds_off(j, hh, lr * S + 2);
-            xo_qc[j] = lds_off(j, 0, lr * S + 2);
+            xo_q[j] = lds_off(j, hh, lr * S + FS - 1);
+            xo_qc[j] = lds_off(j, 0, lr * S + FS - 1);
+#pragma unroll
+            for (int i = 0; i < NPR; ++i) xo_p5[j][i] = lds_off(j, 0, lr * S + 2 * i + hh);
         } else {
             xo_p[j] = lds_off(j, 0, lr * S + (lg < 3 ? lg : 0));
             xo_q[j] = xo_qc[j] = xo_p[j];
@@ -387,17 +425,104 @@ void dwpw_mm_kernel(KArgs a) {
     // operand reads of one input row of the window: the (dh,0)+(dh,1) operand always,
     // the dw = 2 operand when a (0,2)+(1,2) or (2,2) product uses the row (M = 1; with
     // M = 2 the one read of a row holds all three of its taps)
+    // (general FS: the last-column operand of a row when any pair (2jq, FS-1)+(2jq+1,
+    // FS-1) of an output row starts on it)
     auto q_used = [](int ir) {
-        return (ir % S == 0 && ir / S < RW) || (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW);
+        bool u = false;
+        for (int jq = 0; jq < NQP; ++jq)
+            u = u || (ir >= 2 * jq && (ir - 2 * jq) % S == 0 && (ir - 2 * jq) / S < RW);
+        return u;
     };
     constexpr int NQ = [] {
         int n = 0;
-        for (int ir = 0; ir < IHW; ++ir)
-            n += (ir % S == 0 && ir / S < RW) || (ir >= 2 && (ir - 2) % S == 0 && (ir - 2) / S < RW);
+        for (int ir = 0; ir < IHW; ++ir) {
+            bool u = false;
+            for (int jq = 0; jq < NQP; ++jq)
+                u = u || (ir >= 2 * jq && (ir - 2 * jq) % S == 0 && (ir - 2 * jq) / S < RW);
+            n += u;
+        }
         return n;
     }();
+    // epilogue 1 of block j's TH rows and their intermediate writes (5x5 phase A; the
+    // block's parity picks the lane group and half, as tls_w does for og)
+    auto store_block = [&](int j, const f32x4* d, u32x4* dst, auto identity1) {
+        const int cb = blk(j);
+        const uint32_t tw =
+            (uint32_t)(((2 * (cb & 1) + (lg >> 1)) * 16 + lr) * 16 + (lg & 1) * 8);
+#pragma unroll
+        for (int r = 0; r < TH; ++r) {
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = decltype(identity1)::value ? d[r][i]
+                                                  : epilogue(d[r][i], s1r[j][i], b1r[j][i], act1);
+            st8(reinterpret_cast<char*>(dst) + ((r * NKS + (cb >> 1)) * 64) * 16 + tw,
+                pack8<T>(o));
+        }
+    };
     auto phase_a = [&](const u32x4* src, u32x4* dst, auto identity1) {
         const char* xb = reinterpret_cast<const char*>(src) + row0 * ROW_BYTES;
+        if constexpr (FS == 5) {
+            // block by block, software-pipelined by input row: row ir + 1's operand reads
+            // are issued before row ir's products (the scheduling groups keep that order),
+            // so that about two rows of reads are held at a time
+            // (all TH output rows of the tile, IH input rows of the window)
+            const char* xw = reinterpret_cast<const char*>(src);
+            constexpr auto valid = [](int rr) { return rr >= 0 && rr % S == 0 && rr / S < TH; };
+            constexpr auto n_reads = [](int ir) {
+                bool q = false;
+                for (int jq = 0; jq < NQP; ++jq)
+                    q = q || (ir >= 2 * jq && (ir - 2 * jq) % S == 0 && (ir - 2 * jq) / S < TH);
+                return NPR + (q ? 1 : 0);
+            };
+            constexpr auto n_products = [](int ir) {
+                int n = 0;
+                for (int dh = 0; dh < FS; ++dh)
+                    n += (ir >= dh && (ir - dh) % S == 0 && (ir - dh) / S < TH) ? NPR : 0;
+                for (int jq = 0; jq < NQP; ++jq)
+                    n += (ir >= 2 * jq && (ir - 2 * jq) % S == 0 && (ir - 2 * jq) / S < TH) ? 1 : 0;
+                return n;
+            };
+            static_for<0, CBD>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                u32x4 bp[IH][NPR], bq[IH];
+                auto rd = [&](auto irc) {
+                    constexpr int ir = decltype(irc)::value;
+#pragma unroll
+                    for (int i = 0; i < NPR; ++i)
+                        bp[ir][i] =
+                            *reinterpret_cast<const u32x4*>(xw + xo_p5[j][i] + ir * IROW_BYTES);
+                    if constexpr (n_reads(ir) > NPR)
+                        bq[ir] = *reinterpret_cast<const u32x4*>(
+                            xw + (ir + 1 < IH ? xo_q[j] : xo_qc[j]) + ir * IROW_BYTES);
+                };
+                f32x4 d[TH];
+#pragma unroll
+                for (int r = 0; r < TH; ++r) d[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                rd(std::integral_constant<int, 0>{});
+                __builtin_amdgcn_sched_group_barrier(0x100, n_reads(0), 0);
+                static_for<0, IH>([&](auto irc) {
+                    constexpr int ir = decltype(irc)::value;
+                    if constexpr (ir + 1 < IH) rd(std::integral_constant<int, ir + 1>{});
+#pragma unroll
+                    for (int dh = 0; dh < FS; ++dh)
+                        if (valid(ir - dh))
+#pragma unroll
+                            for (int i = 0; i < NPR; ++i)
+                                d[(ir - dh) / S] = mfma<T>(dw_operand(wdc[j][dh * NPR + i]),
+                                                           bp[ir][i], d[(ir - dh) / S]);
+#pragma unroll
+                    for (int jq = 0; jq < NQP; ++jq)
+                        if (valid(ir - 2 * jq))
+                            d[(ir - 2 * jq) / S] = mfma<T>(dw_operand(wdc[j][FS * NPR + jq]),
+                                                           bq[ir], d[(ir - 2 * jq) / S]);
+                    if constexpr (ir + 1 < IH)
+                        __builtin_amdgcn_sched_group_barrier(0x100, n_reads(ir + 1), 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, n_products(ir), 0);
+                });
+                store_block(j, d, dst, identity1);
+            });
+        } else {
         // every operand of the window is requested first, then the products run (the
         // scheduling groups below keep that order), so the LDS latency is paid once per
         // phase instead of once per product
@@ -449,6 +574,7 @@ void dwpw_mm_kernel(KArgs a) {
         }
         __builtin_amdgcn_sched_group_barrier(0x100, CBW * (IHW + (M == 1 ? NQ : 0)), 0);  // reads
         __builtin_amdgcn_sched_group_barrier(0x008, CBW * RW * NTP, 0);  // products
+        }
     };
     // phase B of one tile: pointwise on the matrix cores, this wave's KW output
     // channels for its RW rows, epilogue 2, 16-byte stores; always NST stores per lane
@@ -548,18 +674,18 @@ void dwpw_mm_kernel(KArgs a) {
     mm::wait_vmcnt<0>();
 }
 
-template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M, int FS>
 int launch_dwpw_mm(const KArgs& a, int grid, void* stream) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL((dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC, M>), dim3(grid),
+    hipLaunchKernelGGL((dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC, M, FS>), dim3(grid),
                        dim3(64 * NW), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
-template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M, int FS>
 int occ_dwpw_mm() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC, M>, 64 * NW, 0) != hipSuccess)
+            &n, dwpw_mm_kernel<T, S, TH, TW, KT, CC, NW, OCC, M, FS>, 64 * NW, 0) != hipSuccess)
         return 0;
     return n;
 }
@@ -568,12 +694,15 @@ int occ_dwpw_mm() {
 #define FCM_V_DWPW32(...)
 #define FCM_V_B2B(...)
 #define FCM_V_B2B_MM(...)
-#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC)                                 \
-    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1>(const KArgs&, int, void*); \
-    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1>();
-#define FCM_V_DWPW_MMM(name, dt, CT, S, M, TH, TW, KT, CC, NW, OCC)                            \
-    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M>(const KArgs&, int, void*); \
-    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M>();
+#define FCM_V_DWPW_MM(name, dt, CT, S, TH, TW, KT, CC, NW, OCC)                                    \
+    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1, 3>(const KArgs&, int, void*); \
+    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1, 3>();
+#define FCM_V_DWPW_MMM(name, dt, CT, S, M, TH, TW, KT, CC, NW, OCC)                               \
+    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M, 3>(const KArgs&, int, void*); \
+    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, M, 3>();
+#define FCM_V_DWPW_MMF(name, dt, CT, S, FS, TH, TW, KT, CC, NW, OCC)                               \
+    template int launch_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1, FS>(const KArgs&, int, void*); \
+    template int occ_dwpw_mm<CT, S, TH, TW, KT, CC, NW, OCC, 1, FS>();
 #define FCM_V_DWPW_MMW(...)
 #include "../variants.def"
 #undef FCM_V_DWPW
@@ -581,6 +710,7 @@ int occ_dwpw_mm() {
 #undef FCM_V_B2B
 #undef FCM_V_DWPW_MM
 #undef FCM_V_DWPW_MMM
+#undef FCM_V_DWPW_MMF
 #undef FCM_V_B2B_MM
 #undef FCM_V_DWPW_MMW
 

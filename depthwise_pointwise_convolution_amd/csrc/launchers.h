@@ -17,10 +17,10 @@ int launch_dwpw_f32(const KArgs& a, int grid, void* stream);
 template <int S, int TH, int TW, int KT, int CC>
 int occ_dwpw_f32();
 
-// M: depth multiplier of the depthwise layer (1 or 2)
-template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M>
+// M: depth multiplier of the depthwise layer (1 or 2); FS: its filter size (3 or 5)
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M, int FS>
 int launch_dwpw_mm(const KArgs& a, int grid, void* stream);
-template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M>
+template <typename T, int S, int TH, int TW, int KT, int CC, int NW, int OCC, int M, int FS>
 int occ_dwpw_mm();
 
 template <typename T, int S, int TH, int TW, int KT, int CMAX, int NW, int OCC, int D>

@@ -54,6 +54,8 @@ const VariantDesc kVariants[] = {
     {#name, VK_DWPW_MMW, dt, S, TH, TW, KT, 64, 0, 3, 0, OCC, NW, CMAX, 0, 3, D, 1},
 #define FCM_V_DWPW_MMM(name, dt, CT, S, M, TH, TW, KT, CC, NW, OCC) \
     {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, NW, 0, 0, 3, 1, M},
+#define FCM_V_DWPW_MMF(name, dt, CT, S, FS, TH, TW, KT, CC, NW, OCC) \
+    {#name, VK_DWPW_MM, dt, S, TH, TW, KT, CC, 1, 2, 0, OCC, NW, 0, 0, FS, 1, 1},
 #define FCM_V_DWPW_WS(name, dt, CTy, S, TH, TW, CT, KT, NW) \
     {#name, VK_DWPW_WS, dt, S, TH, TW, KT, CT, 1, 2, 0, NW / 4, NW, CT, 0},
 #define FCM_V_DWPW_WSL(name, dt, CT, S, TH, TW, KT, CMAX, NW) \
@@ -77,6 +79,7 @@ const VariantDesc kVariants[] = {
 #undef FCM_V_DWPW_MMW
 #undef FCM_V_DWPW_MMWD
 #undef FCM_V_DWPW_MMM
+#undef FCM_V_DWPW_MMF
 #undef FCM_V_PWDW_MM
 #undef FCM_V_PWDWPW_MM
 #undef FCM_V_DWPW_WS
@@ -174,8 +177,9 @@ int variant_lds_bytes(const VariantDesc& v) {
                      v.fs * v.fs * cm * 4 + 2 * cm * 4) +
                2 * v.kt * 4 + red;
     }
-    // (a variant compiled for dilated taps spans 2 dil + 1 pixels per window side)
-    const int ext = v.dil > 1 ? 2 * v.dil + 1 : 3;
+    // (a variant compiled for another filter size or dilated taps spans (fs - 1) dil + 1
+    // pixels per window side)
+    const int ext = v.fs > 0 ? (v.fs - 1) * std::max(v.dil, 1) + 1 : 3;
     const int IH = (v.th - 1) * v.stride + ext, IW = (v.tw - 1) * v.stride + ext;
     const int P = v.th * v.tw;
     switch (v.vkind) {
@@ -299,11 +303,14 @@ int variant_vgpr_estimate(const VariantDesc& v) {
         // plan, accumulators of its rows, staging and addressing
         // (a depth multiplier: three depthwise operands per channel block, not five)
         const int cbw = v.cc / 64, nks = v.cc / 32, kbw = v.kt / 64, nt = 64 * v.waves;
-        const int rw = v.th * 4 / v.waves, m = std::max(v.mult, 1);
-        const int slots = ((v.th - 1) * v.stride + 3) * ((v.tw - 1) * v.stride + 3) * (v.cc / (8 * m));
+        // (a 5x5 filter: 13 compact operands per block and one block's operand reads)
+        const int rw = v.th * 4 / v.waves, m = std::max(v.mult, 1), fs = v.fs > 0 ? v.fs : 3;
+        const int slots = ((v.th - 1) * v.stride + fs) * ((v.tw - 1) * v.stride + fs) * (v.cc / (8 * m));
+        const int dwops = fs == 5 ? cbw * 13 + 3 * ((rw - 1) * v.stride + fs) * 4
+                                  : cbw * (m > 1 ? 12 : 20);
         (void)MBW;
-        return nks * kbw * 4 + v.kt / 8 + cbw * (m > 1 ? 12 : 20) + cbw * 8 +
-               2 * ((slots + nt - 1) / nt) + rw * 4 + rw * kbw * 4 + 24 + 16;
+        return nks * kbw * 4 + v.kt / 8 + dwops + cbw * 8 + 2 * ((slots + nt - 1) / nt) +
+               rw * 4 + rw * kbw * 4 + 24 + 16;
     }
     case VK_B2B_MM: {
         // per wave: 18 resident 3x3 operands, 8 resident 1x1 operands, 32 epilogue-2
@@ -581,23 +588,23 @@ bool variant_runs(const VariantDesc& v, const fcm_problem& p, std::string* why) 
         }
         return true;
     }
-    // the matrix-core variants compiled for a depth multiplier run the generalised
-    // problems with an undilated 3x3 layer and that multiplier, C * M intermediate
-    // channels in one pass
-    if (v.vkind == VK_DWPW_MM && v.mult > 1) {
-        if (!prob_is_gen(p) || v.dtype != p.dtype || p.R != 3 || p.S != 3 ||
-            prob_dil_h(p) != 1 || prob_dil_w(p) != 1 || prob_mult(p) != v.mult ||
+    // the matrix-core variants compiled for a depth multiplier or another filter size run
+    // the generalised problems with an undilated layer of that filter size and multiplier,
+    // C * M intermediate channels in one pass
+    if (v.vkind == VK_DWPW_MM && (v.mult > 1 || v.fs > 3)) {
+        if (!prob_is_gen(p) || v.dtype != p.dtype || p.R != v.fs || p.S != v.fs ||
+            prob_dil_h(p) != 1 || prob_dil_w(p) != 1 || prob_mult(p) != std::max(v.mult, 1) ||
             v.stride != p.stride_h) {
-            if (why) *why = "matrix-core multiplier variant is for an undilated 3x3 depthwise "
-                            "layer with its multiplier, its stride and storage type";
+            if (why) *why = "matrix-core generalised variant is for an undilated depthwise layer "
+                            "with its filter size and multiplier, its stride and storage type";
             return false;
         }
-        if ((int64_t)p.C * v.mult > v.cc) {
-            if (why) *why = "matrix-core multiplier variant needs C * mult <= its channel chunk";
+        if ((int64_t)p.C * std::max(v.mult, 1) > v.cc) {
+            if (why) *why = "matrix-core generalised variant needs C * mult <= its channel chunk";
             return false;
         }
-        const int Ho = conv_out(p.H, p.pad_h, 3, p.stride_h);
-        const int Wo = conv_out(p.W, p.pad_w, 3, p.stride_w);
+        const int Ho = conv_out(p.H, p.pad_h, v.fs, p.stride_h);
+        const int Wo = conv_out(p.W, p.pad_w, v.fs, p.stride_w);
         if (sat_mul({p.N, p.H, p.W, p.C, 2}) >= ((int64_t)1 << 31) ||
             sat_mul({p.N, Ho, Wo, p.K, 2}) >= ((int64_t)1 << 31)) {
             if (why) *why = "matrix-core depthwise variant addresses whole tensors below 2 GiB";
@@ -872,7 +879,7 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
     // (first-layer outputs: K1 for B2B, C * mult for DW->PW)
     const int n1 = p.kind == FCM_KIND_B2B ? p.K1 : p.C * prob_mult(p);
     const int64_t w1_bytes =
-        (int64_t)(p.kind == FCM_KIND_B2B ? (int64_t)p.K1 * 9 * p.C : 9LL * n1) * e;
+        (int64_t)(p.kind == FCM_KIND_B2B ? (int64_t)p.K1 * 9 * p.C : (int64_t)p.R * p.S * n1) * e;
     const int64_t w2_slice = (int64_t)std::min(v.kt, p.K) * n1 * e;
     const int64_t epi = (int64_t)4 * 2 * (n1 + v.kt);
     int64_t w_reads;
@@ -932,10 +939,12 @@ Estimate estimate(const VariantDesc& v, const fcm_problem& p, const fcm_device_s
         t_mat = P * pad_px * (2.0 * c64 * p.K + 384.0 * c64 * ktiles) / (2.0 * d.mfma_f16_flops);
         t_vec = P * pad_px * 5.0 * ((double)n1 * ktiles + p.K) / lane_ops_per_s;
     } else if (v.vkind == VK_DWPW_MM) {
-        // (with a depth multiplier: 3 instructions per 16 intermediate channels x 16
-        // pixels, 192 flop-equivalents per intermediate channel and pixel)
-        t_mat = P * pad_px * (2.0 * n1 * p.K + (v.mult > 1 ? 192.0 : 320.0) * v.cc * ktiles) /
-                d.mfma_f16_flops;
+        // (64 flop-equivalents per intermediate channel and pixel for each of the ntp
+        // instructions per 16 channels x 16 pixels: 5 for 3x3, 3 with multiplier 2, 13 for
+        // 5x5)
+        const int fs = v.fs > 0 ? v.fs : 3;
+        const int ntp = v.mult > 1 ? 3 : fs * (fs / 2) + (fs + 1) / 2;
+        t_mat = P * pad_px * (2.0 * n1 * p.K + 64.0 * ntp * v.cc * ktiles) / d.mfma_f16_flops;
         // operand expansion when a wave owns several depthwise channel blocks
         t_vec = P * pad_px * (epi_ops + (v.cc > 64 ? 1.25 * v.cc * ktiles : 0.0)) /
                 lane_ops_per_s;

@@ -631,7 +631,7 @@ def test_generalised_plan_accounting_and_variant_match():
         vname = F.fcm_variant_name(pl.variant)
         # (a dilated 3x3 layer with C a multiple of 64 may run on the chunked
         # matrix-core kernel compiled for its dilation)
-        assert vname.startswith(("gen_", "mmwd_", "mmm_")), vname
+        assert vname.startswith(("gen_", "mmwd_", "mmm_", "mmf_")), vname
         e = acct.ELEM_BYTES[wl.dtype]
         assert pl.w1_packed_bytes == wl.C * wl.mult * wl.R * wl.S * e
         # the packed pointwise filters: the plain [K][C*mult] array and its blocked copy

@@ -29,6 +29,8 @@ CASES = [
     ("f16", 1, 9, 35, 64, 136, 5, 1, 1, 2, 2, "relu6", "relu6", True),
     ("f16", 2, 11, 7, 24, 40, 5, 1, 1, 1, 0, "none", "relu", False),
     ("f16", 1, 15, 17, 72, 64, 7, 1, 1, 1, 3, "relu", "relu", True),
+    ("f16", 2, 9, 18, 120, 40, 5, 1, 1, 1, 1, "relu", "none", True),
+    ("f16", 1, 10, 29, 128, 72, 5, 1, 1, 1, 2, "relu6", "relu6", True),
     ("f16", 2, 12, 19, 96, 264, 3, 2, 1, 1, 2, "relu6", "none", True),
     ("f16", 1, 8, 9, 32, 40, 3, 2, 1, 1, 1, "none", "none", True),
     ("f16", 1, 11, 21, 128, 72, 3, 2, 1, 1, 2, "relu6", "relu", True),
