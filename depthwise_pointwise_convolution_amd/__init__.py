@@ -106,7 +106,8 @@ EXPORTS = ("fcm_default_device_spec", "fcm_query_device_spec", "fcm_plan", "fcm_
            "fcm_num_variants", "fcm_variant_name", "fcm_pack_weights", "fcm_dwpw_fwd",
            "fcm_tune",
            "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_pwpw_fwd", "fcm_dw_fwd", "fcm_pw_fwd",
-           "fcm_conv_fwd", "fcm_pwdwpw_fwd", "fcm_pwdwpw_lbl", "fcm_tune_pwdwpw",
+           "fcm_conv_fwd", "fcm_pwdwpw_fwd", "fcm_pwdwpw_lbl", "fcm_pwdwpw_lbl_noalloc",
+           "fcm_tune_pwdwpw",
            "fcm_status_str",
            "fcm_last_error")
 
@@ -150,6 +151,8 @@ def lib() -> ctypes.CDLL:
                                          vp, vp]
             L.fcm_pwdwpw_lbl.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp, fp, fp,
                                          vp, vp, vp, vp]
+            L.fcm_pwdwpw_lbl_noalloc.argtypes = [P(fcm_plan_t), vp, vp, fp, fp, vp, fp, fp, vp,
+                                                 fp, fp, vp, vp]
             L.fcm_tune_pwdwpw.argtypes = [P(fcm_problem), P(fcm_device_spec), _i32, P(vp), vp,
                                           fp, fp, vp, fp, fp, vp, fp, fp, P(vp), vp, _i32,
                                           P(fcm_plan_t)]
@@ -164,7 +167,7 @@ def lib() -> ctypes.CDLL:
                          "fcm_plan_variant", "fcm_pack_weights", "fcm_dwpw_fwd",
                          "fcm_b2b_conv_fwd", "fcm_pwdw_fwd", "fcm_pwpw_fwd", "fcm_dw_fwd",
                          "fcm_pw_fwd", "fcm_conv_fwd", "fcm_pwdwpw_fwd", "fcm_pwdwpw_lbl",
-                         "fcm_tune_pwdwpw", "fcm_tune"):
+                         "fcm_pwdwpw_lbl_noalloc", "fcm_tune_pwdwpw", "fcm_tune"):
                 getattr(L, name).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -335,6 +338,18 @@ def fcm_pwdwpw_lbl(plan, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bi
                                 _ptr(bias1), _ptr(w2), _ptr(scale2), _ptr(bias2), _ptr(w3),
                                 _ptr(scale3), _ptr(bias3), _ptr(t1), _ptr(t2), _ptr(y),
                                 _stream(stream)), "fcm_pwdwpw_lbl")
+
+
+# largest plan->workspace_bytes fcm_pwdwpw_lbl_noalloc takes (FCM_NOALLOC_SCRATCH_BYTES)
+FCM_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def fcm_pwdwpw_lbl_noalloc(plan, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3,
+                           y, stream=None):
+    _check(lib().fcm_pwdwpw_lbl_noalloc(ctypes.byref(plan), _ptr(x), _ptr(w1), _ptr(scale1),
+                                        _ptr(bias1), _ptr(w2), _ptr(scale2), _ptr(bias2),
+                                        _ptr(w3), _ptr(scale3), _ptr(bias3), _ptr(y),
+                                        _stream(stream)), "fcm_pwdwpw_lbl_noalloc")
 
 
 def fcm_tune_pwdwpw(prob, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3, y,

@@ -665,6 +665,78 @@ fcm_status fcm_pwdwpw_lbl(const fcm_plan_t* plan, const void* x, const void* w1,
     return launched(launch_pw_lbl(p.dtype, a, stream));
 }
 
+// ---- no-allocation layer-by-layer PW->DW->PW -----------------------------------------
+// The two intermediates of fcm_pwdwpw_lbl_noalloc live in this file-scope device array
+// (one copy per GPU, at its own address).  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per device with that
+// device current, and is kept per device.
+static __device__ __align__(256) unsigned char scratch[FCM_NOALLOC_SCRATCH_BYTES];
+
+namespace fcm {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// device address of `scratch` on the device that runs `stream` (the current device for
+// the null stream)
+fcm_status scratch_address(void* stream, void** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess)
+        return fail(FCM_ERR_HIP, std::string("hipGetDevice failed: ") + hipGetErrorString(e));
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d = 0;
+        e = hipStreamGetDevice((hipStream_t)stream, &d);
+        if (e != hipSuccess)
+            return fail(FCM_ERR_HIP,
+                        std::string("hipStreamGetDevice failed: ") + hipGetErrorString(e));
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(FCM_ERR_UNSUPPORTED, "device index beyond the static scratch table");
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(FCM_ERR_HIP, std::string("hipSetDevice failed: ") + hipGetErrorString(e));
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !ptr)
+            return fail(FCM_ERR_HIP, std::string("hipGetSymbolAddress(scratch) failed: ") +
+                                         hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ok();
+}
+}  // namespace
+}  // namespace fcm
+
+fcm_status fcm_pwdwpw_lbl_noalloc(const fcm_plan_t* plan, const void* x, const void* w1,
+                                  const float* scale1, const float* bias1, const void* w2,
+                                  const float* scale2, const float* bias2, const void* w3,
+                                  const float* scale3, const float* bias3, void* y,
+                                  void* stream) {
+    using namespace fcm;
+    FCM_TRY(check_plan(plan, FCM_KIND_PWDWPW));
+    if (plan->workspace_bytes > FCM_NOALLOC_SCRATCH_BYTES)
+        return fail(FCM_ERR_UNSUPPORTED,
+                    "layer-by-layer intermediates need " +
+                        std::to_string((long long)plan->workspace_bytes) +
+                        " bytes, more than the " +
+                        std::to_string((long long)FCM_NOALLOC_SCRATCH_BYTES) +
+                        "-byte static scratch of the no-allocation entry point");
+    void* base = nullptr;
+    FCM_TRY(scratch_address(stream, &base));
+    const fcm_problem& p = plan->prob;
+    const int e = p.dtype == FCM_F32 ? 4 : p.dtype == FCM_I8 ? 1 : 2;
+    const int64_t t1_bytes = (int64_t)p.N * p.H * p.W * p.K1 * e;
+    return fcm_pwdwpw_lbl(plan, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3,
+                          base, (char*)base + t1_bytes, y, stream);
+}
+
 
 fcm_status fcm_tune(const fcm_problem* prob, const fcm_device_spec* spec, int32_t nsets,
                     const void* const* x, const void* w1, const float* scale1,

@@ -355,6 +355,25 @@ fcm_status fcm_pwdwpw_lbl(const fcm_plan_t* plan, const void* x, const void* w1,
                           const float* scale3, const float* bias3, void* t1, void* t2, void* y,
                           void* stream);
 
+/* Largest workspace (plan->workspace_bytes) fcm_pwdwpw_lbl_noalloc takes: 32 MiB. */
+#define FCM_NOALLOC_SCRATCH_BYTES (32ll << 20)
+
+/* fcm_pwdwpw_lbl for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same three kernels,
+ * with t1 and t2 placed in a static device array of FCM_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (t1's bytes, then t2's).
+ * Allocates nothing.  Every call on one GPU shares that array, so calls that overlap on
+ * one GPU (two streams, or two host threads) race; calls in one stream are ordered.
+ * Nothing in the array needs clearing: each call writes t1 and t2 whole before reading
+ * them.  Same arguments as fcm_pwdwpw_lbl without t1 and t2.  Errors: INVALID_ARG
+ * (plan/pointer checks), UNSUPPORTED (plan->workspace_bytes above
+ * FCM_NOALLOC_SCRATCH_BYTES), HIP (device query, symbol address or launch failure). */
+fcm_status fcm_pwdwpw_lbl_noalloc(const fcm_plan_t* plan, const void* x, const void* w1,
+                                  const float* scale1, const float* bias1, const void* w2,
+                                  const float* scale2, const float* bias2, const void* w3,
+                                  const float* scale3, const float* bias3, void* y,
+                                  void* stream);
+
 /* fcm_tune for the PW -> DW -> PW module: every fused variant able to take `prob`
  * (kind FCM_KIND_PWDWPW) at each persistent grid, timed over the nsets pairs x[i], y[i]
  * with the three layers' filters and epilogues as fcm_pwdwpw_fwd takes them.  Writes

@@ -3,6 +3,7 @@ declares and the Python binding gives each a signature; the planner's integers a
 with the oracle's byte accounting and with brute-force tile enumeration; invalid
 problems and arguments are rejected on the host with the documented status codes
 before any HIP call."""
+import ctypes
 import itertools
 import math
 import os
@@ -766,3 +767,27 @@ def test_plan_paper_estimates_equal_the_oracle_transcription(name):
             assert math.isinf(pv.gma_paper_fused), F.fcm_variant_name(v)
         else:
             assert pv.gma_paper_fused == pytest.approx(fv, rel=1e-12), F.fcm_variant_name(v)
+
+
+def test_noalloc_entry_point_refuses_workspaces_above_its_static_scratch():
+    """fcm_pwdwpw_lbl_noalloc checks plan->workspace_bytes against the static scratch size
+    (the header's FCM_NOALLOC_SCRATCH_BYTES, mirrored in the binding) before any device
+    call, and refuses a larger plan with UNSUPPORTED and a message naming the limit."""
+    F = _lib()
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "fcm.h")).read()
+    m = re.search(r"#define FCM_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == F.FCM_NOALLOC_SCRATCH_BYTES
+    wl = fcm_inputs.WORKLOADS["pwdwpw_f16_32x112x112_c16_k96_k24_s2"]
+    pl = F.fcm_plan(_problem(F, wl), _spec(F))
+    assert pl.workspace_bytes > F.FCM_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x1000)
+    st = F.lib().fcm_pwdwpw_lbl_noalloc(ctypes.byref(pl), fake, fake, None, None, fake, None,
+                                        None, fake, None, None, fake, None)
+    assert st == F.FCM_ERR_UNSUPPORTED
+    assert "static scratch" in F.lib().fcm_last_error().decode()
+    # a plan of another module kind is an argument error
+    other = F.fcm_plan(_problem(F, fcm_inputs.WORKLOADS["mbv1_f16_8x112x112_c64_k128"]),
+                       _spec(F))
+    st = F.lib().fcm_pwdwpw_lbl_noalloc(ctypes.byref(other), fake, fake, None, None, fake,
+                                        None, None, fake, None, None, fake, None)
+    assert st == F.FCM_ERR_INVALID_ARG
