@@ -1463,13 +1463,14 @@ fcm_status plan_problem(const fcm_problem* p, const fcm_device_spec* spec, int f
             // different waves of a SIMD, which overlaps them; the roofline terms are the
             // same
             better = specialised(v.vkind);
-        } else if (std::min(e.wgs_per_cu * v.waves, 8) !=
-                   std::min(be.wgs_per_cu * kVariants[best].waves, 8)) {
-            // resident waves per CU, up to two per SIMD: more hide more latency (the kernels
-            // are latency and issue bound, which the roofline terms do not see); beyond
-            // that the measured builds gained nothing
-            better = std::min(e.wgs_per_cu * v.waves, 8) >
-                     std::min(be.wgs_per_cu * kVariants[best].waves, 8);
+        } else if (std::min(e.wgs_per_cu * v.waves, 12) !=
+                   std::min(be.wgs_per_cu * kVariants[best].waves, 12)) {
+            // resident waves per CU, up to three per SIMD: more hide more latency (the
+            // kernels are latency and issue bound, which the roofline terms do not see);
+            // beyond that the measured builds gained nothing (mbv1: three workgroups of
+            // four waves per CU 9.44 us against two 9.80 us)
+            better = std::min(e.wgs_per_cu * v.waves, 12) >
+                     std::min(be.wgs_per_cu * kVariants[best].waves, 12);
         } else if (e.pred != be.pred) {
             better = e.pred < be.pred;
         } else if (e.waste != be.waste) {
