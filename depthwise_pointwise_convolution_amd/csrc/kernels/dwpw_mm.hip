@@ -54,7 +54,7 @@
 // address arithmetic at all.
 //
 // Depth multiplier M = 2 (the depthwise layer of the PyTorch forum's "Using optimised
-// depthwise convolutions", with in_chans * 2 outputs: output channel j reads input
+// depthwise convolutions", two outputs per input channel: output channel j reads input
 // channel j / 2).  CC then counts intermediate channels, the window holds CC / 2 input
 // channels, and the 16 intermediate channels of a block read 8 input channels, one
 // 16-byte piece per pixel.  A product then takes one input row's three taps in its four
