@@ -11,6 +11,7 @@ kernels.  The functions carry the C ABI's names (see ``include/fcm.h``):
     fcm_pwpw_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, y)
     fcm_pwdwpw_fwd(plan, x, w1, scale1, bias1, w2, scale2, bias2, w3, scale3, bias3, y)
     fcm_dw_fwd / fcm_pw_fwd / fcm_conv_fwd / fcm_pwdwpw_lbl   (layer-by-layer baselines)
+    fcm_pwdwpw_lbl_noalloc   (the three-layer baseline with the library's static scratch)
 
 Tensor arguments are torch tensors on the GPU (or raw integer device addresses, or
 None where the ABI allows NULL); PyTorch only provides device memory and the stream
