@@ -791,3 +791,43 @@ def test_noalloc_entry_point_refuses_workspaces_above_its_static_scratch():
     st = F.lib().fcm_pwdwpw_lbl_noalloc(ctypes.byref(other), fake, fake, None, None, fake,
                                         None, None, fake, None, None, fake, None)
     assert st == F.FCM_ERR_INVALID_ARG
+
+
+def test_matrix_core_generalised_builds_take_exactly_their_problems():
+    """The multiplier-2 build (mmm_*) runs undilated 3x3 layers with multiplier 2 and
+    C * 2 <= 64 at stride 1; the 5x5 build (mmf_*) undilated 5x5 layers with multiplier 1
+    and C <= 128 at stride 1.  Every other generalised problem is refused with a reason,
+    and neither build takes a plain 3x3 module."""
+    F = _lib()
+    spec = _spec(F)
+    names = {F.fcm_variant_name(v): v for v in range(F.fcm_num_variants())}
+    mmm = names["mmm_f16_s1_m2_t4x16_k128_c64_o2"]
+    mmf = names["mmf_f16_s1_f5_t4x16_k128_c128_w8_o2"]
+
+    def runs(v, **kw):
+        base = dict(kind="dwpw", dtype="f16", N=1, H=12, W=20, C=32, K=64, K1=32, R=3, S=3,
+                    stride=1, pad=1, dil=1, mult=1)
+        base.update(kw)
+        wl = fcm_inputs.Workload("probe", **base)
+        try:
+            F.fcm_plan_variant(_problem(F, wl), v, spec)
+            return True
+        except F.FcmError as e:
+            assert e.status in (F.FCM_ERR_UNSUPPORTED, F.FCM_ERR_INVALID_ARG)
+            assert F.lib().fcm_last_error()
+            return False
+
+    assert runs(mmm, C=32, K1=64, mult=2)
+    assert runs(mmm, C=8, K1=16, mult=2, K=8)
+    assert not runs(mmm, C=40, K1=80, mult=2)              # C * 2 above the 64-channel pass
+    assert not runs(mmm, C=32, K1=64, mult=2, stride=2)
+    assert not runs(mmm, C=32, K1=64, mult=2, dil=2, pad=2)
+    assert not runs(mmm, C=32, K1=32)                      # plain module
+    assert not runs(mmm, C=16, K1=48, mult=3)
+    assert runs(mmf, C=120, K1=120, R=5, S=5, pad=2)
+    assert runs(mmf, C=128, K1=128, R=5, S=5, pad=0)
+    assert not runs(mmf, C=136, K1=136, R=5, S=5, pad=2)   # above the 128-channel pass
+    assert not runs(mmf, C=64, K1=64, R=5, S=5, pad=2, stride=2)
+    assert not runs(mmf, C=64, K1=64, R=7, S=7, pad=3)
+    assert not runs(mmf, C=64, K1=128, R=5, S=5, pad=2, mult=2)
+    assert not runs(mmf, C=64, K1=64)                      # plain module
