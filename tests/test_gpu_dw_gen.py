@@ -37,6 +37,7 @@ CASES = [
     ("f16", 2, 10, 23, 32, 128, 3, 1, 2, 1, 1, "relu6", "relu6", True),
     ("f16", 1, 17, 13, 48, 72, 3, 1, 2, 2, 1, "relu", "none", True),
     ("f16", 1, 9, 37, 24, 72, 3, 1, 2, 1, 0, "relu", "relu", True),
+    ("f16", 2, 6, 40, 8, 24, 3, 1, 2, 1, 1, "relu", "relu6", True),
     ("bf16", 2, 13, 14, 40, 56, 5, 1, 1, 1, 2, "relu", "relu6", True),
     ("bf16", 1, 9, 11, 64, 64, 3, 2, 1, 1, 2, "none", "relu", True),
     ("bf16", 2, 7, 20, 16, 136, 3, 1, 2, 1, 1, "relu6", "none", False),
